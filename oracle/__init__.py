@@ -1,0 +1,158 @@
+"""fp64 CPU oracle for the head-wise LSTM / Elman forward recurrence and the plain multi-layer LSTM.
+
+TEST INFRASTRUCTURE ONLY: the test-suite, the smoke check and the benchmark's CPU-baseline leg may
+use this package; the product path (``head_wise_lstm_amd``) never imports, loads or calls it, and
+this package imports nothing from the product.
+
+The arithmetic lives in ``frnn_oracle.c`` (plain C, double precision, OpenMP over independent
+(batch, head) rows); this module only marshals numpy float64 arrays to it. What is computed:
+
+* ``headwise_fwd`` -- FlashRNN usage example (hottg.com/neural/9889): layouts Wx[B,T,G,N,D],
+  R[G,N,D,D], b[G,N,D], states[S,B,T,N,D], last_states[S,B,1,N,D]; the cell is the one of
+  "5.3 LSTM" (developnotes.readthedocs.io, operator.html) applied per head, gates i, f, z, o along
+  G; Elman: h = tanh(Wx + h.R + b).
+* ``lstm_stack_p3`` -- "5.3 LSTM", MyLSTM.set_weights and MyLSTM.forward: time loop outermost,
+  layers inside it, bias = bias_ih + bias_hh, Wi stored [in, 4H], Wh stored [H, 4H].
+
+Pins (tests/test_oracle_pins.py): closed forms (R = 0 geometric gating, saturated forget gate,
+Elman scalar iteration) computed independently at 40 significant digits, torch.nn.LSTM / nn.RNN in
+float64 as library special cases, head / batch / continuation invariants, and hand-stepped tiny
+cases.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+SOURCE = os.path.join(_HERE, "frnn_oracle.c")
+LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+CELL_LSTM = 0
+CELL_ELMAN = 1
+
+
+def build(verbose: bool = False, source: str = SOURCE, out: str = LIB_PATH) -> str:
+    """Compile the oracle with gcc (IEEE double, no fast-math) into a shared library."""
+    cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99", source, "-o", out, "-lm"]
+    if verbose:
+        print(" ".join(cmd))
+    subprocess.run(cmd, check=True)
+    return out
+
+
+def _f64(a):
+    if a is None:
+        return None
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def _ptr(a):
+    if a is None:
+        return None
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+class Oracle:
+    """ctypes front of one compiled copy of frnn_oracle.c."""
+
+    def __init__(self, lib_path: str = LIB_PATH):
+        if not os.path.exists(lib_path):
+            if lib_path != LIB_PATH:
+                raise FileNotFoundError(lib_path)
+            build()
+        lib = ctypes.CDLL(lib_path)
+        dp = ctypes.POINTER(ctypes.c_double)
+        lib.oracle_headwise_fwd.restype = ctypes.c_int
+        lib.oracle_headwise_fwd.argtypes = [
+            ctypes.c_int, ctypes.c_long, ctypes.c_long, ctypes.c_long, ctypes.c_long,
+            dp, dp, dp, dp, dp, dp, ctypes.POINTER(ctypes.c_long), ctypes.c_long,
+        ]
+        lib.oracle_lstm_stack_p3.restype = ctypes.c_int
+        lib.oracle_lstm_stack_p3.argtypes = [
+            ctypes.c_long, ctypes.c_long, ctypes.c_long, ctypes.c_long, ctypes.c_long,
+            dp, ctypes.POINTER(dp), ctypes.POINTER(dp), ctypes.POINTER(dp), ctypes.POINTER(dp),
+            dp, dp, dp, dp, dp,
+        ]
+        self.lib = lib
+
+    def headwise_fwd(self, cell: str, Wx, R, b, states0=None, pairs=None, want_states: bool = True):
+        """Head-wise forward in float64.
+
+        Wx [B,T,G,N,D], R [G,N,D,D], b [G,N,D] (None = zeros), states0 [S,B,1,N,D] or None
+        (zeros). ``pairs``: optional iterable of flattened (b*N + n) rows to compute (the others
+        stay NaN). Returns (states [S,B,T,N,D] or None, last_states [S,B,1,N,D]).
+        """
+        c = {"lstm": CELL_LSTM, "elman": CELL_ELMAN}[cell]
+        G, S = (4, 2) if c == CELL_LSTM else (1, 1)
+        Wx, R = _f64(Wx), _f64(R)
+        B, T, G_, N, D = Wx.shape
+        b = np.zeros((G, N, D)) if b is None else _f64(b)
+        states0 = _f64(states0)
+        if G_ != G or R.shape != (G, N, D, D) or b.shape != (G, N, D):
+            raise ValueError("shape mismatch")
+        if states0 is not None and states0.shape != (S, B, 1, N, D):
+            raise ValueError("states0 shape mismatch")
+        states = np.full((S, B, T, N, D), np.nan) if want_states else None
+        last = np.full((S, B, 1, N, D), np.nan)
+        if pairs is not None:
+            pr = np.ascontiguousarray(np.asarray(list(pairs), dtype=np.int64))
+            pp, npairs = pr.ctypes.data_as(ctypes.POINTER(ctypes.c_long)), len(pr)
+        else:
+            pr, pp, npairs = None, None, 0
+        rc = self.lib.oracle_headwise_fwd(c, B, T, N, D, _ptr(Wx), _ptr(R), _ptr(b), _ptr(states0),
+                                          _ptr(states), _ptr(last), pp, npairs)
+        if rc != 0:
+            raise RuntimeError("oracle_headwise_fwd failed")
+        return states, last
+
+    def lstm_stack_p3(self, x, Wi, Wh, b_ih, b_hh, h0=None, c0=None):
+        """Plain multi-layer LSTM of "5.3 LSTM" in float64.
+
+        x [T,B,I]; Wi, Wh, b_ih, b_hh: lists over layers ([in,4H], [H,4H], [4H], [4H]; a bias
+        may be None = zeros); h0, c0 [L,B,H] or None. Returns (out [T,B,H], hn, cn [L,B,H]).
+        """
+        x = _f64(x)
+        T, B, I = x.shape
+        L = len(Wi)
+        H = Wh[0].shape[0]
+        Wi = [_f64(w) for w in Wi]
+        Wh = [_f64(w) for w in Wh]
+        b_ih = [np.zeros(4 * H) if v is None else _f64(v) for v in b_ih]
+        b_hh = [np.zeros(4 * H) if v is None else _f64(v) for v in b_hh]
+        for l in range(L):
+            if Wi[l].shape != ((I if l == 0 else H), 4 * H) or Wh[l].shape != (H, 4 * H):
+                raise ValueError("weight shape mismatch")
+        h0, c0 = _f64(h0), _f64(c0)
+        out = np.empty((T, B, H))
+        hn = np.empty((L, B, H))
+        cn = np.empty((L, B, H))
+        arr = ctypes.POINTER(ctypes.c_double) * L
+        rc = self.lib.oracle_lstm_stack_p3(
+            L, T, B, I, H, _ptr(x), arr(*[_ptr(w) for w in Wi]), arr(*[_ptr(w) for w in Wh]),
+            arr(*[_ptr(v) for v in b_ih]), arr(*[_ptr(v) for v in b_hh]), _ptr(h0), _ptr(c0),
+            _ptr(out), _ptr(hn), _ptr(cn))
+        if rc != 0:
+            raise RuntimeError("oracle_lstm_stack_p3 failed")
+        return out, hn, cn
+
+
+_default = None
+
+
+def default() -> Oracle:
+    global _default
+    if _default is None:
+        _default = Oracle()
+    return _default
+
+
+def headwise_fwd(*args, **kwargs):
+    return default().headwise_fwd(*args, **kwargs)
+
+
+def lstm_stack_p3(*args, **kwargs):
+    return default().lstm_stack_p3(*args, **kwargs)

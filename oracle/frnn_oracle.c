@@ -1,0 +1,204 @@
+/*
+ * frnn_oracle.c -- plain, slow, fp64 CPU oracle for the head-wise LSTM / Elman forward recurrence
+ * and for the plain multi-layer LSTM.
+ *
+ * TEST INFRASTRUCTURE ONLY. Nothing on the product path may link, load or call this file: it is
+ * used by the test-suite, by the smoke check and by the benchmark's CPU-baseline leg. It shares no
+ * code, header, table or constant with the HIP library.
+ *
+ * Sources of what is computed (cited by page title and section):
+ *  - "FlashRNN: optimisation of RNNs on modern hardware" (hottg.com/neural/9889), usage example:
+ *    tensor layouts Wx[B,T,G,N,D], R[G,N,D,D], b[G,N,D], states_initial[S,B,1,N,D],
+ *    states[S,B,T,N,D]; for the LSTM the hidden state h is the first of [h, c]; the call returns
+ *    (states, last_states). The page names the cells lstm / elman but prints no equations.
+ *  - "5.3 LSTM" (developnotes.readthedocs.io, operator.html), MyLSTM.forward: per step
+ *    ifgo = x_t*Wi + h*Wh + bias, split into four column blocks i, f, g, o; i, f, o pass a sigmoid,
+ *    g a tanh; c = f*c + i*g; h = o*tanh(c); layer l >= 1 takes layer l-1's new h as its input;
+ *    out[t] is the top layer's h; MyLSTM.set_weights: bias = bias_ih + bias_hh.
+ *  - The head-wise reading: the 5.3 cell applied independently to every head n with that head's
+ *    recurrent matrix R[:, n] (h as a row vector: pre[g][e] = sum_d h[d] * R[g,n,d,e]), the gate
+ *    order along G being i, f, z (=g), o. Elman: h = tanh(Wx + h*R + b), G = 1, S = 1.
+ *
+ * Everything is computed in double precision; inputs arrive already widened (exactly) to double.
+ * Summation over d runs d = 0..D-1 in order for every output e. No blocking, fusion or reordering.
+ * Batch rows and heads never interact, so (b, n) pairs run in parallel (OpenMP), which changes no
+ * arithmetic.
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORACLE_CELL_LSTM 0
+#define ORACLE_CELL_ELMAN 1
+
+/* Logistic sigmoid, textbook definition (5.3 LSTM: torch.sigmoid). */
+static double sigmoid(double x) { return 1.0 / (1.0 + exp(-x)); }
+
+int oracle_abi_version(void) { return 1; }
+
+/*
+ * Head-wise forward (FlashRNN usage example layouts; 5.3 LSTM cell equations).
+ *   Wx      [B,T,G,N,D]   already-projected inputs
+ *   R       [G,N,D,D]     recurrent matrices, pre[g][e] += h[d] * R[g,n,d,e]
+ *   b       [G,N,D]       bias, added every step
+ *   states0 [S,B,1,N,D]   initial (h, c) or NULL for zeros
+ *   states  [S,B,T,N,D]   state after consuming Wx[:,t] (NULL: not written)
+ *   last    [S,B,1,N,D]   state after the last step (T == 0: the initial state); NULL: not written
+ *   pairs   list of flattened (b*N + n) indices to compute, or NULL for all B*N
+ * Returns 0, or -1 on bad arguments / allocation failure.
+ */
+int oracle_headwise_fwd(int cell, long B, long T, long N, long D, const double* Wx, const double* R,
+                        const double* b, const double* states0, double* states, double* last,
+                        const long* pairs, long npairs) {
+  if (cell != ORACLE_CELL_LSTM && cell != ORACLE_CELL_ELMAN) return -1;
+  if (B <= 0 || N <= 0 || D <= 0 || T < 0) return -1;
+  const long G = (cell == ORACLE_CELL_LSTM) ? 4 : 1;
+  const long S = (cell == ORACLE_CELL_LSTM) ? 2 : 1;
+  const long count = pairs ? npairs : B * N;
+  int failed = 0;
+
+#pragma omp parallel for schedule(dynamic, 1)
+  for (long p = 0; p < count; ++p) {
+    const long bn = pairs ? pairs[p] : p;
+    if (bn < 0 || bn >= B * N) { failed = 1; continue; }
+    const long bi = bn / N, n = bn % N;
+    double* h = (double*)malloc(sizeof(double) * D);
+    double* c = (double*)malloc(sizeof(double) * D);
+    double* hn = (double*)malloc(sizeof(double) * D);
+    double* acc = (double*)malloc(sizeof(double) * G * D);
+    double* pre = (double*)malloc(sizeof(double) * G * D);
+    if (!h || !c || !hn || !acc || !pre) {
+      failed = 1;
+      free(h); free(c); free(hn); free(acc); free(pre);
+      continue;
+    }
+    /* initial state: states0[s, bi, 0, n, :] or zeros */
+    for (long e = 0; e < D; ++e) {
+      h[e] = states0 ? states0[((0 * B + bi) * N + n) * D + e] : 0.0;
+      c[e] = (S == 2 && states0) ? states0[((1 * B + bi) * N + n) * D + e] : 0.0;
+    }
+    for (long t = 0; t < T; ++t) {
+      /* recurrent contraction with the previous step's full h (synchronous update) */
+      for (long g = 0; g < G; ++g) {
+        double* a = acc + g * D;
+        for (long e = 0; e < D; ++e) a[e] = 0.0;
+        for (long d = 0; d < D; ++d) {
+          const double hd = h[d];
+          const double* row = R + ((g * N + n) * D + d) * D;
+          for (long e = 0; e < D; ++e) a[e] += hd * row[e];
+        }
+        /* pre-activation = Wx + R.h + b, in the order the equation is written */
+        for (long e = 0; e < D; ++e)
+          pre[g * D + e] = Wx[(((bi * T + t) * G + g) * N + n) * D + e] + a[e] + b[(g * N + n) * D + e];
+      }
+      if (cell == ORACLE_CELL_LSTM) {
+        for (long e = 0; e < D; ++e) {
+          const double ig = sigmoid(pre[0 * D + e]);
+          const double fg = sigmoid(pre[1 * D + e]);
+          const double zg = tanh(pre[2 * D + e]);
+          const double og = sigmoid(pre[3 * D + e]);
+          c[e] = fg * c[e] + ig * zg;
+          hn[e] = og * tanh(c[e]);
+        }
+      } else {
+        for (long e = 0; e < D; ++e) hn[e] = tanh(pre[e]);
+      }
+      memcpy(h, hn, sizeof(double) * D);
+      if (states) {
+        for (long e = 0; e < D; ++e) {
+          states[(((0 * B + bi) * T + t) * N + n) * D + e] = h[e];
+          if (S == 2) states[(((1 * B + bi) * T + t) * N + n) * D + e] = c[e];
+        }
+      }
+    }
+    if (last) {
+      for (long e = 0; e < D; ++e) {
+        last[((0 * B + bi) * N + n) * D + e] = h[e];
+        if (S == 2) last[((1 * B + bi) * N + n) * D + e] = c[e];
+      }
+    }
+    free(h); free(c); free(hn); free(acc); free(pre);
+  }
+  return failed ? -1 : 0;
+}
+
+/*
+ * Plain multi-layer LSTM, 5.3 LSTM (MyLSTM.set_weights / MyLSTM.forward), unidirectional:
+ *   x   [T,B,I] input sequence
+ *   Wi[l] [in_l, 4H]  (in_0 = I, in_l = H for l >= 1); Wh[l] [H, 4H]
+ *   b_ih[l], b_hh[l] [4H]; the bias used is their sum (set_weights)
+ *   h0, c0 [L,B,H] or NULL for zeros
+ *   out [T,B,H] top layer's h at every step; hn, cn [L,B,H] final states (NULL: not written)
+ * The time loop is outermost and the layers run inside it, as the page writes it. Rows of the
+ * batch are independent and run in parallel.
+ */
+int oracle_lstm_stack_p3(long L, long T, long B, long I, long H, const double* x,
+                         const double* const* Wi, const double* const* Wh, const double* const* b_ih,
+                         const double* const* b_hh, const double* h0, const double* c0, double* out,
+                         double* hn, double* cn) {
+  if (L <= 0 || B <= 0 || I <= 0 || H <= 0 || T < 0) return -1;
+  const long H4 = 4 * H;
+  int failed = 0;
+  /* set_weights: bias = bias_ih + bias_hh */
+  double* bias = (double*)malloc(sizeof(double) * L * H4);
+  if (!bias) return -1;
+  for (long l = 0; l < L; ++l)
+    for (long j = 0; j < H4; ++j) bias[l * H4 + j] = b_ih[l][j] + b_hh[l][j];
+
+#pragma omp parallel for schedule(dynamic, 1)
+  for (long bi = 0; bi < B; ++bi) {
+    double* h = (double*)malloc(sizeof(double) * L * H);
+    double* c = (double*)malloc(sizeof(double) * L * H);
+    double* xi = (double*)malloc(sizeof(double) * H4);
+    double* hh = (double*)malloc(sizeof(double) * H4);
+    double* ifgo = (double*)malloc(sizeof(double) * H4);
+    if (!h || !c || !xi || !hh || !ifgo) {
+      failed = 1;
+      free(h); free(c); free(xi); free(hh); free(ifgo);
+      continue;
+    }
+    for (long l = 0; l < L; ++l)
+      for (long e = 0; e < H; ++e) {
+        h[l * H + e] = h0 ? h0[(l * B + bi) * H + e] : 0.0;
+        c[l * H + e] = c0 ? c0[(l * B + bi) * H + e] : 0.0;
+      }
+    for (long t = 0; t < T; ++t) {
+      for (long l = 0; l < L; ++l) {
+        /* layer input: x[t] for layer 0, the new h of layer l-1 otherwise */
+        const double* in = (l == 0) ? x + (t * B + bi) * I : h + (l - 1) * H;
+        const long K = (l == 0) ? I : H;
+        for (long j = 0; j < H4; ++j) { xi[j] = 0.0; hh[j] = 0.0; }
+        for (long k = 0; k < K; ++k) {
+          const double v = in[k];
+          const double* row = Wi[l] + k * H4;
+          for (long j = 0; j < H4; ++j) xi[j] += v * row[j];
+        }
+        for (long k = 0; k < H; ++k) {
+          const double v = h[l * H + k];
+          const double* row = Wh[l] + k * H4;
+          for (long j = 0; j < H4; ++j) hh[j] += v * row[j];
+        }
+        for (long j = 0; j < H4; ++j) ifgo[j] = xi[j] + hh[j] + bias[l * H4 + j];
+        for (long e = 0; e < H; ++e) {
+          const double ig = sigmoid(ifgo[0 * H + e]);
+          const double fg = sigmoid(ifgo[1 * H + e]);
+          const double gg = tanh(ifgo[2 * H + e]);
+          const double og = sigmoid(ifgo[3 * H + e]);
+          c[l * H + e] = fg * c[l * H + e] + ig * gg;
+          h[l * H + e] = og * tanh(c[l * H + e]);
+        }
+      }
+      if (out)
+        for (long e = 0; e < H; ++e) out[(t * B + bi) * H + e] = h[(L - 1) * H + e];
+    }
+    for (long l = 0; l < L; ++l)
+      for (long e = 0; e < H; ++e) {
+        if (hn) hn[(l * B + bi) * H + e] = h[l * H + e];
+        if (cn) cn[(l * B + bi) * H + e] = c[l * H + e];
+      }
+    free(h); free(c); free(xi); free(hh); free(ifgo);
+  }
+  free(bias);
+  return failed ? -1 : 0;
+}

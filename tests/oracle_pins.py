@@ -1,0 +1,378 @@
+"""Pins of the fp64 oracle to facts that do not come from the oracle itself.
+
+Every pin takes an ``oracle.Oracle`` and raises AssertionError when the oracle disagrees. The same
+pins run against the real oracle (tests/test_oracle_pins.py) and against deliberately broken copies
+of its C source (tests/test_oracle_mutants.py), which must each fail at least one pin.
+
+Kinds of pin:
+* golden fixtures (tests/golden/*.txt): closed forms and hand-stepped scalar recurrences evaluated
+  with 50-digit decimals, independent of the oracle's code;
+* closed forms evaluated here with numpy (R = 0 geometric gating; saturated forget gate);
+* library special cases: torch.nn.LSTM / torch.nn.RNN in float64 (the "5.3 LSTM" page builds its
+  weights from exactly that module's state_dict names);
+* invariants: heads independent (= one wide head with block-diagonal R), batch permutation,
+  continuation through last_states, T = 0, state bounds, row subsets;
+* two formulations: the page's time-major multi-layer loop against a layer-major composition of
+  head-wise runs.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+
+from golden_io import load
+
+ATOL_GOLD = 5e-15
+
+
+def _sig(x):
+    return 1.0 / (1.0 + np.exp(-x))
+
+
+# ----------------------------------------------------------------------------- golden fixtures
+def pin_golden_pre_0010(orc):
+    """R = 0, pre = (0, 0, 1, 0): c_t = tanh(1)(1 - 2^-t), h_t = tanh(c_t)/2."""
+    g = load("lstm_r0_pre_0010.txt")
+    T = len(g["c"])
+    Wx = np.zeros((1, T, 4, 1, 1))
+    Wx[0, :, 2, 0, 0] = 1.0
+    st, last = orc.headwise_fwd("lstm", Wx, np.zeros((4, 1, 1, 1)), np.zeros((4, 1, 1)))
+    np.testing.assert_allclose(st[0, 0, :, 0, 0], g["h"], rtol=0, atol=ATOL_GOLD)
+    np.testing.assert_allclose(st[1, 0, :, 0, 0], g["c"], rtol=0, atol=ATOL_GOLD)
+    np.testing.assert_allclose(last[:, 0, 0, 0, 0], [g["h"][-1], g["c"][-1]], rtol=0, atol=ATOL_GOLD)
+
+
+def pin_golden_general_const(orc):
+    """R = 0, constant Wx and b split, nonzero c0 and h0: geometric closed form."""
+    g = load("lstm_r0_general.txt")
+    T = len(g["c"])
+    Wx = np.zeros((1, T, 4, 1, 1))
+    for k in range(4):
+        Wx[0, :, k, 0, 0] = g["wx"][k]
+    b = np.array(g["b"]).reshape(4, 1, 1)
+    s0 = np.zeros((2, 1, 1, 1, 1))
+    s0[0] = 0.3  # h0 is irrelevant when R = 0
+    s0[1] = g["c0"][0]
+    st, _ = orc.headwise_fwd("lstm", Wx, np.zeros((4, 1, 1, 1)), b, s0)
+    np.testing.assert_allclose(st[1, 0, :, 0, 0], g["c"], rtol=0, atol=ATOL_GOLD)
+    np.testing.assert_allclose(st[0, 0, :, 0, 0], g["h"], rtol=0, atol=ATOL_GOLD)
+
+
+def pin_golden_elman_scalar(orc):
+    """Elman D = 1: h_t = tanh(1 + 0.5 h_{t-1}), hand-stepped at 50 digits."""
+    g = load("elman_scalar.txt")
+    T = len(g["h"])
+    Wx = np.ones((1, T, 1, 1, 1))
+    R = np.full((1, 1, 1, 1), 0.5)
+    st, last = orc.headwise_fwd("elman", Wx, R, np.zeros((1, 1, 1)))
+    np.testing.assert_allclose(st[0, 0, :, 0, 0], g["h"], rtol=0, atol=ATOL_GOLD)
+    assert last.shape == (1, 1, 1, 1, 1)
+
+
+def _tiny():
+    g = load("lstm_tiny_d2_t4.txt")
+    Wh = np.array(g["wh"]).reshape(2, 8)
+    bias = np.array(g["bias"])
+    xw = np.array(g["xw"]).reshape(4, 8)
+    h = np.array(g["h"]).reshape(4, 2)
+    c = np.array(g["c"]).reshape(4, 2)
+    return g, Wh, bias, xw, h, c
+
+
+def pin_golden_tiny_headwise(orc):
+    """D = 2, T = 4 hand-stepped dense-form LSTM, mapped onto the head-wise layouts."""
+    g, Wh, bias, xw, h, c = _tiny()
+    Wx = np.zeros((1, 4, 4, 1, 2))
+    R = np.zeros((4, 1, 2, 2))
+    b = np.zeros((4, 1, 2))
+    for gate in range(4):
+        Wx[0, :, gate, 0, :] = xw[:, gate * 2:(gate + 1) * 2]
+        R[gate, 0] = Wh[:, gate * 2:(gate + 1) * 2]
+        b[gate, 0] = bias[gate * 2:(gate + 1) * 2]
+    s0 = np.zeros((2, 1, 1, 1, 2))
+    s0[0, 0, 0, 0] = g["h0"]
+    s0[1, 0, 0, 0] = g["c0"]
+    st, _ = orc.headwise_fwd("lstm", Wx, R, b, s0)
+    np.testing.assert_allclose(st[0, 0, :, 0, :], h, rtol=0, atol=ATOL_GOLD)
+    np.testing.assert_allclose(st[1, 0, :, 0, :], c, rtol=0, atol=ATOL_GOLD)
+
+
+def pin_golden_tiny_stack(orc):
+    """The same hand-stepped case through the page's dense multi-layer loop (Wi = identity)."""
+    g, Wh, bias, xw, h, c = _tiny()
+    x = xw.reshape(4, 1, 8)
+    out, hn, cn = orc.lstm_stack_p3(x, [np.eye(8)], [Wh], [bias], [np.zeros(8)],
+                                    np.array(g["h0"]).reshape(1, 1, 2), np.array(g["c0"]).reshape(1, 1, 2))
+    np.testing.assert_allclose(out[:, 0, :], h, rtol=0, atol=ATOL_GOLD)
+    np.testing.assert_allclose(cn[0, 0], c[-1], rtol=0, atol=ATOL_GOLD)
+    np.testing.assert_allclose(hn[0, 0], h[-1], rtol=0, atol=ATOL_GOLD)
+
+
+# ----------------------------------------------------------------------------- closed forms
+def pin_closed_form_random_const(orc):
+    """R = 0 and Wx constant over t: per unit c_t = f^t c0 + i z (1 - f^t)/(1 - f)."""
+    rng = np.random.default_rng(11)
+    B, T, N, D = 2, 30, 2, 8
+    wx = rng.normal(size=(B, 1, 4, N, D))
+    Wx = np.repeat(wx, T, axis=1)
+    b = rng.normal(size=(4, N, D)) * 0.5
+    s0 = rng.normal(size=(2, B, 1, N, D))
+    st, _ = orc.headwise_fwd("lstm", Wx, np.zeros((4, N, D, D)), b, s0)
+    pre = wx[:, 0] + b[None]  # [B,4,N,D]
+    i, f, z, o = _sig(pre[:, 0]), _sig(pre[:, 1]), np.tanh(pre[:, 2]), _sig(pre[:, 3])
+    for t in range(1, T + 1):
+        ft = f ** t
+        ct = ft * s0[1, :, 0] + i * z * (1 - ft) / (1 - f)
+        np.testing.assert_allclose(st[1, :, t - 1], ct, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(st[0, :, t - 1], o * np.tanh(ct), rtol=0, atol=1e-12)
+
+
+def pin_saturated_forget(orc):
+    """b_f = +40, b_i = -40 (f rounds to 1, i ~ 4e-18): c stays c0, and with R[o] = 0,
+    h_t = sigmoid(Wx_o[t] + b_o) tanh(c0)."""
+    rng = np.random.default_rng(12)
+    B, T, N, D = 3, 25, 2, 6
+    Wx = rng.normal(size=(B, T, 4, N, D))
+    Wx[:, :, 0:2] = 0.0
+    R = rng.normal(size=(4, N, D, D)) * (0.5 / math.sqrt(D))
+    R[3] = 0.0
+    b = rng.normal(size=(4, N, D)) * 0.3
+    b[0] = -40.0
+    b[1] = 40.0
+    s0 = rng.normal(size=(2, B, 1, N, D))
+    st, _ = orc.headwise_fwd("lstm", Wx, R, b, s0)
+    c0 = s0[1, :, 0]
+    for t in range(T):
+        np.testing.assert_allclose(st[1, :, t], c0, rtol=0, atol=(t + 1) * 1e-16 + 1e-15)
+        h_exp = _sig(Wx[:, t, 3] + b[3][None]) * np.tanh(c0)
+        np.testing.assert_allclose(st[0, :, t], h_exp, rtol=0, atol=1e-14)
+
+
+def pin_elman_r0(orc):
+    """Elman with R = 0 is the elementwise map h_t = tanh(Wx_t + b)."""
+    rng = np.random.default_rng(13)
+    B, T, N, D = 2, 9, 3, 5
+    Wx = rng.normal(size=(B, T, 1, N, D))
+    b = rng.normal(size=(1, N, D))
+    st, _ = orc.headwise_fwd("elman", Wx, np.zeros((1, N, D, D)), b)
+    np.testing.assert_allclose(st[0], np.tanh(Wx[:, :, 0] + b[0][None, None]), rtol=0, atol=1e-15)
+
+
+# ----------------------------------------------------------------------------- library cases
+def _torch_lstm(I, H, layers, seed):
+    torch.manual_seed(seed)
+    m = torch.nn.LSTM(I, H, num_layers=layers, dtype=torch.float64)
+    return m
+
+
+def pin_torch_lstm_stack(orc):
+    """The page's MyLSTM reads weight_ih_l{k}.T, weight_hh_l{k}.T, bias_ih + bias_hh from a
+    torch.nn.LSTM state_dict; in float64 the two must agree."""
+    T, B, I, H, L = 7, 3, 5, 4, 2
+    m = _torch_lstm(I, H, L, 21)
+    rng = np.random.default_rng(21)
+    x = rng.normal(size=(T, B, I))
+    h0 = rng.normal(size=(L, B, H))
+    c0 = rng.normal(size=(L, B, H))
+    with torch.no_grad():
+        ref, (rh, rc) = m(torch.from_numpy(x), (torch.from_numpy(h0), torch.from_numpy(c0)))
+    sd = m.state_dict()
+    Wi = [sd[f"weight_ih_l{l}"].numpy().T for l in range(L)]
+    Wh = [sd[f"weight_hh_l{l}"].numpy().T for l in range(L)]
+    bi = [sd[f"bias_ih_l{l}"].numpy() for l in range(L)]
+    bh = [sd[f"bias_hh_l{l}"].numpy() for l in range(L)]
+    out, hn, cn = orc.lstm_stack_p3(x, Wi, Wh, bi, bh, h0, c0)
+    np.testing.assert_allclose(out, ref.numpy(), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(hn, rh.numpy(), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(cn, rc.numpy(), rtol=0, atol=1e-12)
+
+
+def pin_torch_lstm_headwise(orc):
+    """N independent torch.nn.LSTM layers (one per head) equal one head-wise run with
+    Wx[b,t,g,n,:] = (x_n W_ih^T)[b, gH:(g+1)H], R[g,n,d,e] = W_hh[gH+e, d], b = b_ih + b_hh."""
+    T, B, I, H, N = 6, 3, 4, 5, 3
+    rng = np.random.default_rng(22)
+    Wx = np.zeros((B, T, 4, N, H))
+    R = np.zeros((4, N, H, H))
+    b = np.zeros((4, N, H))
+    s0 = rng.normal(size=(2, B, 1, N, H))
+    refs_h, refs_c = [], []
+    for n in range(N):
+        m = _torch_lstm(I, H, 1, 100 + n)
+        sd = m.state_dict()
+        x = rng.normal(size=(T, B, I))
+        with torch.no_grad():
+            ref, (rh, rc) = m(torch.from_numpy(x), (torch.from_numpy(s0[0, :, 0, n][None].copy()),
+                                                   torch.from_numpy(s0[1, :, 0, n][None].copy())))
+        proj = x @ sd["weight_ih_l0"].numpy().T  # [T,B,4H]
+        whh = sd["weight_hh_l0"].numpy()
+        bias = sd["bias_ih_l0"].numpy() + sd["bias_hh_l0"].numpy()
+        for g in range(4):
+            Wx[:, :, g, n, :] = proj[:, :, g * H:(g + 1) * H].transpose(1, 0, 2)
+            R[g, n] = whh[g * H:(g + 1) * H, :].T
+            b[g, n] = bias[g * H:(g + 1) * H]
+        refs_h.append(ref.numpy())
+        refs_c.append(rc.numpy()[0])
+    st, last = orc.headwise_fwd("lstm", Wx, R, b, s0)
+    for n in range(N):
+        np.testing.assert_allclose(st[0, :, :, n].transpose(1, 0, 2), refs_h[n], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(last[1, :, 0, n], refs_c[n], rtol=0, atol=1e-12)
+
+
+def pin_torch_rnn_elman(orc):
+    """Elman heads equal torch.nn.RNN(nonlinearity='tanh') layers in float64."""
+    T, B, I, H, N = 8, 2, 3, 4, 2
+    rng = np.random.default_rng(23)
+    Wx = np.zeros((B, T, 1, N, H))
+    R = np.zeros((1, N, H, H))
+    b = np.zeros((1, N, H))
+    s0 = rng.normal(size=(1, B, 1, N, H))
+    refs = []
+    for n in range(N):
+        torch.manual_seed(200 + n)
+        m = torch.nn.RNN(I, H, nonlinearity="tanh", dtype=torch.float64)
+        sd = m.state_dict()
+        x = rng.normal(size=(T, B, I))
+        with torch.no_grad():
+            ref, _ = m(torch.from_numpy(x), torch.from_numpy(s0[0, :, 0, n][None].copy()))
+        Wx[:, :, 0, n, :] = (x @ sd["weight_ih_l0"].numpy().T).transpose(1, 0, 2)
+        R[0, n] = sd["weight_hh_l0"].numpy().T
+        b[0, n] = sd["bias_ih_l0"].numpy() + sd["bias_hh_l0"].numpy()
+        refs.append(ref.numpy())
+    st, _ = orc.headwise_fwd("elman", Wx, R, b, s0)
+    for n in range(N):
+        np.testing.assert_allclose(st[0, :, :, n].transpose(1, 0, 2), refs[n], rtol=0, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------- invariants
+def _rand_problem(cell, B, T, N, D, seed, with_s0=True):
+    rng = np.random.default_rng(seed)
+    G, S = (4, 2) if cell == "lstm" else (1, 1)
+    Wx = rng.normal(size=(B, T, G, N, D))
+    R = rng.normal(size=(G, N, D, D)) / math.sqrt(D)
+    b = rng.normal(size=(G, N, D)) * 0.3
+    s0 = rng.normal(size=(S, B, 1, N, D)) if with_s0 else None
+    return Wx, R, b, s0
+
+
+def pin_heads_blockdiag(orc):
+    """N heads of width D == one head of width N*D whose R is block-diagonal."""
+    for cell in ("lstm", "elman"):
+        B, T, N, D = 2, 6, 3, 4
+        Wx, R, b, s0 = _rand_problem(cell, B, T, N, D, 31)
+        G = Wx.shape[2]
+        Wx1 = Wx.reshape(B, T, G, 1, N * D)
+        R1 = np.zeros((G, 1, N * D, N * D))
+        for n in range(N):
+            R1[:, 0, n * D:(n + 1) * D, n * D:(n + 1) * D] = R[:, n]
+        st, last = orc.headwise_fwd(cell, Wx, R, b, s0)
+        st1, last1 = orc.headwise_fwd(cell, Wx1, R1, b.reshape(G, 1, N * D),
+                                      s0.reshape(s0.shape[0], B, 1, 1, N * D))
+        np.testing.assert_allclose(st1.reshape(st.shape), st, rtol=0, atol=1e-14)
+        np.testing.assert_allclose(last1.reshape(last.shape), last, rtol=0, atol=1e-14)
+
+
+def pin_heads_separate(orc):
+    """An N-head run equals N separate one-head runs."""
+    B, T, N, D = 2, 5, 3, 4
+    Wx, R, b, s0 = _rand_problem("lstm", B, T, N, D, 32)
+    st, _ = orc.headwise_fwd("lstm", Wx, R, b, s0)
+    for n in range(N):
+        stn, _ = orc.headwise_fwd("lstm", Wx[:, :, :, n:n + 1], R[:, n:n + 1], b[:, n:n + 1],
+                                  s0[:, :, :, n:n + 1])
+        np.testing.assert_array_equal(stn[:, :, :, 0], st[:, :, :, n])
+
+
+def pin_batch_permutation(orc):
+    """Permuting batch rows permutes the outputs (rows never interact)."""
+    B, T, N, D = 5, 6, 2, 4
+    Wx, R, b, s0 = _rand_problem("lstm", B, T, N, D, 33)
+    perm = np.array([3, 0, 4, 1, 2])
+    st, last = orc.headwise_fwd("lstm", Wx, R, b, s0)
+    stp, lastp = orc.headwise_fwd("lstm", Wx[perm], R, b, s0[:, perm])
+    np.testing.assert_array_equal(stp, st[:, perm])
+    np.testing.assert_array_equal(lastp, last[:, perm])
+
+
+def pin_continuation(orc):
+    """Feeding last_states back as the initial state continues the sequence exactly."""
+    for cell in ("lstm", "elman"):
+        B, T, N, D = 2, 16, 2, 4
+        Wx, R, b, s0 = _rand_problem(cell, B, T, N, D, 34)
+        st, last = orc.headwise_fwd(cell, Wx, R, b, s0)
+        st1, last1 = orc.headwise_fwd(cell, Wx[:, :7], R, b, s0)
+        st2, last2 = orc.headwise_fwd(cell, Wx[:, 7:], R, b, last1)
+        np.testing.assert_array_equal(np.concatenate([st1, st2], axis=2), st)
+        np.testing.assert_array_equal(last2, last)
+        np.testing.assert_array_equal(last, st[:, :, -1:])
+
+
+def pin_t0(orc):
+    """T = 0: last_states is the initial state (zeros when none is given)."""
+    B, N, D = 2, 2, 3
+    Wx, R, b, s0 = _rand_problem("lstm", B, 0, N, D, 35)
+    st, last = orc.headwise_fwd("lstm", Wx, R, b, s0)
+    assert st.shape == (2, B, 0, N, D)
+    np.testing.assert_array_equal(last, s0)
+    _, last0 = orc.headwise_fwd("lstm", Wx, R, b, None)
+    np.testing.assert_array_equal(last0, np.zeros_like(s0))
+
+
+def pin_bounds(orc):
+    """|h| <= 1 always; |c_t| <= |c0| + t (|i z| <= 1, 0 <= f <= 1)."""
+    B, T, N, D = 3, 40, 2, 8
+    Wx, R, b, s0 = _rand_problem("lstm", B, T, N, D, 36)
+    Wx *= 5.0
+    R *= 3.0
+    st, _ = orc.headwise_fwd("lstm", Wx, R, b, s0)
+    assert np.all(np.abs(st[0]) <= 1.0)
+    for t in range(T):
+        assert np.all(np.abs(st[1, :, t]) <= np.abs(s0[1, :, 0]) + (t + 1) + 1e-12)
+    We, Re, be, se = _rand_problem("elman", B, T, N, D, 37)
+    ste, _ = orc.headwise_fwd("elman", We * 5.0, Re * 3.0, be, se)
+    assert np.all(np.abs(ste) <= 1.0)
+
+
+def pin_pairs_subset(orc):
+    """Computing a subset of (batch, head) rows gives exactly those rows of the full run."""
+    B, T, N, D = 3, 5, 2, 4
+    Wx, R, b, s0 = _rand_problem("lstm", B, T, N, D, 38)
+    st, last = orc.headwise_fwd("lstm", Wx, R, b, s0)
+    pairs = [5, 1, 2]
+    sts, lasts = orc.headwise_fwd("lstm", Wx, R, b, s0, pairs=pairs)
+    for p in pairs:
+        bi, n = divmod(p, N)
+        np.testing.assert_array_equal(sts[:, bi, :, n], st[:, bi, :, n])
+        np.testing.assert_array_equal(lasts[:, bi, :, n], last[:, bi, :, n])
+
+
+def pin_layer_major(orc):
+    """The page's time-major multi-layer loop equals layer-major head-wise runs (projection of
+    each layer's whole input sequence first, then its recurrence)."""
+    T, B, I, H, L = 9, 3, 5, 4, 2
+    rng = np.random.default_rng(39)
+    x = rng.normal(size=(T, B, I))
+    Wi = [rng.normal(size=(I, 4 * H)) * 0.4, rng.normal(size=(H, 4 * H)) * 0.4]
+    Wh = [rng.normal(size=(H, 4 * H)) * 0.4 for _ in range(L)]
+    bi = [rng.normal(size=4 * H) * 0.2 for _ in range(L)]
+    bh = [rng.normal(size=4 * H) * 0.2 for _ in range(L)]
+    h0 = rng.normal(size=(L, B, H))
+    c0 = rng.normal(size=(L, B, H))
+    out, hn, cn = orc.lstm_stack_p3(x, Wi, Wh, bi, bh, h0, c0)
+    inp = x
+    for l in range(L):
+        proj = inp @ Wi[l]  # [T,B,4H]
+        Wx = proj.reshape(T, B, 4, 1, H).transpose(1, 0, 2, 3, 4)
+        R = Wh[l].reshape(H, 4, H).transpose(1, 0, 2)[:, None]  # R[g,0,d,e] = Wh[d, gH+e]
+        b = (bi[l] + bh[l]).reshape(4, 1, H)
+        s0 = np.stack([h0[l], c0[l]])[:, :, None, None, :]
+        st, last = orc.headwise_fwd("lstm", Wx, R, b, s0)
+        inp = st[0, :, :, 0].transpose(1, 0, 2)
+        np.testing.assert_allclose(last[0, :, 0, 0], hn[l], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(last[1, :, 0, 0], cn[l], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(inp, out, rtol=0, atol=1e-12)
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -1,0 +1,58 @@
+"""Plausible mistakes planted in copies of the oracle's C source must each fail at least one pin.
+
+This shows the pins are sharp enough to catch a dropped term, a wrong sign, a wrong index or a
+transposed operand. The mutants are compiled on the CPU into a temporary folder; the real oracle
+is untouched."""
+import os
+import subprocess
+
+import pytest
+
+import oracle
+from oracle_pins import ALL_PINS
+
+SRC = open(oracle.SOURCE).read()
+
+MUTANTS = {
+    "sigmoid_sign": ("return 1.0 / (1.0 + exp(-x));", "return 1.0 / (1.0 + exp(x));"),
+    "swap_i_f": ("const double ig = sigmoid(pre[0 * D + e]);", "const double ig = sigmoid(pre[1 * D + e]);"),
+    "z_sigmoid": ("const double zg = tanh(pre[2 * D + e]);", "const double zg = sigmoid(pre[2 * D + e]);"),
+    "R_transposed": ("for (long e = 0; e < D; ++e) a[e] += hd * row[e];",
+                     "for (long e = 0; e < D; ++e) a[e] += hd * R[((g * N + n) * D + e) * D + d];"),
+    "drop_bias": (" + a[e] + b[(g * N + n) * D + e];", " + a[e];"),
+    "drop_Wx": ("Wx[(((bi * T + t) * G + g) * N + n) * D + e] + a[e]",
+                "0.0 * Wx[(((bi * T + t) * G + g) * N + n) * D + e] + a[e]"),
+    "wx_head0": ("Wx[(((bi * T + t) * G + g) * N + n) * D + e]", "Wx[(((bi * T + t) * G + g) * N + 0) * D + e]"),
+    "c_uses_o": ("c[e] = fg * c[e] + ig * zg;", "c[e] = fg * c[e] + ig * og;"),
+    "h_no_tanh": ("hn[e] = og * tanh(c[e]);", "hn[e] = og * c[e];"),
+    "c0_ignored": ("c[e] = (S == 2 && states0) ? states0[((1 * B + bi) * N + n) * D + e] : 0.0;", "c[e] = 0.0;"),
+    "h0_ignored": ("h[e] = states0 ? states0[((0 * B + bi) * N + n) * D + e] : 0.0;", "h[e] = 0.0;"),
+    "states_time_reversed": ("states[(((0 * B + bi) * T + t) * N + n) * D + e] = h[e];",
+                             "states[(((0 * B + bi) * T + (T - 1 - t)) * N + n) * D + e] = h[e];"),
+    "elman_identity": ("for (long e = 0; e < D; ++e) hn[e] = tanh(pre[e]);",
+                       "for (long e = 0; e < D; ++e) hn[e] = pre[e] / (1.0 + fabs(pre[e]));"),
+    "async_update": ("memcpy(h, hn, sizeof(double) * D);", "memcpy(h, hn, sizeof(double) * D); h[0] = c[0];"),
+    "stack_bias_hh_dropped": ("bias[l * H4 + j] = b_ih[l][j] + b_hh[l][j];", "bias[l * H4 + j] = b_ih[l][j];"),
+    "stack_layer_input": ("const double* in = (l == 0) ? x + (t * B + bi) * I : h + (l - 1) * H;",
+                          "const double* in = (l == 0) ? x + (t * B + bi) * I : h + l * H;"),
+    "stack_wh_layer0": ("const double* row = Wh[l] + k * H4;", "const double* row = Wh[0] + k * H4;"),
+    "stack_gate_blocks": ("const double gg = tanh(ifgo[2 * H + e]);", "const double gg = tanh(ifgo[3 * H + e]);"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmp_path):
+    old, new = MUTANTS[name]
+    assert SRC.count(old) >= 1, f"mutation anchor for {name} not found in the oracle source"
+    src = tmp_path / f"oracle_{name}.c"
+    src.write_text(SRC.replace(old, new))
+    lib = str(tmp_path / f"liboracle_{name}.so")
+    oracle.build(source=str(src), out=lib)
+    mutant = oracle.Oracle(lib)
+    failures = []
+    for pin in ALL_PINS:
+        try:
+            pin(mutant)
+        except (AssertionError, RuntimeError, ValueError) as e:
+            failures.append(pin.__name__)
+    assert failures, f"mutant {name} passed every pin"
