@@ -1,0 +1,178 @@
+#!/usr/bin/env python3
+"""Benchmark of the head-wise LSTM forward recurrence on one MI355X.
+
+A step is one full forward call (all T timesteps of the recurrence) over one batch of synthetic
+inputs already resident in device memory. Default workload: LSTM, bf16 inputs with fp32
+accumulation, B=16, T=1024, N=1 head, D=768 (gates i, f, z, o), fused path.
+
+Prints ONE JSON line: the metric (achieved TFLOP/s of the recurrent contraction, with
+microseconds per timestep beside it), a roofline object for the dominant kernel measured with HIP
+events on the stream the kernel runs on, and the fp64 oracle timed on a bounded sample on the
+host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "LSTM fwd µs/timestep + achieved TFLOP/s (% MFMA bf16 peak), B=16 N=1 D=768"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+
+
+def headwise_flops(w) -> float:
+    """Algorithmic FLOPs of one forward call: the recurrent contraction only, 2*B*N*G*D^2*T."""
+    return 2.0 * w.B * w.N * w.G * w.D * w.D * w.T
+
+
+def headwise_bytes(w, elt: int) -> float:
+    """Algorithmic HBM bytes of one call: Wx, R, b, states0 read once; states written once (fp32)."""
+    rd = (w.B * w.T * w.G * w.N * w.D + w.G * w.N * w.D * w.D + w.G * w.N * w.D) * elt
+    if w.s0_var is not None:
+        rd += w.S * w.B * w.N * w.D * elt
+    wr = w.S * w.B * w.T * w.N * w.D * 4 + w.S * w.B * w.N * w.D * 4
+    return float(rd + wr)
+
+
+def cpu_baseline(w, sample_T: int):
+    """The oracle as it stands, on all (batch, head) rows for the first sample_T steps."""
+    import numpy as np
+
+    import frnn_inputs as fi
+    import oracle
+
+    x = fi.make_inputs(w)
+    Wx = fi.to_f64(x["Wx"])[:, :sample_T]
+    args = (Wx, fi.to_f64(x["R"]), fi.to_f64(x["b"]), fi.to_f64(x["states0"]))
+    oracle.headwise_fwd(w.cell, Wx[:, :2], *args[1:])  # warm (loads the library)
+    t0 = time.perf_counter()
+    oracle.headwise_fwd(w.cell, *args)
+    dt = time.perf_counter() - t0
+    flops = 2.0 * w.B * w.N * w.G * w.D * w.D * sample_T
+    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"all {w.B * w.N} (batch, head) rows x first {sample_T} of {w.T} timesteps, fp64, "
+                      f"{dt:.2f} s wall",
+            "us_per_timestep": dt / sample_T * 1e6}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="lstm_bf16_B16_T1024_N1_D768")
+    ap.add_argument("--path", default="fused", choices=["fused", "alternating"])
+    ap.add_argument("--cpu-sample-T", type=int, default=128)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
+                    help="per-launch HBM bytes measured with rocprofv3 counters for this workload/path")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: the recurrence is built for a single MI355X and this "
+              f"build has no multi-GPU path (asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import frnn_inputs as fi
+    import head_wise_lstm_amd as hw
+
+    if not os.path.exists(hw.lib_path()):
+        from head_wise_lstm_amd import build as hb
+        hb.build(verbose=False)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    w = fi.WORKLOADS[args.workload]
+    x = fi.make_inputs(w)
+    g = {k: (v.to(dev) if isinstance(v, torch.Tensor) else ([t.to(dev) for t in v] if isinstance(v, list) else v))
+         for k, v in x.items()}
+    stream = torch.cuda.current_stream(dev)
+
+    if isinstance(w, fi.HeadwiseWorkload):
+        G, S = w.G, w.S
+        desc = hw._desc(w.B, w.T, w.N, w.D, w.cell, w.dtype)
+        ws = torch.empty(hw.frnn_workspace_bytes(desc, args.path), dtype=torch.uint8, device=dev)
+        out = (torch.empty((S, w.B, w.T, w.N, w.D), dtype=torch.float32, device=dev),
+               torch.empty((S, w.B, 1, w.N, w.D), dtype=torch.float32, device=dev))
+        plan = hw.frnn_plan_str(desc, args.path)
+
+        def step():
+            hw.frnn_fwd(g["Wx"], g["R"], g["b"], g["states0"], cell=w.cell, path=args.path, out=out, workspace=ws,
+                        check=False)
+        flops = headwise_flops(w)
+        elt = 2 if w.dtype == torch.bfloat16 else 4
+        nbytes = headwise_bytes(w, elt)
+        timesteps = w.T
+        config = {"workload": w.name, "cell": w.cell, "B": w.B, "T": w.T, "N": w.N, "D": w.D, "G": G,
+                  "in_dtype": str(w.dtype).replace("torch.", ""), "states_dtype": "float32", "path": args.path,
+                  "plan": plan}
+        dtype = "bf16" if w.dtype == torch.bfloat16 else "f32"
+    else:
+        ws = torch.empty(hw.frnn_lstm_stack_workspace_bytes(w.L, w.T, w.B, w.I, w.H, args.path), dtype=torch.uint8,
+                         device=dev)
+        out = (torch.empty((w.T, w.B, w.H), dtype=torch.float32, device=dev),
+               torch.empty((w.L, w.B, w.H), dtype=torch.float32, device=dev),
+               torch.empty((w.L, w.B, w.H), dtype=torch.float32, device=dev))
+
+        def step():
+            hw.frnn_lstm_stack_fwd(g["x"], g["Wi"], g["Wh"], g["b_ih"], g["b_hh"], g["h0"], g["c0"], path=args.path,
+                                   out=out, workspace=ws, check=False)
+        flops = 2.0 * w.B * 4 * w.H * w.H * w.T * w.L  # recurrent contraction of all layers
+        nbytes = 0.0
+        timesteps = w.T * w.L
+        config = {"workload": w.name, "L": w.L, "T": w.T, "B": w.B, "I": w.I, "H": w.H, "path": args.path,
+                  "projection_gflop": 2.0 * w.T * w.B * 4 * w.H * (w.I + w.H * (w.L - 1)) / 1e9}
+        dtype = "bf16"
+
+    for _ in range(args.warmup):
+        step()
+    hw.frnn_check(ws)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    hw.frnn_check(ws)
+    ms = e0.elapsed_time(e1) / args.steps
+    sec = ms / 1e3
+    tflops = flops / sec / 1e12
+    roof = {"bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": tflops / PEAK_BF16_TFLOPS, "traffic": None,
+            "kernel": "frnn::fused_fwd_kernel" if args.path == "fused" else "frnn::alt_gemm_kernel+alt_gate_kernel",
+            "per_launch_flop": flops, "launch_ms": ms}
+    if nbytes:
+        roof["algorithmic_bytes"] = nbytes
+        roof["hbm_frac"] = nbytes / sec / 1e9 / PEAK_HBM_GBS
+    try:
+        with open(args.traffic_json) as f:
+            tj = json.load(f).get(f"{config['workload']}:{args.path}")
+        if tj:
+            roof["traffic"] = tj["bytes_per_launch"]
+    except (OSError, ValueError):
+        pass
+    res = {"metric": METRIC, "value": tflops, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": dtype, "data": "synthetic (seeded, shapes and distributions of the workload)",
+           "config": config, "us_per_timestep": ms * 1e3 / timesteps,
+           "pct_mfma_bf16_peak": 100.0 * tflops / PEAK_BF16_TFLOPS, "wall_s_timed": wall, "roofline": roof}
+    if not args.no_cpu_baseline and isinstance(w, fi.HeadwiseWorkload):
+        res["cpu_baseline"] = cpu_baseline(w, min(args.cpu_sample_T, w.T))
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

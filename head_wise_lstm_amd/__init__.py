@@ -1,0 +1,243 @@
+"""head_wise_lstm_amd -- Python binding of libfrnn, the gfx950 head-wise LSTM / Elman forward
+recurrence library (C ABI in include/frnn.h).
+
+The binding only marshals arguments: it checks tensor shapes and dtypes, allocates the outputs and
+the workspace with torch (device memory is torch's), and passes raw device pointers and torch's
+current stream to the C entry points of the same names. Every step of the computation runs in the
+library's HIP kernels. There is no fallback: if libfrnn.so is missing or no gfx950 device is
+present, the calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import torch
+
+__all__ = [
+    "FRNN_PATH_ALTERNATING", "FRNN_PATH_FUSED", "FrnnError", "Desc", "lib_path", "load",
+    "frnn_abi_version", "frnn_status_str", "frnn_workspace_bytes", "frnn_plan_str", "frnn_fwd",
+    "frnn_check", "frnn_lstm_stack_workspace_bytes", "frnn_lstm_stack_fwd",
+]
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_NAME = "libfrnn.so"
+
+FRNN_OK = 0
+FRNN_CELL_LSTM, FRNN_CELL_ELMAN = 0, 1
+FRNN_F32, FRNN_BF16 = 0, 1
+FRNN_PATH_ALTERNATING, FRNN_PATH_FUSED = 0, 1
+
+_CELLS = {"lstm": FRNN_CELL_LSTM, "elman": FRNN_CELL_ELMAN}
+_PATHS = {"alternating": FRNN_PATH_ALTERNATING, "fused": FRNN_PATH_FUSED}
+_DTYPES = {torch.float32: FRNN_F32, torch.bfloat16: FRNN_BF16}
+
+
+class FrnnError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {frnn_status_str(status)} ({status})")
+
+
+class Desc(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("B", "T", "N", "D", "cell", "in_dtype", "out_dtype", "reserved")]
+
+
+_lib = None
+
+
+def lib_path() -> str:
+    return os.path.join(HERE, _LIB_NAME)
+
+
+def load():
+    """Load libfrnn.so from this package folder (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = lib_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m head_wise_lstm_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, sz, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+    dptr = ctypes.POINTER(Desc)
+    lib.frnn_abi_version.restype = i32
+    lib.frnn_abi_version.argtypes = []
+    lib.frnn_status_str.restype = ctypes.c_char_p
+    lib.frnn_status_str.argtypes = [i32]
+    lib.frnn_workspace_bytes.restype = i32
+    lib.frnn_workspace_bytes.argtypes = [dptr, i32, ctypes.POINTER(sz)]
+    lib.frnn_plan_str.restype = i32
+    lib.frnn_plan_str.argtypes = [dptr, i32, ctypes.c_char_p, sz]
+    lib.frnn_fwd.restype = i32
+    lib.frnn_fwd.argtypes = [dptr, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.frnn_check.restype = i32
+    lib.frnn_check.argtypes = [vp, vp]
+    lib.frnn_lstm_stack_workspace_bytes.restype = i32
+    lib.frnn_lstm_stack_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, ctypes.POINTER(sz)]
+    lib.frnn_lstm_stack_fwd.restype = i32
+    lib.frnn_lstm_stack_fwd.argtypes = [i32, i32, i32, i32, i32, i32, vp, ctypes.POINTER(vp), ctypes.POINTER(vp),
+                                        ctypes.POINTER(vp), ctypes.POINTER(vp), vp, vp, vp, vp, vp, vp, sz, vp]
+    _lib = lib
+    return lib
+
+
+def frnn_abi_version() -> int:
+    return load().frnn_abi_version()
+
+
+def frnn_status_str(status: int) -> str:
+    return load().frnn_status_str(int(status)).decode()
+
+
+def _desc(B, T, N, D, cell, in_dtype, out_dtype=FRNN_F32) -> Desc:
+    return Desc(B, T, N, D, _CELLS[cell] if isinstance(cell, str) else cell,
+                _DTYPES[in_dtype] if isinstance(in_dtype, torch.dtype) else in_dtype, out_dtype, 0)
+
+
+def _path(path) -> int:
+    return _PATHS[path] if isinstance(path, str) else int(path)
+
+
+def frnn_workspace_bytes(desc: Desc, path="fused") -> int:
+    n = ctypes.c_size_t(0)
+    rc = load().frnn_workspace_bytes(ctypes.byref(desc), _path(path), ctypes.byref(n))
+    if rc != FRNN_OK:
+        raise FrnnError(rc, "frnn_workspace_bytes")
+    return n.value
+
+
+def frnn_plan_str(desc: Desc, path="fused") -> str:
+    buf = ctypes.create_string_buffer(1024)
+    rc = load().frnn_plan_str(ctypes.byref(desc), _path(path), buf, 1024)
+    if rc != FRNN_OK:
+        raise FrnnError(rc, "frnn_plan_str")
+    return buf.value.decode()
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream_handle(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def frnn_check(workspace: torch.Tensor, stream=None) -> None:
+    """Wait for the stream, then raise if the device reported an error into the workspace."""
+    st = _stream_handle(workspace.device) if stream is None else ctypes.c_void_p(stream)
+    rc = load().frnn_check(_ptr(workspace), st)
+    if rc != FRNN_OK:
+        raise FrnnError(rc, "frnn_check")
+
+
+def _check_tensor(t, name, shape, dtype, device):
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor) or t.device != device or t.dtype != dtype:
+        raise ValueError(f"{name}: expected a {dtype} tensor on {device}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+
+
+def frnn_fwd(Wx: torch.Tensor, R: torch.Tensor, b: Optional[torch.Tensor] = None,
+             states: Optional[torch.Tensor] = None, cell: str = "lstm", path="fused",
+             out: Optional[Sequence[torch.Tensor]] = None, workspace: Optional[torch.Tensor] = None,
+             check: bool = True):
+    """Head-wise forward: (states [S,B,T,N,D] fp32, last_states [S,B,1,N,D] fp32).
+
+    Wx [B,T,G,N,D], R [G,N,D,D], b [G,N,D] or None, states (initial) [S,B,1,N,D] or None; all of
+    one dtype (float32 or bfloat16) on one device. ``out`` may pass preallocated (states,
+    last_states); ``workspace`` a preallocated uint8 tensor of at least frnn_workspace_bytes().
+    With ``check`` the call waits for the stream and raises on a device-side error.
+    """
+    G, S = (4, 2) if cell == "lstm" else (1, 1)
+    if Wx.dim() != 5:
+        raise ValueError("Wx must be [B,T,G,N,D]")
+    B, T, G_, N, D = Wx.shape
+    dev, dt = Wx.device, Wx.dtype
+    if G_ != G or dt not in _DTYPES:
+        raise ValueError("Wx: wrong gate count or dtype")
+    _check_tensor(Wx, "Wx", (B, T, G, N, D), dt, dev)
+    _check_tensor(R, "R", (G, N, D, D), dt, dev)
+    _check_tensor(b, "b", (G, N, D), dt, dev)
+    _check_tensor(states, "states", (S, B, 1, N, D), dt, dev)
+    desc = _desc(B, T, N, D, cell, dt)
+    p = _path(path)
+    if out is None:
+        st_out = torch.empty((S, B, T, N, D), dtype=torch.float32, device=dev)
+        last = torch.empty((S, B, 1, N, D), dtype=torch.float32, device=dev)
+    else:
+        st_out, last = out
+        _check_tensor(st_out, "out[0]", (S, B, T, N, D), torch.float32, dev)
+        _check_tensor(last, "out[1]", (S, B, 1, N, D), torch.float32, dev)
+    need = frnn_workspace_bytes(desc, p)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    elif workspace.numel() < need or workspace.device != dev:
+        raise ValueError("workspace too small")
+    rc = load().frnn_fwd(ctypes.byref(desc), p, _ptr(Wx), _ptr(R), _ptr(b), _ptr(states), _ptr(st_out),
+                         _ptr(last), _ptr(workspace), workspace.numel(), _stream_handle(dev))
+    if rc != FRNN_OK:
+        raise FrnnError(rc, "frnn_fwd")
+    if check:
+        frnn_check(workspace)
+    return st_out, last
+
+
+def frnn_lstm_stack_workspace_bytes(L, T, B, I, H, path="fused") -> int:
+    n = ctypes.c_size_t(0)
+    rc = load().frnn_lstm_stack_workspace_bytes(L, T, B, I, H, _path(path), ctypes.byref(n))
+    if rc != FRNN_OK:
+        raise FrnnError(rc, "frnn_lstm_stack_workspace_bytes")
+    return n.value
+
+
+def frnn_lstm_stack_fwd(x: torch.Tensor, Wi: Sequence[torch.Tensor], Wh: Sequence[torch.Tensor],
+                        b_ih: Sequence[Optional[torch.Tensor]], b_hh: Sequence[Optional[torch.Tensor]],
+                        h0: Optional[torch.Tensor] = None, c0: Optional[torch.Tensor] = None, path="fused",
+                        out: Optional[Sequence[torch.Tensor]] = None, workspace: Optional[torch.Tensor] = None,
+                        check: bool = True):
+    """Multi-layer LSTM with input projection: (out [T,B,H], hn [L,B,H], cn [L,B,H]), fp32.
+
+    x [T,B,I]; Wi[l] [in,4H]; Wh[l] [H,4H]; b_ih[l], b_hh[l] [4H] or None; h0, c0 [L,B,H] or None;
+    every tensor bfloat16 on one device.
+    """
+    T, B, I = x.shape
+    L = len(Wi)
+    H = Wh[0].shape[0]
+    dev, bf = x.device, torch.bfloat16
+    _check_tensor(x, "x", (T, B, I), bf, dev)
+    for l in range(L):
+        _check_tensor(Wi[l], f"Wi[{l}]", ((I if l == 0 else H), 4 * H), bf, dev)
+        _check_tensor(Wh[l], f"Wh[{l}]", (H, 4 * H), bf, dev)
+        _check_tensor(b_ih[l], f"b_ih[{l}]", (4 * H,), bf, dev)
+        _check_tensor(b_hh[l], f"b_hh[{l}]", (4 * H,), bf, dev)
+    _check_tensor(h0, "h0", (L, B, H), bf, dev)
+    _check_tensor(c0, "c0", (L, B, H), bf, dev)
+    p = _path(path)
+    if out is None:
+        o = torch.empty((T, B, H), dtype=torch.float32, device=dev)
+        hn = torch.empty((L, B, H), dtype=torch.float32, device=dev)
+        cn = torch.empty((L, B, H), dtype=torch.float32, device=dev)
+    else:
+        o, hn, cn = out
+    need = frnn_lstm_stack_workspace_bytes(L, T, B, I, H, p)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    elif workspace.numel() < need:
+        raise ValueError("workspace too small")
+    arr = ctypes.c_void_p * L
+    rc = load().frnn_lstm_stack_fwd(
+        L, T, B, I, H, p, _ptr(x), arr(*[w.data_ptr() for w in Wi]), arr(*[w.data_ptr() for w in Wh]),
+        arr(*[0 if v is None else v.data_ptr() for v in b_ih]), arr(*[0 if v is None else v.data_ptr() for v in b_hh]),
+        _ptr(h0), _ptr(c0), _ptr(o), _ptr(hn), _ptr(cn), _ptr(workspace), workspace.numel(), _stream_handle(dev))
+    if rc != FRNN_OK:
+        raise FrnnError(rc, "frnn_lstm_stack_fwd")
+    if check:
+        frnn_check(workspace)
+    return o, hn, cn

@@ -1,0 +1,180 @@
+// Alternating forward recurrence for gfx950: per step, one MFMA kernel computes h.R for all heads
+// and batch rows, then one coalesced pointwise kernel applies the gates. R is packed once per call
+// into MFMA-fragment order, so every per-step operand load is a contiguous 1 KiB per wave.
+//
+// Tiles follow the fused design: a 16-row tile of R^T holds the four gates of four units (LSTM)
+// or sixteen units (Elman); lane l of the MFMA result holds rows 4*(l/16)+i of batch column l%16.
+#pragma once
+
+#include "frnn_device.hpp"
+
+namespace frnn {
+
+struct AltArgs {
+  int B, T, N, D, cell;
+  int r_is_f32;  // R, bias and the exchanged h are fp32 (fp32 MFMA) or bf16 (bf16 MFMA)
+  const void* Wx;
+  int wx_f32;
+  long long wx_sb, wx_st;
+  const void* R;
+  long long r_sg, r_sn, r_sd;
+  const void* bias;
+  const void* s0_h;
+  const void* s0_c;
+  int s0_f32;
+  long long s0_sb;
+  float* out_h;
+  float* out_c;
+  long long out_sb, out_st;
+  float* last_h;
+  float* last_c;
+  long long last_sb;
+  void* rpack;    // packed R fragments: [N][TPH][KT][64][8 bf16] or [N][TPH][KT][64] fp32
+  float* rh;      // h.R per step: LSTM [B][N][D][4], Elman [B][N][D]
+  void* hcur;     // current h, MFMA operand type: [N][B][D]
+  float* ccur;    // current c: [B][N][D]
+};
+
+// One thread per (n, tile, k-tile, lane): gathers the lane's 8 (bf16) or 1 (fp32) R^T values.
+__global__ void __launch_bounds__(256) alt_pack_kernel(AltArgs a) {
+  const int G = a.cell == CELL_LSTM ? 4 : 1;
+  const int TPH = G * a.D / 16;
+  const int KW = a.r_is_f32 ? 4 : 32;
+  const int KT = a.D / KW;
+  const long long total = (long long)a.N * TPH * KT * 64;
+  for (long long idx = (long long)blockIdx.x * 256 + threadIdx.x; idx < total; idx += (long long)gridDim.x * 256) {
+    const int lane = (int)(idx & 63);
+    long long r = idx >> 6;
+    const int kt = (int)(r % KT);
+    r /= KT;
+    const int tt = (int)(r % TPH);
+    const int n = (int)(r / TPH);
+    const int m = lane & 15, quad = lane >> 4;
+    int u, g;
+    if (a.cell == CELL_LSTM) { u = 4 * tt + (m >> 2); g = m & 3; }
+    else { u = 16 * tt + m; g = 0; }
+    const long long base = (long long)g * a.r_sg + (long long)n * a.r_sn + u;
+    if (a.r_is_f32) {
+      const int k = kt * 4 + quad;
+      reinterpret_cast<float*>(a.rpack)[idx] = reinterpret_cast<const float*>(a.R)[base + (long long)k * a.r_sd];
+    } else {
+      const uint16_t* Rp = reinterpret_cast<const uint16_t*>(a.R);
+      const int k = kt * 32 + 8 * quad;
+      u32x4_t pk;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        pk[i] = (uint32_t)Rp[base + (long long)(k + 2 * i) * a.r_sd] |
+                ((uint32_t)Rp[base + (long long)(k + 2 * i + 1) * a.r_sd] << 16);
+      reinterpret_cast<u32x4_t*>(a.rpack)[idx] = pk;
+    }
+  }
+}
+
+// Initial state into the working buffers: hcur[n][b][d] (operand type), ccur[b][n][d].
+__global__ void __launch_bounds__(256) alt_init_kernel(AltArgs a) {
+  const long long total = (long long)a.B * a.N * a.D;
+  for (long long idx = (long long)blockIdx.x * 256 + threadIdx.x; idx < total; idx += (long long)gridDim.x * 256) {
+    const int d = (int)(idx % a.D);
+    const long long r = idx / a.D;
+    const int n = (int)(r % a.N);
+    const int b = (int)(r / a.N);
+    const long long s = (long long)b * a.s0_sb + (long long)n * a.D + d;
+    const float h = a.s0_h ? ld_f(a.s0_h, s, a.s0_f32) : 0.0f;
+    const float c = a.s0_c ? ld_f(a.s0_c, s, a.s0_f32) : 0.0f;
+    const long long hi = ((long long)n * a.B + b) * a.D + d;
+    if (a.r_is_f32) reinterpret_cast<float*>(a.hcur)[hi] = h;
+    else reinterpret_cast<uint16_t*>(a.hcur)[hi] = f2bf(h);
+    a.ccur[idx] = c;
+  }
+}
+
+// Per step: grid (ceil(TPH/4), ceil(B/16), N), 4 waves, one R^T tile per wave, full K.
+// Four independent accumulators break the MFMA dependency chain.
+template <bool F32>
+__global__ void __launch_bounds__(256) alt_gemm_kernel(AltArgs a) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int col = lane & 15, quad = lane >> 4;
+  const int G = a.cell == CELL_LSTM ? 4 : 1;
+  const int TPH = G * a.D / 16;
+  const int tt = blockIdx.x * 4 + wave;
+  const int b0 = blockIdx.y * 16;
+  const int n = blockIdx.z;
+  if (tt >= TPH) return;
+  const int KW = F32 ? 4 : 32;
+  const int KT = a.D / KW;
+  const bool colv = b0 + col < a.B;
+  f32x4_t acc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  if constexpr (F32) {
+    const float* rp = reinterpret_cast<const float*>(a.rpack) + ((long long)n * TPH + tt) * KT * 64 + lane;
+    const float* hp = reinterpret_cast<const float*>(a.hcur) + ((long long)n * a.B + b0 + col) * a.D + quad;
+    for (int kt = 0; kt < KT; ++kt) {
+      const float bv = colv ? hp[kt * 4] : 0.0f;
+      acc[kt & 3] = mfma_f32(rp[(long long)kt * 64], bv, acc[kt & 3]);
+    }
+  } else {
+    const u32x4_t* rp = reinterpret_cast<const u32x4_t*>(a.rpack) + ((long long)n * TPH + tt) * KT * 64 + lane;
+    const uint16_t* hp = reinterpret_cast<const uint16_t*>(a.hcur) + ((long long)n * a.B + b0 + col) * a.D + 8 * quad;
+    for (int kt = 0; kt < KT; ++kt) {
+      u32x4_t bv = {0u, 0u, 0u, 0u};
+      if (colv) bv = *reinterpret_cast<const u32x4_t*>(hp + kt * 32);
+      acc[kt & 3] = mfma_bf16(__builtin_bit_cast(bf16x8_t, rp[(long long)kt * 64]), __builtin_bit_cast(bf16x8_t, bv), acc[kt & 3]);
+    }
+  }
+  const f32x4_t s = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+  if (!colv) return;
+  const long long b = b0 + col;
+  if (a.cell == CELL_LSTM) {
+    const int u = 4 * tt + quad;
+    *reinterpret_cast<f32x4_t*>(a.rh + ((b * a.N + n) * a.D + u) * 4) = s;
+  } else {
+    const int u = 16 * tt + 4 * quad;
+    *reinterpret_cast<f32x4_t*>(a.rh + (b * a.N + n) * a.D + u) = s;
+  }
+}
+
+// Per step: one thread per (b, n, unit); consecutive threads take consecutive units, so the Wx,
+// bias, state and output accesses of a wave are contiguous.
+__global__ void __launch_bounds__(256) alt_gate_kernel(AltArgs a, int t) {
+  const long long total = (long long)a.B * a.N * a.D;
+  const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= total) return;
+  const int u = (int)(idx % a.D);
+  const long long r = idx / a.D;
+  const int n = (int)(r % a.N);
+  const long long b = r / a.N;
+  const int N = a.N, D = a.D;
+  const long long wbase = b * a.wx_sb + (long long)t * a.wx_st;
+  const long long o = b * a.out_sb + (long long)t * a.out_st + (long long)n * D + u;
+  const bool rf = a.r_is_f32;
+  float h, c = 0.0f;
+  if (a.cell == CELL_LSTM) {
+    const f32x4_t rh = *reinterpret_cast<const f32x4_t*>(a.rh + idx * 4);
+    float pre[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const long long off = (long long)(g * N + n) * D + u;
+      pre[g] = rh[g] + ld_f(a.Wx, wbase + off, a.wx_f32) + (a.bias ? ld_f(a.bias, off, rf) : 0.0f);
+    }
+    const float ig = sigmoid_f(pre[0]), fg = sigmoid_f(pre[1]), zg = tanh_f(pre[2]), og = sigmoid_f(pre[3]);
+    c = fg * a.ccur[idx] + ig * zg;
+    a.ccur[idx] = c;
+    h = og * tanh_f(c);
+  } else {
+    const long long off = (long long)n * D + u;
+    h = tanh_f(a.rh[idx] + ld_f(a.Wx, wbase + off, a.wx_f32) + (a.bias ? ld_f(a.bias, off, rf) : 0.0f));
+  }
+  if (a.out_h) a.out_h[o] = h;
+  if (a.out_c && a.cell == CELL_LSTM) a.out_c[o] = c;
+  if (t == a.T - 1) {
+    const long long lo = b * a.last_sb + (long long)n * D + u;
+    if (a.last_h) a.last_h[lo] = h;
+    if (a.last_c && a.cell == CELL_LSTM) a.last_c[lo] = c;
+  }
+  const long long hi = ((long long)n * a.B + b) * D + u;
+  if (rf) reinterpret_cast<float*>(a.hcur)[hi] = h;
+  else reinterpret_cast<uint16_t*>(a.hcur)[hi] = f2bf(h);
+}
+
+}  // namespace frnn

@@ -1,0 +1,614 @@
+// Host side of libfrnn: argument validation, launch planning, workspace layout and the C ABI
+// declared in include/frnn.h. Validation and planning are plain host code and run before any HIP
+// call, so they are testable without a GPU.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "frnn.h"
+#include "frnn_alt.hpp"
+#include "frnn_device.hpp"
+#include "frnn_fused.hpp"
+#include "frnn_proj.hpp"
+
+using namespace frnn;
+
+namespace {
+
+// ----------------------------------------------------------------------------- small kernels
+__global__ void __launch_bounds__(256) fill_u32_kernel(uint32_t* p, long long n, uint32_t v) {
+  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long long)gridDim.x * 256) p[i] = v;
+}
+
+// last_states <- states0 (or zeros) for T == 0, widened to fp32. n = S * B * N * D elements.
+__global__ void __launch_bounds__(256) copy_init_kernel(const void* s0, int s0_f32, float* dst, long long n) {
+  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long long)gridDim.x * 256)
+    dst[i] = s0 ? ld_f(s0, i, s0_f32) : 0.0f;
+}
+
+// Records the hardware die id of each workgroup (used once to learn the dispatch pattern).
+__global__ void xcc_map_kernel(int* out) {
+  if (threadIdx.x == 0) out[blockIdx.x] = xcc_id();
+}
+
+constexpr size_t kErrBytes = 256;
+constexpr int kMaxDies = 8;
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// ----------------------------------------------------------------------------- device facts
+struct DevInfo {
+  bool ok = false;
+  int device = -1;
+  int cus = 256;
+  int n_xcd = 8;
+  bool periodic = true;
+  int xcc_of[kMaxDies] = {0, 1, 2, 3, 4, 5, 6, 7};
+  long long wall_khz = 100000;
+};
+
+std::mutex g_dev_mu;
+std::vector<DevInfo> g_dev;
+
+int get_devinfo(DevInfo* out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return FRNN_ENODEVICE;
+  std::lock_guard<std::mutex> lk(g_dev_mu);
+  if ((int)g_dev.size() <= dev) g_dev.resize(dev + 1);
+  DevInfo& di = g_dev[dev];
+  if (!di.ok) {
+    hipDeviceProp_t p;
+    if (hipGetDeviceProperties(&p, dev) != hipSuccess) return FRNN_ENODEVICE;
+    if (std::strncmp(p.gcnArchName, "gfx950", 6) != 0) return FRNN_ENODEVICE;
+    di.device = dev;
+    di.cus = p.multiProcessorCount;
+    int khz = 0;
+    if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) == hipSuccess && khz > 0) di.wall_khz = khz;
+    // Learn how workgroups are dealt to dies: run a grid of one workgroup per CU and read the
+    // die id of each. The fused design needs the pattern to be periodic in the workgroup index.
+    di.n_xcd = std::max(1, std::min(kMaxDies, di.cus / 32));
+    const int nb = di.cus;
+    int* d_map = nullptr;
+    std::vector<int> map(nb, -1);
+    if (hipMalloc(&d_map, sizeof(int) * nb) != hipSuccess) return FRNN_EHIP;
+    hipLaunchKernelGGL(xcc_map_kernel, dim3(nb), dim3(64), 0, 0, d_map);
+    hipError_t e = hipDeviceSynchronize();
+    if (e == hipSuccess) e = hipMemcpy(map.data(), d_map, sizeof(int) * nb, hipMemcpyDeviceToHost);
+    (void)hipFree(d_map);
+    if (e != hipSuccess) return FRNN_EHIP;
+    di.periodic = true;
+    for (int d = 0; d < di.n_xcd; ++d) di.xcc_of[d] = map[d];
+    for (int b = 0; b < nb; ++b)
+      if (map[b] != map[b % di.n_xcd]) di.periodic = false;
+    for (int d = 0; d < di.n_xcd; ++d)
+      for (int d2 = 0; d2 < d; ++d2)
+        if (di.xcc_of[d] == di.xcc_of[d2]) di.periodic = false;
+    di.ok = true;
+  }
+  *out = di;
+  return FRNN_OK;
+}
+
+DevInfo default_devinfo() { return DevInfo(); }
+
+// ----------------------------------------------------------------------------- kernel tables
+typedef void (*fused_fn)(FusedArgs);
+
+struct FusedVariant {
+  int cell, f32, local, ks, mtw, ktw;
+  fused_fn fn;
+};
+
+#define FV(CELL, F32, LOCAL, KS, MTW, KTW) \
+  {CELL, F32, LOCAL, KS, MTW, KTW, &fused_fwd_kernel<CELL, F32, LOCAL, KS, MTW, KTW>}
+#define FV_BOTH_CELLS(F32, LOCAL, KS, MTW, KTW) FV(CELL_LSTM, F32, LOCAL, KS, MTW, KTW), FV(CELL_ELMAN, F32, LOCAL, KS, MTW, KTW)
+
+const FusedVariant kFused[] = {
+    // die-local multi-workgroup design (bf16)
+    FV_BOTH_CELLS(false, false, 4, 1, 1), FV_BOTH_CELLS(false, false, 4, 2, 1), FV_BOTH_CELLS(false, false, 4, 1, 2),
+    FV_BOTH_CELLS(false, false, 4, 2, 2), FV_BOTH_CELLS(false, false, 4, 3, 3), FV_BOTH_CELLS(false, false, 4, 4, 4),
+    FV_BOTH_CELLS(false, false, 4, 6, 6), FV_BOTH_CELLS(false, false, 4, 2, 4), FV_BOTH_CELLS(false, false, 4, 4, 2),
+    FV_BOTH_CELLS(false, false, 4, 4, 1), FV_BOTH_CELLS(false, false, 2, 2, 2),
+    FV_BOTH_CELLS(false, false, 2, 1, 1), FV_BOTH_CELLS(false, false, 2, 2, 1), FV_BOTH_CELLS(false, false, 2, 1, 2),
+    FV_BOTH_CELLS(false, false, 1, 1, 1), FV_BOTH_CELLS(false, false, 1, 1, 2),
+    // single-workgroup design (bf16)
+    FV_BOTH_CELLS(false, true, 1, 1, 1), FV_BOTH_CELLS(false, true, 1, 2, 1), FV_BOTH_CELLS(false, true, 1, 1, 2),
+    FV_BOTH_CELLS(false, true, 1, 4, 2), FV_BOTH_CELLS(false, true, 1, 6, 3), FV_BOTH_CELLS(false, true, 1, 8, 4),
+    FV_BOTH_CELLS(false, true, 1, 2, 4), FV_BOTH_CELLS(false, true, 1, 4, 8), FV_BOTH_CELLS(false, true, 1, 1, 4),
+    // single-workgroup design (fp32)
+    FV_BOTH_CELLS(true, true, 1, 2, 8), FV_BOTH_CELLS(true, true, 1, 1, 8), FV_BOTH_CELLS(true, true, 1, 4, 16),
+    FV_BOTH_CELLS(true, true, 1, 1, 16),
+};
+
+const FusedVariant* find_fused(int cell, int f32, int local, int ks, int mtw, int ktw) {
+  for (const auto& v : kFused)
+    if (v.cell == cell && v.f32 == f32 && v.local == local && v.ks == ks && v.mtw == mtw && v.ktw == ktw) return &v;
+  return nullptr;
+}
+
+// ----------------------------------------------------------------------------- problem
+struct Problem {
+  int B, T, N, D, cell;
+  int r_f32;   // R / bias / MFMA operand type fp32 (else bf16)
+  const void* Wx;
+  int wx_f32;
+  long long wx_sb, wx_st;
+  const void* R;
+  long long r_sg, r_sn, r_sd;
+  const void* bias;
+  const void* s0_h;
+  const void* s0_c;
+  int s0_f32;
+  long long s0_sb;
+  float* out_h;
+  float* out_c;
+  long long out_sb, out_st;
+  float* last_h;
+  float* last_c;
+  long long last_sb;
+};
+
+int gates_of(int cell) { return cell == FRNN_CELL_LSTM ? 4 : 1; }
+
+struct FusedPlan {
+  const FusedVariant* v = nullptr;
+  int local = 0, W = 1, BR = 16, groups = 0, ks = 1, mtw = 0, ktw = 0, n_xcd = 1, slots = 0, grid = 0;
+  size_t lds = 0;
+};
+
+int env_int(const char* name, int dflt) {
+  const char* s = std::getenv(name);
+  if (!s || !*s) return dflt;
+  return std::atoi(s);
+}
+
+// Choose the fused design for a problem. The workgroup-local design is used when the whole head
+// fits in one workgroup's registers and the per-wave MFMA chain stays short; otherwise W
+// workgroups per group on one die, W as large as possible (least MFMA work per CU), then the
+// fewest batch rows per group (least h polled per step) that still fit the die.
+int plan_fused(const Problem& p, const DevInfo& di, FusedPlan* out) {
+  const int G = gates_of(p.cell);
+  const int TPH = G * p.D / 16;
+  const int KW = p.r_f32 ? 4 : 32;
+  if (p.D % 32 != 0 || TPH < 1) return FRNN_EUNSUPPORTED;
+  const int KT = p.D / KW;
+  const int force_w = env_int("FRNN_FUSED_W", 0);
+  const int force_br = env_int("FRNN_FUSED_BR", 0);
+  // workgroup-local
+  if (force_w <= 1) {
+    const int mtw = (TPH + 3) / 4;
+    const FusedVariant* v = find_fused(p.cell, p.r_f32, 1, 1, mtw, KT);
+    const int per_wave = mtw * KT;
+    if (v && (per_wave <= 64 || force_w == 1)) {
+      FusedPlan fp;
+      fp.v = v;
+      fp.local = 1;
+      fp.W = 1;
+      fp.BR = (force_br >= 1 && force_br <= 16) ? force_br : 16;
+      fp.groups = p.N * ((p.B + fp.BR - 1) / fp.BR);
+      fp.ks = 1;
+      fp.mtw = mtw;
+      fp.ktw = KT;
+      fp.grid = fp.groups;
+      const int elt = p.r_f32 ? 4 : 2;
+      fp.lds = (size_t)2 * 16 * (p.D + fused_hpad(p.r_f32)) * elt;
+      *out = fp;
+      return FRNN_OK;
+    }
+    if (force_w == 1) return FRNN_EUNSUPPORTED;
+  }
+  if (p.r_f32 || !di.periodic) return FRNN_EUNSUPPORTED;
+  const int slots_per_die = std::max(1, di.cus / di.n_xcd);
+  for (int W = std::min(32, slots_per_die); W >= 2; --W) {
+    if (force_w > 1 && W != force_w) continue;
+    if (TPH % W) continue;
+    const int mt_wg = TPH / W;
+    for (int ks : {4, 2, 1}) {
+      const int ms = 4 / ks;
+      if (mt_wg % ms || KT % ks) continue;
+      const int mtw = mt_wg / ms, ktw = KT / ks;
+      const FusedVariant* v = find_fused(p.cell, 0, 0, ks, mtw, ktw);
+      if (!v) continue;
+      for (int BR = 1; BR <= 16; ++BR) {
+        if (force_br && BR != force_br) continue;
+        const int groups = p.N * ((p.B + BR - 1) / BR);
+        const int per_die = (groups + di.n_xcd - 1) / di.n_xcd;
+        if (per_die * W > slots_per_die) continue;
+        FusedPlan fp;
+        fp.v = v;
+        fp.local = 0;
+        fp.W = W;
+        fp.BR = BR;
+        fp.groups = groups;
+        fp.ks = ks;
+        fp.mtw = mtw;
+        fp.ktw = ktw;
+        fp.n_xcd = di.n_xcd;
+        fp.slots = per_die * W;
+        fp.grid = fp.slots * di.n_xcd;
+        fp.lds = ks > 1 ? (size_t)2 * ks * mt_wg * 64 * 16 : 0;
+        *out = fp;
+        return FRNN_OK;
+      }
+    }
+  }
+  return FRNN_EUNSUPPORTED;
+}
+
+// Scratch needed by the recurrence of a problem on a path, beside the error word (independent
+// of T).
+size_t rec_scratch_bytes(int B, int N, int D, int cell, int r_f32, int path) {
+  const int G = gates_of(cell);
+  const size_t elt = r_f32 ? 4 : 2;
+  if (path == FRNN_PATH_FUSED) {
+    // exchange words: groups * BR <= N * (B + 15) rows, two parities
+    return align256((size_t)2 * N * (B + 15) * D * 4);
+  }
+  size_t s = 0;
+  s += align256((size_t)G * N * D * D * elt);  // packed R
+  s += align256((size_t)B * N * D * G * 4);    // h.R
+  s += align256((size_t)N * B * D * elt);      // current h
+  s += align256((size_t)B * N * D * 4);        // current c
+  return s;
+}
+
+hipError_t launch_fill(void* p, size_t bytes, hipStream_t st) {
+  const long long n = (long long)(bytes / 4);
+  if (n <= 0) return hipSuccess;
+  const int blocks = (int)std::min<long long>((n + 255) / 256, 1024);
+  hipLaunchKernelGGL(fill_u32_kernel, dim3(blocks), dim3(256), 0, st, reinterpret_cast<uint32_t*>(p), n, 0u);
+  return hipGetLastError();
+}
+
+void trace(const char* fmt, const std::string& s) {
+  if (env_int("FRNN_TRACE", 0)) std::fprintf(stderr, fmt, s.c_str());
+}
+
+std::string plan_string(const Problem& p, int path, const FusedPlan* fp) {
+  char buf[512];
+  if (path == FRNN_PATH_FUSED && fp) {
+    std::snprintf(buf, sizeof(buf),
+                  "fused design=%s cell=%s dtype=%s B=%d T=%d N=%d D=%d BR=%d groups=%d W=%d KS=%d MTW=%d KTW=%d "
+                  "dies=%d slots/die=%d grid=%d lds=%zu",
+                  fp->local ? "workgroup-local" : "die-local", p.cell == FRNN_CELL_LSTM ? "lstm" : "elman",
+                  p.r_f32 ? "f32" : "bf16", p.B, p.T, p.N, p.D, fp->BR, fp->groups, fp->W, fp->ks, fp->mtw, fp->ktw,
+                  fp->n_xcd, fp->slots, fp->grid, fp->lds);
+  } else {
+    const int G = gates_of(p.cell);
+    const int TPH = G * p.D / 16;
+    std::snprintf(buf, sizeof(buf),
+                  "alternating cell=%s dtype=%s B=%d T=%d N=%d D=%d gemm_grid=(%d,%d,%d) gate_grid=%lld launches=%d",
+                  p.cell == FRNN_CELL_LSTM ? "lstm" : "elman", p.r_f32 ? "f32" : "bf16", p.B, p.T, p.N, p.D,
+                  (TPH + 3) / 4, (p.B + 15) / 16, p.N, ((long long)p.B * p.N * p.D + 255) / 256, 2 * p.T + 2);
+  }
+  return std::string(buf);
+}
+
+// Run the recurrence of a validated problem. `scratch` holds at least rec_scratch_bytes();
+// device-side errors are or-ed into `err` (cleared by the caller once per API call).
+int run_recurrence(const Problem& p, int path, int* err, void* scratch, hipStream_t st) {
+  DevInfo di;
+  int rc = get_devinfo(&di);
+  if (rc != FRNN_OK) return rc;
+  char* base = reinterpret_cast<char*>(scratch);
+  if (path == FRNN_PATH_FUSED) {
+    FusedPlan fp;
+    rc = plan_fused(p, di, &fp);
+    if (rc != FRNN_OK) return rc;
+    trace("[frnn] %s\n", plan_string(p, path, &fp));
+    const size_t xbytes = fp.local ? 0 : (size_t)fp.groups * 2 * fp.BR * p.D * 4;
+    if (launch_fill(scratch, xbytes, st) != hipSuccess) return FRNN_EHIP;
+    FusedArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.B = p.B; a.T = p.T; a.N = p.N; a.D = p.D;
+    a.BR = fp.BR; a.groups = fp.groups; a.W = fp.W; a.n_xcd = fp.n_xcd;
+    a.check_xcc = fp.local ? 0 : 1;
+    for (int d = 0; d < kMaxDies; ++d) a.xcc_of[d] = di.xcc_of[d];
+    a.Wx = p.Wx; a.wx_f32 = p.wx_f32; a.wx_sb = p.wx_sb; a.wx_st = p.wx_st;
+    a.R = p.R; a.r_sg = p.r_sg; a.r_sn = p.r_sn; a.r_sd = p.r_sd; a.bias = p.bias;
+    a.s0_h = p.s0_h; a.s0_c = p.s0_c; a.s0_f32 = p.s0_f32; a.s0_sb = p.s0_sb;
+    a.out_h = p.out_h; a.out_c = p.out_c; a.out_sb = p.out_sb; a.out_st = p.out_st;
+    a.last_h = p.last_h; a.last_c = p.last_c; a.last_sb = p.last_sb;
+    a.xbuf = reinterpret_cast<uint32_t*>(base);
+    a.err = err;
+    a.timeout_ticks = (long long)env_int("FRNN_TIMEOUT_MS", 2000) * di.wall_khz;
+    const void* fn = reinterpret_cast<const void*>(fp.v->fn);
+    if (fp.lds > 48 * 1024) {
+      if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)fp.lds) != hipSuccess) return FRNN_EHIP;
+    }
+    void* args[] = {&a};
+    hipError_t e;
+    if (fp.local) {
+      e = hipLaunchKernel(fn, dim3(fp.grid), dim3(256), args, fp.lds, st);
+    } else {
+      e = hipLaunchCooperativeKernel(fn, dim3(fp.grid), dim3(256), args, (unsigned)fp.lds, st);
+      if (e == hipErrorCooperativeLaunchTooLarge) return FRNN_ENORESIDENT;
+    }
+    return e == hipSuccess ? FRNN_OK : FRNN_EHIP;
+  }
+  // alternating
+  trace("[frnn] %s\n", plan_string(p, path, nullptr));
+  const int G = gates_of(p.cell);
+  const size_t elt = p.r_f32 ? 4 : 2;
+  AltArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.B = p.B; a.T = p.T; a.N = p.N; a.D = p.D; a.cell = p.cell; a.r_is_f32 = p.r_f32;
+  a.Wx = p.Wx; a.wx_f32 = p.wx_f32; a.wx_sb = p.wx_sb; a.wx_st = p.wx_st;
+  a.R = p.R; a.r_sg = p.r_sg; a.r_sn = p.r_sn; a.r_sd = p.r_sd; a.bias = p.bias;
+  a.s0_h = p.s0_h; a.s0_c = p.s0_c; a.s0_f32 = p.s0_f32; a.s0_sb = p.s0_sb;
+  a.out_h = p.out_h; a.out_c = p.out_c; a.out_sb = p.out_sb; a.out_st = p.out_st;
+  a.last_h = p.last_h; a.last_c = p.last_c; a.last_sb = p.last_sb;
+  char* q = base;
+  a.rpack = q; q += align256((size_t)G * p.N * p.D * p.D * elt);
+  a.rh = reinterpret_cast<float*>(q); q += align256((size_t)p.B * p.N * p.D * G * 4);
+  a.hcur = q; q += align256((size_t)p.N * p.B * p.D * elt);
+  a.ccur = reinterpret_cast<float*>(q);
+  const int TPH = G * p.D / 16;
+  const int KT = p.D / (p.r_f32 ? 4 : 32);
+  const long long npack = (long long)p.N * TPH * KT * 64;
+  hipLaunchKernelGGL(alt_pack_kernel, dim3((unsigned)std::min<long long>((npack + 255) / 256, 4096)), dim3(256), 0, st, a);
+  const long long nstate = (long long)p.B * p.N * p.D;
+  hipLaunchKernelGGL(alt_init_kernel, dim3((unsigned)std::min<long long>((nstate + 255) / 256, 4096)), dim3(256), 0, st, a);
+  const dim3 ggrid((TPH + 3) / 4, (p.B + 15) / 16, p.N);
+  const dim3 tgrid((unsigned)((nstate + 255) / 256));
+  for (int t = 0; t < p.T; ++t) {
+    if (p.r_f32) hipLaunchKernelGGL(alt_gemm_kernel<true>, ggrid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL(alt_gemm_kernel<false>, ggrid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL(alt_gate_kernel, tgrid, dim3(256), 0, st, a, t);
+  }
+  return hipGetLastError() == hipSuccess ? FRNN_OK : FRNN_EHIP;
+}
+
+bool misaligned(const void* p) { return p && (reinterpret_cast<uintptr_t>(p) & 15u); }
+
+int validate_desc(const frnn_desc* d, int path) {
+  if (!d) return FRNN_EINVAL;
+  if (d->reserved != 0) return FRNN_EINVAL;
+  if (d->B < 1 || d->N < 1 || d->D < 1 || d->T < 0) return FRNN_EINVAL;
+  if (d->cell != FRNN_CELL_LSTM && d->cell != FRNN_CELL_ELMAN) return FRNN_EINVAL;
+  if (d->in_dtype != FRNN_F32 && d->in_dtype != FRNN_BF16) return FRNN_EINVAL;
+  if (d->out_dtype != FRNN_F32 && d->out_dtype != FRNN_BF16) return FRNN_EINVAL;
+  if (path != FRNN_PATH_ALTERNATING && path != FRNN_PATH_FUSED) return FRNN_EINVAL;
+  const long long elems = (long long)d->B * d->T * gates_of(d->cell) * d->N * d->D;
+  if (elems < 0 || elems > (1LL << 40)) return FRNN_EINVAL;
+  if (d->out_dtype != FRNN_F32) return FRNN_EUNSUPPORTED;
+  if (d->D % 32 != 0 || d->D > 1024) return FRNN_EUNSUPPORTED;
+  return FRNN_OK;
+}
+
+Problem problem_from_desc(const frnn_desc* d, const void* Wx, const void* R, const void* b, const void* s0,
+                          void* states, void* last) {
+  Problem p;
+  std::memset(&p, 0, sizeof(p));
+  const int G = gates_of(d->cell);
+  const long long B = d->B, T = d->T, N = d->N, D = d->D;
+  const int f32 = d->in_dtype == FRNN_F32;
+  const size_t elt = f32 ? 4 : 2;
+  p.B = d->B; p.T = d->T; p.N = d->N; p.D = d->D; p.cell = d->cell; p.r_f32 = f32;
+  p.Wx = Wx; p.wx_f32 = f32; p.wx_sb = T * G * N * D; p.wx_st = (long long)G * N * D;
+  p.R = R; p.r_sg = N * D * D; p.r_sn = D * D; p.r_sd = D;
+  p.bias = b;
+  p.s0_h = s0;
+  p.s0_c = (s0 && d->cell == FRNN_CELL_LSTM) ? reinterpret_cast<const char*>(s0) + (size_t)B * N * D * elt : nullptr;
+  p.s0_f32 = f32; p.s0_sb = N * D;
+  float* st = reinterpret_cast<float*>(states);
+  p.out_h = st;
+  p.out_c = (st && d->cell == FRNN_CELL_LSTM) ? st + B * T * N * D : nullptr;
+  p.out_sb = T * N * D; p.out_st = N * D;
+  float* ls = reinterpret_cast<float*>(last);
+  p.last_h = ls;
+  p.last_c = (ls && d->cell == FRNN_CELL_LSTM) ? ls + B * N * D : nullptr;
+  p.last_sb = N * D;
+  return p;
+}
+
+}  // namespace
+
+// ============================================================================= C ABI
+extern "C" {
+
+int frnn_abi_version(void) { return FRNN_ABI_VERSION; }
+
+const char* frnn_status_str(int s) {
+  switch (s) {
+    case FRNN_OK: return "ok";
+    case FRNN_EINVAL: return "invalid argument";
+    case FRNN_EUNSUPPORTED: return "unsupported by this build (dtype, head dimension or path)";
+    case FRNN_EWORKSPACE: return "workspace missing or too small";
+    case FRNN_ENORESIDENT: return "persistent grid cannot be co-resident on this device";
+    case FRNN_EHIP: return "HIP runtime error";
+    case FRNN_ETIMEOUT: return "a bounded inter-workgroup wait ran out on the device";
+    case FRNN_EPLACEMENT: return "a workgroup ran on a different accelerator die than planned";
+    case FRNN_ENODEVICE: return "no usable gfx950 device";
+    default: return "unknown status";
+  }
+}
+
+int frnn_workspace_bytes(const frnn_desc* d, int path, size_t* bytes) {
+  const int rc = validate_desc(d, path);
+  if (rc != FRNN_OK) return rc;
+  if (!bytes) return FRNN_EINVAL;
+  *bytes = kErrBytes + rec_scratch_bytes(d->B, d->N, d->D, d->cell, d->in_dtype == FRNN_F32, path);
+  return FRNN_OK;
+}
+
+int frnn_plan_str(const frnn_desc* d, int path, char* buf, size_t cap) {
+  int rc = validate_desc(d, path);
+  if (rc != FRNN_OK) return rc;
+  if (!buf || cap == 0) return FRNN_EINVAL;
+  Problem p = problem_from_desc(d, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr);
+  std::string s;
+  if (path == FRNN_PATH_FUSED) {
+    DevInfo di;
+    if (get_devinfo(&di) != FRNN_OK) di = default_devinfo();
+    FusedPlan fp;
+    rc = plan_fused(p, di, &fp);
+    if (rc != FRNN_OK) return rc;
+    s = plan_string(p, path, &fp);
+  } else {
+    s = plan_string(p, path, nullptr);
+  }
+  std::snprintf(buf, cap, "%s", s.c_str());
+  return FRNN_OK;
+}
+
+int frnn_fwd(const frnn_desc* d, int path, const void* Wx, const void* R, const void* b, const void* states0,
+             void* states, void* last_states, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = validate_desc(d, path);
+  if (rc != FRNN_OK) return rc;
+  if (d->T > 0 && (!Wx || !R)) return FRNN_EINVAL;
+  if (misaligned(Wx) || misaligned(R) || misaligned(b) || misaligned(states0) || misaligned(states) ||
+      misaligned(last_states) || misaligned(workspace))
+    return FRNN_EINVAL;
+  const size_t need = kErrBytes + rec_scratch_bytes(d->B, d->N, d->D, d->cell, d->in_dtype == FRNN_F32, path);
+  if (!workspace || workspace_bytes < need) return FRNN_EWORKSPACE;
+  Problem p = problem_from_desc(d, Wx, R, b, states0, states, last_states);
+  if (path == FRNN_PATH_FUSED) {
+    DevInfo di;
+    rc = get_devinfo(&di);
+    if (rc != FRNN_OK) return rc;
+    FusedPlan fp;
+    rc = plan_fused(p, di, &fp);
+    if (rc != FRNN_OK) return rc;
+  } else {
+    DevInfo di;
+    rc = get_devinfo(&di);
+    if (rc != FRNN_OK) return rc;
+  }
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (launch_fill(workspace, kErrBytes, st) != hipSuccess) return FRNN_EHIP;
+  if (d->T == 0) {
+    if (last_states) {
+      const long long n = (long long)(d->cell == FRNN_CELL_LSTM ? 2 : 1) * d->B * d->N * d->D;
+      hipLaunchKernelGGL(copy_init_kernel, dim3((unsigned)std::min<long long>((n + 255) / 256, 4096)), dim3(256), 0, st,
+                         states0, d->in_dtype == FRNN_F32 ? 1 : 0, reinterpret_cast<float*>(last_states), n);
+      if (hipGetLastError() != hipSuccess) return FRNN_EHIP;
+    }
+    return FRNN_OK;
+  }
+  return run_recurrence(p, path, reinterpret_cast<int*>(workspace), reinterpret_cast<char*>(workspace) + kErrBytes, st);
+}
+
+int frnn_check(const void* workspace, void* stream) {
+  if (!workspace) return FRNN_EINVAL;
+  if (hipStreamSynchronize(reinterpret_cast<hipStream_t>(stream)) != hipSuccess) return FRNN_EHIP;
+  int word = 0;
+  if (hipMemcpy(&word, workspace, sizeof(int), hipMemcpyDeviceToHost) != hipSuccess) return FRNN_EHIP;
+  if (word & DEVERR_PLACEMENT) return FRNN_EPLACEMENT;
+  if (word & DEVERR_TIMEOUT) return FRNN_ETIMEOUT;
+  return FRNN_OK;
+}
+
+static int validate_stack(int L, int T, int B, int I, int H, int path) {
+  if (L < 1 || T < 0 || B < 1 || I < 1 || H < 1) return FRNN_EINVAL;
+  if (path != FRNN_PATH_ALTERNATING && path != FRNN_PATH_FUSED) return FRNN_EINVAL;
+  if ((long long)T * B * 4 * H > (1LL << 40)) return FRNN_EINVAL;
+  if (H % 32 != 0 || H > 1024) return FRNN_EUNSUPPORTED;
+  return FRNN_OK;
+}
+
+static size_t stack_ws_bytes(int L, int T, int B, int H, int path) {
+  size_t s = kErrBytes;
+  s += align256((size_t)T * B * 4 * H * 4);           // projected inputs of one layer, fp32
+  if (L > 1) s += align256((size_t)T * B * H * 4);    // h sequence handed to the next layer, fp32
+  s += rec_scratch_bytes(B, 1, H, FRNN_CELL_LSTM, 0, path);
+  return s;
+}
+
+int frnn_lstm_stack_workspace_bytes(int L, int T, int B, int I, int H, int path, size_t* bytes) {
+  const int rc = validate_stack(L, T, B, I, H, path);
+  if (rc != FRNN_OK) return rc;
+  if (!bytes) return FRNN_EINVAL;
+  *bytes = stack_ws_bytes(L, T, B, H, path);
+  return FRNN_OK;
+}
+
+int frnn_lstm_stack_fwd(int L, int T, int B, int I, int H, int path, const void* x, const void* const* Wi,
+                        const void* const* Wh, const void* const* b_ih, const void* const* b_hh, const void* h0,
+                        const void* c0, void* out, void* hn, void* cn, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  int rc = validate_stack(L, T, B, I, H, path);
+  if (rc != FRNN_OK) return rc;
+  if (!Wi || !Wh) return FRNN_EINVAL;
+  if (T > 0 && !x) return FRNN_EINVAL;
+  for (int l = 0; l < L; ++l) {
+    if (!Wi[l] || !Wh[l]) return FRNN_EINVAL;
+    if (misaligned(Wi[l]) || misaligned(Wh[l])) return FRNN_EINVAL;
+    if (b_ih && misaligned(b_ih[l])) return FRNN_EINVAL;
+    if (b_hh && misaligned(b_hh[l])) return FRNN_EINVAL;
+  }
+  if (misaligned(x) || misaligned(h0) || misaligned(c0) || misaligned(out) || misaligned(hn) || misaligned(cn) ||
+      misaligned(workspace))
+    return FRNN_EINVAL;
+  if (!workspace || workspace_bytes < stack_ws_bytes(L, T, B, H, path)) return FRNN_EWORKSPACE;
+  DevInfo di;
+  rc = get_devinfo(&di);
+  if (rc != FRNN_OK) return rc;
+  // the per-layer recurrence plan must exist before anything is enqueued
+  Problem probe;
+  std::memset(&probe, 0, sizeof(probe));
+  probe.B = B; probe.T = T; probe.N = 1; probe.D = H; probe.cell = FRNN_CELL_LSTM; probe.r_f32 = 0;
+  if (path == FRNN_PATH_FUSED) {
+    FusedPlan fp;
+    rc = plan_fused(probe, di, &fp);
+    if (rc != FRNN_OK) return rc;
+  }
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  char* base = reinterpret_cast<char*>(workspace);
+  if (launch_fill(workspace, kErrBytes, st) != hipSuccess) return FRNN_EHIP;
+  char* q = base + kErrBytes;
+  float* wx = reinterpret_cast<float*>(q);
+  q += align256((size_t)T * B * 4 * H * 4);
+  float* hseq = nullptr;
+  if (L > 1) { hseq = reinterpret_cast<float*>(q); q += align256((size_t)T * B * H * 4); }
+  void* rws = q;
+  const long long LBH = (long long)B * H;
+  for (int l = 0; l < L; ++l) {
+    float* last_h = hn ? reinterpret_cast<float*>(hn) + l * LBH : nullptr;
+    float* last_c = cn ? reinterpret_cast<float*>(cn) + l * LBH : nullptr;
+    const void* s0h = h0 ? reinterpret_cast<const uint16_t*>(h0) + l * LBH : nullptr;
+    const void* s0c = c0 ? reinterpret_cast<const uint16_t*>(c0) + l * LBH : nullptr;
+    if (T == 0) {
+      if (last_h) hipLaunchKernelGGL(copy_init_kernel, dim3((unsigned)((LBH + 255) / 256)), dim3(256), 0, st, s0h, 0, last_h, LBH);
+      if (last_c) hipLaunchKernelGGL(copy_init_kernel, dim3((unsigned)((LBH + 255) / 256)), dim3(256), 0, st, s0c, 0, last_c, LBH);
+      continue;
+    }
+    // projection of the layer's whole input sequence: rows m = t*B + b
+    ProjArgs pa;
+    pa.M = T * B; pa.Nc = 4 * H; pa.K = (l == 0) ? I : H;
+    pa.A = (l == 0) ? x : hseq;
+    pa.a_f32 = (l == 0) ? 0 : 1;
+    pa.lda = pa.K;
+    pa.Bw = reinterpret_cast<const uint16_t*>(Wi[l]);
+    pa.ldb = 4 * H;
+    pa.b1 = b_ih ? reinterpret_cast<const uint16_t*>(b_ih[l]) : nullptr;
+    pa.b2 = b_hh ? reinterpret_cast<const uint16_t*>(b_hh[l]) : nullptr;
+    pa.C = wx;
+    pa.ldc = 4 * H;
+    hipLaunchKernelGGL(proj_gemm_kernel, dim3((pa.Nc + PJ_BN - 1) / PJ_BN, (pa.M + PJ_BM - 1) / PJ_BM), dim3(256), 0, st, pa);
+    if (hipGetLastError() != hipSuccess) return FRNN_EHIP;
+    // recurrence with Wh [H, 4H] read through strides: R[g][0][d][e] = Wh[d][g*H + e]
+    Problem p;
+    std::memset(&p, 0, sizeof(p));
+    p.B = B; p.T = T; p.N = 1; p.D = H; p.cell = FRNN_CELL_LSTM; p.r_f32 = 0;
+    p.Wx = wx; p.wx_f32 = 1; p.wx_sb = 4LL * H; p.wx_st = 4LL * H * B;
+    p.R = Wh[l]; p.r_sg = H; p.r_sn = 0; p.r_sd = 4LL * H;
+    p.bias = nullptr;
+    p.s0_h = s0h; p.s0_c = s0c; p.s0_f32 = 0; p.s0_sb = H;
+    p.out_h = (l == L - 1) ? reinterpret_cast<float*>(out) : hseq;
+    p.out_c = nullptr;
+    p.out_sb = H; p.out_st = (long long)B * H;
+    p.last_h = last_h; p.last_c = last_c; p.last_sb = H;
+    rc = run_recurrence(p, path, reinterpret_cast<int*>(workspace), rws, st);
+    if (rc != FRNN_OK) return rc;
+  }
+  return FRNN_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,149 @@
+/*
+ * frnn.h -- C ABI of the MI355X (gfx950) head-wise LSTM / Elman forward-recurrence library.
+ *
+ * What is computed (FlashRNN usage example, hottg.com/neural/9889; cell equations of
+ * "5.3 LSTM", developnotes.readthedocs.io operator.html, applied per head):
+ *
+ *   for every batch row b and head n, for t = 0 .. T-1, with h, c the state after step t-1:
+ *     pre[g][e] = Wx[b,t,g,n,e] + sum_d h[d] * R[g,n,d,e] + bias[g,n,e]
+ *     LSTM  (G = 4 gates i, f, z, o; S = 2 states h, c):
+ *        i = sigmoid(pre[0]), f = sigmoid(pre[1]), z = tanh(pre[2]), o = sigmoid(pre[3])
+ *        c = f * c + i * z;   h = o * tanh(c)
+ *     Elman (G = 1, S = 1):   h = tanh(pre[0])
+ *     states[0,b,t,n,:] = h;  (LSTM) states[1,b,t,n,:] = c
+ *   last_states[:,b,0,n,:] = the state after the last step (T == 0: the initial state).
+ *
+ * Every step uses the complete h of the previous step (synchronous update); batch rows and heads
+ * never interact.
+ *
+ * Conventions shared by every entry point:
+ *  - All tensor arguments are DEVICE pointers owned by the caller; the library never allocates,
+ *    frees or synchronises them. Work is enqueued on `stream` (a hipStream_t passed as void*;
+ *    NULL = the default stream) and runs asynchronously.
+ *  - Arguments are validated on the host before anything is enqueued; on any error nothing is
+ *    enqueued and a negative frnn_status is returned.
+ *  - The workspace is caller-owned device memory of at least the size the matching
+ *    *_workspace_bytes function reports; its size does not depend on T for frnn_fwd. One
+ *    workspace must not be used by two calls that may run concurrently.
+ *  - Errors that can only be seen on the device (a bounded wait that ran out, a workgroup that
+ *    landed on an unexpected accelerator die) are written into the workspace and reported by
+ *    frnn_check() after the stream has reached the call.
+ *  - Tensors are dense, row-major, with the layouts stated below, and 16-byte aligned.
+ */
+#ifndef FRNN_H
+#define FRNN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FRNN_ABI_VERSION 1
+
+/* Status codes (0 = success). */
+enum {
+  FRNN_OK = 0,
+  FRNN_EINVAL = -1,          /* bad dimension, NULL required pointer, misaligned pointer, bad enum */
+  FRNN_EUNSUPPORTED = -2,    /* valid request this build has no kernel for (dtype, D, path) */
+  FRNN_EWORKSPACE = -3,      /* workspace NULL or smaller than required */
+  FRNN_ENORESIDENT = -4,     /* the persistent grid cannot be co-resident on this device */
+  FRNN_EHIP = -5,            /* a HIP runtime call failed */
+  FRNN_ETIMEOUT = -6,        /* (frnn_check) a bounded inter-workgroup wait ran out */
+  FRNN_EPLACEMENT = -7,      /* (frnn_check) a workgroup ran on another die than planned */
+  FRNN_ENODEVICE = -8        /* no usable gfx950 device */
+};
+
+/* Cells (FlashRNN cell names "lstm" and "elman"). */
+enum { FRNN_CELL_LSTM = 0, FRNN_CELL_ELMAN = 1 };
+
+/* Element types. */
+enum { FRNN_F32 = 0, FRNN_BF16 = 1 };
+
+/* Kernel designs (the FlashRNN page's "alternating" and "fused" variants, re-designed for
+ * gfx950):
+ *  ALTERNATING: per step, one MFMA kernel computes h.R for every head and one coalesced
+ *               pointwise kernel applies the gates; 2*T launches on `stream`.
+ *  FUSED:       one persistent cooperative launch; R stays in registers for all T steps; the
+ *               workgroups sharing a head exchange h through the die-local L2 every step. */
+enum { FRNN_PATH_ALTERNATING = 0, FRNN_PATH_FUSED = 1 };
+
+/* Problem description for frnn_fwd. G and S follow from `cell` (LSTM: 4, 2; Elman: 1, 1). */
+typedef struct frnn_desc {
+  int32_t B;          /* batch size, >= 1 */
+  int32_t T;          /* sequence length, >= 0 */
+  int32_t N;          /* number of heads, >= 1 */
+  int32_t D;          /* head dimension, >= 1 (this build: a multiple of 32, <= 1024) */
+  int32_t cell;       /* FRNN_CELL_* */
+  int32_t in_dtype;   /* dtype of Wx, R, b, states0: FRNN_F32 or FRNN_BF16 */
+  int32_t out_dtype;  /* dtype of states and last_states: FRNN_F32 (the only one supported) */
+  int32_t reserved;   /* must be 0 */
+} frnn_desc;
+
+/* ABI version of the loaded library (FRNN_ABI_VERSION). */
+int frnn_abi_version(void);
+
+/* Static, human-readable text for a status code. */
+const char* frnn_status_str(int status);
+
+/* Workspace bytes frnn_fwd needs for `d` on `path`. Returns FRNN_OK and writes *bytes, or a
+ * negative status when `d` is invalid or unsupported. Independent of T. */
+int frnn_workspace_bytes(const frnn_desc* d, int path, size_t* bytes);
+
+/*
+ * Head-wise forward recurrence (FlashRNN functional call: states, last_states = f(Wx, R, b,
+ * states_initial)). Layouts (FlashRNN usage example):
+ *   Wx          [B, T, G, N, D]   in_dtype, read-only (the already-projected input W.x)
+ *   R           [G, N, D, D]      in_dtype, read-only; h (as a row vector) times R[g, n]
+ *   b           [G, N, D]         in_dtype, read-only; NULL = zero bias
+ *   states0     [S, B, 1, N, D]   in_dtype, read-only; NULL = zero initial h (and c)
+ *   states      [S, B, T, N, D]   out_dtype, written; NULL = not written
+ *   last_states [S, B, 1, N, D]   out_dtype, written; NULL = not written
+ * For the LSTM, index 0 along S is h and index 1 is c. T == 0 is valid: last_states receives
+ * states0 (or zeros) and states is untouched.
+ */
+int frnn_fwd(const frnn_desc* d, int path, const void* Wx, const void* R, const void* b,
+             const void* states0, void* states, void* last_states, void* workspace,
+             size_t workspace_bytes, void* stream);
+
+/*
+ * Plain multi-layer unidirectional LSTM with input projection ("5.3 LSTM": MyLSTM.set_weights,
+ * MyLSTM.forward). Per layer l and step t:
+ *   gates = in_t . Wi[l] + h . Wh[l] + (b_ih[l] + b_hh[l]),   column blocks i | f | g | o of width H
+ *   c = f*c + i*g, h = o*tanh(c);   in_t = x[t] for l = 0, else layer l-1's new h at step t.
+ * Layouts (bf16 unless stated):
+ *   x          [T, B, I]
+ *   Wi[l]      [I, 4H] for l = 0, [H, 4H] for l >= 1   (array of L device pointers, host array)
+ *   Wh[l]      [H, 4H]                                 (host array of L device pointers)
+ *   b_ih[l], b_hh[l]  [4H]                             (host arrays; an entry may be NULL = 0)
+ *   h0, c0     [L, B, H] or NULL (zeros)
+ *   out        [T, B, H]  fp32, top layer's h at every step (NULL = not written)
+ *   hn, cn     [L, B, H]  fp32, final states (NULL = not written)
+ * The layers run in layer-major order (all T steps of layer 0, then layer 1), which gives the
+ * same result as the page's time-major order because layer l at step t depends only on layer
+ * l-1 at step t and layer l at step t-1. Each layer's projection over all T runs as one MFMA
+ * GEMM before its recurrence.
+ */
+int frnn_lstm_stack_fwd(int L, int T, int B, int I, int H, int path, const void* x,
+                        const void* const* Wi, const void* const* Wh, const void* const* b_ih,
+                        const void* const* b_hh, const void* h0, const void* c0, void* out,
+                        void* hn, void* cn, void* workspace, size_t workspace_bytes,
+                        void* stream);
+
+/* Workspace bytes frnn_lstm_stack_fwd needs (grows with T: it holds the projected inputs). */
+int frnn_lstm_stack_workspace_bytes(int L, int T, int B, int I, int H, int path, size_t* bytes);
+
+/* Waits for `stream`, then reads the device-side error word of the last call that used
+ * `workspace` (FRNN_OK, FRNN_ETIMEOUT, FRNN_EPLACEMENT, or FRNN_EHIP if the wait failed). */
+int frnn_check(const void* workspace, void* stream);
+
+/* Description of the launch frnn_fwd would make for `d` on `path` (for logs and tests):
+ * writes up to `cap` bytes of text into `buf`. Returns FRNN_OK or a negative status. */
+int frnn_plan_str(const frnn_desc* d, int path, char* buf, size_t cap);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FRNN_H */

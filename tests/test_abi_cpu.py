@@ -1,0 +1,162 @@
+"""Host-side checks of libfrnn that need no GPU: the library loads, exports every entry point
+include/frnn.h declares, validates arguments before touching a device, sizes workspaces, and plans
+launches. No compute call is made here."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+import torch
+
+import head_wise_lstm_amd as hw
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "frnn.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(hw.lib_path()):
+        from head_wise_lstm_amd import build as hb
+        hb.build(verbose=False)
+    return hw.load()
+
+
+def header_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|const char\*|size_t)\s+(frnn_\w+)\s*\(", text, re.M)))
+
+
+def header_enum(name):
+    m = re.search(rf"\b{name}\s*=\s*(-?\d+)", open(HEADER).read())
+    return int(m.group(1))
+
+
+def test_exports_every_declared_function(lib):
+    funcs = header_functions()
+    assert "frnn_fwd" in funcs and "frnn_lstm_stack_fwd" in funcs and len(funcs) >= 8
+    out = subprocess.run(["nm", "-D", "--defined-only", hw.lib_path()], capture_output=True, text=True, check=True).stdout
+    exported = set(l.split()[-1] for l in out.splitlines() if l.strip())
+    for f in funcs:
+        assert f in exported, f"{f} declared in frnn.h but not exported"
+        assert hasattr(lib, f)
+
+
+def test_abi_version_and_status_strings(lib):
+    m = re.search(r"#define FRNN_ABI_VERSION (\d+)", open(HEADER).read())
+    assert hw.frnn_abi_version() == int(m.group(1))
+    for code in ("FRNN_OK", "FRNN_EINVAL", "FRNN_EUNSUPPORTED", "FRNN_EWORKSPACE", "FRNN_ENORESIDENT", "FRNN_EHIP",
+                 "FRNN_ETIMEOUT", "FRNN_EPLACEMENT", "FRNN_ENODEVICE"):
+        s = hw.frnn_status_str(header_enum(code))
+        assert s and s != "unknown status"
+    assert hw.frnn_status_str(12345) == "unknown status"
+
+
+def D(B=2, T=3, N=1, Dm=64, cell=0, ind=1, outd=0, res=0):
+    return hw.Desc(B, T, N, Dm, cell, ind, outd, res)
+
+
+def ws_bytes(desc, path):
+    n = ctypes.c_size_t(0)
+    rc = hw.load().frnn_workspace_bytes(ctypes.byref(desc), path, ctypes.byref(n))
+    return rc, n.value
+
+
+EINVAL, EUNSUP, EWS = -1, -2, -3
+
+
+@pytest.mark.parametrize("desc,code", [
+    (D(B=0), EINVAL), (D(N=0), EINVAL), (D(Dm=0), EINVAL), (D(T=-1), EINVAL), (D(cell=2), EINVAL),
+    (D(ind=7), EINVAL), (D(outd=9), EINVAL), (D(res=1), EINVAL), (D(outd=1), EUNSUP), (D(Dm=48), EUNSUP),
+    (D(Dm=2048), EUNSUP),
+])
+def test_workspace_bytes_validation(lib, desc, code):
+    for path in (0, 1):
+        assert ws_bytes(desc, path)[0] == code
+    assert ws_bytes(D(), 3)[0] == EINVAL
+
+
+def test_workspace_bytes_independent_of_T(lib):
+    for path in (0, 1):
+        rc1, n1 = ws_bytes(D(B=16, T=1, N=1, Dm=768), path)
+        rc2, n2 = ws_bytes(D(B=16, T=100000, N=1, Dm=768), path)
+        assert rc1 == rc2 == 0 and n1 == n2 > 256
+
+
+def test_fwd_rejects_before_any_device_call(lib):
+    """Every argument error is returned before the library looks for a device."""
+    f = lib.frnn_fwd
+    p = ctypes.c_void_p(0x100000)  # never dereferenced: validation fails first
+    odd = ctypes.c_void_p(0x100002)
+    d = D(B=2, T=3, N=1, Dm=64)
+    need = ws_bytes(d, 1)[1]
+    assert f(None, 1, p, p, None, None, p, p, p, need, None) == EINVAL
+    assert f(ctypes.byref(D(B=0)), 1, p, p, None, None, p, p, p, need, None) == EINVAL
+    assert f(ctypes.byref(d), 1, None, p, None, None, p, p, p, need, None) == EINVAL   # Wx NULL with T > 0
+    assert f(ctypes.byref(d), 1, p, None, None, None, p, p, p, need, None) == EINVAL   # R NULL with T > 0
+    assert f(ctypes.byref(d), 1, odd, p, None, None, p, p, p, need, None) == EINVAL    # misaligned
+    assert f(ctypes.byref(d), 1, p, p, None, None, p, p, None, need, None) == EWS      # no workspace
+    assert f(ctypes.byref(d), 1, p, p, None, None, p, p, p, need - 1, None) == EWS     # too small
+    assert f(ctypes.byref(D(Dm=40)), 1, p, p, None, None, p, p, p, need, None) == EUNSUP
+
+
+def test_stack_validation(lib):
+    n = ctypes.c_size_t(0)
+    g = lib.frnn_lstm_stack_workspace_bytes
+    assert g(2, 512, 32, 512, 512, 1, ctypes.byref(n)) == 0 and n.value > 512 * 32 * 2048 * 4
+    assert g(0, 512, 32, 512, 512, 1, ctypes.byref(n)) == EINVAL
+    assert g(2, 512, 32, 512, 500, 1, ctypes.byref(n)) == EUNSUP
+    arr = ctypes.c_void_p * 2
+    p = ctypes.c_void_p(0x100000)
+    ptrs = arr(0x100000, 0x100000)
+    f = lib.frnn_lstm_stack_fwd
+    assert f(2, 4, 2, 64, 64, 1, p, None, ptrs, None, None, None, None, p, p, p, p, 1 << 30, None) == EINVAL
+    assert f(2, 4, 2, 64, 64, 1, p, ptrs, ptrs, None, None, None, None, p, p, p, p, 16, None) == EWS
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-device answer")
+def test_valid_call_without_device_reports_no_device(lib):
+    d = D(B=2, T=3, N=1, Dm=64)
+    p = ctypes.c_void_p(0x100000)
+    need = ws_bytes(d, 1)[1]
+    assert lib.frnn_fwd(ctypes.byref(d), 1, p, p, None, None, p, p, p, need, None) == header_enum("FRNN_ENODEVICE")
+
+
+def plan(desc, path):
+    return hw.frnn_plan_str(desc, path)
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="planner model of a 256-CU, 8-die device (no GPU here)")
+def test_planner_choices_for_the_workloads(lib):
+    # LSTM D=768 B=16: one head split over the 32 CUs of a die, two batch rows per die
+    s = plan(D(B=16, T=1024, N=1, Dm=768), 1)
+    assert "die-local" in s and "BR=2 " in s and "groups=8 " in s and "W=32 " in s and "KS=4 MTW=6 KTW=6" in s
+    # LSTM D=256 B=8 N=3: four rows per group, six groups
+    s = plan(D(B=8, T=1024, N=3, Dm=256), 1)
+    assert "die-local" in s and "BR=4 " in s and "groups=6 " in s and "W=32 " in s
+    # Elman D=64: a whole head per workgroup
+    s = plan(D(B=64, T=2048, N=12, Dm=64, cell=1), 1)
+    assert "workgroup-local" in s and "groups=48 " in s
+    # fp32 LSTM D=32
+    s = plan(D(B=2, T=16, N=1, Dm=32, ind=0), 1)
+    assert "workgroup-local" in s and "dtype=f32" in s
+    # fp32 beyond the single-workgroup design is not offered on the fused path
+    with pytest.raises(hw.FrnnError):
+        plan(D(B=2, T=16, N=1, Dm=512, ind=0), 1)
+    s = plan(D(B=2, T=16, N=1, Dm=512, ind=0), 0)
+    assert s.startswith("alternating")
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="planner model of a 256-CU, 8-die device (no GPU here)")
+def test_planner_grid_fits_one_workgroup_per_cu(lib):
+    for (B, N, Dm, cell) in [(16, 1, 768, 0), (8, 3, 256, 0), (32, 1, 512, 0), (5, 7, 256, 0), (64, 4, 512, 1),
+                             (1, 1, 1024, 0), (16, 16, 256, 0)]:
+        try:
+            s = plan(D(B=B, T=8, N=N, Dm=Dm, cell=cell), 1)
+        except hw.FrnnError:
+            continue
+        if "die-local" in s:
+            grid = int(re.search(r"grid=(\d+)", s).group(1))
+            slots = int(re.search(r"slots/die=(\d+)", s).group(1))
+            assert grid <= 256 and slots <= 32

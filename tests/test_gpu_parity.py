@@ -1,0 +1,226 @@
+"""HIP path against the fp64 oracle, element by element, on identical seeded inputs.
+
+Tolerances (max abs error on h and c): 1e-4 for fp32 inputs, 3e-2 for bf16 inputs with fp32
+accumulation. Small cases run every row; the full-size workloads run the launch configuration the
+benchmark times and check a sample of (batch, head) rows that the oracle computes one by one.
+"""
+import math
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import frnn_inputs as fi
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+TOL = {torch.float32: 1e-4, torch.bfloat16: 3e-2}
+
+
+def _hw():
+    import head_wise_lstm_amd as hw
+    return hw
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    _hw().load()
+
+
+def _log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def run_case(w, path, pairs=None, env=None):
+    hw = _hw()
+    x = fi.make_inputs(w)
+    dev = torch.device("cuda:0")
+    args = {k: (v.to(dev) if v is not None else None) for k, v in x.items()}
+    old = {}
+    for k, v in (env or {}).items():
+        old[k] = os.environ.get(k)
+        os.environ[k] = str(v)
+    try:
+        _log(f"case {w.name} cell={w.cell} B={w.B} T={w.T} N={w.N} D={w.D} path={path} env={env}")
+        st, last = hw.frnn_fwd(args["Wx"], args["R"], args["b"], args["states0"], cell=w.cell, path=path)
+        torch.cuda.synchronize()
+    finally:
+        for k, v in old.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+    ref_st, ref_last = oracle.headwise_fwd(w.cell, fi.to_f64(x["Wx"]), fi.to_f64(x["R"]), fi.to_f64(x["b"]),
+                                           fi.to_f64(x["states0"]), pairs=pairs)
+    got = st.double().cpu().numpy()
+    gl = last.double().cpu().numpy()
+    if pairs is not None:
+        bs = [p // w.N for p in pairs]
+        ns = [p % w.N for p in pairs]
+        got_s = np.stack([got[:, b, :, n] for b, n in zip(bs, ns)])
+        ref_s = np.stack([ref_st[:, b, :, n] for b, n in zip(bs, ns)])
+        gl_s = np.stack([gl[:, b, :, n] for b, n in zip(bs, ns)])
+        rl_s = np.stack([ref_last[:, b, :, n] for b, n in zip(bs, ns)])
+    else:
+        got_s, ref_s, gl_s, rl_s = got, ref_st, gl, ref_last
+    assert np.all(np.isfinite(got_s))
+    err = np.abs(got_s - ref_s).max() if got_s.size else 0.0
+    err_last = np.abs(gl_s - rl_s).max()
+    _log(f"  max|err| states={err:.3e} last={err_last:.3e}")
+    tol = TOL[w.dtype]
+    assert err <= tol, f"states max abs err {err} > {tol}"
+    assert err_last <= tol
+    # last_states is the final slice of states
+    if w.T > 0:
+        np.testing.assert_array_equal(gl, got[:, :, -1:])
+    return err
+
+
+SMALL = [
+    fi.HeadwiseWorkload("lstm_bf16_ragged_D64", "lstm", torch.bfloat16, B=5, T=13, N=2, D=64, seed=101, s0_var=1.0),
+    fi.HeadwiseWorkload("lstm_bf16_ragged_D96", "lstm", torch.bfloat16, B=19, T=7, N=2, D=96, seed=102, s0_var=0.5),
+    fi.HeadwiseWorkload("lstm_bf16_D256", "lstm", torch.bfloat16, B=9, T=12, N=2, D=256, seed=103, s0_var=1.0, b_var=1.0),
+    fi.HeadwiseWorkload("lstm_bf16_D512", "lstm", torch.bfloat16, B=6, T=6, N=1, D=512, seed=104),
+    fi.HeadwiseWorkload("lstm_bf16_D768", "lstm", torch.bfloat16, B=16, T=5, N=1, D=768, seed=105),
+    fi.HeadwiseWorkload("elman_bf16_ragged_D64", "elman", torch.bfloat16, B=21, T=9, N=3, D=64, seed=106, s0_var=1.0),
+    fi.HeadwiseWorkload("elman_bf16_D128", "elman", torch.bfloat16, B=7, T=10, N=2, D=128, seed=107),
+    fi.HeadwiseWorkload("elman_bf16_D512", "elman", torch.bfloat16, B=3, T=8, N=2, D=512, seed=108, s0_var=1.0),
+    fi.HeadwiseWorkload("lstm_f32_D32", "lstm", torch.float32, B=3, T=11, N=2, D=32, seed=109, s0_var=1.0),
+    fi.HeadwiseWorkload("lstm_f32_D64", "lstm", torch.float32, B=17, T=6, N=1, D=64, seed=110),
+    fi.HeadwiseWorkload("elman_f32_D64", "elman", torch.float32, B=4, T=9, N=3, D=64, seed=111, s0_var=1.0),
+    fi.HeadwiseWorkload("lstm_bf16_T1", "lstm", torch.bfloat16, B=1, T=1, N=1, D=64, seed=112, s0_var=1.0),
+]
+
+
+@pytest.mark.parametrize("path", ["alternating", "fused"])
+@pytest.mark.parametrize("w", SMALL, ids=lambda w: w.name)
+def test_small(w, path):
+    if path == "fused" and w.dtype == torch.float32 and w.D > 64:
+        pytest.skip("fp32 fused covers D <= 64")
+    run_case(w, path)
+
+
+# Die-local multi-workgroup design forced onto small shapes: several workgroups per group,
+# several groups per die, ragged last batch block.
+FORCED = [
+    (fi.HeadwiseWorkload("lstm_forced_W4", "lstm", torch.bfloat16, B=7, T=9, N=3, D=64, seed=121, s0_var=1.0),
+     {"FRNN_FUSED_W": 4, "FRNN_FUSED_BR": 3}),
+    (fi.HeadwiseWorkload("lstm_forced_W8", "lstm", torch.bfloat16, B=11, T=6, N=2, D=128, seed=122, s0_var=1.0),
+     {"FRNN_FUSED_W": 8, "FRNN_FUSED_BR": 5}),
+    (fi.HeadwiseWorkload("elman_forced_W2", "elman", torch.bfloat16, B=9, T=8, N=2, D=64, seed=123, s0_var=1.0),
+     {"FRNN_FUSED_W": 2, "FRNN_FUSED_BR": 4}),
+    (fi.HeadwiseWorkload("lstm_forced_W16_BR16", "lstm", torch.bfloat16, B=16, T=5, N=1, D=256, seed=124),
+     {"FRNN_FUSED_W": 16, "FRNN_FUSED_BR": 16}),
+]
+
+
+@pytest.mark.parametrize("w,env", FORCED, ids=lambda x: getattr(x, "name", ""))
+def test_forced_die_local(w, env):
+    run_case(w, "fused", env=env)
+
+
+def test_t0_returns_initial_state():
+    hw = _hw()
+    dev = torch.device("cuda:0")
+    for path in ("alternating", "fused"):
+        Wx = torch.zeros((3, 0, 4, 2, 64), dtype=torch.bfloat16, device=dev)
+        R = torch.randn((4, 2, 64, 64), device=dev).to(torch.bfloat16)
+        s0 = torch.randn((2, 3, 1, 2, 64), device=dev).to(torch.bfloat16)
+        st, last = hw.frnn_fwd(Wx, R, None, s0, cell="lstm", path=path)
+        assert st.shape == (2, 3, 0, 2, 64)
+        torch.testing.assert_close(last, s0.float(), rtol=0, atol=0)
+        st, last = hw.frnn_fwd(Wx, R, None, None, cell="lstm", path=path)
+        assert torch.count_nonzero(last).item() == 0
+
+
+def test_continuation_matches_single_call():
+    hw = _hw()
+    w = fi.HeadwiseWorkload("cont", "lstm", torch.bfloat16, B=6, T=20, N=2, D=128, seed=131, s0_var=1.0)
+    x = {k: (v.cuda() if v is not None else None) for k, v in fi.make_inputs(w).items()}
+    for path in ("alternating", "fused"):
+        st, last = hw.frnn_fwd(x["Wx"], x["R"], x["b"], x["states0"], cell="lstm", path=path)
+        st1, last1 = hw.frnn_fwd(x["Wx"][:, :8].contiguous(), x["R"], x["b"], x["states0"], cell="lstm", path=path)
+        # the continuation starts from fp32 states rounded to the input dtype, so compare to tolerance
+        st2, last2 = hw.frnn_fwd(x["Wx"][:, 8:].contiguous(), x["R"], x["b"], last1.to(torch.bfloat16), cell="lstm",
+                                 path=path)
+        torch.testing.assert_close(st1, st[:, :, :8], rtol=0, atol=0)
+        assert (st2 - st[:, :, 8:]).abs().max().item() < 3e-2
+
+
+def test_fused_and_alternating_agree():
+    hw = _hw()
+    w = fi.HeadwiseWorkload("agree", "lstm", torch.bfloat16, B=8, T=30, N=2, D=256, seed=141, s0_var=1.0)
+    x = {k: (v.cuda() if v is not None else None) for k, v in fi.make_inputs(w).items()}
+    a, _ = hw.frnn_fwd(x["Wx"], x["R"], x["b"], x["states0"], cell="lstm", path="alternating")
+    f, _ = hw.frnn_fwd(x["Wx"], x["R"], x["b"], x["states0"], cell="lstm", path="fused")
+    assert (a - f).abs().max().item() < 2e-2
+
+
+def test_repeat_calls_reuse_workspace():
+    """Back-to-back calls on one workspace: the exchange buffer holds the previous call's tags."""
+    hw = _hw()
+    w = fi.HeadwiseWorkload("rep", "lstm", torch.bfloat16, B=16, T=17, N=1, D=256, seed=151)
+    x = {k: (v.cuda() if v is not None else None) for k, v in fi.make_inputs(w).items()}
+    d = hw._desc(16, 17, 1, 256, "lstm", torch.bfloat16)
+    ws = torch.empty(hw.frnn_workspace_bytes(d, "fused"), dtype=torch.uint8, device="cuda")
+    outs = [hw.frnn_fwd(x["Wx"], x["R"], x["b"], None, cell="lstm", path="fused", workspace=ws)[0] for _ in range(3)]
+    for o in outs[1:]:
+        torch.testing.assert_close(o, outs[0], rtol=0, atol=0)
+
+
+# ------------------------------------------------------------------ full-size workloads
+FULL_PAIRS = {
+    "lstm_f32_B2_T16_N1_D32": None,
+    "lstm_bf16_B8_T1024_N3_D256": [0, 4, 10, 23],
+    "lstm_bf16_B16_T1024_N1_D768": [0, 5, 15],
+    "elman_bf16_B64_T2048_N12_D64": [0, 13, 250, 511, 767],
+}
+
+
+@pytest.mark.parametrize("path", ["fused", "alternating"])
+@pytest.mark.parametrize("name", list(FULL_PAIRS))
+def test_full_workload(name, path):
+    run_case(fi.WORKLOADS[name], path, pairs=FULL_PAIRS[name])
+
+
+def _stack_case(w, path, rows):
+    hw = _hw()
+    x = fi.make_inputs(w)
+    dev = torch.device("cuda:0")
+    _log(f"stack case {w.name} L={w.L} T={w.T} B={w.B} I={w.I} H={w.H} path={path}")
+    g = lambda t: None if t is None else t.to(dev)
+    out, hn, cn = hw.frnn_lstm_stack_fwd(g(x["x"]), [g(t) for t in x["Wi"]], [g(t) for t in x["Wh"]],
+                                         [g(t) for t in x["b_ih"]], [g(t) for t in x["b_hh"]], g(x["h0"]), g(x["c0"]),
+                                         path=path)
+    torch.cuda.synchronize()
+    f = fi.to_f64
+    sel = lambda a, axis: np.take(a, rows, axis=axis)
+    ro, rh, rc = oracle.lstm_stack_p3(sel(f(x["x"]), 1), [f(t) for t in x["Wi"]], [f(t) for t in x["Wh"]],
+                                      [f(t) for t in x["b_ih"]], [f(t) for t in x["b_hh"]],
+                                      None if x["h0"] is None else sel(f(x["h0"]), 1),
+                                      None if x["c0"] is None else sel(f(x["c0"]), 1))
+    go = sel(out.double().cpu().numpy(), 1)
+    gh = sel(hn.double().cpu().numpy(), 1)
+    gc = sel(cn.double().cpu().numpy(), 1)
+    e = max(np.abs(go - ro).max(), np.abs(gh - rh).max(), np.abs(gc - rc).max())
+    _log(f"  max|err| out/hn/cn = {e:.3e}")
+    assert np.isfinite(e) and e <= 3e-2
+
+
+STACK_SMALL = fi.StackWorkload("stack_small", torch.bfloat16, L=2, T=19, B=10, I=96, H=128, seed=161, zero_init=False)
+
+
+@pytest.mark.parametrize("path", ["fused", "alternating"])
+def test_stack_small(path):
+    _stack_case(STACK_SMALL, path, list(range(STACK_SMALL.B)))
+
+
+@pytest.mark.parametrize("path", ["fused", "alternating"])
+def test_stack_full(path):
+    _stack_case(fi.WORKLOADS["lstm2_bf16_T512_B32_I512_H512"], path, [0, 7, 31])
