@@ -101,34 +101,41 @@ DevInfo default_devinfo() { return DevInfo(); }
 typedef void (*fused_fn)(FusedArgs);
 
 struct FusedVariant {
-  int cell, f32, local, ks, mtw, ktw;
+  int cell, f32, local, ncw, ks, mtw, ktw;
   fused_fn fn;
+  int spills;  // the compiler spills registers for this variant (kept for measurements only)
 };
 
-#define FV(CELL, F32, LOCAL, KS, MTW, KTW) \
-  {CELL, F32, LOCAL, KS, MTW, KTW, &fused_fwd_kernel<CELL, F32, LOCAL, KS, MTW, KTW>}
-#define FV_BOTH_CELLS(F32, LOCAL, KS, MTW, KTW) FV(CELL_LSTM, F32, LOCAL, KS, MTW, KTW), FV(CELL_ELMAN, F32, LOCAL, KS, MTW, KTW)
+#define FV(CELL, F32, LOCAL, NCW, KS, MTW, KTW) \
+  {CELL, F32, LOCAL, NCW, KS, MTW, KTW, &fused_fwd_kernel<CELL, F32, LOCAL, NCW, KS, MTW, KTW>, SPILLS(NCW, KS, MTW, KTW)}
+#define SPILLS(NCW, KS, MTW, KTW) (((NCW) == 4 && (MTW) == 6 && (KTW) == 6) || ((NCW) == 8 && (MTW) == 6 && (KTW) == 3))
+#define FV2(F32, LOCAL, NCW, KS, MTW, KTW) FV(CELL_LSTM, F32, LOCAL, NCW, KS, MTW, KTW), FV(CELL_ELMAN, F32, LOCAL, NCW, KS, MTW, KTW)
 
+// Instantiated designs: (compute waves, K split, tiles per wave, k-tiles per wave). Each fits the
+// register file without spilling at its wave count (checked with -Rpass-analysis).
 const FusedVariant kFused[] = {
     // die-local multi-workgroup design (bf16)
-    FV_BOTH_CELLS(false, false, 4, 1, 1), FV_BOTH_CELLS(false, false, 4, 2, 1), FV_BOTH_CELLS(false, false, 4, 1, 2),
-    FV_BOTH_CELLS(false, false, 4, 2, 2), FV_BOTH_CELLS(false, false, 4, 3, 3), FV_BOTH_CELLS(false, false, 4, 4, 4),
-    FV_BOTH_CELLS(false, false, 4, 6, 6), FV_BOTH_CELLS(false, false, 4, 2, 4), FV_BOTH_CELLS(false, false, 4, 4, 2),
-    FV_BOTH_CELLS(false, false, 4, 4, 1), FV_BOTH_CELLS(false, false, 2, 2, 2),
-    FV_BOTH_CELLS(false, false, 2, 1, 1), FV_BOTH_CELLS(false, false, 2, 2, 1), FV_BOTH_CELLS(false, false, 2, 1, 2),
-    FV_BOTH_CELLS(false, false, 1, 1, 1), FV_BOTH_CELLS(false, false, 1, 1, 2),
+    FV2(false, false, 4, 4, 1, 1), FV2(false, false, 4, 4, 2, 1), FV2(false, false, 4, 4, 1, 2),
+    FV2(false, false, 4, 4, 2, 2), FV2(false, false, 4, 4, 3, 3), FV2(false, false, 4, 4, 4, 4),
+    FV2(false, false, 4, 4, 2, 4), FV2(false, false, 4, 4, 4, 2), FV2(false, false, 4, 4, 4, 1),
+    FV2(false, false, 4, 2, 1, 1), FV2(false, false, 4, 2, 2, 1), FV2(false, false, 4, 2, 1, 2),
+    FV2(false, false, 4, 2, 2, 2), FV2(false, false, 4, 1, 1, 1), FV2(false, false, 4, 1, 1, 2),
+    FV2(false, false, 8, 8, 6, 3), FV2(false, false, 8, 8, 4, 2), FV2(false, false, 8, 8, 2, 1),
+    FV2(false, false, 6, 6, 6, 4), FV2(false, false, 4, 4, 6, 6),
     // single-workgroup design (bf16)
-    FV_BOTH_CELLS(false, true, 1, 1, 1), FV_BOTH_CELLS(false, true, 1, 2, 1), FV_BOTH_CELLS(false, true, 1, 1, 2),
-    FV_BOTH_CELLS(false, true, 1, 4, 2), FV_BOTH_CELLS(false, true, 1, 6, 3), FV_BOTH_CELLS(false, true, 1, 8, 4),
-    FV_BOTH_CELLS(false, true, 1, 2, 4), FV_BOTH_CELLS(false, true, 1, 4, 8), FV_BOTH_CELLS(false, true, 1, 1, 4),
+    FV2(false, true, 4, 1, 1, 1), FV2(false, true, 4, 1, 2, 1), FV2(false, true, 4, 1, 1, 2),
+    FV2(false, true, 4, 1, 4, 2), FV2(false, true, 4, 1, 6, 3), FV2(false, true, 4, 1, 2, 4),
+    FV2(false, true, 4, 1, 1, 4),
     // single-workgroup design (fp32)
-    FV_BOTH_CELLS(true, true, 1, 2, 8), FV_BOTH_CELLS(true, true, 1, 1, 8), FV_BOTH_CELLS(true, true, 1, 4, 16),
-    FV_BOTH_CELLS(true, true, 1, 1, 16),
+    FV2(true, true, 4, 1, 2, 8), FV2(true, true, 4, 1, 1, 8), FV2(true, true, 4, 1, 4, 16),
+    FV2(true, true, 4, 1, 1, 16),
 };
 
-const FusedVariant* find_fused(int cell, int f32, int local, int ks, int mtw, int ktw) {
+const FusedVariant* find_fused(int cell, int f32, int local, int ncw, int ks, int mtw, int ktw) {
   for (const auto& v : kFused)
-    if (v.cell == cell && v.f32 == f32 && v.local == local && v.ks == ks && v.mtw == mtw && v.ktw == ktw) return &v;
+    if (v.cell == cell && v.f32 == f32 && v.local == local && v.ncw == ncw && v.ks == ks && v.mtw == mtw &&
+        v.ktw == ktw)
+      return &v;
   return nullptr;
 }
 
@@ -158,7 +165,7 @@ int gates_of(int cell) { return cell == FRNN_CELL_LSTM ? 4 : 1; }
 
 struct FusedPlan {
   const FusedVariant* v = nullptr;
-  int local = 0, W = 1, BR = 16, groups = 0, ks = 1, mtw = 0, ktw = 0, n_xcd = 1, slots = 0, grid = 0;
+  int local = 0, W = 1, BR = 16, groups = 0, ncw = 4, ks = 1, mtw = 0, ktw = 0, n_xcd = 1, slots = 0, grid = 0;
   size_t lds = 0;
 };
 
@@ -182,22 +189,32 @@ int plan_fused(const Problem& p, const DevInfo& di, FusedPlan* out) {
   const int force_br = env_int("FRNN_FUSED_BR", 0);
   // workgroup-local
   if (force_w <= 1) {
-    const int mtw = (TPH + 3) / 4;
-    const FusedVariant* v = find_fused(p.cell, p.r_f32, 1, 1, mtw, KT);
-    const int per_wave = mtw * KT;
-    if (v && (per_wave <= 64 || force_w == 1)) {
+    for (int ncw : {4, 8}) {
+      const int mtw = (TPH + ncw - 1) / ncw;
+      const FusedVariant* v = find_fused(p.cell, p.r_f32, 1, ncw, 1, mtw, KT);
+      if (!v) continue;
+      const int per_wave = mtw * KT;
+      // the I/O wave moves at most 64 * epl words of Wx and as many output pairs per step
+      const int epl = fused_epl(true, ncw);
+      const int words_per_row = G * p.D / (p.wx_f32 ? 2 : 4);
+      const int br_cap = std::min(16, std::min(64 * epl / words_per_row, 64 * epl * 2 / p.D));
+      if (br_cap < 1 || (per_wave > 64 && force_w != 1)) continue;
       FusedPlan fp;
       fp.v = v;
       fp.local = 1;
       fp.W = 1;
-      fp.BR = (force_br >= 1 && force_br <= 16) ? force_br : 16;
+      // fewest batch rows per workgroup such that the groups still fit one workgroup per CU: the
+      // per-step latency does not depend on the rows, the I/O wave's work per step does
+      int br = 1;
+      while (br < br_cap && (long long)p.N * ((p.B + br - 1) / br) > di.cus) ++br;
+      fp.BR = (force_br >= 1 && force_br <= br_cap) ? force_br : br;
       fp.groups = p.N * ((p.B + fp.BR - 1) / fp.BR);
+      fp.ncw = ncw;
       fp.ks = 1;
       fp.mtw = mtw;
       fp.ktw = KT;
       fp.grid = fp.groups;
-      const int elt = p.r_f32 ? 4 : 2;
-      fp.lds = (size_t)2 * 16 * (p.D + fused_hpad(p.r_f32)) * elt;
+      fp.lds = (size_t)fused_lds(true, p.r_f32, ncw, 1, mtw, p.D).total;
       *out = fp;
       return FRNN_OK;
     }
@@ -209,14 +226,23 @@ int plan_fused(const Problem& p, const DevInfo& di, FusedPlan* out) {
     if (force_w > 1 && W != force_w) continue;
     if (TPH % W) continue;
     const int mt_wg = TPH / W;
-    for (int ks : {4, 2, 1}) {
-      const int ms = 4 / ks;
+    // (compute waves, K split) in order of preference; a spilling variant is only taken when forced
+    const int cand[][2] = {{4, 4}, {6, 6}, {8, 8}, {4, 2}, {8, 4}, {4, 1}, {8, 2}};
+    const int force_ncw = env_int("FRNN_FUSED_NCW", 0), force_ks = env_int("FRNN_FUSED_KS", 0);
+    for (const auto& nk : cand) {
+      const int ncw = nk[0], ks = nk[1];
+      if ((force_ncw && ncw != force_ncw) || (force_ks && ks != force_ks)) continue;
+      const int ms = ncw / ks;
       if (mt_wg % ms || KT % ks) continue;
       const int mtw = mt_wg / ms, ktw = KT / ks;
-      const FusedVariant* v = find_fused(p.cell, 0, 0, ks, mtw, ktw);
+      const FusedVariant* v = find_fused(p.cell, 0, 0, ncw, ks, mtw, ktw);
       if (!v) continue;
+      if (v->spills && !(force_ncw || force_ks)) continue;
+      const int u_wg = mt_wg * (G == 4 ? 4 : 16);
       for (int BR = 1; BR <= 16; ++BR) {
         if (force_br && BR != force_br) continue;
+        const int epl = fused_epl(false, ncw);
+        if (BR * G * u_wg / (p.wx_f32 ? 2 : 4) > 64 * epl || BR * u_wg / 2 > 64 * epl) continue;
         const int groups = p.N * ((p.B + BR - 1) / BR);
         const int per_die = (groups + di.n_xcd - 1) / di.n_xcd;
         if (per_die * W > slots_per_die) continue;
@@ -226,13 +252,14 @@ int plan_fused(const Problem& p, const DevInfo& di, FusedPlan* out) {
         fp.W = W;
         fp.BR = BR;
         fp.groups = groups;
+        fp.ncw = ncw;
         fp.ks = ks;
         fp.mtw = mtw;
         fp.ktw = ktw;
         fp.n_xcd = di.n_xcd;
         fp.slots = per_die * W;
         fp.grid = fp.slots * di.n_xcd;
-        fp.lds = ks > 1 ? (size_t)2 * ks * mt_wg * 64 * 16 : 0;
+        fp.lds = (size_t)fused_lds(false, false, ncw, ks, mtw, p.D).total;
         *out = fp;
         return FRNN_OK;
       }
@@ -274,10 +301,10 @@ std::string plan_string(const Problem& p, int path, const FusedPlan* fp) {
   char buf[512];
   if (path == FRNN_PATH_FUSED && fp) {
     std::snprintf(buf, sizeof(buf),
-                  "fused design=%s cell=%s dtype=%s B=%d T=%d N=%d D=%d BR=%d groups=%d W=%d KS=%d MTW=%d KTW=%d "
+                  "fused design=%s cell=%s dtype=%s B=%d T=%d N=%d D=%d BR=%d groups=%d W=%d NCW=%d KS=%d MTW=%d KTW=%d "
                   "dies=%d slots/die=%d grid=%d lds=%zu",
                   fp->local ? "workgroup-local" : "die-local", p.cell == FRNN_CELL_LSTM ? "lstm" : "elman",
-                  p.r_f32 ? "f32" : "bf16", p.B, p.T, p.N, p.D, fp->BR, fp->groups, fp->W, fp->ks, fp->mtw, fp->ktw,
+                  p.r_f32 ? "f32" : "bf16", p.B, p.T, p.N, p.D, fp->BR, fp->groups, fp->W, fp->ncw, fp->ks, fp->mtw, fp->ktw,
                   fp->n_xcd, fp->slots, fp->grid, fp->lds);
   } else {
     const int G = gates_of(p.cell);
@@ -309,7 +336,8 @@ int run_recurrence(const Problem& p, int path, int* err, void* scratch, hipStrea
     a.B = p.B; a.T = p.T; a.N = p.N; a.D = p.D;
     a.BR = fp.BR; a.groups = fp.groups; a.W = fp.W; a.n_xcd = fp.n_xcd;
     a.check_xcc = fp.local ? 0 : 1;
-    for (int d = 0; d < kMaxDies; ++d) a.xcc_of[d] = di.xcc_of[d];
+    a.xcc_of = 0;
+    for (int d = 0; d < kMaxDies; ++d) a.xcc_of |= (uint32_t)(di.xcc_of[d] & 0xF) << (4 * d);
     a.Wx = p.Wx; a.wx_f32 = p.wx_f32; a.wx_sb = p.wx_sb; a.wx_st = p.wx_st;
     a.R = p.R; a.r_sg = p.r_sg; a.r_sn = p.r_sn; a.r_sd = p.r_sd; a.bias = p.bias;
     a.s0_h = p.s0_h; a.s0_c = p.s0_c; a.s0_f32 = p.s0_f32; a.s0_sb = p.s0_sb;
@@ -318,6 +346,9 @@ int run_recurrence(const Problem& p, int path, int* err, void* scratch, hipStrea
     a.xbuf = reinterpret_cast<uint32_t*>(base);
     a.err = err;
     a.timeout_ticks = (long long)env_int("FRNN_TIMEOUT_MS", 2000) * di.wall_khz;
+#ifdef FRNN_PHASE_TRACE
+    if (const char* tp = std::getenv("FRNN_TRACE_PTR")) a.trace = reinterpret_cast<long long*>(std::strtoull(tp, nullptr, 0));
+#endif
     const void* fn = reinterpret_cast<const void*>(fp.v->fn);
     if (fp.lds > 48 * 1024) {
       if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)fp.lds) != hipSuccess) return FRNN_EHIP;
@@ -325,9 +356,9 @@ int run_recurrence(const Problem& p, int path, int* err, void* scratch, hipStrea
     void* args[] = {&a};
     hipError_t e;
     if (fp.local) {
-      e = hipLaunchKernel(fn, dim3(fp.grid), dim3(256), args, fp.lds, st);
+      e = hipLaunchKernel(fn, dim3(fp.grid), dim3(fused_threads(fp.ncw)), args, fp.lds, st);
     } else {
-      e = hipLaunchCooperativeKernel(fn, dim3(fp.grid), dim3(256), args, (unsigned)fp.lds, st);
+      e = hipLaunchCooperativeKernel(fn, dim3(fp.grid), dim3(fused_threads(fp.ncw)), args, (unsigned)fp.lds, st);
       if (e == hipErrorCooperativeLaunchTooLarge) return FRNN_ENORESIDENT;
     }
     return e == hipSuccess ? FRNN_OK : FRNN_EHIP;
@@ -553,7 +584,7 @@ int frnn_lstm_stack_fwd(int L, int T, int B, int I, int H, int path, const void*
   // the per-layer recurrence plan must exist before anything is enqueued
   Problem probe;
   std::memset(&probe, 0, sizeof(probe));
-  probe.B = B; probe.T = T; probe.N = 1; probe.D = H; probe.cell = FRNN_CELL_LSTM; probe.r_f32 = 0;
+  probe.B = B; probe.T = T; probe.N = 1; probe.D = H; probe.cell = FRNN_CELL_LSTM; probe.r_f32 = 0; probe.wx_f32 = 1;
   if (path == FRNN_PATH_FUSED) {
     FusedPlan fp;
     rc = plan_fused(probe, di, &fp);

@@ -6,20 +6,24 @@
 // sixteen units. W workgroups share a group, each owning MT_WG consecutive tiles; their R^T
 // fragments stay in VGPRs for all T steps (the page's "weights kept in registers").
 //
-// Per step, each of the 4 waves of a workgroup runs MFMA v_mfma_f32_16x16x32_bf16 with
+// Waves. Four compute waves run MFMA v_mfma_f32_16x16x32_bf16 with
 //   A = R^T tile (16 rows x 32 k), B = h^T (32 k x 16 batch columns), D = pre-activations,
 // so that lane l ends up holding all four gates of unit (4*tile + l/16) for batch column l%16:
-// the gate math needs no cross-lane traffic. With KS > 1 the waves split K and the partial sums
-// are added through LDS.
+// the gate math needs no cross-lane traffic. With KS > 1 the compute waves split K and add the
+// partial sums through LDS. A fifth wave does all other global-memory traffic: it streams Wx
+// several steps ahead into an LDS ring and writes the state outputs from an LDS ring two steps
+// behind. On gfx9 a wave's vector-memory counter retires in issue order, so keeping those
+// long-latency accesses out of the compute waves keeps them off the serial chain: a compute wave
+// only ever waits on its own exchange traffic. One workgroup barrier per step orders the rings.
 //
 // h exchange between the W workgroups of a group (W > 1): every group is placed on one
 // accelerator die (XCD), whose L2 is shared by its 32 CUs. A new h value travels as a 32-bit word
 // (bf16 << 16 | step tag) written with a plain store (CU caches are write-through to the die's L2)
 // and is read back with 64-bit agent-scope atomic loads, which bypass the reader's CU cache. Every
-// 32-bit half carries its own tag, so a reader never needs a flag, a fence or a second round trip:
-// a word is either the current step's or it is polled again. Two parities of the buffer alternate
-// by step. Placement is checked against the hardware XCC id; a workgroup on the wrong die reports
-// an error instead of computing. Every wait is bounded by a wall-clock limit.
+// 32-bit half carries its own tag, so a reader needs no flag, fence or second round trip: a word
+// is either the current step's or it is polled again. Two parities of the buffer alternate by
+// step. Placement is checked against the hardware XCC id; a workgroup on the wrong die reports an
+// error instead of computing. Every wait is bounded by a wall-clock limit.
 //
 // With W == 1 ("LOCAL") the whole head sits in one workgroup and h is exchanged through LDS.
 #pragma once
@@ -37,7 +41,7 @@ struct FusedArgs {
   int W;        // workgroups per group (1 for the LDS-local design)
   int n_xcd;    // dies the grid is spread over: workgroup index = slot * n_xcd + die
   int check_xcc;
-  int xcc_of[8];  // expected hardware XCC id of die slot d
+  uint32_t xcc_of;  // expected hardware XCC id of die slot d in bits [4d, 4d+4)
   const void* Wx;
   int wx_f32;
   long long wx_sb, wx_st;  // element strides of Wx for b and t; [G][N][D] packed inside
@@ -57,19 +61,251 @@ struct FusedArgs {
   uint32_t* xbuf;  // exchange words [groups][2][BR][D]
   int* err;
   long long timeout_ticks;  // bound of every wait, in wall-clock (100 MHz) ticks
+  long long* trace;         // phase timestamps (only in builds with FRNN_PHASE_TRACE), or null
 };
 
-// LDS bytes the kernel needs (dynamic shared memory).
-__host__ __device__ constexpr int fused_hpad(bool f32) { return f32 ? 4 : 8; }
+#ifdef FRNN_PHASE_TRACE
+// Shader-clock timestamp of phase `ph` of step t, recorded by lane 0 of compute wave 0 of the
+// first and the last workgroup; at most 4096 steps.
+#define FRNN_TRACE(ph)                                                                          \
+  do {                                                                                          \
+    if (a.trace && lane == 0 && wave == 0 && (blockIdx.x == 0 || blockIdx.x == gridDim.x - 1) && t < 4096) \
+      a.trace[((blockIdx.x == 0 ? 0 : 1) * 4096 + t) * 8 + (ph)] = (long long)clock64();       \
+  } while (0)
+#else
+#define FRNN_TRACE(ph) \
+  do {                 \
+  } while (0)
+#endif
 
-template <int CELL, bool F32, bool LOCAL, int KS, int MTW, int KTW>
-__global__ void __launch_bounds__(256, 1) fused_fwd_kernel(FusedArgs a) {
-  constexpr int MS = 4 / KS;
+constexpr int FUSED_IO_STAGES = 4;   // Wx steps in flight in the I/O wave
+// max 64-bit Wx words (and output pairs) one I/O lane moves per step: the die-local design moves
+// few (its workgroups own few units), the single-workgroup design a whole head's rows
+__host__ __device__ constexpr int fused_epl(bool local, int ncw) { return !local ? 2 : (ncw == 4 ? 8 : 4); }
+
+__host__ __device__ constexpr int fused_hpad(bool f32) { return f32 ? 4 : 8; }
+// gated tiles per compute wave (NCW compute waves, K split KS ways, MTW tiles per wave)
+__host__ __device__ constexpr int fused_gt(int ncw, int ks, int mtw) {
+  return ks == 1 ? mtw : (mtw * (ncw / ks) + ncw - 1) / ncw;
+}
+__host__ __device__ constexpr int fused_threads(int ncw) { return (ncw + 1) * 64; }
+
+struct FusedLds {
+  int h, part, wx, out, total;
+};
+
+// Byte offsets of the LDS regions (identical on host and device).
+__host__ __device__ inline FusedLds fused_lds(bool local, bool f32, int ncw, int ks, int mtw, int D) {
+  FusedLds L;
+  const int gt = fused_gt(ncw, ks, mtw);
+  const int mt_wg = mtw * (ncw / ks);
+  L.h = 0;
+  const int hbytes = local ? 2 * 16 * (D + fused_hpad(f32)) * (f32 ? 4 : 2) : 0;
+  L.part = (hbytes + 15) & ~15;
+  const int pbytes = (!local && ks > 1) ? 2 * ks * mt_wg * 1024 : 0;
+  L.wx = L.part + pbytes;
+  L.out = L.wx + 2 * ncw * gt * 1024;
+  L.total = L.out + 2 * ncw * gt * 1024;
+  return L;
+}
+
+__device__ __forceinline__ void block_barrier() { __syncthreads(); }
+
+
+// ---------------------------------------------------------------------------- I/O wave
+// Everything the I/O wave needs, as plain values (no reference to the kernel argument).
+struct IoCtx {
+  const char* wxb;
+  int wx_f32;
+  long long wx_sb, wx_st;
+  float* out_h;
+  float* out_c;
+  long long out_sb, out_st;
+  int b0, nvalid, n, N, D, T, U_wg, u_base, lane;
+};
+
+// Float index, in slot 0 of an LDS ring, of hidden unit u (local to the workgroup) of batch column
+// b and gate g: the compute lane, wave and gated-tile slot that own it, and the component of the
+// lane's f32x4.
+template <int CELL, int NCW, int KS, int MTW, int GT>
+__device__ __forceinline__ int io_ring_float(int b, int g, int u) {
+  int tq, ln, comp;
+  if (CELL == CELL_LSTM) { tq = u >> 2; ln = b + 16 * (u & 3); comp = g; }
+  else { tq = u >> 4; ln = b + 16 * ((u & 15) >> 2); comp = u & 3; }
+  const int wv = (KS == 1) ? tq / MTW : (tq % NCW);
+  const int q = (KS == 1) ? tq % MTW : (tq / NCW);
+  return ((wv * GT + q) * 64 + ln) * 4 + comp;
+}
+
+// Per-lane descriptors of the I/O wave, computed once. The Wx of one step for the workgroup is
+// nvalid x G x U_wg elements (u fastest), read as 64-bit words (4 bf16 or 2 fp32 each, so that
+// consecutive lanes read consecutive addresses); the outputs of one step are nvalid x U_wg
+// (h and, for the LSTM, c), written as pairs of floats.
+template <int CELL, int NCW, int KS, int MTW, int EPL>
+struct IoDesc {
+  static constexpr int G = (CELL == CELL_LSTM) ? 4 : 1;
+  static constexpr int GT = fused_gt(NCW, KS, MTW);
+  static constexpr int E = EPL;
+  // consecutive units of one word land 16 lanes apart (LSTM) or in consecutive components (Elman)
+  static constexpr int USTEP = (CELL == CELL_LSTM) ? 64 : 1;
+  long long wofs[E];  // byte offset of the word for step 0
+  int wlds[E];        // float index of its first element in slot 0 of the Wx ring (-1: none)
+  long long oofs[E];  // element offset of the output pair for step 0
+  int olds[E];        // float index of its first element in slot 0 of the output ring (-1: none)
+  int epw;            // elements per 64-bit word
+
+  __device__ __forceinline__ void init(const IoCtx& c) {
+    epw = c.wx_f32 ? 2 : 4;
+    const int esz = c.wx_f32 ? 4 : 2;
+    const int wpr = c.U_wg / epw;  // words per (b, g) row of Wx
+    const int ppr = c.U_wg / 2;    // output pairs per row b
+    const int nw = c.nvalid * G * wpr;
+    const int no = c.nvalid * ppr;
+    // word index lane + 64 e, walked incrementally (one division per lane, not per element)
+    int row = c.lane / wpr, uw = c.lane - row * wpr;
+    int orow = c.lane / ppr, ou = c.lane - orow * ppr;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int wi = c.lane + 64 * e;
+      wlds[e] = -1;
+      wofs[e] = 0;
+      if (wi < nw) {
+        const int g = row % G, b = row / G;
+        const int u = uw * epw;
+        wofs[e] = ((long long)(c.b0 + b) * c.wx_sb + (long long)(g * c.N + c.n) * c.D + c.u_base + u) * esz;
+        wlds[e] = io_ring_float<CELL, NCW, KS, MTW, GT>(b, g, u);
+      }
+      olds[e] = -1;
+      oofs[e] = 0;
+      if (wi < no) {
+        const int u = ou * 2;
+        oofs[e] = (long long)(c.b0 + orow) * c.out_sb + (long long)c.n * c.D + c.u_base + u;
+        olds[e] = io_ring_float<CELL, NCW, KS, MTW, GT>(orow, 0, u);
+      }
+      uw += 64;
+      while (uw >= wpr) { uw -= wpr; ++row; }
+      ou += 64;
+      while (ou >= ppr) { ou -= ppr; ++orow; }
+    }
+  }
+};
+
+typedef uint32_t io_word_t __attribute__((ext_vector_type(2)));
+
+template <int CELL, int NCW, int KS, int MTW, int EPL>
+__device__ __forceinline__ void io_issue(const IoCtx& c, const IoDesc<CELL, NCW, KS, MTW, EPL>& d, int s,
+                                         io_word_t (&r)[EPL]) {
+  const long long step = (long long)s * c.wx_st * (c.wx_f32 ? 4 : 2);
+#pragma unroll
+  for (int e = 0; e < EPL; ++e)
+    if (d.wlds[e] >= 0) r[e] = *reinterpret_cast<const io_word_t*>(c.wxb + d.wofs[e] + step);
+}
+
+template <int CELL, int NCW, int KS, int MTW, int EPL>
+__device__ __forceinline__ void io_put(const IoCtx& c, const IoDesc<CELL, NCW, KS, MTW, EPL>& d, int s,
+                                       const io_word_t (&r)[EPL], f32x4_t* wxs) {
+  typedef IoDesc<CELL, NCW, KS, MTW, EPL> Dd;
+  float* wf = reinterpret_cast<float*>(wxs) + (s & 1) * (NCW * Dd::GT * 64 * 4);
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) {
+    const int i = d.wlds[e];
+    if (i >= 0) {
+      if (c.wx_f32) {
+        wf[i] = __uint_as_float(r[e][0]);
+        wf[i + Dd::USTEP] = __uint_as_float(r[e][1]);
+      } else {
+        wf[i] = __uint_as_float(r[e][0] << 16);
+        wf[i + Dd::USTEP] = __uint_as_float(r[e][0] & 0xFFFF0000u);
+        wf[i + 2 * Dd::USTEP] = __uint_as_float(r[e][1] << 16);
+        wf[i + 3 * Dd::USTEP] = __uint_as_float(r[e][1] & 0xFFFF0000u);
+      }
+    }
+  }
+}
+
+template <int CELL, int NCW, int KS, int MTW, int EPL>
+__device__ __forceinline__ void io_store(const IoCtx& c, const IoDesc<CELL, NCW, KS, MTW, EPL>& d, int s, const f32x4_t* outs) {
+  typedef IoDesc<CELL, NCW, KS, MTW, EPL> Dd;
+  const float* of = reinterpret_cast<const float*>(outs) + (s & 1) * (NCW * Dd::GT * 64 * 4);
+  const long long step = (long long)s * c.out_st;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) {
+    const int i = d.olds[e];
+    if (i >= 0) {
+      const long long o = d.oofs[e] + step;
+      // h is component 0 (LSTM, c is component 1) of the owning lane; Elman units are components
+      if (c.out_h) {
+        float2 hv;
+        hv.x = of[i];
+        hv.y = of[i + Dd::USTEP];
+        *reinterpret_cast<float2*>(c.out_h + o) = hv;
+      }
+      if (CELL == CELL_LSTM && c.out_c) {
+        float2 cv;
+        cv.x = of[i + 1];
+        cv.y = of[i + Dd::USTEP + 1];
+        *reinterpret_cast<float2*>(c.out_c + o) = cv;
+      }
+    }
+  }
+}
+
+// One ring stage: interval k writes Wx of step k+1-G0 into LDS (and refills the stage with step
+// k+1-G0+L), stores the outputs of step k-1-G0, then joins the step's barrier.
+template <int CELL, int NCW, int KS, int MTW, int EPL, int G0, int ST>
+__device__ __forceinline__ bool io_interval(const IoCtx& c, const IoDesc<CELL, NCW, KS, MTW, EPL>& d, int k,
+                                            io_word_t (&raw)[FUSED_IO_STAGES][EPL], f32x4_t* wxs,
+                                            const f32x4_t* outs, const int* abort_flag) {
+  constexpr int L = FUSED_IO_STAGES;
+  const int s_wx = k + 1 - G0;
+  if (s_wx >= 0 && s_wx < c.T) {
+    io_put<CELL, NCW, KS, MTW, EPL>(c, d, s_wx, raw[ST], wxs);
+    if (s_wx + L < c.T) io_issue<CELL, NCW, KS, MTW, EPL>(c, d, s_wx + L, raw[ST]);
+  }
+  const int s_out = k - 1 - G0;
+  if (s_out >= 0 && s_out < c.T) io_store<CELL, NCW, KS, MTW, EPL>(c, d, s_out, outs);
+  block_barrier();
+  return *abort_flag != 0;
+}
+
+// The I/O wave: runs barriers -1 .. T in step with the compute waves (see the kernel).
+template <int CELL, int NCW, int KS, int MTW, int EPL, int G0>
+__device__ __forceinline__ void io_wave(const IoCtx& c, f32x4_t* wxs, const f32x4_t* outs, const int* abort_flag) {
+  constexpr int L = FUSED_IO_STAGES;
+  static_assert(L == 4, "the interval loop below is unrolled for four stages");
+  IoDesc<CELL, NCW, KS, MTW, EPL> d;
+  d.init(c);
+  io_word_t raw[L][EPL];
+  if (0 < c.T) io_issue<CELL, NCW, KS, MTW, EPL>(c, d, 0, raw[0]);
+  if (1 < c.T) io_issue<CELL, NCW, KS, MTW, EPL>(c, d, 1, raw[1]);
+  if (2 < c.T) io_issue<CELL, NCW, KS, MTW, EPL>(c, d, 2, raw[2]);
+  if (3 < c.T) io_issue<CELL, NCW, KS, MTW, EPL>(c, d, 3, raw[3]);
+  // k runs -1 .. T; the stage of the Wx step written in interval k is (k + 1 - G0) mod 4.
+  constexpr int S0 = ((0 - G0) % L + L) % L, S1 = ((1 - G0) % L + L) % L;
+  constexpr int S2 = ((2 - G0) % L + L) % L, S3 = ((3 - G0) % L + L) % L;
+  for (int kb = -1; kb <= c.T; kb += L) {
+    if (io_interval<CELL, NCW, KS, MTW, EPL, G0, S0>(c, d, kb, raw, wxs, outs, abort_flag)) return;
+    if (kb + 1 > c.T) break;
+    if (io_interval<CELL, NCW, KS, MTW, EPL, G0, S1>(c, d, kb + 1, raw, wxs, outs, abort_flag)) return;
+    if (kb + 2 > c.T) break;
+    if (io_interval<CELL, NCW, KS, MTW, EPL, G0, S2>(c, d, kb + 2, raw, wxs, outs, abort_flag)) return;
+    if (kb + 3 > c.T) break;
+    if (io_interval<CELL, NCW, KS, MTW, EPL, G0, S3>(c, d, kb + 3, raw, wxs, outs, abort_flag)) return;
+  }
+  if (G0 == 1 && c.T >= 1) io_store<CELL, NCW, KS, MTW, EPL>(c, d, c.T - 1, outs);
+}
+
+template <int CELL, bool F32, bool LOCAL, int NCW, int KS, int MTW, int KTW>
+__global__ void __launch_bounds__((NCW + 1) * 64, 1) fused_fwd_kernel(FusedArgs a) {
+  constexpr int NT = (NCW + 1) * 64;
+  constexpr int MS = NCW / KS;
   constexpr int MT_WG = MTW * MS;
   constexpr int KW = F32 ? 4 : 32;
-  constexpr int GT = (KS == 1) ? MTW : (MT_WG + 3) / 4;
+  constexpr int GT = fused_gt(NCW, KS, MTW);
   constexpr int G = (CELL == CELL_LSTM) ? 4 : 1;
-  static_assert(KS == 1 || KS == 2 || KS == 4, "KS");
+  constexpr int UPT = (CELL == CELL_LSTM) ? 4 : 16;  // hidden units per tile
+  constexpr int G0 = LOCAL ? 0 : 1;                  // gating of step s happens in interval s + G0
+  static_assert((NCW == 4 || NCW == 6 || NCW == 8) && NCW % KS == 0, "compute waves / K split");
   static_assert(!(F32 && !LOCAL), "fp32 runs only in the workgroup-local design");
   static_assert(!(LOCAL && KS != 1), "the workgroup-local design does not split K");
   typedef typename std::conditional<F32, float, bf16x8_t>::type frag_t;
@@ -78,7 +314,6 @@ __global__ void __launch_bounds__(256, 1) fused_fwd_kernel(FusedArgs a) {
   __shared__ int s_abort;
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int ks = wave % KS, ms = wave / KS;
   const int col = lane & 15, quad = lane >> 4;
   const int D = a.D, N = a.N, T = a.T;
   const int TPH = (G * D) / 16;
@@ -92,7 +327,7 @@ __global__ void __launch_bounds__(256, 1) fused_fwd_kernel(FusedArgs a) {
     group = (slot / a.W) * a.n_xcd + die;
     w = slot % a.W;
     if (group >= a.groups) return;
-    if (a.check_xcc && xcc_id() != a.xcc_of[die]) {
+    if (a.check_xcc && xcc_id() != (int)((a.xcc_of >> (4 * die)) & 0xFu)) {
       if (threadIdx.x == 0) atomicOr(a.err, DEVERR_PLACEMENT);
       return;
     }
@@ -104,6 +339,56 @@ __global__ void __launch_bounds__(256, 1) fused_fwd_kernel(FusedArgs a) {
   const int b0 = bblk * a.BR;
   const int nvalid = min(a.BR, a.B - b0);
   const int tile0 = w * MT_WG;
+  const FusedLds lay = fused_lds(LOCAL, F32, NCW, KS, MTW, D);
+  constexpr int HPAD = fused_hpad(F32);
+  const int HS = D + HPAD;  // row stride of the LDS h buffer (elements)
+  float* hbuf_f = reinterpret_cast<float*>(smem + lay.h);
+  uint16_t* hbuf_b = reinterpret_cast<uint16_t*>(smem + lay.h);
+  f32x4_t* part = reinterpret_cast<f32x4_t*>(smem + lay.part);
+  f32x4_t* wxs = reinterpret_cast<f32x4_t*>(smem + lay.wx);
+  f32x4_t* outs = reinterpret_cast<f32x4_t*>(smem + lay.out);
+
+  // zero the Wx ring (lanes of padding batch columns read zeros) and, for LOCAL, write
+  // h_{-1} (the initial state) into parity 1 of the LDS h buffer
+  for (int i = threadIdx.x; i < 2 * NCW * GT * 64; i += NT) wxs[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  if (LOCAL) {
+    for (int idx = threadIdx.x; idx < 16 * D; idx += NT) {
+      const int c = idx / D, k = idx - c * D;
+      float v = 0.0f;
+      if (a.s0_h && c < nvalid) v = ld_f(a.s0_h, (long long)(b0 + c) * a.s0_sb + (long long)n * D + k, a.s0_f32);
+      if (F32) hbuf_f[(1 * 16 + c) * HS + k] = v;
+      else hbuf_b[(1 * 16 + c) * HS + k] = f2bf(v);
+    }
+  }
+
+  const int u_base = tile0 * UPT;                   // first hidden unit of this workgroup
+  const int U_wg = min(MT_WG * UPT, D - u_base);    // its hidden units (the last tiles may be idle)
+
+  if (wave == NCW) {
+    IoCtx c;
+    c.wxb = reinterpret_cast<const char*>(a.Wx);
+    c.wx_f32 = a.wx_f32;
+    c.wx_sb = a.wx_sb;
+    c.wx_st = a.wx_st;
+    c.out_h = a.out_h;
+    c.out_c = a.out_c;
+    c.out_sb = a.out_sb;
+    c.out_st = a.out_st;
+    c.b0 = b0;
+    c.nvalid = nvalid;
+    c.n = n;
+    c.N = N;
+    c.D = D;
+    c.T = T;
+    c.U_wg = U_wg;
+    c.u_base = u_base;
+    c.lane = lane;
+    io_wave<CELL, NCW, KS, MTW, fused_epl(LOCAL, NCW), G0>(c, wxs, outs, &s_abort);
+    return;
+  }
+
+  // ==================================================================== compute waves
+  const int ks = wave % KS, ms = wave / KS;
   const bool colv = col < nvalid;
   const long long bcol = b0 + col;
   const bool r_f32 = F32;
@@ -138,22 +423,19 @@ __global__ void __launch_bounds__(256, 1) fused_fwd_kernel(FusedArgs a) {
     }
   }
 
-  // ---- tiles this wave applies the gates to, their bias, initial c and Wx.
-  int gu[GT];       // LSTM: the lane's unit; Elman: first of the lane's four units
+  // ---- tiles this wave applies the gates to, their bias and initial c.
+  int gu[GT];  // LSTM: the lane's unit; Elman: first of the lane's four units
   bool gval[GT];
-  float bia[GT][4], wxv[GT][4], creg[GT];
+  float bia[GT][4], creg[GT];
 #pragma unroll
   for (int q = 0; q < GT; ++q) {
-    const int tq = (KS == 1) ? ms * MTW + q : wave + 4 * q;
+    const int tq = (KS == 1) ? ms * MTW + q : wave + NCW * q;
     const int tt = tile0 + tq;
     gval[q] = (tq < MT_WG) && (tt < TPH);
     gu[q] = (CELL == CELL_LSTM) ? 4 * tt + quad : 16 * tt + 4 * quad;
     creg[q] = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      bia[q][i] = 0.0f;
-      wxv[q][i] = 0.0f;
-    }
+    for (int i = 0; i < 4; ++i) bia[q][i] = 0.0f;
     if (gval[q]) {
       if (a.bias) {
 #pragma unroll
@@ -166,51 +448,31 @@ __global__ void __launch_bounds__(256, 1) fused_fwd_kernel(FusedArgs a) {
         creg[q] = ld_f(a.s0_c, bcol * a.s0_sb + (long long)n * D + gu[q], a.s0_f32);
     }
   }
-  auto load_wx = [&](int t) {
-#pragma unroll
-    for (int q = 0; q < GT; ++q) {
-      if (gval[q] && colv) {
-        const long long base = bcol * a.wx_sb + (long long)t * a.wx_st;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const long long off = (CELL == CELL_LSTM) ? (long long)(i * N + n) * D + gu[q] : (long long)n * D + gu[q] + i;
-          wxv[q][i] = ld_f(a.Wx, base + off, a.wx_f32);
-        }
-      }
-    }
-  };
+  block_barrier();  // barrier -1
 
-  // ---- LDS layout.
-  constexpr int HPAD = fused_hpad(F32);
-  const int HS = D + HPAD;  // row stride of the LDS h buffer (elements)
-  float* hbuf_f = reinterpret_cast<float*>(smem);
-  uint16_t* hbuf_b = reinterpret_cast<uint16_t*>(smem);
-  f32x4_t* part = reinterpret_cast<f32x4_t*>(smem);
-
-  if (LOCAL) {
-    // h_{-1} (the initial state) goes to parity 1.
-    for (int idx = threadIdx.x; idx < 16 * D; idx += 256) {
-      const int c = idx / D, k = idx - c * D;
-      float v = 0.0f;
-      if (a.s0_h && c < nvalid) v = ld_f(a.s0_h, (long long)(b0 + c) * a.s0_sb + (long long)n * D + k, a.s0_f32);
-      if (F32) hbuf_f[(1 * 16 + c) * HS + k] = v;
-      else hbuf_b[(1 * 16 + c) * HS + k] = f2bf(v);
-    }
-  }
-  load_wx(0);
-  __syncthreads();
-
-  const long long xgroup = (long long)group * 2 * a.BR * D;
+  // exchange words of this group: uniform base (scalar registers) plus 32-bit lane offsets
+  uint32_t* const xb = a.xbuf + (long long)group * 2 * a.BR * D;
+  const int xpar = a.BR * D;  // words per parity
+  float hlast[GT][4];         // h of the last step, written out after the loop
 
   for (int t = 0; t < T; ++t) {
-    frag_t Bf[KTW];
-    // ---- 1. h_{t-1} as the B operand.
+    FRNN_TRACE(0);
+    // ---- 1+2. h_{t-1} as the B operand, multiplied on MFMA as each k-tile becomes available.
+    f32x4_t acc[MTW];
+#pragma unroll
+    for (int j = 0; j < MTW; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     if (LOCAL) {
       const int p = (t + 1) & 1;
 #pragma unroll
       for (int kk = 0; kk < KTW; ++kk) {
-        if constexpr (F32) Bf[kk] = hbuf_f[(p * 16 + col) * HS + kk * KW + quad];
-        else Bf[kk] = *reinterpret_cast<const bf16x8_t*>(&hbuf_b[(p * 16 + col) * HS + kk * KW + 8 * quad]);
+        frag_t bk;
+        if constexpr (F32) bk = hbuf_f[(p * 16 + col) * HS + kk * KW + quad];
+        else bk = *reinterpret_cast<const bf16x8_t*>(&hbuf_b[(p * 16 + col) * HS + kk * KW + 8 * quad]);
+#pragma unroll
+        for (int j = 0; j < MTW; ++j) {
+          if constexpr (F32) acc[j] = mfma_f32(Ra[j][kk], bk, acc[j]);
+          else acc[j] = mfma_bf16(Ra[j][kk], bk, acc[j]);
+        }
       }
     } else if constexpr (!F32) {
       if (t == 0) {
@@ -226,19 +488,24 @@ __global__ void __launch_bounds__(256, 1) fused_fwd_kernel(FusedArgs a) {
               pk[i] = lo | (hi << 16);
             }
           }
-          Bf[kk] = __builtin_bit_cast(bf16x8_t, pk);
+          const bf16x8_t bk = __builtin_bit_cast(bf16x8_t, pk);
+#pragma unroll
+          for (int j = 0; j < MTW; ++j) acc[j] = mfma_bf16(Ra[j][kk], bk, acc[j]);
         }
       } else {
         const int pp = (t - 1) & 1;
         const uint32_t tag = (uint32_t)t & 0xFFFFu;
-        const uint32_t* rowp = a.xbuf + xgroup + ((long long)pp * a.BR + col) * D + 8 * quad;
-        uint32_t pend = colv ? ((1u << KTW) - 1u) : 0u;
+        const uint32_t* rowp = xb + (pp * xpar + col * D + 8 * quad);
+        constexpr uint32_t ALL = (1u << KTW) - 1u;
+        uint32_t pend = colv ? ALL : 0u;  // per lane: k-tiles whose words are not yet this step's
+        uint32_t done = 0;                // wave-uniform: k-tiles already multiplied
         uint64_t v[KTW][4];
 #pragma unroll
-        for (int kk = 0; kk < KTW; ++kk) Bf[kk] = __builtin_bit_cast(bf16x8_t, u32x4_t{0u, 0u, 0u, 0u});
+        for (int kk = 0; kk < KTW; ++kk)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v[kk][i] = 0;  // padding columns multiply zeros
         long long t_first = 0;
         int spins = 0;
-        bool dead = false;
         while (true) {
 #pragma unroll
           for (int kk = 0; kk < KTW; ++kk) {
@@ -254,114 +521,95 @@ __global__ void __launch_bounds__(256, 1) fused_fwd_kernel(FusedArgs a) {
             if (pend & (1u << kk)) {
               uint32_t bad = 0;
 #pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                const uint32_t lo = (uint32_t)v[kk][i], hi = (uint32_t)(v[kk][i] >> 32);
-                bad |= ((lo ^ tag) | (hi ^ tag)) & 0xFFFFu;
-              }
-              if (bad == 0) {
-                u32x4_t pk;
+              for (int i = 0; i < 4; ++i) bad |= (((uint32_t)v[kk][i] ^ tag) | ((uint32_t)(v[kk][i] >> 32) ^ tag)) & 0xFFFFu;
+              if (bad == 0) pend &= ~(1u << kk);
+            }
+            // multiply k-tile kk once no lane of the wave waits for it and every earlier k-tile is
+            // done: a fixed accumulation order keeps the results bitwise reproducible
+            if (done == (1u << kk) - 1u && !__any((pend >> kk) & 1u)) {
+              u32x4_t pk;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) pk[i] = pack_hi((uint32_t)v[kk][i], (uint32_t)(v[kk][i] >> 32));
-                Bf[kk] = __builtin_bit_cast(bf16x8_t, pk);
-                pend &= ~(1u << kk);
-              }
+              for (int i = 0; i < 4; ++i) pk[i] = pack_hi((uint32_t)v[kk][i], (uint32_t)(v[kk][i] >> 32));
+              const bf16x8_t bk = __builtin_bit_cast(bf16x8_t, pk);
+#pragma unroll
+              for (int j = 0; j < MTW; ++j) acc[j] = mfma_bf16(Ra[j][kk], bk, acc[j]);
+              done |= 1u << kk;
             }
           }
-          if (!__any(pend != 0u)) break;
+          if (done == ALL) break;
           if ((++spins & 63) == 0) {
             const long long now = (long long)wall_clock64();
             if (t_first == 0) t_first = now;
             if (now - t_first > a.timeout_ticks ||
                 __hip_atomic_load(a.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) {
               if (lane == 0) atomicOr(a.err, DEVERR_TIMEOUT);
-              dead = true;
+              s_abort = 1;  // every wave leaves after the next barrier
               break;
             }
           }
         }
-        if (dead) {
-          if (KS == 1) return;  // no workgroup barrier in this loop: leave directly
-          s_abort = 1;
-        }
       }
     }
+    FRNN_TRACE(1);
 
-    // ---- 2. recurrent contraction on MFMA.
-    f32x4_t acc[MTW];
-#pragma unroll
-    for (int j = 0; j < MTW; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kk = 0; kk < KTW; ++kk) {
-#pragma unroll
-      for (int j = 0; j < MTW; ++j) {
-        if constexpr (F32) acc[j] = mfma_f32(Ra[j][kk], Bf[kk], acc[j]);
-        else acc[j] = mfma_bf16(Ra[j][kk], Bf[kk], acc[j]);
-      }
-    }
-
-    // ---- 3. K-split partial sums through LDS.
+    // ---- 3. (die-local design) the step's barrier; K-split partial sums through LDS.
     f32x4_t pre[GT];
     if constexpr (KS == 1) {
 #pragma unroll
       for (int q = 0; q < GT; ++q) pre[q] = acc[q];
+      if (!LOCAL) {
+        block_barrier();
+        if (s_abort) return;
+      }
     } else {
       const int pp = t & 1;
 #pragma unroll
       for (int j = 0; j < MTW; ++j) part[((pp * KS + ks) * MT_WG + ms * MTW + j) * 64 + lane] = acc[j];
-      __syncthreads();
+      FRNN_TRACE(2);
+      block_barrier();
+      FRNN_TRACE(3);
       if (s_abort) return;
 #pragma unroll
       for (int q = 0; q < GT; ++q) {
         pre[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         if (gval[q]) {
-          const int tq = wave + 4 * q;
+          const int tq = wave + NCW * q;
 #pragma unroll
           for (int k2 = 0; k2 < KS; ++k2) pre[q] += part[((pp * KS + k2) * MT_WG + tq) * 64 + lane];
         }
       }
     }
 
-    // ---- 4. gates, state update, outputs, exchange.
+    FRNN_TRACE(4);
+    // ---- 4. gates, state update, exchange; outputs go to the LDS ring for the I/O wave.
     const uint32_t wtag = (uint32_t)(t + 1) & 0xFFFFu;
 #pragma unroll
     for (int q = 0; q < GT; ++q) {
       if (!gval[q]) continue;
+      const int ri = (((t & 1) * NCW + wave) * GT + q) * 64 + lane;
+      const f32x4_t wx4 = wxs[ri];
       if constexpr (CELL == CELL_LSTM) {
-        const float ig = sigmoid_f(pre[q][0] + wxv[q][0] + bia[q][0]);
-        const float fg = sigmoid_f(pre[q][1] + wxv[q][1] + bia[q][1]);
-        const float zg = tanh_f(pre[q][2] + wxv[q][2] + bia[q][2]);
-        const float og = sigmoid_f(pre[q][3] + wxv[q][3] + bia[q][3]);
+        const float ig = sigmoid_f(pre[q][0] + wx4[0] + bia[q][0]);
+        const float fg = sigmoid_f(pre[q][1] + wx4[1] + bia[q][1]);
+        const float zg = tanh_f(pre[q][2] + wx4[2] + bia[q][2]);
+        const float og = sigmoid_f(pre[q][3] + wx4[3] + bia[q][3]);
         const float c = fg * creg[q] + ig * zg;
         creg[q] = c;
         const float h = og * tanh_f(c);
         const int u = gu[q];
-        if (colv) {
-          const long long o = bcol * a.out_sb + (long long)t * a.out_st + (long long)n * D + u;
-          if (a.out_h) a.out_h[o] = h;
-          if (a.out_c) a.out_c[o] = c;
-          if (t == T - 1) {
-            const long long lo = bcol * a.last_sb + (long long)n * D + u;
-            if (a.last_h) a.last_h[lo] = h;
-            if (a.last_c) a.last_c[lo] = c;
-          }
-        }
         if (LOCAL) {
           if constexpr (F32) hbuf_f[((t & 1) * 16 + col) * HS + u] = h;
           else hbuf_b[((t & 1) * 16 + col) * HS + u] = f2bf(h);
         } else if (colv) {
-          a.xbuf[xgroup + ((long long)(t & 1) * a.BR + col) * D + u] = ((uint32_t)f2bf(h) << 16) | wtag;
+          xb[(t & 1) * xpar + col * D + u] = ((uint32_t)f2bf(h) << 16) | wtag;
         }
+        outs[ri] = f32x4_t{h, c, 0.f, 0.f};
+        hlast[q][0] = h;
       } else {
         float h[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) h[i] = tanh_f(pre[q][i] + wxv[q][i] + bia[q][i]);
+        for (int i = 0; i < 4; ++i) h[i] = tanh_f(pre[q][i] + wx4[i] + bia[q][i]);
         const int u = gu[q];
-        if (colv) {
-          const long long o = bcol * a.out_sb + (long long)t * a.out_st + (long long)n * D + u;
-          if (a.out_h) *reinterpret_cast<f32x4_t*>(a.out_h + o) = f32x4_t{h[0], h[1], h[2], h[3]};
-          if (t == T - 1 && a.last_h)
-            *reinterpret_cast<f32x4_t*>(a.last_h + bcol * a.last_sb + (long long)n * D + u) = f32x4_t{h[0], h[1], h[2], h[3]};
-        }
         if (LOCAL) {
           if constexpr (F32) {
             *reinterpret_cast<f32x4_t*>(&hbuf_f[((t & 1) * 16 + col) * HS + u]) = f32x4_t{h[0], h[1], h[2], h[3]};
@@ -373,14 +621,32 @@ __global__ void __launch_bounds__(256, 1) fused_fwd_kernel(FusedArgs a) {
           u32x4_t wv;
 #pragma unroll
           for (int i = 0; i < 4; ++i) wv[i] = ((uint32_t)f2bf(h[i]) << 16) | wtag;
-          *reinterpret_cast<u32x4_t*>(a.xbuf + xgroup + ((long long)(t & 1) * a.BR + col) * D + u) = wv;
+          *reinterpret_cast<u32x4_t*>(xb + ((t & 1) * xpar + col * D + u)) = wv;
         }
+        outs[ri] = f32x4_t{h[0], h[1], h[2], h[3]};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) hlast[q][i] = h[i];
       }
     }
+    FRNN_TRACE(5);
     // Keep the exchange stores ahead of the next step's polling in program order.
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    if (t + 1 < T) load_wx(t + 1);
-    if (LOCAL) __syncthreads();
+    if (LOCAL) block_barrier();
+  }
+  block_barrier();  // barrier T: the last step's outputs are in LDS for the I/O wave
+  // last_states: the state after the last step, straight from registers
+  if (T > 0 && colv) {
+#pragma unroll
+    for (int q = 0; q < GT; ++q) {
+      if (!gval[q]) continue;
+      const long long lo = bcol * a.last_sb + (long long)n * D + gu[q];
+      if constexpr (CELL == CELL_LSTM) {
+        if (a.last_h) a.last_h[lo] = hlast[q][0];
+        if (a.last_c) a.last_c[lo] = creg[q];
+      } else if (a.last_h) {
+        *reinterpret_cast<f32x4_t*>(a.last_h + lo) = f32x4_t{hlast[q][0], hlast[q][1], hlast[q][2], hlast[q][3]};
+      }
+    }
   }
 }
 

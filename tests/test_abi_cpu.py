@@ -131,13 +131,15 @@ def plan(desc, path):
 def test_planner_choices_for_the_workloads(lib):
     # LSTM D=768 B=16: one head split over the 32 CUs of a die, two batch rows per die
     s = plan(D(B=16, T=1024, N=1, Dm=768), 1)
-    assert "die-local" in s and "BR=2 " in s and "groups=8 " in s and "W=32 " in s and "KS=4 MTW=6 KTW=6" in s
+    assert "die-local" in s and "BR=2 " in s and "groups=8 " in s and "W=32 " in s
+    # R^T of a 32-CU slice (147 KB) must stay in registers: no variant that spills is chosen
+    assert "NCW=6 KS=6 MTW=6 KTW=4" in s
     # LSTM D=256 B=8 N=3: four rows per group, six groups
     s = plan(D(B=8, T=1024, N=3, Dm=256), 1)
     assert "die-local" in s and "BR=4 " in s and "groups=6 " in s and "W=32 " in s
-    # Elman D=64: a whole head per workgroup
+    # Elman D=64: a whole head per workgroup, four batch rows each so that 192 workgroups fill the CUs
     s = plan(D(B=64, T=2048, N=12, Dm=64, cell=1), 1)
-    assert "workgroup-local" in s and "groups=48 " in s
+    assert "workgroup-local" in s and "BR=4 " in s and "groups=192 " in s
     # fp32 LSTM D=32
     s = plan(D(B=2, T=16, N=1, Dm=32, ind=0), 1)
     assert "workgroup-local" in s and "dtype=f32" in s

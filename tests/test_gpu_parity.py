@@ -115,8 +115,12 @@ FORCED = [
      {"FRNN_FUSED_W": 8, "FRNN_FUSED_BR": 5}),
     (fi.HeadwiseWorkload("elman_forced_W2", "elman", torch.bfloat16, B=9, T=8, N=2, D=64, seed=123, s0_var=1.0),
      {"FRNN_FUSED_W": 2, "FRNN_FUSED_BR": 4}),
-    (fi.HeadwiseWorkload("lstm_forced_W16_BR16", "lstm", torch.bfloat16, B=16, T=5, N=1, D=256, seed=124),
-     {"FRNN_FUSED_W": 16, "FRNN_FUSED_BR": 16}),
+    (fi.HeadwiseWorkload("lstm_forced_W16_BR8", "lstm", torch.bfloat16, B=16, T=5, N=1, D=256, seed=124),
+     {"FRNN_FUSED_W": 16, "FRNN_FUSED_BR": 8}),
+    (fi.HeadwiseWorkload("lstm_D768_8waves", "lstm", torch.bfloat16, B=16, T=9, N=1, D=768, seed=125, s0_var=1.0),
+     {"FRNN_FUSED_NCW": 8}),
+    (fi.HeadwiseWorkload("lstm_D768_4waves", "lstm", torch.bfloat16, B=16, T=9, N=1, D=768, seed=126, s0_var=1.0),
+     {"FRNN_FUSED_NCW": 4}),
 ]
 
 
