@@ -70,7 +70,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="lstm_bf16_B16_T1024_N1_D768")
     ap.add_argument("--path", default="fused", choices=["fused", "alternating"])
-    ap.add_argument("--cpu-sample-T", type=int, default=128)
+    ap.add_argument("--cpu-sample-T", type=int, default=0, help="timesteps of the CPU-baseline sample (0 = all)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (read MIB, write MIB), five times, for "
+                         "scaling the HBM byte counters, and exit")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="per-launch HBM bytes measured with rocprofv3 counters for this workload/path")
@@ -81,6 +84,17 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.copy_calibration:
+        n = args.copy_calibration * (1 << 20) // 4
+        src = torch.randn(n, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_mib": args.copy_calibration, "launches": 5,
+                          "bytes_read_per_launch": n * 4, "bytes_written_per_launch": n * 4}))
+        return
 
     import frnn_inputs as fi
     import head_wise_lstm_amd as hw
@@ -157,12 +171,18 @@ def main():
     if nbytes:
         roof["algorithmic_bytes"] = nbytes
         roof["hbm_frac"] = nbytes / sec / 1e9 / PEAK_HBM_GBS
+    # HBM bytes per launch counted by rocprofv3 (FETCH_SIZE + WRITE_SIZE, calibrated on a plain
+    # copy), valid only for the kernel source they were taken on
     try:
+        import hashlib
         with open(args.traffic_json) as f:
             tj = json.load(f).get(f"{config['workload']}:{args.path}")
-        if tj:
+        src = os.path.join(ROOT, "head_wise_lstm_amd", "csrc", "frnn_fused.hpp")
+        cur = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+        if tj and tj.get("kernel_source_sha256_16") == cur:
             roof["traffic"] = tj["bytes_per_launch"]
-    except (OSError, ValueError):
+            roof["traffic_over_algorithmic"] = tj["bytes_per_launch"] / tj["algorithmic_bytes"]
+    except (OSError, ValueError, KeyError):
         pass
     res = {"metric": METRIC, "value": tflops, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
@@ -170,7 +190,7 @@ def main():
            "config": config, "us_per_timestep": ms * 1e3 / timesteps,
            "pct_mfma_bf16_peak": 100.0 * tflops / PEAK_BF16_TFLOPS, "wall_s_timed": wall, "roofline": roof}
     if not args.no_cpu_baseline and isinstance(w, fi.HeadwiseWorkload):
-        res["cpu_baseline"] = cpu_baseline(w, min(args.cpu_sample_T, w.T))
+        res["cpu_baseline"] = cpu_baseline(w, min(args.cpu_sample_T or w.T, w.T))
     print(json.dumps(res), flush=True)
 
 
