@@ -239,7 +239,7 @@ int plan_fused(const Problem& p, const DevInfo& di, FusedPlan* out) {
       if (!v) continue;
       if (v->spills && !(force_ncw || force_ks)) continue;
       const int u_wg = mt_wg * (G == 4 ? 4 : 16);
-      for (int BR = 1; BR <= 16; ++BR) {
+      for (int BR = 1; BR <= FUSED_DIE_MAX_BR; ++BR) {
         if (force_br && BR != force_br) continue;
         const int epl = fused_epl(false, ncw);
         if (BR * G * u_wg / (p.wx_f32 ? 2 : 4) > 64 * epl || BR * u_wg / 2 > 64 * epl) continue;

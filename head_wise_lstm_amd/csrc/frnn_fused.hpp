@@ -95,12 +95,19 @@ struct FusedLds {
 };
 
 // Byte offsets of the LDS regions (identical on host and device).
+// Words (32-bit, two bf16 units each) per row of a compute wave's poll stage, padded by 16 bytes.
+__host__ __device__ constexpr int fused_stage_row(int ktw) { return ktw * 16 + 4; }
+// Batch rows per group of the die-local design (bounds the polling registers).
+constexpr int FUSED_DIE_MAX_BR = 4;
+
 __host__ __device__ inline FusedLds fused_lds(bool local, bool f32, int ncw, int ks, int mtw, int D) {
   FusedLds L;
   const int gt = fused_gt(ncw, ks, mtw);
   const int mt_wg = mtw * (ncw / ks);
+  const int ktw = D / (f32 ? 4 : 32) / ks;
   L.h = 0;
-  const int hbytes = local ? 2 * 16 * (D + fused_hpad(f32)) * (f32 ? 4 : 2) : 0;
+  // LOCAL: the h buffer; die-local: each compute wave's poll stage, 16 rows
+  const int hbytes = local ? 2 * 16 * (D + fused_hpad(f32)) * (f32 ? 4 : 2) : ncw * 16 * fused_stage_row(ktw) * 4;
   L.part = (hbytes + 15) & ~15;
   const int pbytes = (!local && ks > 1) ? 2 * ks * mt_wg * 1024 : 0;
   L.wx = L.part + pbytes;
@@ -351,6 +358,10 @@ __global__ void __launch_bounds__((NCW + 1) * 64, 1) fused_fwd_kernel(FusedArgs 
   // zero the Wx ring (lanes of padding batch columns read zeros) and, for LOCAL, write
   // h_{-1} (the initial state) into parity 1 of the LDS h buffer
   for (int i = threadIdx.x; i < 2 * NCW * GT * 64; i += NT) wxs[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  if (!LOCAL) {  // poll stages: rows of padding batch columns stay zero
+    uint32_t* st = reinterpret_cast<uint32_t*>(smem + lay.h);
+    for (int i = threadIdx.x; i < NCW * 16 * fused_stage_row(KTW); i += NT) st[i] = 0u;
+  }
   if (LOCAL) {
     for (int idx = threadIdx.x; idx < 16 * D; idx += NT) {
       const int c = idx / D, k = idx - c * D;
@@ -493,50 +504,45 @@ __global__ void __launch_bounds__((NCW + 1) * 64, 1) fused_fwd_kernel(FusedArgs 
           for (int j = 0; j < MTW; ++j) acc[j] = mfma_bf16(Ra[j][kk], bk, acc[j]);
         }
       } else {
+        // Poll this wave's K range (KTW k-tiles of 32 units) for the group's nvalid rows with all
+        // 64 lanes, a few 64-bit words each; words whose tags are this step's are unpacked into
+        // the wave's LDS stage, from which the MFMA B fragments are read once everything is in.
         const int pp = (t - 1) & 1;
         const uint32_t tag = (uint32_t)t & 0xFFFFu;
-        const uint32_t* rowp = xb + (pp * xpar + col * D + 8 * quad);
-        constexpr uint32_t ALL = (1u << KTW) - 1u;
-        uint32_t pend = colv ? ALL : 0u;  // per lane: k-tiles whose words are not yet this step's
-        uint32_t done = 0;                // wave-uniform: k-tiles already multiplied
-        uint64_t v[KTW][4];
+        constexpr int WPR = KTW * 16;                             // 64-bit words per row
+        constexpr int NP = (FUSED_DIE_MAX_BR * WPR + 63) / 64;    // words per lane (upper bound)
+        constexpr int SROW = fused_stage_row(KTW);
+        uint32_t* stage = reinterpret_cast<uint32_t*>(smem + lay.h) + wave * 16 * SROW;
+        const uint64_t* src = reinterpret_cast<const uint64_t*>(xb + pp * xpar) + ks * WPR;
+        const int nw = nvalid * WPR;
+        uint32_t pend = 0;
 #pragma unroll
-        for (int kk = 0; kk < KTW; ++kk)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) v[kk][i] = 0;  // padding columns multiply zeros
+        for (int e = 0; e < NP; ++e)
+          if (lane + 64 * e < nw) pend |= 1u << e;
+        uint64_t v[NP];
         long long t_first = 0;
         int spins = 0;
         while (true) {
 #pragma unroll
-          for (int kk = 0; kk < KTW; ++kk) {
-            if (pend & (1u << kk)) {
-              const uint64_t* src = reinterpret_cast<const uint64_t*>(rowp + (ks * KTW + kk) * 32);
-#pragma unroll
-              for (int i = 0; i < 4; ++i)
-                v[kk][i] = __hip_atomic_load(src + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          for (int e = 0; e < NP; ++e) {
+            if (pend & (1u << e)) {
+              const int wi = lane + 64 * e, r = wi / WPR, wr = wi - r * WPR;
+              const uint32_t off = (uint32_t)(r * (D / 2) + wr);  // 32-bit offset from a uniform base
+              v[e] = __hip_atomic_load(src + off, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
           }
 #pragma unroll
-          for (int kk = 0; kk < KTW; ++kk) {
-            if (pend & (1u << kk)) {
-              uint32_t bad = 0;
-#pragma unroll
-              for (int i = 0; i < 4; ++i) bad |= (((uint32_t)v[kk][i] ^ tag) | ((uint32_t)(v[kk][i] >> 32) ^ tag)) & 0xFFFFu;
-              if (bad == 0) pend &= ~(1u << kk);
-            }
-            // multiply k-tile kk once no lane of the wave waits for it and every earlier k-tile is
-            // done: a fixed accumulation order keeps the results bitwise reproducible
-            if (done == (1u << kk) - 1u && !__any((pend >> kk) & 1u)) {
-              u32x4_t pk;
-#pragma unroll
-              for (int i = 0; i < 4; ++i) pk[i] = pack_hi((uint32_t)v[kk][i], (uint32_t)(v[kk][i] >> 32));
-              const bf16x8_t bk = __builtin_bit_cast(bf16x8_t, pk);
-#pragma unroll
-              for (int j = 0; j < MTW; ++j) acc[j] = mfma_bf16(Ra[j][kk], bk, acc[j]);
-              done |= 1u << kk;
+          for (int e = 0; e < NP; ++e) {
+            if (pend & (1u << e)) {
+              const uint32_t lo = (uint32_t)v[e], hi = (uint32_t)(v[e] >> 32);
+              if ((((lo ^ tag) | (hi ^ tag)) & 0xFFFFu) == 0) {
+                const int wi = lane + 64 * e, r = wi / WPR, wr = wi - r * WPR;
+                stage[r * SROW + wr] = pack_hi(lo, hi);
+                pend &= ~(1u << e);
+              }
             }
           }
-          if (done == ALL) break;
+          if (!__any(pend != 0u)) break;
           if ((++spins & 63) == 0) {
             const long long now = (long long)wall_clock64();
             if (t_first == 0) t_first = now;
@@ -547,6 +553,12 @@ __global__ void __launch_bounds__((NCW + 1) * 64, 1) fused_fwd_kernel(FusedArgs 
               break;
             }
           }
+        }
+#pragma unroll
+        for (int kk = 0; kk < KTW; ++kk) {
+          const bf16x8_t bk = *reinterpret_cast<const bf16x8_t*>(stage + col * SROW + kk * 16 + 4 * quad);
+#pragma unroll
+          for (int j = 0; j < MTW; ++j) acc[j] = mfma_bf16(Ra[j][kk], bk, acc[j]);
         }
       }
     }

@@ -112,11 +112,11 @@ FORCED = [
     (fi.HeadwiseWorkload("lstm_forced_W4", "lstm", torch.bfloat16, B=7, T=9, N=3, D=64, seed=121, s0_var=1.0),
      {"FRNN_FUSED_W": 4, "FRNN_FUSED_BR": 3}),
     (fi.HeadwiseWorkload("lstm_forced_W8", "lstm", torch.bfloat16, B=11, T=6, N=2, D=128, seed=122, s0_var=1.0),
-     {"FRNN_FUSED_W": 8, "FRNN_FUSED_BR": 5}),
+     {"FRNN_FUSED_W": 8, "FRNN_FUSED_BR": 4}),
     (fi.HeadwiseWorkload("elman_forced_W2", "elman", torch.bfloat16, B=9, T=8, N=2, D=64, seed=123, s0_var=1.0),
      {"FRNN_FUSED_W": 2, "FRNN_FUSED_BR": 4}),
-    (fi.HeadwiseWorkload("lstm_forced_W16_BR8", "lstm", torch.bfloat16, B=16, T=5, N=1, D=256, seed=124),
-     {"FRNN_FUSED_W": 16, "FRNN_FUSED_BR": 8}),
+    (fi.HeadwiseWorkload("lstm_forced_W16_BR4", "lstm", torch.bfloat16, B=15, T=5, N=1, D=256, seed=124),
+     {"FRNN_FUSED_W": 16, "FRNN_FUSED_BR": 4}),
     (fi.HeadwiseWorkload("lstm_D768_8waves", "lstm", torch.bfloat16, B=16, T=9, N=1, D=768, seed=125, s0_var=1.0),
      {"FRNN_FUSED_NCW": 8}),
     (fi.HeadwiseWorkload("lstm_D768_4waves", "lstm", torch.bfloat16, B=16, T=9, N=1, D=768, seed=126, s0_var=1.0),
