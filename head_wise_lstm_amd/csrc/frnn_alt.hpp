@@ -35,41 +35,6 @@ struct AltArgs {
   float* ccur;    // current c: [B][N][D]
 };
 
-// One thread per (n, tile, k-tile, lane): gathers the lane's 8 (bf16) or 1 (fp32) R^T values.
-__global__ void __launch_bounds__(256) alt_pack_kernel(AltArgs a) {
-  const int G = a.cell == CELL_LSTM ? 4 : 1;
-  const int TPH = G * a.D / 16;
-  const int KW = a.r_is_f32 ? 4 : 32;
-  const int KT = a.D / KW;
-  const long long total = (long long)a.N * TPH * KT * 64;
-  for (long long idx = (long long)blockIdx.x * 256 + threadIdx.x; idx < total; idx += (long long)gridDim.x * 256) {
-    const int lane = (int)(idx & 63);
-    long long r = idx >> 6;
-    const int kt = (int)(r % KT);
-    r /= KT;
-    const int tt = (int)(r % TPH);
-    const int n = (int)(r / TPH);
-    const int m = lane & 15, quad = lane >> 4;
-    int u, g;
-    if (a.cell == CELL_LSTM) { u = 4 * tt + (m >> 2); g = m & 3; }
-    else { u = 16 * tt + m; g = 0; }
-    const long long base = (long long)g * a.r_sg + (long long)n * a.r_sn + u;
-    if (a.r_is_f32) {
-      const int k = kt * 4 + quad;
-      reinterpret_cast<float*>(a.rpack)[idx] = reinterpret_cast<const float*>(a.R)[base + (long long)k * a.r_sd];
-    } else {
-      const uint16_t* Rp = reinterpret_cast<const uint16_t*>(a.R);
-      const int k = kt * 32 + 8 * quad;
-      u32x4_t pk;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        pk[i] = (uint32_t)Rp[base + (long long)(k + 2 * i) * a.r_sd] |
-                ((uint32_t)Rp[base + (long long)(k + 2 * i + 1) * a.r_sd] << 16);
-      reinterpret_cast<u32x4_t*>(a.rpack)[idx] = pk;
-    }
-  }
-}
-
 // Initial state into the working buffers: hcur[n][b][d] (operand type), ccur[b][n][d].
 __global__ void __launch_bounds__(256) alt_init_kernel(AltArgs a) {
   const long long total = (long long)a.B * a.N * a.D;

@@ -16,6 +16,7 @@
 #include "frnn_device.hpp"
 #include "frnn_fused.hpp"
 #include "frnn_proj.hpp"
+#include "frnn_rpack.hpp"
 
 using namespace frnn;
 
@@ -239,7 +240,9 @@ int plan_fused(const Problem& p, const DevInfo& di, FusedPlan* out) {
       if (!v) continue;
       if (v->spills && !(force_ncw || force_ks)) continue;
       const int u_wg = mt_wg * (G == 4 ? 4 : 16);
-      for (int BR = 1; BR <= FUSED_DIE_MAX_BR; ++BR) {
+      // the packed K-split partials hold BRP batch columns per tile
+      const int br_max = ks > 1 ? std::min(FUSED_DIE_MAX_BR, fused_brp(ks, mtw)) : FUSED_DIE_MAX_BR;
+      for (int BR = 1; BR <= br_max; ++BR) {
         if (force_br && BR != force_br) continue;
         const int epl = fused_epl(false, ncw);
         if (BR * G * u_wg / (p.wx_f32 ? 2 : 4) > 64 * epl || BR * u_wg / 2 > 64 * epl) continue;
@@ -273,16 +276,33 @@ int plan_fused(const Problem& p, const DevInfo& di, FusedPlan* out) {
 size_t rec_scratch_bytes(int B, int N, int D, int cell, int r_f32, int path) {
   const int G = gates_of(cell);
   const size_t elt = r_f32 ? 4 : 2;
+  size_t s = align256((size_t)G * N * D * D * elt);  // packed R
   if (path == FRNN_PATH_FUSED) {
     // exchange words: groups * BR <= N * (B + 15) rows, two parities
-    return align256((size_t)2 * N * (B + 15) * D * 4);
+    return s + align256((size_t)2 * N * (B + 15) * D * 4);
   }
-  size_t s = 0;
-  s += align256((size_t)G * N * D * D * elt);  // packed R
   s += align256((size_t)B * N * D * G * 4);    // h.R
   s += align256((size_t)N * B * D * elt);      // current h
   s += align256((size_t)B * N * D * 4);        // current c
   return s;
+}
+
+// R^T into MFMA fragment order (rpack); the coalesced kernel when the strides allow 8-byte rows.
+hipError_t launch_rpack(const Problem& p, void* out, hipStream_t st) {
+  RpackArgs ra;
+  ra.N = p.N; ra.D = p.D; ra.cell = p.cell; ra.R = p.R;
+  ra.r_sg = p.r_sg; ra.r_sn = p.r_sn; ra.r_sd = p.r_sd; ra.out = out;
+  const bool vec = !p.r_f32 && p.D % 32 == 0 && ((p.r_sg | p.r_sn | p.r_sd) & 3) == 0 &&
+                   (reinterpret_cast<uintptr_t>(p.R) & 7u) == 0;
+  if (vec) {
+    hipLaunchKernelGGL(rpack_bf16_kernel, dim3((p.D + RPACK_UB - 1) / RPACK_UB, p.D / 32, p.N), dim3(256), 0, st, ra);
+  } else {
+    const int G = gates_of(p.cell);
+    const long long total = (long long)p.N * (G * p.D / 16) * (p.D / (p.r_f32 ? 4 : 32)) * 64;
+    hipLaunchKernelGGL(rpack_any_kernel, dim3((unsigned)std::min<long long>((total + 255) / 256, 4096)), dim3(256), 0,
+                       st, ra, p.r_f32);
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_fill(void* p, size_t bytes, hipStream_t st) {
@@ -329,8 +349,11 @@ int run_recurrence(const Problem& p, int path, int* err, void* scratch, hipStrea
     rc = plan_fused(p, di, &fp);
     if (rc != FRNN_OK) return rc;
     trace("[frnn] %s\n", plan_string(p, path, &fp));
+    const size_t rbytes = align256((size_t)gates_of(p.cell) * p.N * p.D * p.D * (p.r_f32 ? 4 : 2));
+    char* xw = base + rbytes;
     const size_t xbytes = fp.local ? 0 : (size_t)fp.groups * 2 * fp.BR * p.D * 4;
-    if (launch_fill(scratch, xbytes, st) != hipSuccess) return FRNN_EHIP;
+    if (!p.r_f32 && launch_rpack(p, base, st) != hipSuccess) return FRNN_EHIP;
+    if (launch_fill(xw, xbytes, st) != hipSuccess) return FRNN_EHIP;
     FusedArgs a;
     std::memset(&a, 0, sizeof(a));
     a.B = p.B; a.T = p.T; a.N = p.N; a.D = p.D;
@@ -343,7 +366,8 @@ int run_recurrence(const Problem& p, int path, int* err, void* scratch, hipStrea
     a.s0_h = p.s0_h; a.s0_c = p.s0_c; a.s0_f32 = p.s0_f32; a.s0_sb = p.s0_sb;
     a.out_h = p.out_h; a.out_c = p.out_c; a.out_sb = p.out_sb; a.out_st = p.out_st;
     a.last_h = p.last_h; a.last_c = p.last_c; a.last_sb = p.last_sb;
-    a.xbuf = reinterpret_cast<uint32_t*>(base);
+    a.rpack = base;
+    a.xbuf = reinterpret_cast<uint32_t*>(xw);
     a.err = err;
     a.timeout_ticks = (long long)env_int("FRNN_TIMEOUT_MS", 2000) * di.wall_khz;
 #ifdef FRNN_PHASE_TRACE
@@ -381,9 +405,7 @@ int run_recurrence(const Problem& p, int path, int* err, void* scratch, hipStrea
   a.hcur = q; q += align256((size_t)p.N * p.B * p.D * elt);
   a.ccur = reinterpret_cast<float*>(q);
   const int TPH = G * p.D / 16;
-  const int KT = p.D / (p.r_f32 ? 4 : 32);
-  const long long npack = (long long)p.N * TPH * KT * 64;
-  hipLaunchKernelGGL(alt_pack_kernel, dim3((unsigned)std::min<long long>((npack + 255) / 256, 4096)), dim3(256), 0, st, a);
+  if (launch_rpack(p, a.rpack, st) != hipSuccess) return FRNN_EHIP;
   const long long nstate = (long long)p.B * p.N * p.D;
   hipLaunchKernelGGL(alt_init_kernel, dim3((unsigned)std::min<long long>((nstate + 255) / 256, 4096)), dim3(256), 0, st, a);
   const dim3 ggrid((TPH + 3) / 4, (p.B + 15) / 16, p.N);

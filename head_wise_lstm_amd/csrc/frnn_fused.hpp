@@ -47,6 +47,7 @@ struct FusedArgs {
   long long wx_sb, wx_st;  // element strides of Wx for b and t; [G][N][D] packed inside
   const void* R;
   long long r_sg, r_sn, r_sd;  // element strides of R for g, n, d; e contiguous
+  const void* rpack;           // bf16: R^T in fragment order [N][TPH][D/32][64] x 8 bf16
   const void* bias;            // [G][N][D], same dtype as R, or null
   const void* s0_h;
   const void* s0_c;
@@ -94,6 +95,15 @@ struct FusedLds {
   int h, part, wx, out, total;
 };
 
+// K-split partial sums are exchanged packed: only the first BR of the 16 MFMA batch columns are
+// real, so a wave moves the real columns of its MTW tiles next to each other in every 16-lane row
+// (tile j, column c at position j*BRP + c) before writing them to LDS. BRP is the column stride
+// of the packing, and bounds the batch rows per group of the design.
+__host__ __device__ constexpr int fused_brp(int ks, int mtw) {
+  return (ks * 4 <= 16 && mtw * 4 <= 16) ? 4 : (ks * 2 <= 16 && mtw * 2 <= 16) ? 2 : 1;
+}
+constexpr int FUSED_PART_ROW = 65;  // f32x4 entries per wave's packed partials (one of padding)
+
 // Byte offsets of the LDS regions (identical on host and device).
 // Words (32-bit, two bf16 units each) per row of a compute wave's poll stage, padded by 16 bytes.
 __host__ __device__ constexpr int fused_stage_row(int ktw) { return ktw * 16 + 4; }
@@ -109,7 +119,7 @@ __host__ __device__ inline FusedLds fused_lds(bool local, bool f32, int ncw, int
   // LOCAL: the h buffer; die-local: each compute wave's poll stage, 16 rows
   const int hbytes = local ? 2 * 16 * (D + fused_hpad(f32)) * (f32 ? 4 : 2) : ncw * 16 * fused_stage_row(ktw) * 4;
   L.part = (hbytes + 15) & ~15;
-  const int pbytes = (!local && ks > 1) ? 2 * ks * mt_wg * 1024 : 0;
+  const int pbytes = (!local && ks > 1) ? 2 * ncw * FUSED_PART_ROW * 16 : 0;
   L.wx = L.part + pbytes;
   L.out = L.wx + 2 * ncw * gt * 1024;
   L.total = L.out + 2 * ncw * gt * 1024;
@@ -117,6 +127,42 @@ __host__ __device__ inline FusedLds fused_lds(bool local, bool f32, int ncw, int
 }
 
 __device__ __forceinline__ void block_barrier() { __syncthreads(); }
+
+// DPP lane moves within 16-lane rows. row_shr:n makes lane l read lane l-n of its row, row_shl:n
+// lane l+n; a lane outside the bank mask, or whose source falls outside the row, keeps `old`
+// (or reads 0 with bound_ctrl).
+// Place columns 0..BRP-1 of tiles J..MTW-1 of acc at row positions j*BRP + c of P, in increasing
+// j: positions below j*BRP keep what earlier tiles put there (their source lane is outside the
+// row), positions above are overwritten by later tiles or unused.
+template <int BRP, int J, int MTW>
+__device__ __forceinline__ void pack_tiles(f32x4_t& P, const f32x4_t (&acc)[MTW]) {
+  if constexpr (J < MTW) {
+    constexpr int sh = J * BRP;
+    constexpr int b0 = sh / 4, b1 = (sh + BRP - 1) / 4;
+    constexpr int bank = ((1 << (b1 + 1)) - 1) & ~((1 << b0) - 1);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      P[i] = __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(P[i]), __float_as_int(acc[J][i]),
+                                                        0x110 + sh, 0xF, bank, false));
+    pack_tiles<BRP, J + 1, MTW>(P, acc);
+  }
+}
+
+// x[p] += x[p + d] for d = D, 2D, ... < LIM within each row (positions past the row read 0):
+// position c ends up with the sum over positions c + m*D.
+template <int D, int LIM>
+__device__ __forceinline__ void row_reduce(f32x4_t& x) {
+  if constexpr (D < LIM) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      x[i] += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x[i]), 0x100 + D, 0xF, 0xF, true));
+    row_reduce<2 * D, LIM>(x);
+  }
+}
+
+// A flag every lane reads the same, as a wave-uniform value: branches on it stay scalar, so loops
+// that leave on it keep a plain structure (and the compiler's count of loads in flight exact).
+__device__ __forceinline__ bool uniform_flag(int v) { return __builtin_amdgcn_readfirstlane(v) != 0; }
 
 
 // ---------------------------------------------------------------------------- I/O wave
@@ -171,11 +217,14 @@ struct IoDesc {
     // word index lane + 64 e, walked incrementally (one division per lane, not per element)
     int row = c.lane / wpr, uw = c.lane - row * wpr;
     int orow = c.lane / ppr, ou = c.lane - orow * ppr;
+    // a lane without a word of its own reloads the workgroup's first word, so that every load is
+    // unconditional (a load under a lane mask makes the compiler wait for it on the spot)
+    const long long w0 = ((long long)c.b0 * c.wx_sb + (long long)c.n * c.D + c.u_base) * esz;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       const int wi = c.lane + 64 * e;
       wlds[e] = -1;
-      wofs[e] = 0;
+      wofs[e] = w0;
       if (wi < nw) {
         const int g = row % G, b = row / G;
         const int u = uw * epw;
@@ -204,8 +253,7 @@ __device__ __forceinline__ void io_issue(const IoCtx& c, const IoDesc<CELL, NCW,
                                          io_word_t (&r)[EPL]) {
   const long long step = (long long)s * c.wx_st * (c.wx_f32 ? 4 : 2);
 #pragma unroll
-  for (int e = 0; e < EPL; ++e)
-    if (d.wlds[e] >= 0) r[e] = *reinterpret_cast<const io_word_t*>(c.wxb + d.wofs[e] + step);
+  for (int e = 0; e < EPL; ++e) r[e] = *reinterpret_cast<const io_word_t*>(c.wxb + d.wofs[e] + step);
 }
 
 template <int CELL, int NCW, int KS, int MTW, int EPL>
@@ -265,14 +313,15 @@ __device__ __forceinline__ bool io_interval(const IoCtx& c, const IoDesc<CELL, N
                                             const f32x4_t* outs, const int* abort_flag) {
   constexpr int L = FUSED_IO_STAGES;
   const int s_wx = k + 1 - G0;
-  if (s_wx >= 0 && s_wx < c.T) {
-    io_put<CELL, NCW, KS, MTW, EPL>(c, d, s_wx, raw[ST], wxs);
-    if (s_wx + L < c.T) io_issue<CELL, NCW, KS, MTW, EPL>(c, d, s_wx + L, raw[ST]);
-  }
+  if (s_wx >= 0 && s_wx < c.T) io_put<CELL, NCW, KS, MTW, EPL>(c, d, s_wx, raw[ST], wxs);
+  // Every interval issues the same loads (outside the range the step is clamped and the reload
+  // is never used), so that the compiler can count the loads in flight on every path and wait
+  // for the one four intervals back only.
+  io_issue<CELL, NCW, KS, MTW, EPL>(c, d, min(max(s_wx + L, 0), c.T - 1), raw[ST]);
   const int s_out = k - 1 - G0;
   if (s_out >= 0 && s_out < c.T) io_store<CELL, NCW, KS, MTW, EPL>(c, d, s_out, outs);
   block_barrier();
-  return *abort_flag != 0;
+  return uniform_flag(*abort_flag);
 }
 
 // The I/O wave: runs barriers -1 .. T in step with the compute waves (see the kernel).
@@ -283,22 +332,32 @@ __device__ __forceinline__ void io_wave(const IoCtx& c, f32x4_t* wxs, const f32x
   IoDesc<CELL, NCW, KS, MTW, EPL> d;
   d.init(c);
   io_word_t raw[L][EPL];
-  if (0 < c.T) io_issue<CELL, NCW, KS, MTW, EPL>(c, d, 0, raw[0]);
-  if (1 < c.T) io_issue<CELL, NCW, KS, MTW, EPL>(c, d, 1, raw[1]);
-  if (2 < c.T) io_issue<CELL, NCW, KS, MTW, EPL>(c, d, 2, raw[2]);
-  if (3 < c.T) io_issue<CELL, NCW, KS, MTW, EPL>(c, d, 3, raw[3]);
-  // k runs -1 .. T; the stage of the Wx step written in interval k is (k + 1 - G0) mod 4.
+  // k runs -1 .. T; the stage of the Wx step written in interval k is (k + 1 - G0) mod 4, and
+  // stage s first holds step s. The first loads go out in the stage order of intervals -1, 0, 1,
+  // 2, as they do in the loop, so that the loop is entered with the same loads in flight.
   constexpr int S0 = ((0 - G0) % L + L) % L, S1 = ((1 - G0) % L + L) % L;
   constexpr int S2 = ((2 - G0) % L + L) % L, S3 = ((3 - G0) % L + L) % L;
-  for (int kb = -1; kb <= c.T; kb += L) {
-    if (io_interval<CELL, NCW, KS, MTW, EPL, G0, S0>(c, d, kb, raw, wxs, outs, abort_flag)) return;
-    if (kb + 1 > c.T) break;
-    if (io_interval<CELL, NCW, KS, MTW, EPL, G0, S1>(c, d, kb + 1, raw, wxs, outs, abort_flag)) return;
-    if (kb + 2 > c.T) break;
-    if (io_interval<CELL, NCW, KS, MTW, EPL, G0, S2>(c, d, kb + 2, raw, wxs, outs, abort_flag)) return;
-    if (kb + 3 > c.T) break;
-    if (io_interval<CELL, NCW, KS, MTW, EPL, G0, S3>(c, d, kb + 3, raw, wxs, outs, abort_flag)) return;
+  if (c.T == 0) {  // intervals -1 and 0: the compute waves' two barriers, nothing to move
+    block_barrier();
+    block_barrier();
+    return;
   }
+  io_issue<CELL, NCW, KS, MTW, EPL>(c, d, min(S0, c.T - 1), raw[S0]);
+  io_issue<CELL, NCW, KS, MTW, EPL>(c, d, min(S1, c.T - 1), raw[S1]);
+  io_issue<CELL, NCW, KS, MTW, EPL>(c, d, min(S2, c.T - 1), raw[S2]);
+  io_issue<CELL, NCW, KS, MTW, EPL>(c, d, min(S3, c.T - 1), raw[S3]);
+  // Whole groups of four intervals in the loop (no exit inside the body, so every path into an
+  // interval has the same loads in flight), then at most three more.
+  int k = -1;
+  for (; k + 3 <= c.T; k += L) {
+    if (io_interval<CELL, NCW, KS, MTW, EPL, G0, S0>(c, d, k, raw, wxs, outs, abort_flag)) return;
+    if (io_interval<CELL, NCW, KS, MTW, EPL, G0, S1>(c, d, k + 1, raw, wxs, outs, abort_flag)) return;
+    if (io_interval<CELL, NCW, KS, MTW, EPL, G0, S2>(c, d, k + 2, raw, wxs, outs, abort_flag)) return;
+    if (io_interval<CELL, NCW, KS, MTW, EPL, G0, S3>(c, d, k + 3, raw, wxs, outs, abort_flag)) return;
+  }
+  if (k <= c.T && io_interval<CELL, NCW, KS, MTW, EPL, G0, S0>(c, d, k, raw, wxs, outs, abort_flag)) return;
+  if (k + 1 <= c.T && io_interval<CELL, NCW, KS, MTW, EPL, G0, S1>(c, d, k + 1, raw, wxs, outs, abort_flag)) return;
+  if (k + 2 <= c.T && io_interval<CELL, NCW, KS, MTW, EPL, G0, S2>(c, d, k + 2, raw, wxs, outs, abort_flag)) return;
   if (G0 == 1 && c.T >= 1) io_store<CELL, NCW, KS, MTW, EPL>(c, d, c.T - 1, outs);
 }
 
@@ -404,32 +463,43 @@ __global__ void __launch_bounds__((NCW + 1) * 64, 1) fused_fwd_kernel(FusedArgs 
   const long long bcol = b0 + col;
   const bool r_f32 = F32;
 
-  // ---- R^T fragments, resident for the whole sequence.
+  // ---- R^T fragments, resident for the whole sequence. bf16: 16 contiguous bytes per lane from
+  // the packed copy, all loads in flight at once (tiles past the head read its last tile and are
+  // zeroed).
   frag_t Ra[MTW][KTW];
+  if constexpr (F32) {
 #pragma unroll
-  for (int j = 0; j < MTW; ++j) {
-    const int tt = tile0 + ms * MTW + j;
-    const bool tv = tt < TPH;
-    int u, g;
-    if (CELL == CELL_LSTM) { u = 4 * tt + (col >> 2); g = col & 3; }
-    else { u = 16 * tt + col; g = 0; }
-    const long long rbase = (long long)g * a.r_sg + (long long)n * a.r_sn + u;
+    for (int j = 0; j < MTW; ++j) {
+      const int tt = tile0 + ms * MTW + j;
+      const bool tv = tt < TPH;
+      int u, g;
+      if (CELL == CELL_LSTM) { u = 4 * tt + (col >> 2); g = col & 3; }
+      else { u = 16 * tt + col; g = 0; }
+      const long long rbase = (long long)g * a.r_sg + (long long)n * a.r_sn + u;
 #pragma unroll
-    for (int kk = 0; kk < KTW; ++kk) {
-      if constexpr (F32) {
+      for (int kk = 0; kk < KTW; ++kk) {
         const int k = (ks * KTW + kk) * KW + quad;
         Ra[j][kk] = tv ? reinterpret_cast<const float*>(a.R)[rbase + (long long)k * a.r_sd] : 0.0f;
-      } else {
-        const int k = (ks * KTW + kk) * KW + 8 * quad;
-        const uint16_t* Rp = reinterpret_cast<const uint16_t*>(a.R);
-        u32x4_t pk;
+      }
+    }
+  } else {
+    const int KT = D / 32;
+    const u32x4_t* rp = reinterpret_cast<const u32x4_t*>(a.rpack) + (long long)n * TPH * KT * 64 + lane;
+    u32x4_t raw[MTW][KTW];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          uint32_t lo = tv ? Rp[rbase + (long long)(k + 2 * i) * a.r_sd] : 0u;
-          uint32_t hi = tv ? Rp[rbase + (long long)(k + 2 * i + 1) * a.r_sd] : 0u;
-          pk[i] = lo | (hi << 16);
-        }
-        Ra[j][kk] = __builtin_bit_cast(bf16x8_t, pk);
+    for (int j = 0; j < MTW; ++j) {
+      const int tt = min(tile0 + ms * MTW + j, TPH - 1);
+#pragma unroll
+      for (int kk = 0; kk < KTW; ++kk) raw[j][kk] = rp[((long long)tt * KT + ks * KTW + kk) * 64];
+    }
+#pragma unroll
+    for (int j = 0; j < MTW; ++j) {
+      const bool tv = tile0 + ms * MTW + j < TPH;
+#pragma unroll
+      for (int kk = 0; kk < KTW; ++kk) {
+        u32x4_t v = raw[j][kk];
+        if (!tv) v = u32x4_t{0u, 0u, 0u, 0u};
+        Ra[j][kk] = __builtin_bit_cast(bf16x8_t, v);
       }
     }
   }
@@ -468,6 +538,13 @@ __global__ void __launch_bounds__((NCW + 1) * 64, 1) fused_fwd_kernel(FusedArgs 
 
   for (int t = 0; t < T; ++t) {
     FRNN_TRACE(0);
+    // Wx of this step (the ring slot t & 1, written by the I/O wave before the barrier that
+    // precedes the gating): read as early as that barrier allows
+    f32x4_t wxq[GT];
+    if (LOCAL) {
+#pragma unroll
+      for (int q = 0; q < GT; ++q) wxq[q] = wxs[(((t & 1) * NCW + wave) * GT + q) * 64 + lane];
+    }
     // ---- 1+2. h_{t-1} as the B operand, multiplied on MFMA as each k-tile becomes available.
     f32x4_t acc[MTW];
 #pragma unroll
@@ -505,8 +582,8 @@ __global__ void __launch_bounds__((NCW + 1) * 64, 1) fused_fwd_kernel(FusedArgs 
         }
       } else {
         // Poll this wave's K range (KTW k-tiles of 32 units) for the group's nvalid rows with all
-        // 64 lanes, a few 64-bit words each; words whose tags are this step's are unpacked into
-        // the wave's LDS stage, from which the MFMA B fragments are read once everything is in.
+        // 64 lanes, a few 64-bit words each; once every word carries this step's tag they are
+        // unpacked into the wave's LDS stage, from which the MFMA B fragments are read.
         const int pp = (t - 1) & 1;
         const uint32_t tag = (uint32_t)t & 0xFFFFu;
         constexpr int WPR = KTW * 16;                             // 64-bit words per row
@@ -515,39 +592,38 @@ __global__ void __launch_bounds__((NCW + 1) * 64, 1) fused_fwd_kernel(FusedArgs 
         uint32_t* stage = reinterpret_cast<uint32_t*>(smem + lay.h) + wave * 16 * SROW;
         const uint64_t* src = reinterpret_cast<const uint64_t*>(xb + pp * xpar) + ks * WPR;
         const int nw = nvalid * WPR;
-        uint32_t pend = 0;
-#pragma unroll
-        for (int e = 0; e < NP; ++e)
-          if (lane + 64 * e < nw) pend |= 1u << e;
+        // every round re-reads all of the lane's words (a word, once current, stays current until
+        // this workgroup has published its own h of this step), so no load depends on the last round
         uint64_t v[NP];
         long long t_first = 0;
         int spins = 0;
         while (true) {
+          bool ok = true;
 #pragma unroll
           for (int e = 0; e < NP; ++e) {
-            if (pend & (1u << e)) {
+            const int wi = lane + 64 * e, r = wi / WPR, wr = wi - r * WPR;
+            const uint32_t off = (uint32_t)(r * (D / 2) + wr);  // 32-bit offset from a uniform base
+            v[e] = 0;
+            if (wi < nw) v[e] = __hip_atomic_load(src + off, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
+#pragma unroll
+          for (int e = 0; e < NP; ++e) {
+            const uint32_t lo = (uint32_t)v[e], hi = (uint32_t)(v[e] >> 32);
+            if (lane + 64 * e < nw && (((lo ^ tag) | (hi ^ tag)) & 0xFFFFu) != 0) ok = false;
+          }
+          if (__all(ok)) {
+#pragma unroll
+            for (int e = 0; e < NP; ++e) {
               const int wi = lane + 64 * e, r = wi / WPR, wr = wi - r * WPR;
-              const uint32_t off = (uint32_t)(r * (D / 2) + wr);  // 32-bit offset from a uniform base
-              v[e] = __hip_atomic_load(src + off, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              if (wi < nw) stage[r * SROW + wr] = pack_hi((uint32_t)v[e], (uint32_t)(v[e] >> 32));
             }
+            break;
           }
-#pragma unroll
-          for (int e = 0; e < NP; ++e) {
-            if (pend & (1u << e)) {
-              const uint32_t lo = (uint32_t)v[e], hi = (uint32_t)(v[e] >> 32);
-              if ((((lo ^ tag) | (hi ^ tag)) & 0xFFFFu) == 0) {
-                const int wi = lane + 64 * e, r = wi / WPR, wr = wi - r * WPR;
-                stage[r * SROW + wr] = pack_hi(lo, hi);
-                pend &= ~(1u << e);
-              }
-            }
-          }
-          if (!__any(pend != 0u)) break;
           if ((++spins & 63) == 0) {
             const long long now = (long long)wall_clock64();
             if (t_first == 0) t_first = now;
             if (now - t_first > a.timeout_ticks ||
-                __hip_atomic_load(a.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) {
+                uniform_flag(__hip_atomic_load(a.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))) {
               if (lane == 0) atomicOr(a.err, DEVERR_TIMEOUT);
               s_abort = 1;  // every wave leaves after the next barrier
               break;
@@ -571,25 +647,37 @@ __global__ void __launch_bounds__((NCW + 1) * 64, 1) fused_fwd_kernel(FusedArgs 
       for (int q = 0; q < GT; ++q) pre[q] = acc[q];
       if (!LOCAL) {
         block_barrier();
-        if (s_abort) return;
+#pragma unroll
+        for (int q = 0; q < GT; ++q) wxq[q] = wxs[(((t & 1) * NCW + wave) * GT + q) * 64 + lane];
+        if (uniform_flag(s_abort)) return;
       }
     } else {
+      // pack the real batch columns of this wave's MTW tiles into one f32x4 per lane and write it;
+      // after the barrier one read gathers, for each tile this wave gates, the KS partials of
+      // its columns (source k2, column c at row position k2*BRP + c), and row_reduce adds them
+      constexpr int BRP = fused_brp(KS, MTW);
       const int pp = t & 1;
-#pragma unroll
-      for (int j = 0; j < MTW; ++j) part[((pp * KS + ks) * MT_WG + ms * MTW + j) * 64 + lane] = acc[j];
+      f32x4_t P = acc[0];
+      pack_tiles<BRP, 1, MTW>(P, acc);
+      part[(pp * NCW + wave) * FUSED_PART_ROW + lane] = P;
       FRNN_TRACE(2);
       block_barrier();
       FRNN_TRACE(3);
-      if (s_abort) return;
+      // the reads go out before the abort flag is looked at (they are harmless if it is set)
+#pragma unroll
+      for (int q = 0; q < GT; ++q) wxq[q] = wxs[(((t & 1) * NCW + wave) * GT + q) * 64 + lane];
+      const int k2 = col / BRP, cc = col - k2 * BRP;
 #pragma unroll
       for (int q = 0; q < GT; ++q) {
         pre[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        if (gval[q]) {
-          const int tq = wave + NCW * q;
-#pragma unroll
-          for (int k2 = 0; k2 < KS; ++k2) pre[q] += part[((pp * KS + k2) * MT_WG + tq) * 64 + lane];
-        }
+        const int tq = wave + NCW * q;
+        const int msq = tq / MTW, jq = tq - msq * MTW;
+        if (gval[q] && k2 < KS)
+          pre[q] = part[(pp * NCW + msq * KS + k2) * FUSED_PART_ROW + quad * 16 + jq * BRP + cc];
       }
+      if (uniform_flag(s_abort)) return;
+#pragma unroll
+      for (int q = 0; q < GT; ++q) row_reduce<BRP, KS * BRP>(pre[q]);
     }
 
     FRNN_TRACE(4);
@@ -599,7 +687,7 @@ __global__ void __launch_bounds__((NCW + 1) * 64, 1) fused_fwd_kernel(FusedArgs 
     for (int q = 0; q < GT; ++q) {
       if (!gval[q]) continue;
       const int ri = (((t & 1) * NCW + wave) * GT + q) * 64 + lane;
-      const f32x4_t wx4 = wxs[ri];
+      const f32x4_t wx4 = wxq[q];
       if constexpr (CELL == CELL_LSTM) {
         const float ig = sigmoid_f(pre[q][0] + wx4[0] + bia[q][0]);
         const float fg = sigmoid_f(pre[q][1] + wx4[1] + bia[q][1]);
