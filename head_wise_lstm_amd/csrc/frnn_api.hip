@@ -104,12 +104,10 @@ typedef void (*fused_fn)(FusedArgs);
 struct FusedVariant {
   int cell, f32, local, ncw, ks, mtw, ktw;
   fused_fn fn;
-  int spills;  // the compiler spills registers for this variant (kept for measurements only)
 };
 
 #define FV(CELL, F32, LOCAL, NCW, KS, MTW, KTW) \
-  {CELL, F32, LOCAL, NCW, KS, MTW, KTW, &fused_fwd_kernel<CELL, F32, LOCAL, NCW, KS, MTW, KTW>, SPILLS(NCW, KS, MTW, KTW)}
-#define SPILLS(NCW, KS, MTW, KTW) (((NCW) == 4 && (MTW) == 6 && (KTW) == 6) || ((NCW) == 8 && (MTW) == 6 && (KTW) == 3))
+  {CELL, F32, LOCAL, NCW, KS, MTW, KTW, &fused_fwd_kernel<CELL, F32, LOCAL, NCW, KS, MTW, KTW>}
 #define FV2(F32, LOCAL, NCW, KS, MTW, KTW) FV(CELL_LSTM, F32, LOCAL, NCW, KS, MTW, KTW), FV(CELL_ELMAN, F32, LOCAL, NCW, KS, MTW, KTW)
 
 // Instantiated designs: (compute waves, K split, tiles per wave, k-tiles per wave). Each fits the
@@ -178,8 +176,8 @@ int env_int(const char* name, int dflt) {
 
 // Choose the fused design for a problem. The workgroup-local design is used when the whole head
 // fits in one workgroup's registers and the per-wave MFMA chain stays short; otherwise W
-// workgroups per group on one die, W as large as possible (least MFMA work per CU), then the
-// fewest batch rows per group (least h polled per step) that still fit the die.
+// workgroups per group on one die: the fewest batch rows per group that fit some design, and
+// for them the largest W.
 int plan_fused(const Problem& p, const DevInfo& di, FusedPlan* out) {
   const int G = gates_of(p.cell);
   const int TPH = G * p.D / 16;
@@ -223,32 +221,33 @@ int plan_fused(const Problem& p, const DevInfo& di, FusedPlan* out) {
   }
   if (p.r_f32 || !di.periodic) return FRNN_EUNSUPPORTED;
   const int slots_per_die = std::max(1, di.cus / di.n_xcd);
-  for (int W = std::min(32, slots_per_die); W >= 2; --W) {
-    if (force_w > 1 && W != force_w) continue;
-    if (TPH % W) continue;
-    const int mt_wg = TPH / W;
-    // (compute waves, K split) in order of preference; a spilling variant is only taken when forced
-    const int cand[][2] = {{4, 4}, {6, 6}, {8, 8}, {4, 2}, {8, 4}, {4, 1}, {8, 2}};
-    const int force_ncw = env_int("FRNN_FUSED_NCW", 0), force_ks = env_int("FRNN_FUSED_KS", 0);
-    for (const auto& nk : cand) {
-      const int ncw = nk[0], ks = nk[1];
-      if ((force_ncw && ncw != force_ncw) || (force_ks && ks != force_ks)) continue;
-      const int ms = ncw / ks;
-      if (mt_wg % ms || KT % ks) continue;
-      const int mtw = mt_wg / ms, ktw = KT / ks;
-      const FusedVariant* v = find_fused(p.cell, 0, 0, ncw, ks, mtw, ktw);
-      if (!v) continue;
-      if (v->spills && !(force_ncw || force_ks)) continue;
+  const int force_ncw = env_int("FRNN_FUSED_NCW", 0), force_ks = env_int("FRNN_FUSED_KS", 0);
+  // (compute waves, K split) in order of preference
+  const int cand[][2] = {{6, 6}, {4, 4}, {8, 8}, {4, 2}, {8, 4}, {4, 1}, {8, 2}};
+  // Fewest batch rows per group first (least h polled per step and fewest producers per
+  // consumer), then the most workgroups per group that fit a die (least MFMA work per CU).
+  for (int BR = 1; BR <= FUSED_DIE_MAX_BR; ++BR) {
+    if (force_br && BR != force_br) continue;
+    const int groups = p.N * ((p.B + BR - 1) / BR);
+    const int per_die = (groups + di.n_xcd - 1) / di.n_xcd;
+    for (int W = std::min(32, slots_per_die); W >= 2; --W) {
+      if (force_w > 1 && W != force_w) continue;
+      if (TPH % W || per_die * W > slots_per_die) continue;
+      const int mt_wg = TPH / W;
       const int u_wg = mt_wg * (G == 4 ? 4 : 16);
-      // the packed K-split partials hold BRP batch columns per tile
-      const int br_max = ks > 1 ? std::min(FUSED_DIE_MAX_BR, fused_brp(ks, mtw)) : FUSED_DIE_MAX_BR;
-      for (int BR = 1; BR <= br_max; ++BR) {
-        if (force_br && BR != force_br) continue;
+      for (const auto& nk : cand) {
+        const int ncw = nk[0], ks = nk[1];
+        if ((force_ncw && ncw != force_ncw) || (force_ks && ks != force_ks)) continue;
+        const int ms = ncw / ks;
+        if (mt_wg % ms || KT % ks) continue;
+        const int mtw = mt_wg / ms, ktw = KT / ks;
+        const FusedVariant* v = find_fused(p.cell, 0, 0, ncw, ks, mtw, ktw);
+        if (!v) continue;
+        // the packed K-split partials hold BRP batch columns per tile; the polls cover that many rows
+        if (BR > fused_max_br(ks, mtw)) continue;
+        // the I/O wave moves at most 64 * epl words of Wx and as many output pairs per step
         const int epl = fused_epl(false, ncw);
         if (BR * G * u_wg / (p.wx_f32 ? 2 : 4) > 64 * epl || BR * u_wg / 2 > 64 * epl) continue;
-        const int groups = p.N * ((p.B + BR - 1) / BR);
-        const int per_die = (groups + di.n_xcd - 1) / di.n_xcd;
-        if (per_die * W > slots_per_die) continue;
         FusedPlan fp;
         fp.v = v;
         fp.local = 0;
@@ -305,11 +304,11 @@ hipError_t launch_rpack(const Problem& p, void* out, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_fill(void* p, size_t bytes, hipStream_t st) {
+hipError_t launch_fill(void* p, size_t bytes, hipStream_t st, uint32_t value = 0u) {
   const long long n = (long long)(bytes / 4);
   if (n <= 0) return hipSuccess;
   const int blocks = (int)std::min<long long>((n + 255) / 256, 1024);
-  hipLaunchKernelGGL(fill_u32_kernel, dim3(blocks), dim3(256), 0, st, reinterpret_cast<uint32_t*>(p), n, 0u);
+  hipLaunchKernelGGL(fill_u32_kernel, dim3(blocks), dim3(256), 0, st, reinterpret_cast<uint32_t*>(p), n, value);
   return hipGetLastError();
 }
 
@@ -353,7 +352,9 @@ int run_recurrence(const Problem& p, int path, int* err, void* scratch, hipStrea
     char* xw = base + rbytes;
     const size_t xbytes = fp.local ? 0 : (size_t)fp.groups * 2 * fp.BR * p.D * 4;
     if (!p.r_f32 && launch_rpack(p, base, st) != hipSuccess) return FRNN_EHIP;
-    if (launch_fill(xw, xbytes, st) != hipSuccess) return FRNN_EHIP;
+    // exchange words start with tag 0xFFFF, which no step before 65535 polls for (by then every
+    // word has been overwritten)
+    if (launch_fill(xw, xbytes, st, 0xFFFFu) != hipSuccess) return FRNN_EHIP;
     FusedArgs a;
     std::memset(&a, 0, sizeof(a));
     a.B = p.B; a.T = p.T; a.N = p.N; a.D = p.D;
@@ -372,6 +373,7 @@ int run_recurrence(const Problem& p, int path, int* err, void* scratch, hipStrea
     a.timeout_ticks = (long long)env_int("FRNN_TIMEOUT_MS", 2000) * di.wall_khz;
 #ifdef FRNN_PHASE_TRACE
     if (const char* tp = std::getenv("FRNN_TRACE_PTR")) a.trace = reinterpret_cast<long long*>(std::strtoull(tp, nullptr, 0));
+    a.trace_slots = env_int("FRNN_TRACE_SLOTS", 0);  // no slot, no trace store
 #endif
     const void* fn = reinterpret_cast<const void*>(fp.v->fn);
     if (fp.lds > 48 * 1024) {

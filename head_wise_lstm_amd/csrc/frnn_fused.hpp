@@ -63,19 +63,29 @@ struct FusedArgs {
   int* err;
   long long timeout_ticks;  // bound of every wait, in wall-clock (100 MHz) ticks
   long long* trace;         // phase timestamps (only in builds with FRNN_PHASE_TRACE), or null
+  int trace_slots;          // slots of 4096 x 8 timestamps the trace buffer holds
 };
 
 #ifdef FRNN_PHASE_TRACE
 // Shader-clock timestamp of phase `ph` of step t, recorded by lane 0 of compute wave 0 of the
-// first and the last workgroup; at most 4096 steps.
+// first and the last workgroup; at most 4096 steps. FRNN_TRACE_RT records the wall clock
+// (100 MHz, common to all CUs) for the workgroups 0, n_xcd, 2 n_xcd, ... (slots 2, 3, ...).
 #define FRNN_TRACE(ph)                                                                          \
   do {                                                                                          \
-    if (a.trace && lane == 0 && wave == 0 && (blockIdx.x == 0 || blockIdx.x == gridDim.x - 1) && t < 4096) \
+    if (a.trace && a.trace_slots >= 2 && lane == 0 && wave == 0 && (blockIdx.x == 0 || blockIdx.x == gridDim.x - 1) && t < 4096) \
       a.trace[((blockIdx.x == 0 ? 0 : 1) * 4096 + t) * 8 + (ph)] = (long long)clock64();       \
+  } while (0)
+#define FRNN_TRACE_RT(ph)                                                                       \
+  do {                                                                                          \
+    if (a.trace && lane == 0 && wave == 0 && blockIdx.x % a.n_xcd == 0 && 2 + (int)blockIdx.x / a.n_xcd < a.trace_slots && t < 4096) \
+      a.trace[((2 + blockIdx.x / a.n_xcd) * 4096 + t) * 8 + (ph)] = (long long)wall_clock64();  \
   } while (0)
 #else
 #define FRNN_TRACE(ph) \
   do {                 \
+  } while (0)
+#define FRNN_TRACE_RT(ph) \
+  do {                    \
   } while (0)
 #endif
 
@@ -95,6 +105,9 @@ struct FusedLds {
   int h, part, wx, out, total;
 };
 
+// Batch rows per group of the die-local design (bounds the polling registers).
+constexpr int FUSED_DIE_MAX_BR = 4;
+
 // K-split partial sums are exchanged packed: only the first BR of the 16 MFMA batch columns are
 // real, so a wave moves the real columns of its MTW tiles next to each other in every 16-lane row
 // (tile j, column c at position j*BRP + c) before writing them to LDS. BRP is the column stride
@@ -103,12 +116,14 @@ __host__ __device__ constexpr int fused_brp(int ks, int mtw) {
   return (ks * 4 <= 16 && mtw * 4 <= 16) ? 4 : (ks * 2 <= 16 && mtw * 2 <= 16) ? 2 : 1;
 }
 constexpr int FUSED_PART_ROW = 65;  // f32x4 entries per wave's packed partials (one of padding)
+// Most batch rows per group a die-local design takes.
+__host__ __device__ constexpr int fused_max_br(int ks, int mtw) {
+  return ks > 1 ? (fused_brp(ks, mtw) < FUSED_DIE_MAX_BR ? fused_brp(ks, mtw) : FUSED_DIE_MAX_BR) : FUSED_DIE_MAX_BR;
+}
 
 // Byte offsets of the LDS regions (identical on host and device).
 // Words (32-bit, two bf16 units each) per row of a compute wave's poll stage, padded by 16 bytes.
 __host__ __device__ constexpr int fused_stage_row(int ktw) { return ktw * 16 + 4; }
-// Batch rows per group of the die-local design (bounds the polling registers).
-constexpr int FUSED_DIE_MAX_BR = 4;
 
 __host__ __device__ inline FusedLds fused_lds(bool local, bool f32, int ncw, int ks, int mtw, int D) {
   FusedLds L;
@@ -534,6 +549,20 @@ __global__ void __launch_bounds__((NCW + 1) * 64, 1) fused_fwd_kernel(FusedArgs 
   // exchange words of this group: uniform base (scalar registers) plus 32-bit lane offsets
   uint32_t* const xb = a.xbuf + (long long)group * 2 * a.BR * D;
   const int xpar = a.BR * D;  // words per parity
+  // The initial h of this workgroup's units goes out like any later step's h: parity 1, tag 0 (the
+  // buffer starts filled with tag 0xFFFF), so step 0 polls it like every other step.
+  if (!LOCAL && !F32 && colv) {
+#pragma unroll
+    for (int q = 0; q < GT; ++q) {
+      if (!gval[q]) continue;
+#pragma unroll
+      for (int i = 0; i < (CELL == CELL_LSTM ? 1 : 4); ++i) {
+        const int u = gu[q] + i;
+        const float h0 = a.s0_h ? ld_f(a.s0_h, bcol * a.s0_sb + (long long)n * D + u, a.s0_f32) : 0.0f;
+        xb[xpar + col * D + u] = (uint32_t)f2bf(h0) << 16;
+      }
+    }
+  }
   float hlast[GT][4];         // h of the last step, written out after the loop
 
   for (int t = 0; t < T; ++t) {
@@ -563,80 +592,66 @@ __global__ void __launch_bounds__((NCW + 1) * 64, 1) fused_fwd_kernel(FusedArgs 
         }
       }
     } else if constexpr (!F32) {
-      if (t == 0) {
+      // Poll this wave's K range (KTW k-tiles of 32 units) for the group's nvalid rows with all
+      // 64 lanes, a few 64-bit words each; once every word carries this step's tag they are
+      // unpacked into the wave's LDS stage, from which the MFMA B fragments are read. (Taking
+      // k-tiles as they complete, in order, measured slower: the longer rounds poll less often.)
+      const int pp = (t - 1) & 1;
+      const uint32_t tag = (uint32_t)t & 0xFFFFu;
+      constexpr int WPR = KTW * 16;                                // 64-bit words per row
+      constexpr int NP = (fused_max_br(KS, MTW) * WPR + 63) / 64;  // words per lane (upper bound)
+      constexpr int SROW = fused_stage_row(KTW);
+      uint32_t* stage = reinterpret_cast<uint32_t*>(smem + lay.h) + wave * 16 * SROW;
+      const uint64_t* src = reinterpret_cast<const uint64_t*>(xb + pp * xpar) + ks * WPR;
+      const int nw = nvalid * WPR;
+      // Every round re-reads all of the lane's words (a word, once current, stays current until
+      // this workgroup has published its own h of this step), and a lane without a word re-reads
+      // word 0, so that no load sits under a lane mask or depends on the last round.
+      uint32_t off[NP];
 #pragma unroll
-        for (int kk = 0; kk < KTW; ++kk) {
-          u32x4_t pk = {0u, 0u, 0u, 0u};
-          if (colv && a.s0_h) {
-            const long long base = bcol * a.s0_sb + (long long)n * D + (ks * KTW + kk) * 32 + 8 * quad;
+      for (int e = 0; e < NP; ++e) {
+        const int wi = lane + 64 * e, r = wi / WPR, wr = wi - r * WPR;
+        off[e] = wi < nw ? (uint32_t)(r * (D / 2) + wr) : 0u;  // 32-bit offsets from a uniform base
+      }
+      uint64_t v[NP];
+      long long t_first = 0;
+      int spins = 0;
+      while (true) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              uint32_t lo = f2bf(ld_f(a.s0_h, base + 2 * i, a.s0_f32));
-              uint32_t hi = f2bf(ld_f(a.s0_h, base + 2 * i + 1, a.s0_f32));
-              pk[i] = lo | (hi << 16);
-            }
-          }
-          const bf16x8_t bk = __builtin_bit_cast(bf16x8_t, pk);
+        for (int e = 0; e < NP; ++e) v[e] = __hip_atomic_load(src + off[e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        bool ok = true;
 #pragma unroll
-          for (int j = 0; j < MTW; ++j) acc[j] = mfma_bf16(Ra[j][kk], bk, acc[j]);
+        for (int e = 0; e < NP; ++e) {
+          const uint32_t lo = (uint32_t)v[e], hi = (uint32_t)(v[e] >> 32);
+          if (lane + 64 * e < nw && (((lo ^ tag) | (hi ^ tag)) & 0xFFFFu) != 0) ok = false;
         }
-      } else {
-        // Poll this wave's K range (KTW k-tiles of 32 units) for the group's nvalid rows with all
-        // 64 lanes, a few 64-bit words each; once every word carries this step's tag they are
-        // unpacked into the wave's LDS stage, from which the MFMA B fragments are read.
-        const int pp = (t - 1) & 1;
-        const uint32_t tag = (uint32_t)t & 0xFFFFu;
-        constexpr int WPR = KTW * 16;                             // 64-bit words per row
-        constexpr int NP = (FUSED_DIE_MAX_BR * WPR + 63) / 64;    // words per lane (upper bound)
-        constexpr int SROW = fused_stage_row(KTW);
-        uint32_t* stage = reinterpret_cast<uint32_t*>(smem + lay.h) + wave * 16 * SROW;
-        const uint64_t* src = reinterpret_cast<const uint64_t*>(xb + pp * xpar) + ks * WPR;
-        const int nw = nvalid * WPR;
-        // every round re-reads all of the lane's words (a word, once current, stays current until
-        // this workgroup has published its own h of this step), so no load depends on the last round
-        uint64_t v[NP];
-        long long t_first = 0;
-        int spins = 0;
-        while (true) {
-          bool ok = true;
+        if (__all(ok)) {
 #pragma unroll
           for (int e = 0; e < NP; ++e) {
             const int wi = lane + 64 * e, r = wi / WPR, wr = wi - r * WPR;
-            const uint32_t off = (uint32_t)(r * (D / 2) + wr);  // 32-bit offset from a uniform base
-            v[e] = 0;
-            if (wi < nw) v[e] = __hip_atomic_load(src + off, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (wi < nw) stage[r * SROW + wr] = pack_hi((uint32_t)v[e], (uint32_t)(v[e] >> 32));
           }
-#pragma unroll
-          for (int e = 0; e < NP; ++e) {
-            const uint32_t lo = (uint32_t)v[e], hi = (uint32_t)(v[e] >> 32);
-            if (lane + 64 * e < nw && (((lo ^ tag) | (hi ^ tag)) & 0xFFFFu) != 0) ok = false;
-          }
-          if (__all(ok)) {
-#pragma unroll
-            for (int e = 0; e < NP; ++e) {
-              const int wi = lane + 64 * e, r = wi / WPR, wr = wi - r * WPR;
-              if (wi < nw) stage[r * SROW + wr] = pack_hi((uint32_t)v[e], (uint32_t)(v[e] >> 32));
-            }
+          break;
+        }
+        if ((++spins & 63) == 0) {
+          const long long now = (long long)wall_clock64();
+          if (t_first == 0) t_first = now;
+          if (now - t_first > a.timeout_ticks ||
+              uniform_flag(__hip_atomic_load(a.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))) {
+            if (lane == 0) atomicOr(a.err, DEVERR_TIMEOUT);
+            s_abort = 1;  // every wave leaves after the next barrier
             break;
           }
-          if ((++spins & 63) == 0) {
-            const long long now = (long long)wall_clock64();
-            if (t_first == 0) t_first = now;
-            if (now - t_first > a.timeout_ticks ||
-                uniform_flag(__hip_atomic_load(a.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))) {
-              if (lane == 0) atomicOr(a.err, DEVERR_TIMEOUT);
-              s_abort = 1;  // every wave leaves after the next barrier
-              break;
-            }
-          }
-        }
-#pragma unroll
-        for (int kk = 0; kk < KTW; ++kk) {
-          const bf16x8_t bk = *reinterpret_cast<const bf16x8_t*>(stage + col * SROW + kk * 16 + 4 * quad);
-#pragma unroll
-          for (int j = 0; j < MTW; ++j) acc[j] = mfma_bf16(Ra[j][kk], bk, acc[j]);
         }
       }
+#pragma unroll
+      for (int kk = 0; kk < KTW; ++kk) {
+        const bf16x8_t bk = *reinterpret_cast<const bf16x8_t*>(stage + col * SROW + kk * 16 + 4 * quad);
+#pragma unroll
+        for (int j = 0; j < MTW; ++j) acc[j] = mfma_bf16(Ra[j][kk], bk, acc[j]);
+      }
+      FRNN_TRACE(6);
+      FRNN_TRACE_RT(6);
     }
     FRNN_TRACE(1);
 
@@ -729,6 +744,7 @@ __global__ void __launch_bounds__((NCW + 1) * 64, 1) fused_fwd_kernel(FusedArgs 
       }
     }
     FRNN_TRACE(5);
+    FRNN_TRACE_RT(5);
     // Keep the exchange stores ahead of the next step's polling in program order.
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     if (LOCAL) block_barrier();
