@@ -105,6 +105,13 @@ struct FusedLds {
   int h, part, wx, out, total;
 };
 
+// s_sleep units (64 clocks) before a step's first poll round. Polls compete with the stores
+// they wait for; holding back the first, certainly useless, round measured best at 4-6 units
+// (D=768 B=16: 1.35 -> 1.29 us per step), while pauses between later rounds only added latency.
+#ifndef FRNN_POLL_SLEEP0
+#define FRNN_POLL_SLEEP0 5
+#endif
+
 // Batch rows per group of the die-local design (bounds the polling registers).
 constexpr int FUSED_DIE_MAX_BR = 4;
 
@@ -616,6 +623,8 @@ __global__ void __launch_bounds__((NCW + 1) * 64, 1) fused_fwd_kernel(FusedArgs 
       uint64_t v[NP];
       long long t_first = 0;
       int spins = 0;
+      // nothing can have arrived yet (a store takes a few hundred ns to show on another CU)
+      if (t > 0) __builtin_amdgcn_s_sleep(FRNN_POLL_SLEEP0);
       while (true) {
 #pragma unroll
         for (int e = 0; e < NP; ++e) v[e] = __hip_atomic_load(src + off[e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
