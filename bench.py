@@ -41,6 +41,61 @@ def headwise_bytes(w, elt: int) -> float:
     return float(rd + wr)
 
 
+def kernel_sources_hash() -> str:
+    """First 16 hex digits of sha256 over the HIP sources (any change to them stales a traffic figure)."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "head_wise_lstm_amd", "csrc", "*"))):
+        h.update(os.path.basename(f).encode())
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def _counter_mean(csv_path: str, name_part: str) -> tuple:
+    """Mean Counter_Value (KiB per dispatch) over the dispatches of the kernels whose name holds name_part."""
+    import csv
+    vals, names = [], set()
+    with open(csv_path, newline="") as f:
+        for row in csv.DictReader(f):
+            if name_part in row["Kernel_Name"]:
+                vals.append(float(row["Counter_Value"]))
+                names.add(row["Kernel_Name"])
+    if not vals:
+        raise SystemExit(f"{csv_path}: no dispatch of a kernel named like {name_part!r}")
+    return sum(vals) / len(vals), len(vals), sorted(names)
+
+
+def write_traffic(args) -> None:
+    """Turn four rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE and WRITE_SIZE of the
+    benchmark, then of --copy-calibration) into a per-launch HBM byte figure in --traffic-json."""
+    import frnn_inputs as fi
+    fetch_csv, write_csv, fetch_copy_csv, write_copy_csv = args.write_traffic
+    kname = "fused_fwd_kernel" if args.path == "fused" else "alt_gemm_kernel"
+    true_kib = args.copy_mib * 1024.0
+    fc, _, _ = _counter_mean(fetch_copy_csv, "copyBuffer")
+    wc, _, _ = _counter_mean(write_copy_csv, "copyBuffer")
+    fk, nf, names = _counter_mean(fetch_csv, kname)
+    wk, nw, _ = _counter_mean(write_csv, kname)
+    ff, wf = true_kib / fc, true_kib / wc
+    w = fi.WORKLOADS[args.workload]
+    alg = headwise_bytes(w, 2 if "bf16" in w.name else 4)
+    rd, wr = fk * 1024 * ff, wk * 1024 * wf
+    entry = {"kernel": names[0], "dispatches": [nf, nw], "fetch_kib_per_dispatch": fk, "write_kib_per_dispatch": wk,
+             "fetch_factor": ff, "write_factor": wf, "copy_mib": args.copy_mib, "read_bytes": rd, "write_bytes": wr,
+             "bytes_per_launch": rd + wr, "algorithmic_bytes": alg, "kernel_sources_sha256_16": kernel_sources_hash()}
+    try:
+        with open(args.traffic_json) as f:
+            allt = json.load(f)
+    except (OSError, ValueError):
+        allt = {}
+    allt[f"{args.workload}:{args.path}"] = entry
+    with open(args.traffic_json, "w") as f:
+        json.dump(allt, f, indent=1)
+        f.write("\n")
+    print(json.dumps(entry))
+
+
 def cpu_baseline(w, sample_T: int):
     """The oracle as it stands, on all (batch, head) rows for the first sample_T steps."""
     import numpy as np
@@ -75,9 +130,16 @@ def main():
                     help="only run a plain device copy of MIB MiB (read MIB, write MIB), five times, for "
                          "scaling the HBM byte counters, and exit")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--write-traffic", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "FETCH_COPY_CSV", "WRITE_COPY_CSV"),
+                    help="only turn rocprofv3 FETCH_SIZE / WRITE_SIZE counter files of this workload and of "
+                         "--copy-calibration into the --traffic-json entry, and exit (no GPU needed)")
+    ap.add_argument("--copy-mib", type=int, default=256, help="size of the calibration copy (--write-traffic)")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="per-launch HBM bytes measured with rocprofv3 counters for this workload/path")
     args = ap.parse_args()
+    if args.write_traffic:
+        write_traffic(args)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the recurrence is built for a single MI355X and this "
               f"build has no multi-GPU path (asked for --gpus {args.gpus}).", file=sys.stderr)
@@ -174,12 +236,9 @@ def main():
     # HBM bytes per launch counted by rocprofv3 (FETCH_SIZE + WRITE_SIZE, calibrated on a plain
     # copy), valid only for the kernel source they were taken on
     try:
-        import hashlib
         with open(args.traffic_json) as f:
             tj = json.load(f).get(f"{config['workload']}:{args.path}")
-        src = os.path.join(ROOT, "head_wise_lstm_amd", "csrc", "frnn_fused.hpp")
-        cur = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
-        if tj and tj.get("kernel_source_sha256_16") == cur:
+        if tj and tj.get("kernel_sources_sha256_16") == kernel_sources_hash():
             roof["traffic"] = tj["bytes_per_launch"]
             roof["traffic_over_algorithmic"] = tj["bytes_per_launch"] / tj["algorithmic_bytes"]
     except (OSError, ValueError, KeyError):
