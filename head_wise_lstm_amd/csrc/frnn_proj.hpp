@@ -1,11 +1,13 @@
 // Input projection of the multi-layer LSTM ("5.3 LSTM": x_t . Wi + bias_ih + bias_hh) for all T
-// steps at once, as one MFMA GEMM:  C[M][Nc] (fp32) = A[M][K] . Bw[K][Nc] + b1[Nc] + b2[Nc].
-// A is bf16 or fp32 (converted to bf16 while staged), Bw and the biases bf16, row-major.
+// steps at once, as one MFMA GEMM:  C[M][Nc] (fp32) = A[M][K] . Wi[K][Nc] + b1[Nc] + b2[Nc].
+// A is bf16 or fp32 (rounded to bf16 as it is staged), Wi and the biases bf16, row-major.
 //
-// 128 x 128 output tile per workgroup, K staged 32 at a time through LDS, 4 waves in a 2 x 2
-// arrangement each owning 64 x 64 (4 x 4 tiles of v_mfma_f32_16x16x32_bf16). A is staged row-major
-// (the A fragment is 8 consecutive k of one row), Bw transposed to [n][k] (the B fragment is 8
-// consecutive k of one column), so every fragment read is one 16-byte LDS access.
+// Wi is first transposed to Bt[Nc][K] (proj_transpose_kernel), so that both operands are read
+// as rows of K: every global load is 16 contiguous bytes and every MFMA fragment one 16-byte LDS
+// read. The GEMM runs 256 x 128 output tiles per workgroup; each of the 4 waves owns 128 x 64
+// (8 x 4 tiles of v_mfma_f32_16x16x32_bf16, 32 accumulators), which keeps LDS traffic at about
+// 96 bytes per clock per CU. K goes 32 at a time through two LDS buffers: the next step's global
+// loads are in flight in registers while the current step's MFMAs run, one barrier per step.
 #pragma once
 
 #include "frnn_device.hpp"
@@ -13,91 +15,134 @@
 namespace frnn {
 
 struct ProjArgs {
-  int M, Nc, K;
+  int M, Nc, K;      // K a multiple of 32
   const void* A;
   int a_f32;
   long long lda;
-  const uint16_t* Bw;
-  long long ldb;
+  const uint16_t* Bt;  // [Nc][K] bf16 (Wi transposed)
   const uint16_t* b1;
   const uint16_t* b2;
   float* C;
   long long ldc;
 };
 
-constexpr int PJ_BM = 128, PJ_BN = 128, PJ_BK = 32, PJ_LS = PJ_BK + 8;
+constexpr int PJ_BM = 256, PJ_BN = 128, PJ_BK = 32;
+constexpr int PJ_DIES = 8;  // accelerator dies (XCDs) of an MI355X
+constexpr int PJ_LS = PJ_BK + 8;  // LDS row stride (bf16): 80 bytes, spreads a fragment's rows over the banks
 
-__global__ void __launch_bounds__(256) proj_gemm_kernel(ProjArgs p) {
-  __shared__ __attribute__((aligned(16))) uint16_t As[PJ_BM * PJ_LS];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[PJ_BN * PJ_LS];
+// Wi [K][Nc] -> Bt [Nc][K], 32 x 32 tiles through LDS.
+__global__ void __launch_bounds__(256) proj_transpose_kernel(const uint16_t* Wi, long long ldw, int K, int Nc,
+                                                             uint16_t* Bt) {
+  __shared__ uint16_t s[32][33];
+  const int k0 = blockIdx.y * 32, n0 = blockIdx.x * 32;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;  // 32 x 8
+#pragma unroll
+  for (int i = 0; i < 32; i += 8) {
+    const int k = k0 + ty + i, n = n0 + tx;
+    s[ty + i][tx] = (k < K && n < Nc) ? Wi[(long long)k * ldw + n] : (uint16_t)0;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 32; i += 8) {
+    const int n = n0 + ty + i, k = k0 + tx;
+    if (n < Nc && k < K) Bt[(long long)n * K + k] = s[tx][ty + i];
+  }
+}
+
+// 8 bf16 of row `r` (of rows valid below `rows`), k = k0 .. k0+7: 16 bytes (bf16 source) or
+// 32 bytes rounded to bf16 (fp32 source); rows past the end read as zeros.
+__device__ __forceinline__ u32x4_t proj_load8(const void* base, int f32, long long ld, long long r, long long rows,
+                                              int k) {
+  u32x4_t v = {0u, 0u, 0u, 0u};
+  if (r >= rows) return v;
+  if (f32) {
+    const float* p = reinterpret_cast<const float*>(base) + r * ld + k;
+    const f32x4_t x0 = *reinterpret_cast<const f32x4_t*>(p);
+    const f32x4_t x1 = *reinterpret_cast<const f32x4_t*>(p + 4);
+    v[0] = (uint32_t)f2bf(x0[0]) | ((uint32_t)f2bf(x0[1]) << 16);
+    v[1] = (uint32_t)f2bf(x0[2]) | ((uint32_t)f2bf(x0[3]) << 16);
+    v[2] = (uint32_t)f2bf(x1[0]) | ((uint32_t)f2bf(x1[1]) << 16);
+    v[3] = (uint32_t)f2bf(x1[2]) | ((uint32_t)f2bf(x1[3]) << 16);
+  } else {
+    v = *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const uint16_t*>(base) + r * ld + k);
+  }
+  return v;
+}
+
+__global__ void __launch_bounds__(256, 2) proj_gemm_kernel(ProjArgs p) {
+  // two stages of A (256 x 32) and B (128 x 32), rows padded to PJ_LS
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][PJ_BM * PJ_LS];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][PJ_BN * PJ_LS];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int col = lane & 15, quad = lane >> 4;
-  const int wm = wave >> 1, wn = wave & 1;
-  const long long m0 = (long long)blockIdx.y * PJ_BM;
-  const int n0 = blockIdx.x * PJ_BN;
+  const int wm = wave >> 1, wn = wave & 1;  // wave tile: rows wm*128 .., columns wn*64 ..
+  // Die-aware tile order. Workgroups are dealt to the 8 dies round-robin by index, so the die of
+  // workgroup L is L % 8. Tiles are numbered row-major (M tile, then N tile) and each die takes a
+  // contiguous run of them: the N tiles that share an A tile run on one die and read A once into
+  // its L2 (dealt in index order, the A tile would be read by every die).
+  const int ntn = (p.Nc + PJ_BN - 1) / PJ_BN;
+  const int L = blockIdx.x, G = gridDim.x;
+  const int tile = (G % PJ_DIES == 0) ? (L % PJ_DIES) * (G / PJ_DIES) + L / PJ_DIES : L;
+  const long long m0 = (long long)(tile / ntn) * PJ_BM;
+  const int n0 = (tile % ntn) * PJ_BN;
 
-  f32x4_t acc[4][4];
+  // global -> register staging: A 256 rows x 4 chunks of 8 k (4 per thread), B 128 x 4 (2 per
+  // thread); chunk c of thread tid is row (tid + 256 c) / 4, k-chunk tid % 4
+  u32x4_t ra[4], rb[2];
+  const int lrow = tid >> 2, lkc = (tid & 3) * 8;
+  f32x4_t acc[8][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 8; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  for (int k0 = 0; k0 < p.K; k0 += PJ_BK) {
-    // A tile: 128 rows x 32 k; thread -> row tid/2, 16 consecutive k.
-    {
-      const int r = tid >> 1, kh = (tid & 1) * 16;
-      const long long gm = m0 + r;
-      uint16_t v[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int gk = k0 + kh + i;
-        float f = 0.0f;
-        if (gm < p.M && gk < p.K) {
-          const long long off = gm * p.lda + gk;
-          f = p.a_f32 ? reinterpret_cast<const float*>(p.A)[off] : bf2f(reinterpret_cast<const uint16_t*>(p.A)[off]);
-        }
-        v[i] = p.a_f32 ? f2bf(f) : (uint16_t)(__float_as_uint(f) >> 16);
-      }
-#pragma unroll
-      for (int i = 0; i < 16; i += 2)
-        *reinterpret_cast<uint32_t*>(&As[r * PJ_LS + kh + i]) = (uint32_t)v[i] | ((uint32_t)v[i + 1] << 16);
-    }
-    // Bw tile: 32 k x 128 n, stored transposed; thread -> k row tid/8, 16 consecutive n.
-    {
-      const int kr = tid >> 3, nb = (tid & 7) * 16;
-      const int gk = k0 + kr;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int gn = n0 + nb + i;
-        const uint16_t v = (gk < p.K && gn < p.Nc) ? p.Bw[(long long)gk * p.ldb + gn] : (uint16_t)0;
-        Bs[(nb + i) * PJ_LS + kr] = v;
-      }
-    }
-    __syncthreads();
-    bf16x8_t af[4], bfr[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      af[i] = *reinterpret_cast<const bf16x8_t*>(&As[(wm * 64 + i * 16 + col) * PJ_LS + 8 * quad]);
+  const int nk = p.K / PJ_BK;
+#define PJ_GLOAD(K0)                                                                              \
+  do {                                                                                            \
+    _Pragma("unroll") for (int c = 0; c < 4; ++c)                                                 \
+      ra[c] = proj_load8(p.A, p.a_f32, p.lda, m0 + lrow + 64 * c, p.M, (K0) + lkc);               \
+    _Pragma("unroll") for (int c = 0; c < 2; ++c)                                                 \
+      rb[c] = proj_load8(p.Bt, 0, p.K, (long long)n0 + lrow + 64 * c, p.Nc, (K0) + lkc);          \
+  } while (0)
+#define PJ_LSTORE(ST)                                                                             \
+  do {                                                                                            \
+    _Pragma("unroll") for (int c = 0; c < 4; ++c)                                                 \
+      *reinterpret_cast<u32x4_t*>(&As[ST][(lrow + 64 * c) * PJ_LS + lkc]) = ra[c];                \
+    _Pragma("unroll") for (int c = 0; c < 2; ++c)                                                 \
+      *reinterpret_cast<u32x4_t*>(&Bs[ST][(lrow + 64 * c) * PJ_LS + lkc]) = rb[c];                \
+  } while (0)
+  PJ_GLOAD(0);
+  PJ_LSTORE(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int st = kt & 1;
+    if (kt + 1 < nk) PJ_GLOAD((kt + 1) * PJ_BK);
+    bf16x8_t bfr[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      bfr[j] = *reinterpret_cast<const bf16x8_t*>(&Bs[(wn * 64 + j * 16 + col) * PJ_LS + 8 * quad]);
+      bfr[j] = *reinterpret_cast<const bf16x8_t*>(&Bs[st][(wn * 64 + j * 16 + col) * PJ_LS + 8 * quad]);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 8; ++i) {
+      const bf16x8_t af = *reinterpret_cast<const bf16x8_t*>(&As[st][(wm * 128 + i * 16 + col) * PJ_LS + 8 * quad]);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = mfma_bf16(af[i], bfr[j], acc[i][j]);
+      for (int j = 0; j < 4; ++j) acc[i][j] = mfma_bf16(af, bfr[j], acc[i][j]);
+    }
+    if (kt + 1 < nk) PJ_LSTORE(st ^ 1);
     __syncthreads();
   }
-  // Epilogue: lane holds rows 4*quad + r of column col of every 16 x 16 tile.
+#undef PJ_GLOAD
+#undef PJ_LSTORE
+  // Epilogue: lane (col, quad) holds rows 4*quad + r of column col of every 16 x 16 tile.
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int gn = n0 + wn * 64 + j * 16 + col;
     if (gn >= p.Nc) continue;
     const float bias = (p.b1 ? bf2f(p.b1[gn]) : 0.0f) + (p.b2 ? bf2f(p.b2[gn]) : 0.0f);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 8; ++i) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const long long gm = m0 + wm * 64 + i * 16 + 4 * quad + r;
+        const long long gm = m0 + wm * 128 + i * 16 + 4 * quad + r;
         if (gm < p.M) p.C[gm * p.ldc + gn] = acc[i][j][r] + bias;
       }
     }
