@@ -53,42 +53,58 @@ __global__ void __launch_bounds__(256) alt_init_kernel(AltArgs a) {
   }
 }
 
-// Per step: grid (ceil(TPH/4), ceil(B/16), N), 4 waves, one R^T tile per wave, full K.
-// Four independent accumulators break the MFMA dependency chain.
+// Per step: grid (TPH, ceil(B/16), N), one R^T tile per workgroup. The 4 waves take the tile's
+// k-tiles 4 apart (wave w: w, w+4, ...), each with two accumulators, so that every wave has a
+// quarter of the fragment loads in flight at once; the four partial sums meet in LDS.
 template <bool F32>
 __global__ void __launch_bounds__(256) alt_gemm_kernel(AltArgs a) {
+  __shared__ f32x4_t part[4][64];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int col = lane & 15, quad = lane >> 4;
   const int G = a.cell == CELL_LSTM ? 4 : 1;
   const int TPH = G * a.D / 16;
-  const int tt = blockIdx.x * 4 + wave;
+  const int tt = blockIdx.x;
   const int b0 = blockIdx.y * 16;
   const int n = blockIdx.z;
-  if (tt >= TPH) return;
   const int KW = F32 ? 4 : 32;
   const int KT = a.D / KW;
   const bool colv = b0 + col < a.B;
-  f32x4_t acc[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
   if constexpr (F32) {
     const float* rp = reinterpret_cast<const float*>(a.rpack) + ((long long)n * TPH + tt) * KT * 64 + lane;
     const float* hp = reinterpret_cast<const float*>(a.hcur) + ((long long)n * a.B + b0 + col) * a.D + quad;
-    for (int kt = 0; kt < KT; ++kt) {
-      const float bv = colv ? hp[kt * 4] : 0.0f;
-      acc[kt & 3] = mfma_f32(rp[(long long)kt * 64], bv, acc[kt & 3]);
+    int kt = wave;
+    for (; kt + 4 < KT; kt += 8) {
+      const float a0 = rp[(long long)kt * 64], a1 = rp[(long long)(kt + 4) * 64];
+      const float h0 = colv ? hp[kt * 4] : 0.0f, h1 = colv ? hp[(kt + 4) * 4] : 0.0f;
+      acc0 = mfma_f32(a0, h0, acc0);
+      acc1 = mfma_f32(a1, h1, acc1);
     }
+    if (kt < KT) acc0 = mfma_f32(rp[(long long)kt * 64], colv ? hp[kt * 4] : 0.0f, acc0);
   } else {
     const u32x4_t* rp = reinterpret_cast<const u32x4_t*>(a.rpack) + ((long long)n * TPH + tt) * KT * 64 + lane;
     const uint16_t* hp = reinterpret_cast<const uint16_t*>(a.hcur) + ((long long)n * a.B + b0 + col) * a.D + 8 * quad;
-    for (int kt = 0; kt < KT; ++kt) {
-      u32x4_t bv = {0u, 0u, 0u, 0u};
-      if (colv) bv = *reinterpret_cast<const u32x4_t*>(hp + kt * 32);
-      acc[kt & 3] = mfma_bf16(__builtin_bit_cast(bf16x8_t, rp[(long long)kt * 64]), __builtin_bit_cast(bf16x8_t, bv), acc[kt & 3]);
+    int kt = wave;
+    for (; kt + 4 < KT; kt += 8) {
+      const u32x4_t a0 = rp[(long long)kt * 64], a1 = rp[(long long)(kt + 4) * 64];
+      u32x4_t h0 = {0u, 0u, 0u, 0u}, h1 = {0u, 0u, 0u, 0u};
+      if (colv) {
+        h0 = *reinterpret_cast<const u32x4_t*>(hp + kt * 32);
+        h1 = *reinterpret_cast<const u32x4_t*>(hp + (kt + 4) * 32);
+      }
+      acc0 = mfma_bf16(__builtin_bit_cast(bf16x8_t, a0), __builtin_bit_cast(bf16x8_t, h0), acc0);
+      acc1 = mfma_bf16(__builtin_bit_cast(bf16x8_t, a1), __builtin_bit_cast(bf16x8_t, h1), acc1);
+    }
+    if (kt < KT) {
+      u32x4_t h0 = {0u, 0u, 0u, 0u};
+      if (colv) h0 = *reinterpret_cast<const u32x4_t*>(hp + kt * 32);
+      acc0 = mfma_bf16(__builtin_bit_cast(bf16x8_t, rp[(long long)kt * 64]), __builtin_bit_cast(bf16x8_t, h0), acc0);
     }
   }
-  const f32x4_t s = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-  if (!colv) return;
+  part[wave][lane] = acc0 + acc1;
+  __syncthreads();
+  if (wave != 0 || !colv) return;
+  const f32x4_t s = (part[0][lane] + part[1][lane]) + (part[2][lane] + part[3][lane]);
   const long long b = b0 + col;
   if (a.cell == CELL_LSTM) {
     const int u = 4 * tt + quad;

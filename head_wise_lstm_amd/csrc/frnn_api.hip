@@ -333,7 +333,7 @@ std::string plan_string(const Problem& p, int path, const FusedPlan* fp) {
     std::snprintf(buf, sizeof(buf),
                   "alternating cell=%s dtype=%s B=%d T=%d N=%d D=%d gemm_grid=(%d,%d,%d) gate_grid=%lld launches=%d",
                   p.cell == FRNN_CELL_LSTM ? "lstm" : "elman", p.r_f32 ? "f32" : "bf16", p.B, p.T, p.N, p.D,
-                  (TPH + 3) / 4, (p.B + 15) / 16, p.N, ((long long)p.B * p.N * p.D + 255) / 256, 2 * p.T + 2);
+                  TPH, (p.B + 15) / 16, p.N, ((long long)p.B * p.N * p.D + 255) / 256, 2 * p.T + 2);
   }
   return std::string(buf);
 }
@@ -412,7 +412,7 @@ int run_recurrence(const Problem& p, int path, int* err, void* scratch, hipStrea
   if (launch_rpack(p, a.rpack, st) != hipSuccess) return FRNN_EHIP;
   const long long nstate = (long long)p.B * p.N * p.D;
   hipLaunchKernelGGL(alt_init_kernel, dim3((unsigned)std::min<long long>((nstate + 255) / 256, 4096)), dim3(256), 0, st, a);
-  const dim3 ggrid((TPH + 3) / 4, (p.B + 15) / 16, p.N);
+  const dim3 ggrid(TPH, (p.B + 15) / 16, p.N);
   const dim3 tgrid((unsigned)((nstate + 255) / 256));
   for (int t = 0; t < p.T; ++t) {
     if (p.r_f32) hipLaunchKernelGGL(alt_gemm_kernel<true>, ggrid, dim3(256), 0, st, a);
