@@ -195,7 +195,7 @@ int plan_fused(const Problem& p, const DevInfo& di, FusedPlan* out) {
       if (!v) continue;
       const int per_wave = mtw * KT;
       // the I/O wave moves at most 64 * epl words of Wx and as many output pairs per step
-      const int epl = fused_epl(true, ncw);
+      const int epl = fused_epl(true, ncw, p.cell);
       const int words_per_row = G * p.D / (p.wx_f32 ? 2 : 4);
       const int br_cap = std::min(16, std::min(64 * epl / words_per_row, 64 * epl * 2 / p.D));
       if (br_cap < 1 || (per_wave > 64 && force_w != 1)) continue;
@@ -248,7 +248,7 @@ int plan_fused(const Problem& p, const DevInfo& di, FusedPlan* out) {
         // the packed K-split partials hold BRP batch columns per tile; the polls cover that many rows
         if (BR > fused_max_br(ks, mtw)) continue;
         // the I/O wave moves at most 64 * epl words of Wx and as many output pairs per step
-        const int epl = fused_epl(false, ncw);
+        const int epl = fused_epl(false, ncw, p.cell);
         if (BR * G * u_wg / (p.wx_f32 ? 2 : 4) > 64 * epl || BR * u_wg / 2 > 64 * epl) continue;
         FusedPlan fp;
         fp.v = v;

@@ -91,8 +91,11 @@ struct FusedArgs {
 
 constexpr int FUSED_IO_STAGES = 4;   // Wx steps in flight in the I/O wave
 // max 64-bit Wx words (and output pairs) one I/O lane moves per step: the die-local design moves
-// few (its workgroups own few units), the single-workgroup design a whole head's rows
-__host__ __device__ constexpr int fused_epl(bool local, int ncw) { return !local ? 2 : (ncw == 4 ? 8 : 4); }
+// few (its workgroups own few units), the single-workgroup design a whole head's rows (an Elman
+// head has a quarter of an LSTM head's Wx and half its outputs). Every slot costs a load per step.
+__host__ __device__ constexpr int fused_epl(bool local, int ncw, int cell) {
+  return !local ? 2 : (cell == CELL_ELMAN ? 2 : (ncw == 4 ? 8 : 4));
+}
 
 __host__ __device__ constexpr int fused_hpad(bool f32) { return f32 ? 4 : 8; }
 // gated tiles per compute wave (NCW compute waves, K split KS ways, MTW tiles per wave)
@@ -475,7 +478,7 @@ __global__ void __launch_bounds__((NCW + 1) * 64, 1) fused_fwd_kernel(FusedArgs 
     c.U_wg = U_wg;
     c.u_base = u_base;
     c.lane = lane;
-    io_wave<CELL, NCW, KS, MTW, fused_epl(LOCAL, NCW), G0>(c, wxs, outs, &s_abort);
+    io_wave<CELL, NCW, KS, MTW, fused_epl(LOCAL, NCW, CELL), G0>(c, wxs, outs, &s_abort);
     return;
   }
 
