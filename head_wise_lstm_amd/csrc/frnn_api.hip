@@ -652,8 +652,9 @@ int frnn_lstm_stack_fwd(int L, int T, int B, int I, int H, int path, const void*
     pa.ldc = 4 * H;
     hipLaunchKernelGGL(proj_transpose_kernel, dim3((pa.Nc + 31) / 32, (pa.K + 31) / 32), dim3(256), 0, st,
                        reinterpret_cast<const uint16_t*>(Wi[l]), (long long)pa.Nc, pa.K, pa.Nc, wit);
-    hipLaunchKernelGGL(proj_gemm_kernel, dim3(((pa.Nc + PJ_BN - 1) / PJ_BN) * ((pa.M + PJ_BM - 1) / PJ_BM)), dim3(256), 0,
-                       st, pa);
+    const dim3 pgrid(((pa.Nc + PJ_BN - 1) / PJ_BN) * ((pa.M + PJ_BM - 1) / PJ_BM));
+    if (pa.a_f32) hipLaunchKernelGGL(proj_gemm_kernel<true>, pgrid, dim3(256), 0, st, pa);
+    else hipLaunchKernelGGL(proj_gemm_kernel<false>, pgrid, dim3(256), 0, st, pa);
     if (hipGetLastError() != hipSuccess) return FRNN_EHIP;
     // recurrence with Wh [H, 4H] read through strides: R[g][0][d][e] = Wh[d][g*H + e]
     Problem p;

@@ -10,6 +10,8 @@
 // loads are in flight in registers while the current step's MFMAs run, one barrier per step.
 #pragma once
 
+#include <type_traits>
+
 #include "frnn_device.hpp"
 
 namespace frnn {
@@ -49,26 +51,45 @@ __global__ void __launch_bounds__(256) proj_transpose_kernel(const uint16_t* Wi,
   }
 }
 
-// 8 bf16 of row `r` (of rows valid below `rows`), k = k0 .. k0+7: 16 bytes (bf16 source) or
-// 32 bytes rounded to bf16 (fp32 source); rows past the end read as zeros.
-__device__ __forceinline__ u32x4_t proj_load8(const void* base, int f32, long long ld, long long r, long long rows,
-                                              int k) {
-  u32x4_t v = {0u, 0u, 0u, 0u};
-  if (r >= rows) return v;
-  if (f32) {
-    const float* p = reinterpret_cast<const float*>(base) + r * ld + k;
-    const f32x4_t x0 = *reinterpret_cast<const f32x4_t*>(p);
-    const f32x4_t x1 = *reinterpret_cast<const f32x4_t*>(p + 4);
-    v[0] = (uint32_t)f2bf(x0[0]) | ((uint32_t)f2bf(x0[1]) << 16);
-    v[1] = (uint32_t)f2bf(x0[2]) | ((uint32_t)f2bf(x0[3]) << 16);
-    v[2] = (uint32_t)f2bf(x1[0]) | ((uint32_t)f2bf(x1[1]) << 16);
-    v[3] = (uint32_t)f2bf(x1[2]) | ((uint32_t)f2bf(x1[3]) << 16);
+// Staging of 8 consecutive k of one row in registers: 16 bytes of bf16, or 32 bytes of fp32 kept
+// raw (rounded to bf16 only when written to LDS, so that no load is waited for when issued).
+template <bool F32>
+struct Stage8 {
+  typename std::conditional<F32, f32x4_t, u32x4_t>::type v[F32 ? 2 : 1];
+};
+
+template <bool F32>
+__device__ __forceinline__ void proj_load8(Stage8<F32>& st, const void* base, long long ld, long long r, long long rows,
+                                           int k) {
+  const bool ok = r < rows;
+  const long long rr = ok ? r : 0;  // rows past the end load row 0 and are zeroed when stored
+  if constexpr (F32) {
+    const float* p = reinterpret_cast<const float*>(base) + rr * ld + k;
+    st.v[0] = *reinterpret_cast<const f32x4_t*>(p);
+    st.v[1] = *reinterpret_cast<const f32x4_t*>(p + 4);
+    if (!ok) st.v[0] = st.v[1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   } else {
-    v = *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const uint16_t*>(base) + r * ld + k);
+    st.v[0] = *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const uint16_t*>(base) + rr * ld + k);
+    if (!ok) st.v[0] = u32x4_t{0u, 0u, 0u, 0u};
   }
-  return v;
 }
 
+template <bool F32>
+__device__ __forceinline__ void proj_store8(uint16_t* dst, const Stage8<F32>& st) {
+  u32x4_t v;
+  if constexpr (F32) {
+    v[0] = (uint32_t)f2bf(st.v[0][0]) | ((uint32_t)f2bf(st.v[0][1]) << 16);
+    v[1] = (uint32_t)f2bf(st.v[0][2]) | ((uint32_t)f2bf(st.v[0][3]) << 16);
+    v[2] = (uint32_t)f2bf(st.v[1][0]) | ((uint32_t)f2bf(st.v[1][1]) << 16);
+    v[3] = (uint32_t)f2bf(st.v[1][2]) | ((uint32_t)f2bf(st.v[1][3]) << 16);
+  } else {
+    v = st.v[0];
+  }
+  *reinterpret_cast<u32x4_t*>(dst) = v;
+}
+
+// AF32: A is fp32. Two workgroups per CU: while one waits for its loads, the other multiplies.
+template <bool AF32>
 __global__ void __launch_bounds__(256, 2) proj_gemm_kernel(ProjArgs p) {
   // two stages of A (256 x 32) and B (128 x 32), rows padded to PJ_LS
   __shared__ __attribute__((aligned(16))) uint16_t As[2][PJ_BM * PJ_LS];
@@ -86,9 +107,10 @@ __global__ void __launch_bounds__(256, 2) proj_gemm_kernel(ProjArgs p) {
   const long long m0 = (long long)(tile / ntn) * PJ_BM;
   const int n0 = (tile % ntn) * PJ_BN;
 
-  // global -> register staging: A 256 rows x 4 chunks of 8 k (4 per thread), B 128 x 4 (2 per
-  // thread); chunk c of thread tid is row (tid + 256 c) / 4, k-chunk tid % 4
-  u32x4_t ra[4], rb[2];
+  // global -> register staging of the next K step: A 256 rows x 4 chunks of 8 k (4 per thread),
+  // B 128 x 4 (2 per thread); chunk c of thread tid is row tid / 4 + 64 c, k-chunk tid % 4
+  Stage8<AF32> ra[4];
+  Stage8<false> rb[2];
   const int lrow = tid >> 2, lkc = (tid & 3) * 8;
   f32x4_t acc[8][4];
 #pragma unroll
@@ -100,16 +122,16 @@ __global__ void __launch_bounds__(256, 2) proj_gemm_kernel(ProjArgs p) {
 #define PJ_GLOAD(K0)                                                                              \
   do {                                                                                            \
     _Pragma("unroll") for (int c = 0; c < 4; ++c)                                                 \
-      ra[c] = proj_load8(p.A, p.a_f32, p.lda, m0 + lrow + 64 * c, p.M, (K0) + lkc);               \
+      proj_load8<AF32>(ra[c], p.A, p.lda, m0 + lrow + 64 * c, p.M, (K0) + lkc);                   \
     _Pragma("unroll") for (int c = 0; c < 2; ++c)                                                 \
-      rb[c] = proj_load8(p.Bt, 0, p.K, (long long)n0 + lrow + 64 * c, p.Nc, (K0) + lkc);          \
+      proj_load8<false>(rb[c], p.Bt, p.K, (long long)n0 + lrow + 64 * c, p.Nc, (K0) + lkc);       \
   } while (0)
 #define PJ_LSTORE(ST)                                                                             \
   do {                                                                                            \
     _Pragma("unroll") for (int c = 0; c < 4; ++c)                                                 \
-      *reinterpret_cast<u32x4_t*>(&As[ST][(lrow + 64 * c) * PJ_LS + lkc]) = ra[c];                \
+      proj_store8<AF32>(&As[ST][(lrow + 64 * c) * PJ_LS + lkc], ra[c]);                           \
     _Pragma("unroll") for (int c = 0; c < 2; ++c)                                                 \
-      *reinterpret_cast<u32x4_t*>(&Bs[ST][(lrow + 64 * c) * PJ_LS + lkc]) = rb[c];                \
+      proj_store8<false>(&Bs[ST][(lrow + 64 * c) * PJ_LS + lkc], rb[c]);                          \
   } while (0)
   PJ_GLOAD(0);
   PJ_LSTORE(0);
