@@ -121,11 +121,40 @@ FORCED = [
      {"FRNN_FUSED_NCW": 8}),
     (fi.HeadwiseWorkload("lstm_D768_4waves", "lstm", torch.bfloat16, B=16, T=9, N=1, D=768, seed=126, s0_var=1.0),
      {"FRNN_FUSED_NCW": 4}),
+    (fi.HeadwiseWorkload("lstm_D512_W16_4waves", "lstm", torch.bfloat16, B=3, T=6, N=1, D=512, seed=127, s0_var=1.0),
+     {"FRNN_FUSED_W": 16, "FRNN_FUSED_NCW": 4, "FRNN_FUSED_BR": 2}),
+    (fi.HeadwiseWorkload("lstm_D512_W16_8waves", "lstm", torch.bfloat16, B=5, T=5, N=1, D=512, seed=128, s0_var=1.0),
+     {"FRNN_FUSED_W": 16, "FRNN_FUSED_NCW": 8, "FRNN_FUSED_BR": 2}),
+    (fi.HeadwiseWorkload("lstm_D256_W16_8waves", "lstm", torch.bfloat16, B=5, T=7, N=2, D=256, seed=129, s0_var=1.0),
+     {"FRNN_FUSED_W": 16, "FRNN_FUSED_NCW": 8, "FRNN_FUSED_BR": 2}),
 ]
+
+# the design each forced case must get (compute waves, K split, tiles and k-tiles per wave)
+FORCED_PLAN = {
+    "lstm_D768_8waves": "NCW=8 KS=8 MTW=6 KTW=3",
+    "lstm_D768_4waves": "NCW=4 KS=4 MTW=6 KTW=6",
+    "lstm_D512_W16_4waves": "NCW=4 KS=4 MTW=8 KTW=4",
+    "lstm_D512_W16_8waves": "NCW=8 KS=8 MTW=8 KTW=2",
+    "lstm_D256_W16_8waves": "NCW=8 KS=8 MTW=4 KTW=1",
+}
 
 
 @pytest.mark.parametrize("w,env", FORCED, ids=lambda x: getattr(x, "name", ""))
 def test_forced_die_local(w, env):
+    hw = _hw()
+    old = {k: os.environ.get(k) for k in env}
+    os.environ.update({k: str(v) for k, v in env.items()})
+    try:
+        plan = hw.frnn_plan_str(hw._desc(w.B, w.T, w.N, w.D, w.cell, w.dtype), "fused")
+    finally:
+        for k, v in old.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+    assert "die-local" in plan, plan
+    if w.name in FORCED_PLAN:
+        assert FORCED_PLAN[w.name] in plan, plan
     run_case(w, "fused", env=env)
 
 
