@@ -10,14 +10,16 @@ The arithmetic lives in ``frnn_oracle.c`` (plain C, double precision, OpenMP ove
 * ``headwise_fwd`` -- FlashRNN usage example (hottg.com/neural/9889): layouts Wx[B,T,G,N,D],
   R[G,N,D,D], b[G,N,D], states[S,B,T,N,D], last_states[S,B,1,N,D]; the cell is the one of
   "5.3 LSTM" (developnotes.readthedocs.io, operator.html) applied per head, gates i, f, z, o along
-  G; Elman: h = tanh(Wx + h.R + b).
+  G; Elman: h = tanh(Wx + h.R + b); GRU (named in the FlashRNN cell list, equations not printed):
+  the textbook cell with gates r, z, n along G, the reset gate scaling the candidate's recurrent
+  part h.R_n + b_n, h' = (1 - z) n + z h, S = 1.
 * ``lstm_stack_p3`` -- "5.3 LSTM", MyLSTM.set_weights and MyLSTM.forward: time loop outermost,
   layers inside it, bias = bias_ih + bias_hh, Wi stored [in, 4H], Wh stored [H, 4H].
 
 Pins (tests/test_oracle_pins.py): closed forms (R = 0 geometric gating, saturated forget gate,
-Elman scalar iteration) computed independently at 40 significant digits, torch.nn.LSTM / nn.RNN in
-float64 as library special cases, head / batch / continuation invariants, and hand-stepped tiny
-cases.
+Elman and GRU scalar iterations) computed independently at 50 significant digits, GRU closed forms
+(R = 0, saturated update gate, shut reset gate), torch.nn.LSTM / nn.RNN / nn.GRU in float64 as
+library special cases, head / batch / continuation invariants, and hand-stepped tiny cases.
 """
 from __future__ import annotations
 
@@ -33,6 +35,7 @@ LIB_PATH = os.path.join(_HERE, "liboracle.so")
 
 CELL_LSTM = 0
 CELL_ELMAN = 1
+CELL_GRU = 2
 
 
 def build(verbose: bool = False, source: str = SOURCE, out: str = LIB_PATH) -> str:
@@ -86,8 +89,8 @@ class Oracle:
         (zeros). ``pairs``: optional iterable of flattened (b*N + n) rows to compute (the others
         stay NaN). Returns (states [S,B,T,N,D] or None, last_states [S,B,1,N,D]).
         """
-        c = {"lstm": CELL_LSTM, "elman": CELL_ELMAN}[cell]
-        G, S = (4, 2) if c == CELL_LSTM else (1, 1)
+        c = {"lstm": CELL_LSTM, "elman": CELL_ELMAN, "gru": CELL_GRU}[cell]
+        G, S = {CELL_LSTM: (4, 2), CELL_ELMAN: (1, 1), CELL_GRU: (3, 1)}[c]
         Wx, R = _f64(Wx), _f64(R)
         B, T, G_, N, D = Wx.shape
         b = np.zeros((G, N, D)) if b is None else _f64(b)

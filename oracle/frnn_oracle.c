@@ -1,5 +1,5 @@
 /*
- * frnn_oracle.c -- plain, slow, fp64 CPU oracle for the head-wise LSTM / Elman forward recurrence
+ * frnn_oracle.c -- plain, slow, fp64 CPU oracle for the head-wise LSTM / Elman / GRU forward recurrence
  * and for the plain multi-layer LSTM.
  *
  * TEST INFRASTRUCTURE ONLY. Nothing on the product path may link, load or call this file: it is
@@ -18,6 +18,13 @@
  *  - The head-wise reading: the 5.3 cell applied independently to every head n with that head's
  *    recurrent matrix R[:, n] (h as a row vector: pre[g][e] = sum_d h[d] * R[g,n,d,e]), the gate
  *    order along G being i, f, z (=g), o. Elman: h = tanh(Wx + h*R + b), G = 1, S = 1.
+ *  - GRU (named in the FlashRNN page's list of cells, equations not printed): the textbook gated
+ *    recurrent unit in the form where the reset gate scales the recurrent part of the candidate
+ *    after its matrix product. G = 3 (r, z, n), S = 1. With a = h*R per gate:
+ *      r = sigmoid(Wx_r + a_r + b_r),  z = sigmoid(Wx_z + a_z + b_z),
+ *      n = tanh(Wx_n + r * (a_n + b_n)),  h_new = (1 - z) * n + z * h.
+ *    Wx carries the input-side terms (the input projection and its biases); b holds the
+ *    recurrent-side biases, b_n being the one inside the reset product.
  *
  * Everything is computed in double precision; inputs arrive already widened (exactly) to double.
  * Summation over d runs d = 0..D-1 in order for every output e. No blocking, fusion or reordering.
@@ -31,6 +38,7 @@
 
 #define ORACLE_CELL_LSTM 0
 #define ORACLE_CELL_ELMAN 1
+#define ORACLE_CELL_GRU 2
 
 /* Logistic sigmoid, textbook definition (5.3 LSTM: torch.sigmoid). */
 static double sigmoid(double x) { return 1.0 / (1.0 + exp(-x)); }
@@ -51,9 +59,9 @@ int oracle_abi_version(void) { return 1; }
 int oracle_headwise_fwd(int cell, long B, long T, long N, long D, const double* Wx, const double* R,
                         const double* b, const double* states0, double* states, double* last,
                         const long* pairs, long npairs) {
-  if (cell != ORACLE_CELL_LSTM && cell != ORACLE_CELL_ELMAN) return -1;
+  if (cell != ORACLE_CELL_LSTM && cell != ORACLE_CELL_ELMAN && cell != ORACLE_CELL_GRU) return -1;
   if (B <= 0 || N <= 0 || D <= 0 || T < 0) return -1;
-  const long G = (cell == ORACLE_CELL_LSTM) ? 4 : 1;
+  const long G = (cell == ORACLE_CELL_LSTM) ? 4 : (cell == ORACLE_CELL_GRU) ? 3 : 1;
   const long S = (cell == ORACLE_CELL_LSTM) ? 2 : 1;
   const long count = pairs ? npairs : B * N;
   int failed = 0;
@@ -88,9 +96,12 @@ int oracle_headwise_fwd(int cell, long B, long T, long N, long D, const double* 
           const double* row = R + ((g * N + n) * D + d) * D;
           for (long e = 0; e < D; ++e) a[e] += hd * row[e];
         }
-        /* pre-activation = Wx + R.h + b, in the order the equation is written */
-        for (long e = 0; e < D; ++e)
-          pre[g * D + e] = Wx[(((bi * T + t) * G + g) * N + n) * D + e] + a[e] + b[(g * N + n) * D + e];
+        /* pre-activation = Wx + R.h + b, in the order the equation is written (the GRU candidate
+           keeps its recurrent part a_n + b_n apart: the reset gate scales it below) */
+        for (long e = 0; e < D; ++e) {
+          if (cell == ORACLE_CELL_GRU && g == 2) pre[g * D + e] = a[e] + b[(g * N + n) * D + e];
+          else pre[g * D + e] = Wx[(((bi * T + t) * G + g) * N + n) * D + e] + a[e] + b[(g * N + n) * D + e];
+        }
       }
       if (cell == ORACLE_CELL_LSTM) {
         for (long e = 0; e < D; ++e) {
@@ -100,6 +111,13 @@ int oracle_headwise_fwd(int cell, long B, long T, long N, long D, const double* 
           const double og = sigmoid(pre[3 * D + e]);
           c[e] = fg * c[e] + ig * zg;
           hn[e] = og * tanh(c[e]);
+        }
+      } else if (cell == ORACLE_CELL_GRU) {
+        for (long e = 0; e < D; ++e) {
+          const double rg = sigmoid(pre[0 * D + e]);
+          const double zg = sigmoid(pre[1 * D + e]);
+          const double ng = tanh(Wx[(((bi * T + t) * G + 2) * N + n) * D + e] + rg * pre[2 * D + e]);
+          hn[e] = (1.0 - zg) * ng + zg * h[e];
         }
       } else {
         for (long e = 0; e < D; ++e) hn[e] = tanh(pre[e]);

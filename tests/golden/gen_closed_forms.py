@@ -3,8 +3,9 @@
 Independent of the oracle: everything here is evaluated with Python's ``decimal`` module at 50
 significant digits, from the cell equations of "5.3 LSTM" (developnotes.readthedocs.io,
 operator.html: i, f, o through a sigmoid, the cell input through tanh, c = f*c + i*g,
-h = o*tanh(c)) and the Elman cell h = tanh(Wx + r*h + b) of the FlashRNN cell list. The pages
-print no numeric example of their own; every value below is derived, and each file says how.
+h = o*tanh(c)), the Elman cell h = tanh(Wx + r*h + b) of the FlashRNN cell list, and the textbook
+GRU (named in that list, equations not printed). The pages print no numeric example of their own;
+every value below is derived, and each file says how.
 
 Run:  python tests/golden/gen_closed_forms.py
 """
@@ -129,6 +130,27 @@ def main():
         "projected input, 8 columns). Outputs h, c listed t-major: h[t=1][0], h[t=1][1], h[t=2][0] ...",
     ], {"wh": flat_wh, "bias": bias, "xw": flat_xw, "h0": [Decimal("0.25"), Decimal("-0.5")],
         "c0": [Decimal("0.5"), Decimal("-1.0")], "h": hs, "c": cs})
+
+    # 5. GRU, D = 1, nonzero recurrent weights, hand-stepped: r = sig(wx_r + R_r h + b_r),
+    #    z = sig(wx_z + R_z h + b_z), n = tanh(wx_n + r (R_n h + b_n)), h' = (1 - z) n + z h.
+    gwx = [Decimal("0.5"), Decimal("-0.25"), Decimal("0.75")]
+    gR = [Decimal("0.5"), Decimal("-0.75"), Decimal("1.25")]
+    gb = [Decimal("0.125"), Decimal("0.25"), Decimal("-0.5")]
+    h = Decimal("-0.5")
+    hs = []
+    for _ in range(8):
+        r = sig(gwx[0] + gR[0] * h + gb[0])
+        z = sig(gwx[1] + gR[1] * h + gb[1])
+        n = tanh(gwx[2] + r * (gR[2] * h + gb[2]))
+        h = (1 - z) * n + z * h
+        hs.append(h)
+    write("gru_scalar.txt", [
+        "GRU, one unit, stepped by hand for t = 1..8 in 50-digit decimal arithmetic, in the textbook",
+        "form whose reset gate scales the recurrent part of the candidate after the product:",
+        "r = sig(wx_r + R_r h + b_r), z = sig(wx_z + R_z h + b_z), n = tanh(wx_n + r (R_n h + b_n)),",
+        "h' = (1 - z) n + z h. Gate order r, z, n; wx constant over t; h0 = -0.5. (The FlashRNN page",
+        "names the GRU among its cells without printing its equations.)",
+    ], {"wx": gwx, "r": gR, "b": gb, "h0": [Decimal("-0.5")], "h": hs})
 
 
 if __name__ == "__main__":

@@ -7,9 +7,10 @@ of its C source (tests/test_oracle_mutants.py), which must each fail at least on
 Kinds of pin:
 * golden fixtures (tests/golden/*.txt): closed forms and hand-stepped scalar recurrences evaluated
   with 50-digit decimals, independent of the oracle's code;
-* closed forms evaluated here with numpy (R = 0 geometric gating; saturated forget gate);
-* library special cases: torch.nn.LSTM / torch.nn.RNN in float64 (the "5.3 LSTM" page builds its
-  weights from exactly that module's state_dict names);
+* closed forms evaluated here with numpy (R = 0 geometric gating; saturated forget gate; GRU with
+  R = 0, a saturated update gate, a shut reset gate);
+* library special cases: torch.nn.LSTM / torch.nn.RNN / torch.nn.GRU in float64 (the "5.3 LSTM"
+  page builds its weights from exactly that module's state_dict names);
 * invariants: heads independent (= one wide head with block-diagonal R), batch permutation,
   continuation through last_states, T = 0, state bounds, row subsets;
 * two formulations: the page's time-major multi-layer loop against a layer-major composition of
@@ -67,6 +68,21 @@ def pin_golden_elman_scalar(orc):
     Wx = np.ones((1, T, 1, 1, 1))
     R = np.full((1, 1, 1, 1), 0.5)
     st, last = orc.headwise_fwd("elman", Wx, R, np.zeros((1, 1, 1)))
+    np.testing.assert_allclose(st[0, 0, :, 0, 0], g["h"], rtol=0, atol=ATOL_GOLD)
+    assert last.shape == (1, 1, 1, 1, 1)
+
+
+def pin_golden_gru_scalar(orc):
+    """GRU D = 1 with nonzero recurrent weights, hand-stepped at 50 digits (gate order r, z, n)."""
+    g = load("gru_scalar.txt")
+    T = len(g["h"])
+    Wx = np.zeros((1, T, 3, 1, 1))
+    for k in range(3):
+        Wx[0, :, k, 0, 0] = g["wx"][k]
+    R = np.array(g["r"]).reshape(3, 1, 1, 1)
+    b = np.array(g["b"]).reshape(3, 1, 1)
+    s0 = np.array(g["h0"]).reshape(1, 1, 1, 1, 1)
+    st, last = orc.headwise_fwd("gru", Wx, R, b, s0)
     np.testing.assert_allclose(st[0, 0, :, 0, 0], g["h"], rtol=0, atol=ATOL_GOLD)
     assert last.shape == (1, 1, 1, 1, 1)
 
@@ -160,6 +176,69 @@ def pin_elman_r0(orc):
     np.testing.assert_allclose(st[0], np.tanh(Wx[:, :, 0] + b[0][None, None]), rtol=0, atol=1e-15)
 
 
+def pin_gru_r0_closed_form(orc):
+    """GRU with R = 0 and Wx constant over t: r, z, n are constant per unit and the update is an
+    affine contraction, h_t = n + z^t (h0 - n) with n = tanh(Wx_n + r b_n)."""
+    rng = np.random.default_rng(14)
+    B, T, N, D = 2, 30, 2, 6
+    wx = rng.normal(size=(B, 1, 3, N, D))
+    Wx = np.repeat(wx, T, axis=1)
+    b = rng.normal(size=(3, N, D)) * 0.7
+    s0 = rng.normal(size=(1, B, 1, N, D))
+    st, last = orc.headwise_fwd("gru", Wx, np.zeros((3, N, D, D)), b, s0)
+    r = _sig(wx[:, 0, 0] + b[0][None])
+    z = _sig(wx[:, 0, 1] + b[1][None])
+    n = np.tanh(wx[:, 0, 2] + r * b[2][None])
+    h0 = s0[0, :, 0]
+    for t in range(1, T + 1):
+        np.testing.assert_allclose(st[0, :, t - 1], n + z ** t * (h0 - n), rtol=0, atol=1e-14)
+    np.testing.assert_array_equal(last[0, :, 0], st[0, :, -1])
+
+
+def pin_gru_update_saturated(orc):
+    """GRU with b_z = +40 (z = 1 - 4e-18): the state is carried through unchanged, whatever the
+    candidate."""
+    rng = np.random.default_rng(15)
+    B, T, N, D = 3, 20, 2, 5
+    Wx = rng.normal(size=(B, T, 3, N, D))
+    Wx[:, :, 1] = 0.0
+    R = rng.normal(size=(3, N, D, D)) * (0.5 / math.sqrt(D))
+    R[1] = 0.0
+    b = rng.normal(size=(3, N, D)) * 0.3
+    b[1] = 40.0
+    s0 = rng.normal(size=(1, B, 1, N, D)) * 0.5
+    st, _ = orc.headwise_fwd("gru", Wx, R, b, s0)
+    for t in range(T):
+        np.testing.assert_allclose(st[0, :, t], s0[0, :, 0], rtol=0, atol=(t + 1) * 1e-16 + 1e-15)
+
+
+def pin_gru_reset_closed(orc):
+    """GRU with the reset gate shut (b_r = -40, no input or recurrent drive to r): the candidate is
+    tanh(Wx_n), so the candidate's recurrent weights and bias no longer matter, while z still does."""
+    rng = np.random.default_rng(16)
+    B, T, N, D = 2, 12, 2, 5
+    Wx = rng.normal(size=(B, T, 3, N, D))
+    Wx[:, :, 0] = 0.0
+    R = rng.normal(size=(3, N, D, D)) / math.sqrt(D)
+    R[0] = 0.0
+    b = rng.normal(size=(3, N, D)) * 0.3
+    b[0] = -40.0
+    s0 = rng.normal(size=(1, B, 1, N, D)) * 0.5
+    st, _ = orc.headwise_fwd("gru", Wx, R, b, s0)
+    R2, b2 = R.copy(), b.copy()
+    R2[2] = rng.normal(size=(N, D, D))
+    b2[2] = rng.normal(size=(N, D))
+    st2, _ = orc.headwise_fwd("gru", Wx, R2, b2, s0)
+    np.testing.assert_allclose(st2, st, rtol=0, atol=1e-14)
+    # stepped here: h' = (1 - z) tanh(Wx_n) + z h, z = sigmoid(Wx_z + h.R_z + b_z)
+    h = s0[0, :, 0]
+    for t in range(T):
+        az = np.einsum("bnd,nde->bne", h, R[1])
+        z = _sig(Wx[:, t, 1] + az + b[1][None])
+        h = (1 - z) * np.tanh(Wx[:, t, 2]) + z * h
+        np.testing.assert_allclose(st[0, :, t], h, rtol=0, atol=1e-13)
+
+
 # ----------------------------------------------------------------------------- library cases
 def _torch_lstm(I, H, layers, seed):
     torch.manual_seed(seed)
@@ -246,10 +325,45 @@ def pin_torch_rnn_elman(orc):
         np.testing.assert_allclose(st[0, :, :, n].transpose(1, 0, 2), refs[n], rtol=0, atol=1e-12)
 
 
+def pin_torch_gru_headwise(orc):
+    """GRU heads equal torch.nn.GRU layers in float64 (gates r, z, n; the reset gate multiplies
+    W_hn h + b_hn), with Wx[b,t,g,n,:] = x W_ig^T + b_ig, R[g,n,d,e] = W_hg[e,d] and b = b_hg."""
+    T, B, I, H, N = 7, 3, 4, 5, 3
+    rng = np.random.default_rng(24)
+    Wx = np.zeros((B, T, 3, N, H))
+    R = np.zeros((3, N, H, H))
+    b = np.zeros((3, N, H))
+    s0 = rng.normal(size=(1, B, 1, N, H))
+    refs, lasts = [], []
+    for n in range(N):
+        torch.manual_seed(300 + n)
+        m = torch.nn.GRU(I, H, dtype=torch.float64)
+        with torch.no_grad():  # biases of the default init are small; widen them so each one counts
+            m.bias_ih_l0.mul_(4.0)
+            m.bias_hh_l0.mul_(4.0)
+        sd = m.state_dict()
+        x = rng.normal(size=(T, B, I))
+        with torch.no_grad():
+            ref, rh = m(torch.from_numpy(x), torch.from_numpy(s0[0, :, 0, n][None].copy()))
+        proj = x @ sd["weight_ih_l0"].numpy().T + sd["bias_ih_l0"].numpy()  # [T,B,3H]
+        whh = sd["weight_hh_l0"].numpy()
+        bhh = sd["bias_hh_l0"].numpy()
+        for g in range(3):
+            Wx[:, :, g, n, :] = proj[:, :, g * H:(g + 1) * H].transpose(1, 0, 2)
+            R[g, n] = whh[g * H:(g + 1) * H, :].T
+            b[g, n] = bhh[g * H:(g + 1) * H]
+        refs.append(ref.numpy())
+        lasts.append(rh.numpy()[0])
+    st, last = orc.headwise_fwd("gru", Wx, R, b, s0)
+    for n in range(N):
+        np.testing.assert_allclose(st[0, :, :, n].transpose(1, 0, 2), refs[n], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(last[0, :, 0, n], lasts[n], rtol=0, atol=1e-12)
+
+
 # ----------------------------------------------------------------------------- invariants
 def _rand_problem(cell, B, T, N, D, seed, with_s0=True):
     rng = np.random.default_rng(seed)
-    G, S = (4, 2) if cell == "lstm" else (1, 1)
+    G, S = {"lstm": (4, 2), "elman": (1, 1), "gru": (3, 1)}[cell]
     Wx = rng.normal(size=(B, T, G, N, D))
     R = rng.normal(size=(G, N, D, D)) / math.sqrt(D)
     b = rng.normal(size=(G, N, D)) * 0.3
@@ -259,7 +373,7 @@ def _rand_problem(cell, B, T, N, D, seed, with_s0=True):
 
 def pin_heads_blockdiag(orc):
     """N heads of width D == one head of width N*D whose R is block-diagonal."""
-    for cell in ("lstm", "elman"):
+    for cell in ("lstm", "elman", "gru"):
         B, T, N, D = 2, 6, 3, 4
         Wx, R, b, s0 = _rand_problem(cell, B, T, N, D, 31)
         G = Wx.shape[2]
@@ -298,7 +412,7 @@ def pin_batch_permutation(orc):
 
 def pin_continuation(orc):
     """Feeding last_states back as the initial state continues the sequence exactly."""
-    for cell in ("lstm", "elman"):
+    for cell in ("lstm", "elman", "gru"):
         B, T, N, D = 2, 16, 2, 4
         Wx, R, b, s0 = _rand_problem(cell, B, T, N, D, 34)
         st, last = orc.headwise_fwd(cell, Wx, R, b, s0)
@@ -333,6 +447,18 @@ def pin_bounds(orc):
     We, Re, be, se = _rand_problem("elman", B, T, N, D, 37)
     ste, _ = orc.headwise_fwd("elman", We * 5.0, Re * 3.0, be, se)
     assert np.all(np.abs(ste) <= 1.0)
+    # GRU: h' is a convex combination of h and n in (-1, 1), so |h_t| <= max(1, |h0|), and the
+    # step is a contraction towards (-1, 1): from |h0| > 1 the excess never grows
+    Wg, Rg, bg, sg = _rand_problem("gru", B, T, N, D, 40)
+    sg *= 3.0
+    stg, _ = orc.headwise_fwd("gru", Wg * 5.0, Rg * 3.0, bg, sg)
+    bound = np.maximum(1.0, np.abs(sg[0, :, 0]))
+    prev = np.abs(sg[0, :, 0])
+    for t in range(T):
+        cur = np.abs(stg[0, :, t])
+        assert np.all(cur <= bound + 1e-15)
+        assert np.all(np.maximum(cur - 1.0, 0.0) <= np.maximum(prev - 1.0, 0.0) + 1e-15)
+        prev = cur
 
 
 def pin_pairs_subset(orc):

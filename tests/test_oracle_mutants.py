@@ -32,6 +32,15 @@ MUTANTS = {
     "elman_identity": ("for (long e = 0; e < D; ++e) hn[e] = tanh(pre[e]);",
                        "for (long e = 0; e < D; ++e) hn[e] = pre[e] / (1.0 + fabs(pre[e]));"),
     "async_update": ("memcpy(h, hn, sizeof(double) * D);", "memcpy(h, hn, sizeof(double) * D); h[0] = c[0];"),
+    "gru_reset_dropped": ("tanh(Wx[(((bi * T + t) * G + 2) * N + n) * D + e] + rg * pre[2 * D + e])",
+                          "tanh(Wx[(((bi * T + t) * G + 2) * N + n) * D + e] + pre[2 * D + e])"),
+    "gru_reset_covers_wx": ("if (cell == ORACLE_CELL_GRU && g == 2) pre[g * D + e] = a[e] + b[(g * N + n) * D + e];",
+                            "if (0) pre[g * D + e] = 0.0;"),
+    "gru_bias_n_outside_reset": ("+ rg * pre[2 * D + e])",
+                                 "+ rg * pre[2 * D + e] + (1.0 - rg) * b[(2 * N + n) * D + e])"),
+    "gru_update_swapped": ("hn[e] = (1.0 - zg) * ng + zg * h[e];", "hn[e] = zg * ng + (1.0 - zg) * h[e];"),
+    "gru_r_z_swapped": ("const double rg = sigmoid(pre[0 * D + e]);", "const double rg = sigmoid(pre[1 * D + e]);"),
+    "gru_n_sigmoid": ("const double ng = tanh(Wx[", "const double ng = sigmoid(Wx["),
     "stack_bias_hh_dropped": ("bias[l * H4 + j] = b_ih[l][j] + b_hh[l][j];", "bias[l * H4 + j] = b_ih[l][j];"),
     "stack_layer_input": ("const double* in = (l == 0) ? x + (t * B + bi) * I : h + (l - 1) * H;",
                           "const double* in = (l == 0) ? x + (t * B + bi) * I : h + l * H;"),
