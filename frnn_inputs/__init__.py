@@ -23,7 +23,7 @@ import torch
 class HeadwiseWorkload:
     """A head-wise forward workload: Wx[B,T,G,N,D], R[G,N,D,D], b[G,N,D], states0[S,B,1,N,D]."""
     name: str
-    cell: str            # "lstm" (G=4, S=2) or "elman" (G=1, S=1)
+    cell: str            # "lstm" (G=4, S=2), "elman" (G=1, S=1) or "gru" (G=3, S=1)
     dtype: torch.dtype   # stored dtype of Wx, R, b, states0
     B: int
     T: int
@@ -37,7 +37,7 @@ class HeadwiseWorkload:
 
     @property
     def G(self) -> int:
-        return 4 if self.cell == "lstm" else 1
+        return {"lstm": 4, "elman": 1, "gru": 3}[self.cell]
 
     @property
     def S(self) -> int:
@@ -78,6 +78,20 @@ WORKLOADS = {
 }
 
 HEADLINE = "lstm_bf16_B16_T1024_N1_D768"
+
+# The GRU cell (named in the FlashRNN cell list) on the shapes of the LSTM workloads above: the
+# headline shape, the three-head shape with random initial state, and a small fp32 case.
+GRU_WORKLOADS = {
+    "gru_f32_B2_T16_N1_D32": HeadwiseWorkload(
+        "gru_f32_B2_T16_N1_D32", "gru", torch.float32, B=2, T=16, N=1, D=32, seed=10, b_var=0.1,
+        s0_var=0.25),
+    "gru_bf16_B8_T1024_N3_D256": HeadwiseWorkload(
+        "gru_bf16_B8_T1024_N3_D256", "gru", torch.bfloat16, B=8, T=1024, N=3, D=256, seed=11,
+        b_var=1.0, s0_var=1.0),
+    "gru_bf16_B16_T1024_N1_D768": HeadwiseWorkload(
+        "gru_bf16_B16_T1024_N1_D768", "gru", torch.bfloat16, B=16, T=1024, N=1, D=768, seed=12,
+        b_var=0.1),
+}
 
 
 def _normal(g: torch.Generator, shape, var: float) -> torch.Tensor:
@@ -121,8 +135,13 @@ def stack_inputs(w: StackWorkload):
     return {"x": x, "Wi": Wi, "Wh": Wh, "b_ih": bih, "b_hh": bhh, "h0": h0, "c0": c0}
 
 
+def get_workload(name: str):
+    """A named workload from WORKLOADS or GRU_WORKLOADS."""
+    return WORKLOADS[name] if name in WORKLOADS else GRU_WORKLOADS[name]
+
+
 def make_inputs(name_or_workload):
-    w = WORKLOADS[name_or_workload] if isinstance(name_or_workload, str) else name_or_workload
+    w = get_workload(name_or_workload) if isinstance(name_or_workload, str) else name_or_workload
     if isinstance(w, HeadwiseWorkload):
         return headwise_inputs(w)
     return stack_inputs(w)

@@ -1,5 +1,5 @@
-"""head_wise_lstm_amd -- Python binding of libfrnn, the gfx950 head-wise LSTM / Elman forward
-recurrence library (C ABI in include/frnn.h).
+"""head_wise_lstm_amd -- Python binding of libfrnn, the gfx950 head-wise LSTM / Elman / GRU
+forward recurrence library (C ABI in include/frnn.h).
 
 The binding only marshals arguments: it checks tensor shapes and dtypes, allocates the outputs and
 the workspace with torch (device memory is torch's), and passes raw device pointers and torch's
@@ -25,11 +25,12 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_NAME = "libfrnn.so"
 
 FRNN_OK = 0
-FRNN_CELL_LSTM, FRNN_CELL_ELMAN = 0, 1
+FRNN_CELL_LSTM, FRNN_CELL_ELMAN, FRNN_CELL_GRU = 0, 1, 2
 FRNN_F32, FRNN_BF16 = 0, 1
 FRNN_PATH_ALTERNATING, FRNN_PATH_FUSED = 0, 1
 
-_CELLS = {"lstm": FRNN_CELL_LSTM, "elman": FRNN_CELL_ELMAN}
+_CELLS = {"lstm": FRNN_CELL_LSTM, "elman": FRNN_CELL_ELMAN, "gru": FRNN_CELL_GRU}
+_GATES_STATES = {"lstm": (4, 2), "elman": (1, 1), "gru": (3, 1)}
 _PATHS = {"alternating": FRNN_PATH_ALTERNATING, "fused": FRNN_PATH_FUSED}
 _DTYPES = {torch.float32: FRNN_F32, torch.bfloat16: FRNN_BF16}
 
@@ -155,7 +156,9 @@ def frnn_fwd(Wx: torch.Tensor, R: torch.Tensor, b: Optional[torch.Tensor] = None
     last_states); ``workspace`` a preallocated uint8 tensor of at least frnn_workspace_bytes().
     With ``check`` the call waits for the stream and raises on a device-side error.
     """
-    G, S = (4, 2) if cell == "lstm" else (1, 1)
+    if cell not in _GATES_STATES:
+        raise ValueError(f"unknown cell {cell!r}")
+    G, S = _GATES_STATES[cell]
     if Wx.dim() != 5:
         raise ValueError("Wx must be [B,T,G,N,D]")
     B, T, G_, N, D = Wx.shape

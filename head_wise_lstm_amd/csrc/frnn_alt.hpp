@@ -2,8 +2,9 @@
 // and batch rows, then one coalesced pointwise kernel applies the gates. R is packed once per call
 // into MFMA-fragment order, so every per-step operand load is a contiguous 1 KiB per wave.
 //
-// Tiles follow the fused design: a 16-row tile of R^T holds the four gates of four units (LSTM)
-// or sixteen units (Elman); lane l of the MFMA result holds rows 4*(l/16)+i of batch column l%16.
+// Tiles follow the fused design: a 16-row tile of R^T holds the four gate rows of four units
+// (LSTM; GRU with a zero fourth row) or sixteen units (Elman); lane l of the MFMA result holds
+// rows 4*(l/16)+i of batch column l%16.
 #pragma once
 
 #include "frnn_device.hpp"
@@ -30,12 +31,13 @@ struct AltArgs {
   float* last_c;
   long long last_sb;
   void* rpack;    // packed R fragments: [N][TPH][KT][64][8 bf16] or [N][TPH][KT][64] fp32
-  float* rh;      // h.R per step: LSTM [B][N][D][4], Elman [B][N][D]
+  float* rh;      // h.R per step: LSTM, GRU [B][N][D][4]; Elman [B][N][D]
   void* hcur;     // current h, MFMA operand type: [N][B][D]
-  float* ccur;    // current c: [B][N][D]
+  float* ccur;    // current c (LSTM) or h in fp32 (GRU): [B][N][D]
 };
 
-// Initial state into the working buffers: hcur[n][b][d] (operand type), ccur[b][n][d].
+// Initial state into the working buffers: hcur[n][b][d] (operand type), ccur[b][n][d] (the
+// LSTM's c, the GRU's h).
 __global__ void __launch_bounds__(256) alt_init_kernel(AltArgs a) {
   const long long total = (long long)a.B * a.N * a.D;
   for (long long idx = (long long)blockIdx.x * 256 + threadIdx.x; idx < total; idx += (long long)gridDim.x * 256) {
@@ -45,7 +47,7 @@ __global__ void __launch_bounds__(256) alt_init_kernel(AltArgs a) {
     const int b = (int)(r / a.N);
     const long long s = (long long)b * a.s0_sb + (long long)n * a.D + d;
     const float h = a.s0_h ? ld_f(a.s0_h, s, a.s0_f32) : 0.0f;
-    const float c = a.s0_c ? ld_f(a.s0_c, s, a.s0_f32) : 0.0f;
+    const float c = a.cell == CELL_GRU ? h : a.s0_c ? ld_f(a.s0_c, s, a.s0_f32) : 0.0f;
     const long long hi = ((long long)n * a.B + b) * a.D + d;
     if (a.r_is_f32) reinterpret_cast<float*>(a.hcur)[hi] = h;
     else reinterpret_cast<uint16_t*>(a.hcur)[hi] = f2bf(h);
@@ -61,8 +63,8 @@ __global__ void __launch_bounds__(256) alt_gemm_kernel(AltArgs a) {
   __shared__ f32x4_t part[4][64];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int col = lane & 15, quad = lane >> 4;
-  const int G = a.cell == CELL_LSTM ? 4 : 1;
-  const int TPH = G * a.D / 16;
+  const int GS = cell_slots(a.cell);
+  const int TPH = GS * a.D / 16;
   const int tt = blockIdx.x;
   const int b0 = blockIdx.y * 16;
   const int n = blockIdx.z;
@@ -106,7 +108,7 @@ __global__ void __launch_bounds__(256) alt_gemm_kernel(AltArgs a) {
   if (wave != 0 || !colv) return;
   const f32x4_t s = (part[0][lane] + part[1][lane]) + (part[2][lane] + part[3][lane]);
   const long long b = b0 + col;
-  if (a.cell == CELL_LSTM) {
+  if (GS == 4) {
     const int u = 4 * tt + quad;
     *reinterpret_cast<f32x4_t*>(a.rh + ((b * a.N + n) * a.D + u) * 4) = s;
   } else {
@@ -142,6 +144,21 @@ __global__ void __launch_bounds__(256) alt_gate_kernel(AltArgs a, int t) {
     c = fg * a.ccur[idx] + ig * zg;
     a.ccur[idx] = c;
     h = og * tanh_f(c);
+  } else if (a.cell == CELL_GRU) {
+    // the reset gate scales the candidate's recurrent part (h.R_n + b_n), not its Wx
+    const f32x4_t rh = *reinterpret_cast<const f32x4_t*>(a.rh + idx * 4);
+    float wx[3], bb[3];
+#pragma unroll
+    for (int g = 0; g < 3; ++g) {
+      const long long off = (long long)(g * N + n) * D + u;
+      wx[g] = ld_f(a.Wx, wbase + off, a.wx_f32);
+      bb[g] = a.bias ? ld_f(a.bias, off, rf) : 0.0f;
+    }
+    const float rg = sigmoid_f(rh[0] + wx[0] + bb[0]);
+    const float zg = sigmoid_f(rh[1] + wx[1] + bb[1]);
+    const float ng = tanh_f(wx[2] + rg * (rh[2] + bb[2]));
+    h = ng + zg * (a.ccur[idx] - ng);  // (1 - z) n + z h
+    a.ccur[idx] = h;
   } else {
     const long long off = (long long)n * D + u;
     h = tanh_f(a.rh[idx] + ld_f(a.Wx, wbase + off, a.wx_f32) + (a.bias ? ld_f(a.bias, off, rf) : 0.0f));

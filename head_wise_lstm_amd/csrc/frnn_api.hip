@@ -14,9 +14,9 @@
 #include "frnn.h"
 #include "frnn_alt.hpp"
 #include "frnn_device.hpp"
-#include "frnn_fused.hpp"
 #include "frnn_proj.hpp"
 #include "frnn_rpack.hpp"
+#include "frnn_variants.hpp"
 
 using namespace frnn;
 
@@ -99,43 +99,16 @@ int get_devinfo(DevInfo* out) {
 DevInfo default_devinfo() { return DevInfo(); }
 
 // ----------------------------------------------------------------------------- kernel tables
-typedef void (*fused_fn)(FusedArgs);
-
-struct FusedVariant {
-  int cell, f32, local, ncw, ks, mtw, ktw;
-  fused_fn fn;
-};
-
-#define FV(CELL, F32, LOCAL, NCW, KS, MTW, KTW) \
-  {CELL, F32, LOCAL, NCW, KS, MTW, KTW, &fused_fwd_kernel<CELL, F32, LOCAL, NCW, KS, MTW, KTW>}
-#define FV2(F32, LOCAL, NCW, KS, MTW, KTW) FV(CELL_LSTM, F32, LOCAL, NCW, KS, MTW, KTW), FV(CELL_ELMAN, F32, LOCAL, NCW, KS, MTW, KTW)
-
-// Instantiated designs: (compute waves, K split, tiles per wave, k-tiles per wave). Each fits the
-// register file without spilling at its wave count (checked with -Rpass-analysis).
-const FusedVariant kFused[] = {
-    // die-local multi-workgroup design (bf16)
-    FV2(false, false, 4, 4, 1, 1), FV2(false, false, 4, 4, 2, 1), FV2(false, false, 4, 4, 1, 2),
-    FV2(false, false, 4, 4, 2, 2), FV2(false, false, 4, 4, 3, 3), FV2(false, false, 4, 4, 4, 4),
-    FV2(false, false, 4, 4, 2, 4), FV2(false, false, 4, 4, 4, 2), FV2(false, false, 4, 4, 4, 1),
-    FV2(false, false, 4, 2, 1, 1), FV2(false, false, 4, 2, 2, 1), FV2(false, false, 4, 2, 1, 2),
-    FV2(false, false, 4, 2, 2, 2), FV2(false, false, 4, 1, 1, 1), FV2(false, false, 4, 1, 1, 2),
-    FV2(false, false, 8, 8, 6, 3), FV2(false, false, 8, 8, 4, 2), FV2(false, false, 8, 8, 2, 1),
-    FV2(false, false, 6, 6, 6, 4), FV2(false, false, 4, 4, 6, 6), FV2(false, false, 8, 8, 8, 2),
-    FV2(false, false, 4, 4, 8, 4), FV2(false, false, 8, 8, 4, 1),
-    // single-workgroup design (bf16)
-    FV2(false, true, 4, 1, 1, 1), FV2(false, true, 4, 1, 2, 1), FV2(false, true, 4, 1, 1, 2),
-    FV2(false, true, 4, 1, 4, 2), FV2(false, true, 4, 1, 6, 3), FV2(false, true, 4, 1, 2, 4),
-    FV2(false, true, 4, 1, 1, 4),
-    // single-workgroup design (fp32)
-    FV2(true, true, 4, 1, 2, 8), FV2(true, true, 4, 1, 1, 8), FV2(true, true, 4, 1, 4, 16),
-    FV2(true, true, 4, 1, 1, 16),
-};
-
 const FusedVariant* find_fused(int cell, int f32, int local, int ncw, int ks, int mtw, int ktw) {
-  for (const auto& v : kFused)
+  const FusedTable t = cell == FRNN_CELL_LSTM ? fused_table_lstm()
+                       : cell == FRNN_CELL_GRU ? fused_table_gru()
+                                               : fused_table_elman();
+  for (int i = 0; i < t.n; ++i) {
+    const FusedVariant& v = t.v[i];
     if (v.cell == cell && v.f32 == f32 && v.local == local && v.ncw == ncw && v.ks == ks && v.mtw == mtw &&
         v.ktw == ktw)
       return &v;
+  }
   return nullptr;
 }
 
@@ -161,7 +134,10 @@ struct Problem {
   long long last_sb;
 };
 
-int gates_of(int cell) { return cell == FRNN_CELL_LSTM ? 4 : 1; }
+// Gates stored in Wx, R and b; rows per unit in a tile of packed R^T (see cell_slots).
+int gates_of(int cell) { return cell_gates(cell); }
+int slots_of(int cell) { return cell_slots(cell); }
+const char* cell_name(int cell) { return cell == FRNN_CELL_LSTM ? "lstm" : cell == FRNN_CELL_GRU ? "gru" : "elman"; }
 
 struct FusedPlan {
   const FusedVariant* v = nullptr;
@@ -181,7 +157,8 @@ int env_int(const char* name, int dflt) {
 // for them the largest W.
 int plan_fused(const Problem& p, const DevInfo& di, FusedPlan* out) {
   const int G = gates_of(p.cell);
-  const int TPH = G * p.D / 16;
+  const int GS = slots_of(p.cell);
+  const int TPH = GS * p.D / 16;
   const int KW = p.r_f32 ? 4 : 32;
   if (p.D % 32 != 0 || TPH < 1) return FRNN_EUNSUPPORTED;
   const int KT = p.D / KW;
@@ -236,7 +213,7 @@ int plan_fused(const Problem& p, const DevInfo& di, FusedPlan* out) {
       if (force_w > 1 && W != force_w) continue;
       if (TPH % W || per_die * W > slots_per_die) continue;
       const int mt_wg = TPH / W;
-      const int u_wg = mt_wg * (G == 4 ? 4 : 16);
+      const int u_wg = mt_wg * (GS == 4 ? 4 : 16);
       for (const auto& nk : cand) {
         const int ncw = nk[0], ks = nk[1];
         if ((force_ncw && ncw != force_ncw) || (force_ks && ks != force_ks)) continue;
@@ -275,14 +252,14 @@ int plan_fused(const Problem& p, const DevInfo& di, FusedPlan* out) {
 // Scratch needed by the recurrence of a problem on a path, beside the error word (independent
 // of T).
 size_t rec_scratch_bytes(int B, int N, int D, int cell, int r_f32, int path) {
-  const int G = gates_of(cell);
+  const int GS = slots_of(cell);
   const size_t elt = r_f32 ? 4 : 2;
-  size_t s = align256((size_t)G * N * D * D * elt);  // packed R
+  size_t s = align256((size_t)GS * N * D * D * elt);  // packed R
   if (path == FRNN_PATH_FUSED) {
     // exchange words: groups * BR <= N * (B + 15) rows, two parities
     return s + align256((size_t)2 * N * (B + 15) * D * 4);
   }
-  s += align256((size_t)B * N * D * G * 4);    // h.R
+  s += align256((size_t)B * N * D * GS * 4);   // h.R
   s += align256((size_t)N * B * D * elt);      // current h
   s += align256((size_t)B * N * D * 4);        // current c
   return s;
@@ -298,8 +275,7 @@ hipError_t launch_rpack(const Problem& p, void* out, hipStream_t st) {
   if (vec) {
     hipLaunchKernelGGL(rpack_bf16_kernel, dim3((p.D + RPACK_UB - 1) / RPACK_UB, p.D / 32, p.N), dim3(256), 0, st, ra);
   } else {
-    const int G = gates_of(p.cell);
-    const long long total = (long long)p.N * (G * p.D / 16) * (p.D / (p.r_f32 ? 4 : 32)) * 64;
+    const long long total = (long long)p.N * (slots_of(p.cell) * p.D / 16) * (p.D / (p.r_f32 ? 4 : 32)) * 64;
     hipLaunchKernelGGL(rpack_any_kernel, dim3((unsigned)std::min<long long>((total + 255) / 256, 4096)), dim3(256), 0,
                        st, ra, p.r_f32);
   }
@@ -324,15 +300,14 @@ std::string plan_string(const Problem& p, int path, const FusedPlan* fp) {
     std::snprintf(buf, sizeof(buf),
                   "fused design=%s cell=%s dtype=%s B=%d T=%d N=%d D=%d BR=%d groups=%d W=%d NCW=%d KS=%d MTW=%d KTW=%d "
                   "dies=%d slots/die=%d grid=%d lds=%zu",
-                  fp->local ? "workgroup-local" : "die-local", p.cell == FRNN_CELL_LSTM ? "lstm" : "elman",
+                  fp->local ? "workgroup-local" : "die-local", cell_name(p.cell),
                   p.r_f32 ? "f32" : "bf16", p.B, p.T, p.N, p.D, fp->BR, fp->groups, fp->W, fp->ncw, fp->ks, fp->mtw, fp->ktw,
                   fp->n_xcd, fp->slots, fp->grid, fp->lds);
   } else {
-    const int G = gates_of(p.cell);
-    const int TPH = G * p.D / 16;
+    const int TPH = slots_of(p.cell) * p.D / 16;
     std::snprintf(buf, sizeof(buf),
                   "alternating cell=%s dtype=%s B=%d T=%d N=%d D=%d gemm_grid=(%d,%d,%d) gate_grid=%lld launches=%d",
-                  p.cell == FRNN_CELL_LSTM ? "lstm" : "elman", p.r_f32 ? "f32" : "bf16", p.B, p.T, p.N, p.D,
+                  cell_name(p.cell), p.r_f32 ? "f32" : "bf16", p.B, p.T, p.N, p.D,
                   TPH, (p.B + 15) / 16, p.N, ((long long)p.B * p.N * p.D + 255) / 256, 2 * p.T + 2);
   }
   return std::string(buf);
@@ -350,7 +325,7 @@ int run_recurrence(const Problem& p, int path, int* err, void* scratch, hipStrea
     rc = plan_fused(p, di, &fp);
     if (rc != FRNN_OK) return rc;
     trace("[frnn] %s\n", plan_string(p, path, &fp));
-    const size_t rbytes = align256((size_t)gates_of(p.cell) * p.N * p.D * p.D * (p.r_f32 ? 4 : 2));
+    const size_t rbytes = align256((size_t)slots_of(p.cell) * p.N * p.D * p.D * (p.r_f32 ? 4 : 2));
     char* xw = base + rbytes;
     const size_t xbytes = fp.local ? 0 : (size_t)fp.groups * 2 * fp.BR * p.D * 4;
     if (!p.r_f32 && launch_rpack(p, base, st) != hipSuccess) return FRNN_EHIP;
@@ -393,7 +368,7 @@ int run_recurrence(const Problem& p, int path, int* err, void* scratch, hipStrea
   }
   // alternating
   trace("[frnn] %s\n", plan_string(p, path, nullptr));
-  const int G = gates_of(p.cell);
+  const int GS = slots_of(p.cell);
   const size_t elt = p.r_f32 ? 4 : 2;
   AltArgs a;
   std::memset(&a, 0, sizeof(a));
@@ -404,11 +379,11 @@ int run_recurrence(const Problem& p, int path, int* err, void* scratch, hipStrea
   a.out_h = p.out_h; a.out_c = p.out_c; a.out_sb = p.out_sb; a.out_st = p.out_st;
   a.last_h = p.last_h; a.last_c = p.last_c; a.last_sb = p.last_sb;
   char* q = base;
-  a.rpack = q; q += align256((size_t)G * p.N * p.D * p.D * elt);
-  a.rh = reinterpret_cast<float*>(q); q += align256((size_t)p.B * p.N * p.D * G * 4);
+  a.rpack = q; q += align256((size_t)GS * p.N * p.D * p.D * elt);
+  a.rh = reinterpret_cast<float*>(q); q += align256((size_t)p.B * p.N * p.D * GS * 4);
   a.hcur = q; q += align256((size_t)p.N * p.B * p.D * elt);
   a.ccur = reinterpret_cast<float*>(q);
-  const int TPH = G * p.D / 16;
+  const int TPH = GS * p.D / 16;
   if (launch_rpack(p, a.rpack, st) != hipSuccess) return FRNN_EHIP;
   const long long nstate = (long long)p.B * p.N * p.D;
   hipLaunchKernelGGL(alt_init_kernel, dim3((unsigned)std::min<long long>((nstate + 255) / 256, 4096)), dim3(256), 0, st, a);
@@ -428,7 +403,7 @@ int validate_desc(const frnn_desc* d, int path) {
   if (!d) return FRNN_EINVAL;
   if (d->reserved != 0) return FRNN_EINVAL;
   if (d->B < 1 || d->N < 1 || d->D < 1 || d->T < 0) return FRNN_EINVAL;
-  if (d->cell != FRNN_CELL_LSTM && d->cell != FRNN_CELL_ELMAN) return FRNN_EINVAL;
+  if (d->cell != FRNN_CELL_LSTM && d->cell != FRNN_CELL_ELMAN && d->cell != FRNN_CELL_GRU) return FRNN_EINVAL;
   if (d->in_dtype != FRNN_F32 && d->in_dtype != FRNN_BF16) return FRNN_EINVAL;
   if (d->out_dtype != FRNN_F32 && d->out_dtype != FRNN_BF16) return FRNN_EINVAL;
   if (path != FRNN_PATH_ALTERNATING && path != FRNN_PATH_FUSED) return FRNN_EINVAL;

@@ -12,7 +12,14 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint16_t u16x4_t __attribute__((ext_vector_type(4)));
 
-enum { CELL_LSTM = 0, CELL_ELMAN = 1 };
+enum { CELL_LSTM = 0, CELL_ELMAN = 1, CELL_GRU = 2 };
+
+// Gates of a cell as they are stored in Wx, R and b (LSTM i, f, z, o; GRU r, z, n; Elman one).
+__host__ __device__ constexpr int cell_gates(int cell) { return cell == CELL_LSTM ? 4 : cell == CELL_GRU ? 3 : 1; }
+// Rows a hidden unit takes in a 16-row MFMA tile of R^T: the LSTM and the GRU put one unit's gates
+// in four consecutive rows (the GRU's fourth row is zero), so that one lane of the result holds
+// all of them; an Elman tile holds sixteen units.
+__host__ __device__ constexpr int cell_slots(int cell) { return cell == CELL_ELMAN ? 1 : 4; }
 
 // Bits of the device error word kept at the start of every workspace.
 enum { DEVERR_TIMEOUT = 1, DEVERR_PLACEMENT = 2 };

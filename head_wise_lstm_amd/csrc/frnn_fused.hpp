@@ -1,9 +1,10 @@
 // Persistent fused forward recurrence for gfx950.
 //
 // Work split. A "group" is one head n and one block of BR <= 16 batch rows; groups never
-// interact. The G*D rows of R^T of a head are cut into 16-row tiles; an LSTM tile holds the four
-// gates (i, f, z, o) of four consecutive hidden units (row m = 4*unit + gate), an Elman tile
-// sixteen units. W workgroups share a group, each owning MT_WG consecutive tiles; their R^T
+// interact. The rows of R^T of a head are cut into 16-row tiles; an LSTM tile holds the four
+// gates (i, f, z, o) of four consecutive hidden units (row m = 4*unit + gate), a GRU tile the
+// gates r, z, n of four units in the same places (row 4*unit + 3 is zero), an Elman tile sixteen
+// units. W workgroups share a group, each owning MT_WG consecutive tiles; their R^T
 // fragments stay in VGPRs for all T steps (the page's "weights kept in registers").
 //
 // Waves. Four compute waves run MFMA v_mfma_f32_16x16x32_bf16 with
@@ -208,7 +209,7 @@ struct IoCtx {
 template <int CELL, int NCW, int KS, int MTW, int GT>
 __device__ __forceinline__ int io_ring_float(int b, int g, int u) {
   int tq, ln, comp;
-  if (CELL == CELL_LSTM) { tq = u >> 2; ln = b + 16 * (u & 3); comp = g; }
+  if (cell_slots(CELL) == 4) { tq = u >> 2; ln = b + 16 * (u & 3); comp = g; }
   else { tq = u >> 4; ln = b + 16 * ((u & 15) >> 2); comp = u & 3; }
   const int wv = (KS == 1) ? tq / MTW : (tq % NCW);
   const int q = (KS == 1) ? tq % MTW : (tq / NCW);
@@ -221,11 +222,12 @@ __device__ __forceinline__ int io_ring_float(int b, int g, int u) {
 // (h and, for the LSTM, c), written as pairs of floats.
 template <int CELL, int NCW, int KS, int MTW, int EPL>
 struct IoDesc {
-  static constexpr int G = (CELL == CELL_LSTM) ? 4 : 1;
+  static constexpr int G = cell_gates(CELL);
   static constexpr int GT = fused_gt(NCW, KS, MTW);
   static constexpr int E = EPL;
-  // consecutive units of one word land 16 lanes apart (LSTM) or in consecutive components (Elman)
-  static constexpr int USTEP = (CELL == CELL_LSTM) ? 64 : 1;
+  // consecutive units of one word land 16 lanes apart (LSTM, GRU) or in consecutive components
+  // (Elman)
+  static constexpr int USTEP = (cell_slots(CELL) == 4) ? 64 : 1;
   long long wofs[E];  // byte offset of the word for step 0
   int wlds[E];        // float index of its first element in slot 0 of the Wx ring (-1: none)
   long long oofs[E];  // element offset of the output pair for step 0
@@ -393,8 +395,10 @@ __global__ void __launch_bounds__((NCW + 1) * 64, 1) fused_fwd_kernel(FusedArgs 
   constexpr int MT_WG = MTW * MS;
   constexpr int KW = F32 ? 4 : 32;
   constexpr int GT = fused_gt(NCW, KS, MTW);
-  constexpr int G = (CELL == CELL_LSTM) ? 4 : 1;
-  constexpr int UPT = (CELL == CELL_LSTM) ? 4 : 16;  // hidden units per tile
+  constexpr int G = cell_gates(CELL);    // gates stored in Wx, R, b
+  constexpr int GS = cell_slots(CELL);   // rows of a unit in a tile
+  constexpr bool QUAD = GS == 4;         // a lane gates one unit (LSTM, GRU) or four (Elman)
+  constexpr int UPT = QUAD ? 4 : 16;     // hidden units per tile
   constexpr int G0 = LOCAL ? 0 : 1;                  // gating of step s happens in interval s + G0
   static_assert((NCW == 4 || NCW == 6 || NCW == 8) && NCW % KS == 0, "compute waves / K split");
   static_assert(!(F32 && !LOCAL), "fp32 runs only in the workgroup-local design");
@@ -407,7 +411,7 @@ __global__ void __launch_bounds__((NCW + 1) * 64, 1) fused_fwd_kernel(FusedArgs 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int col = lane & 15, quad = lane >> 4;
   const int D = a.D, N = a.N, T = a.T;
-  const int TPH = (G * D) / 16;
+  const int TPH = (GS * D) / 16;
 
   int group, w;
   if (LOCAL) {
@@ -498,13 +502,14 @@ __global__ void __launch_bounds__((NCW + 1) * 64, 1) fused_fwd_kernel(FusedArgs 
       const int tt = tile0 + ms * MTW + j;
       const bool tv = tt < TPH;
       int u, g;
-      if (CELL == CELL_LSTM) { u = 4 * tt + (col >> 2); g = col & 3; }
+      if (QUAD) { u = 4 * tt + (col >> 2); g = col & 3; }
       else { u = 16 * tt + col; g = 0; }
-      const long long rbase = (long long)g * a.r_sg + (long long)n * a.r_sn + u;
+      const bool rv = tv && g < G;  // rows of gates the cell does not have are zero
+      const long long rbase = (long long)(g < G ? g : 0) * a.r_sg + (long long)n * a.r_sn + u;
 #pragma unroll
       for (int kk = 0; kk < KTW; ++kk) {
         const int k = (ks * KTW + kk) * KW + quad;
-        Ra[j][kk] = tv ? reinterpret_cast<const float*>(a.R)[rbase + (long long)k * a.r_sd] : 0.0f;
+        Ra[j][kk] = rv ? reinterpret_cast<const float*>(a.R)[rbase + (long long)k * a.r_sd] : 0.0f;
       }
     }
   } else {
@@ -529,8 +534,9 @@ __global__ void __launch_bounds__((NCW + 1) * 64, 1) fused_fwd_kernel(FusedArgs 
     }
   }
 
-  // ---- tiles this wave applies the gates to, their bias and initial c.
-  int gu[GT];  // LSTM: the lane's unit; Elman: first of the lane's four units
+  // ---- tiles this wave applies the gates to, their bias and initial state (LSTM c; GRU h,
+  // kept in fp32 for the update while the MFMA operand is its bf16 copy).
+  int gu[GT];  // LSTM, GRU: the lane's unit; Elman: first of the lane's four units
   bool gval[GT];
   float bia[GT][4], creg[GT];
 #pragma unroll
@@ -538,20 +544,22 @@ __global__ void __launch_bounds__((NCW + 1) * 64, 1) fused_fwd_kernel(FusedArgs 
     const int tq = (KS == 1) ? ms * MTW + q : wave + NCW * q;
     const int tt = tile0 + tq;
     gval[q] = (tq < MT_WG) && (tt < TPH);
-    gu[q] = (CELL == CELL_LSTM) ? 4 * tt + quad : 16 * tt + 4 * quad;
+    gu[q] = QUAD ? 4 * tt + quad : 16 * tt + 4 * quad;
     creg[q] = 0.0f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) bia[q][i] = 0.0f;
     if (gval[q]) {
       if (a.bias) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const long long off = (CELL == CELL_LSTM) ? (long long)(i * N + n) * D + gu[q] : (long long)n * D + gu[q] + i;
+        for (int i = 0; i < (QUAD ? G : 4); ++i) {
+          const long long off = QUAD ? (long long)(i * N + n) * D + gu[q] : (long long)n * D + gu[q] + i;
           bia[q][i] = ld_f(a.bias, off, r_f32);
         }
       }
       if (CELL == CELL_LSTM && a.s0_c && colv)
         creg[q] = ld_f(a.s0_c, bcol * a.s0_sb + (long long)n * D + gu[q], a.s0_f32);
+      if (CELL == CELL_GRU && a.s0_h && colv)
+        creg[q] = ld_f(a.s0_h, bcol * a.s0_sb + (long long)n * D + gu[q], a.s0_f32);
     }
   }
   block_barrier();  // barrier -1
@@ -566,7 +574,7 @@ __global__ void __launch_bounds__((NCW + 1) * 64, 1) fused_fwd_kernel(FusedArgs 
     for (int q = 0; q < GT; ++q) {
       if (!gval[q]) continue;
 #pragma unroll
-      for (int i = 0; i < (CELL == CELL_LSTM ? 1 : 4); ++i) {
+      for (int i = 0; i < (QUAD ? 1 : 4); ++i) {
         const int u = gu[q] + i;
         const float h0 = a.s0_h ? ld_f(a.s0_h, bcol * a.s0_sb + (long long)n * D + u, a.s0_f32) : 0.0f;
         xb[xpar + col * D + u] = (uint32_t)f2bf(h0) << 16;
@@ -715,14 +723,23 @@ __global__ void __launch_bounds__((NCW + 1) * 64, 1) fused_fwd_kernel(FusedArgs 
       if (!gval[q]) continue;
       const int ri = (((t & 1) * NCW + wave) * GT + q) * 64 + lane;
       const f32x4_t wx4 = wxq[q];
-      if constexpr (CELL == CELL_LSTM) {
-        const float ig = sigmoid_f(pre[q][0] + wx4[0] + bia[q][0]);
-        const float fg = sigmoid_f(pre[q][1] + wx4[1] + bia[q][1]);
-        const float zg = tanh_f(pre[q][2] + wx4[2] + bia[q][2]);
-        const float og = sigmoid_f(pre[q][3] + wx4[3] + bia[q][3]);
-        const float c = fg * creg[q] + ig * zg;
-        creg[q] = c;
-        const float h = og * tanh_f(c);
+      if constexpr (QUAD) {
+        float h, c = 0.0f;
+        if constexpr (CELL == CELL_LSTM) {
+          const float ig = sigmoid_f(pre[q][0] + wx4[0] + bia[q][0]);
+          const float fg = sigmoid_f(pre[q][1] + wx4[1] + bia[q][1]);
+          const float zg = tanh_f(pre[q][2] + wx4[2] + bia[q][2]);
+          const float og = sigmoid_f(pre[q][3] + wx4[3] + bia[q][3]);
+          c = fg * creg[q] + ig * zg;
+          creg[q] = c;
+          h = og * tanh_f(c);
+        } else {  // GRU: the reset gate scales the candidate's recurrent part only
+          const float rg = sigmoid_f(pre[q][0] + wx4[0] + bia[q][0]);
+          const float zg = sigmoid_f(pre[q][1] + wx4[1] + bia[q][1]);
+          const float ng = tanh_f(wx4[2] + rg * (pre[q][2] + bia[q][2]));
+          h = ng + zg * (creg[q] - ng);  // (1 - z) n + z h
+          creg[q] = h;
+        }
         const int u = gu[q];
         if (LOCAL) {
           if constexpr (F32) hbuf_f[((t & 1) * 16 + col) * HS + u] = h;
@@ -768,9 +785,9 @@ __global__ void __launch_bounds__((NCW + 1) * 64, 1) fused_fwd_kernel(FusedArgs 
     for (int q = 0; q < GT; ++q) {
       if (!gval[q]) continue;
       const long long lo = bcol * a.last_sb + (long long)n * D + gu[q];
-      if constexpr (CELL == CELL_LSTM) {
+      if constexpr (QUAD) {
         if (a.last_h) a.last_h[lo] = hlast[q][0];
-        if (a.last_c) a.last_c[lo] = creg[q];
+        if (CELL == CELL_LSTM && a.last_c) a.last_c[lo] = creg[q];
       } else if (a.last_h) {
         *reinterpret_cast<f32x4_t*>(a.last_h + lo) = f32x4_t{hlast[q][0], hlast[q][1], hlast[q][2], hlast[q][3]};
       }

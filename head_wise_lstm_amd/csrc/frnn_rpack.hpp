@@ -2,13 +2,15 @@
 //
 // The recurrent contraction of a head is pre[g][e] = sum_d h[d] R[g][n][d][e] (h as a row vector
 // times R, the reading the pages' single-layer form matmul(h, Wh) fixes). On MFMA the rows of the
-// A operand are the outputs: a 16-row tile of R^T holds the four gates of four consecutive hidden
-// units (row m = 4*unit + gate; an Elman tile sixteen units), and one k-tile is 32 values of d
+// A operand are the outputs: a 16-row tile of R^T holds the four gate rows of four consecutive
+// hidden units (row m = 4*unit + gate; a GRU unit's fourth row is zero; an Elman tile holds
+// sixteen units), and one k-tile is 32 values of d
 // (bf16, v_mfma_f32_16x16x32_bf16) or 4 (fp32, v_mfma_f32_16x16x4f32). Lane l = 16*quad + m of a
 // fragment holds row m at k = 8*quad .. 8*quad+7 (bf16) or k = quad (fp32).
 //
-// Packed layout: [N][TPH][KT][64 lanes] x (8 bf16 | 1 fp32), TPH = G*D/16 tiles, KT = D/32 (bf16)
-// or D/4 (fp32) k-tiles; it has exactly as many elements as R.
+// Packed layout: [N][TPH][KT][64 lanes] x (8 bf16 | 1 fp32), TPH = slots*D/16 tiles (slots = 4
+// rows per unit, or 1 for Elman), KT = D/32 (bf16) or D/4 (fp32) k-tiles; it has slots*N*D*D
+// elements (as many as R, a third more for the GRU).
 #pragma once
 
 #include "frnn_device.hpp"
@@ -30,9 +32,9 @@ constexpr int RPACK_UB = 64;  // hidden units per block of the bf16 pack kernel
 __global__ void __launch_bounds__(256) rpack_bf16_kernel(RpackArgs a) {
   constexpr int SROW = RPACK_UB + 8;  // LDS row stride (elements)
   __shared__ uint16_t s[4 * 32 * SROW];
-  const int G = a.cell == CELL_LSTM ? 4 : 1;
-  const int UPT = a.cell == CELL_LSTM ? 4 : 16;
-  const int TPH = G * a.D / 16, KT = a.D / 32;
+  const int G = cell_gates(a.cell), GS = cell_slots(a.cell);
+  const int UPT = GS == 4 ? 4 : 16;
+  const int TPH = GS * a.D / 16, KT = a.D / 32;
   const int ub = blockIdx.x, kt = blockIdx.y, n = blockIdx.z;
   const int u0 = ub * RPACK_UB;
   const uint16_t* R = reinterpret_cast<const uint16_t*>(a.R);
@@ -54,14 +56,16 @@ __global__ void __launch_bounds__(256) rpack_bf16_kernel(RpackArgs a) {
     if (tt >= TPH) continue;
     const int m = lane & 15, quad = lane >> 4;
     int ul, g;
-    if (a.cell == CELL_LSTM) { ul = 4 * tl + (m >> 2); g = m & 3; }
+    if (GS == 4) { ul = 4 * tl + (m >> 2); g = m & 3; }
     else { ul = 16 * tl + m; g = 0; }
-    u32x4_t pk;
+    u32x4_t pk = {0u, 0u, 0u, 0u};  // rows of gates the cell does not have stay zero
+    if (g < G) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t lo = s[(g * 32 + 8 * quad + 2 * j) * SROW + ul];
-      const uint32_t hi = s[(g * 32 + 8 * quad + 2 * j + 1) * SROW + ul];
-      pk[j] = lo | (hi << 16);
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t lo = s[(g * 32 + 8 * quad + 2 * j) * SROW + ul];
+        const uint32_t hi = s[(g * 32 + 8 * quad + 2 * j + 1) * SROW + ul];
+        pk[j] = lo | (hi << 16);
+      }
     }
     reinterpret_cast<u32x4_t*>(a.out)[(((long long)n * TPH + tt) * KT + kt) * 64 + lane] = pk;
   }
@@ -69,8 +73,8 @@ __global__ void __launch_bounds__(256) rpack_bf16_kernel(RpackArgs a) {
 
 // Any strides and fp32: one thread per (head, tile, k-tile, lane) gathers its values directly.
 __global__ void __launch_bounds__(256) rpack_any_kernel(RpackArgs a, int f32) {
-  const int G = a.cell == CELL_LSTM ? 4 : 1;
-  const int TPH = G * a.D / 16;
+  const int G = cell_gates(a.cell), GS = cell_slots(a.cell);
+  const int TPH = GS * a.D / 16;
   const int KT = a.D / (f32 ? 4 : 32);
   const long long total = (long long)a.N * TPH * KT * 64;
   for (long long idx = (long long)blockIdx.x * 256 + threadIdx.x; idx < total; idx += (long long)gridDim.x * 256) {
@@ -82,19 +86,23 @@ __global__ void __launch_bounds__(256) rpack_any_kernel(RpackArgs a, int f32) {
     const int n = (int)(r / TPH);
     const int m = lane & 15, quad = lane >> 4;
     int u, g;
-    if (a.cell == CELL_LSTM) { u = 4 * tt + (m >> 2); g = m & 3; }
+    if (GS == 4) { u = 4 * tt + (m >> 2); g = m & 3; }
     else { u = 16 * tt + m; g = 0; }
-    const long long base = (long long)g * a.r_sg + (long long)n * a.r_sn + u;
+    const bool gv = g < G;  // rows of gates the cell does not have are zero
+    const long long base = (long long)(gv ? g : 0) * a.r_sg + (long long)n * a.r_sn + u;
     if (f32) {
-      reinterpret_cast<float*>(a.out)[idx] = reinterpret_cast<const float*>(a.R)[base + (long long)(kt * 4 + quad) * a.r_sd];
+      reinterpret_cast<float*>(a.out)[idx] =
+          gv ? reinterpret_cast<const float*>(a.R)[base + (long long)(kt * 4 + quad) * a.r_sd] : 0.0f;
     } else {
       const uint16_t* Rp = reinterpret_cast<const uint16_t*>(a.R);
       const int k = kt * 32 + 8 * quad;
-      u32x4_t pk;
+      u32x4_t pk = {0u, 0u, 0u, 0u};
+      if (gv) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        pk[i] = (uint32_t)Rp[base + (long long)(k + 2 * i) * a.r_sd] |
-                ((uint32_t)Rp[base + (long long)(k + 2 * i + 1) * a.r_sd] << 16);
+        for (int i = 0; i < 4; ++i)
+          pk[i] = (uint32_t)Rp[base + (long long)(k + 2 * i) * a.r_sd] |
+                  ((uint32_t)Rp[base + (long long)(k + 2 * i + 1) * a.r_sd] << 16);
+      }
       reinterpret_cast<u32x4_t*>(a.out)[idx] = pk;
     }
   }

@@ -1,0 +1,47 @@
+// The fused kernel's instantiated designs. Each cell's instantiations live in a translation unit
+// of their own (frnn_fused_<cell>.hip), so that the three compile in parallel; the host planner
+// looks designs up in the tables those units export.
+#pragma once
+
+#include "frnn_fused.hpp"
+
+namespace frnn {
+
+typedef void (*fused_fn)(FusedArgs);
+
+struct FusedVariant {
+  int cell, f32, local, ncw, ks, mtw, ktw;
+  fused_fn fn;
+};
+
+struct FusedTable {
+  const FusedVariant* v;
+  int n;
+};
+
+// X(F32, LOCAL, NCW, KS, MTW, KTW): (compute waves, K split, tiles per wave, k-tiles per wave).
+// Each fits the register file without spilling at its wave count (checked with
+// -Rpass-analysis=kernel-resource-usage).
+#define FRNN_FUSED_DESIGNS(X)                                                                      \
+  /* die-local multi-workgroup design (bf16) */                                                    \
+  X(false, false, 4, 4, 1, 1) X(false, false, 4, 4, 2, 1) X(false, false, 4, 4, 1, 2)              \
+  X(false, false, 4, 4, 2, 2) X(false, false, 4, 4, 3, 3) X(false, false, 4, 4, 4, 4)              \
+  X(false, false, 4, 4, 2, 4) X(false, false, 4, 4, 4, 2) X(false, false, 4, 4, 4, 1)              \
+  X(false, false, 4, 2, 1, 1) X(false, false, 4, 2, 2, 1) X(false, false, 4, 2, 1, 2)              \
+  X(false, false, 4, 2, 2, 2) X(false, false, 4, 1, 1, 1) X(false, false, 4, 1, 1, 2)              \
+  X(false, false, 8, 8, 6, 3) X(false, false, 8, 8, 4, 2) X(false, false, 8, 8, 2, 1)              \
+  X(false, false, 6, 6, 6, 4) X(false, false, 4, 4, 6, 6) X(false, false, 8, 8, 8, 2)              \
+  X(false, false, 4, 4, 8, 4) X(false, false, 8, 8, 4, 1)                                          \
+  /* single-workgroup design (bf16) */                                                             \
+  X(false, true, 4, 1, 1, 1) X(false, true, 4, 1, 2, 1) X(false, true, 4, 1, 1, 2)                 \
+  X(false, true, 4, 1, 4, 2) X(false, true, 4, 1, 6, 3) X(false, true, 4, 1, 2, 4)                 \
+  X(false, true, 4, 1, 1, 4)                                                                       \
+  /* single-workgroup design (fp32) */                                                             \
+  X(true, true, 4, 1, 2, 8) X(true, true, 4, 1, 1, 8) X(true, true, 4, 1, 4, 16)                   \
+  X(true, true, 4, 1, 1, 16)
+
+FusedTable fused_table_lstm();
+FusedTable fused_table_elman();
+FusedTable fused_table_gru();
+
+}  // namespace frnn

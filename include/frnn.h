@@ -1,5 +1,5 @@
 /*
- * frnn.h -- C ABI of the MI355X (gfx950) head-wise LSTM / Elman forward-recurrence library.
+ * frnn.h -- C ABI of the MI355X (gfx950) head-wise LSTM / Elman / GRU forward-recurrence library.
  *
  * What is computed (FlashRNN usage example, hottg.com/neural/9889; cell equations of
  * "5.3 LSTM", developnotes.readthedocs.io operator.html, applied per head):
@@ -10,6 +10,13 @@
  *        i = sigmoid(pre[0]), f = sigmoid(pre[1]), z = tanh(pre[2]), o = sigmoid(pre[3])
  *        c = f * c + i * z;   h = o * tanh(c)
  *     Elman (G = 1, S = 1):   h = tanh(pre[0])
+ *     GRU   (G = 3 gates r, z, n; S = 1): the FlashRNN page names the cell without equations;
+ *        this is the textbook form in which the reset gate scales the candidate's recurrent part
+ *        after the product, so the n gate keeps Wx apart:
+ *        a[g][e] = sum_d h[d] * R[g,n,d,e]
+ *        r = sigmoid(Wx[0] + a[0] + bias[0]), z = sigmoid(Wx[1] + a[1] + bias[1])
+ *        n = tanh(Wx[2] + r * (a[2] + bias[2])),   h = (1 - z) * n + z * h
+ *        (Wx carries the input-side terms and their biases, bias the recurrent-side ones)
  *     states[0,b,t,n,:] = h;  (LSTM) states[1,b,t,n,:] = c
  *   last_states[:,b,0,n,:] = the state after the last step (T == 0: the initial state).
  *
@@ -55,8 +62,8 @@ enum {
   FRNN_ENODEVICE = -8        /* no usable gfx950 device */
 };
 
-/* Cells (FlashRNN cell names "lstm" and "elman"). */
-enum { FRNN_CELL_LSTM = 0, FRNN_CELL_ELMAN = 1 };
+/* Cells (FlashRNN cell names "lstm", "elman" and "gru"). */
+enum { FRNN_CELL_LSTM = 0, FRNN_CELL_ELMAN = 1, FRNN_CELL_GRU = 2 };
 
 /* Element types. */
 enum { FRNN_F32 = 0, FRNN_BF16 = 1 };
@@ -69,7 +76,8 @@ enum { FRNN_F32 = 0, FRNN_BF16 = 1 };
  *               workgroups sharing a head exchange h through the die-local L2 every step. */
 enum { FRNN_PATH_ALTERNATING = 0, FRNN_PATH_FUSED = 1 };
 
-/* Problem description for frnn_fwd. G and S follow from `cell` (LSTM: 4, 2; Elman: 1, 1). */
+/* Problem description for frnn_fwd. G and S follow from `cell` (LSTM: 4, 2; Elman: 1, 1;
+ * GRU: 3, 1). */
 typedef struct frnn_desc {
   int32_t B;          /* batch size, >= 1 */
   int32_t T;          /* sequence length, >= 0 */

@@ -67,7 +67,8 @@ EINVAL, EUNSUP, EWS = -1, -2, -3
 
 
 @pytest.mark.parametrize("desc,code", [
-    (D(B=0), EINVAL), (D(N=0), EINVAL), (D(Dm=0), EINVAL), (D(T=-1), EINVAL), (D(cell=2), EINVAL),
+    (D(B=0), EINVAL), (D(N=0), EINVAL), (D(Dm=0), EINVAL), (D(T=-1), EINVAL), (D(cell=3), EINVAL),
+    (D(cell=-1), EINVAL),
     (D(ind=7), EINVAL), (D(outd=9), EINVAL), (D(res=1), EINVAL), (D(outd=1), EUNSUP), (D(Dm=48), EUNSUP),
     (D(Dm=2048), EUNSUP),
 ])
@@ -162,3 +163,32 @@ def test_planner_grid_fits_one_workgroup_per_cu(lib):
             grid = int(re.search(r"grid=(\d+)", s).group(1))
             slots = int(re.search(r"slots/die=(\d+)", s).group(1))
             assert grid <= 256 and slots <= 32
+
+
+def test_gru_cell_accepted_and_sized(lib):
+    """The GRU (cell 2) packs R^T with four rows per unit like the LSTM (its fourth is zero), so its
+    workspace equals the LSTM's on both paths."""
+    assert header_enum("FRNN_CELL_GRU") == 2
+    for path in (0, 1):
+        rc_g, n_g = ws_bytes(D(B=16, T=8, N=2, Dm=256, cell=2), path)
+        rc_l, n_l = ws_bytes(D(B=16, T=8, N=2, Dm=256, cell=0), path)
+        assert rc_g == rc_l == 0 and n_g == n_l
+    s = plan(D(B=4, T=8, N=1, Dm=64, cell=2), 0)
+    assert s.startswith("alternating cell=gru")
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="planner model of a 256-CU, 8-die device (no GPU here)")
+def test_planner_gru_matches_lstm_tiles(lib):
+    """A GRU head has as many 16-row tiles as an LSTM head of the same width, so it gets the same
+    design on the same shape."""
+    for (B, N, Dm) in [(16, 1, 768), (8, 3, 256), (2, 1, 32), (64, 12, 64)]:
+        for ind in (0, 1):
+            try:
+                sl = plan(D(B=B, T=8, N=N, Dm=Dm, ind=ind), 1)
+            except hw.FrnnError:
+                with pytest.raises(hw.FrnnError):
+                    plan(D(B=B, T=8, N=N, Dm=Dm, cell=2, ind=ind), 1)
+                continue
+            sg = plan(D(B=B, T=8, N=N, Dm=Dm, cell=2, ind=ind), 1)
+            assert "cell=gru" in sg
+            assert sg.replace("cell=gru", "cell=lstm") == sl

@@ -95,6 +95,13 @@ SMALL = [
     fi.HeadwiseWorkload("lstm_f32_D64", "lstm", torch.float32, B=17, T=6, N=1, D=64, seed=110),
     fi.HeadwiseWorkload("elman_f32_D64", "elman", torch.float32, B=4, T=9, N=3, D=64, seed=111, s0_var=1.0),
     fi.HeadwiseWorkload("lstm_bf16_T1", "lstm", torch.bfloat16, B=1, T=1, N=1, D=64, seed=112, s0_var=1.0),
+    fi.HeadwiseWorkload("gru_bf16_ragged_D64", "gru", torch.bfloat16, B=5, T=13, N=2, D=64, seed=113, s0_var=1.0),
+    fi.HeadwiseWorkload("gru_bf16_ragged_D96", "gru", torch.bfloat16, B=19, T=7, N=2, D=96, seed=114, s0_var=0.5),
+    fi.HeadwiseWorkload("gru_bf16_D256", "gru", torch.bfloat16, B=9, T=12, N=2, D=256, seed=115, s0_var=1.0, b_var=1.0),
+    fi.HeadwiseWorkload("gru_bf16_D768", "gru", torch.bfloat16, B=16, T=5, N=1, D=768, seed=116),
+    fi.HeadwiseWorkload("gru_f32_D32", "gru", torch.float32, B=3, T=11, N=2, D=32, seed=117, s0_var=1.0),
+    fi.HeadwiseWorkload("gru_f32_D64", "gru", torch.float32, B=17, T=6, N=1, D=64, seed=118),
+    fi.HeadwiseWorkload("gru_bf16_T1", "gru", torch.bfloat16, B=1, T=1, N=1, D=64, seed=119, s0_var=1.0),
 ]
 
 
@@ -127,6 +134,14 @@ FORCED = [
      {"FRNN_FUSED_W": 16, "FRNN_FUSED_NCW": 8, "FRNN_FUSED_BR": 2}),
     (fi.HeadwiseWorkload("lstm_D256_W16_8waves", "lstm", torch.bfloat16, B=5, T=7, N=2, D=256, seed=129, s0_var=1.0),
      {"FRNN_FUSED_W": 16, "FRNN_FUSED_NCW": 8, "FRNN_FUSED_BR": 2}),
+    (fi.HeadwiseWorkload("gru_forced_W4", "gru", torch.bfloat16, B=7, T=9, N=3, D=64, seed=130, s0_var=1.0),
+     {"FRNN_FUSED_W": 4, "FRNN_FUSED_BR": 3}),
+    (fi.HeadwiseWorkload("gru_D768_8waves", "gru", torch.bfloat16, B=16, T=9, N=1, D=768, seed=132, s0_var=1.0),
+     {"FRNN_FUSED_NCW": 8}),
+    (fi.HeadwiseWorkload("gru_D768_6waves", "gru", torch.bfloat16, B=6, T=7, N=1, D=768, seed=133, s0_var=1.0),
+     {"FRNN_FUSED_NCW": 6, "FRNN_FUSED_BR": 2}),
+    (fi.HeadwiseWorkload("gru_D512_W16_4waves", "gru", torch.bfloat16, B=3, T=6, N=1, D=512, seed=134, s0_var=1.0),
+     {"FRNN_FUSED_W": 16, "FRNN_FUSED_NCW": 4, "FRNN_FUSED_BR": 2}),
 ]
 
 # the design each forced case must get (compute waves, K split, tiles and k-tiles per wave)
@@ -136,6 +151,9 @@ FORCED_PLAN = {
     "lstm_D512_W16_4waves": "NCW=4 KS=4 MTW=8 KTW=4",
     "lstm_D512_W16_8waves": "NCW=8 KS=8 MTW=8 KTW=2",
     "lstm_D256_W16_8waves": "NCW=8 KS=8 MTW=4 KTW=1",
+    "gru_D768_8waves": "NCW=8 KS=8 MTW=6 KTW=3",
+    "gru_D768_6waves": "NCW=6 KS=6 MTW=6 KTW=4",
+    "gru_D512_W16_4waves": "NCW=4 KS=4 MTW=8 KTW=4",
 }
 
 
@@ -158,40 +176,43 @@ def test_forced_die_local(w, env):
     run_case(w, "fused", env=env)
 
 
-def test_t0_returns_initial_state():
+@pytest.mark.parametrize("cell,G,S", [("lstm", 4, 2), ("gru", 3, 1)])
+def test_t0_returns_initial_state(cell, G, S):
     hw = _hw()
     dev = torch.device("cuda:0")
     for path in ("alternating", "fused"):
-        Wx = torch.zeros((3, 0, 4, 2, 64), dtype=torch.bfloat16, device=dev)
-        R = torch.randn((4, 2, 64, 64), device=dev).to(torch.bfloat16)
-        s0 = torch.randn((2, 3, 1, 2, 64), device=dev).to(torch.bfloat16)
-        st, last = hw.frnn_fwd(Wx, R, None, s0, cell="lstm", path=path)
-        assert st.shape == (2, 3, 0, 2, 64)
+        Wx = torch.zeros((3, 0, G, 2, 64), dtype=torch.bfloat16, device=dev)
+        R = torch.randn((G, 2, 64, 64), device=dev).to(torch.bfloat16)
+        s0 = torch.randn((S, 3, 1, 2, 64), device=dev).to(torch.bfloat16)
+        st, last = hw.frnn_fwd(Wx, R, None, s0, cell=cell, path=path)
+        assert st.shape == (S, 3, 0, 2, 64)
         torch.testing.assert_close(last, s0.float(), rtol=0, atol=0)
-        st, last = hw.frnn_fwd(Wx, R, None, None, cell="lstm", path=path)
+        st, last = hw.frnn_fwd(Wx, R, None, None, cell=cell, path=path)
         assert torch.count_nonzero(last).item() == 0
 
 
-def test_continuation_matches_single_call():
+@pytest.mark.parametrize("cell", ["lstm", "gru"])
+def test_continuation_matches_single_call(cell):
     hw = _hw()
-    w = fi.HeadwiseWorkload("cont", "lstm", torch.bfloat16, B=6, T=20, N=2, D=128, seed=131, s0_var=1.0)
+    w = fi.HeadwiseWorkload("cont", cell, torch.bfloat16, B=6, T=20, N=2, D=128, seed=131, s0_var=1.0)
     x = {k: (v.cuda() if v is not None else None) for k, v in fi.make_inputs(w).items()}
     for path in ("alternating", "fused"):
-        st, last = hw.frnn_fwd(x["Wx"], x["R"], x["b"], x["states0"], cell="lstm", path=path)
-        st1, last1 = hw.frnn_fwd(x["Wx"][:, :8].contiguous(), x["R"], x["b"], x["states0"], cell="lstm", path=path)
+        st, last = hw.frnn_fwd(x["Wx"], x["R"], x["b"], x["states0"], cell=cell, path=path)
+        st1, last1 = hw.frnn_fwd(x["Wx"][:, :8].contiguous(), x["R"], x["b"], x["states0"], cell=cell, path=path)
         # the continuation starts from fp32 states rounded to the input dtype, so compare to tolerance
-        st2, last2 = hw.frnn_fwd(x["Wx"][:, 8:].contiguous(), x["R"], x["b"], last1.to(torch.bfloat16), cell="lstm",
+        st2, last2 = hw.frnn_fwd(x["Wx"][:, 8:].contiguous(), x["R"], x["b"], last1.to(torch.bfloat16), cell=cell,
                                  path=path)
         torch.testing.assert_close(st1, st[:, :, :8], rtol=0, atol=0)
         assert (st2 - st[:, :, 8:]).abs().max().item() < 3e-2
 
 
-def test_fused_and_alternating_agree():
+@pytest.mark.parametrize("cell", ["lstm", "gru"])
+def test_fused_and_alternating_agree(cell):
     hw = _hw()
-    w = fi.HeadwiseWorkload("agree", "lstm", torch.bfloat16, B=8, T=30, N=2, D=256, seed=141, s0_var=1.0)
+    w = fi.HeadwiseWorkload("agree", cell, torch.bfloat16, B=8, T=30, N=2, D=256, seed=141, s0_var=1.0)
     x = {k: (v.cuda() if v is not None else None) for k, v in fi.make_inputs(w).items()}
-    a, _ = hw.frnn_fwd(x["Wx"], x["R"], x["b"], x["states0"], cell="lstm", path="alternating")
-    f, _ = hw.frnn_fwd(x["Wx"], x["R"], x["b"], x["states0"], cell="lstm", path="fused")
+    a, _ = hw.frnn_fwd(x["Wx"], x["R"], x["b"], x["states0"], cell=cell, path="alternating")
+    f, _ = hw.frnn_fwd(x["Wx"], x["R"], x["b"], x["states0"], cell=cell, path="fused")
     assert (a - f).abs().max().item() < 2e-2
 
 
@@ -213,13 +234,16 @@ FULL_PAIRS = {
     "lstm_bf16_B8_T1024_N3_D256": [0, 4, 10, 23],
     "lstm_bf16_B16_T1024_N1_D768": [0, 5, 15],
     "elman_bf16_B64_T2048_N12_D64": [0, 13, 250, 511, 767],
+    "gru_f32_B2_T16_N1_D32": None,
+    "gru_bf16_B8_T1024_N3_D256": [0, 4, 10, 23],
+    "gru_bf16_B16_T1024_N1_D768": [0, 5, 15],
 }
 
 
 @pytest.mark.parametrize("path", ["fused", "alternating"])
 @pytest.mark.parametrize("name", list(FULL_PAIRS))
 def test_full_workload(name, path):
-    run_case(fi.WORKLOADS[name], path, pairs=FULL_PAIRS[name])
+    run_case(fi.get_workload(name), path, pairs=FULL_PAIRS[name])
 
 
 def _stack_case(w, path, rows):

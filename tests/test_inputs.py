@@ -45,3 +45,11 @@ def test_stack_inputs_uniform_bound():
 def test_to_f64_exact():
     t = torch.tensor([1.0, -2.5, 3.140625], dtype=torch.bfloat16)
     np.testing.assert_array_equal(fi.to_f64(t), np.array([1.0, -2.5, 3.140625]))
+
+
+def test_gru_workloads_shapes():
+    for name, w in fi.GRU_WORKLOADS.items():
+        assert fi.get_workload(name) is w and w.cell == "gru" and (w.G, w.S) == (3, 1)
+    x = fi.make_inputs("gru_f32_B2_T16_N1_D32")
+    assert tuple(x["Wx"].shape) == (2, 16, 3, 1, 32) and tuple(x["R"].shape) == (3, 1, 32, 32)
+    assert tuple(x["b"].shape) == (3, 1, 32) and tuple(x["states0"].shape) == (1, 2, 1, 1, 32)
