@@ -13,13 +13,19 @@ The arithmetic lives in ``frnn_oracle.c`` (plain C, double precision, OpenMP ove
   G; Elman: h = tanh(Wx + h.R + b); GRU (named in the FlashRNN cell list, equations not printed):
   the textbook cell with gates r, z, n along G, the reset gate scaling the candidate's recurrent
   part h.R_n + b_n, h' = (1 - z) n + z h, S = 1.
+* ``headwise_bwd`` -- back-propagation through time of ``headwise_fwd``: the gradients of
+  sum(dstates * states) + sum(dlast * last_states) with respect to Wx, R, b and states0. The pages
+  print no gradient formulas; the C source writes out the chain rule of the cell equations.
 * ``lstm_stack_p3`` -- "5.3 LSTM", MyLSTM.set_weights and MyLSTM.forward: time loop outermost,
   layers inside it, bias = bias_ih + bias_hh, Wi stored [in, 4H], Wh stored [H, 4H].
 
 Pins (tests/test_oracle_pins.py): closed forms (R = 0 geometric gating, saturated forget gate,
 Elman and GRU scalar iterations) computed independently at 50 significant digits, GRU closed forms
 (R = 0, saturated update gate, shut reset gate), torch.nn.LSTM / nn.RNN / nn.GRU in float64 as
-library special cases, head / batch / continuation invariants, and hand-stepped tiny cases.
+library special cases, head / batch / continuation invariants, and hand-stepped tiny cases. The
+backward: torch autograd through float64 torch.nn.LSTM / GRU / RNN layers with identity input
+weights (so that their input is Wx), central finite differences of the pinned forward on every
+entry, linearity in the cotangent, and T = 0.
 """
 from __future__ import annotations
 
@@ -74,6 +80,11 @@ class Oracle:
             ctypes.c_int, ctypes.c_long, ctypes.c_long, ctypes.c_long, ctypes.c_long,
             dp, dp, dp, dp, dp, dp, ctypes.POINTER(ctypes.c_long), ctypes.c_long,
         ]
+        lib.oracle_headwise_bwd.restype = ctypes.c_int
+        lib.oracle_headwise_bwd.argtypes = [
+            ctypes.c_int, ctypes.c_long, ctypes.c_long, ctypes.c_long, ctypes.c_long,
+            dp, dp, dp, dp, dp, dp, dp, dp, dp, dp,
+        ]
         lib.oracle_lstm_stack_p3.restype = ctypes.c_int
         lib.oracle_lstm_stack_p3.argtypes = [
             ctypes.c_long, ctypes.c_long, ctypes.c_long, ctypes.c_long, ctypes.c_long,
@@ -111,6 +122,36 @@ class Oracle:
         if rc != 0:
             raise RuntimeError("oracle_headwise_fwd failed")
         return states, last
+
+    def headwise_bwd(self, cell: str, Wx, R, b, states0=None, dstates=None, dlast=None):
+        """Head-wise backward in float64: the gradients of L = sum(dstates * states) +
+        sum(dlast * last_states) with respect to the forward's inputs.
+
+        Same inputs as headwise_fwd, plus dstates [S,B,T,N,D] and dlast [S,B,1,N,D] (None =
+        zeros). Returns (dWx [B,T,G,N,D], dR [G,N,D,D], db [G,N,D], dstates0 [S,B,1,N,D]).
+        """
+        c = {"lstm": CELL_LSTM, "elman": CELL_ELMAN, "gru": CELL_GRU}[cell]
+        G, S = {CELL_LSTM: (4, 2), CELL_ELMAN: (1, 1), CELL_GRU: (3, 1)}[c]
+        Wx, R = _f64(Wx), _f64(R)
+        B, T, G_, N, D = Wx.shape
+        b = np.zeros((G, N, D)) if b is None else _f64(b)
+        states0, dstates, dlast = _f64(states0), _f64(dstates), _f64(dlast)
+        if G_ != G or R.shape != (G, N, D, D) or b.shape != (G, N, D):
+            raise ValueError("shape mismatch")
+        for name, a, shp in (("states0", states0, (S, B, 1, N, D)), ("dstates", dstates, (S, B, T, N, D)),
+                             ("dlast", dlast, (S, B, 1, N, D))):
+            if a is not None and a.shape != shp:
+                raise ValueError(f"{name} shape mismatch")
+        dWx = np.empty((B, T, G, N, D))
+        dR = np.empty((G, N, D, D))
+        db = np.empty((G, N, D))
+        ds0 = np.empty((S, B, 1, N, D))
+        rc = self.lib.oracle_headwise_bwd(c, B, T, N, D, _ptr(Wx), _ptr(R), _ptr(b), _ptr(states0),
+                                          _ptr(dstates), _ptr(dlast), _ptr(dWx), _ptr(dR), _ptr(db),
+                                          _ptr(ds0))
+        if rc != 0:
+            raise RuntimeError("oracle_headwise_bwd failed")
+        return dWx, dR, db, ds0
 
     def lstm_stack_p3(self, x, Wi, Wh, b_ih, b_hh, h0=None, c0=None):
         """Plain multi-layer LSTM of "5.3 LSTM" in float64.
@@ -155,6 +196,10 @@ def default() -> Oracle:
 
 def headwise_fwd(*args, **kwargs):
     return default().headwise_fwd(*args, **kwargs)
+
+
+def headwise_bwd(*args, **kwargs):
+    return default().headwise_bwd(*args, **kwargs)
 
 
 def lstm_stack_p3(*args, **kwargs):

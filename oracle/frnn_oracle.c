@@ -1,6 +1,6 @@
 /*
- * frnn_oracle.c -- plain, slow, fp64 CPU oracle for the head-wise LSTM / Elman / GRU forward recurrence
- * and for the plain multi-layer LSTM.
+ * frnn_oracle.c -- plain, slow, fp64 CPU oracle for the head-wise LSTM / Elman / GRU forward
+ * recurrence, its backward (back-propagation through time), and the plain multi-layer LSTM.
  *
  * TEST INFRASTRUCTURE ONLY. Nothing on the product path may link, load or call this file: it is
  * used by the test-suite, by the smoke check and by the benchmark's CPU-baseline leg. It shares no
@@ -138,6 +138,210 @@ int oracle_headwise_fwd(int cell, long B, long T, long N, long D, const double* 
     }
     free(h); free(c); free(hn); free(acc); free(pre);
   }
+  return failed ? -1 : 0;
+}
+
+/*
+ * Head-wise backward (back-propagation through time) of oracle_headwise_fwd, for the loss
+ *   L = sum(dstates * states) + sum(dlast * last_states),
+ * i.e. given the gradients dstates [S,B,T,N,D] and dlast [S,B,1,N,D] of the two outputs (either
+ * may be NULL for zeros) it returns
+ *   dWx [B,T,G,N,D], dR [G,N,D,D], db [G,N,D], dstates0 [S,B,1,N,D]   (any may be NULL).
+ * The pages print no gradient formulas; these are the chain rule applied to the forward cell
+ * equations above (5.3 LSTM cell; Elman; the GRU reading), written out per step:
+ *   LSTM: tc = tanh(c_t);  dc = dc_in + dh*o*(1 - tc^2);  d_o = dh*tc
+ *         dpre_i = dc*z * i(1-i);  dpre_f = dc*c_{t-1} * f(1-f);  dpre_z = dc*i * (1-z^2);
+ *         dpre_o = d_o * o(1-o);   dc carried to step t-1: dc*f
+ *   Elman: dpre = dh * (1 - h_t^2)
+ *   GRU:  dn = dh*(1-z);  dz = dh*(h_{t-1} - n);  dh carried directly to step t-1: dh*z
+ *         dq = dn*(1-n^2) (q = the tanh argument);  dWx_n = dq;  da_n = dq*r;
+ *         dr = dq*(a_n + b_n);  dpre_r = dr*r(1-r);  dpre_z = dz*z(1-z)
+ * Here "da" is the gradient of the recurrent pre-activation part h*R (+ b): for the LSTM and
+ * Elman da = dWx = dpre; for the GRU they differ in the n gate. Then
+ *   dh_{t-1}[d] += sum_g sum_e da[g][e] * R[g,n,d,e]
+ *   dR[g,n,d,e]  = sum_b sum_t h_{t-1}[b,n,d] * da_t[b][g][e],   db[g,n,e] = sum_b sum_t da_t[b][g][e]
+ *   dstates0     = the gradient that reaches the initial state (h through R, plus the carried
+ *                  direct parts: LSTM c, GRU h).
+ * Each (b, n) row is run forward once more (keeping every step's gates and states), then walked
+ * backwards from t = T-1 to 0. dR and db are summed afterwards in a fixed order (b, then t).
+ */
+int oracle_headwise_bwd(int cell, long B, long T, long N, long D, const double* Wx, const double* R,
+                        const double* b, const double* states0, const double* dstates,
+                        const double* dlast, double* dWx, double* dR, double* db, double* dstates0) {
+  if (cell != ORACLE_CELL_LSTM && cell != ORACLE_CELL_ELMAN && cell != ORACLE_CELL_GRU) return -1;
+  if (B <= 0 || N <= 0 || D <= 0 || T < 0) return -1;
+  const long G = (cell == ORACLE_CELL_LSTM) ? 4 : (cell == ORACLE_CELL_GRU) ? 3 : 1;
+  const long S = (cell == ORACLE_CELL_LSTM) ? 2 : 1;
+  const long P = B * N;
+  /* per (b, n) row: hh[t] = h before step t (hh[T] = after the last), cc likewise (LSTM),
+     act[t][g][e] = gate values of step t, qn[t][e] = a_n + b_n (GRU), da[t][g][e] */
+  double* hh = (double*)malloc(sizeof(double) * P * (T + 1) * D);
+  double* cc = (double*)malloc(sizeof(double) * P * (T + 1) * D);
+  double* act = (double*)malloc(sizeof(double) * P * (T > 0 ? T : 1) * G * D);
+  double* qn = (double*)malloc(sizeof(double) * P * (T > 0 ? T : 1) * D);
+  double* da = (double*)malloc(sizeof(double) * P * (T > 0 ? T : 1) * G * D);
+  if (!hh || !cc || !act || !qn || !da) {
+    free(hh); free(cc); free(act); free(qn); free(da);
+    return -1;
+  }
+  int failed = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (long p = 0; p < P; ++p) {
+    const long bi = p / N, n = p % N;
+    double* H = hh + p * (T + 1) * D;
+    double* C = cc + p * (T + 1) * D;
+    double* A = act + p * (T > 0 ? T : 1) * G * D;
+    double* Q = qn + p * (T > 0 ? T : 1) * D;
+    double* DA = da + p * (T > 0 ? T : 1) * G * D;
+    double* pre = (double*)malloc(sizeof(double) * G * D);
+    double* dh = (double*)malloc(sizeof(double) * D);
+    double* dc = (double*)malloc(sizeof(double) * D);
+    double* dhn = (double*)malloc(sizeof(double) * D);
+    if (!pre || !dh || !dc || !dhn) {
+      free(pre); free(dh); free(dc); free(dhn);
+#pragma omp atomic write
+      failed = 1;
+      continue;
+    }
+    for (long e = 0; e < D; ++e) {
+      H[e] = states0 ? states0[((0 * B + bi) * N + n) * D + e] : 0.0;
+      C[e] = (S == 2 && states0) ? states0[((1 * B + bi) * N + n) * D + e] : 0.0;
+    }
+    /* forward, keeping what the backward needs */
+    for (long t = 0; t < T; ++t) {
+      const double* h = H + t * D;
+      for (long g = 0; g < G; ++g) {
+        for (long e = 0; e < D; ++e) pre[g * D + e] = b[(g * N + n) * D + e];
+        for (long d = 0; d < D; ++d) {
+          const double* row = R + ((g * N + n) * D + d) * D;
+          for (long e = 0; e < D; ++e) pre[g * D + e] += h[d] * row[e];
+        }
+      }
+      double* a = A + t * G * D;
+      for (long e = 0; e < D; ++e) {
+        const double wx0 = Wx[(((bi * T + t) * G + 0) * N + n) * D + e];
+        if (cell == ORACLE_CELL_LSTM) {
+          const double ig = sigmoid(wx0 + pre[0 * D + e]);
+          const double fg = sigmoid(Wx[(((bi * T + t) * G + 1) * N + n) * D + e] + pre[1 * D + e]);
+          const double zg = tanh(Wx[(((bi * T + t) * G + 2) * N + n) * D + e] + pre[2 * D + e]);
+          const double og = sigmoid(Wx[(((bi * T + t) * G + 3) * N + n) * D + e] + pre[3 * D + e]);
+          a[0 * D + e] = ig; a[1 * D + e] = fg; a[2 * D + e] = zg; a[3 * D + e] = og;
+          C[(t + 1) * D + e] = fg * C[t * D + e] + ig * zg;
+          H[(t + 1) * D + e] = og * tanh(C[(t + 1) * D + e]);
+        } else if (cell == ORACLE_CELL_GRU) {
+          const double rg = sigmoid(wx0 + pre[0 * D + e]);
+          const double zg = sigmoid(Wx[(((bi * T + t) * G + 1) * N + n) * D + e] + pre[1 * D + e]);
+          const double ng = tanh(Wx[(((bi * T + t) * G + 2) * N + n) * D + e] + rg * pre[2 * D + e]);
+          a[0 * D + e] = rg; a[1 * D + e] = zg; a[2 * D + e] = ng;
+          Q[t * D + e] = pre[2 * D + e];
+          H[(t + 1) * D + e] = (1.0 - zg) * ng + zg * h[e];
+        } else {
+          a[e] = tanh(wx0 + pre[e]);
+          H[(t + 1) * D + e] = a[e];
+        }
+      }
+    }
+    /* backward: dh, dc hold the gradient reaching the state after step t */
+    for (long e = 0; e < D; ++e) {
+      dh[e] = dlast ? dlast[((0 * B + bi) * N + n) * D + e] : 0.0;
+      dc[e] = (S == 2 && dlast) ? dlast[((1 * B + bi) * N + n) * D + e] : 0.0;
+    }
+    for (long t = T - 1; t >= 0; --t) {
+      const double* a = A + t * G * D;
+      double* dat = DA + t * G * D;
+      for (long e = 0; e < D; ++e) {
+        if (dstates) {
+          dh[e] += dstates[(((0 * B + bi) * T + t) * N + n) * D + e];
+          if (S == 2) dc[e] += dstates[(((1 * B + bi) * T + t) * N + n) * D + e];
+        }
+      }
+      for (long e = 0; e < D; ++e) {
+        double dw[4] = {0.0, 0.0, 0.0, 0.0};
+        if (cell == ORACLE_CELL_LSTM) {
+          const double ig = a[0 * D + e], fg = a[1 * D + e], zg = a[2 * D + e], og = a[3 * D + e];
+          const double tc = tanh(C[(t + 1) * D + e]);
+          const double dct = dc[e] + dh[e] * og * (1.0 - tc * tc);
+          dw[0] = dct * zg * ig * (1.0 - ig);
+          dw[1] = dct * C[t * D + e] * fg * (1.0 - fg);
+          dw[2] = dct * ig * (1.0 - zg * zg);
+          dw[3] = dh[e] * tc * og * (1.0 - og);
+          for (long g = 0; g < 4; ++g) dat[g * D + e] = dw[g];
+          dc[e] = dct * fg;
+          dh[e] = 0.0; /* h_{t-1} is reached only through R, added below */
+        } else if (cell == ORACLE_CELL_GRU) {
+          const double rg = a[0 * D + e], zg = a[1 * D + e], ng = a[2 * D + e];
+          const double dn = dh[e] * (1.0 - zg);
+          const double dz = dh[e] * (H[t * D + e] - ng);
+          const double dq = dn * (1.0 - ng * ng);
+          dw[0] = dq * Q[t * D + e] * rg * (1.0 - rg);
+          dw[1] = dz * zg * (1.0 - zg);
+          dw[2] = dq;
+          dat[0 * D + e] = dw[0];
+          dat[1 * D + e] = dw[1];
+          dat[2 * D + e] = dq * rg;
+          dh[e] = dh[e] * zg; /* the direct part; the part through R is added below */
+        } else {
+          const double ht = a[e];
+          dw[0] = dh[e] * (1.0 - ht * ht);
+          dat[e] = dw[0];
+          dh[e] = 0.0;
+        }
+        if (dWx)
+          for (long g = 0; g < G; ++g) dWx[(((bi * T + t) * G + g) * N + n) * D + e] = dw[g];
+      }
+      /* gradient reaching h_{t-1} through the contraction */
+      for (long d = 0; d < D; ++d) {
+        double s = 0.0;
+        for (long g = 0; g < G; ++g) {
+          const double* row = R + ((g * N + n) * D + d) * D;
+          for (long e = 0; e < D; ++e) s += dat[g * D + e] * row[e];
+        }
+        dhn[d] = s;
+      }
+      for (long d = 0; d < D; ++d) dh[d] += dhn[d];
+    }
+    if (dstates0) {
+      for (long e = 0; e < D; ++e) {
+        dstates0[((0 * B + bi) * N + n) * D + e] = dh[e];
+        if (S == 2) dstates0[((1 * B + bi) * N + n) * D + e] = dc[e];
+      }
+    }
+    free(pre); free(dh); free(dc); free(dhn);
+  }
+  if (!failed && (dR || db)) {
+    /* dR[g,n,d,e] = sum_b sum_t h_{t-1}[d] da_t[g][e]; db[g,n,e] = sum_b sum_t da_t[g][e] */
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long gn = 0; gn < G * N; ++gn) {
+      const long g = gn / N, n = gn % N;
+      for (long d = 0; d < D; ++d) {
+        double* out = dR ? dR + ((g * N + n) * D + d) * D : NULL;
+        if (out)
+          for (long e = 0; e < D; ++e) out[e] = 0.0;
+        for (long bi = 0; bi < B; ++bi) {
+          const long p = bi * N + n;
+          const double* H = hh + p * (T + 1) * D;
+          const double* DA = da + p * (T > 0 ? T : 1) * G * D;
+          for (long t = 0; t < T; ++t) {
+            const double hd = H[t * D + d];
+            if (out)
+              for (long e = 0; e < D; ++e) out[e] += hd * DA[(t * G + g) * D + e];
+          }
+        }
+      }
+      if (db) {
+        for (long e = 0; e < D; ++e) {
+          double s = 0.0;
+          for (long bi = 0; bi < B; ++bi) {
+            const long p = bi * N + n;
+            const double* DA = da + p * (T > 0 ? T : 1) * G * D;
+            for (long t = 0; t < T; ++t) s += DA[(t * G + g) * D + e];
+          }
+          db[(g * N + n) * D + e] = s;
+        }
+      }
+    }
+  }
+  free(hh); free(cc); free(act); free(qn); free(da);
   return failed ? -1 : 0;
 }
 

@@ -501,4 +501,154 @@ def pin_layer_major(orc):
     np.testing.assert_allclose(inp, out, rtol=0, atol=1e-12)
 
 
+# ----------------------------------------------------------------------------- backward
+_GS = {"lstm": (4, 2), "elman": (1, 1), "gru": (3, 1)}
+
+
+def _torch_identity_input_module(cell, H, seed):
+    """A float64 torch recurrent layer whose input weight is the identity and input bias zero, so
+    that its input x is exactly the head-wise Wx (torch's gate order: LSTM i, f, g, o; GRU r, z, n)
+    and its recurrent-side weight and bias are R and b."""
+    torch.manual_seed(seed)
+    G = _GS[cell][0]
+    if cell == "lstm":
+        m = torch.nn.LSTM(G * H, H, dtype=torch.float64)
+    elif cell == "gru":
+        m = torch.nn.GRU(G * H, H, dtype=torch.float64)
+    else:
+        m = torch.nn.RNN(H, H, nonlinearity="tanh", dtype=torch.float64)
+    with torch.no_grad():
+        m.weight_ih_l0.copy_(torch.eye(G * H, dtype=torch.float64))
+        m.bias_ih_l0.zero_()
+        m.bias_hh_l0.mul_(4.0)
+        m.weight_hh_l0.mul_(2.0)
+    return m
+
+
+def _pin_torch_autograd(orc, cell):
+    """Backward of N heads equals torch autograd through N float64 torch layers, for the loss
+    sum(dh * h_t) over all t + sum(dlast * last_states). torch returns c only at the end, so the
+    per-step c gradient is zero here (finite differences cover it)."""
+    G, S = _GS[cell]
+    T, B, H, N = 6, 3, 4, 2
+    rng = np.random.default_rng({"lstm": 51, "elman": 52, "gru": 53}[cell])
+    Wx = rng.normal(size=(B, T, G, N, H))
+    s0 = rng.normal(size=(S, B, 1, N, H)) * 0.7
+    dstates = np.zeros((S, B, T, N, H))
+    dstates[0] = rng.normal(size=(B, T, N, H))
+    dlast = rng.normal(size=(S, B, 1, N, H))
+    R = np.zeros((G, N, H, H))
+    b = np.zeros((G, N, H))
+    ref = {"dWx": np.zeros_like(Wx), "dR": np.zeros_like(R), "db": np.zeros_like(b), "ds0": np.zeros_like(s0)}
+    for n in range(N):
+        m = _torch_identity_input_module(cell, H, 400 + 10 * n + G)
+        whh = m.weight_hh_l0.detach().numpy()
+        bhh = m.bias_hh_l0.detach().numpy()
+        for g in range(G):
+            R[g, n] = whh[g * H:(g + 1) * H, :].T
+            b[g, n] = bhh[g * H:(g + 1) * H]
+        x = torch.tensor(Wx[:, :, :, n, :].reshape(B, T, G * H).transpose(1, 0, 2).copy(), requires_grad=True)
+        h0 = torch.tensor(s0[0, :, 0, n][None].copy(), requires_grad=True)
+        if cell == "lstm":
+            c0 = torch.tensor(s0[1, :, 0, n][None].copy(), requires_grad=True)
+            out, (hn, cn) = m(x, (h0, c0))
+            loss = (out * torch.from_numpy(dstates[0, :, :, n].transpose(1, 0, 2).copy())).sum() \
+                + (hn[0] * torch.from_numpy(dlast[0, :, 0, n].copy())).sum() \
+                + (cn[0] * torch.from_numpy(dlast[1, :, 0, n].copy())).sum()
+        else:
+            out, hn = m(x, h0)
+            loss = (out * torch.from_numpy(dstates[0, :, :, n].transpose(1, 0, 2).copy())).sum() \
+                + (hn[0] * torch.from_numpy(dlast[0, :, 0, n].copy())).sum()
+        loss.backward()
+        gx = x.grad.numpy().transpose(1, 0, 2).reshape(B, T, G, H)
+        ref["dWx"][:, :, :, n, :] = gx
+        gw = m.weight_hh_l0.grad.numpy()
+        gb = m.bias_hh_l0.grad.numpy()
+        for g in range(G):
+            ref["dR"][g, n] = gw[g * H:(g + 1) * H, :].T
+            ref["db"][g, n] = gb[g * H:(g + 1) * H]
+        ref["ds0"][0, :, 0, n] = h0.grad.numpy()[0]
+        if cell == "lstm":
+            ref["ds0"][1, :, 0, n] = c0.grad.numpy()[0]
+    dWx, dR, db, ds0 = orc.headwise_bwd(cell, Wx, R, b, s0, dstates, dlast)
+    np.testing.assert_allclose(dWx, ref["dWx"], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dR, ref["dR"], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(db, ref["db"], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(ds0, ref["ds0"], rtol=0, atol=1e-12)
+
+
+def pin_bwd_torch_lstm(orc):
+    _pin_torch_autograd(orc, "lstm")
+
+
+def pin_bwd_torch_gru(orc):
+    _pin_torch_autograd(orc, "gru")
+
+
+def pin_bwd_torch_elman(orc):
+    _pin_torch_autograd(orc, "elman")
+
+
+def _loss(orc, cell, Wx, R, b, s0, dstates, dlast):
+    st, last = orc.headwise_fwd(cell, Wx, R, b, s0)
+    return float((st * dstates).sum() + (last * dlast).sum())
+
+
+def pin_bwd_finite_differences(orc):
+    """Every gradient entry, on tiny problems of each cell with per-step c gradients, against
+    central differences of the (independently pinned) forward: |error| <= 1e-7."""
+    for cell, seed in (("lstm", 61), ("gru", 62), ("elman", 63)):
+        G, S = _GS[cell]
+        B, T, N, D = 2, 3, 2, 3
+        rng = np.random.default_rng(seed)
+        Wx = rng.normal(size=(B, T, G, N, D))
+        R = rng.normal(size=(G, N, D, D)) * 0.6
+        b = rng.normal(size=(G, N, D)) * 0.5
+        s0 = rng.normal(size=(S, B, 1, N, D)) * 0.5
+        dstates = rng.normal(size=(S, B, T, N, D))
+        dlast = rng.normal(size=(S, B, 1, N, D))
+        grads = orc.headwise_bwd(cell, Wx, R, b, s0, dstates, dlast)
+        eps = 1e-5
+        for k, arr in enumerate((Wx, R, b, s0)):
+            num = np.zeros_like(arr)
+            for idx in np.ndindex(arr.shape):
+                old = arr[idx]
+                arr[idx] = old + eps
+                lp = _loss(orc, cell, Wx, R, b, s0, dstates, dlast)
+                arr[idx] = old - eps
+                lm = _loss(orc, cell, Wx, R, b, s0, dstates, dlast)
+                arr[idx] = old
+                num[idx] = (lp - lm) / (2 * eps)
+            np.testing.assert_allclose(grads[k], num, rtol=0, atol=1e-7, err_msg=f"{cell} input {k}")
+
+
+def pin_bwd_linear_in_cotangent(orc):
+    """The backward is linear in (dstates, dlast), and zero cotangents give zero gradients."""
+    for cell in ("lstm", "gru", "elman"):
+        G, S = _GS[cell]
+        B, T, N, D = 2, 5, 2, 4
+        Wx, R, b, s0 = _rand_problem(cell, B, T, N, D, 64)
+        rng = np.random.default_rng(65)
+        d1, d2 = rng.normal(size=(S, B, T, N, D)), rng.normal(size=(S, B, T, N, D))
+        l1, l2 = rng.normal(size=(S, B, 1, N, D)), rng.normal(size=(S, B, 1, N, D))
+        g1 = orc.headwise_bwd(cell, Wx, R, b, s0, d1, l1)
+        g2 = orc.headwise_bwd(cell, Wx, R, b, s0, d2, l2)
+        g3 = orc.headwise_bwd(cell, Wx, R, b, s0, 2.0 * d1 - 3.0 * d2, 2.0 * l1 - 3.0 * l2)
+        for a, c, e in zip(g1, g2, g3):
+            np.testing.assert_allclose(e, 2.0 * a - 3.0 * c, rtol=1e-12, atol=1e-12)
+        for z in orc.headwise_bwd(cell, Wx, R, b, s0, None, None):
+            assert not np.any(z)
+
+
+def pin_bwd_t0(orc):
+    """T = 0: last_states is the initial state, so dstates0 = dlast and the rest is zero."""
+    for cell in ("lstm", "gru"):
+        G, S = _GS[cell]
+        Wx, R, b, s0 = _rand_problem(cell, 2, 0, 2, 3, 66)
+        dlast = np.random.default_rng(67).normal(size=(S, 2, 1, 2, 3))
+        dWx, dR, db, ds0 = orc.headwise_bwd(cell, Wx, R, b, s0, None, dlast)
+        assert dWx.shape == (2, 0, G, 2, 3) and not np.any(dR) and not np.any(db)
+        np.testing.assert_array_equal(ds0, dlast)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
