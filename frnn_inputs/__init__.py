@@ -115,6 +115,16 @@ def headwise_inputs(w: HeadwiseWorkload):
     return {"Wx": Wx, "R": R, "b": b, "states0": s0}
 
 
+def backward_cotangents(w: HeadwiseWorkload):
+    """Gradients of the forward's two outputs for a backward run: dstates [S,B,T,N,D] and dlast
+    [S,B,1,N,D], float32 ~N(0,1), drawn in that order from a generator seeded with seed + 1000."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(w.seed + 1000)
+    dstates = _normal(g, (w.S, w.B, w.T, w.N, w.D), 1.0)
+    dlast = _normal(g, (w.S, w.B, 1, w.N, w.D), 1.0)
+    return {"dstates": dstates, "dlast": dlast}
+
+
 def stack_inputs(w: StackWorkload):
     """Return dict(x, Wi[], Wh[], b_ih[], b_hh[], h0, c0) of CPU tensors in ``w.dtype``."""
     g = torch.Generator(device="cpu")

@@ -18,7 +18,8 @@ import torch
 __all__ = [
     "FRNN_PATH_ALTERNATING", "FRNN_PATH_FUSED", "FrnnError", "Desc", "lib_path", "load",
     "frnn_abi_version", "frnn_status_str", "frnn_workspace_bytes", "frnn_plan_str", "frnn_fwd",
-    "frnn_check", "frnn_lstm_stack_workspace_bytes", "frnn_lstm_stack_fwd",
+    "frnn_check", "frnn_lstm_stack_workspace_bytes", "frnn_lstm_stack_fwd", "frnn_bwd_workspace_bytes",
+    "frnn_bwd_plan_str", "frnn_bwd", "flashrnn",
 ]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -76,6 +77,12 @@ def load():
     lib.frnn_fwd.argtypes = [dptr, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.frnn_check.restype = i32
     lib.frnn_check.argtypes = [vp, vp]
+    lib.frnn_bwd_workspace_bytes.restype = i32
+    lib.frnn_bwd_workspace_bytes.argtypes = [dptr, i32, ctypes.POINTER(sz)]
+    lib.frnn_bwd_plan_str.restype = i32
+    lib.frnn_bwd_plan_str.argtypes = [dptr, i32, ctypes.c_char_p, sz]
+    lib.frnn_bwd.restype = i32
+    lib.frnn_bwd.argtypes = [dptr, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.frnn_lstm_stack_workspace_bytes.restype = i32
     lib.frnn_lstm_stack_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, ctypes.POINTER(sz)]
     lib.frnn_lstm_stack_fwd.restype = i32
@@ -190,6 +197,91 @@ def frnn_fwd(Wx: torch.Tensor, R: torch.Tensor, b: Optional[torch.Tensor] = None
     if check:
         frnn_check(workspace)
     return st_out, last
+
+
+def frnn_bwd_workspace_bytes(desc: Desc, path="alternating") -> int:
+    n = ctypes.c_size_t(0)
+    rc = load().frnn_bwd_workspace_bytes(ctypes.byref(desc), _path(path), ctypes.byref(n))
+    if rc != FRNN_OK:
+        raise FrnnError(rc, "frnn_bwd_workspace_bytes")
+    return n.value
+
+
+def frnn_bwd_plan_str(desc: Desc, path="alternating") -> str:
+    buf = ctypes.create_string_buffer(1024)
+    rc = load().frnn_bwd_plan_str(ctypes.byref(desc), _path(path), buf, 1024)
+    if rc != FRNN_OK:
+        raise FrnnError(rc, "frnn_bwd_plan_str")
+    return buf.value.decode()
+
+
+def frnn_bwd(Wx: torch.Tensor, R: torch.Tensor, b: Optional[torch.Tensor], states0: Optional[torch.Tensor],
+             states: torch.Tensor, dstates: Optional[torch.Tensor], dlast: Optional[torch.Tensor],
+             cell: str = "lstm", path="alternating", workspace: Optional[torch.Tensor] = None, check: bool = True):
+    """Backward of frnn_fwd: (dWx [B,T,G,N,D], dR [G,N,D,D], db [G,N,D], dstates0 [S,B,1,N,D]), fp32.
+
+    Wx, R, b, states0 as for frnn_fwd; states [S,B,T,N,D] fp32 is what frnn_fwd returned for them;
+    dstates [S,B,T,N,D] and dlast [S,B,1,N,D] (fp32 or None) are the gradients of its two outputs.
+    """
+    if cell not in _GATES_STATES:
+        raise ValueError(f"unknown cell {cell!r}")
+    G, S = _GATES_STATES[cell]
+    B, T, G_, N, D = Wx.shape
+    dev, dt = Wx.device, Wx.dtype
+    if G_ != G or dt not in _DTYPES:
+        raise ValueError("Wx: wrong gate count or dtype")
+    _check_tensor(R, "R", (G, N, D, D), dt, dev)
+    _check_tensor(b, "b", (G, N, D), dt, dev)
+    _check_tensor(states0, "states0", (S, B, 1, N, D), dt, dev)
+    _check_tensor(states, "states", (S, B, T, N, D), torch.float32, dev)
+    _check_tensor(dstates, "dstates", (S, B, T, N, D), torch.float32, dev)
+    _check_tensor(dlast, "dlast", (S, B, 1, N, D), torch.float32, dev)
+    desc = _desc(B, T, N, D, cell, dt)
+    p = _path(path)
+    f = torch.float32
+    dWx = torch.empty((B, T, G, N, D), dtype=f, device=dev)
+    dR = torch.empty((G, N, D, D), dtype=f, device=dev)
+    db = torch.empty((G, N, D), dtype=f, device=dev)
+    ds0 = torch.empty((S, B, 1, N, D), dtype=f, device=dev)
+    need = frnn_bwd_workspace_bytes(desc, p)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    elif workspace.numel() < need or workspace.device != dev:
+        raise ValueError("workspace too small")
+    rc = load().frnn_bwd(ctypes.byref(desc), p, _ptr(Wx), _ptr(R), _ptr(b), _ptr(states0), _ptr(states),
+                         _ptr(dstates), _ptr(dlast), _ptr(dWx), _ptr(dR), _ptr(db), _ptr(ds0), _ptr(workspace),
+                         workspace.numel(), _stream_handle(dev))
+    if rc != FRNN_OK:
+        raise FrnnError(rc, "frnn_bwd")
+    if check:
+        frnn_check(workspace)
+    return dWx, dR, db, ds0
+
+
+class _FlashRNNFunction(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, Wx, R, b, states0, cell, path, bwd_path):
+        states, last = frnn_fwd(Wx, R, b, states0, cell=cell, path=path)
+        ctx.save_for_backward(Wx, R, b, states0, states)
+        ctx.cell, ctx.bwd_path = cell, bwd_path
+        return states, last
+
+    @staticmethod
+    def backward(ctx, dstates, dlast):
+        Wx, R, b, states0, states = ctx.saved_tensors
+        c = lambda t: None if t is None else t.float().contiguous()
+        dWx, dR, db, ds0 = frnn_bwd(Wx, R, b, states0, states, c(dstates), c(dlast), cell=ctx.cell,
+                                    path=ctx.bwd_path)
+        cast = lambda g, like: None if like is None else g.to(like.dtype)
+        return cast(dWx, Wx), cast(dR, R), cast(db, b), cast(ds0, states0), None, None, None
+
+
+def flashrnn(Wx: torch.Tensor, R: torch.Tensor, b: Optional[torch.Tensor] = None,
+             states: Optional[torch.Tensor] = None, cell: str = "lstm", path="fused", bwd_path="alternating"):
+    """Differentiable head-wise forward (the FlashRNN page's functional call): returns (states,
+    last_states) like frnn_fwd; torch autograd runs frnn_bwd for the gradients of Wx, R, b and the
+    initial states (cast to their dtypes)."""
+    return _FlashRNNFunction.apply(Wx, R, b, states, cell, path, bwd_path)
 
 
 def frnn_lstm_stack_workspace_bytes(L, T, B, I, H, path="fused") -> int:

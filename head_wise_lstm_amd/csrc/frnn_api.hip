@@ -13,6 +13,7 @@
 
 #include "frnn.h"
 #include "frnn_alt.hpp"
+#include "frnn_bwd.hpp"
 #include "frnn_device.hpp"
 #include "frnn_proj.hpp"
 #include "frnn_rpack.hpp"
@@ -290,6 +291,38 @@ hipError_t launch_fill(void* p, size_t bytes, hipStream_t st, uint32_t value = 0
   return hipGetLastError();
 }
 
+// dst[j][k] = src[k][j] (K rows of Nc elements, 2- or 4-byte elements).
+template <typename E>
+void launch_transpose(const E* src, long long lds, int K, int Nc, E* dst, long long ldd, hipStream_t st) {
+  if (K <= 0 || Nc <= 0) return;
+  const int ty = (int)std::min<long long>(((long long)K + 31) / 32, 65535);
+  hipLaunchKernelGGL(transpose_kernel<E>, dim3((Nc + 31) / 32, ty), dim3(256), 0, st, src, lds, K, Nc, dst, ldd);
+}
+
+// C[M][Nc] = A[M][K] . Bt[Nc][K]^T in fp32: the tiled MFMA kernel for bf16 operands, the plain
+// fp32 MFMA kernel for fp32 ones. K is a multiple of 32.
+hipError_t launch_gemm(bool f32, int M, int Nc, int K, const void* A, long long lda, const void* Bt, long long ldb,
+                       float* C, long long ldc, hipStream_t st) {
+  if (M <= 0 || Nc <= 0) return hipSuccess;
+  if (K % 32 != 0) return hipErrorInvalidValue;
+  if (f32) {
+    const long long tiles = (long long)((M + 15) / 16) * ((Nc + 15) / 16);
+    hipLaunchKernelGGL(gemm_f32_kernel, dim3((unsigned)((tiles + 3) / 4)), dim3(256), 0, st, M, Nc, K,
+                       reinterpret_cast<const float*>(A), lda, reinterpret_cast<const float*>(Bt), ldb, C, ldc);
+    return hipGetLastError();
+  }
+  if (ldb != K) return hipErrorInvalidValue;  // the tiled kernel reads Bt rows with stride K
+  ProjArgs pa;
+  pa.M = M; pa.Nc = Nc; pa.K = K;
+  pa.A = A; pa.a_f32 = 0; pa.lda = lda;
+  pa.Bt = reinterpret_cast<const uint16_t*>(Bt);
+  pa.b1 = nullptr; pa.b2 = nullptr;
+  pa.C = C; pa.ldc = ldc;
+  const dim3 pgrid(((Nc + PJ_BN - 1) / PJ_BN) * ((M + PJ_BM - 1) / PJ_BM));
+  hipLaunchKernelGGL(proj_gemm_kernel<false>, pgrid, dim3(256), 0, st, pa);
+  return hipGetLastError();
+}
+
 void trace(const char* fmt, const std::string& s) {
   if (env_int("FRNN_TRACE", 0)) std::fprintf(stderr, fmt, s.c_str());
 }
@@ -395,6 +428,43 @@ int run_recurrence(const Problem& p, int path, int* err, void* scratch, hipStrea
     hipLaunchKernelGGL(alt_gate_kernel, tgrid, dim3(256), 0, st, a, t);
   }
   return hipGetLastError() == hipSuccess ? FRNN_OK : FRNN_EHIP;
+}
+
+// ----------------------------------------------------------------------------- backward
+// Workspace of frnn_bwd after the error word (grows with T: it holds every step's h.R and da).
+struct BwdLayout {
+  size_t hprev, hprevT, rt, hr, da, daT, tmp, dhrec, carry, total;
+};
+
+BwdLayout bwd_layout(int B, int T, int N, int D, int cell, int f32) {
+  const size_t G = gates_of(cell), elt = f32 ? 4 : 2;
+  const size_t Kp = ((size_t)T * B + 31) / 32 * 32;
+  BwdLayout L;
+  size_t q = 0;
+  L.hprev = q;  q += align256((size_t)N * Kp * D * elt);
+  L.hprevT = q; q += align256((size_t)N * (D + 1) * Kp * elt);
+  L.rt = q;     q += align256((size_t)N * G * D * D * elt);
+  L.hr = q;     q += align256((size_t)N * T * B * G * D * 4);
+  L.da = q;     q += align256((size_t)N * Kp * G * D * elt);
+  L.daT = q;    q += align256((size_t)N * G * D * Kp * elt);
+  L.tmp = q;    q += align256((size_t)N * (D + 1) * G * D * 4);
+  L.dhrec = q;  q += align256((size_t)B * N * D * 4);
+  L.carry = q;  q += align256((size_t)B * N * D * 4);
+  L.total = q;
+  return L;
+}
+
+std::string bwd_plan_string(const frnn_desc* d, int path) {
+  char buf[384];
+  const int G = gates_of(d->cell);
+  const long long Kp = ((long long)d->T * d->B + 31) / 32 * 32;
+  std::snprintf(buf, sizeof(buf),
+                "backward path=%s cell=%s dtype=%s B=%d T=%d N=%d D=%d hr_gemm=%lldx%dx%d dR_gemm=%dx%dx%lld "
+                "step_launches=%d",
+                path == FRNN_PATH_FUSED ? "fused" : "alternating", cell_name(d->cell),
+                d->in_dtype == FRNN_F32 ? "f32" : "bf16", d->B, d->T, d->N, d->D, (long long)d->T * d->B, G * d->D,
+                d->D, d->D + 1, G * d->D, Kp, 2 * d->T);
+  return std::string(buf);
 }
 
 bool misaligned(const void* p) { return p && (reinterpret_cast<uintptr_t>(p) & 15u); }
@@ -537,6 +607,147 @@ int frnn_check(const void* workspace, void* stream) {
   return FRNN_OK;
 }
 
+int frnn_bwd_workspace_bytes(const frnn_desc* d, int path, size_t* bytes) {
+  const int rc = validate_desc(d, path);
+  if (rc != FRNN_OK) return rc;
+  if (!bytes) return FRNN_EINVAL;
+  if (path != FRNN_PATH_ALTERNATING) return FRNN_EUNSUPPORTED;
+  *bytes = kErrBytes + bwd_layout(d->B, d->T, d->N, d->D, d->cell, d->in_dtype == FRNN_F32).total;
+  return FRNN_OK;
+}
+
+int frnn_bwd(const frnn_desc* d, int path, const void* Wx, const void* R, const void* b, const void* states0,
+             const void* states, const void* dstates, const void* dlast, void* dWx, void* dR, void* db,
+             void* dstates0, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = validate_desc(d, path);
+  if (rc != FRNN_OK) return rc;
+  if (path != FRNN_PATH_ALTERNATING) return FRNN_EUNSUPPORTED;
+  if (d->T > 0 && (!Wx || !R || !states)) return FRNN_EINVAL;
+  for (const void* p : {Wx, R, b, states0, states, dstates, dlast, (const void*)dWx, (const void*)dR, (const void*)db,
+                        (const void*)dstates0, (const void*)workspace})
+    if (misaligned(p)) return FRNN_EINVAL;
+  const int f32 = d->in_dtype == FRNN_F32;
+  const BwdLayout L = bwd_layout(d->B, d->T, d->N, d->D, d->cell, f32);
+  if (!workspace || workspace_bytes < kErrBytes + L.total) return FRNN_EWORKSPACE;
+  DevInfo di;
+  rc = get_devinfo(&di);
+  if (rc != FRNN_OK) return rc;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  trace("[frnn] %s\n", bwd_plan_string(d, path));
+  const int B = d->B, T = d->T, N = d->N, D = d->D, G = gates_of(d->cell), S = d->cell == FRNN_CELL_LSTM ? 2 : 1;
+  const long long BND = (long long)B * N * D;
+  const size_t elt = f32 ? 4 : 2;
+  if (launch_fill(workspace, kErrBytes, st) != hipSuccess) return FRNN_EHIP;
+  const unsigned sgrid = (unsigned)((BND + 255) / 256);
+  if (T == 0) {
+    // last_states is the initial state: dstates0 = dlast, and nothing else receives a gradient
+    if (dstates0) {
+      const long long n = (long long)S * BND;
+      if (dlast)
+        hipLaunchKernelGGL(copy_init_kernel, dim3((unsigned)std::min<long long>((n + 255) / 256, 4096)), dim3(256), 0, st,
+                           dlast, 1, reinterpret_cast<float*>(dstates0), n);
+      else if (launch_fill(dstates0, (size_t)n * 4, st) != hipSuccess) return FRNN_EHIP;
+    }
+    if (dR && launch_fill(dR, (size_t)G * N * D * D * 4, st) != hipSuccess) return FRNN_EHIP;
+    if (db && launch_fill(db, (size_t)G * N * D * 4, st) != hipSuccess) return FRNN_EHIP;
+    return hipGetLastError() == hipSuccess ? FRNN_OK : FRNN_EHIP;
+  }
+  char* base = reinterpret_cast<char*>(workspace) + kErrBytes;
+  const int Kp = (int)(((long long)T * B + 31) / 32 * 32);
+  BwdArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.B = B; a.T = T; a.N = N; a.D = D; a.cell = d->cell; a.f32 = f32; a.Kp = Kp;
+  a.Wx = Wx; a.wx_sb = (long long)T * G * N * D; a.wx_st = (long long)G * N * D;
+  a.R = R; a.r_sg = (long long)N * D * D; a.r_sn = (long long)D * D; a.r_sd = D;
+  a.bias = b;
+  a.s0_h = states0;
+  a.s0_c = (states0 && S == 2) ? reinterpret_cast<const char*>(states0) + (size_t)BND * elt : nullptr;
+  a.s0_sb = (long long)N * D;
+  const float* stf = reinterpret_cast<const float*>(states);
+  a.st_h = stf; a.st_c = S == 2 ? stf + (long long)B * T * N * D : nullptr;
+  a.st_sb = (long long)T * N * D; a.st_st = (long long)N * D;
+  const float* dsf = reinterpret_cast<const float*>(dstates);
+  a.ds_h = dsf; a.ds_c = (dsf && S == 2) ? dsf + (long long)B * T * N * D : nullptr;
+  const float* dlf = reinterpret_cast<const float*>(dlast);
+  a.dl_h = dlf; a.dl_c = (dlf && S == 2) ? dlf + BND : nullptr;
+  a.last_sb = (long long)N * D;
+  a.dWx = reinterpret_cast<float*>(dWx);
+  a.ds0_h = reinterpret_cast<float*>(dstates0);
+  a.ds0_c = (dstates0 && S == 2) ? reinterpret_cast<float*>(dstates0) + BND : nullptr;
+  a.hprev = base + L.hprev;
+  a.hr = reinterpret_cast<const float*>(base + L.hr);
+  a.da = base + L.da;
+  a.dhrec = reinterpret_cast<float*>(base + L.dhrec);
+  a.carry = reinterpret_cast<float*>(base + L.carry);
+  char* hT = base + L.hprevT;
+  char* rt = base + L.rt;
+  char* daT = base + L.daT;
+  float* tmp = reinterpret_cast<float*>(base + L.tmp);
+  float* hr = reinterpret_cast<float*>(base + L.hr);
+  // carried gradients start at zero; da's rows past T*B stay zero for the dR GEMM
+  if (launch_fill(a.dhrec, (size_t)BND * 4, st) != hipSuccess || launch_fill(a.carry, (size_t)BND * 4, st) != hipSuccess ||
+      launch_fill(a.da, (size_t)N * Kp * G * D * elt, st) != hipSuccess)
+    return FRNN_EHIP;
+  // 1. h_{t-1} for every step, R^T, and h.R for every step
+  hipLaunchKernelGGL(bwd_hprev_kernel, dim3((unsigned)std::min<long long>(((long long)N * Kp * D + 255) / 256, 65536)),
+                     dim3(256), 0, st, a);
+  for (int n = 0; n < N; ++n) {
+    for (int g = 0; g < G; ++g) {
+      const size_t src = (size_t)g * a.r_sg + (size_t)n * a.r_sn, dst = ((size_t)n * G + g) * D * D;
+      if (f32) launch_transpose<uint32_t>(reinterpret_cast<const uint32_t*>(R) + src, D, D, D, reinterpret_cast<uint32_t*>(rt) + dst, D, st);
+      else launch_transpose<uint16_t>(reinterpret_cast<const uint16_t*>(R) + src, D, D, D, reinterpret_cast<uint16_t*>(rt) + dst, D, st);
+    }
+    if (launch_gemm(f32, T * B, G * D, D, base + L.hprev + (size_t)n * Kp * D * elt, D, rt + (size_t)n * G * D * D * elt, D,
+                    hr + (size_t)n * T * B * G * D, (long long)G * D, st) != hipSuccess)
+      return FRNN_EHIP;
+  }
+  // 2. the serial part
+  for (int t = T - 1; t >= 0; --t) {
+    hipLaunchKernelGGL(bwd_gate_kernel, dim3(sgrid), dim3(256), 0, st, a, t);
+    const dim3 hgrid(D / 16, (B + 15) / 16, N);
+    if (f32) hipLaunchKernelGGL(bwd_dh_kernel<true>, hgrid, dim3(256), 0, st, a, t);
+    else hipLaunchKernelGGL(bwd_dh_kernel<false>, hgrid, dim3(256), 0, st, a, t);
+  }
+  hipLaunchKernelGGL(bwd_final_kernel, dim3(sgrid), dim3(256), 0, st, a);
+  if (hipGetLastError() != hipSuccess) return FRNN_EHIP;
+  // 3. dR and db: per head, [D+1 rows: h^T and ones] x [G*D columns of da], over K = T*B
+  if (dR || db) {
+    for (int n = 0; n < N; ++n) {
+      const size_t hoff = (size_t)n * Kp * D, toff = (size_t)n * (D + 1) * Kp;
+      const size_t doff = (size_t)n * Kp * G * D, dtoff = (size_t)n * G * D * Kp;
+      if (f32) {
+        launch_transpose<uint32_t>(reinterpret_cast<const uint32_t*>(a.hprev) + hoff, D, Kp, D, reinterpret_cast<uint32_t*>(hT) + toff, Kp, st);
+        launch_transpose<uint32_t>(reinterpret_cast<const uint32_t*>(a.da) + doff, (long long)G * D, Kp, G * D,
+                                   reinterpret_cast<uint32_t*>(daT) + dtoff, Kp, st);
+      } else {
+        launch_transpose<uint16_t>(reinterpret_cast<const uint16_t*>(a.hprev) + hoff, D, Kp, D, reinterpret_cast<uint16_t*>(hT) + toff, Kp, st);
+        launch_transpose<uint16_t>(reinterpret_cast<const uint16_t*>(a.da) + doff, (long long)G * D, Kp, G * D,
+                                   reinterpret_cast<uint16_t*>(daT) + dtoff, Kp, st);
+      }
+    }
+    hipLaunchKernelGGL(bwd_ones_row_kernel, dim3((unsigned)std::min<long long>(((long long)N * Kp + 255) / 256, 4096)),
+                       dim3(256), 0, st, hT, N, D, Kp, f32);
+    for (int n = 0; n < N; ++n) {
+      if (launch_gemm(f32, D + 1, G * D, Kp, hT + (size_t)n * (D + 1) * Kp * elt, Kp, daT + (size_t)n * G * D * Kp * elt, Kp,
+                      tmp + (size_t)n * (D + 1) * G * D, (long long)G * D, st) != hipSuccess)
+        return FRNN_EHIP;
+    }
+    const long long nt = (long long)N * (D + 1) * G * D;
+    hipLaunchKernelGGL(bwd_scatter_kernel, dim3((unsigned)std::min<long long>((nt + 255) / 256, 65536)), dim3(256), 0, st,
+                       tmp, N, D, G, reinterpret_cast<float*>(dR), reinterpret_cast<float*>(db));
+  }
+  return hipGetLastError() == hipSuccess ? FRNN_OK : FRNN_EHIP;
+}
+
+int frnn_bwd_plan_str(const frnn_desc* d, int path, char* buf, size_t cap) {
+  const int rc = validate_desc(d, path);
+  if (rc != FRNN_OK) return rc;
+  if (!buf || cap == 0) return FRNN_EINVAL;
+  if (path != FRNN_PATH_ALTERNATING) return FRNN_EUNSUPPORTED;
+  std::snprintf(buf, cap, "%s", bwd_plan_string(d, path).c_str());
+  return FRNN_OK;
+}
+
 static int validate_stack(int L, int T, int B, int I, int H, int path) {
   if (L < 1 || T < 0 || B < 1 || I < 1 || H < 1) return FRNN_EINVAL;
   if (path != FRNN_PATH_ALTERNATING && path != FRNN_PATH_FUSED) return FRNN_EINVAL;
@@ -625,8 +836,7 @@ int frnn_lstm_stack_fwd(int L, int T, int B, int I, int H, int path, const void*
     pa.b2 = b_hh ? reinterpret_cast<const uint16_t*>(b_hh[l]) : nullptr;
     pa.C = wx;
     pa.ldc = 4 * H;
-    hipLaunchKernelGGL(proj_transpose_kernel, dim3((pa.Nc + 31) / 32, (pa.K + 31) / 32), dim3(256), 0, st,
-                       reinterpret_cast<const uint16_t*>(Wi[l]), (long long)pa.Nc, pa.K, pa.Nc, wit);
+    launch_transpose<uint16_t>(reinterpret_cast<const uint16_t*>(Wi[l]), pa.Nc, pa.K, pa.Nc, wit, pa.K, st);
     const dim3 pgrid(((pa.Nc + PJ_BN - 1) / PJ_BN) * ((pa.M + PJ_BM - 1) / PJ_BM));
     if (pa.a_f32) hipLaunchKernelGGL(proj_gemm_kernel<true>, pgrid, dim3(256), 0, st, pa);
     else hipLaunchKernelGGL(proj_gemm_kernel<false>, pgrid, dim3(256), 0, st, pa);

@@ -2,7 +2,7 @@
 // steps at once, as one MFMA GEMM:  C[M][Nc] (fp32) = A[M][K] . Wi[K][Nc] + b1[Nc] + b2[Nc].
 // A is bf16 or fp32 (rounded to bf16 as it is staged), Wi and the biases bf16, row-major.
 //
-// Wi is first transposed to Bt[Nc][K] (proj_transpose_kernel), so that both operands are read
+// Wi is first transposed to Bt[Nc][K] (transpose_kernel), so that both operands are read
 // as rows of K: every global load is 16 contiguous bytes and every MFMA fragment one 16-byte LDS
 // read. The GEMM runs 256 x 128 output tiles per workgroup; each of the 4 waves owns 128 x 64
 // (8 x 4 tiles of v_mfma_f32_16x16x32_bf16, 32 accumulators), which keeps LDS traffic at about
@@ -32,22 +32,28 @@ constexpr int PJ_BM = 256, PJ_BN = 128, PJ_BK = 32;
 constexpr int PJ_DIES = 8;  // accelerator dies (XCDs) of an MI355X
 constexpr int PJ_LS = PJ_BK + 8;  // LDS row stride (bf16): 80 bytes, spreads a fragment's rows over the banks
 
-// Wi [K][Nc] -> Bt [Nc][K], 32 x 32 tiles through LDS.
-__global__ void __launch_bounds__(256) proj_transpose_kernel(const uint16_t* Wi, long long ldw, int K, int Nc,
-                                                             uint16_t* Bt) {
-  __shared__ uint16_t s[32][33];
-  const int k0 = blockIdx.y * 32, n0 = blockIdx.x * 32;
+// dst[j][k] = src[k][j] for k < K, j < Nc (src row stride lds, dst row stride ldd), 32 x 32 tiles
+// through LDS. Grid (ceil(Nc/32), min(ceil(K/32), 65535)); the y tiles repeat by gridDim.y.
+template <typename E>
+__global__ void __launch_bounds__(256) transpose_kernel(const E* src, long long lds, int K, int Nc, E* dst,
+                                                        long long ldd) {
+  __shared__ E s[32][33];
+  const int n0 = blockIdx.x * 32;
   const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;  // 32 x 8
+  for (int kb = blockIdx.y; kb * 32 < K; kb += gridDim.y) {
+    const int k0 = kb * 32;
 #pragma unroll
-  for (int i = 0; i < 32; i += 8) {
-    const int k = k0 + ty + i, n = n0 + tx;
-    s[ty + i][tx] = (k < K && n < Nc) ? Wi[(long long)k * ldw + n] : (uint16_t)0;
-  }
-  __syncthreads();
+    for (int i = 0; i < 32; i += 8) {
+      const int k = k0 + ty + i, n = n0 + tx;
+      s[ty + i][tx] = (k < K && n < Nc) ? src[(long long)k * lds + n] : (E)0;
+    }
+    __syncthreads();
 #pragma unroll
-  for (int i = 0; i < 32; i += 8) {
-    const int n = n0 + ty + i, k = k0 + tx;
-    if (n < Nc && k < K) Bt[(long long)n * K + k] = s[tx][ty + i];
+    for (int i = 0; i < 32; i += 8) {
+      const int n = n0 + ty + i, k = k0 + tx;
+      if (n < Nc && k < K) dst[(long long)n * ldd + k] = s[tx][ty + i];
+    }
+    __syncthreads();
   }
 }
 

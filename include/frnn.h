@@ -116,6 +116,38 @@ int frnn_fwd(const frnn_desc* d, int path, const void* Wx, const void* R, const 
              size_t workspace_bytes, void* stream);
 
 /*
+ * Backward of frnn_fwd (back-propagation through time). The FlashRNN usage example creates its
+ * inputs with requires_grad; the pages print no gradient formulas, so this is the chain rule of
+ * the cell equations above. For the loss
+ *     L = sum(dstates * states) + sum(dlast * last_states)
+ * it writes dWx = dL/dWx, dR = dL/dR, db = dL/db and dstates0 = dL/dstates0. Layouts:
+ *   Wx, R, b, states0   as for frnn_fwd (in_dtype; b and states0 may be NULL = zeros)
+ *   states      [S, B, T, N, D]   fp32, read-only: the states frnn_fwd returned for these inputs
+ *                                 (required when T > 0; the backward recomputes the gates from them)
+ *   dstates     [S, B, T, N, D]   fp32, read-only, or NULL = zeros
+ *   dlast       [S, B, 1, N, D]   fp32, read-only, or NULL = zeros
+ *   dWx         [B, T, G, N, D]   fp32, written, or NULL
+ *   dR          [G, N, D, D]      fp32, written, or NULL
+ *   db          [G, N, D]         fp32, written, or NULL
+ *   dstates0    [S, B, 1, N, D]   fp32, written, or NULL
+ * The contractions take bf16 operands (fp32 for fp32 inputs) with fp32 accumulation, like the
+ * forward. T == 0: dstates0 = dlast, dR = db = 0. Only FRNN_PATH_ALTERNATING is offered (per
+ * step: a pointwise kernel and an MFMA kernel; before the steps one GEMM recomputes h.R for all
+ * of them, after them one GEMM forms dR and db); FRNN_PATH_FUSED returns FRNN_EUNSUPPORTED. The
+ * workspace grows with T (it holds every step's h.R and gradient).
+ */
+int frnn_bwd(const frnn_desc* d, int path, const void* Wx, const void* R, const void* b,
+             const void* states0, const void* states, const void* dstates, const void* dlast,
+             void* dWx, void* dR, void* db, void* dstates0, void* workspace,
+             size_t workspace_bytes, void* stream);
+
+/* Workspace bytes frnn_bwd needs for `d` on `path` (grows with T). */
+int frnn_bwd_workspace_bytes(const frnn_desc* d, int path, size_t* bytes);
+
+/* Description of the launches frnn_bwd would make (for logs and tests). */
+int frnn_bwd_plan_str(const frnn_desc* d, int path, char* buf, size_t cap);
+
+/*
  * Plain multi-layer unidirectional LSTM with input projection ("5.3 LSTM": MyLSTM.set_weights,
  * MyLSTM.forward). Per layer l and step t:
  *   gates = in_t . Wi[l] + h . Wh[l] + (b_ih[l] + b_hh[l]),   column blocks i | f | g | o of width H

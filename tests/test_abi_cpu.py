@@ -192,3 +192,26 @@ def test_planner_gru_matches_lstm_tiles(lib):
             sg = plan(D(B=B, T=8, N=N, Dm=Dm, cell=2, ind=ind), 1)
             assert "cell=gru" in sg
             assert sg.replace("cell=gru", "cell=lstm") == sl
+
+
+def test_bwd_validation_and_workspace(lib):
+    """frnn_bwd: validated before any device call; the workspace grows with T; only the
+    alternating path is offered."""
+    f = lib.frnn_bwd
+    p = ctypes.c_void_p(0x100000)
+    d = D(B=2, T=3, N=1, Dm=64)
+    n = ctypes.c_size_t(0)
+    assert lib.frnn_bwd_workspace_bytes(ctypes.byref(d), 0, ctypes.byref(n)) == 0
+    need = n.value
+    assert lib.frnn_bwd_workspace_bytes(ctypes.byref(d), 1, ctypes.byref(n)) == EUNSUP
+    assert lib.frnn_bwd_workspace_bytes(ctypes.byref(D(B=2, T=300, N=1, Dm=64)), 0, ctypes.byref(n)) == 0
+    assert n.value > need
+    args = lambda ws, nb: (p, p, None, None, p, None, None, p, p, p, p, ws, nb, None)
+    assert f(ctypes.byref(d), 1, *args(p, need)) == EUNSUP                       # fused backward
+    assert f(ctypes.byref(D(B=0)), 0, *args(p, need)) == EINVAL
+    assert f(ctypes.byref(d), 0, p, p, None, None, None, None, None, p, p, p, p, p, need, None) == EINVAL  # states NULL
+    assert f(ctypes.byref(d), 0, *args(None, need)) == EWS
+    assert f(ctypes.byref(d), 0, *args(p, need - 1)) == EWS
+    assert f(ctypes.byref(d), 0, ctypes.c_void_p(0x100004), *args(p, need)[1:]) == EINVAL  # misaligned Wx
+    s = hw.frnn_bwd_plan_str(D(B=16, T=1024, N=1, Dm=768), 0)
+    assert s.startswith("backward path=alternating cell=lstm") and "hr_gemm=16384x3072x768" in s

@@ -1,0 +1,127 @@
+"""HIP backward (frnn_bwd) against the fp64 oracle's back-propagation through time.
+
+The GPU runs its own forward, then the backward from the states it returned; the oracle runs
+both in fp64 on the same stored inputs and the same seeded cotangents (dstates, dlast ~ N(0,1)).
+
+Bar, per gradient tensor X (dWx, dR, db, dstates0): max|X_gpu - X_oracle| <= tol * max(1,
+max|X_oracle|), tol = 1e-4 for fp32 inputs and 3e-2 for bf16 inputs (the forward's bars, taken
+relative to the tensor's scale: dR and db are sums over all B*T steps and grow with them).
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import frnn_inputs as fi
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+TOL = {torch.float32: 1e-4, torch.bfloat16: 3e-2}
+
+
+def _hw():
+    import head_wise_lstm_amd as hw
+    return hw
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    _hw().load()
+
+
+def _log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def run_bwd_case(w, path="alternating"):
+    hw = _hw()
+    x = fi.make_inputs(w)
+    ct = fi.backward_cotangents(w)
+    dev = torch.device("cuda:0")
+    g = lambda t: None if t is None else t.to(dev)
+    _log(f"bwd case {w.name} cell={w.cell} B={w.B} T={w.T} N={w.N} D={w.D} path={path}")
+    st, last = hw.frnn_fwd(g(x["Wx"]), g(x["R"]), g(x["b"]), g(x["states0"]), cell=w.cell, path="fused"
+                           if w.dtype == torch.bfloat16 or w.D <= 64 else "alternating")
+    grads = hw.frnn_bwd(g(x["Wx"]), g(x["R"]), g(x["b"]), g(x["states0"]), st, g(ct["dstates"]), g(ct["dlast"]),
+                        cell=w.cell, path=path)
+    torch.cuda.synchronize()
+    f = fi.to_f64
+    ref = oracle.headwise_bwd(w.cell, f(x["Wx"]), f(x["R"]), f(x["b"]), f(x["states0"]), f(ct["dstates"]),
+                              f(ct["dlast"]))
+    tol = TOL[w.dtype]
+    errs = {}
+    for name, gv, rv in zip(("dWx", "dR", "db", "dstates0"), grads, ref):
+        gv = gv.double().cpu().numpy()
+        assert gv.shape == rv.shape, name
+        assert np.all(np.isfinite(gv)), name
+        scale = max(1.0, float(np.abs(rv).max())) if rv.size else 1.0
+        err = float(np.abs(gv - rv).max()) if rv.size else 0.0
+        errs[name] = (err, scale)
+    _log("  " + " ".join(f"{k}: err={e:.3e} scale={s:.3g} rel={e / s:.2e}" for k, (e, s) in errs.items()))
+    for k, (e, s) in errs.items():
+        assert e <= tol * s, f"{k}: max abs err {e} > {tol} * {s}"
+    return errs
+
+
+SMALL = [
+    fi.HeadwiseWorkload("bwd_lstm_bf16_ragged_D64", "lstm", torch.bfloat16, B=5, T=13, N=2, D=64, seed=201, s0_var=1.0),
+    fi.HeadwiseWorkload("bwd_lstm_bf16_D96", "lstm", torch.bfloat16, B=19, T=7, N=2, D=96, seed=202, s0_var=0.5),
+    fi.HeadwiseWorkload("bwd_lstm_bf16_D256", "lstm", torch.bfloat16, B=9, T=12, N=2, D=256, seed=203, s0_var=1.0,
+                        b_var=1.0),
+    fi.HeadwiseWorkload("bwd_elman_bf16_D64", "elman", torch.bfloat16, B=21, T=9, N=3, D=64, seed=204, s0_var=1.0),
+    fi.HeadwiseWorkload("bwd_elman_bf16_D128", "elman", torch.bfloat16, B=7, T=10, N=2, D=128, seed=205),
+    fi.HeadwiseWorkload("bwd_gru_bf16_D64", "gru", torch.bfloat16, B=5, T=13, N=2, D=64, seed=206, s0_var=1.0),
+    fi.HeadwiseWorkload("bwd_gru_bf16_D256", "gru", torch.bfloat16, B=9, T=12, N=2, D=256, seed=207, s0_var=1.0,
+                        b_var=1.0),
+    fi.HeadwiseWorkload("bwd_lstm_f32_D32", "lstm", torch.float32, B=3, T=11, N=2, D=32, seed=208, s0_var=1.0),
+    fi.HeadwiseWorkload("bwd_elman_f32_D64", "elman", torch.float32, B=4, T=9, N=3, D=64, seed=209, s0_var=1.0),
+    fi.HeadwiseWorkload("bwd_gru_f32_D32", "gru", torch.float32, B=3, T=11, N=2, D=32, seed=210, s0_var=1.0),
+    fi.HeadwiseWorkload("bwd_lstm_bf16_T1", "lstm", torch.bfloat16, B=1, T=1, N=1, D=64, seed=211, s0_var=1.0),
+]
+
+
+@pytest.mark.parametrize("w", SMALL, ids=lambda w: w.name)
+def test_bwd_small(w):
+    run_bwd_case(w)
+
+
+@pytest.mark.parametrize("name", ["lstm_bf16_B16_T1024_N1_D768", "lstm_bf16_B8_T1024_N3_D256",
+                                  "gru_bf16_B16_T1024_N1_D768", "lstm_f32_B2_T16_N1_D32"])
+def test_bwd_full(name):
+    run_bwd_case(fi.get_workload(name))
+
+
+def test_bwd_t0():
+    hw = _hw()
+    dev = torch.device("cuda:0")
+    for cell, G, S in (("lstm", 4, 2), ("gru", 3, 1)):
+        Wx = torch.zeros((3, 0, G, 2, 64), dtype=torch.bfloat16, device=dev)
+        R = torch.randn((G, 2, 64, 64), device=dev).to(torch.bfloat16)
+        st = torch.zeros((S, 3, 0, 2, 64), device=dev)
+        dlast = torch.randn((S, 3, 1, 2, 64), device=dev)
+        dWx, dR, db, ds0 = hw.frnn_bwd(Wx, R, None, None, st, None, dlast, cell=cell)
+        assert dWx.shape == (3, 0, G, 2, 64)
+        assert torch.count_nonzero(dR).item() == 0 and torch.count_nonzero(db).item() == 0
+        torch.testing.assert_close(ds0, dlast, rtol=0, atol=0)
+
+
+def test_autograd_function_matches_frnn_bwd():
+    """flashrnn() under torch autograd gives the gradients frnn_bwd returns (cast to the inputs'
+    dtypes)."""
+    hw = _hw()
+    w = fi.HeadwiseWorkload("ag", "lstm", torch.float32, B=4, T=9, N=2, D=64, seed=221, s0_var=1.0)
+    x = fi.make_inputs(w)
+    ct = fi.backward_cotangents(w)
+    dev = torch.device("cuda:0")
+    leaves = [x[k].to(dev).requires_grad_(True) for k in ("Wx", "R", "b", "states0")]
+    st, last = hw.flashrnn(*leaves, cell="lstm")
+    loss = (st * ct["dstates"].to(dev)).sum() + (last * ct["dlast"].to(dev)).sum()
+    loss.backward()
+    ref = hw.frnn_bwd(*[t.detach() for t in leaves], st.detach(), ct["dstates"].to(dev), ct["dlast"].to(dev), cell="lstm")
+    for leaf, r in zip(leaves, ref):
+        torch.testing.assert_close(leaf.grad, r, rtol=1e-5, atol=1e-5)
