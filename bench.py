@@ -96,8 +96,9 @@ def write_traffic(args) -> None:
     print(json.dumps(entry))
 
 
-def cpu_baseline(w, sample_T: int):
-    """The oracle as it stands, on all (batch, head) rows for the first sample_T steps."""
+def cpu_baseline(w, sample_T: int, backward: bool = False):
+    """The oracle as it stands, on all (batch, head) rows for the first sample_T steps (the
+    backward: its back-propagation through those steps, forward replay included)."""
     import numpy as np
 
     import frnn_inputs as fi
@@ -107,14 +108,19 @@ def cpu_baseline(w, sample_T: int):
     Wx = fi.to_f64(x["Wx"])[:, :sample_T]
     args = (Wx, fi.to_f64(x["R"]), fi.to_f64(x["b"]), fi.to_f64(x["states0"]))
     oracle.headwise_fwd(w.cell, Wx[:, :2], *args[1:])  # warm (loads the library)
-    t0 = time.perf_counter()
-    oracle.headwise_fwd(w.cell, *args)
-    dt = time.perf_counter() - t0
     flops = 2.0 * w.B * w.N * w.G * w.D * w.D * sample_T
+    t0 = time.perf_counter()
+    if backward:
+        ct = fi.backward_cotangents(w)
+        oracle.headwise_bwd(w.cell, *args, fi.to_f64(ct["dstates"])[:, :, :sample_T], fi.to_f64(ct["dlast"]))
+        flops = 2.0 * flops + 2.0 * (w.D + 1) * w.G * w.D * w.B * sample_T * w.N
+    else:
+        oracle.headwise_fwd(w.cell, *args)
+    dt = time.perf_counter() - t0
     cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
             "sample": f"all {w.B * w.N} (batch, head) rows x first {sample_T} of {w.T} timesteps, fp64, "
-                      f"{dt:.2f} s wall",
+                      f"{dt:.2f} s wall" + (", backward" if backward else ""),
             "us_per_timestep": dt / sample_T * 1e6}
 
 
@@ -124,7 +130,11 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="lstm_bf16_B16_T1024_N1_D768")
-    ap.add_argument("--path", default="fused", choices=["fused", "alternating"])
+    ap.add_argument("--path", default=None, choices=["fused", "alternating"],
+                    help="default: fused (forward), alternating (--backward)")
+    ap.add_argument("--backward", action="store_true",
+                    help="time frnn_bwd (back-propagation through time) instead of the forward: the "
+                         "forward states are computed once before the timed region")
     ap.add_argument("--cpu-sample-T", type=int, default=0, help="timesteps of the CPU-baseline sample (0 = all)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (read MIB, write MIB), five times, for "
@@ -137,6 +147,8 @@ def main():
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="per-launch HBM bytes measured with rocprofv3 counters for this workload/path")
     args = ap.parse_args()
+    if args.path is None:
+        args.path = "alternating" if args.backward else "fused"
     if args.write_traffic:
         write_traffic(args)
         return
@@ -186,12 +198,23 @@ def main():
             hw.frnn_fwd(g["Wx"], g["R"], g["b"], g["states0"], cell=w.cell, path=args.path, out=out, workspace=ws,
                         check=False)
         flops = headwise_flops(w)
+        if args.backward:
+            fwd_st, _ = hw.frnn_fwd(g["Wx"], g["R"], g["b"], g["states0"], cell=w.cell, path="fused")
+            ct = {k: v.to(dev) for k, v in fi.backward_cotangents(w).items()}
+            ws = torch.empty(hw.frnn_bwd_workspace_bytes(desc, args.path), dtype=torch.uint8, device=dev)
+            plan = hw.frnn_bwd_plan_str(desc, args.path)
+
+            def step():
+                hw.frnn_bwd(g["Wx"], g["R"], g["b"], g["states0"], fwd_st, ct["dstates"], ct["dlast"], cell=w.cell,
+                            path=args.path, workspace=ws, check=False)
+            # the serial contraction (da . R^T per step), the h.R recompute and the dR GEMM
+            flops = 2.0 * headwise_flops(w) + 2.0 * (w.D + 1) * w.G * w.D * w.B * w.T * w.N
         elt = 2 if w.dtype == torch.bfloat16 else 4
         nbytes = headwise_bytes(w, elt)
         timesteps = w.T
         config = {"workload": w.name, "cell": w.cell, "B": w.B, "T": w.T, "N": w.N, "D": w.D, "G": G,
                   "in_dtype": str(w.dtype).replace("torch.", ""), "states_dtype": "float32", "path": args.path,
-                  "plan": plan}
+                  "plan": plan, "pass": "backward" if args.backward else "forward"}
         dtype = "bf16" if w.dtype == torch.bfloat16 else "f32"
     else:
         ws = torch.empty(hw.frnn_lstm_stack_workspace_bytes(w.L, w.T, w.B, w.I, w.H, args.path), dtype=torch.uint8,
@@ -228,9 +251,10 @@ def main():
     tflops = flops / sec / 1e12
     roof = {"bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": tflops / PEAK_BF16_TFLOPS, "traffic": None,
-            "kernel": "frnn::fused_fwd_kernel" if args.path == "fused" else "frnn::alt_gemm_kernel+alt_gate_kernel",
+            "kernel": ("frnn::bwd_gate_kernel+bwd_dh_kernel (+ GEMMs)" if args.backward else
+                       "frnn::fused_fwd_kernel" if args.path == "fused" else "frnn::alt_gemm_kernel+alt_gate_kernel"),
             "per_launch_flop": flops, "launch_ms": ms}
-    if nbytes:
+    if nbytes and not args.backward:
         roof["algorithmic_bytes"] = nbytes
         roof["hbm_frac"] = nbytes / sec / 1e9 / PEAK_HBM_GBS
     # HBM bytes per launch counted by rocprofv3 (FETCH_SIZE + WRITE_SIZE, calibrated on a plain
@@ -243,14 +267,19 @@ def main():
             roof["traffic_over_algorithmic"] = tj["bytes_per_launch"] / tj["algorithmic_bytes"]
     except (OSError, ValueError, KeyError):
         pass
-    metric = METRIC if w.name == fi.HEADLINE else f"{w.name} fwd achieved TFLOP/s of the recurrent contraction"
+    if args.backward:
+        metric = f"{w.name} backward achieved TFLOP/s (serial contraction, h.R recompute and dR GEMM)"
+    elif w.name == fi.HEADLINE:
+        metric = METRIC
+    else:
+        metric = f"{w.name} fwd achieved TFLOP/s of the recurrent contraction"
     res = {"metric": metric, "value": tflops, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "dtype": dtype, "data": "synthetic (seeded, shapes and distributions of the workload)",
            "config": config, "us_per_timestep": ms * 1e3 / timesteps,
            "pct_mfma_bf16_peak": 100.0 * tflops / PEAK_BF16_TFLOPS, "wall_s_timed": wall, "roofline": roof}
     if not args.no_cpu_baseline and isinstance(w, fi.HeadwiseWorkload):
-        res["cpu_baseline"] = cpu_baseline(w, min(args.cpu_sample_T or w.T, w.T))
+        res["cpu_baseline"] = cpu_baseline(w, min(args.cpu_sample_T or w.T, w.T), backward=args.backward)
     print(json.dumps(res), flush=True)
 
 

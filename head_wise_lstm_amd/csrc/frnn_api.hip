@@ -433,7 +433,7 @@ int run_recurrence(const Problem& p, int path, int* err, void* scratch, hipStrea
 // ----------------------------------------------------------------------------- backward
 // Workspace of frnn_bwd after the error word (grows with T: it holds every step's h.R and da).
 struct BwdLayout {
-  size_t hprev, hprevT, rt, hr, da, daT, tmp, dhrec, carry, total;
+  size_t zeros, hprev, hprevT, rt, rpk, hr, da, daT, tmp, dhpart, carry, total;
 };
 
 BwdLayout bwd_layout(int B, int T, int N, int D, int cell, int f32) {
@@ -441,14 +441,16 @@ BwdLayout bwd_layout(int B, int T, int N, int D, int cell, int f32) {
   const size_t Kp = ((size_t)T * B + 31) / 32 * 32;
   BwdLayout L;
   size_t q = 0;
+  L.zeros = q;  q += 256;
   L.hprev = q;  q += align256((size_t)N * Kp * D * elt);
   L.hprevT = q; q += align256((size_t)N * (D + 1) * Kp * elt);
   L.rt = q;     q += align256((size_t)N * G * D * D * elt);
+  L.rpk = q;    q += align256((size_t)N * G * D * D * elt);
   L.hr = q;     q += align256((size_t)N * T * B * G * D * 4);
   L.da = q;     q += align256((size_t)N * Kp * G * D * elt);
   L.daT = q;    q += align256((size_t)N * G * D * Kp * elt);
   L.tmp = q;    q += align256((size_t)N * (D + 1) * G * D * 4);
-  L.dhrec = q;  q += align256((size_t)B * N * D * 4);
+  L.dhpart = q; q += align256((size_t)BWD_KS * B * N * D * 4);
   L.carry = q;  q += align256((size_t)B * N * D * 4);
   L.total = q;
   return L;
@@ -622,6 +624,7 @@ int frnn_bwd(const frnn_desc* d, int path, const void* Wx, const void* R, const 
   int rc = validate_desc(d, path);
   if (rc != FRNN_OK) return rc;
   if (path != FRNN_PATH_ALTERNATING) return FRNN_EUNSUPPORTED;
+  if ((long long)((d->B + 15) / 16) * d->N > 65535) return FRNN_EUNSUPPORTED;  // dh kernel grid
   if (d->T > 0 && (!Wx || !R || !states)) return FRNN_EINVAL;
   for (const void* p : {Wx, R, b, states0, states, dstates, dlast, (const void*)dWx, (const void*)dR, (const void*)db,
                         (const void*)dstates0, (const void*)workspace})
@@ -677,7 +680,10 @@ int frnn_bwd(const frnn_desc* d, int path, const void* Wx, const void* R, const 
   a.hprev = base + L.hprev;
   a.hr = reinterpret_cast<const float*>(base + L.hr);
   a.da = base + L.da;
-  a.dhrec = reinterpret_cast<float*>(base + L.dhrec);
+  a.zeros = reinterpret_cast<const float*>(base + L.zeros);
+  a.rpk = base + L.rpk;
+  a.dhpart = reinterpret_cast<float*>(base + L.dhpart);
+  a.ks = std::min(BWD_KS, G * D / (f32 ? 4 : 32));
   a.carry = reinterpret_cast<float*>(base + L.carry);
   char* hT = base + L.hprevT;
   char* rt = base + L.rt;
@@ -685,7 +691,8 @@ int frnn_bwd(const frnn_desc* d, int path, const void* Wx, const void* R, const 
   float* tmp = reinterpret_cast<float*>(base + L.tmp);
   float* hr = reinterpret_cast<float*>(base + L.hr);
   // carried gradients start at zero; da's rows past T*B stay zero for the dR GEMM
-  if (launch_fill(a.dhrec, (size_t)BND * 4, st) != hipSuccess || launch_fill(a.carry, (size_t)BND * 4, st) != hipSuccess ||
+  if (launch_fill(base + L.zeros, 256, st) != hipSuccess ||
+      launch_fill(a.dhpart, (size_t)BWD_KS * BND * 4, st) != hipSuccess || launch_fill(a.carry, (size_t)BND * 4, st) != hipSuccess ||
       launch_fill(a.da, (size_t)N * Kp * G * D * elt, st) != hipSuccess)
     return FRNN_EHIP;
   // 1. h_{t-1} for every step, R^T, and h.R for every step
@@ -701,10 +708,24 @@ int frnn_bwd(const frnn_desc* d, int path, const void* Wx, const void* R, const 
                     hr + (size_t)n * T * B * G * D, (long long)G * D, st) != hipSuccess)
       return FRNN_EHIP;
   }
-  // 2. the serial part
+  // 2. the serial part (R packed once as the dh kernel's A fragments)
+  {
+    const long long np = (long long)N * (D / 16) * (G * D / (f32 ? 4 : 32)) * 64;
+    hipLaunchKernelGGL(bwd_rpack_kernel, dim3((unsigned)std::min<long long>((np + 255) / 256, 65536)), dim3(256), 0, st, a,
+                       (void*)(base + L.rpk));
+  }
+  const dim3 hgrid(D / 16, a.ks, ((B + 15) / 16) * N);
   for (int t = T - 1; t >= 0; --t) {
-    hipLaunchKernelGGL(bwd_gate_kernel, dim3(sgrid), dim3(256), 0, st, a, t);
-    const dim3 hgrid(D / 16, (B + 15) / 16, N);
+    const dim3 g64((unsigned)((BND + 63) / 64)), b64(64);
+    if (f32) {
+      if (d->cell == FRNN_CELL_LSTM) hipLaunchKernelGGL((bwd_gate_kernel<CELL_LSTM, true>), g64, b64, 0, st, a, t);
+      else if (d->cell == FRNN_CELL_GRU) hipLaunchKernelGGL((bwd_gate_kernel<CELL_GRU, true>), g64, b64, 0, st, a, t);
+      else hipLaunchKernelGGL((bwd_gate_kernel<CELL_ELMAN, true>), g64, b64, 0, st, a, t);
+    } else {
+      if (d->cell == FRNN_CELL_LSTM) hipLaunchKernelGGL((bwd_gate_kernel<CELL_LSTM, false>), g64, b64, 0, st, a, t);
+      else if (d->cell == FRNN_CELL_GRU) hipLaunchKernelGGL((bwd_gate_kernel<CELL_GRU, false>), g64, b64, 0, st, a, t);
+      else hipLaunchKernelGGL((bwd_gate_kernel<CELL_ELMAN, false>), g64, b64, 0, st, a, t);
+    }
     if (f32) hipLaunchKernelGGL(bwd_dh_kernel<true>, hgrid, dim3(256), 0, st, a, t);
     else hipLaunchKernelGGL(bwd_dh_kernel<false>, hgrid, dim3(256), 0, st, a, t);
   }

@@ -8,12 +8,15 @@
 //      N = G*D), not by a serial loop;
 //   2. the serial part, t = T-1 .. 0: a pointwise kernel turns the step's incoming gradient into
 //      dWx and da (the gradient of the step's h.R part), then an MFMA kernel forms the gradient
-//      that reaches h_{t-1}, dh = sum_g da_g . R_g^T;
+//      that reaches h_{t-1}, dh = sum_g da_g . R_g^T, in BWD_KS parts over K that the next
+//      pointwise kernel adds;
 //   3. dR = sum over (t, b) of h_{t-1}^T da, one GEMM per head over K = T*B, with db from a row of
 //      ones appended to h^T.
 // Operands of the contractions are bf16 (fp32 for fp32 inputs) with fp32 accumulation, like the
 // forward; every carried gradient and every output is fp32.
 #pragma once
+
+#include <type_traits>
 
 #include "frnn_device.hpp"
 
@@ -45,9 +48,14 @@ struct BwdArgs {
   void* hprev;        // [N][Kp][D] operand: row t*B + b = h_{t-1} of batch row b
   const float* hr;    // [N][T*B][G*D]: h_{t-1} . R recomputed
   void* da;           // [N][Kp][G*D] operand: gradient of the h.R part of step t
-  float* dhrec;       // [B][N][D]: gradient reaching h through R from the step after
+  const void* rpk;    // R packed as the dh kernel's A fragments (bwd_rpack_kernel)
+  float* dhpart;      // [BWD_KS][B][N][D]: K-split parts of the gradient reaching h through R
+  int ks;             // parts in use (<= BWD_KS)
   float* carry;       // [B][N][D]: LSTM dc, GRU direct dh carried to the step before
+  const float* zeros; // 256 zero bytes: absent inputs read element 0 of it, so no load is conditional
 };
+
+constexpr int BWD_KS = 4;  // K split of the dh kernel
 
 __device__ __forceinline__ void st_op(void* p, long long i, float v, bool f32) {
   if (f32) reinterpret_cast<float*>(p)[i] = v;
@@ -77,42 +85,64 @@ __global__ void __launch_bounds__(256) bwd_hprev_kernel(BwdArgs a) {
 // Step t of the serial part: one thread per (b, n, unit), consecutive threads on consecutive
 // units. Reads the recomputed h.R, Wx, bias and the forward states of the step, adds the
 // incoming gradients, and writes dWx, da (operand type, for the dh kernel and dR) and the carry.
-__global__ void __launch_bounds__(256) bwd_gate_kernel(BwdArgs a, int t) {
+template <int CELL, bool F32>
+__global__ void __launch_bounds__(64) bwd_gate_kernel(BwdArgs a, int t) {
+  constexpr int G = cell_gates(CELL);
+  typedef typename std::conditional<F32, float, uint16_t>::type op_t;
   const long long total = (long long)a.B * a.N * a.D;
-  const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
+  const long long idx = (long long)blockIdx.x * 64 + threadIdx.x;
   if (idx >= total) return;
   const int u = (int)(idx % a.D);
   const long long r = idx / a.D;
   const int n = (int)(r % a.N);
   const int b = (int)(r / a.N);
-  const int N = a.N, D = a.D, G = cell_gates(a.cell);
-  const bool f32 = a.f32;
+  const int N = a.N, D = a.D;
   const long long tb = (long long)t * a.B + b;
   const float* hr = a.hr + ((long long)n * a.T * a.B + tb) * G * D + u;
   const long long wbase = (long long)b * a.wx_sb + (long long)t * a.wx_st + (long long)n * D + u;
   const long long sidx = (long long)b * a.st_sb + (long long)t * a.st_st + (long long)n * D + u;
   const long long lidx = (long long)b * a.last_sb + (long long)n * D + u;
-  float pre[4] = {0.f, 0.f, 0.f, 0.f}, wx[4] = {0.f, 0.f, 0.f, 0.f}, bb[4] = {0.f, 0.f, 0.f, 0.f};
+  const long long s0idx = (long long)b * a.s0_sb + (long long)n * D + u;
+  // every input is read unconditionally: an absent one (or one this step does not use) is read
+  // at element 0 of the zero page instead
+  const op_t* zop = reinterpret_cast<const op_t*>(a.zeros);
+  const op_t* wxp = reinterpret_cast<const op_t*>(a.Wx);
+  const bool hb = a.bias != nullptr, hds = a.ds_h != nullptr, hdl = a.dl_h != nullptr && t == a.T - 1;
+  const op_t* bp = hb ? reinterpret_cast<const op_t*>(a.bias) : zop;
+  const float* dsh = hds ? a.ds_h : a.zeros;
+  const float* dlh = hdl ? a.dl_h : a.zeros;
+  auto f = [](op_t v) -> float {
+    if constexpr (F32) return v;
+    else return bf2f(v);
+  };
+  float pre[G], wx[G], bb[G], dp[BWD_KS];
+#pragma unroll
   for (int g = 0; g < G; ++g) {
     pre[g] = hr[(long long)g * D];
-    wx[g] = ld_f(a.Wx, wbase + (long long)g * N * D, f32);
-    bb[g] = a.bias ? ld_f(a.bias, (long long)(g * N + n) * D + u, f32) : 0.0f;
+    wx[g] = f(wxp[wbase + (long long)g * N * D]);
+    bb[g] = f(bp[hb ? (long long)(g * N + n) * D + u : 0]);
   }
-  float dh = a.dhrec[idx];
-  if (a.ds_h) dh += a.ds_h[sidx];
-  if (t == a.T - 1 && a.dl_h) dh += a.dl_h[lidx];
-  float dw[4] = {0.f, 0.f, 0.f, 0.f}, dav[4];
-  if (a.cell == CELL_LSTM) {
+  const long long BND = (long long)a.B * N * D;
+#pragma unroll
+  for (int k = 0; k < BWD_KS; ++k) dp[k] = a.dhpart[(k < a.ks ? k * BND : 0) + idx];
+  float dh = dsh[hds ? sidx : 0] + dlh[hdl ? lidx : 0];
+#pragma unroll
+  for (int k = 0; k < BWD_KS; ++k) dh += k < a.ks ? dp[k] : 0.0f;
+  float dw[G], dav[G];
+  if constexpr (CELL == CELL_LSTM) {
+    const bool hdc = a.ds_c != nullptr, hlc = a.dl_c != nullptr && t == a.T - 1, hs0 = a.s0_c != nullptr;
+    const float* dsc = hdc ? a.ds_c : a.zeros;
+    const float* dlc = hlc ? a.dl_c : a.zeros;
+    const op_t* s0c = hs0 ? reinterpret_cast<const op_t*>(a.s0_c) : zop;
+    const float ct = a.st_c[sidx];
+    const float cprev = a.st_c[t > 0 ? sidx - a.st_st : sidx];
+    const float c0 = f(s0c[hs0 ? s0idx : 0]);
+    const float cp = t > 0 ? cprev : c0;
+    const float dc = a.carry[idx] + dsc[hdc ? sidx : 0] + dlc[hlc ? lidx : 0];
     const float ig = sigmoid_f(pre[0] + wx[0] + bb[0]);
     const float fg = sigmoid_f(pre[1] + wx[1] + bb[1]);
     const float zg = tanh_f(pre[2] + wx[2] + bb[2]);
     const float og = sigmoid_f(pre[3] + wx[3] + bb[3]);
-    const float ct = a.st_c[sidx];
-    const float cp = t > 0 ? a.st_c[sidx - a.st_st]
-                           : (a.s0_c ? ld_f(a.s0_c, (long long)b * a.s0_sb + (long long)n * D + u, f32) : 0.0f);
-    float dc = a.carry[idx];
-    if (a.ds_c) dc += a.ds_c[sidx];
-    if (t == a.T - 1 && a.dl_c) dc += a.dl_c[lidx];
     const float tc = tanh_f(ct);
     const float dct = dc + dh * og * (1.0f - tc * tc);
     dw[0] = dct * zg * ig * (1.0f - ig);
@@ -120,15 +150,19 @@ __global__ void __launch_bounds__(256) bwd_gate_kernel(BwdArgs a, int t) {
     dw[2] = dct * ig * (1.0f - zg * zg);
     dw[3] = dh * tc * og * (1.0f - og);
     a.carry[idx] = dct * fg;
+#pragma unroll
     for (int g = 0; g < 4; ++g) dav[g] = dw[g];
-  } else if (a.cell == CELL_GRU) {
+  } else if constexpr (CELL == CELL_GRU) {
+    const bool hs0 = a.s0_h != nullptr;
+    const op_t* s0h = hs0 ? reinterpret_cast<const op_t*>(a.s0_h) : zop;
+    const float hprev = a.st_h[t > 0 ? sidx - a.st_st : sidx];
+    const float h0 = f(s0h[hs0 ? s0idx : 0]);
+    const float hp = t > 0 ? hprev : h0;
     dh += a.carry[idx];
     const float rg = sigmoid_f(pre[0] + wx[0] + bb[0]);
     const float zg = sigmoid_f(pre[1] + wx[1] + bb[1]);
     const float q = pre[2] + bb[2];
     const float ng = tanh_f(wx[2] + rg * q);
-    const float hp = t > 0 ? a.st_h[sidx - a.st_st]
-                           : (a.s0_h ? ld_f(a.s0_h, (long long)b * a.s0_sb + (long long)n * D + u, f32) : 0.0f);
     const float dq = dh * (1.0f - zg) * (1.0f - ng * ng);
     dw[0] = dq * q * rg * (1.0f - rg);
     dw[1] = dh * (hp - ng) * zg * (1.0f - zg);
@@ -142,54 +176,102 @@ __global__ void __launch_bounds__(256) bwd_gate_kernel(BwdArgs a, int t) {
     dw[0] = dh * (1.0f - ht * ht);
     dav[0] = dw[0];
   }
-  if (a.dWx)
+  if (a.dWx) {
+#pragma unroll
     for (int g = 0; g < G; ++g) a.dWx[wbase + (long long)g * N * D] = dw[g];
+  }
   const long long drow = ((long long)n * a.Kp + tb) * G * D + u;
-  for (int g = 0; g < G; ++g) st_op(a.da, drow + (long long)g * D, dav[g], f32);
+#pragma unroll
+  for (int g = 0; g < G; ++g) st_op(a.da, drow + (long long)g * D, dav[g], F32);
 }
 
-// dh of step t-1: dhrec[b][n][d] = sum_g sum_e da[n][t*B + b][g*D + e] * R[g][n][d][e].
-// MFMA with A = R rows (16 values of d; k = (g, e), 32 at a time within one gate: 16 contiguous
-// bytes of a row of R per lane) and B = da^T (batch in the 16 columns). Grid (D/16, ceil(B/16),
-// N); the 4 waves take k-tiles 4 apart and meet in LDS.
+// R in the dh kernel's A-fragment order: [N][D/16 row tiles][G*D/KW k-tiles][64 lanes] x (8 bf16
+// | 1 fp32); lane (m, quad) of tile (dt, kt) holds R[g][n][16 dt + m][e0 + 8 quad ..] (bf16) or
+// [e0 + quad] (fp32), with (g, e0) the k-tile's gate and first unit. One thread per lane entry.
+__global__ void __launch_bounds__(256) bwd_rpack_kernel(BwdArgs a, void* out) {
+  const int G = cell_gates(a.cell), D = a.D;
+  const int KW = a.f32 ? 4 : 32;
+  const int KT = G * D / KW, DT = D / 16;
+  const long long total = (long long)a.N * DT * KT * 64;
+  for (long long idx = (long long)blockIdx.x * 256 + threadIdx.x; idx < total; idx += (long long)gridDim.x * 256) {
+    const int lane = (int)(idx & 63);
+    long long r = idx >> 6;
+    const int kt = (int)(r % KT);
+    r /= KT;
+    const int dt = (int)(r % DT);
+    const int n = (int)(r / DT);
+    const int m = lane & 15, quad = lane >> 4;
+    const int g = kt * KW / D, e0 = kt * KW % D;
+    const long long row = (long long)g * a.r_sg + (long long)n * a.r_sn + (long long)(dt * 16 + m) * a.r_sd + e0;
+    if (a.f32) {
+      reinterpret_cast<float*>(out)[idx] = reinterpret_cast<const float*>(a.R)[row + quad];
+    } else {
+      reinterpret_cast<u32x4_t*>(out)[idx] =
+          *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const uint16_t*>(a.R) + row + 8 * quad);
+    }
+  }
+}
+
+// dh of step t-1, part ks of the K split: dhpart[ks][b][n][d] = sum over k-tiles kt of this part
+// of sum_e da[n][t*B + b][k] * R[g][n][d][e] (k = (g, e)). MFMA with A = packed R (16 values of
+// d, 1 KiB per wave-load) and B = da^T (batch in the 16 columns). Grid (D/16, ks, ceil(B/16)*N);
+// the 4 waves take the part's k-tiles 4 apart and meet in LDS.
 template <bool F32>
 __global__ void __launch_bounds__(256) bwd_dh_kernel(BwdArgs a, int t) {
   __shared__ f32x4_t part[4][64];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int col = lane & 15, quad = lane >> 4;
   const int G = cell_gates(a.cell), D = a.D;
-  const int d0 = blockIdx.x * 16, b0 = blockIdx.y * 16, n = blockIdx.z;
+  const int dt = blockIdx.x, ks = blockIdx.y;
+  const int nbb = (a.B + 15) / 16;
+  const int n = blockIdx.z / nbb, b0 = (blockIdx.z % nbb) * 16;
   const int KW = F32 ? 4 : 32;
   const int KT = G * D / KW;
+  const int k_lo = (int)((long long)KT * ks / a.ks), k_hi = (int)((long long)KT * (ks + 1) / a.ks);
   const bool colv = b0 + col < a.B;
   const long long drow = ((long long)n * a.Kp + (long long)t * a.B + b0 + col) * G * D;
+  const long long rbase = (((long long)n * (D / 16) + dt) * KT) * 64 + lane;
   f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-  for (int kt = wave; kt < KT; kt += 8) {
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int k = kt + 4 * h;
-      if (k >= KT) break;
-      const int g = (k * KW) / D, e0 = (k * KW) % D;
-      const long long rrow = (long long)g * a.r_sg + (long long)n * a.r_sn + (long long)(d0 + col) * a.r_sd + e0;
-      if constexpr (F32) {
-        const float av = reinterpret_cast<const float*>(a.R)[rrow + quad];
-        const float bv = colv ? reinterpret_cast<const float*>(a.da)[drow + k * KW + quad] : 0.0f;
-        if (h == 0) acc0 = mfma_f32(av, bv, acc0);
-        else acc1 = mfma_f32(av, bv, acc1);
-      } else {
-        const u32x4_t av = *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const uint16_t*>(a.R) + rrow + 8 * quad);
-        u32x4_t bv = {0u, 0u, 0u, 0u};
-        if (colv) bv = *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const uint16_t*>(a.da) + drow + k * KW + 8 * quad);
-        if (h == 0) acc0 = mfma_bf16(__builtin_bit_cast(bf16x8_t, av), __builtin_bit_cast(bf16x8_t, bv), acc0);
-        else acc1 = mfma_bf16(__builtin_bit_cast(bf16x8_t, av), __builtin_bit_cast(bf16x8_t, bv), acc1);
+  int k = k_lo + wave;
+  for (; k + 4 < k_hi; k += 8) {
+    if constexpr (F32) {
+      const float* rp = reinterpret_cast<const float*>(a.rpk) + rbase;
+      const float* dp = reinterpret_cast<const float*>(a.da) + drow + quad;
+      const float a0 = rp[(long long)k * 64], a1 = rp[(long long)(k + 4) * 64];
+      const float h0 = colv ? dp[k * KW] : 0.0f, h1 = colv ? dp[(k + 4) * KW] : 0.0f;
+      acc0 = mfma_f32(a0, h0, acc0);
+      acc1 = mfma_f32(a1, h1, acc1);
+    } else {
+      const u32x4_t* rp = reinterpret_cast<const u32x4_t*>(a.rpk) + rbase;
+      const uint16_t* dp = reinterpret_cast<const uint16_t*>(a.da) + drow + 8 * quad;
+      const u32x4_t a0 = rp[(long long)k * 64], a1 = rp[(long long)(k + 4) * 64];
+      u32x4_t h0 = {0u, 0u, 0u, 0u}, h1 = {0u, 0u, 0u, 0u};
+      if (colv) {
+        h0 = *reinterpret_cast<const u32x4_t*>(dp + k * KW);
+        h1 = *reinterpret_cast<const u32x4_t*>(dp + (k + 4) * KW);
       }
+      acc0 = mfma_bf16(__builtin_bit_cast(bf16x8_t, a0), __builtin_bit_cast(bf16x8_t, h0), acc0);
+      acc1 = mfma_bf16(__builtin_bit_cast(bf16x8_t, a1), __builtin_bit_cast(bf16x8_t, h1), acc1);
+    }
+  }
+  if (k < k_hi) {
+    if constexpr (F32) {
+      const float a0 = reinterpret_cast<const float*>(a.rpk)[rbase + (long long)k * 64];
+      const float h0 = colv ? reinterpret_cast<const float*>(a.da)[drow + k * KW + quad] : 0.0f;
+      acc0 = mfma_f32(a0, h0, acc0);
+    } else {
+      const u32x4_t a0 = reinterpret_cast<const u32x4_t*>(a.rpk)[rbase + (long long)k * 64];
+      u32x4_t h0 = {0u, 0u, 0u, 0u};
+      if (colv) h0 = *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const uint16_t*>(a.da) + drow + k * KW + 8 * quad);
+      acc0 = mfma_bf16(__builtin_bit_cast(bf16x8_t, a0), __builtin_bit_cast(bf16x8_t, h0), acc0);
     }
   }
   part[wave][lane] = acc0 + acc1;
   __syncthreads();
   if (wave != 0 || !colv) return;
   const f32x4_t s = (part[0][lane] + part[1][lane]) + (part[2][lane] + part[3][lane]);
-  *reinterpret_cast<f32x4_t*>(a.dhrec + ((long long)(b0 + col) * a.N + n) * D + d0 + 4 * quad) = s;
+  const long long BND = (long long)a.B * a.N * D;
+  *reinterpret_cast<f32x4_t*>(a.dhpart + ks * BND + ((long long)(b0 + col) * a.N + n) * D + dt * 16 + 4 * quad) = s;
 }
 
 // dstates0 from what reaches the initial state: h through R (plus the GRU's direct part), and
@@ -198,7 +280,10 @@ __global__ void __launch_bounds__(256) bwd_final_kernel(BwdArgs a) {
   const long long total = (long long)a.B * a.N * a.D;
   const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
   if (idx >= total) return;
-  if (a.ds0_h) a.ds0_h[idx] = a.dhrec[idx] + (a.cell == CELL_GRU ? a.carry[idx] : 0.0f);
+  const long long BND = (long long)a.B * a.N * a.D;
+  float dh = a.cell == CELL_GRU ? a.carry[idx] : 0.0f;
+  for (int k = 0; k < a.ks; ++k) dh += a.dhpart[k * BND + idx];
+  if (a.ds0_h) a.ds0_h[idx] = dh;
   if (a.ds0_c && a.cell == CELL_LSTM) a.ds0_c[idx] = a.carry[idx];
 }
 
