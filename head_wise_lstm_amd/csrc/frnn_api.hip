@@ -113,6 +113,17 @@ const FusedVariant* find_fused(int cell, int f32, int local, int ncw, int ks, in
   return nullptr;
 }
 
+const FusedBwdVariant* find_fused_bwd(int cell, int ncw, int ks, int mtw, int ktw) {
+  const FusedBwdTable t = cell == FRNN_CELL_LSTM ? fused_bwd_table_lstm()
+                          : cell == FRNN_CELL_GRU ? fused_bwd_table_gru()
+                                                  : fused_bwd_table_elman();
+  for (int i = 0; i < t.n; ++i) {
+    const FusedBwdVariant& v = t.v[i];
+    if (v.cell == cell && v.ncw == ncw && v.ks == ks && v.mtw == mtw && v.ktw == ktw) return &v;
+  }
+  return nullptr;
+}
+
 // ----------------------------------------------------------------------------- problem
 struct Problem {
   int B, T, N, D, cell;
@@ -433,10 +444,56 @@ int run_recurrence(const Problem& p, int path, int* err, void* scratch, hipStrea
 // ----------------------------------------------------------------------------- backward
 // Workspace of frnn_bwd after the error word (grows with T: it holds every step's h.R and da).
 struct BwdLayout {
-  size_t zeros, hprev, hprevT, rt, rpk, hr, da, daT, tmp, dhpart, carry, total;
+  size_t zeros, hprev, hprevT, rt, rpk, hr, da, daT, tmp, dhpart, carry, rec, dstate, xbuf, total;
 };
 
-BwdLayout bwd_layout(int B, int T, int N, int D, int cell, int f32) {
+// Fused backward design: groups of BR batch rows of one head on one die, W workgroups each owning
+// MT_WG 16-unit tiles of R's rows, (compute waves, K split) over K = G*D.
+struct FusedBwdPlan {
+  const FusedBwdVariant* v = nullptr;
+  int W = 0, BR = 0, groups = 0, ncw = 0, ks = 0, mtw = 0, ktw = 0, n_xcd = 1, slots = 0, grid = 0, U = 0;
+  size_t lds = 0;
+};
+
+int plan_fused_bwd(int B, int N, int D, int cell, int f32, const DevInfo& di, FusedBwdPlan* out) {
+  if (f32 || !di.periodic || D % 32 != 0) return FRNN_EUNSUPPORTED;
+  const int G = gates_of(cell);
+  const int TPH = D / 16, KT = G * D / 32;
+  const int slots_per_die = std::max(1, di.cus / di.n_xcd);
+  const int force_w = env_int("FRNN_FUSED_BWD_W", 0), force_br = env_int("FRNN_FUSED_BWD_BR", 0);
+  const int force_ncw = env_int("FRNN_FUSED_BWD_NCW", 0);
+  const int cand[][2] = {{8, 8}, {6, 6}, {4, 4}, {4, 2}};
+  for (int BR = 1; BR <= FUSED_DIE_MAX_BR; ++BR) {
+    if (force_br && BR != force_br) continue;
+    const int groups = N * ((B + BR - 1) / BR);
+    const int per_die = (groups + di.n_xcd - 1) / di.n_xcd;
+    for (int W = std::min(32, slots_per_die); W >= 2; --W) {
+      if (force_w && W != force_w) continue;
+      if (TPH % W || per_die * W > slots_per_die) continue;
+      const int mt_wg = TPH / W, U = mt_wg * 16;
+      // the I/O wave moves at most 64 * BWD_EPL_IN record words and 64 * BWD_EPL_OUT output words
+      if (BR * U * BWD_REC / 2 > 64 * BWD_EPL_IN || BR * U > 64 * BWD_EPL_OUT) continue;
+      for (const auto& nk : cand) {
+        const int ncw = nk[0], ks = nk[1];
+        if (force_ncw && ncw != force_ncw) continue;
+        const int ms = ncw / ks;
+        if (mt_wg % ms || KT % ks) continue;
+        const int mtw = mt_wg / ms, ktw = KT / ks;
+        const FusedBwdVariant* v = find_fused_bwd(cell, ncw, ks, mtw, ktw);
+        if (!v || BR > fused_max_br(ks, mtw)) continue;
+        FusedBwdPlan fp;
+        fp.v = v; fp.W = W; fp.BR = BR; fp.groups = groups; fp.ncw = ncw; fp.ks = ks; fp.mtw = mtw; fp.ktw = ktw;
+        fp.n_xcd = di.n_xcd; fp.slots = per_die * W; fp.grid = fp.slots * di.n_xcd; fp.U = U;
+        fp.lds = (size_t)fused_bwd_lds(ncw, ks, ktw, BR, U).total;
+        *out = fp;
+        return FRNN_OK;
+      }
+    }
+  }
+  return FRNN_EUNSUPPORTED;
+}
+
+BwdLayout bwd_layout(int B, int T, int N, int D, int cell, int f32, int path) {
   const size_t G = gates_of(cell), elt = f32 ? 4 : 2;
   const size_t Kp = ((size_t)T * B + 31) / 32 * 32;
   BwdLayout L;
@@ -452,12 +509,27 @@ BwdLayout bwd_layout(int B, int T, int N, int D, int cell, int f32) {
   L.tmp = q;    q += align256((size_t)N * (D + 1) * G * D * 4);
   L.dhpart = q; q += align256((size_t)BWD_KS * B * N * D * 4);
   L.carry = q;  q += align256((size_t)B * N * D * 4);
+  L.rec = L.dstate = L.xbuf = q;
+  if (path == FRNN_PATH_FUSED) {
+    L.rec = q;    q += align256((size_t)T * B * N * D * BWD_REC * 4);
+    L.dstate = q; q += align256((size_t)T * B * N * D * 2 * 4);
+    // exchange words: groups * BR <= N * (B + 3) rows (BR <= 4), two parities, G*D words a row
+    L.xbuf = q;   q += align256((size_t)2 * N * (B + FUSED_DIE_MAX_BR - 1) * G * D * 4);
+  }
   L.total = q;
   return L;
 }
 
-std::string bwd_plan_string(const frnn_desc* d, int path) {
-  char buf[384];
+std::string bwd_plan_string(const frnn_desc* d, int path, const FusedBwdPlan* fp = nullptr) {
+  char buf[512];
+  if (path == FRNN_PATH_FUSED && fp) {
+    std::snprintf(buf, sizeof(buf),
+                  "backward path=fused design=die-local cell=%s dtype=bf16 B=%d T=%d N=%d D=%d BR=%d groups=%d W=%d "
+                  "NCW=%d KS=%d MTW=%d KTW=%d dies=%d slots/die=%d grid=%d lds=%zu",
+                  cell_name(d->cell), d->B, d->T, d->N, d->D, fp->BR, fp->groups, fp->W, fp->ncw, fp->ks, fp->mtw,
+                  fp->ktw, fp->n_xcd, fp->slots, fp->grid, fp->lds);
+    return std::string(buf);
+  }
   const int G = gates_of(d->cell);
   const long long Kp = ((long long)d->T * d->B + 31) / 32 * 32;
   std::snprintf(buf, sizeof(buf),
@@ -467,6 +539,43 @@ std::string bwd_plan_string(const frnn_desc* d, int path) {
                 d->in_dtype == FRNN_F32 ? "f32" : "bf16", d->B, d->T, d->N, d->D, (long long)d->T * d->B, G * d->D,
                 d->D, d->D + 1, G * d->D, Kp, 2 * d->T);
   return std::string(buf);
+}
+
+// The fused serial part: records of every step, the persistent kernel, then dWx / da / carries.
+int run_fused_bwd(const frnn_desc* d, const BwdArgs& a, const FusedBwdPlan& fp, const DevInfo& di, char* base,
+                  const BwdLayout& L, hipStream_t st) {
+  const long long total = (long long)a.T * a.B * a.N * a.D;
+  const unsigned pgrid = (unsigned)((total + 255) / 256);
+  float* rec = reinterpret_cast<float*>(base + L.rec);
+  float* dstate = reinterpret_cast<float*>(base + L.dstate);
+  if (d->cell == FRNN_CELL_LSTM) hipLaunchKernelGGL((bwd_record_kernel<CELL_LSTM, false>), dim3(pgrid), dim3(256), 0, st, a, rec);
+  else if (d->cell == FRNN_CELL_GRU) hipLaunchKernelGGL((bwd_record_kernel<CELL_GRU, false>), dim3(pgrid), dim3(256), 0, st, a, rec);
+  else hipLaunchKernelGGL((bwd_record_kernel<CELL_ELMAN, false>), dim3(pgrid), dim3(256), 0, st, a, rec);
+  const size_t xbytes = (size_t)fp.groups * 2 * fp.BR * gates_of(d->cell) * a.D * 4;
+  if (launch_fill(base + L.xbuf, xbytes, st, 0xFFFFu) != hipSuccess) return FRNN_EHIP;
+  FusedBwdArgs f;
+  std::memset(&f, 0, sizeof(f));
+  f.B = a.B; f.T = a.T; f.N = a.N; f.D = a.D;
+  f.BR = fp.BR; f.groups = fp.groups; f.W = fp.W; f.n_xcd = fp.n_xcd; f.check_xcc = 1;
+  f.xcc_of = 0;
+  for (int k = 0; k < kMaxDies; ++k) f.xcc_of |= (uint32_t)(di.xcc_of[k] & 0xF) << (4 * k);
+  f.rpk = a.rpk;
+  f.rec = rec;
+  f.dstate = dstate;
+  f.xbuf = reinterpret_cast<uint32_t*>(base + L.xbuf);
+  f.err = reinterpret_cast<int*>(base - kErrBytes);
+  f.timeout_ticks = (long long)env_int("FRNN_TIMEOUT_MS", 2000) * di.wall_khz;
+  const void* fn = reinterpret_cast<const void*>(fp.v->fn);
+  if (fp.lds > 48 * 1024 && hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)fp.lds) != hipSuccess)
+    return FRNN_EHIP;
+  void* args[] = {&f};
+  const hipError_t e = hipLaunchCooperativeKernel(fn, dim3(fp.grid), dim3(fused_threads(fp.ncw)), args, (unsigned)fp.lds, st);
+  if (e == hipErrorCooperativeLaunchTooLarge) return FRNN_ENORESIDENT;
+  if (e != hipSuccess) return FRNN_EHIP;
+  if (d->cell == FRNN_CELL_LSTM) hipLaunchKernelGGL((bwd_post_kernel<CELL_LSTM, false>), dim3(pgrid), dim3(256), 0, st, a, rec, dstate);
+  else if (d->cell == FRNN_CELL_GRU) hipLaunchKernelGGL((bwd_post_kernel<CELL_GRU, false>), dim3(pgrid), dim3(256), 0, st, a, rec, dstate);
+  else hipLaunchKernelGGL((bwd_post_kernel<CELL_ELMAN, false>), dim3(pgrid), dim3(256), 0, st, a, rec, dstate);
+  return hipGetLastError() == hipSuccess ? FRNN_OK : FRNN_EHIP;
 }
 
 bool misaligned(const void* p) { return p && (reinterpret_cast<uintptr_t>(p) & 15u); }
@@ -613,8 +722,8 @@ int frnn_bwd_workspace_bytes(const frnn_desc* d, int path, size_t* bytes) {
   const int rc = validate_desc(d, path);
   if (rc != FRNN_OK) return rc;
   if (!bytes) return FRNN_EINVAL;
-  if (path != FRNN_PATH_ALTERNATING) return FRNN_EUNSUPPORTED;
-  *bytes = kErrBytes + bwd_layout(d->B, d->T, d->N, d->D, d->cell, d->in_dtype == FRNN_F32).total;
+  if (path == FRNN_PATH_FUSED && d->in_dtype == FRNN_F32) return FRNN_EUNSUPPORTED;
+  *bytes = kErrBytes + bwd_layout(d->B, d->T, d->N, d->D, d->cell, d->in_dtype == FRNN_F32, path).total;
   return FRNN_OK;
 }
 
@@ -623,20 +732,25 @@ int frnn_bwd(const frnn_desc* d, int path, const void* Wx, const void* R, const 
              void* dstates0, void* workspace, size_t workspace_bytes, void* stream) {
   int rc = validate_desc(d, path);
   if (rc != FRNN_OK) return rc;
-  if (path != FRNN_PATH_ALTERNATING) return FRNN_EUNSUPPORTED;
+  if (path == FRNN_PATH_FUSED && d->in_dtype == FRNN_F32) return FRNN_EUNSUPPORTED;
   if ((long long)((d->B + 15) / 16) * d->N > 65535) return FRNN_EUNSUPPORTED;  // dh kernel grid
   if (d->T > 0 && (!Wx || !R || !states)) return FRNN_EINVAL;
   for (const void* p : {Wx, R, b, states0, states, dstates, dlast, (const void*)dWx, (const void*)dR, (const void*)db,
                         (const void*)dstates0, (const void*)workspace})
     if (misaligned(p)) return FRNN_EINVAL;
   const int f32 = d->in_dtype == FRNN_F32;
-  const BwdLayout L = bwd_layout(d->B, d->T, d->N, d->D, d->cell, f32);
+  const BwdLayout L = bwd_layout(d->B, d->T, d->N, d->D, d->cell, f32, path);
   if (!workspace || workspace_bytes < kErrBytes + L.total) return FRNN_EWORKSPACE;
   DevInfo di;
   rc = get_devinfo(&di);
   if (rc != FRNN_OK) return rc;
+  FusedBwdPlan fbp;
+  if (path == FRNN_PATH_FUSED) {
+    rc = plan_fused_bwd(d->B, d->N, d->D, d->cell, f32, di, &fbp);
+    if (rc != FRNN_OK) return rc;
+  }
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  trace("[frnn] %s\n", bwd_plan_string(d, path));
+  trace("[frnn] %s\n", bwd_plan_string(d, path, path == FRNN_PATH_FUSED ? &fbp : nullptr));
   const int B = d->B, T = d->T, N = d->N, D = d->D, G = gates_of(d->cell), S = d->cell == FRNN_CELL_LSTM ? 2 : 1;
   const long long BND = (long long)B * N * D;
   const size_t elt = f32 ? 4 : 2;
@@ -708,14 +822,20 @@ int frnn_bwd(const frnn_desc* d, int path, const void* Wx, const void* R, const 
                     hr + (size_t)n * T * B * G * D, (long long)G * D, st) != hipSuccess)
       return FRNN_EHIP;
   }
-  // 2. the serial part (R packed once as the dh kernel's A fragments)
+  // 2. the serial part (R packed once as the dh kernels' A fragments)
   {
     const long long np = (long long)N * (D / 16) * (G * D / (f32 ? 4 : 32)) * 64;
     hipLaunchKernelGGL(bwd_rpack_kernel, dim3((unsigned)std::min<long long>((np + 255) / 256, 65536)), dim3(256), 0, st, a,
                        (void*)(base + L.rpk));
   }
   const dim3 hgrid(D / 16, a.ks, ((B + 15) / 16) * N);
-  for (int t = T - 1; t >= 0; --t) {
+  if (path == FRNN_PATH_FUSED) {
+    rc = run_fused_bwd(d, a, fbp, di, base, L, st);
+    if (rc != FRNN_OK) return rc;
+    // the gradient that reaches the initial state through R: one more contraction, of step 0's da
+    hipLaunchKernelGGL(bwd_dh_kernel<false>, hgrid, dim3(256), 0, st, a, 0);
+  }
+  for (int t = (path == FRNN_PATH_FUSED ? -1 : T - 1); t >= 0; --t) {
     const dim3 g64((unsigned)((BND + 63) / 64)), b64(64);
     if (f32) {
       if (d->cell == FRNN_CELL_LSTM) hipLaunchKernelGGL((bwd_gate_kernel<CELL_LSTM, true>), g64, b64, 0, st, a, t);
@@ -764,8 +884,14 @@ int frnn_bwd_plan_str(const frnn_desc* d, int path, char* buf, size_t cap) {
   const int rc = validate_desc(d, path);
   if (rc != FRNN_OK) return rc;
   if (!buf || cap == 0) return FRNN_EINVAL;
-  if (path != FRNN_PATH_ALTERNATING) return FRNN_EUNSUPPORTED;
-  std::snprintf(buf, cap, "%s", bwd_plan_string(d, path).c_str());
+  FusedBwdPlan fbp;
+  if (path == FRNN_PATH_FUSED) {
+    DevInfo di;
+    if (get_devinfo(&di) != FRNN_OK) di = default_devinfo();
+    const int prc = plan_fused_bwd(d->B, d->N, d->D, d->cell, d->in_dtype == FRNN_F32, di, &fbp);
+    if (prc != FRNN_OK) return prc;
+  }
+  std::snprintf(buf, cap, "%s", bwd_plan_string(d, path, path == FRNN_PATH_FUSED ? &fbp : nullptr).c_str());
   return FRNN_OK;
 }
 

@@ -185,6 +185,143 @@ __global__ void __launch_bounds__(64) bwd_gate_kernel(BwdArgs a, int t) {
   for (int g = 0; g < G; ++g) st_op(a.da, drow + (long long)g * D, dav[g], F32);
 }
 
+// Coefficient records of every step, for the fused serial part (layout: frnn_fused_bwd.hpp): one
+// thread per (t, b, n, unit); record index s = T-1-t. The gradients of the step's outputs (and of
+// last_states at t = T-1) ride along.
+template <int CELL, bool F32>
+__global__ void __launch_bounds__(256) bwd_record_kernel(BwdArgs a, float* rec) {
+  constexpr int G = cell_gates(CELL);
+  typedef typename std::conditional<F32, float, uint16_t>::type op_t;
+  const long long total = (long long)a.T * a.B * a.N * a.D;
+  const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= total) return;
+  const int u = (int)(idx % a.D);
+  long long r = idx / a.D;
+  const int n = (int)(r % a.N);
+  r /= a.N;
+  const int b = (int)(r % a.B);
+  const int t = (int)(r / a.B);
+  const int N = a.N, D = a.D;
+  const long long tb = (long long)t * a.B + b;
+  const float* hr = a.hr + ((long long)n * a.T * a.B + tb) * G * D + u;
+  const long long wbase = (long long)b * a.wx_sb + (long long)t * a.wx_st + (long long)n * D + u;
+  const long long sidx = (long long)b * a.st_sb + (long long)t * a.st_st + (long long)n * D + u;
+  const long long lidx = (long long)b * a.last_sb + (long long)n * D + u;
+  const long long s0idx = (long long)b * a.s0_sb + (long long)n * D + u;
+  const op_t* zop = reinterpret_cast<const op_t*>(a.zeros);
+  const op_t* wxp = reinterpret_cast<const op_t*>(a.Wx);
+  const bool hb = a.bias != nullptr, hds = a.ds_h != nullptr, hdl = a.dl_h != nullptr && t == a.T - 1;
+  const op_t* bp = hb ? reinterpret_cast<const op_t*>(a.bias) : zop;
+  const float* dsh = hds ? a.ds_h : a.zeros;
+  const float* dlh = hdl ? a.dl_h : a.zeros;
+  auto f = [](op_t v) -> float {
+    if constexpr (F32) return v;
+    else return bf2f(v);
+  };
+  float pre[G], wx[G], bb[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    pre[g] = hr[(long long)g * D];
+    wx[g] = f(wxp[wbase + (long long)g * N * D]);
+    bb[g] = f(bp[hb ? (long long)(g * N + n) * D + u : 0]);
+  }
+  const float ds_h = dsh[hds ? sidx : 0] + dlh[hdl ? lidx : 0];
+  f32x4_t r0, r1;
+  if constexpr (CELL == CELL_LSTM) {
+    const bool hdc = a.ds_c != nullptr, hlc = a.dl_c != nullptr && t == a.T - 1, hs0 = a.s0_c != nullptr;
+    const float* dsc = hdc ? a.ds_c : a.zeros;
+    const float* dlc = hlc ? a.dl_c : a.zeros;
+    const op_t* s0c = hs0 ? reinterpret_cast<const op_t*>(a.s0_c) : zop;
+    const float ct = a.st_c[sidx];
+    const float cprev = a.st_c[t > 0 ? sidx - a.st_st : sidx];
+    const float c0 = f(s0c[hs0 ? s0idx : 0]);
+    const float cp = t > 0 ? cprev : c0;
+    const float ds_c = dsc[hdc ? sidx : 0] + dlc[hlc ? lidx : 0];
+    const float ig = sigmoid_f(pre[0] + wx[0] + bb[0]);
+    const float fg = sigmoid_f(pre[1] + wx[1] + bb[1]);
+    const float zg = tanh_f(pre[2] + wx[2] + bb[2]);
+    const float og = sigmoid_f(pre[3] + wx[3] + bb[3]);
+    const float tc = tanh_f(ct);
+    r0 = f32x4_t{og * (1.0f - tc * tc), zg * ig * (1.0f - ig), cp * fg * (1.0f - fg), ig * (1.0f - zg * zg)};
+    r1 = f32x4_t{tc * og * (1.0f - og), fg, ds_h, ds_c};
+  } else if constexpr (CELL == CELL_GRU) {
+    const bool hs0 = a.s0_h != nullptr;
+    const op_t* s0h = hs0 ? reinterpret_cast<const op_t*>(a.s0_h) : zop;
+    const float hprev = a.st_h[t > 0 ? sidx - a.st_st : sidx];
+    const float h0 = f(s0h[hs0 ? s0idx : 0]);
+    const float hp = t > 0 ? hprev : h0;
+    const float rg = sigmoid_f(pre[0] + wx[0] + bb[0]);
+    const float zg = sigmoid_f(pre[1] + wx[1] + bb[1]);
+    const float q = pre[2] + bb[2];
+    const float ng = tanh_f(wx[2] + rg * q);
+    const float c3 = (1.0f - zg) * (1.0f - ng * ng);
+    r0 = f32x4_t{c3 * q * rg * (1.0f - rg), (hp - ng) * zg * (1.0f - zg), c3 * rg, zg};
+    r1 = f32x4_t{ds_h, c3, 0.0f, 0.0f};
+  } else {
+    const float ht = a.st_h[sidx];
+    r0 = f32x4_t{1.0f - ht * ht, ds_h, 0.0f, 0.0f};
+    r1 = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+  const long long s = (long long)(a.T - 1 - t);
+  f32x4_t* out = reinterpret_cast<f32x4_t*>(rec + ((((s * a.B + b) * N + n) * D + u) * 8));
+  out[0] = r0;
+  out[1] = r1;
+}
+
+// dWx, the dR operand da and (at t = 0) the carries from the fused serial part's (dh, dc) and the
+// records: one thread per (t, b, n, unit).
+template <int CELL, bool F32>
+__global__ void __launch_bounds__(256) bwd_post_kernel(BwdArgs a, const float* rec, const float* dstate) {
+  constexpr int G = cell_gates(CELL);
+  const long long total = (long long)a.T * a.B * a.N * a.D;
+  const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= total) return;
+  const int u = (int)(idx % a.D);
+  long long r = idx / a.D;
+  const int n = (int)(r % a.N);
+  r /= a.N;
+  const int b = (int)(r % a.B);
+  const int t = (int)(r / a.B);
+  const int N = a.N, D = a.D;
+  const long long s = (long long)(a.T - 1 - t);
+  const long long ri = ((s * a.B + b) * N + n) * D + u;
+  const f32x4_t r0 = reinterpret_cast<const f32x4_t*>(rec)[ri * 2];
+  const f32x4_t r1 = reinterpret_cast<const f32x4_t*>(rec)[ri * 2 + 1];
+  const float2 st = reinterpret_cast<const float2*>(dstate)[ri];
+  const float dh = st.x, dc = st.y;
+  float dw[G], dav[G];
+  float carry = 0.0f;
+  if constexpr (CELL == CELL_LSTM) {
+    dw[0] = dc * r0[1];
+    dw[1] = dc * r0[2];
+    dw[2] = dc * r0[3];
+    dw[3] = dh * r1[0];
+    carry = dc * r1[1];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) dav[g] = dw[g];
+  } else if constexpr (CELL == CELL_GRU) {
+    dw[0] = dh * r0[0];
+    dw[1] = dh * r0[1];
+    dw[2] = dh * r1[1];
+    dav[0] = dw[0];
+    dav[1] = dw[1];
+    dav[2] = dh * r0[2];
+    carry = dh * r0[3];
+  } else {
+    dw[0] = dh * r0[0];
+    dav[0] = dw[0];
+  }
+  const long long wbase = (long long)b * a.wx_sb + (long long)t * a.wx_st + (long long)n * D + u;
+  if (a.dWx) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) a.dWx[wbase + (long long)g * N * D] = dw[g];
+  }
+  const long long drow = ((long long)n * a.Kp + (long long)t * a.B + b) * G * D + u;
+#pragma unroll
+  for (int g = 0; g < G; ++g) st_op(a.da, drow + (long long)g * D, dav[g], F32);
+  if (t == 0) a.carry[((long long)b * N + n) * D + u] = carry;
+}
+
 // R in the dh kernel's A-fragment order: [N][D/16 row tiles][G*D/KW k-tiles][64 lanes] x (8 bf16
 // | 1 fp32); lane (m, quad) of tile (dt, kt) holds R[g][n][16 dt + m][e0 + 8 quad ..] (bf16) or
 // [e0 + quad] (fp32), with (g, e0) the k-tile's gate and first unit. One thread per lane entry.

@@ -1,0 +1,426 @@
+// Persistent fused backward recurrence (the serial part of back-propagation through time) for
+// gfx950.
+//
+// Once the forward's states are known, every step's gates are known, and the backward of a step
+// is linear in the two gradients it carries (dh, and the LSTM's dc) with per-element coefficients
+// that depend only on the step. Those coefficients are computed for all steps at once beforehand
+// (bwd_record_kernel), so the serial part is a linear recurrence:
+//   LSTM:  dh = dh_R + ds_h;  dc = dc' + ds_c + dh*A1;  da = (dc*A2, dc*A3, dc*A4, dh*A5);  dc' <- dc*A6
+//   GRU:   dh = dh_R + ds_h + dh';  da = (dh*C1, dh*C2, dh*C4);  dh' <- dh*C5
+//   Elman: dh = dh_R + ds_h;  da = dh*E1
+//   dh_R of the step before = sum_g da_g . R_g^T
+// (ds_h, ds_c: the gradients of the step's outputs). Steps run in reverse: step s of the kernel is
+// timestep t = T-1-s.
+//
+// The kernel is the forward's die-local design with the roles of h and R^T exchanged: the W
+// workgroups of a group (one head, BR batch rows, one die) each own 16-unit tiles of R's rows d,
+// resident in VGPRs for all steps, with k = (g, e) over G*D. Lane l of an MFMA result holds
+// dh_R of units 4*(l/16)..+3 of its tile for batch column l%16, applies the step to them, and
+// publishes their da (G words per unit, bf16 << 16 | step tag) through the die's L2; every
+// workgroup polls the da of the whole group (its K range per wave) as the next step's B operand.
+// A fifth kind of wave, the I/O wave, streams the step records into an LDS ring four steps ahead
+// and writes each step's (dh, dc) out of another ring. dWx and the dR operand are formed from
+// (dh, dc) afterwards, for all steps at once (bwd_post_kernel).
+#pragma once
+
+#include "frnn_fused.hpp"
+
+namespace frnn {
+
+// floats per (step, batch row, head, unit) record:
+//   LSTM  [A1 A2 A3 A4 | A5 A6 ds_h ds_c]
+//   GRU   [C1 C2 C4 C5 | ds_h C3 0 0]
+//   Elman [E1 ds_h 0 0 | 0 0 0 0]
+constexpr int BWD_REC = 8;
+constexpr int BWD_EPL_IN = 8;   // 64-bit record words one I/O lane moves per step (at most)
+constexpr int BWD_EPL_OUT = 2;  // 64-bit (dh, dc) words one I/O lane moves per step (at most)
+
+struct FusedBwdArgs {
+  int B, T, N, D;
+  int BR, groups, W, n_xcd, check_xcc;
+  uint32_t xcc_of;
+  const void* rpk;   // R as A fragments: [N][D/16][G*D/32][64] x 8 bf16 (bwd_rpack_kernel)
+  const float* rec;  // [T][B][N][D][BWD_REC], indexed by the kernel step s
+  float* dstate;     // [T][B][N][D][2]: (dh, dc) of kernel step s
+  uint32_t* xbuf;    // [groups][2][BR][G*D] exchange words
+  int* err;
+  long long timeout_ticks;
+};
+
+struct FusedBwdLds {
+  int stage, part, rin, rout, total;
+};
+
+__host__ __device__ inline FusedBwdLds fused_bwd_lds(int ncw, int ks, int ktw, int BR, int U) {
+  FusedBwdLds L;
+  L.stage = 0;
+  const int sbytes = ncw * 16 * fused_stage_row(ktw) * 4;
+  L.part = (sbytes + 15) & ~15;
+  const int pbytes = ks > 1 ? 2 * ncw * FUSED_PART_ROW * 16 : 0;
+  L.rin = L.part + pbytes;
+  L.rout = L.rin + 2 * BR * U * BWD_REC * 4;
+  L.total = L.rout + 2 * BR * U * 2 * 4;
+  return L;
+}
+
+// ---------------------------------------------------------------------------- I/O wave
+// The workgroup's slice of a step's records is nvalid rows of U*BWD_REC contiguous floats, and
+// its (dh, dc) output nvalid rows of U*2 floats; both rings hold them densely, [row][...].
+struct BwdIo {
+  const char* rec;      // bytes
+  float* dst;
+  long long in_base, in_row, in_step;     // floats
+  long long out_base, out_row, out_step;  // floats
+  int nvalid, U, T, BR, lane;
+  long long iofs[BWD_EPL_IN];  // float offset of the lane's record word for step 0
+  int ilds[BWD_EPL_IN];        // float index in slot 0 of the input ring (-1: none)
+  long long oofs[BWD_EPL_OUT];
+  int olds[BWD_EPL_OUT];
+
+  __device__ __forceinline__ void init() {
+    const int wpr = U * BWD_REC / 2, opr = U;  // 64-bit words per row
+#pragma unroll
+    for (int e = 0; e < BWD_EPL_IN; ++e) {
+      const int wi = lane + 64 * e;
+      const int r = wi / wpr, w = wi - r * wpr;
+      const bool ok = r < nvalid;
+      iofs[e] = ok ? in_base + r * in_row + 2 * w : in_base;  // no word: reload the first one
+      ilds[e] = ok ? r * U * BWD_REC + 2 * w : -1;
+    }
+#pragma unroll
+    for (int e = 0; e < BWD_EPL_OUT; ++e) {
+      const int wi = lane + 64 * e;
+      const int r = wi / opr, w = wi - r * opr;
+      const bool ok = r < nvalid;
+      oofs[e] = ok ? out_base + r * out_row + 2 * w : 0;
+      olds[e] = ok ? r * U * 2 + 2 * w : -1;
+    }
+  }
+};
+
+__device__ __forceinline__ void bio_issue(const BwdIo& c, int s, io_word_t (&r)[BWD_EPL_IN]) {
+  const long long step = (long long)s * c.in_step * 4;
+#pragma unroll
+  for (int e = 0; e < BWD_EPL_IN; ++e) r[e] = *reinterpret_cast<const io_word_t*>(c.rec + c.iofs[e] * 4 + step);
+}
+
+__device__ __forceinline__ void bio_put(const BwdIo& c, int s, const io_word_t (&r)[BWD_EPL_IN], float* rin) {
+  float* slot = rin + (s & 1) * (c.BR * c.U * BWD_REC);
+#pragma unroll
+  for (int e = 0; e < BWD_EPL_IN; ++e) {
+    const int i = c.ilds[e];
+    if (i >= 0) *reinterpret_cast<io_word_t*>(slot + i) = r[e];
+  }
+}
+
+__device__ __forceinline__ void bio_store(const BwdIo& c, int s, const float* rout) {
+  const float* slot = rout + (s & 1) * (c.BR * c.U * 2);
+  const long long step = (long long)s * c.out_step;
+#pragma unroll
+  for (int e = 0; e < BWD_EPL_OUT; ++e) {
+    const int i = c.olds[e];
+    if (i >= 0) *reinterpret_cast<float2*>(c.dst + c.oofs[e] + step) = *reinterpret_cast<const float2*>(slot + i);
+  }
+}
+
+// Interval k: put the records of step k into the ring, refill the stage with step k + 4, store
+// the outputs of step k - 2, then join barrier k (the compute waves' step barrier).
+template <int ST>
+__device__ __forceinline__ bool bio_interval(const BwdIo& c, int k, io_word_t (&raw)[FUSED_IO_STAGES][BWD_EPL_IN],
+                                             float* rin, const float* rout, const int* abort_flag) {
+  constexpr int L = FUSED_IO_STAGES;
+  if (k >= 0 && k < c.T) bio_put(c, k, raw[ST], rin);
+  bio_issue(c, min(max(k + L, 0), c.T - 1), raw[ST]);  // unconditional (clamped) so every path has the same loads in flight
+  if (k - 2 >= 0 && k - 2 < c.T) bio_store(c, k - 2, rout);
+  block_barrier();
+  return uniform_flag(*abort_flag);
+}
+
+__device__ __forceinline__ void bio_wave(BwdIo& c, float* rin, const float* rout, const int* abort_flag) {
+  constexpr int L = FUSED_IO_STAGES;
+  static_assert(L == 4, "the interval loop below is unrolled for four stages");
+  c.init();
+  io_word_t raw[L][BWD_EPL_IN];
+  // stage (k mod 4) holds step k; interval -1 uses stage 3
+  if (c.T == 0) {
+    block_barrier();
+    block_barrier();
+    return;
+  }
+  bio_issue(c, min(3, c.T - 1), raw[3]);
+  bio_issue(c, 0, raw[0]);
+  bio_issue(c, min(1, c.T - 1), raw[1]);
+  bio_issue(c, min(2, c.T - 1), raw[2]);
+  int k = -1;
+  for (; k + 3 <= c.T; k += L) {
+    if (bio_interval<3>(c, k, raw, rin, rout, abort_flag)) return;
+    if (bio_interval<0>(c, k + 1, raw, rin, rout, abort_flag)) return;
+    if (bio_interval<1>(c, k + 2, raw, rin, rout, abort_flag)) return;
+    if (bio_interval<2>(c, k + 3, raw, rin, rout, abort_flag)) return;
+  }
+  if (k <= c.T && bio_interval<3>(c, k, raw, rin, rout, abort_flag)) return;
+  if (k + 1 <= c.T && bio_interval<0>(c, k + 1, raw, rin, rout, abort_flag)) return;
+  if (k + 2 <= c.T && bio_interval<1>(c, k + 2, raw, rin, rout, abort_flag)) return;
+  if (c.T >= 1) bio_store(c, c.T - 1, rout);
+}
+
+// ---------------------------------------------------------------------------- kernel
+template <int CELL, int NCW, int KS, int MTW, int KTW>
+__global__ void __launch_bounds__((NCW + 1) * 64, 1) fused_bwd_kernel(FusedBwdArgs a) {
+  constexpr int G = cell_gates(CELL);
+  constexpr int MS = NCW / KS;
+  constexpr int MT_WG = MTW * MS;
+  constexpr int GT = fused_gt(NCW, KS, MTW);
+  static_assert((NCW == 4 || NCW == 6 || NCW == 8) && NCW % KS == 0, "compute waves / K split");
+
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  __shared__ int s_abort;
+
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int col = lane & 15, quad = lane >> 4;
+  const int D = a.D, N = a.N, T = a.T;
+  const int GD = G * D;
+  const int TPH = D / 16;     // row tiles of a head
+  const int KT = GD / 32;     // k-tiles of a head
+
+  const int die = blockIdx.x % a.n_xcd, slot = blockIdx.x / a.n_xcd;
+  const int group = (slot / a.W) * a.n_xcd + die;
+  const int w = slot % a.W;
+  if (group >= a.groups) return;
+  if (a.check_xcc && xcc_id() != (int)((a.xcc_of >> (4 * die)) & 0xFu)) {
+    if (threadIdx.x == 0) atomicOr(a.err, DEVERR_PLACEMENT);
+    return;
+  }
+  if (threadIdx.x == 0) s_abort = 0;
+
+  const int n = group % N, bblk = group / N;
+  const int b0 = bblk * a.BR;
+  const int nvalid = min(a.BR, a.B - b0);
+  const int tile0 = w * MT_WG;
+  const int u_base = tile0 * 16;
+  const int U = MT_WG * 16;  // units of this workgroup (the planner divides the head evenly)
+  const FusedBwdLds lay = fused_bwd_lds(NCW, KS, KTW, a.BR, U);
+  constexpr int SROW = fused_stage_row(KTW);
+  f32x4_t* part = reinterpret_cast<f32x4_t*>(smem + lay.part);
+  float* rin = reinterpret_cast<float*>(smem + lay.rin);
+  float* rout = reinterpret_cast<float*>(smem + lay.rout);
+  {  // poll stages: rows of padding batch columns stay zero
+    uint32_t* st = reinterpret_cast<uint32_t*>(smem + lay.stage);
+    for (int i = threadIdx.x; i < NCW * 16 * SROW; i += (NCW + 1) * 64) st[i] = 0u;
+  }
+
+  if (wave == NCW) {
+    BwdIo c;
+    c.rec = reinterpret_cast<const char*>(a.rec);
+    c.dst = a.dstate;
+    c.in_row = (long long)N * D * BWD_REC;
+    c.in_step = (long long)a.B * N * D * BWD_REC;
+    c.in_base = ((long long)b0 * N + n) * D * BWD_REC + (long long)u_base * BWD_REC;
+    c.out_row = (long long)N * D * 2;
+    c.out_step = (long long)a.B * N * D * 2;
+    c.out_base = ((long long)b0 * N + n) * D * 2 + (long long)u_base * 2;
+    c.nvalid = nvalid;
+    c.U = U;
+    c.T = T;
+    c.BR = a.BR;
+    c.lane = lane;
+    bio_wave(c, rin, rout, &s_abort);
+    return;
+  }
+
+  // ==================================================================== compute waves
+  const int ks = wave % KS, ms = wave / KS;
+  const bool colv = col < nvalid;
+
+  // ---- R fragments (rows d of this workgroup's tiles, k = (g, e) of this wave's K range)
+  bf16x8_t Ra[MTW][KTW];
+  {
+    const u32x4_t* rp = reinterpret_cast<const u32x4_t*>(a.rpk) + (long long)n * TPH * KT * 64 + lane;
+    u32x4_t raw[MTW][KTW];
+#pragma unroll
+    for (int j = 0; j < MTW; ++j) {
+      const int tt = min(tile0 + ms * MTW + j, TPH - 1);
+#pragma unroll
+      for (int kk = 0; kk < KTW; ++kk) raw[j][kk] = rp[((long long)tt * KT + ks * KTW + kk) * 64];
+    }
+#pragma unroll
+    for (int j = 0; j < MTW; ++j) {
+      const bool tv = tile0 + ms * MTW + j < TPH;
+#pragma unroll
+      for (int kk = 0; kk < KTW; ++kk) {
+        u32x4_t v = raw[j][kk];
+        if (!tv) v = u32x4_t{0u, 0u, 0u, 0u};
+        Ra[j][kk] = __builtin_bit_cast(bf16x8_t, v);
+      }
+    }
+  }
+
+  // ---- tiles this wave applies the step to: lane (col, quad) owns units gu .. gu+3
+  int gu[GT];
+  bool gval[GT];
+  float cr[GT][4];  // LSTM dc, GRU dh carried to the next kernel step
+#pragma unroll
+  for (int q = 0; q < GT; ++q) {
+    const int tq = (KS == 1) ? ms * MTW + q : wave + NCW * q;
+    const int tt = tile0 + tq;
+    gval[q] = (tq < MT_WG) && (tt < TPH);
+    gu[q] = 16 * tt + 4 * quad;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) cr[q][i] = 0.0f;
+  }
+  block_barrier();  // barrier -1
+
+  uint32_t* const xb = a.xbuf + (long long)group * 2 * a.BR * GD;
+  const int xpar = a.BR * GD;  // words per parity
+  // Step 0 has no dh_R: publish zero da with tag 0 (parity 1), which step 0 polls like any other.
+  if (colv) {
+#pragma unroll
+    for (int q = 0; q < GT; ++q) {
+      if (!gval[q]) continue;
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+        *reinterpret_cast<u32x4_t*>(xb + xpar + col * GD + g * D + gu[q]) = u32x4_t{0u, 0u, 0u, 0u};
+    }
+  }
+
+  for (int s = 0; s < T; ++s) {
+    // ---- 1+2. da of the step before as the B operand (this wave's K range), on MFMA
+    f32x4_t acc[MTW];
+#pragma unroll
+    for (int j = 0; j < MTW; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    {
+      const int pp = (s - 1) & 1;
+      const uint32_t tag = (uint32_t)s & 0xFFFFu;
+      constexpr int WPR = KTW * 16;                                // 64-bit words per row
+      constexpr int NP = (fused_max_br(KS, MTW) * WPR + 63) / 64;  // words per lane (upper bound)
+      uint32_t* stage = reinterpret_cast<uint32_t*>(smem + lay.stage) + wave * 16 * SROW;
+      const uint64_t* src = reinterpret_cast<const uint64_t*>(xb + pp * xpar) + ks * WPR;
+      const int nw = nvalid * WPR;
+      uint32_t off[NP];
+#pragma unroll
+      for (int e = 0; e < NP; ++e) {
+        const int wi = lane + 64 * e, r = wi / WPR, wr = wi - r * WPR;
+        off[e] = wi < nw ? (uint32_t)(r * (GD / 2) + wr) : 0u;
+      }
+      uint64_t v[NP];
+      long long t_first = 0;
+      int spins = 0;
+      if (s > 0) __builtin_amdgcn_s_sleep(FRNN_POLL_SLEEP0);
+      while (true) {
+#pragma unroll
+        for (int e = 0; e < NP; ++e) v[e] = __hip_atomic_load(src + off[e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        bool ok = true;
+#pragma unroll
+        for (int e = 0; e < NP; ++e) {
+          const uint32_t lo = (uint32_t)v[e], hi = (uint32_t)(v[e] >> 32);
+          if (lane + 64 * e < nw && (((lo ^ tag) | (hi ^ tag)) & 0xFFFFu) != 0) ok = false;
+        }
+        if (__all(ok)) {
+#pragma unroll
+          for (int e = 0; e < NP; ++e) {
+            const int wi = lane + 64 * e, r = wi / WPR, wr = wi - r * WPR;
+            if (wi < nw) stage[r * SROW + wr] = pack_hi((uint32_t)v[e], (uint32_t)(v[e] >> 32));
+          }
+          break;
+        }
+        if ((++spins & 63) == 0) {
+          const long long now = (long long)wall_clock64();
+          if (t_first == 0) t_first = now;
+          if (now - t_first > a.timeout_ticks ||
+              uniform_flag(__hip_atomic_load(a.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))) {
+            if (lane == 0) atomicOr(a.err, DEVERR_TIMEOUT);
+            s_abort = 1;  // every wave leaves after the next barrier
+            break;
+          }
+        }
+      }
+#pragma unroll
+      for (int kk = 0; kk < KTW; ++kk) {
+        const bf16x8_t bk = *reinterpret_cast<const bf16x8_t*>(stage + col * SROW + kk * 16 + 4 * quad);
+#pragma unroll
+        for (int j = 0; j < MTW; ++j) acc[j] = mfma_bf16(Ra[j][kk], bk, acc[j]);
+      }
+    }
+
+    // ---- 3. the step's barrier; K-split partial sums through LDS
+    f32x4_t pre[GT];
+    if constexpr (KS == 1) {
+#pragma unroll
+      for (int q = 0; q < GT; ++q) pre[q] = acc[q];
+      block_barrier();
+      if (uniform_flag(s_abort)) return;
+    } else {
+      constexpr int BRP = fused_brp(KS, MTW);
+      const int pp = s & 1;
+      f32x4_t P = acc[0];
+      pack_tiles<BRP, 1, MTW>(P, acc);
+      part[(pp * NCW + wave) * FUSED_PART_ROW + lane] = P;
+      block_barrier();
+      const int k2 = col / BRP, cc = col - k2 * BRP;
+#pragma unroll
+      for (int q = 0; q < GT; ++q) {
+        pre[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        const int tq = wave + NCW * q;
+        const int msq = tq / MTW, jq = tq - msq * MTW;
+        if (gval[q] && k2 < KS)
+          pre[q] = part[(pp * NCW + msq * KS + k2) * FUSED_PART_ROW + quad * 16 + jq * BRP + cc];
+      }
+      if (uniform_flag(s_abort)) return;
+#pragma unroll
+      for (int q = 0; q < GT; ++q) row_reduce<BRP, KS * BRP>(pre[q]);
+    }
+
+    // ---- 4. the linear step for the lane's four units; da out through the exchange, (dh, dc)
+    // to the output ring
+    const uint32_t wtag = (uint32_t)(s + 1) & 0xFFFFu;
+    if (colv) {
+#pragma unroll
+      for (int q = 0; q < GT; ++q) {
+        if (!gval[q]) continue;
+        const int ul = gu[q] - u_base;
+        const float* rr = rin + ((s & 1) * a.BR + col) * U * BWD_REC + ul * BWD_REC;
+        float* ro = rout + ((s & 1) * a.BR + col) * U * 2 + ul * 2;
+        float da[G][4], dh[4], dc[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const f32x4_t r0 = *reinterpret_cast<const f32x4_t*>(rr + i * BWD_REC);
+          const f32x4_t r1 = *reinterpret_cast<const f32x4_t*>(rr + i * BWD_REC + 4);
+          if constexpr (CELL == CELL_LSTM) {
+            dh[i] = pre[q][i] + r1[2];
+            dc[i] = cr[q][i] + r1[3] + dh[i] * r0[0];
+            da[0][i] = dc[i] * r0[1];
+            da[1][i] = dc[i] * r0[2];
+            da[2 % G][i] = dc[i] * r0[3];
+            da[3 % G][i] = dh[i] * r1[0];
+            cr[q][i] = dc[i] * r1[1];
+          } else if constexpr (CELL == CELL_GRU) {
+            dh[i] = pre[q][i] + r1[0] + cr[q][i];
+            dc[i] = 0.0f;
+            da[0][i] = dh[i] * r0[0];
+            da[1 % G][i] = dh[i] * r0[1];
+            da[2 % G][i] = dh[i] * r0[2];
+            cr[q][i] = dh[i] * r0[3];
+          } else {
+            dh[i] = pre[q][i] + r0[1];
+            dc[i] = 0.0f;
+            da[0][i] = dh[i] * r0[0];
+          }
+        }
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          u32x4_t wv;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) wv[i] = ((uint32_t)f2bf(da[g][i]) << 16) | wtag;
+          *reinterpret_cast<u32x4_t*>(xb + ((s & 1) * xpar + col * GD + g * D + gu[q])) = wv;
+        }
+        *reinterpret_cast<f32x4_t*>(ro) = f32x4_t{dh[0], dc[0], dh[1], dc[1]};
+        *reinterpret_cast<f32x4_t*>(ro + 4) = f32x4_t{dh[2], dc[2], dh[3], dc[3]};
+      }
+    }
+    // Keep the exchange stores ahead of the next step's polling in program order.
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  }
+  block_barrier();  // barrier T: the last step's outputs are in LDS for the I/O wave
+}
+
+}  // namespace frnn

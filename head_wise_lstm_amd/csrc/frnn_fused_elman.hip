@@ -1,4 +1,5 @@
-// Instantiations of the fused kernel for the elman cell (one translation unit per cell).
+// Instantiations of the fused forward and backward kernels for the elman cell (one translation
+// unit per cell).
 #include "frnn_variants.hpp"
 
 namespace frnn {
@@ -9,7 +10,14 @@ namespace {
 const FusedVariant kTable[] = {FRNN_FUSED_DESIGNS(FRNN_FV)};
 #undef FRNN_FV
 
+#define FRNN_FBV(NCW, KS, MTW, KTW) \
+  {CELL_ELMAN, NCW, KS, MTW, KTW, &fused_bwd_kernel<CELL_ELMAN, NCW, KS, MTW, KTW>},
+const FusedBwdVariant kBwdTable[] = {FRNN_FUSED_BWD_ELMAN(FRNN_FBV)};
+#undef FRNN_FBV
+
 }  // namespace
+
+FusedBwdTable fused_bwd_table_elman() { return FusedBwdTable{kBwdTable, (int)(sizeof(kBwdTable) / sizeof(kBwdTable[0]))}; }
 
 FusedTable fused_table_elman() { return FusedTable{kTable, (int)(sizeof(kTable) / sizeof(kTable[0]))}; }
 

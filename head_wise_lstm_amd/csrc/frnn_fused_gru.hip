@@ -1,4 +1,5 @@
-// Instantiations of the fused kernel for the gru cell (one translation unit per cell).
+// Instantiations of the fused forward and backward kernels for the gru cell (one translation
+// unit per cell).
 #include "frnn_variants.hpp"
 
 namespace frnn {
@@ -9,7 +10,14 @@ namespace {
 const FusedVariant kTable[] = {FRNN_FUSED_DESIGNS(FRNN_FV)};
 #undef FRNN_FV
 
+#define FRNN_FBV(NCW, KS, MTW, KTW) \
+  {CELL_GRU, NCW, KS, MTW, KTW, &fused_bwd_kernel<CELL_GRU, NCW, KS, MTW, KTW>},
+const FusedBwdVariant kBwdTable[] = {FRNN_FUSED_BWD_GRU(FRNN_FBV)};
+#undef FRNN_FBV
+
 }  // namespace
+
+FusedBwdTable fused_bwd_table_gru() { return FusedBwdTable{kBwdTable, (int)(sizeof(kBwdTable) / sizeof(kBwdTable[0]))}; }
 
 FusedTable fused_table_gru() { return FusedTable{kTable, (int)(sizeof(kTable) / sizeof(kTable[0]))}; }
 

@@ -4,6 +4,7 @@
 #pragma once
 
 #include "frnn_fused.hpp"
+#include "frnn_fused_bwd.hpp"
 
 namespace frnn {
 
@@ -43,5 +44,35 @@ struct FusedTable {
 FusedTable fused_table_lstm();
 FusedTable fused_table_elman();
 FusedTable fused_table_gru();
+
+// The fused backward's designs, per cell: X(NCW, KS, MTW, KTW) with K = G*D split KS ways.
+typedef void (*fused_bwd_fn)(FusedBwdArgs);
+
+struct FusedBwdVariant {
+  int cell, ncw, ks, mtw, ktw;
+  fused_bwd_fn fn;
+};
+
+struct FusedBwdTable {
+  const FusedBwdVariant* v;
+  int n;
+};
+
+// D = 768 (head split 24 ways), 512, 256, 128 and 64
+#define FRNN_FUSED_BWD_LSTM(X)                                                          \
+  X(8, 8, 2, 12) X(6, 6, 2, 16) X(8, 8, 2, 8) X(8, 8, 1, 8) X(8, 8, 2, 4) X(4, 4, 2, 8) \
+  X(8, 8, 1, 4) X(4, 4, 1, 8) X(8, 8, 1, 2) X(4, 4, 1, 4) X(8, 8, 2, 2) X(4, 4, 2, 4)   \
+  X(4, 4, 1, 2) X(4, 4, 2, 2) X(4, 2, 1, 4)
+#define FRNN_FUSED_BWD_GRU(X)                                                           \
+  X(8, 8, 2, 9) X(6, 6, 2, 12) X(8, 8, 2, 6) X(8, 8, 1, 6) X(8, 8, 2, 3) X(6, 6, 2, 4)  \
+  X(8, 8, 1, 3) X(6, 6, 1, 4) X(6, 6, 1, 2) X(6, 6, 2, 2) X(4, 4, 2, 3) X(6, 6, 1, 1)   \
+  X(6, 6, 2, 1) X(4, 2, 1, 3)
+#define FRNN_FUSED_BWD_ELMAN(X)                                                         \
+  X(8, 8, 1, 2) X(8, 8, 2, 2) X(8, 8, 1, 1) X(8, 8, 2, 1) X(4, 4, 1, 2) X(4, 4, 2, 2)   \
+  X(4, 4, 1, 1) X(4, 4, 2, 1) X(4, 2, 1, 2) X(4, 2, 1, 1)
+
+FusedBwdTable fused_bwd_table_lstm();
+FusedBwdTable fused_bwd_table_elman();
+FusedBwdTable fused_bwd_table_gru();
 
 }  // namespace frnn

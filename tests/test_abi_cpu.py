@@ -195,19 +195,20 @@ def test_planner_gru_matches_lstm_tiles(lib):
 
 
 def test_bwd_validation_and_workspace(lib):
-    """frnn_bwd: validated before any device call; the workspace grows with T; only the
-    alternating path is offered."""
+    """frnn_bwd: validated before any device call; the workspace grows with T; the fused path
+    takes bf16 inputs only."""
     f = lib.frnn_bwd
     p = ctypes.c_void_p(0x100000)
     d = D(B=2, T=3, N=1, Dm=64)
     n = ctypes.c_size_t(0)
     assert lib.frnn_bwd_workspace_bytes(ctypes.byref(d), 0, ctypes.byref(n)) == 0
     need = n.value
-    assert lib.frnn_bwd_workspace_bytes(ctypes.byref(d), 1, ctypes.byref(n)) == EUNSUP
+    assert lib.frnn_bwd_workspace_bytes(ctypes.byref(d), 1, ctypes.byref(n)) == 0 and n.value > need
+    assert lib.frnn_bwd_workspace_bytes(ctypes.byref(D(B=2, T=3, N=1, Dm=64, ind=0)), 1, ctypes.byref(n)) == EUNSUP
     assert lib.frnn_bwd_workspace_bytes(ctypes.byref(D(B=2, T=300, N=1, Dm=64)), 0, ctypes.byref(n)) == 0
     assert n.value > need
     args = lambda ws, nb: (p, p, None, None, p, None, None, p, p, p, p, ws, nb, None)
-    assert f(ctypes.byref(d), 1, *args(p, need)) == EUNSUP                       # fused backward
+    assert f(ctypes.byref(D(B=2, T=3, N=1, Dm=64, ind=0)), 1, *args(p, 1 << 30)) == EUNSUP  # fused fp32
     assert f(ctypes.byref(D(B=0)), 0, *args(p, need)) == EINVAL
     assert f(ctypes.byref(d), 0, p, p, None, None, None, None, None, p, p, p, p, p, need, None) == EINVAL  # states NULL
     assert f(ctypes.byref(d), 0, *args(None, need)) == EWS
@@ -215,3 +216,20 @@ def test_bwd_validation_and_workspace(lib):
     assert f(ctypes.byref(d), 0, ctypes.c_void_p(0x100004), *args(p, need)[1:]) == EINVAL  # misaligned Wx
     s = hw.frnn_bwd_plan_str(D(B=16, T=1024, N=1, Dm=768), 0)
     assert s.startswith("backward path=alternating cell=lstm") and "hr_gemm=16384x3072x768" in s
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="planner model of a 256-CU, 8-die device (no GPU here)")
+def test_fused_bwd_planner(lib):
+    """The fused backward splits a head's rows into 16-unit tiles over the workgroups of one die."""
+    s = hw.frnn_bwd_plan_str(D(B=16, T=1024, N=1, Dm=768), 1)
+    assert "design=die-local" in s and "BR=2 " in s and "W=24 " in s and "NCW=8 KS=8 MTW=2 KTW=12" in s
+    s = hw.frnn_bwd_plan_str(D(B=16, T=1024, N=1, Dm=768, cell=2), 1)
+    assert "cell=gru" in s and "W=24 " in s and "KTW=9" in s
+    s = hw.frnn_bwd_plan_str(D(B=8, T=1024, N=3, Dm=256), 1)
+    assert "design=die-local" in s
+    for (B, N, Dm, cell) in [(16, 1, 768, 0), (8, 3, 256, 0), (5, 2, 64, 0), (9, 2, 256, 2), (7, 2, 128, 1)]:
+        s = hw.frnn_bwd_plan_str(D(B=B, T=8, N=N, Dm=Dm, cell=cell), 1)
+        grid = int(re.search(r"grid=(\d+)", s).group(1))
+        slots = int(re.search(r"slots/die=(\d+)", s).group(1))
+        lds = int(re.search(r"lds=(\d+)", s).group(1))
+        assert grid <= 256 and slots <= 32 and lds <= 160 * 1024, s

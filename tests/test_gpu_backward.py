@@ -45,6 +45,8 @@ def run_bwd_case(w, path="alternating"):
     dev = torch.device("cuda:0")
     g = lambda t: None if t is None else t.to(dev)
     _log(f"bwd case {w.name} cell={w.cell} B={w.B} T={w.T} N={w.N} D={w.D} path={path}")
+    if path == "fused":
+        _log("  plan: " + hw.frnn_bwd_plan_str(hw._desc(w.B, w.T, w.N, w.D, w.cell, w.dtype), "fused"))
     st, last = hw.frnn_fwd(g(x["Wx"]), g(x["R"]), g(x["b"]), g(x["states0"]), cell=w.cell, path="fused"
                            if w.dtype == torch.bfloat16 or w.D <= 64 else "alternating")
     grads = hw.frnn_bwd(g(x["Wx"]), g(x["R"]), g(x["b"]), g(x["states0"]), st, g(ct["dstates"]), g(ct["dlast"]),
@@ -85,15 +87,46 @@ SMALL = [
 ]
 
 
+def _fused_plan_or_skip(w):
+    hw = _hw()
+    try:
+        return hw.frnn_bwd_plan_str(hw._desc(w.B, w.T, w.N, w.D, w.cell, w.dtype), "fused")
+    except hw.FrnnError as e:
+        if e.status == -2:
+            pytest.skip("no fused backward design for this shape or dtype (fp32, or no die-local tiling)")
+        raise
+
+
+@pytest.mark.parametrize("path", ["alternating", "fused"])
 @pytest.mark.parametrize("w", SMALL, ids=lambda w: w.name)
-def test_bwd_small(w):
-    run_bwd_case(w)
+def test_bwd_small(w, path):
+    if path == "fused":
+        _fused_plan_or_skip(w)
+    run_bwd_case(w, path)
 
 
+@pytest.mark.parametrize("path", ["alternating", "fused"])
 @pytest.mark.parametrize("name", ["lstm_bf16_B16_T1024_N1_D768", "lstm_bf16_B8_T1024_N3_D256",
                                   "gru_bf16_B16_T1024_N1_D768", "lstm_f32_B2_T16_N1_D32"])
-def test_bwd_full(name):
-    run_bwd_case(fi.get_workload(name))
+def test_bwd_full(name, path):
+    w = fi.get_workload(name)
+    if path == "fused":
+        _fused_plan_or_skip(w)
+    run_bwd_case(w, path)
+
+
+def test_bwd_fused_matches_alternating():
+    """The two backward paths agree closely (same operand roundings, different summation orders)."""
+    hw = _hw()
+    w = fi.HeadwiseWorkload("bwd_agree", "lstm", torch.bfloat16, B=8, T=40, N=2, D=256, seed=231, s0_var=1.0)
+    x = {k: (v.cuda() if v is not None else None) for k, v in fi.make_inputs(w).items()}
+    ct = {k: v.cuda() for k, v in fi.backward_cotangents(w).items()}
+    st, _ = hw.frnn_fwd(x["Wx"], x["R"], x["b"], x["states0"], cell="lstm")
+    ga = hw.frnn_bwd(x["Wx"], x["R"], x["b"], x["states0"], st, ct["dstates"], ct["dlast"], cell="lstm", path="alternating")
+    gf = hw.frnn_bwd(x["Wx"], x["R"], x["b"], x["states0"], st, ct["dstates"], ct["dlast"], cell="lstm", path="fused")
+    for a, f in zip(ga, gf):
+        scale = max(1.0, a.abs().max().item())
+        assert (a - f).abs().max().item() <= 1e-2 * scale
 
 
 def test_bwd_t0():
