@@ -130,8 +130,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="lstm_bf16_B16_T1024_N1_D768")
-    ap.add_argument("--path", default=None, choices=["fused", "alternating"],
-                    help="default: fused (forward), alternating (--backward)")
+    ap.add_argument("--path", default="fused", choices=["fused", "alternating"])
     ap.add_argument("--backward", action="store_true",
                     help="time frnn_bwd (back-propagation through time) instead of the forward: the "
                          "forward states are computed once before the timed region")
@@ -147,8 +146,6 @@ def main():
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="per-launch HBM bytes measured with rocprofv3 counters for this workload/path")
     args = ap.parse_args()
-    if args.path is None:
-        args.path = "alternating" if args.backward else "fused"
     if args.write_traffic:
         write_traffic(args)
         return
@@ -251,7 +248,8 @@ def main():
     tflops = flops / sec / 1e12
     roof = {"bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": tflops / PEAK_BF16_TFLOPS, "traffic": None,
-            "kernel": ("frnn::bwd_gate_kernel+bwd_dh_kernel (+ GEMMs)" if args.backward else
+            "kernel": (("frnn::fused_bwd_kernel (+ GEMMs, records)" if args.path == "fused" else
+                        "frnn::bwd_gate_kernel+bwd_dh_kernel (+ GEMMs)") if args.backward else
                        "frnn::fused_fwd_kernel" if args.path == "fused" else "frnn::alt_gemm_kernel+alt_gate_kernel"),
             "per_launch_flop": flops, "launch_ms": ms}
     if nbytes and not args.backward:

@@ -310,26 +310,30 @@ void launch_transpose(const E* src, long long lds, int K, int Nc, E* dst, long l
   hipLaunchKernelGGL(transpose_kernel<E>, dim3((Nc + 31) / 32, ty), dim3(256), 0, st, src, lds, K, Nc, dst, ldd);
 }
 
-// C[M][Nc] = A[M][K] . Bt[Nc][K]^T in fp32: the tiled MFMA kernel for bf16 operands, the plain
-// fp32 MFMA kernel for fp32 ones. K is a multiple of 32.
+// C[M][Nc] = A[M][K] . Bt[Nc][K]^T in fp32, for parts z = 0 .. parts-1 at once (A, Bt and C
+// offset by z * a_z, b_z, c_z elements): the tiled MFMA kernel for bf16 operands, the plain fp32
+// MFMA kernel for fp32 ones. K is a multiple of 32.
 hipError_t launch_gemm(bool f32, int M, int Nc, int K, const void* A, long long lda, const void* Bt, long long ldb,
-                       float* C, long long ldc, hipStream_t st) {
+                       float* C, long long ldc, hipStream_t st, int parts = 1, long long a_z = 0, long long b_z = 0,
+                       long long c_z = 0) {
   if (M <= 0 || Nc <= 0) return hipSuccess;
-  if (K % 32 != 0) return hipErrorInvalidValue;
+  if (K % 32 != 0 || parts < 1) return hipErrorInvalidValue;
   if (f32) {
     const long long tiles = (long long)((M + 15) / 16) * ((Nc + 15) / 16);
-    hipLaunchKernelGGL(gemm_f32_kernel, dim3((unsigned)((tiles + 3) / 4)), dim3(256), 0, st, M, Nc, K,
-                       reinterpret_cast<const float*>(A), lda, reinterpret_cast<const float*>(Bt), ldb, C, ldc);
+    hipLaunchKernelGGL(gemm_f32_kernel, dim3((unsigned)((tiles + 3) / 4), parts), dim3(256), 0, st, M, Nc, K,
+                       reinterpret_cast<const float*>(A), lda, reinterpret_cast<const float*>(Bt), ldb, C, ldc, a_z, b_z,
+                       c_z);
     return hipGetLastError();
   }
-  if (ldb != K) return hipErrorInvalidValue;  // the tiled kernel reads Bt rows with stride K
   ProjArgs pa;
   pa.M = M; pa.Nc = Nc; pa.K = K;
   pa.A = A; pa.a_f32 = 0; pa.lda = lda;
   pa.Bt = reinterpret_cast<const uint16_t*>(Bt);
+  pa.ldb = ldb;
   pa.b1 = nullptr; pa.b2 = nullptr;
   pa.C = C; pa.ldc = ldc;
-  const dim3 pgrid(((Nc + PJ_BN - 1) / PJ_BN) * ((M + PJ_BM - 1) / PJ_BM));
+  pa.a_z = a_z; pa.b_z = b_z; pa.c_z = c_z;
+  const dim3 pgrid(((Nc + PJ_BN - 1) / PJ_BN) * ((M + PJ_BM - 1) / PJ_BM), parts);
   hipLaunchKernelGGL(proj_gemm_kernel<false>, pgrid, dim3(256), 0, st, pa);
   return hipGetLastError();
 }
@@ -443,6 +447,16 @@ int run_recurrence(const Problem& p, int path, int* err, void* scratch, hipStrea
 
 // ----------------------------------------------------------------------------- backward
 // Workspace of frnn_bwd after the error word (grows with T: it holds every step's h.R and da).
+// K split of the dR GEMM (K = T*B is long and its output small): the parts are summed by the
+// scatter kernel.
+constexpr int BWD_DR_PARTS = 8;
+
+// Rows of the (t, b) operand buffers: T*B padded to whole 32-wide k-tiles of every dR part.
+size_t bwd_kp(int T, int B) {
+  const size_t q = 32 * BWD_DR_PARTS;
+  return ((size_t)T * B + q - 1) / q * q;
+}
+
 struct BwdLayout {
   size_t zeros, hprev, hprevT, rt, rpk, hr, da, daT, tmp, dhpart, carry, rec, dstate, xbuf, total;
 };
@@ -495,7 +509,7 @@ int plan_fused_bwd(int B, int N, int D, int cell, int f32, const DevInfo& di, Fu
 
 BwdLayout bwd_layout(int B, int T, int N, int D, int cell, int f32, int path) {
   const size_t G = gates_of(cell), elt = f32 ? 4 : 2;
-  const size_t Kp = ((size_t)T * B + 31) / 32 * 32;
+  const size_t Kp = bwd_kp(T, B);
   BwdLayout L;
   size_t q = 0;
   L.zeros = q;  q += 256;
@@ -506,7 +520,7 @@ BwdLayout bwd_layout(int B, int T, int N, int D, int cell, int f32, int path) {
   L.hr = q;     q += align256((size_t)N * T * B * G * D * 4);
   L.da = q;     q += align256((size_t)N * Kp * G * D * elt);
   L.daT = q;    q += align256((size_t)N * G * D * Kp * elt);
-  L.tmp = q;    q += align256((size_t)N * (D + 1) * G * D * 4);
+  L.tmp = q;    q += align256((size_t)BWD_DR_PARTS * N * (D + 1) * G * D * 4);
   L.dhpart = q; q += align256((size_t)BWD_KS * B * N * D * 4);
   L.carry = q;  q += align256((size_t)B * N * D * 4);
   L.rec = L.dstate = L.xbuf = q;
@@ -531,7 +545,7 @@ std::string bwd_plan_string(const frnn_desc* d, int path, const FusedBwdPlan* fp
     return std::string(buf);
   }
   const int G = gates_of(d->cell);
-  const long long Kp = ((long long)d->T * d->B + 31) / 32 * 32;
+  const long long Kp = (long long)bwd_kp(d->T, d->B);
   std::snprintf(buf, sizeof(buf),
                 "backward path=%s cell=%s dtype=%s B=%d T=%d N=%d D=%d hr_gemm=%lldx%dx%d dR_gemm=%dx%dx%lld "
                 "step_launches=%d",
@@ -770,7 +784,7 @@ int frnn_bwd(const frnn_desc* d, int path, const void* Wx, const void* R, const 
     return hipGetLastError() == hipSuccess ? FRNN_OK : FRNN_EHIP;
   }
   char* base = reinterpret_cast<char*>(workspace) + kErrBytes;
-  const int Kp = (int)(((long long)T * B + 31) / 32 * 32);
+  const int Kp = (int)bwd_kp(T, B);
   BwdArgs a;
   std::memset(&a, 0, sizeof(a));
   a.B = B; a.T = T; a.N = N; a.D = D; a.cell = d->cell; a.f32 = f32; a.Kp = Kp;
@@ -868,14 +882,18 @@ int frnn_bwd(const frnn_desc* d, int path, const void* Wx, const void* R, const 
     }
     hipLaunchKernelGGL(bwd_ones_row_kernel, dim3((unsigned)std::min<long long>(((long long)N * Kp + 255) / 256, 4096)),
                        dim3(256), 0, st, hT, N, D, Kp, f32);
+    // K split into BWD_DR_PARTS equal parts, computed in one launch per head and summed by the
+    // scatter kernel
+    const int parts = BWD_DR_PARTS, kpart = Kp / parts;
+    const long long ptot = (long long)N * (D + 1) * G * D;
     for (int n = 0; n < N; ++n) {
-      if (launch_gemm(f32, D + 1, G * D, Kp, hT + (size_t)n * (D + 1) * Kp * elt, Kp, daT + (size_t)n * G * D * Kp * elt, Kp,
-                      tmp + (size_t)n * (D + 1) * G * D, (long long)G * D, st) != hipSuccess)
+      if (launch_gemm(f32, D + 1, G * D, kpart, hT + (size_t)n * (D + 1) * Kp * elt, Kp, daT + (size_t)n * G * D * Kp * elt, Kp,
+                      tmp + (size_t)n * (D + 1) * G * D, (long long)G * D, st, parts, kpart, kpart, ptot) != hipSuccess)
         return FRNN_EHIP;
     }
-    const long long nt = (long long)N * (D + 1) * G * D;
+    const long long nt = ptot;
     hipLaunchKernelGGL(bwd_scatter_kernel, dim3((unsigned)std::min<long long>((nt + 255) / 256, 65536)), dim3(256), 0, st,
-                       tmp, N, D, G, reinterpret_cast<float*>(dR), reinterpret_cast<float*>(db));
+                       tmp, parts, N, D, G, reinterpret_cast<float*>(dR), reinterpret_cast<float*>(db));
   }
   return hipGetLastError() == hipSuccess ? FRNN_OK : FRNN_EHIP;
 }
@@ -979,6 +997,8 @@ int frnn_lstm_stack_fwd(int L, int T, int B, int I, int H, int path, const void*
     pa.a_f32 = (l == 0) ? 0 : 1;
     pa.lda = pa.K;
     pa.Bt = wit;
+    pa.ldb = pa.K;
+    pa.a_z = pa.b_z = pa.c_z = 0;
     pa.b1 = b_ih ? reinterpret_cast<const uint16_t*>(b_ih[l]) : nullptr;
     pa.b2 = b_hh ? reinterpret_cast<const uint16_t*>(b_hh[l]) : nullptr;
     pa.C = wx;

@@ -424,20 +424,24 @@ __global__ void __launch_bounds__(256) bwd_final_kernel(BwdArgs a) {
   if (a.ds0_c && a.cell == CELL_LSTM) a.ds0_c[idx] = a.carry[idx];
 }
 
-// dR[g][n][d][e] = tmp[n][d][g*D + e] and db[g][n][e] = tmp[n][D][g*D + e] (tmp: [N][D+1][G*D]
-// fp32, the dR GEMM's output with its row of ones).
-__global__ void __launch_bounds__(256) bwd_scatter_kernel(const float* tmp, int N, int D, int G, float* dR, float* db) {
+// dR[g][n][d][e] = sum_p tmp[p][n][d][g*D + e] and db[g][n][e] = sum_p tmp[p][n][D][g*D + e]
+// (tmp: [parts][N][D+1][G*D] fp32, the K-split parts of the dR GEMM's output with its row of
+// ones), the parts added in order.
+__global__ void __launch_bounds__(256) bwd_scatter_kernel(const float* tmp, int parts, int N, int D, int G, float* dR,
+                                                          float* db) {
   const long long total = (long long)N * (D + 1) * G * D;
   for (long long idx = (long long)blockIdx.x * 256 + threadIdx.x; idx < total; idx += (long long)gridDim.x * 256) {
+    float v = 0.0f;
+    for (int p = 0; p < parts; ++p) v += tmp[p * total + idx];
     const int col = (int)(idx % (G * D));
     const long long r = idx / (G * D);
     const int d = (int)(r % (D + 1));
     const int n = (int)(r / (D + 1));
     const int g = col / D, e = col % D;
     if (d < D) {
-      if (dR) dR[(((long long)g * N + n) * D + d) * D + e] = tmp[idx];
+      if (dR) dR[(((long long)g * N + n) * D + d) * D + e] = v;
     } else if (db) {
-      db[((long long)g * N + n) * D + e] = tmp[idx];
+      db[((long long)g * N + n) * D + e] = v;
     }
   }
 }
@@ -455,7 +459,11 @@ __global__ void __launch_bounds__(256) bwd_ones_row_kernel(void* hT, int N, int 
 // Plain fp32 GEMM for the fp32 inputs: C[M][Nc] = A[M][K] . Bt[Nc][K]^T, one 16 x 16 tile per
 // wave on v_mfma_f32_16x16x4f32, operands read straight from memory (K a multiple of 4).
 __global__ void __launch_bounds__(256) gemm_f32_kernel(int M, int Nc, int K, const float* A, long long lda,
-                                                       const float* Bt, long long ldb, float* C, long long ldc) {
+                                                       const float* Bt, long long ldb, float* C, long long ldc,
+                                                       long long a_z, long long b_z, long long c_z) {
+  A += blockIdx.y * a_z;  // part blockIdx.y of a batch of independent products
+  Bt += blockIdx.y * b_z;
+  C += blockIdx.y * c_z;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int col = lane & 15, quad = lane >> 4;
   const int tn = (Nc + 15) / 16;

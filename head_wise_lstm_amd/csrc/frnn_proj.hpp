@@ -21,11 +21,13 @@ struct ProjArgs {
   const void* A;
   int a_f32;
   long long lda;
-  const uint16_t* Bt;  // [Nc][K] bf16 (Wi transposed)
+  const uint16_t* Bt;  // [Nc][K] bf16 (Wi transposed), rows ldb apart
+  long long ldb;
   const uint16_t* b1;
   const uint16_t* b2;
   float* C;
   long long ldc;
+  long long a_z, b_z, c_z;  // element offsets of A, Bt and C per blockIdx.y (independent parts)
 };
 
 constexpr int PJ_BM = 256, PJ_BN = 128, PJ_BK = 32;
@@ -103,6 +105,11 @@ __global__ void __launch_bounds__(256, 2) proj_gemm_kernel(ProjArgs p) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int col = lane & 15, quad = lane >> 4;
   const int wm = wave >> 1, wn = wave & 1;  // wave tile: rows wm*128 .., columns wn*64 ..
+  if (blockIdx.y) {  // part z of a batch of independent products
+    p.A = reinterpret_cast<const char*>(p.A) + blockIdx.y * p.a_z * (AF32 ? 4 : 2);
+    p.Bt += blockIdx.y * p.b_z;
+    p.C += blockIdx.y * p.c_z;
+  }
   // Die-aware tile order. Workgroups are dealt to the 8 dies round-robin by index, so the die of
   // workgroup L is L % 8. Tiles are numbered row-major (M tile, then N tile) and each die takes a
   // contiguous run of them: the N tiles that share an A tile run on one die and read A once into
@@ -130,7 +137,7 @@ __global__ void __launch_bounds__(256, 2) proj_gemm_kernel(ProjArgs p) {
     _Pragma("unroll") for (int c = 0; c < 4; ++c)                                                 \
       proj_load8<AF32>(ra[c], p.A, p.lda, m0 + lrow + 64 * c, p.M, (K0) + lkc);                   \
     _Pragma("unroll") for (int c = 0; c < 2; ++c)                                                 \
-      proj_load8<false>(rb[c], p.Bt, p.K, (long long)n0 + lrow + 64 * c, p.Nc, (K0) + lkc);       \
+      proj_load8<false>(rb[c], p.Bt, p.ldb, (long long)n0 + lrow + 64 * c, p.Nc, (K0) + lkc);     \
   } while (0)
 #define PJ_LSTORE(ST)                                                                             \
   do {                                                                                            \
