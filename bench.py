@@ -71,7 +71,10 @@ def write_traffic(args) -> None:
     benchmark, then of --copy-calibration) into a per-launch HBM byte figure in --traffic-json."""
     import frnn_inputs as fi
     fetch_csv, write_csv, fetch_copy_csv, write_copy_csv = args.write_traffic
-    kname = "fused_fwd_kernel" if args.path == "fused" else "alt_gemm_kernel"
+    if args.backward:
+        kname = "fused_bwd_kernel" if args.path == "fused" else "bwd_dh_kernel"
+    else:
+        kname = "fused_fwd_kernel" if args.path == "fused" else "alt_gemm_kernel"
     true_kib = args.copy_mib * 1024.0
     fc, _, _ = _counter_mean(fetch_copy_csv, "copyBuffer")
     wc, _, _ = _counter_mean(write_copy_csv, "copyBuffer")
@@ -79,7 +82,11 @@ def write_traffic(args) -> None:
     wk, nw, _ = _counter_mean(write_csv, kname)
     ff, wf = true_kib / fc, true_kib / wc
     w = fi.get_workload(args.workload)
-    alg = headwise_bytes(w, 2 if "bf16" in w.name else 4)
+    if args.backward:
+        # the serial kernel's own: the step records read once, (dh, dc) written once, R read once
+        alg = float(w.T * w.B * w.N * w.D * (8 + 2) * 4 + w.G * w.N * w.D * w.D * 2)
+    else:
+        alg = headwise_bytes(w, 2 if "bf16" in w.name else 4)
     rd, wr = fk * 1024 * ff, wk * 1024 * wf
     entry = {"kernel": names[0], "dispatches": [nf, nw], "fetch_kib_per_dispatch": fk, "write_kib_per_dispatch": wk,
              "fetch_factor": ff, "write_factor": wf, "copy_mib": args.copy_mib, "read_bytes": rd, "write_bytes": wr,
@@ -89,7 +96,7 @@ def write_traffic(args) -> None:
             allt = json.load(f)
     except (OSError, ValueError):
         allt = {}
-    allt[f"{args.workload}:{args.path}"] = entry
+    allt[f"{args.workload}:{args.path}" + (":backward" if args.backward else "")] = entry
     with open(args.traffic_json, "w") as f:
         json.dump(allt, f, indent=1)
         f.write("\n")
@@ -259,7 +266,7 @@ def main():
     # copy), valid only for the kernel source they were taken on
     try:
         with open(args.traffic_json) as f:
-            tj = json.load(f).get(f"{config['workload']}:{args.path}")
+            tj = json.load(f).get(f"{config['workload']}:{args.path}" + (":backward" if args.backward else ""))
         if tj and tj.get("kernel_sources_sha256_16") == kernel_sources_hash():
             roof["traffic"] = tj["bytes_per_launch"]
             roof["traffic_over_algorithmic"] = tj["bytes_per_launch"] / tj["algorithmic_bytes"]
