@@ -277,10 +277,20 @@ class _FlashRNNFunction(torch.autograd.Function):
 
 
 def flashrnn(Wx: torch.Tensor, R: torch.Tensor, b: Optional[torch.Tensor] = None,
-             states: Optional[torch.Tensor] = None, cell: str = "lstm", path="fused", bwd_path="alternating"):
+             states: Optional[torch.Tensor] = None, cell: str = "lstm", path="fused", bwd_path=None):
     """Differentiable head-wise forward (the FlashRNN page's functional call): returns (states,
     last_states) like frnn_fwd; torch autograd runs frnn_bwd for the gradients of Wx, R, b and the
-    initial states (cast to their dtypes)."""
+    initial states (cast to their dtypes). bwd_path None: the fused backward where this build has
+    a design for the shape and dtype, else the alternating one (both are HIP paths)."""
+    if bwd_path is None:
+        B, T, _, N, D = Wx.shape
+        try:
+            frnn_bwd_plan_str(_desc(B, T, N, D, cell, Wx.dtype), "fused")
+            bwd_path = "fused"
+        except FrnnError as e:
+            if e.status != -2:
+                raise
+            bwd_path = "alternating"
     return _FlashRNNFunction.apply(Wx, R, b, states, cell, path, bwd_path)
 
 
