@@ -154,6 +154,8 @@ const char* cell_name(int cell) { return cell == FRNN_CELL_LSTM ? "lstm" : cell 
 struct FusedPlan {
   const FusedVariant* v = nullptr;
   int local = 0, W = 1, BR = 16, groups = 0, ncw = 4, ks = 1, mtw = 0, ktw = 0, n_xcd = 1, slots = 0, grid = 0;
+  int chunks = 1, Bc = 0;  // the batch runs as `chunks` launches of at most Bc rows
+  double cost_us = 0.0;    // predicted time of the whole call
   size_t lds = 0;
 };
 
@@ -163,10 +165,32 @@ int env_int(const char* name, int dflt) {
   return std::atoi(s);
 }
 
-// Choose the fused design for a problem. The workgroup-local design is used when the whole head
-// fits in one workgroup's registers and the per-wave MFMA chain stays short; otherwise W
-// workgroups per group on one die: the fewest batch rows per group that fit some design, and
-// for them the largest W.
+// Predicted time of one step of the fused kernel (µs), fitted by least squares to 61 measured
+// die-local designs on ten shapes (LSTM, GRU, Elman; D 128-768; B 4-32): a base for the exchange,
+// the barrier and the gates, plus each compute wave's MFMA chain (MTW*KTW tiles) and its poll
+// words per lane (64-bit words of h it reads per round). The single-workgroup design has no
+// exchange: its base is lower and its chain runs over the whole K.
+constexpr double kStepBaseDie = 0.731, kStepBaseLocal = 0.37, kStepPerMfma = 0.0184, kStepPerPollWord = 0.0637;
+constexpr double kLaunchUs = 15.0;  // R packing, fills and the launch of one chunk
+
+double step_cost(bool local, int br, int mtw, int ktw) {
+  if (local) return kStepBaseLocal + kStepPerMfma * mtw * ktw;
+  const int np = (br * ktw * 16 + 63) / 64;
+  return kStepBaseDie + kStepPerMfma * mtw * ktw + kStepPerPollWord * np;
+}
+
+// Choose the fused design by integer constraint search. The variables are:
+//   single-workgroup or die-local; batch rows per group BR; workgroups per group W;
+//   compute waves and K split (NCW, KS), which fix the tiles and k-tiles per wave (MTW, KTW);
+//   and the number of batch chunks.
+// The constraints are:
+//   divisibility of the head's tiles and k-tiles;
+//   an instantiated kernel for the design (each fits the register file without spilling);
+//   the K-split packing's and the I/O wave's batch-row limits;
+//   co-residency: one workgroup per CU, a group's workgroups on one die.
+// The objective is the predicted time of the call: chunks x (T x step cost + launch). A batch
+// that cannot be co-resident runs as several launches over chunks of rows (rows never interact).
+// FRNN_FUSED_W / BR / NCW / KS pin variables for measurements.
 int plan_fused(const Problem& p, const DevInfo& di, FusedPlan* out) {
   const int G = gates_of(p.cell);
   const int GS = slots_of(p.cell);
@@ -176,89 +200,87 @@ int plan_fused(const Problem& p, const DevInfo& di, FusedPlan* out) {
   const int KT = p.D / KW;
   const int force_w = env_int("FRNN_FUSED_W", 0);
   const int force_br = env_int("FRNN_FUSED_BR", 0);
-  // workgroup-local
-  if (force_w <= 1) {
+  const int force_ncw = env_int("FRNN_FUSED_NCW", 0), force_ks = env_int("FRNN_FUSED_KS", 0);
+  const int T = std::max(p.T, 1);
+  FusedPlan best;
+  bool found = false;
+  auto consider = [&](FusedPlan fp, int max_groups) {
+    // the largest chunk of rows whose groups fit at once, and the chunks the batch needs
+    if (max_groups < p.N) return;
+    const long long bmax = (long long)fp.BR * (max_groups / p.N);
+    fp.chunks = (int)((p.B + bmax - 1) / bmax);
+    fp.Bc = (int)(((long long)p.B + fp.chunks - 1) / fp.chunks);
+    fp.groups = p.N * ((fp.Bc + fp.BR - 1) / fp.BR);
+    fp.cost_us = fp.chunks * (T * step_cost(fp.local, fp.BR, fp.mtw, fp.ktw) + kLaunchUs);
+    if (!fp.local) {
+      const int per_die = (fp.groups + di.n_xcd - 1) / di.n_xcd;
+      fp.slots = per_die * fp.W;
+      fp.grid = fp.slots * di.n_xcd;
+    } else {
+      fp.grid = fp.groups;
+    }
+    // ties: fewer chunks, then fewer rows per group
+    if (!found || fp.cost_us < best.cost_us - 1e-9 ||
+        (std::abs(fp.cost_us - best.cost_us) <= 1e-9 && (fp.chunks < best.chunks || (fp.chunks == best.chunks && fp.BR < best.BR)))) {
+      best = fp;
+      found = true;
+    }
+  };
+  // single-workgroup design: a whole head per workgroup, one workgroup per CU
+  if (force_w <= 1 && !force_ks) {
     for (int ncw : {4, 8}) {
+      if (force_ncw && ncw != force_ncw) continue;
       const int mtw = (TPH + ncw - 1) / ncw;
       const FusedVariant* v = find_fused(p.cell, p.r_f32, 1, ncw, 1, mtw, KT);
       if (!v) continue;
-      const int per_wave = mtw * KT;
-      // the I/O wave moves at most 64 * epl words of Wx and as many output pairs per step
+      // a long per-wave MFMA chain makes the die-local split faster (measured); keep the design
+      // for heads whose chain is short
+      if (mtw * KT > 64 && force_w != 1) continue;
       const int epl = fused_epl(true, ncw, p.cell);
       const int words_per_row = G * p.D / (p.wx_f32 ? 2 : 4);
       const int br_cap = std::min(16, std::min(64 * epl / words_per_row, 64 * epl * 2 / p.D));
-      if (br_cap < 1 || (per_wave > 64 && force_w != 1)) continue;
-      FusedPlan fp;
-      fp.v = v;
-      fp.local = 1;
-      fp.W = 1;
-      // fewest batch rows per workgroup such that the groups still fit one workgroup per CU: the
-      // per-step latency does not depend on the rows, the I/O wave's work per step does
-      int br = 1;
-      while (br < br_cap && (long long)p.N * ((p.B + br - 1) / br) > di.cus) ++br;
-      fp.BR = (force_br >= 1 && force_br <= br_cap) ? force_br : br;
-      fp.groups = p.N * ((p.B + fp.BR - 1) / fp.BR);
-      fp.ncw = ncw;
-      fp.ks = 1;
-      fp.mtw = mtw;
-      fp.ktw = KT;
-      fp.grid = fp.groups;
-      fp.lds = (size_t)fused_lds(true, p.r_f32, ncw, 1, mtw, p.D).total;
-      *out = fp;
-      return FRNN_OK;
-    }
-    if (force_w == 1) return FRNN_EUNSUPPORTED;
-  }
-  if (p.r_f32 || !di.periodic) return FRNN_EUNSUPPORTED;
-  const int slots_per_die = std::max(1, di.cus / di.n_xcd);
-  const int force_ncw = env_int("FRNN_FUSED_NCW", 0), force_ks = env_int("FRNN_FUSED_KS", 0);
-  // (compute waves, K split) in order of preference: six or eight compute waves measured faster
-  // than four (D=768: 1.26 / 1.27 / 1.46 us per step; H=512 B=32: eight 1.33, four 1.54)
-  const int cand[][2] = {{6, 6}, {8, 8}, {4, 4}, {4, 2}, {8, 4}, {4, 1}, {8, 2}};
-  // Fewest batch rows per group first (least h polled per step and fewest producers per
-  // consumer), then the most workgroups per group that fit a die (least MFMA work per CU).
-  for (int BR = 1; BR <= FUSED_DIE_MAX_BR; ++BR) {
-    if (force_br && BR != force_br) continue;
-    const int groups = p.N * ((p.B + BR - 1) / BR);
-    const int per_die = (groups + di.n_xcd - 1) / di.n_xcd;
-    for (int W = std::min(32, slots_per_die); W >= 2; --W) {
-      if (force_w > 1 && W != force_w) continue;
-      if (TPH % W || per_die * W > slots_per_die) continue;
-      const int mt_wg = TPH / W;
-      const int u_wg = mt_wg * (GS == 4 ? 4 : 16);
-      for (const auto& nk : cand) {
-        const int ncw = nk[0], ks = nk[1];
-        if ((force_ncw && ncw != force_ncw) || (force_ks && ks != force_ks)) continue;
-        const int ms = ncw / ks;
-        if (mt_wg % ms || KT % ks) continue;
-        const int mtw = mt_wg / ms, ktw = KT / ks;
-        const FusedVariant* v = find_fused(p.cell, 0, 0, ncw, ks, mtw, ktw);
-        if (!v) continue;
-        // the packed K-split partials hold BRP batch columns per tile; the polls cover that many rows
-        if (BR > fused_max_br(ks, mtw)) continue;
-        // the I/O wave moves at most 64 * epl words of Wx and as many output pairs per step
-        const int epl = fused_epl(false, ncw, p.cell);
-        if (BR * G * u_wg / (p.wx_f32 ? 2 : 4) > 64 * epl || BR * u_wg / 2 > 64 * epl) continue;
+      for (int br = 1; br <= br_cap; ++br) {
+        if (force_br && br != force_br) continue;
         FusedPlan fp;
-        fp.v = v;
-        fp.local = 0;
-        fp.W = W;
-        fp.BR = BR;
-        fp.groups = groups;
-        fp.ncw = ncw;
-        fp.ks = ks;
-        fp.mtw = mtw;
-        fp.ktw = ktw;
-        fp.n_xcd = di.n_xcd;
-        fp.slots = per_die * W;
-        fp.grid = fp.slots * di.n_xcd;
-        fp.lds = (size_t)fused_lds(false, false, ncw, ks, mtw, p.D).total;
-        *out = fp;
-        return FRNN_OK;
+        fp.v = v; fp.local = 1; fp.W = 1; fp.BR = br; fp.ncw = ncw; fp.ks = 1; fp.mtw = mtw; fp.ktw = KT;
+        fp.lds = (size_t)fused_lds(true, p.r_f32, ncw, 1, mtw, p.D).total;
+        consider(fp, di.cus);
       }
     }
   }
-  return FRNN_EUNSUPPORTED;
+  // die-local design: W workgroups per group on one die
+  if (!p.r_f32 && di.periodic && force_w != 1) {
+    const int slots_per_die = std::max(1, di.cus / di.n_xcd);
+    const int cand[][2] = {{4, 1}, {4, 2}, {4, 4}, {6, 6}, {8, 2}, {8, 4}, {8, 8}};
+    for (int BR = 1; BR <= FUSED_DIE_MAX_BR; ++BR) {
+      if (force_br && BR != force_br) continue;
+      for (int W = 2; W <= std::min(32, slots_per_die); ++W) {
+        if ((force_w > 1 && W != force_w) || TPH % W) continue;
+        const int mt_wg = TPH / W;
+        const int u_wg = mt_wg * (GS == 4 ? 4 : 16);
+        for (const auto& nk : cand) {
+          const int ncw = nk[0], ks = nk[1];
+          if ((force_ncw && ncw != force_ncw) || (force_ks && ks != force_ks)) continue;
+          const int ms = ncw / ks;
+          if (mt_wg % ms || KT % ks) continue;
+          const int mtw = mt_wg / ms, ktw = KT / ks;
+          const FusedVariant* v = find_fused(p.cell, 0, 0, ncw, ks, mtw, ktw);
+          if (!v || BR > fused_max_br(ks, mtw)) continue;
+          // the I/O wave moves at most 64 * epl words of Wx and as many output pairs per step
+          const int epl = fused_epl(false, ncw, p.cell);
+          if (BR * G * u_wg / (p.wx_f32 ? 2 : 4) > 64 * epl || BR * u_wg / 2 > 64 * epl) continue;
+          FusedPlan fp;
+          fp.v = v; fp.local = 0; fp.W = W; fp.BR = BR; fp.ncw = ncw; fp.ks = ks; fp.mtw = mtw; fp.ktw = ktw;
+          fp.n_xcd = di.n_xcd;
+          fp.lds = (size_t)fused_lds(false, false, ncw, ks, mtw, p.D).total;
+          consider(fp, (slots_per_die / W) * di.n_xcd);
+        }
+      }
+    }
+  }
+  if (!found) return FRNN_EUNSUPPORTED;
+  *out = best;
+  return FRNN_OK;
 }
 
 // Scratch needed by the recurrence of a problem on a path, beside the error word (independent
@@ -347,10 +369,10 @@ std::string plan_string(const Problem& p, int path, const FusedPlan* fp) {
   if (path == FRNN_PATH_FUSED && fp) {
     std::snprintf(buf, sizeof(buf),
                   "fused design=%s cell=%s dtype=%s B=%d T=%d N=%d D=%d BR=%d groups=%d W=%d NCW=%d KS=%d MTW=%d KTW=%d "
-                  "dies=%d slots/die=%d grid=%d lds=%zu",
+                  "dies=%d slots/die=%d grid=%d lds=%zu chunks=%d rows/chunk=%d predicted_us=%.1f",
                   fp->local ? "workgroup-local" : "die-local", cell_name(p.cell),
                   p.r_f32 ? "f32" : "bf16", p.B, p.T, p.N, p.D, fp->BR, fp->groups, fp->W, fp->ncw, fp->ks, fp->mtw, fp->ktw,
-                  fp->n_xcd, fp->slots, fp->grid, fp->lds);
+                  fp->n_xcd, fp->slots, fp->grid, fp->lds, fp->chunks, fp->Bc, fp->cost_us);
   } else {
     const int TPH = slots_of(p.cell) * p.D / 16;
     std::snprintf(buf, sizeof(buf),
@@ -375,44 +397,60 @@ int run_recurrence(const Problem& p, int path, int* err, void* scratch, hipStrea
     trace("[frnn] %s\n", plan_string(p, path, &fp));
     const size_t rbytes = align256((size_t)slots_of(p.cell) * p.N * p.D * p.D * (p.r_f32 ? 4 : 2));
     char* xw = base + rbytes;
-    const size_t xbytes = fp.local ? 0 : (size_t)fp.groups * 2 * fp.BR * p.D * 4;
     if (!p.r_f32 && launch_rpack(p, base, st) != hipSuccess) return FRNN_EHIP;
-    // exchange words start with tag 0xFFFF, which no step before 65535 polls for (by then every
-    // word has been overwritten)
-    if (launch_fill(xw, xbytes, st, 0xFFFFu) != hipSuccess) return FRNN_EHIP;
-    FusedArgs a;
-    std::memset(&a, 0, sizeof(a));
-    a.B = p.B; a.T = p.T; a.N = p.N; a.D = p.D;
-    a.BR = fp.BR; a.groups = fp.groups; a.W = fp.W; a.n_xcd = fp.n_xcd;
-    a.check_xcc = fp.local ? 0 : 1;
-    a.xcc_of = 0;
-    for (int d = 0; d < kMaxDies; ++d) a.xcc_of |= (uint32_t)(di.xcc_of[d] & 0xF) << (4 * d);
-    a.Wx = p.Wx; a.wx_f32 = p.wx_f32; a.wx_sb = p.wx_sb; a.wx_st = p.wx_st;
-    a.R = p.R; a.r_sg = p.r_sg; a.r_sn = p.r_sn; a.r_sd = p.r_sd; a.bias = p.bias;
-    a.s0_h = p.s0_h; a.s0_c = p.s0_c; a.s0_f32 = p.s0_f32; a.s0_sb = p.s0_sb;
-    a.out_h = p.out_h; a.out_c = p.out_c; a.out_sb = p.out_sb; a.out_st = p.out_st;
-    a.last_h = p.last_h; a.last_c = p.last_c; a.last_sb = p.last_sb;
-    a.rpack = base;
-    a.xbuf = reinterpret_cast<uint32_t*>(xw);
-    a.err = err;
-    a.timeout_ticks = (long long)env_int("FRNN_TIMEOUT_MS", 2000) * di.wall_khz;
-#ifdef FRNN_PHASE_TRACE
-    if (const char* tp = std::getenv("FRNN_TRACE_PTR")) a.trace = reinterpret_cast<long long*>(std::strtoull(tp, nullptr, 0));
-    a.trace_slots = env_int("FRNN_TRACE_SLOTS", 0);  // no slot, no trace store
-#endif
     const void* fn = reinterpret_cast<const void*>(fp.v->fn);
     if (fp.lds > 48 * 1024) {
       if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)fp.lds) != hipSuccess) return FRNN_EHIP;
     }
-    void* args[] = {&a};
-    hipError_t e;
-    if (fp.local) {
-      e = hipLaunchKernel(fn, dim3(fp.grid), dim3(fused_threads(fp.ncw)), args, fp.lds, st);
-    } else {
-      e = hipLaunchCooperativeKernel(fn, dim3(fp.grid), dim3(fused_threads(fp.ncw)), args, (unsigned)fp.lds, st);
-      if (e == hipErrorCooperativeLaunchTooLarge) return FRNN_ENORESIDENT;
+    const size_t wx_elt = p.wx_f32 ? 4 : 2, s0_elt = p.s0_f32 ? 4 : 2;
+    // the batch in chunks of at most Bc rows, one launch each (rows never interact)
+    for (int b0 = 0; b0 < p.B; b0 += fp.Bc) {
+      const int Bch = std::min(fp.Bc, p.B - b0);
+      const int groups = p.N * ((Bch + fp.BR - 1) / fp.BR);
+      int grid = groups;
+      if (!fp.local) grid = ((groups + fp.n_xcd - 1) / fp.n_xcd) * fp.W * fp.n_xcd;
+      // exchange words start with tag 0xFFFF, which no step before 65535 polls for (by then
+      // every word has been overwritten)
+      const size_t xbytes = fp.local ? 0 : (size_t)groups * 2 * fp.BR * p.D * 4;
+      if (launch_fill(xw, xbytes, st, 0xFFFFu) != hipSuccess) return FRNN_EHIP;
+      FusedArgs a;
+      std::memset(&a, 0, sizeof(a));
+      a.B = Bch; a.T = p.T; a.N = p.N; a.D = p.D;
+      a.BR = fp.BR; a.groups = groups; a.W = fp.W; a.n_xcd = fp.n_xcd;
+      a.check_xcc = fp.local ? 0 : 1;
+      a.xcc_of = 0;
+      for (int d = 0; d < kMaxDies; ++d) a.xcc_of |= (uint32_t)(di.xcc_of[d] & 0xF) << (4 * d);
+      a.Wx = reinterpret_cast<const char*>(p.Wx) + (size_t)b0 * p.wx_sb * wx_elt;
+      a.wx_f32 = p.wx_f32; a.wx_sb = p.wx_sb; a.wx_st = p.wx_st;
+      a.R = p.R; a.r_sg = p.r_sg; a.r_sn = p.r_sn; a.r_sd = p.r_sd; a.bias = p.bias;
+      a.s0_h = p.s0_h ? reinterpret_cast<const char*>(p.s0_h) + (size_t)b0 * p.s0_sb * s0_elt : nullptr;
+      a.s0_c = p.s0_c ? reinterpret_cast<const char*>(p.s0_c) + (size_t)b0 * p.s0_sb * s0_elt : nullptr;
+      a.s0_f32 = p.s0_f32; a.s0_sb = p.s0_sb;
+      a.out_h = p.out_h ? p.out_h + (size_t)b0 * p.out_sb : nullptr;
+      a.out_c = p.out_c ? p.out_c + (size_t)b0 * p.out_sb : nullptr;
+      a.out_sb = p.out_sb; a.out_st = p.out_st;
+      a.last_h = p.last_h ? p.last_h + (size_t)b0 * p.last_sb : nullptr;
+      a.last_c = p.last_c ? p.last_c + (size_t)b0 * p.last_sb : nullptr;
+      a.last_sb = p.last_sb;
+      a.rpack = base;
+      a.xbuf = reinterpret_cast<uint32_t*>(xw);
+      a.err = err;
+      a.timeout_ticks = (long long)env_int("FRNN_TIMEOUT_MS", 2000) * di.wall_khz;
+#ifdef FRNN_PHASE_TRACE
+      if (const char* tp = std::getenv("FRNN_TRACE_PTR")) a.trace = reinterpret_cast<long long*>(std::strtoull(tp, nullptr, 0));
+      a.trace_slots = env_int("FRNN_TRACE_SLOTS", 0);  // no slot, no trace store
+#endif
+      void* args[] = {&a};
+      hipError_t e;
+      if (fp.local) {
+        e = hipLaunchKernel(fn, dim3(grid), dim3(fused_threads(fp.ncw)), args, fp.lds, st);
+      } else {
+        e = hipLaunchCooperativeKernel(fn, dim3(grid), dim3(fused_threads(fp.ncw)), args, (unsigned)fp.lds, st);
+        if (e == hipErrorCooperativeLaunchTooLarge) return FRNN_ENORESIDENT;
+      }
+      if (e != hipSuccess) return FRNN_EHIP;
     }
-    return e == hipSuccess ? FRNN_OK : FRNN_EHIP;
+    return FRNN_OK;
   }
   // alternating
   trace("[frnn] %s\n", plan_string(p, path, nullptr));

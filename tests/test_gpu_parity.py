@@ -176,6 +176,17 @@ def test_forced_die_local(w, env):
     run_case(w, "fused", env=env)
 
 
+@pytest.mark.parametrize("cell", ["lstm", "gru"])
+def test_fused_batch_chunks(cell):
+    """A batch that does not fit co-resident runs as several launches over chunks of rows: the
+    chunk boundaries are invisible in the result."""
+    hw = _hw()
+    w = fi.HeadwiseWorkload(f"{cell}_chunks_B40", cell, torch.bfloat16, B=40, T=6, N=1, D=768, seed=241, s0_var=1.0)
+    plan = hw.frnn_plan_str(hw._desc(w.B, w.T, w.N, w.D, w.cell, w.dtype), "fused")
+    assert "chunks=3 " in plan, plan
+    run_case(w, "fused")
+
+
 @pytest.mark.parametrize("cell,G,S", [("lstm", 4, 2), ("gru", 3, 1)])
 def test_t0_returns_initial_state(cell, G, S):
     hw = _hw()
