@@ -504,6 +504,7 @@ struct BwdLayout {
 struct FusedBwdPlan {
   const FusedBwdVariant* v = nullptr;
   int W = 0, BR = 0, groups = 0, ncw = 0, ks = 0, mtw = 0, ktw = 0, n_xcd = 1, slots = 0, grid = 0, U = 0;
+  int chunks = 1, Bc = 0;  // the batch runs as `chunks` launches of at most Bc rows
   size_t lds = 0;
 };
 
@@ -515,13 +516,22 @@ int plan_fused_bwd(int B, int N, int D, int cell, int f32, const DevInfo& di, Fu
   const int force_w = env_int("FRNN_FUSED_BWD_W", 0), force_br = env_int("FRNN_FUSED_BWD_BR", 0);
   const int force_ncw = env_int("FRNN_FUSED_BWD_NCW", 0);
   const int cand[][2] = {{8, 8}, {6, 6}, {4, 4}, {4, 2}};
+  // Fewest launches first (a batch whose groups cannot all be co-resident runs in chunks of rows,
+  // one launch each), then fewest batch rows per group, then the widest split, then the
+  // (compute waves, K split) order above.
+  FusedBwdPlan best;
+  bool found = false;
   for (int BR = 1; BR <= FUSED_DIE_MAX_BR; ++BR) {
     if (force_br && BR != force_br) continue;
-    const int groups = N * ((B + BR - 1) / BR);
-    const int per_die = (groups + di.n_xcd - 1) / di.n_xcd;
     for (int W = std::min(32, slots_per_die); W >= 2; --W) {
       if (force_w && W != force_w) continue;
-      if (TPH % W || per_die * W > slots_per_die) continue;
+      const int max_groups = (slots_per_die / W) * di.n_xcd;
+      if (TPH % W || max_groups < N) continue;
+      const long long bmax = (long long)BR * (max_groups / N);
+      const int chunks = (int)((B + bmax - 1) / bmax);
+      const int Bc = (B + chunks - 1) / chunks;
+      const int groups = N * ((Bc + BR - 1) / BR);
+      const int per_die = (groups + di.n_xcd - 1) / di.n_xcd;
       const int mt_wg = TPH / W, U = mt_wg * 16;
       // the I/O wave moves at most 64 * BWD_EPL_IN record words and 64 * BWD_EPL_OUT output words
       if (BR * U * BWD_REC / 2 > 64 * BWD_EPL_IN || BR * U > 64 * BWD_EPL_OUT) continue;
@@ -533,16 +543,21 @@ int plan_fused_bwd(int B, int N, int D, int cell, int f32, const DevInfo& di, Fu
         const int mtw = mt_wg / ms, ktw = KT / ks;
         const FusedBwdVariant* v = find_fused_bwd(cell, ncw, ks, mtw, ktw);
         if (!v || BR > fused_max_br(ks, mtw)) continue;
+        if (found && chunks >= best.chunks) continue;  // earlier candidates win ties
         FusedBwdPlan fp;
         fp.v = v; fp.W = W; fp.BR = BR; fp.groups = groups; fp.ncw = ncw; fp.ks = ks; fp.mtw = mtw; fp.ktw = ktw;
         fp.n_xcd = di.n_xcd; fp.slots = per_die * W; fp.grid = fp.slots * di.n_xcd; fp.U = U;
+        fp.chunks = chunks; fp.Bc = Bc;
         fp.lds = (size_t)fused_bwd_lds(ncw, ks, ktw, BR, U).total;
-        *out = fp;
-        return FRNN_OK;
+        best = fp;
+        found = true;
+        break;
       }
     }
   }
-  return FRNN_EUNSUPPORTED;
+  if (!found) return FRNN_EUNSUPPORTED;
+  *out = best;
+  return FRNN_OK;
 }
 
 BwdLayout bwd_layout(int B, int T, int N, int D, int cell, int f32, int path) {
@@ -577,9 +592,9 @@ std::string bwd_plan_string(const frnn_desc* d, int path, const FusedBwdPlan* fp
   if (path == FRNN_PATH_FUSED && fp) {
     std::snprintf(buf, sizeof(buf),
                   "backward path=fused design=die-local cell=%s dtype=bf16 B=%d T=%d N=%d D=%d BR=%d groups=%d W=%d "
-                  "NCW=%d KS=%d MTW=%d KTW=%d dies=%d slots/die=%d grid=%d lds=%zu",
+                  "NCW=%d KS=%d MTW=%d KTW=%d dies=%d slots/die=%d grid=%d lds=%zu chunks=%d rows/chunk=%d",
                   cell_name(d->cell), d->B, d->T, d->N, d->D, fp->BR, fp->groups, fp->W, fp->ncw, fp->ks, fp->mtw,
-                  fp->ktw, fp->n_xcd, fp->slots, fp->grid, fp->lds);
+                  fp->ktw, fp->n_xcd, fp->slots, fp->grid, fp->lds, fp->chunks, fp->Bc);
     return std::string(buf);
   }
   const int G = gates_of(d->cell);
@@ -603,27 +618,33 @@ int run_fused_bwd(const frnn_desc* d, const BwdArgs& a, const FusedBwdPlan& fp, 
   if (d->cell == FRNN_CELL_LSTM) hipLaunchKernelGGL((bwd_record_kernel<CELL_LSTM, false>), dim3(pgrid), dim3(256), 0, st, a, rec);
   else if (d->cell == FRNN_CELL_GRU) hipLaunchKernelGGL((bwd_record_kernel<CELL_GRU, false>), dim3(pgrid), dim3(256), 0, st, a, rec);
   else hipLaunchKernelGGL((bwd_record_kernel<CELL_ELMAN, false>), dim3(pgrid), dim3(256), 0, st, a, rec);
-  const size_t xbytes = (size_t)fp.groups * 2 * fp.BR * gates_of(d->cell) * a.D * 4;
-  if (launch_fill(base + L.xbuf, xbytes, st, 0xFFFFu) != hipSuccess) return FRNN_EHIP;
-  FusedBwdArgs f;
-  std::memset(&f, 0, sizeof(f));
-  f.B = a.B; f.T = a.T; f.N = a.N; f.D = a.D;
-  f.BR = fp.BR; f.groups = fp.groups; f.W = fp.W; f.n_xcd = fp.n_xcd; f.check_xcc = 1;
-  f.xcc_of = 0;
-  for (int k = 0; k < kMaxDies; ++k) f.xcc_of |= (uint32_t)(di.xcc_of[k] & 0xF) << (4 * k);
-  f.rpk = a.rpk;
-  f.rec = rec;
-  f.dstate = dstate;
-  f.xbuf = reinterpret_cast<uint32_t*>(base + L.xbuf);
-  f.err = reinterpret_cast<int*>(base - kErrBytes);
-  f.timeout_ticks = (long long)env_int("FRNN_TIMEOUT_MS", 2000) * di.wall_khz;
   const void* fn = reinterpret_cast<const void*>(fp.v->fn);
   if (fp.lds > 48 * 1024 && hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)fp.lds) != hipSuccess)
     return FRNN_EHIP;
-  void* args[] = {&f};
-  const hipError_t e = hipLaunchCooperativeKernel(fn, dim3(fp.grid), dim3(fused_threads(fp.ncw)), args, (unsigned)fp.lds, st);
-  if (e == hipErrorCooperativeLaunchTooLarge) return FRNN_ENORESIDENT;
-  if (e != hipSuccess) return FRNN_EHIP;
+  // the batch in chunks of at most Bc rows, one launch each (rows never interact)
+  for (int b0 = 0; b0 < a.B; b0 += fp.Bc) {
+    const int Bch = std::min(fp.Bc, a.B - b0);
+    const int groups = a.N * ((Bch + fp.BR - 1) / fp.BR);
+    const int grid = ((groups + fp.n_xcd - 1) / fp.n_xcd) * fp.W * fp.n_xcd;
+    const size_t xbytes = (size_t)groups * 2 * fp.BR * gates_of(d->cell) * a.D * 4;
+    if (launch_fill(base + L.xbuf, xbytes, st, 0xFFFFu) != hipSuccess) return FRNN_EHIP;
+    FusedBwdArgs f;
+    std::memset(&f, 0, sizeof(f));
+    f.B = Bch; f.Bs = a.B; f.T = a.T; f.N = a.N; f.D = a.D;
+    f.BR = fp.BR; f.groups = groups; f.W = fp.W; f.n_xcd = fp.n_xcd; f.check_xcc = 1;
+    f.xcc_of = 0;
+    for (int k = 0; k < kMaxDies; ++k) f.xcc_of |= (uint32_t)(di.xcc_of[k] & 0xF) << (4 * k);
+    f.rpk = a.rpk;
+    f.rec = rec + (size_t)b0 * a.N * a.D * BWD_REC;
+    f.dstate = dstate + (size_t)b0 * a.N * a.D * 2;
+    f.xbuf = reinterpret_cast<uint32_t*>(base + L.xbuf);
+    f.err = reinterpret_cast<int*>(base - kErrBytes);
+    f.timeout_ticks = (long long)env_int("FRNN_TIMEOUT_MS", 2000) * di.wall_khz;
+    void* args[] = {&f};
+    const hipError_t e = hipLaunchCooperativeKernel(fn, dim3(grid), dim3(fused_threads(fp.ncw)), args, (unsigned)fp.lds, st);
+    if (e == hipErrorCooperativeLaunchTooLarge) return FRNN_ENORESIDENT;
+    if (e != hipSuccess) return FRNN_EHIP;
+  }
   if (d->cell == FRNN_CELL_LSTM) hipLaunchKernelGGL((bwd_post_kernel<CELL_LSTM, false>), dim3(pgrid), dim3(256), 0, st, a, rec, dstate);
   else if (d->cell == FRNN_CELL_GRU) hipLaunchKernelGGL((bwd_post_kernel<CELL_GRU, false>), dim3(pgrid), dim3(256), 0, st, a, rec, dstate);
   else hipLaunchKernelGGL((bwd_post_kernel<CELL_ELMAN, false>), dim3(pgrid), dim3(256), 0, st, a, rec, dstate);

@@ -36,7 +36,8 @@ constexpr int BWD_EPL_IN = 8;   // 64-bit record words one I/O lane moves per st
 constexpr int BWD_EPL_OUT = 2;  // 64-bit (dh, dc) words one I/O lane moves per step (at most)
 
 struct FusedBwdArgs {
-  int B, T, N, D;
+  int B, T, N, D;    // B: the rows of this launch (a chunk of the batch)
+  int Bs;            // rows of the record and output arrays (their step stride)
   int BR, groups, W, n_xcd, check_xcc;
   uint32_t xcc_of;
   const void* rpk;   // R as A fragments: [N][D/16][G*D/32][64] x 8 bf16 (bwd_rpack_kernel)
@@ -214,10 +215,10 @@ __global__ void __launch_bounds__((NCW + 1) * 64, 1) fused_bwd_kernel(FusedBwdAr
     c.rec = reinterpret_cast<const char*>(a.rec);
     c.dst = a.dstate;
     c.in_row = (long long)N * D * BWD_REC;
-    c.in_step = (long long)a.B * N * D * BWD_REC;
+    c.in_step = (long long)a.Bs * N * D * BWD_REC;
     c.in_base = ((long long)b0 * N + n) * D * BWD_REC + (long long)u_base * BWD_REC;
     c.out_row = (long long)N * D * 2;
-    c.out_step = (long long)a.B * N * D * 2;
+    c.out_step = (long long)a.Bs * N * D * 2;
     c.out_base = ((long long)b0 * N + n) * D * 2 + (long long)u_base * 2;
     c.nvalid = nvalid;
     c.U = U;

@@ -107,12 +107,26 @@ def test_bwd_small(w, path):
 
 @pytest.mark.parametrize("path", ["alternating", "fused"])
 @pytest.mark.parametrize("name", ["lstm_bf16_B16_T1024_N1_D768", "lstm_bf16_B8_T1024_N3_D256",
-                                  "gru_bf16_B16_T1024_N1_D768", "lstm_f32_B2_T16_N1_D32"])
+                                  "gru_bf16_B16_T1024_N1_D768", "lstm_f32_B2_T16_N1_D32",
+                                  "elman_bf16_B64_T2048_N12_D64"])
 def test_bwd_full(name, path):
     w = fi.get_workload(name)
     if path == "fused":
         _fused_plan_or_skip(w)
     run_bwd_case(w, path)
+
+
+@pytest.mark.parametrize("w,chunks", [
+    (fi.HeadwiseWorkload("bwd_gru_chunks_B40", "gru", torch.bfloat16, B=40, T=8, N=1, D=768, seed=251, s0_var=1.0), 3),
+    (fi.HeadwiseWorkload("bwd_lstm_chunks_B40", "lstm", torch.bfloat16, B=40, T=6, N=1, D=768, seed=252, s0_var=1.0), 3),
+    (fi.HeadwiseWorkload("bwd_elman_chunks_B64_N12", "elman", torch.bfloat16, B=64, T=16, N=12, D=64, seed=253,
+                         s0_var=1.0), 2),
+], ids=lambda x: getattr(x, "name", str(x)))
+def test_bwd_fused_chunks(w, chunks):
+    """A batch whose groups cannot all be co-resident runs the fused serial part in chunks of rows."""
+    plan = _fused_plan_or_skip(w)
+    assert f"chunks={chunks} " in plan, plan
+    run_bwd_case(w, "fused")
 
 
 def test_bwd_fused_matches_alternating():
