@@ -651,4 +651,40 @@ def pin_bwd_t0(orc):
         np.testing.assert_array_equal(ds0, dlast)
 
 
+def pin_bwd_torch_lstm_stack(orc):
+    """The multi-layer backward equals torch autograd through a float64 two-layer torch.nn.LSTM
+    (the module whose state_dict the "5.3 LSTM" page reads), for every gradient: x, Wi, Wh,
+    both biases, h0 and c0."""
+    import oracle as _o
+    T, B, I, H, L = 6, 3, 5, 4, 2
+    m = _torch_lstm(I, H, L, 71)
+    rng = np.random.default_rng(71)
+    x = rng.normal(size=(T, B, I))
+    h0 = rng.normal(size=(L, B, H)) * 0.5
+    c0 = rng.normal(size=(L, B, H)) * 0.5
+    dout = rng.normal(size=(T, B, H))
+    dhn = rng.normal(size=(L, B, H))
+    dcn = rng.normal(size=(L, B, H))
+    xt = torch.tensor(x, requires_grad=True)
+    h0t = torch.tensor(h0, requires_grad=True)
+    c0t = torch.tensor(c0, requires_grad=True)
+    out, (hn, cn) = m(xt, (h0t, c0t))
+    loss = (out * torch.from_numpy(dout)).sum() + (hn * torch.from_numpy(dhn)).sum() + (cn * torch.from_numpy(dcn)).sum()
+    loss.backward()
+    sd = m.state_dict()
+    Wi = [sd[f"weight_ih_l{l}"].numpy().T for l in range(L)]
+    Wh = [sd[f"weight_hh_l{l}"].numpy().T for l in range(L)]
+    bi = [sd[f"bias_ih_l{l}"].numpy() for l in range(L)]
+    bh = [sd[f"bias_hh_l{l}"].numpy() for l in range(L)]
+    dx, dWi, dWh, dbi, dbh, dh0, dc0 = _o.lstm_stack_bwd(orc, x, Wi, Wh, bi, bh, h0, c0, dout, dhn, dcn)
+    np.testing.assert_allclose(dx, xt.grad.numpy(), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dh0, h0t.grad.numpy(), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dc0, c0t.grad.numpy(), rtol=0, atol=1e-12)
+    for l in range(L):
+        np.testing.assert_allclose(dWi[l], getattr(m, f"weight_ih_l{l}").grad.numpy().T, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(dWh[l], getattr(m, f"weight_hh_l{l}").grad.numpy().T, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(dbi[l], getattr(m, f"bias_ih_l{l}").grad.numpy(), rtol=0, atol=1e-12)
+        np.testing.assert_allclose(dbh[l], getattr(m, f"bias_hh_l{l}").grad.numpy(), rtol=0, atol=1e-12)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
