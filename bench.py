@@ -231,10 +231,23 @@ def main():
             hw.frnn_lstm_stack_fwd(g["x"], g["Wi"], g["Wh"], g["b_ih"], g["b_hh"], g["h0"], g["c0"], path=args.path,
                                    out=out, workspace=ws, check=False)
         flops = 2.0 * w.B * 4 * w.H * w.H * w.T * w.L  # recurrent contraction of all layers
+        if args.backward:
+            ct = {k: v.to(dev) for k, v in fi.stack_cotangents(w).items()}
+            ws = torch.empty(hw.frnn_lstm_stack_bwd_workspace_bytes(w.L, w.T, w.B, w.I, w.H, args.path),
+                             dtype=torch.uint8, device=dev)
+
+            def step():
+                hw.frnn_lstm_stack_bwd(g["x"], g["Wi"], g["Wh"], g["b_ih"], g["b_hh"], g["h0"], g["c0"], ct["dout"],
+                                       ct["dhn"], ct["dcn"], path=args.path, workspace=ws, check=False)
+            # forward again (recurrent contraction) + per layer the serial da.R^T, the h.R recompute
+            # and the dR GEMM; the projections' GEMMs (forward, dWi, dX) are reported separately
+            flops = 4.0 * flops
         nbytes = 0.0
         timesteps = w.T * w.L
         config = {"workload": w.name, "L": w.L, "T": w.T, "B": w.B, "I": w.I, "H": w.H, "path": args.path,
-                  "projection_gflop": 2.0 * w.T * w.B * 4 * w.H * (w.I + w.H * (w.L - 1)) / 1e9}
+                  "projection_gflop": (3.0 if args.backward else 1.0) * 2.0 * w.T * w.B * 4 * w.H *
+                  (w.I + w.H * (w.L - 1)) / 1e9,
+                  "pass": "backward" if args.backward else "forward"}
         dtype = "bf16"
 
     for _ in range(args.warmup):

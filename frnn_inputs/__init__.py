@@ -125,6 +125,17 @@ def backward_cotangents(w: HeadwiseWorkload):
     return {"dstates": dstates, "dlast": dlast}
 
 
+def stack_cotangents(w: StackWorkload):
+    """Gradients of the multi-layer forward's outputs: dout [T,B,H], dhn and dcn [L,B,H], float32
+    ~N(0,1), drawn in that order from a generator seeded with seed + 1000."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(w.seed + 1000)
+    dout = _normal(g, (w.T, w.B, w.H), 1.0)
+    dhn = _normal(g, (w.L, w.B, w.H), 1.0)
+    dcn = _normal(g, (w.L, w.B, w.H), 1.0)
+    return {"dout": dout, "dhn": dhn, "dcn": dcn}
+
+
 def stack_inputs(w: StackWorkload):
     """Return dict(x, Wi[], Wh[], b_ih[], b_hh[], h0, c0) of CPU tensors in ``w.dtype``."""
     g = torch.Generator(device="cpu")

@@ -19,7 +19,7 @@ __all__ = [
     "FRNN_PATH_ALTERNATING", "FRNN_PATH_FUSED", "FrnnError", "Desc", "lib_path", "load",
     "frnn_abi_version", "frnn_status_str", "frnn_workspace_bytes", "frnn_plan_str", "frnn_fwd",
     "frnn_check", "frnn_lstm_stack_workspace_bytes", "frnn_lstm_stack_fwd", "frnn_bwd_workspace_bytes",
-    "frnn_bwd_plan_str", "frnn_bwd", "flashrnn",
+    "frnn_bwd_plan_str", "frnn_bwd", "flashrnn", "frnn_lstm_stack_bwd_workspace_bytes", "frnn_lstm_stack_bwd",
 ]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -85,6 +85,13 @@ def load():
     lib.frnn_bwd.argtypes = [dptr, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.frnn_lstm_stack_workspace_bytes.restype = i32
     lib.frnn_lstm_stack_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, ctypes.POINTER(sz)]
+    lib.frnn_lstm_stack_bwd_workspace_bytes.restype = i32
+    lib.frnn_lstm_stack_bwd_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, ctypes.POINTER(sz)]
+    lib.frnn_lstm_stack_bwd.restype = i32
+    lib.frnn_lstm_stack_bwd.argtypes = [i32, i32, i32, i32, i32, i32, vp, ctypes.POINTER(vp), ctypes.POINTER(vp),
+                                        ctypes.POINTER(vp), ctypes.POINTER(vp), vp, vp, vp, vp, vp, vp,
+                                        ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.POINTER(vp),
+                                        ctypes.POINTER(vp), vp, vp, vp, sz, vp]
     lib.frnn_lstm_stack_fwd.restype = i32
     lib.frnn_lstm_stack_fwd.argtypes = [i32, i32, i32, i32, i32, i32, vp, ctypes.POINTER(vp), ctypes.POINTER(vp),
                                         ctypes.POINTER(vp), ctypes.POINTER(vp), vp, vp, vp, vp, vp, vp, sz, vp]
@@ -346,3 +353,60 @@ def frnn_lstm_stack_fwd(x: torch.Tensor, Wi: Sequence[torch.Tensor], Wh: Sequenc
     if check:
         frnn_check(workspace)
     return o, hn, cn
+
+
+def frnn_lstm_stack_bwd_workspace_bytes(L, T, B, I, H, path="fused") -> int:
+    n = ctypes.c_size_t(0)
+    rc = load().frnn_lstm_stack_bwd_workspace_bytes(L, T, B, I, H, _path(path), ctypes.byref(n))
+    if rc != FRNN_OK:
+        raise FrnnError(rc, "frnn_lstm_stack_bwd_workspace_bytes")
+    return n.value
+
+
+def frnn_lstm_stack_bwd(x: torch.Tensor, Wi: Sequence[torch.Tensor], Wh: Sequence[torch.Tensor],
+                        b_ih: Sequence[Optional[torch.Tensor]], b_hh: Sequence[Optional[torch.Tensor]],
+                        h0: Optional[torch.Tensor] = None, c0: Optional[torch.Tensor] = None,
+                        dout: Optional[torch.Tensor] = None, dhn: Optional[torch.Tensor] = None,
+                        dcn: Optional[torch.Tensor] = None, path="fused", workspace: Optional[torch.Tensor] = None,
+                        check: bool = True):
+    """Backward of frnn_lstm_stack_fwd: (dx [T,B,I], dWi[], dWh[], db_ih[], db_hh[], dh0, dc0 [L,B,H]), fp32,
+    for the loss sum(dout * out) + sum(dhn * hn) + sum(dcn * cn); dout [T,B,H], dhn, dcn [L,B,H] fp32 or None."""
+    T, B, I = x.shape
+    L = len(Wi)
+    H = Wh[0].shape[0]
+    dev, bf, f = x.device, torch.bfloat16, torch.float32
+    _check_tensor(x, "x", (T, B, I), bf, dev)
+    for l in range(L):
+        _check_tensor(Wi[l], f"Wi[{l}]", ((I if l == 0 else H), 4 * H), bf, dev)
+        _check_tensor(Wh[l], f"Wh[{l}]", (H, 4 * H), bf, dev)
+        _check_tensor(b_ih[l], f"b_ih[{l}]", (4 * H,), bf, dev)
+        _check_tensor(b_hh[l], f"b_hh[{l}]", (4 * H,), bf, dev)
+    _check_tensor(h0, "h0", (L, B, H), bf, dev)
+    _check_tensor(c0, "c0", (L, B, H), bf, dev)
+    _check_tensor(dout, "dout", (T, B, H), f, dev)
+    _check_tensor(dhn, "dhn", (L, B, H), f, dev)
+    _check_tensor(dcn, "dcn", (L, B, H), f, dev)
+    p = _path(path)
+    dx = torch.empty((T, B, I), dtype=f, device=dev)
+    dWi = [torch.empty(((I if l == 0 else H), 4 * H), dtype=f, device=dev) for l in range(L)]
+    dWh = [torch.empty((H, 4 * H), dtype=f, device=dev) for _ in range(L)]
+    dbi = [torch.empty((4 * H,), dtype=f, device=dev) for _ in range(L)]
+    dbh = [torch.empty((4 * H,), dtype=f, device=dev) for _ in range(L)]
+    dh0 = torch.empty((L, B, H), dtype=f, device=dev)
+    dc0 = torch.empty((L, B, H), dtype=f, device=dev)
+    need = frnn_lstm_stack_bwd_workspace_bytes(L, T, B, I, H, p)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    elif workspace.numel() < need:
+        raise ValueError("workspace too small")
+    arr = ctypes.c_void_p * L
+    ptrs = lambda ts: arr(*[0 if t is None else t.data_ptr() for t in ts])
+    rc = load().frnn_lstm_stack_bwd(
+        L, T, B, I, H, p, _ptr(x), ptrs(Wi), ptrs(Wh), ptrs(b_ih), ptrs(b_hh), _ptr(h0), _ptr(c0), _ptr(dout),
+        _ptr(dhn), _ptr(dcn), _ptr(dx), ptrs(dWi), ptrs(dWh), ptrs(dbi), ptrs(dbh), _ptr(dh0), _ptr(dc0),
+        _ptr(workspace), workspace.numel(), _stream_handle(dev))
+    if rc != FRNN_OK:
+        raise FrnnError(rc, "frnn_lstm_stack_bwd")
+    if check:
+        frnn_check(workspace)
+    return dx, dWi, dWh, dbi, dbh, dh0, dc0

@@ -337,7 +337,7 @@ void launch_transpose(const E* src, long long lds, int K, int Nc, E* dst, long l
 // MFMA kernel for fp32 ones. K is a multiple of 32.
 hipError_t launch_gemm(bool f32, int M, int Nc, int K, const void* A, long long lda, const void* Bt, long long ldb,
                        float* C, long long ldc, hipStream_t st, int parts = 1, long long a_z = 0, long long b_z = 0,
-                       long long c_z = 0) {
+                       long long c_z = 0, bool a_f32 = false) {
   if (M <= 0 || Nc <= 0) return hipSuccess;
   if (K % 32 != 0 || parts < 1) return hipErrorInvalidValue;
   if (f32) {
@@ -349,14 +349,15 @@ hipError_t launch_gemm(bool f32, int M, int Nc, int K, const void* A, long long 
   }
   ProjArgs pa;
   pa.M = M; pa.Nc = Nc; pa.K = K;
-  pa.A = A; pa.a_f32 = 0; pa.lda = lda;
+  pa.A = A; pa.a_f32 = a_f32 ? 1 : 0; pa.lda = lda;
   pa.Bt = reinterpret_cast<const uint16_t*>(Bt);
   pa.ldb = ldb;
   pa.b1 = nullptr; pa.b2 = nullptr;
   pa.C = C; pa.ldc = ldc;
   pa.a_z = a_z; pa.b_z = b_z; pa.c_z = c_z;
   const dim3 pgrid(((Nc + PJ_BN - 1) / PJ_BN) * ((M + PJ_BM - 1) / PJ_BM), parts);
-  hipLaunchKernelGGL(proj_gemm_kernel<false>, pgrid, dim3(256), 0, st, pa);
+  if (a_f32) hipLaunchKernelGGL(proj_gemm_kernel<true>, pgrid, dim3(256), 0, st, pa);  // A rounded to bf16 as staged
+  else hipLaunchKernelGGL(proj_gemm_kernel<false>, pgrid, dim3(256), 0, st, pa);
   return hipGetLastError();
 }
 
@@ -608,16 +609,39 @@ std::string bwd_plan_string(const frnn_desc* d, int path, const FusedBwdPlan* fp
   return std::string(buf);
 }
 
+// Launch bwd_gate_kernel (step t) or bwd_record_kernel (rec) instantiated for the cell, the
+// operand dtype and the Wx dtype.
+enum BwdCellKernel { kBwdGate, kBwdRecord };
+
+template <int CELL, bool F32, bool WXF32>
+void launch_bwd_cell_kernel_t(BwdCellKernel k, dim3 grid, dim3 block, hipStream_t st, const BwdArgs& a, int t, float* rec) {
+  if (k == kBwdGate) hipLaunchKernelGGL((bwd_gate_kernel<CELL, F32, WXF32>), grid, block, 0, st, a, t);
+  else hipLaunchKernelGGL((bwd_record_kernel<CELL, F32, WXF32>), grid, block, 0, st, a, rec);
+}
+
+template <int CELL>
+void launch_bwd_cell_kernel_c(BwdCellKernel k, bool f32, bool wx_f32, dim3 grid, dim3 block, hipStream_t st,
+                              const BwdArgs& a, int t, float* rec) {
+  if (f32) launch_bwd_cell_kernel_t<CELL, true, true>(k, grid, block, st, a, t, rec);  // fp32 inputs: Wx fp32 too
+  else if (wx_f32) launch_bwd_cell_kernel_t<CELL, false, true>(k, grid, block, st, a, t, rec);
+  else launch_bwd_cell_kernel_t<CELL, false, false>(k, grid, block, st, a, t, rec);
+}
+
+void launch_bwd_cell_kernel(BwdCellKernel k, int cell, bool f32, bool wx_f32, dim3 grid, dim3 block, hipStream_t st,
+                            const BwdArgs& a, int t, float* rec) {
+  if (cell == FRNN_CELL_LSTM) launch_bwd_cell_kernel_c<CELL_LSTM>(k, f32, wx_f32, grid, block, st, a, t, rec);
+  else if (cell == FRNN_CELL_GRU) launch_bwd_cell_kernel_c<CELL_GRU>(k, f32, wx_f32, grid, block, st, a, t, rec);
+  else launch_bwd_cell_kernel_c<CELL_ELMAN>(k, f32, wx_f32, grid, block, st, a, t, rec);
+}
+
 // The fused serial part: records of every step, the persistent kernel, then dWx / da / carries.
-int run_fused_bwd(const frnn_desc* d, const BwdArgs& a, const FusedBwdPlan& fp, const DevInfo& di, char* base,
+int run_fused_bwd(int cell, const BwdArgs& a, const FusedBwdPlan& fp, const DevInfo& di, char* base,
                   const BwdLayout& L, hipStream_t st) {
   const long long total = (long long)a.T * a.B * a.N * a.D;
   const unsigned pgrid = (unsigned)((total + 255) / 256);
   float* rec = reinterpret_cast<float*>(base + L.rec);
   float* dstate = reinterpret_cast<float*>(base + L.dstate);
-  if (d->cell == FRNN_CELL_LSTM) hipLaunchKernelGGL((bwd_record_kernel<CELL_LSTM, false>), dim3(pgrid), dim3(256), 0, st, a, rec);
-  else if (d->cell == FRNN_CELL_GRU) hipLaunchKernelGGL((bwd_record_kernel<CELL_GRU, false>), dim3(pgrid), dim3(256), 0, st, a, rec);
-  else hipLaunchKernelGGL((bwd_record_kernel<CELL_ELMAN, false>), dim3(pgrid), dim3(256), 0, st, a, rec);
+  launch_bwd_cell_kernel(kBwdRecord, cell, false, a.wx_f32, dim3(pgrid), dim3(256), st, a, 0, rec);
   const void* fn = reinterpret_cast<const void*>(fp.v->fn);
   if (fp.lds > 48 * 1024 && hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)fp.lds) != hipSuccess)
     return FRNN_EHIP;
@@ -626,7 +650,7 @@ int run_fused_bwd(const frnn_desc* d, const BwdArgs& a, const FusedBwdPlan& fp, 
     const int Bch = std::min(fp.Bc, a.B - b0);
     const int groups = a.N * ((Bch + fp.BR - 1) / fp.BR);
     const int grid = ((groups + fp.n_xcd - 1) / fp.n_xcd) * fp.W * fp.n_xcd;
-    const size_t xbytes = (size_t)groups * 2 * fp.BR * gates_of(d->cell) * a.D * 4;
+    const size_t xbytes = (size_t)groups * 2 * fp.BR * gates_of(cell) * a.D * 4;
     if (launch_fill(base + L.xbuf, xbytes, st, 0xFFFFu) != hipSuccess) return FRNN_EHIP;
     FusedBwdArgs f;
     std::memset(&f, 0, sizeof(f));
@@ -645,11 +669,149 @@ int run_fused_bwd(const frnn_desc* d, const BwdArgs& a, const FusedBwdPlan& fp, 
     if (e == hipErrorCooperativeLaunchTooLarge) return FRNN_ENORESIDENT;
     if (e != hipSuccess) return FRNN_EHIP;
   }
-  if (d->cell == FRNN_CELL_LSTM) hipLaunchKernelGGL((bwd_post_kernel<CELL_LSTM, false>), dim3(pgrid), dim3(256), 0, st, a, rec, dstate);
-  else if (d->cell == FRNN_CELL_GRU) hipLaunchKernelGGL((bwd_post_kernel<CELL_GRU, false>), dim3(pgrid), dim3(256), 0, st, a, rec, dstate);
+  if (cell == FRNN_CELL_LSTM) hipLaunchKernelGGL((bwd_post_kernel<CELL_LSTM, false>), dim3(pgrid), dim3(256), 0, st, a, rec, dstate);
+  else if (cell == FRNN_CELL_GRU) hipLaunchKernelGGL((bwd_post_kernel<CELL_GRU, false>), dim3(pgrid), dim3(256), 0, st, a, rec, dstate);
   else hipLaunchKernelGGL((bwd_post_kernel<CELL_ELMAN, false>), dim3(pgrid), dim3(256), 0, st, a, rec, dstate);
   return hipGetLastError() == hipSuccess ? FRNN_OK : FRNN_EHIP;
 }
+
+// A backward problem with explicit element strides: G gates of N heads of D units; the gates of
+// Wx and dWx lie N*D elements apart; dstates shares the states' strides.
+struct BwdProblem {
+  int B, T, N, D, cell;
+  int f32;     // R, bias, initial states and the MFMA operands fp32 (else bf16)
+  int wx_f32;  // Wx fp32 (else as f32)
+  const void* Wx;
+  long long wx_sb, wx_st;
+  const void* R;
+  long long r_sg, r_sn, r_sd;
+  const void* bias;
+  const void* s0_h;
+  const void* s0_c;
+  long long s0_sb;
+  const float* st_h;
+  const float* st_c;
+  long long st_sb, st_st;
+  const float* ds_h;
+  const float* ds_c;
+  const float* dl_h;
+  const float* dl_c;
+  long long last_sb;
+  float* dWx;
+  float* dR;
+  long long dr_sg, dr_sn, dr_sd;
+  float* db;     // [G][N][D]
+  float* ds0_h;  // [B][N][D]
+  float* ds0_c;
+};
+
+// The backward of a validated problem with T > 0 on `path` (the fused plan given for the fused
+// path). `base` is the workspace after its error word, laid out as L.
+int run_backward(const BwdProblem& q, int path, const FusedBwdPlan& fbp, const DevInfo& di, char* base,
+                 const BwdLayout& L, hipStream_t st) {
+  const int B = q.B, T = q.T, N = q.N, D = q.D, G = gates_of(q.cell), f32 = q.f32;
+  const long long BND = (long long)B * N * D;
+  const size_t elt = f32 ? 4 : 2;
+  const unsigned sgrid = (unsigned)((BND + 255) / 256);
+  int rc = FRNN_OK;
+  const int Kp = (int)bwd_kp(T, B);
+  BwdArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.B = B; a.T = T; a.N = N; a.D = D; a.cell = q.cell; a.f32 = f32; a.wx_f32 = f32 || q.wx_f32; a.Kp = Kp;
+  a.Wx = q.Wx; a.wx_sb = q.wx_sb; a.wx_st = q.wx_st;
+  a.R = q.R; a.r_sg = q.r_sg; a.r_sn = q.r_sn; a.r_sd = q.r_sd;
+  a.bias = q.bias;
+  a.s0_h = q.s0_h; a.s0_c = q.s0_c; a.s0_sb = q.s0_sb;
+  a.st_h = q.st_h; a.st_c = q.st_c; a.st_sb = q.st_sb; a.st_st = q.st_st;
+  a.ds_h = q.ds_h; a.ds_c = q.ds_c;
+  a.dl_h = q.dl_h; a.dl_c = q.dl_c; a.last_sb = q.last_sb;
+  a.dWx = q.dWx;
+  a.ds0_h = q.ds0_h; a.ds0_c = q.ds0_c;
+  a.hprev = base + L.hprev;
+  a.hr = reinterpret_cast<const float*>(base + L.hr);
+  a.da = base + L.da;
+  a.zeros = reinterpret_cast<const float*>(base + L.zeros);
+  a.rpk = base + L.rpk;
+  a.dhpart = reinterpret_cast<float*>(base + L.dhpart);
+  a.ks = std::min(BWD_KS, G * D / (f32 ? 4 : 32));
+  a.carry = reinterpret_cast<float*>(base + L.carry);
+  char* hT = base + L.hprevT;
+  char* rt = base + L.rt;
+  char* daT = base + L.daT;
+  float* tmp = reinterpret_cast<float*>(base + L.tmp);
+  float* hr = reinterpret_cast<float*>(base + L.hr);
+  // carried gradients start at zero; da's rows past T*B stay zero for the dR GEMM
+  if (launch_fill(base + L.zeros, 256, st) != hipSuccess ||
+      launch_fill(a.dhpart, (size_t)BWD_KS * BND * 4, st) != hipSuccess || launch_fill(a.carry, (size_t)BND * 4, st) != hipSuccess ||
+      launch_fill(a.da, (size_t)N * Kp * G * D * elt, st) != hipSuccess)
+    return FRNN_EHIP;
+  // 1. h_{t-1} for every step, R^T, and h.R for every step
+  hipLaunchKernelGGL(bwd_hprev_kernel, dim3((unsigned)std::min<long long>(((long long)N * Kp * D + 255) / 256, 65536)),
+                     dim3(256), 0, st, a);
+  for (int n = 0; n < N; ++n) {
+    for (int g = 0; g < G; ++g) {
+      const size_t src = (size_t)g * a.r_sg + (size_t)n * a.r_sn, dst = ((size_t)n * G + g) * D * D;
+      if (f32) launch_transpose<uint32_t>(reinterpret_cast<const uint32_t*>(q.R) + src, a.r_sd, D, D, reinterpret_cast<uint32_t*>(rt) + dst, D, st);
+      else launch_transpose<uint16_t>(reinterpret_cast<const uint16_t*>(q.R) + src, a.r_sd, D, D, reinterpret_cast<uint16_t*>(rt) + dst, D, st);
+    }
+    if (launch_gemm(f32, T * B, G * D, D, base + L.hprev + (size_t)n * Kp * D * elt, D, rt + (size_t)n * G * D * D * elt, D,
+                    hr + (size_t)n * T * B * G * D, (long long)G * D, st) != hipSuccess)
+      return FRNN_EHIP;
+  }
+  // 2. the serial part (R packed once as the dh kernels' A fragments)
+  {
+    const long long np = (long long)N * (D / 16) * (G * D / (f32 ? 4 : 32)) * 64;
+    hipLaunchKernelGGL(bwd_rpack_kernel, dim3((unsigned)std::min<long long>((np + 255) / 256, 65536)), dim3(256), 0, st, a,
+                       (void*)(base + L.rpk));
+  }
+  const dim3 hgrid(D / 16, a.ks, ((B + 15) / 16) * N);
+  if (path == FRNN_PATH_FUSED) {
+    rc = run_fused_bwd(q.cell, a, fbp, di, base, L, st);
+    if (rc != FRNN_OK) return rc;
+    // the gradient that reaches the initial state through R: one more contraction, of step 0's da
+    hipLaunchKernelGGL(bwd_dh_kernel<false>, hgrid, dim3(256), 0, st, a, 0);
+  }
+  for (int t = (path == FRNN_PATH_FUSED ? -1 : T - 1); t >= 0; --t) {
+    const dim3 g64((unsigned)((BND + 63) / 64)), b64(64);
+    launch_bwd_cell_kernel(kBwdGate, q.cell, f32, a.wx_f32, g64, b64, st, a, t, nullptr);
+    if (f32) hipLaunchKernelGGL(bwd_dh_kernel<true>, hgrid, dim3(256), 0, st, a, t);
+    else hipLaunchKernelGGL(bwd_dh_kernel<false>, hgrid, dim3(256), 0, st, a, t);
+  }
+  hipLaunchKernelGGL(bwd_final_kernel, dim3(sgrid), dim3(256), 0, st, a);
+  if (hipGetLastError() != hipSuccess) return FRNN_EHIP;
+  // 3. dR and db: per head, [D+1 rows: h^T and ones] x [G*D columns of da], over K = T*B
+  if (q.dR || q.db) {
+    for (int n = 0; n < N; ++n) {
+      const size_t hoff = (size_t)n * Kp * D, toff = (size_t)n * (D + 1) * Kp;
+      const size_t doff = (size_t)n * Kp * G * D, dtoff = (size_t)n * G * D * Kp;
+      if (f32) {
+        launch_transpose<uint32_t>(reinterpret_cast<const uint32_t*>(a.hprev) + hoff, D, Kp, D, reinterpret_cast<uint32_t*>(hT) + toff, Kp, st);
+        launch_transpose<uint32_t>(reinterpret_cast<const uint32_t*>(a.da) + doff, (long long)G * D, Kp, G * D,
+                                   reinterpret_cast<uint32_t*>(daT) + dtoff, Kp, st);
+      } else {
+        launch_transpose<uint16_t>(reinterpret_cast<const uint16_t*>(a.hprev) + hoff, D, Kp, D, reinterpret_cast<uint16_t*>(hT) + toff, Kp, st);
+        launch_transpose<uint16_t>(reinterpret_cast<const uint16_t*>(a.da) + doff, (long long)G * D, Kp, G * D,
+                                   reinterpret_cast<uint16_t*>(daT) + dtoff, Kp, st);
+      }
+    }
+    hipLaunchKernelGGL(bwd_ones_row_kernel, dim3((unsigned)std::min<long long>(((long long)N * Kp + 255) / 256, 4096)),
+                       dim3(256), 0, st, hT, N, D, Kp, f32);
+    // K split into BWD_DR_PARTS equal parts, computed in one launch per head and summed by the
+    // scatter kernel
+    const int parts = BWD_DR_PARTS, kpart = Kp / parts;
+    const long long ptot = (long long)N * (D + 1) * G * D;
+    for (int n = 0; n < N; ++n) {
+      if (launch_gemm(f32, D + 1, G * D, kpart, hT + (size_t)n * (D + 1) * Kp * elt, Kp, daT + (size_t)n * G * D * Kp * elt, Kp,
+                      tmp + (size_t)n * (D + 1) * G * D, (long long)G * D, st, parts, kpart, kpart, ptot) != hipSuccess)
+        return FRNN_EHIP;
+    }
+    const long long nt = ptot;
+    hipLaunchKernelGGL(bwd_scatter_kernel, dim3((unsigned)std::min<long long>((nt + 255) / 256, 65536)), dim3(256), 0, st,
+                       tmp, parts, N, D, G, q.dR, q.dr_sg, q.dr_sn, q.dr_sd, q.db);
+  }
+  return hipGetLastError() == hipSuccess ? FRNN_OK : FRNN_EHIP;
+}
+
 
 bool misaligned(const void* p) { return p && (reinterpret_cast<uintptr_t>(p) & 15u); }
 
@@ -842,119 +1004,30 @@ int frnn_bwd(const frnn_desc* d, int path, const void* Wx, const void* R, const 
     if (db && launch_fill(db, (size_t)G * N * D * 4, st) != hipSuccess) return FRNN_EHIP;
     return hipGetLastError() == hipSuccess ? FRNN_OK : FRNN_EHIP;
   }
-  char* base = reinterpret_cast<char*>(workspace) + kErrBytes;
-  const int Kp = (int)bwd_kp(T, B);
-  BwdArgs a;
-  std::memset(&a, 0, sizeof(a));
-  a.B = B; a.T = T; a.N = N; a.D = D; a.cell = d->cell; a.f32 = f32; a.Kp = Kp;
-  a.Wx = Wx; a.wx_sb = (long long)T * G * N * D; a.wx_st = (long long)G * N * D;
-  a.R = R; a.r_sg = (long long)N * D * D; a.r_sn = (long long)D * D; a.r_sd = D;
-  a.bias = b;
-  a.s0_h = states0;
-  a.s0_c = (states0 && S == 2) ? reinterpret_cast<const char*>(states0) + (size_t)BND * elt : nullptr;
-  a.s0_sb = (long long)N * D;
+  BwdProblem q;
+  std::memset(&q, 0, sizeof(q));
+  q.B = B; q.T = T; q.N = N; q.D = D; q.cell = d->cell; q.f32 = f32; q.wx_f32 = f32;
+  q.Wx = Wx; q.wx_sb = (long long)T * G * N * D; q.wx_st = (long long)G * N * D;
+  q.R = R; q.r_sg = (long long)N * D * D; q.r_sn = (long long)D * D; q.r_sd = D;
+  q.bias = b;
+  q.s0_h = states0;
+  q.s0_c = (states0 && S == 2) ? reinterpret_cast<const char*>(states0) + (size_t)BND * elt : nullptr;
+  q.s0_sb = (long long)N * D;
   const float* stf = reinterpret_cast<const float*>(states);
-  a.st_h = stf; a.st_c = S == 2 ? stf + (long long)B * T * N * D : nullptr;
-  a.st_sb = (long long)T * N * D; a.st_st = (long long)N * D;
+  q.st_h = stf; q.st_c = S == 2 ? stf + (long long)B * T * N * D : nullptr;
+  q.st_sb = (long long)T * N * D; q.st_st = (long long)N * D;
   const float* dsf = reinterpret_cast<const float*>(dstates);
-  a.ds_h = dsf; a.ds_c = (dsf && S == 2) ? dsf + (long long)B * T * N * D : nullptr;
+  q.ds_h = dsf; q.ds_c = (dsf && S == 2) ? dsf + (long long)B * T * N * D : nullptr;
   const float* dlf = reinterpret_cast<const float*>(dlast);
-  a.dl_h = dlf; a.dl_c = (dlf && S == 2) ? dlf + BND : nullptr;
-  a.last_sb = (long long)N * D;
-  a.dWx = reinterpret_cast<float*>(dWx);
-  a.ds0_h = reinterpret_cast<float*>(dstates0);
-  a.ds0_c = (dstates0 && S == 2) ? reinterpret_cast<float*>(dstates0) + BND : nullptr;
-  a.hprev = base + L.hprev;
-  a.hr = reinterpret_cast<const float*>(base + L.hr);
-  a.da = base + L.da;
-  a.zeros = reinterpret_cast<const float*>(base + L.zeros);
-  a.rpk = base + L.rpk;
-  a.dhpart = reinterpret_cast<float*>(base + L.dhpart);
-  a.ks = std::min(BWD_KS, G * D / (f32 ? 4 : 32));
-  a.carry = reinterpret_cast<float*>(base + L.carry);
-  char* hT = base + L.hprevT;
-  char* rt = base + L.rt;
-  char* daT = base + L.daT;
-  float* tmp = reinterpret_cast<float*>(base + L.tmp);
-  float* hr = reinterpret_cast<float*>(base + L.hr);
-  // carried gradients start at zero; da's rows past T*B stay zero for the dR GEMM
-  if (launch_fill(base + L.zeros, 256, st) != hipSuccess ||
-      launch_fill(a.dhpart, (size_t)BWD_KS * BND * 4, st) != hipSuccess || launch_fill(a.carry, (size_t)BND * 4, st) != hipSuccess ||
-      launch_fill(a.da, (size_t)N * Kp * G * D * elt, st) != hipSuccess)
-    return FRNN_EHIP;
-  // 1. h_{t-1} for every step, R^T, and h.R for every step
-  hipLaunchKernelGGL(bwd_hprev_kernel, dim3((unsigned)std::min<long long>(((long long)N * Kp * D + 255) / 256, 65536)),
-                     dim3(256), 0, st, a);
-  for (int n = 0; n < N; ++n) {
-    for (int g = 0; g < G; ++g) {
-      const size_t src = (size_t)g * a.r_sg + (size_t)n * a.r_sn, dst = ((size_t)n * G + g) * D * D;
-      if (f32) launch_transpose<uint32_t>(reinterpret_cast<const uint32_t*>(R) + src, D, D, D, reinterpret_cast<uint32_t*>(rt) + dst, D, st);
-      else launch_transpose<uint16_t>(reinterpret_cast<const uint16_t*>(R) + src, D, D, D, reinterpret_cast<uint16_t*>(rt) + dst, D, st);
-    }
-    if (launch_gemm(f32, T * B, G * D, D, base + L.hprev + (size_t)n * Kp * D * elt, D, rt + (size_t)n * G * D * D * elt, D,
-                    hr + (size_t)n * T * B * G * D, (long long)G * D, st) != hipSuccess)
-      return FRNN_EHIP;
-  }
-  // 2. the serial part (R packed once as the dh kernels' A fragments)
-  {
-    const long long np = (long long)N * (D / 16) * (G * D / (f32 ? 4 : 32)) * 64;
-    hipLaunchKernelGGL(bwd_rpack_kernel, dim3((unsigned)std::min<long long>((np + 255) / 256, 65536)), dim3(256), 0, st, a,
-                       (void*)(base + L.rpk));
-  }
-  const dim3 hgrid(D / 16, a.ks, ((B + 15) / 16) * N);
-  if (path == FRNN_PATH_FUSED) {
-    rc = run_fused_bwd(d, a, fbp, di, base, L, st);
-    if (rc != FRNN_OK) return rc;
-    // the gradient that reaches the initial state through R: one more contraction, of step 0's da
-    hipLaunchKernelGGL(bwd_dh_kernel<false>, hgrid, dim3(256), 0, st, a, 0);
-  }
-  for (int t = (path == FRNN_PATH_FUSED ? -1 : T - 1); t >= 0; --t) {
-    const dim3 g64((unsigned)((BND + 63) / 64)), b64(64);
-    if (f32) {
-      if (d->cell == FRNN_CELL_LSTM) hipLaunchKernelGGL((bwd_gate_kernel<CELL_LSTM, true>), g64, b64, 0, st, a, t);
-      else if (d->cell == FRNN_CELL_GRU) hipLaunchKernelGGL((bwd_gate_kernel<CELL_GRU, true>), g64, b64, 0, st, a, t);
-      else hipLaunchKernelGGL((bwd_gate_kernel<CELL_ELMAN, true>), g64, b64, 0, st, a, t);
-    } else {
-      if (d->cell == FRNN_CELL_LSTM) hipLaunchKernelGGL((bwd_gate_kernel<CELL_LSTM, false>), g64, b64, 0, st, a, t);
-      else if (d->cell == FRNN_CELL_GRU) hipLaunchKernelGGL((bwd_gate_kernel<CELL_GRU, false>), g64, b64, 0, st, a, t);
-      else hipLaunchKernelGGL((bwd_gate_kernel<CELL_ELMAN, false>), g64, b64, 0, st, a, t);
-    }
-    if (f32) hipLaunchKernelGGL(bwd_dh_kernel<true>, hgrid, dim3(256), 0, st, a, t);
-    else hipLaunchKernelGGL(bwd_dh_kernel<false>, hgrid, dim3(256), 0, st, a, t);
-  }
-  hipLaunchKernelGGL(bwd_final_kernel, dim3(sgrid), dim3(256), 0, st, a);
-  if (hipGetLastError() != hipSuccess) return FRNN_EHIP;
-  // 3. dR and db: per head, [D+1 rows: h^T and ones] x [G*D columns of da], over K = T*B
-  if (dR || db) {
-    for (int n = 0; n < N; ++n) {
-      const size_t hoff = (size_t)n * Kp * D, toff = (size_t)n * (D + 1) * Kp;
-      const size_t doff = (size_t)n * Kp * G * D, dtoff = (size_t)n * G * D * Kp;
-      if (f32) {
-        launch_transpose<uint32_t>(reinterpret_cast<const uint32_t*>(a.hprev) + hoff, D, Kp, D, reinterpret_cast<uint32_t*>(hT) + toff, Kp, st);
-        launch_transpose<uint32_t>(reinterpret_cast<const uint32_t*>(a.da) + doff, (long long)G * D, Kp, G * D,
-                                   reinterpret_cast<uint32_t*>(daT) + dtoff, Kp, st);
-      } else {
-        launch_transpose<uint16_t>(reinterpret_cast<const uint16_t*>(a.hprev) + hoff, D, Kp, D, reinterpret_cast<uint16_t*>(hT) + toff, Kp, st);
-        launch_transpose<uint16_t>(reinterpret_cast<const uint16_t*>(a.da) + doff, (long long)G * D, Kp, G * D,
-                                   reinterpret_cast<uint16_t*>(daT) + dtoff, Kp, st);
-      }
-    }
-    hipLaunchKernelGGL(bwd_ones_row_kernel, dim3((unsigned)std::min<long long>(((long long)N * Kp + 255) / 256, 4096)),
-                       dim3(256), 0, st, hT, N, D, Kp, f32);
-    // K split into BWD_DR_PARTS equal parts, computed in one launch per head and summed by the
-    // scatter kernel
-    const int parts = BWD_DR_PARTS, kpart = Kp / parts;
-    const long long ptot = (long long)N * (D + 1) * G * D;
-    for (int n = 0; n < N; ++n) {
-      if (launch_gemm(f32, D + 1, G * D, kpart, hT + (size_t)n * (D + 1) * Kp * elt, Kp, daT + (size_t)n * G * D * Kp * elt, Kp,
-                      tmp + (size_t)n * (D + 1) * G * D, (long long)G * D, st, parts, kpart, kpart, ptot) != hipSuccess)
-        return FRNN_EHIP;
-    }
-    const long long nt = ptot;
-    hipLaunchKernelGGL(bwd_scatter_kernel, dim3((unsigned)std::min<long long>((nt + 255) / 256, 65536)), dim3(256), 0, st,
-                       tmp, parts, N, D, G, reinterpret_cast<float*>(dR), reinterpret_cast<float*>(db));
-  }
-  return hipGetLastError() == hipSuccess ? FRNN_OK : FRNN_EHIP;
+  q.dl_h = dlf; q.dl_c = (dlf && S == 2) ? dlf + BND : nullptr;
+  q.last_sb = (long long)N * D;
+  q.dWx = reinterpret_cast<float*>(dWx);
+  q.dR = reinterpret_cast<float*>(dR); q.dr_sg = (long long)N * D * D; q.dr_sn = (long long)D * D; q.dr_sd = D;
+  q.db = reinterpret_cast<float*>(db);
+  q.ds0_h = reinterpret_cast<float*>(dstates0);
+  q.ds0_c = (dstates0 && S == 2) ? reinterpret_cast<float*>(dstates0) + BND : nullptr;
+  (void)sgrid;
+  return run_backward(q, path, fbp, di, reinterpret_cast<char*>(workspace) + kErrBytes, L, st);
 }
 
 int frnn_bwd_plan_str(const frnn_desc* d, int path, char* buf, size_t cap) {
@@ -1083,6 +1156,207 @@ int frnn_lstm_stack_fwd(int L, int T, int B, int I, int H, int path, const void*
     if (rc != FRNN_OK) return rc;
   }
   return FRNN_OK;
+}
+
+// ----------------------------------------------------------------------------- stack backward
+// Workspace of frnn_lstm_stack_bwd (after the error word).
+struct StackBwdLayout {
+  size_t wx, st, wit, dwx, dx, xt, dwxt, parts, db, rec, bwd, total;
+  BwdLayout bl;
+};
+
+static StackBwdLayout stack_bwd_layout(int L, int T, int B, int I, int H, int path) {
+  StackBwdLayout S;
+  const size_t TB = (size_t)T * B, IH = (size_t)std::max(I, H), Kp = bwd_kp(T, B);
+  size_t q = 0;
+  S.wx = q;    q += align256((size_t)L * TB * 4 * H * 4);      // every layer's projection, fp32 [T][B][4H]
+  S.st = q;    q += align256((size_t)L * 2 * TB * H * 4);      // every layer's h and c, fp32 [T][B][H]
+  S.wit = q;   q += align256(IH * 4 * H * 2);                  // Wi transposed for the projection GEMM
+  S.dwx = q;   q += align256(TB * 4 * H * 4);                  // dWx of the layer at hand
+  S.dx = q;    q += align256(2 * TB * IH * 4);                 // dX of the layer above / at hand
+  S.xt = q;    q += align256(IH * Kp * 2);                     // the layer's input, transposed, bf16
+  S.dwxt = q;  q += align256((size_t)4 * H * Kp * 2);          // dWx transposed, bf16
+  S.parts = q; q += align256((size_t)BWD_DR_PARTS * IH * 4 * H * 4);  // K parts of dWi
+  S.db = q;    q += align256((size_t)4 * H * 4);
+  S.rec = q;   q += align256(rec_scratch_bytes(B, 1, H, FRNN_CELL_LSTM, 0, path));  // forward recurrence
+  S.bl = bwd_layout(B, T, 1, H, FRNN_CELL_LSTM, 0, path);
+  S.bwd = q;   q += align256(S.bl.total);
+  S.total = q;
+  return S;
+}
+
+int frnn_lstm_stack_bwd_workspace_bytes(int L, int T, int B, int I, int H, int path, size_t* bytes) {
+  const int rc = validate_stack(L, T, B, I, H, path);
+  if (rc != FRNN_OK) return rc;
+  if (!bytes) return FRNN_EINVAL;
+  *bytes = kErrBytes + stack_bwd_layout(L, T, B, I, H, path).total;
+  return FRNN_OK;
+}
+
+int frnn_lstm_stack_bwd(int L, int T, int B, int I, int H, int path, const void* x, const void* const* Wi,
+                        const void* const* Wh, const void* const* b_ih, const void* const* b_hh, const void* h0,
+                        const void* c0, const void* dout, const void* dhn, const void* dcn, void* dx,
+                        void* const* dWi, void* const* dWh, void* const* db_ih, void* const* db_hh, void* dh0,
+                        void* dc0, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = validate_stack(L, T, B, I, H, path);
+  if (rc != FRNN_OK) return rc;
+  if (!Wi || !Wh) return FRNN_EINVAL;
+  if (T > 0 && !x) return FRNN_EINVAL;
+  for (int l = 0; l < L; ++l) {
+    if (!Wi[l] || !Wh[l] || misaligned(Wi[l]) || misaligned(Wh[l])) return FRNN_EINVAL;
+    if ((b_ih && misaligned(b_ih[l])) || (b_hh && misaligned(b_hh[l]))) return FRNN_EINVAL;
+    if ((dWi && misaligned(dWi[l])) || (dWh && misaligned(dWh[l])) || (db_ih && misaligned(db_ih[l])) ||
+        (db_hh && misaligned(db_hh[l])))
+      return FRNN_EINVAL;
+  }
+  for (const void* p : {x, h0, c0, dout, dhn, dcn, (const void*)dx, (const void*)dh0, (const void*)dc0,
+                        (const void*)workspace})
+    if (misaligned(p)) return FRNN_EINVAL;
+  const StackBwdLayout SL = stack_bwd_layout(L, T, B, I, H, path);
+  if (!workspace || workspace_bytes < kErrBytes + SL.total) return FRNN_EWORKSPACE;
+  DevInfo di;
+  rc = get_devinfo(&di);
+  if (rc != FRNN_OK) return rc;
+  // both recurrences' plans must exist before anything is enqueued
+  Problem probe;
+  std::memset(&probe, 0, sizeof(probe));
+  probe.B = B; probe.T = T; probe.N = 1; probe.D = H; probe.cell = FRNN_CELL_LSTM; probe.r_f32 = 0; probe.wx_f32 = 1;
+  FusedPlan fp;
+  FusedBwdPlan fbp;
+  if (path == FRNN_PATH_FUSED) {
+    if ((rc = plan_fused(probe, di, &fp)) != FRNN_OK) return rc;
+    if ((rc = plan_fused_bwd(B, 1, H, FRNN_CELL_LSTM, 0, di, &fbp)) != FRNN_OK) return rc;
+  }
+  if ((long long)((B + 15) / 16) > 65535) return FRNN_EUNSUPPORTED;  // dh kernel grid
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  char* base = reinterpret_cast<char*>(workspace) + kErrBytes;
+  if (launch_fill(workspace, kErrBytes, st) != hipSuccess) return FRNN_EHIP;
+  const long long TB = (long long)T * B, LBH = (long long)B * H;
+  const int Kp = (int)bwd_kp(T, B);
+  auto fill_out = [&](void* p, size_t bytes) { return p ? launch_fill(p, bytes, st) : hipSuccess; };
+  if (T == 0) {  // the final states are the initial ones; nothing else receives a gradient
+    for (int l = 0; l < L; ++l) {
+      const int in = (l == 0) ? I : H;
+      if ((dWi && fill_out(dWi[l], (size_t)in * 4 * H * 4) != hipSuccess) ||
+          (dWh && fill_out(dWh[l], (size_t)H * 4 * H * 4) != hipSuccess) ||
+          (db_ih && fill_out(db_ih[l], (size_t)4 * H * 4) != hipSuccess) ||
+          (db_hh && fill_out(db_hh[l], (size_t)4 * H * 4) != hipSuccess))
+        return FRNN_EHIP;
+    }
+    const long long n = (long long)L * LBH;
+    const unsigned g = (unsigned)std::min<long long>((n + 255) / 256, 4096);
+    if (dh0) {
+      if (dhn) hipLaunchKernelGGL(copy_init_kernel, dim3(g), dim3(256), 0, st, dhn, 1, reinterpret_cast<float*>(dh0), n);
+      else if (fill_out(dh0, (size_t)n * 4) != hipSuccess) return FRNN_EHIP;
+    }
+    if (dc0) {
+      if (dcn) hipLaunchKernelGGL(copy_init_kernel, dim3(g), dim3(256), 0, st, dcn, 1, reinterpret_cast<float*>(dc0), n);
+      else if (fill_out(dc0, (size_t)n * 4) != hipSuccess) return FRNN_EHIP;
+    }
+    return hipGetLastError() == hipSuccess ? FRNN_OK : FRNN_EHIP;
+  }
+  float* wx_all = reinterpret_cast<float*>(base + SL.wx);
+  float* st_all = reinterpret_cast<float*>(base + SL.st);
+  uint16_t* wit = reinterpret_cast<uint16_t*>(base + SL.wit);
+  float* dwx = reinterpret_cast<float*>(base + SL.dwx);
+  float* dxb[2] = {reinterpret_cast<float*>(base + SL.dx),
+                   reinterpret_cast<float*>(base + SL.dx) + (size_t)TB * std::max(I, H)};
+  uint16_t* xt = reinterpret_cast<uint16_t*>(base + SL.xt);
+  uint16_t* dwxt = reinterpret_cast<uint16_t*>(base + SL.dwxt);
+  float* parts = reinterpret_cast<float*>(base + SL.parts);
+  float* dbt = reinterpret_cast<float*>(base + SL.db);
+  int* err = reinterpret_cast<int*>(workspace);
+  auto layer_wx = [&](int l) { return wx_all + (size_t)l * TB * 4 * H; };
+  auto layer_h = [&](int l) { return st_all + (size_t)l * 2 * TB * H; };
+  // 1. the forward again, keeping every layer's projection and states (time-major)
+  for (int l = 0; l < L; ++l) {
+    const int in = (l == 0) ? I : H;
+    ProjArgs pa;
+    pa.M = (int)TB; pa.Nc = 4 * H; pa.K = in;
+    pa.A = (l == 0) ? x : (const void*)layer_h(l - 1);
+    pa.a_f32 = (l == 0) ? 0 : 1;
+    pa.lda = in;
+    pa.Bt = wit;
+    pa.ldb = in;
+    pa.a_z = pa.b_z = pa.c_z = 0;
+    pa.b1 = b_ih ? reinterpret_cast<const uint16_t*>(b_ih[l]) : nullptr;
+    pa.b2 = b_hh ? reinterpret_cast<const uint16_t*>(b_hh[l]) : nullptr;
+    pa.C = layer_wx(l);
+    pa.ldc = 4 * H;
+    launch_transpose<uint16_t>(reinterpret_cast<const uint16_t*>(Wi[l]), 4 * H, in, 4 * H, wit, in, st);
+    const dim3 pgrid(((pa.Nc + PJ_BN - 1) / PJ_BN) * ((pa.M + PJ_BM - 1) / PJ_BM));
+    if (pa.a_f32) hipLaunchKernelGGL(proj_gemm_kernel<true>, pgrid, dim3(256), 0, st, pa);
+    else hipLaunchKernelGGL(proj_gemm_kernel<false>, pgrid, dim3(256), 0, st, pa);
+    if (hipGetLastError() != hipSuccess) return FRNN_EHIP;
+    Problem p;
+    std::memset(&p, 0, sizeof(p));
+    p.B = B; p.T = T; p.N = 1; p.D = H; p.cell = FRNN_CELL_LSTM; p.r_f32 = 0;
+    p.Wx = layer_wx(l); p.wx_f32 = 1; p.wx_sb = 4LL * H; p.wx_st = 4LL * H * B;
+    p.R = Wh[l]; p.r_sg = H; p.r_sn = 0; p.r_sd = 4LL * H;
+    p.s0_h = h0 ? reinterpret_cast<const uint16_t*>(h0) + l * LBH : nullptr;
+    p.s0_c = c0 ? reinterpret_cast<const uint16_t*>(c0) + l * LBH : nullptr;
+    p.s0_f32 = 0; p.s0_sb = H;
+    p.out_h = layer_h(l); p.out_c = layer_h(l) + TB * H;
+    p.out_sb = H; p.out_st = (long long)B * H;
+    rc = run_recurrence(p, path, err, base + SL.rec, st);
+    if (rc != FRNN_OK) return rc;
+  }
+  // 2. the layers from the top: the recurrence's backward, then the projection's
+  for (int l = L - 1; l >= 0; --l) {
+    const int in = (l == 0) ? I : H;
+    BwdProblem q;
+    std::memset(&q, 0, sizeof(q));
+    q.B = B; q.T = T; q.N = 1; q.D = H; q.cell = FRNN_CELL_LSTM; q.f32 = 0; q.wx_f32 = 1;
+    q.Wx = layer_wx(l); q.wx_sb = 4LL * H; q.wx_st = 4LL * H * B;
+    q.R = Wh[l]; q.r_sg = H; q.r_sn = 0; q.r_sd = 4LL * H;
+    q.s0_h = h0 ? reinterpret_cast<const uint16_t*>(h0) + l * LBH : nullptr;
+    q.s0_c = c0 ? reinterpret_cast<const uint16_t*>(c0) + l * LBH : nullptr;
+    q.s0_sb = H;
+    q.st_h = layer_h(l); q.st_c = layer_h(l) + TB * H; q.st_sb = H; q.st_st = (long long)B * H;
+    q.ds_h = (l == L - 1) ? reinterpret_cast<const float*>(dout) : dxb[(l + 1) & 1];
+    q.dl_h = dhn ? reinterpret_cast<const float*>(dhn) + l * LBH : nullptr;
+    q.dl_c = dcn ? reinterpret_cast<const float*>(dcn) + l * LBH : nullptr;
+    q.last_sb = H;
+    q.dWx = dwx;
+    q.dR = dWh ? reinterpret_cast<float*>(dWh[l]) : nullptr;
+    q.dr_sg = H; q.dr_sn = 0; q.dr_sd = 4LL * H;
+    q.db = dbt;  // the bias is folded into Wx: db_ih = db_hh = sum of dWx, which the dR GEMM's ones row gives
+    q.ds0_h = dh0 ? reinterpret_cast<float*>(dh0) + l * LBH : nullptr;
+    q.ds0_c = dc0 ? reinterpret_cast<float*>(dc0) + l * LBH : nullptr;
+    rc = run_backward(q, path, fbp, di, base + SL.bwd, SL.bl, st);
+    if (rc != FRNN_OK) return rc;
+    const long long nb = 4LL * H;
+    if (db_ih && db_ih[l])
+      hipLaunchKernelGGL(copy_init_kernel, dim3((unsigned)((nb + 255) / 256)), dim3(256), 0, st, dbt, 1,
+                         reinterpret_cast<float*>(db_ih[l]), nb);
+    if (db_hh && db_hh[l])
+      hipLaunchKernelGGL(copy_init_kernel, dim3((unsigned)((nb + 255) / 256)), dim3(256), 0, st, dbt, 1,
+                         reinterpret_cast<float*>(db_hh[l]), nb);
+    // dWi = X^T . dWx over K = T*B (bf16 operands, K split in parts summed in order)
+    if (dWi && dWi[l]) {
+      if (launch_fill(xt, (size_t)in * Kp * 2, st) != hipSuccess || launch_fill(dwxt, (size_t)4 * H * Kp * 2, st) != hipSuccess)
+        return FRNN_EHIP;
+      const int ty = (int)std::min<long long>((TB + 31) / 32, 65535);
+      if (l == 0) launch_transpose<uint16_t>(reinterpret_cast<const uint16_t*>(x), in, (int)TB, in, xt, Kp, st);
+      else hipLaunchKernelGGL(transpose_f32_bf16_kernel, dim3((in + 31) / 32, ty), dim3(256), 0, st, layer_h(l - 1),
+                              (long long)in, (int)TB, in, xt, (long long)Kp);
+      hipLaunchKernelGGL(transpose_f32_bf16_kernel, dim3((4 * H + 31) / 32, ty), dim3(256), 0, st, dwx, 4LL * H, (int)TB,
+                         4 * H, dwxt, (long long)Kp);
+      const int kpart = Kp / BWD_DR_PARTS;
+      const long long ptot = (long long)in * 4 * H;
+      if (launch_gemm(false, in, 4 * H, kpart, xt, Kp, dwxt, Kp, parts, 4LL * H, st, BWD_DR_PARTS, kpart, kpart, ptot) !=
+          hipSuccess)
+        return FRNN_EHIP;
+      hipLaunchKernelGGL(sum_parts_kernel, dim3((unsigned)std::min<long long>((ptot + 255) / 256, 65536)), dim3(256), 0, st,
+                         parts, BWD_DR_PARTS, ptot, reinterpret_cast<float*>(dWi[l]));
+    }
+    // dX = dWx . Wi^T: the gradient of the layer below's h sequence, or of x
+    float* dxo = (l == 0) ? reinterpret_cast<float*>(dx) : dxb[l & 1];
+    if (dxo && launch_gemm(false, (int)TB, in, 4 * H, dwx, 4LL * H, Wi[l], 4LL * H, dxo, in, st, 1, 0, 0, 0, true) !=
+                   hipSuccess)
+      return FRNN_EHIP;
+  }
+  return hipGetLastError() == hipSuccess ? FRNN_OK : FRNN_EHIP;
 }
 
 }  // extern "C"

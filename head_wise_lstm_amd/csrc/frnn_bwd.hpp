@@ -24,7 +24,8 @@ namespace frnn {
 
 struct BwdArgs {
   int B, T, N, D, cell;
-  int f32;        // operands fp32 (else bf16)
+  int f32;        // operands fp32 (else bf16): R, bias, initial states, the MFMA operands
+  int wx_f32;     // Wx fp32 (else bf16)
   int Kp;         // T*B rounded up to a multiple of 32: rows of the (t, b) operand buffers
   const void* Wx;
   long long wx_sb, wx_st;
@@ -85,10 +86,11 @@ __global__ void __launch_bounds__(256) bwd_hprev_kernel(BwdArgs a) {
 // Step t of the serial part: one thread per (b, n, unit), consecutive threads on consecutive
 // units. Reads the recomputed h.R, Wx, bias and the forward states of the step, adds the
 // incoming gradients, and writes dWx, da (operand type, for the dh kernel and dR) and the carry.
-template <int CELL, bool F32>
+template <int CELL, bool F32, bool WXF32>
 __global__ void __launch_bounds__(64) bwd_gate_kernel(BwdArgs a, int t) {
   constexpr int G = cell_gates(CELL);
   typedef typename std::conditional<F32, float, uint16_t>::type op_t;
+  typedef typename std::conditional<WXF32, float, uint16_t>::type wx_t;
   const long long total = (long long)a.B * a.N * a.D;
   const long long idx = (long long)blockIdx.x * 64 + threadIdx.x;
   if (idx >= total) return;
@@ -106,7 +108,7 @@ __global__ void __launch_bounds__(64) bwd_gate_kernel(BwdArgs a, int t) {
   // every input is read unconditionally: an absent one (or one this step does not use) is read
   // at element 0 of the zero page instead
   const op_t* zop = reinterpret_cast<const op_t*>(a.zeros);
-  const op_t* wxp = reinterpret_cast<const op_t*>(a.Wx);
+  const wx_t* wxp = reinterpret_cast<const wx_t*>(a.Wx);
   const bool hb = a.bias != nullptr, hds = a.ds_h != nullptr, hdl = a.dl_h != nullptr && t == a.T - 1;
   const op_t* bp = hb ? reinterpret_cast<const op_t*>(a.bias) : zop;
   const float* dsh = hds ? a.ds_h : a.zeros;
@@ -115,11 +117,15 @@ __global__ void __launch_bounds__(64) bwd_gate_kernel(BwdArgs a, int t) {
     if constexpr (F32) return v;
     else return bf2f(v);
   };
+  auto fw = [](wx_t v) -> float {
+    if constexpr (WXF32) return v;
+    else return bf2f(v);
+  };
   float pre[G], wx[G], bb[G], dp[BWD_KS];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     pre[g] = hr[(long long)g * D];
-    wx[g] = f(wxp[wbase + (long long)g * N * D]);
+    wx[g] = fw(wxp[wbase + (long long)g * N * D]);
     bb[g] = f(bp[hb ? (long long)(g * N + n) * D + u : 0]);
   }
   const long long BND = (long long)a.B * N * D;
@@ -188,10 +194,11 @@ __global__ void __launch_bounds__(64) bwd_gate_kernel(BwdArgs a, int t) {
 // Coefficient records of every step, for the fused serial part (layout: frnn_fused_bwd.hpp): one
 // thread per (t, b, n, unit); record index s = T-1-t. The gradients of the step's outputs (and of
 // last_states at t = T-1) ride along.
-template <int CELL, bool F32>
+template <int CELL, bool F32, bool WXF32>
 __global__ void __launch_bounds__(256) bwd_record_kernel(BwdArgs a, float* rec) {
   constexpr int G = cell_gates(CELL);
   typedef typename std::conditional<F32, float, uint16_t>::type op_t;
+  typedef typename std::conditional<WXF32, float, uint16_t>::type wx_t;
   const long long total = (long long)a.T * a.B * a.N * a.D;
   const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
   if (idx >= total) return;
@@ -209,7 +216,7 @@ __global__ void __launch_bounds__(256) bwd_record_kernel(BwdArgs a, float* rec) 
   const long long lidx = (long long)b * a.last_sb + (long long)n * D + u;
   const long long s0idx = (long long)b * a.s0_sb + (long long)n * D + u;
   const op_t* zop = reinterpret_cast<const op_t*>(a.zeros);
-  const op_t* wxp = reinterpret_cast<const op_t*>(a.Wx);
+  const wx_t* wxp = reinterpret_cast<const wx_t*>(a.Wx);
   const bool hb = a.bias != nullptr, hds = a.ds_h != nullptr, hdl = a.dl_h != nullptr && t == a.T - 1;
   const op_t* bp = hb ? reinterpret_cast<const op_t*>(a.bias) : zop;
   const float* dsh = hds ? a.ds_h : a.zeros;
@@ -218,11 +225,15 @@ __global__ void __launch_bounds__(256) bwd_record_kernel(BwdArgs a, float* rec) 
     if constexpr (F32) return v;
     else return bf2f(v);
   };
+  auto fw = [](wx_t v) -> float {
+    if constexpr (WXF32) return v;
+    else return bf2f(v);
+  };
   float pre[G], wx[G], bb[G];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     pre[g] = hr[(long long)g * D];
-    wx[g] = f(wxp[wbase + (long long)g * N * D]);
+    wx[g] = fw(wxp[wbase + (long long)g * N * D]);
     bb[g] = f(bp[hb ? (long long)(g * N + n) * D + u : 0]);
   }
   const float ds_h = dsh[hds ? sidx : 0] + dlh[hdl ? lidx : 0];
@@ -424,11 +435,12 @@ __global__ void __launch_bounds__(256) bwd_final_kernel(BwdArgs a) {
   if (a.ds0_c && a.cell == CELL_LSTM) a.ds0_c[idx] = a.carry[idx];
 }
 
-// dR[g][n][d][e] = sum_p tmp[p][n][d][g*D + e] and db[g][n][e] = sum_p tmp[p][n][D][g*D + e]
+// dR[g][n][d][e] (element strides dr_sg, dr_sn, dr_sd; e contiguous) = sum_p tmp[p][n][d][g*D + e]
+// and db[g][n][e] = sum_p tmp[p][n][D][g*D + e]
 // (tmp: [parts][N][D+1][G*D] fp32, the K-split parts of the dR GEMM's output with its row of
 // ones), the parts added in order.
 __global__ void __launch_bounds__(256) bwd_scatter_kernel(const float* tmp, int parts, int N, int D, int G, float* dR,
-                                                          float* db) {
+                                                          long long dr_sg, long long dr_sn, long long dr_sd, float* db) {
   const long long total = (long long)N * (D + 1) * G * D;
   for (long long idx = (long long)blockIdx.x * 256 + threadIdx.x; idx < total; idx += (long long)gridDim.x * 256) {
     float v = 0.0f;
@@ -439,7 +451,7 @@ __global__ void __launch_bounds__(256) bwd_scatter_kernel(const float* tmp, int 
     const int n = (int)(r / (D + 1));
     const int g = col / D, e = col % D;
     if (d < D) {
-      if (dR) dR[(((long long)g * N + n) * D + d) * D + e] = v;
+      if (dR) dR[(long long)g * dr_sg + (long long)n * dr_sn + (long long)d * dr_sd + e] = v;
     } else if (db) {
       db[((long long)g * N + n) * D + e] = v;
     }

@@ -59,6 +59,38 @@ __global__ void __launch_bounds__(256) transpose_kernel(const E* src, long long 
   }
 }
 
+// dst[j][k] = bf16(src[k][j]) for fp32 src (as transpose_kernel, rounding to nearest even).
+__global__ void __launch_bounds__(256) transpose_f32_bf16_kernel(const float* src, long long lds, int K, int Nc,
+                                                                 uint16_t* dst, long long ldd) {
+  __shared__ float s[32][33];
+  const int n0 = blockIdx.x * 32;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
+  for (int kb = blockIdx.y; kb * 32 < K; kb += gridDim.y) {
+    const int k0 = kb * 32;
+#pragma unroll
+    for (int i = 0; i < 32; i += 8) {
+      const int k = k0 + ty + i, n = n0 + tx;
+      s[ty + i][tx] = (k < K && n < Nc) ? src[(long long)k * lds + n] : 0.0f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 32; i += 8) {
+      const int n = n0 + ty + i, k = k0 + tx;
+      if (n < Nc && k < K) dst[(long long)n * ldd + k] = f2bf(s[tx][ty + i]);
+    }
+    __syncthreads();
+  }
+}
+
+// out[i] = sum over p < parts of in[p * n + i], in order (the K parts of a split GEMM).
+__global__ void __launch_bounds__(256) sum_parts_kernel(const float* in, int parts, long long n, float* out) {
+  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long long)gridDim.x * 256) {
+    float v = 0.0f;
+    for (int p = 0; p < parts; ++p) v += in[p * n + i];
+    out[i] = v;
+  }
+}
+
 // Staging of 8 consecutive k of one row in registers: 16 bytes of bf16, or 32 bytes of fp32 kept
 // raw (rounded to bf16 only when written to LDS, so that no load is waited for when issued).
 template <bool F32>

@@ -174,6 +174,31 @@ int frnn_lstm_stack_fwd(int L, int T, int B, int I, int H, int path, const void*
 /* Workspace bytes frnn_lstm_stack_fwd needs (grows with T: it holds the projected inputs). */
 int frnn_lstm_stack_workspace_bytes(int L, int T, int B, int I, int H, int path, size_t* bytes);
 
+/*
+ * Backward of frnn_lstm_stack_fwd: for the loss
+ *     L = sum(dout * out) + sum(dhn * hn) + sum(dcn * cn)
+ * it writes the gradients of x, Wi[l], Wh[l], b_ih[l], b_hh[l], h0 and c0 ("5.3 LSTM"'s
+ * parameters; the chain rule of its cell and projection, the pages printing no gradients).
+ * Inputs as for frnn_lstm_stack_fwd (bf16), plus (fp32, each may be NULL = zeros):
+ *   dout [T, B, H],   dhn, dcn [L, B, H]
+ * Outputs (fp32; a NULL pointer, or a NULL array, is not written):
+ *   dx [T, B, I];  dWi[l] [in, 4H];  dWh[l] [H, 4H];  db_ih[l], db_hh[l] [4H] (equal: both biases
+ *   enter as their sum);  dh0, dc0 [L, B, H]
+ * The call runs the forward again, keeping every layer's projection and states in the workspace,
+ * then per layer from the top: the head-wise backward (frnn_bwd's kernels on `path`, with Wh read
+ * as R through strides), dWi = X^T . dWx and dX = dWx . Wi^T (MFMA GEMMs, bf16 operands, fp32
+ * accumulation). T == 0: dh0 = dhn, dc0 = dcn, the weight gradients are zero.
+ */
+int frnn_lstm_stack_bwd(int L, int T, int B, int I, int H, int path, const void* x,
+                        const void* const* Wi, const void* const* Wh, const void* const* b_ih,
+                        const void* const* b_hh, const void* h0, const void* c0, const void* dout,
+                        const void* dhn, const void* dcn, void* dx, void* const* dWi,
+                        void* const* dWh, void* const* db_ih, void* const* db_hh, void* dh0,
+                        void* dc0, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes frnn_lstm_stack_bwd needs (grows with T and L). */
+int frnn_lstm_stack_bwd_workspace_bytes(int L, int T, int B, int I, int H, int path, size_t* bytes);
+
 /* Waits for `stream`, then reads the device-side error word of the last call that used
  * `workspace` (FRNN_OK, FRNN_ETIMEOUT, FRNN_EPLACEMENT, or FRNN_EHIP if the wait failed). */
 int frnn_check(const void* workspace, void* stream);

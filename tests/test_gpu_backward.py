@@ -172,3 +172,49 @@ def test_autograd_function_matches_frnn_bwd():
     ref = hw.frnn_bwd(*[t.detach() for t in leaves], st.detach(), ct["dstates"].to(dev), ct["dlast"].to(dev), cell="lstm")
     for leaf, r in zip(leaves, ref):
         torch.testing.assert_close(leaf.grad, r, rtol=1e-5, atol=1e-5)
+
+
+# ------------------------------------------------------------------ multi-layer LSTM backward
+def _stack_bwd_case(w, path):
+    hw = _hw()
+    x = fi.make_inputs(w)
+    ct = fi.stack_cotangents(w)
+    dev = torch.device("cuda:0")
+    g = lambda t: None if t is None else t.to(dev)
+    _log(f"stack bwd case {w.name} L={w.L} T={w.T} B={w.B} I={w.I} H={w.H} path={path}")
+    got = hw.frnn_lstm_stack_bwd(g(x["x"]), [g(t) for t in x["Wi"]], [g(t) for t in x["Wh"]],
+                                 [g(t) for t in x["b_ih"]], [g(t) for t in x["b_hh"]], g(x["h0"]), g(x["c0"]),
+                                 g(ct["dout"]), g(ct["dhn"]), g(ct["dcn"]), path=path)
+    torch.cuda.synchronize()
+    f = fi.to_f64
+    ref = oracle.lstm_stack_bwd_p3(f(x["x"]), [f(t) for t in x["Wi"]], [f(t) for t in x["Wh"]],
+                                   [f(t) for t in x["b_ih"]], [f(t) for t in x["b_hh"]], f(x["h0"]), f(x["c0"]),
+                                   f(ct["dout"]), f(ct["dhn"]), f(ct["dcn"]))
+    names = ("dx", "dWi", "dWh", "db_ih", "db_hh", "dh0", "dc0")
+    worst = 0.0
+    for name, gv, rv in zip(names, got, ref):
+        gl = gv if isinstance(gv, list) else [gv]
+        rl = rv if isinstance(rv, list) else [rv]
+        for k, (a, r) in enumerate(zip(gl, rl)):
+            a = a.double().cpu().numpy()
+            assert a.shape == r.shape and np.all(np.isfinite(a)), name
+            scale = max(1.0, float(np.abs(r).max()))
+            rel = float(np.abs(a - r).max()) / scale
+            worst = max(worst, rel)
+            assert rel <= 3e-2, f"{name}[{k}]: max abs err / scale {rel}"
+    _log(f"  worst max|err| / scale = {worst:.3e}")
+
+
+STACK_BWD_SMALL = fi.StackWorkload("stack_bwd_small", torch.bfloat16, L=2, T=19, B=10, I=96, H=128, seed=261,
+                                   zero_init=False)
+
+
+@pytest.mark.parametrize("path", ["alternating", "fused"])
+def test_stack_bwd_small(path):
+    _stack_bwd_case(STACK_BWD_SMALL, path)
+
+
+@pytest.mark.timeout(600)
+def test_stack_bwd_full():
+    # the float64 oracle takes about a minute at this size (every gradient depends on every step)
+    _stack_bwd_case(fi.WORKLOADS["lstm2_bf16_T512_B32_I512_H512"], "fused")
