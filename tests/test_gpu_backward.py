@@ -116,6 +116,16 @@ def test_bwd_full(name, path):
     run_bwd_case(w, path)
 
 
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("cell", ["lstm", "gru", "elman"])
+def test_bwd_long_sequence_past_tag_wrap(cell):
+    """65,600 steps: the fused backward's 16-bit step tags wrap (every step checked)."""
+    w = fi.HeadwiseWorkload(f"bwd_{cell}_long", cell, torch.bfloat16, B=3, T=65600, N=1, D=64, seed=272, s0_var=1.0)
+    plan = _fused_plan_or_skip(w)
+    assert "die-local" in plan, plan
+    run_bwd_case(w, "fused")
+
+
 @pytest.mark.parametrize("w,chunks", [
     (fi.HeadwiseWorkload("bwd_gru_chunks_B40", "gru", torch.bfloat16, B=40, T=8, N=1, D=768, seed=251, s0_var=1.0), 3),
     (fi.HeadwiseWorkload("bwd_lstm_chunks_B40", "lstm", torch.bfloat16, B=40, T=6, N=1, D=768, seed=252, s0_var=1.0), 3),

@@ -227,6 +227,32 @@ def test_fused_and_alternating_agree(cell):
     assert (a - f).abs().max().item() < 2e-2
 
 
+# The exchange words carry a 16-bit step tag: a sequence longer than 65,536 steps wraps it. Die-local
+# designs (the only ones that use tags) on a small head, every step checked against the oracle.
+LONG_T = 65600
+
+
+@pytest.mark.parametrize("cell,env", [("lstm", {"FRNN_FUSED_W": 4, "FRNN_FUSED_BR": 3}),
+                                      ("gru", {"FRNN_FUSED_W": 4, "FRNN_FUSED_BR": 3}),
+                                      ("elman", {"FRNN_FUSED_W": 2, "FRNN_FUSED_BR": 3})])
+def test_long_sequence_past_tag_wrap(cell, env):
+    w = fi.HeadwiseWorkload(f"{cell}_long_T{LONG_T}", cell, torch.bfloat16, B=3, T=LONG_T, N=1, D=64, seed=271,
+                            s0_var=1.0)
+    hw = _hw()
+    old = {k: os.environ.get(k) for k in env}
+    os.environ.update({k: str(v) for k, v in env.items()})
+    try:
+        plan = hw.frnn_plan_str(hw._desc(w.B, w.T, w.N, w.D, w.cell, w.dtype), "fused")
+    finally:
+        for k, v in old.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+    assert "die-local" in plan, plan
+    run_case(w, "fused", env=env)
+
+
 def test_repeat_calls_reuse_workspace():
     """Back-to-back calls on one workspace: the exchange buffer holds the previous call's tags."""
     hw = _hw()
