@@ -72,7 +72,7 @@ def write_traffic(args) -> None:
     import frnn_inputs as fi
     fetch_csv, write_csv, fetch_copy_csv, write_copy_csv = args.write_traffic
     if args.backward:
-        kname = "fused_bwd_kernel" if args.path == "fused" else "bwd_dh_kernel"
+        kname = "fused_bwd" if args.path == "fused" else "bwd_dh_kernel"  # either fused backward design
     else:
         kname = "fused_fwd_kernel" if args.path == "fused" else "alt_gemm_kernel"
     true_kib = args.copy_mib * 1024.0
@@ -248,6 +248,8 @@ def main():
                   "projection_gflop": (3.0 if args.backward else 1.0) * 2.0 * w.T * w.B * 4 * w.H *
                   (w.I + w.H * (w.L - 1)) / 1e9,
                   "pass": "backward" if args.backward else "forward"}
+        if args.backward:  # each layer's serial part: the head-wise backward of one head of H units
+            config["plan"] = hw.frnn_bwd_plan_str(hw._desc(w.B, w.T, 1, w.H, "lstm", w.dtype), args.path)
         dtype = "bf16"
 
     for _ in range(args.warmup):
@@ -268,7 +270,8 @@ def main():
     tflops = flops / sec / 1e12
     roof = {"bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": tflops / PEAK_BF16_TFLOPS, "traffic": None,
-            "kernel": (("frnn::fused_bwd_kernel (+ GEMMs, records)" if args.path == "fused" else
+            "kernel": ((("frnn::fused_bwdx_kernel" if "die-local-partials" in str(config.get("plan", "")) else
+                         "frnn::fused_bwd_kernel") + " (+ GEMMs, records)" if args.path == "fused" else
                         "frnn::bwd_gate_kernel+bwd_dh_kernel (+ GEMMs)") if args.backward else
                        "frnn::fused_fwd_kernel" if args.path == "fused" else "frnn::alt_gemm_kernel+alt_gate_kernel"),
             "per_launch_flop": flops, "launch_ms": ms}

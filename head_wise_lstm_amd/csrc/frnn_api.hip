@@ -124,6 +124,17 @@ const FusedBwdVariant* find_fused_bwd(int cell, int ncw, int ks, int mtw, int kt
   return nullptr;
 }
 
+const FusedBwdxVariant* find_fused_bwdx(int cell, int ncw, int mtw, int ktw) {
+  const FusedBwdxTable t = cell == FRNN_CELL_LSTM ? fused_bwdx_table_lstm()
+                           : cell == FRNN_CELL_GRU ? fused_bwdx_table_gru()
+                                                   : fused_bwdx_table_elman();
+  for (int i = 0; i < t.n; ++i) {
+    const FusedBwdxVariant& v = t.v[i];
+    if (v.cell == cell && v.ncw == ncw && v.mtw == mtw && v.ktw == ktw) return &v;
+  }
+  return nullptr;
+}
+
 // ----------------------------------------------------------------------------- problem
 struct Problem {
   int B, T, N, D, cell;
@@ -504,13 +515,87 @@ struct BwdLayout {
 // MT_WG 16-unit tiles of R's rows, (compute waves, K split) over K = G*D.
 struct FusedBwdPlan {
   const FusedBwdVariant* v = nullptr;
+  int px = 0;                  // 1: the partial-sum design (fused_bwdx_kernel), 0: the da exchange
+  fused_bwd_fn fn = nullptr;   // the kernel of either design
   int W = 0, BR = 0, groups = 0, ncw = 0, ks = 0, mtw = 0, ktw = 0, n_xcd = 1, slots = 0, grid = 0, U = 0;
   int chunks = 1, Bc = 0;  // the batch runs as `chunks` launches of at most Bc rows
   size_t lds = 0;
 };
 
+// The partial-sum design: workgroup w owns units [w*UW, (w+1)*UW) of a head with all their
+// gates. Constraints: UW a multiple of 8 (an A fragment stays inside one gate) with G*UW a
+// multiple of 32 (whole k-tiles), at most BWDX_MAX_W workgroups (the pollers' words per lane),
+// the (row, unit pair) combinations within the compute waves' pollers, the I/O wave's limits and
+// an instantiated (waves, tiles, k-tiles) design. Same preference order as the da design.
+bool plan_fused_bwdx(int B, int N, int D, int cell, const DevInfo& di, FusedBwdPlan* out) {
+  const int G = gates_of(cell);
+  const int TPH = D / 16;
+  const int slots_per_die = std::max(1, di.cus / di.n_xcd);
+  const int force_w = env_int("FRNN_FUSED_BWD_W", 0), force_br = env_int("FRNN_FUSED_BWD_BR", 0);
+  const int force_ncw = env_int("FRNN_FUSED_BWD_NCW", 0);
+  const int cand[] = {8, 6, 4};
+  FusedBwdPlan best;
+  bool found = false;
+  for (int BR = 1; BR <= FUSED_DIE_MAX_BR; ++BR) {
+    if (force_br && BR != force_br) continue;
+    for (int W = std::min(BWDX_MAX_W, slots_per_die); W >= 2; --W) {
+      if (force_w && W != force_w) continue;
+      if (D % W) continue;
+      const int UW = D / W;
+      if (UW % 8 || (G * UW) % 32) continue;
+      const int max_groups = (slots_per_die / W) * di.n_xcd;
+      if (max_groups < N) continue;
+      const long long bmax = (long long)BR * (max_groups / N);
+      const int chunks = (int)((B + bmax - 1) / bmax);
+      const int Bc = (B + chunks - 1) / chunks;
+      const int groups = N * ((Bc + BR - 1) / BR);
+      const int per_die = (groups + di.n_xcd - 1) / di.n_xcd;
+      if (BR * UW * BWD_REC / 2 > 64 * BWD_EPL_IN || BR * UW > 64 * BWD_EPL_OUT) continue;
+      for (const int ncw : cand) {
+        if (force_ncw && ncw != force_ncw) continue;
+        if (TPH % ncw) continue;
+        const int mtw = TPH / ncw, ktw = G * UW / 32;
+        if (BR * (UW / 2) > BWDX_CPW * ncw) continue;
+        const FusedBwdxVariant* v = find_fused_bwdx(cell, ncw, mtw, ktw);
+        if (!v) continue;
+        if (found && chunks >= best.chunks) continue;
+        FusedBwdPlan fp;
+        fp.px = 1; fp.fn = v->fn; fp.W = W; fp.BR = BR; fp.groups = groups; fp.ncw = ncw; fp.ks = 1; fp.mtw = mtw;
+        fp.ktw = ktw; fp.n_xcd = di.n_xcd; fp.slots = per_die * W; fp.grid = fp.slots * di.n_xcd; fp.U = UW;
+        fp.chunks = chunks; fp.Bc = Bc;
+        fp.lds = (size_t)fused_bwdx_lds(ktw, BR, UW).total;
+        best = fp;
+        found = true;
+        break;
+      }
+    }
+  }
+  if (found) *out = best;
+  return found;
+}
+
+int plan_fused_bwd_da(int B, int N, int D, int cell, const DevInfo& di, FusedBwdPlan* out);
+
+// The partial-sum design where it has a plan with no more launches than the da design, else the
+// da design. FRNN_FUSED_BWD_DESIGN=da / px pins one.
 int plan_fused_bwd(int B, int N, int D, int cell, int f32, const DevInfo& di, FusedBwdPlan* out) {
   if (f32 || !di.periodic || D % 32 != 0) return FRNN_EUNSUPPORTED;
+  const int design = env_int("FRNN_FUSED_BWD_PX", -1);  // 1: partial sums only, 0: da exchange only
+  FusedBwdPlan px, da;
+  const bool has_px = design != 0 && plan_fused_bwdx(B, N, D, cell, di, &px);
+  const bool has_da = design != 1 && plan_fused_bwd_da(B, N, D, cell, di, &da) == FRNN_OK;
+  if (has_px && (!has_da || px.chunks <= da.chunks)) {
+    *out = px;
+    return FRNN_OK;
+  }
+  if (has_da) {
+    *out = da;
+    return FRNN_OK;
+  }
+  return FRNN_EUNSUPPORTED;
+}
+
+int plan_fused_bwd_da(int B, int N, int D, int cell, const DevInfo& di, FusedBwdPlan* out) {
   const int G = gates_of(cell);
   const int TPH = D / 16, KT = G * D / 32;
   const int slots_per_die = std::max(1, di.cus / di.n_xcd);
@@ -546,8 +631,8 @@ int plan_fused_bwd(int B, int N, int D, int cell, int f32, const DevInfo& di, Fu
         if (!v || BR > fused_max_br(ks, mtw)) continue;
         if (found && chunks >= best.chunks) continue;  // earlier candidates win ties
         FusedBwdPlan fp;
-        fp.v = v; fp.W = W; fp.BR = BR; fp.groups = groups; fp.ncw = ncw; fp.ks = ks; fp.mtw = mtw; fp.ktw = ktw;
-        fp.n_xcd = di.n_xcd; fp.slots = per_die * W; fp.grid = fp.slots * di.n_xcd; fp.U = U;
+        fp.v = v; fp.fn = v->fn; fp.W = W; fp.BR = BR; fp.groups = groups; fp.ncw = ncw; fp.ks = ks; fp.mtw = mtw;
+        fp.ktw = ktw; fp.n_xcd = di.n_xcd; fp.slots = per_die * W; fp.grid = fp.slots * di.n_xcd; fp.U = U;
         fp.chunks = chunks; fp.Bc = Bc;
         fp.lds = (size_t)fused_bwd_lds(ncw, ks, ktw, BR, U).total;
         best = fp;
@@ -582,7 +667,9 @@ BwdLayout bwd_layout(int B, int T, int N, int D, int cell, int f32, int path) {
     L.rec = q;    q += align256((size_t)T * B * N * D * BWD_REC * 4);
     L.dstate = q; q += align256((size_t)T * B * N * D * 2 * 4);
     // exchange words: groups * BR <= N * (B + 3) rows (BR <= 4), two parities, G*D words a row
-    L.xbuf = q;   q += align256((size_t)2 * N * (B + FUSED_DIE_MAX_BR - 1) * G * D * 4);
+    // (da design) or W*D words a row (partial-sum design, W <= BWDX_MAX_W)
+    L.xbuf = q;
+    q += align256((size_t)2 * N * (B + FUSED_DIE_MAX_BR - 1) * std::max<size_t>(G, BWDX_MAX_W) * D * 4);
   }
   L.total = q;
   return L;
@@ -592,9 +679,9 @@ std::string bwd_plan_string(const frnn_desc* d, int path, const FusedBwdPlan* fp
   char buf[512];
   if (path == FRNN_PATH_FUSED && fp) {
     std::snprintf(buf, sizeof(buf),
-                  "backward path=fused design=die-local cell=%s dtype=bf16 B=%d T=%d N=%d D=%d BR=%d groups=%d W=%d "
+                  "backward path=fused design=%s cell=%s dtype=bf16 B=%d T=%d N=%d D=%d BR=%d groups=%d W=%d "
                   "NCW=%d KS=%d MTW=%d KTW=%d dies=%d slots/die=%d grid=%d lds=%zu chunks=%d rows/chunk=%d",
-                  cell_name(d->cell), d->B, d->T, d->N, d->D, fp->BR, fp->groups, fp->W, fp->ncw, fp->ks, fp->mtw,
+                  fp->px ? "die-local-partials" : "die-local", cell_name(d->cell), d->B, d->T, d->N, d->D, fp->BR, fp->groups, fp->W, fp->ncw, fp->ks, fp->mtw,
                   fp->ktw, fp->n_xcd, fp->slots, fp->grid, fp->lds, fp->chunks, fp->Bc);
     return std::string(buf);
   }
@@ -642,7 +729,7 @@ int run_fused_bwd(int cell, const BwdArgs& a, const FusedBwdPlan& fp, const DevI
   float* rec = reinterpret_cast<float*>(base + L.rec);
   float* dstate = reinterpret_cast<float*>(base + L.dstate);
   launch_bwd_cell_kernel(kBwdRecord, cell, false, a.wx_f32, dim3(pgrid), dim3(256), st, a, 0, rec);
-  const void* fn = reinterpret_cast<const void*>(fp.v->fn);
+  const void* fn = reinterpret_cast<const void*>(fp.fn);
   if (fp.lds > 48 * 1024 && hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)fp.lds) != hipSuccess)
     return FRNN_EHIP;
   // the batch in chunks of at most Bc rows, one launch each (rows never interact)
@@ -650,7 +737,7 @@ int run_fused_bwd(int cell, const BwdArgs& a, const FusedBwdPlan& fp, const DevI
     const int Bch = std::min(fp.Bc, a.B - b0);
     const int groups = a.N * ((Bch + fp.BR - 1) / fp.BR);
     const int grid = ((groups + fp.n_xcd - 1) / fp.n_xcd) * fp.W * fp.n_xcd;
-    const size_t xbytes = (size_t)groups * 2 * fp.BR * gates_of(cell) * a.D * 4;
+    const size_t xbytes = (size_t)groups * 2 * fp.BR * (fp.px ? fp.W : gates_of(cell)) * a.D * 4;
     if (launch_fill(base + L.xbuf, xbytes, st, 0xFFFFu) != hipSuccess) return FRNN_EHIP;
     FusedBwdArgs f;
     std::memset(&f, 0, sizeof(f));

@@ -425,3 +425,337 @@ __global__ void __launch_bounds__((NCW + 1) * 64, 1) fused_bwd_kernel(FusedBwdAr
 }
 
 }  // namespace frnn
+
+namespace frnn {
+
+// ============================================================================ partial-sum design
+// The same linear recurrence with the work cut the other way. Workgroup w of a group owns the
+// unit slice [w*UW, (w+1)*UW) (UW = D / W) with all its gates, so the step (and da) of its units
+// needs nothing from other workgroups but dh_R of those units. Its compute waves multiply the
+// slice's da (K = G*UW, from LDS) by the R columns of the slice for every row d of the head
+// (all D/16 tiles, MTW per wave), and publish the result as a partial sum of dh_R: D words a row
+// (bf16 << 16 | step tag) in the workgroup's own slot of the exchange. The next step's pollers
+// read their units' words from all W slots (D words a row per workgroup, a quarter of the da
+// exchange of the LSTM design above for G = 4) and add them in fp32.
+//
+// Per step s: poll waves (the first PW compute waves, eight (row, unit pair) combinations each,
+// eight slot chunks per combination in adjacent lanes, summed by three DPP row shifts) poll,
+// apply the step (its records read from LDS before the poll) and write da into the
+// stage of parity s (bf16 B fragments [batch row][k], k = g*UW + unit) and (dh, dc) into the output
+// ring; the step's barrier; every compute wave multiplies the stage by its R fragments and
+// publishes. The stage has two parities: a workgroup's pollers wait only for the waves that own
+// their units, so another wave may still read the stage of step s while step s+1 is written.
+// The I/O wave puts the records of step k+1 into the ring in interval k (the step is applied
+// before the barrier) and stores the outputs of step k-1.
+
+constexpr int BWDX_CPW = 8;  // (row, unit pair) combinations per poll wave
+constexpr int BWDX_J = 8;    // slot chunks per combination (lanes = CPW * J = 64)
+constexpr int BWDX_NP = 4;   // 64-bit words per lane and round: W <= BWDX_J * BWDX_NP
+constexpr int BWDX_MAX_W = BWDX_J * BWDX_NP;
+// s_sleep units (64 clocks) before a step's first poll round (see FRNN_POLL_SLEEP0)
+#ifndef FRNN_BWDX_SLEEP0
+#define FRNN_BWDX_SLEEP0 FRNN_POLL_SLEEP0
+#endif
+
+struct FusedBwdxLds {
+  int stage, rin, rout, total;
+};
+
+__host__ __device__ inline FusedBwdxLds fused_bwdx_lds(int ktw, int BR, int U) {
+  FusedBwdxLds L;
+  L.stage = 0;
+  L.rin = 2 * 16 * fused_stage_row(ktw) * 4;
+  L.rout = L.rin + 2 * BR * U * BWD_REC * 4;
+  L.total = L.rout + 2 * BR * U * 2 * 4;
+  return L;
+}
+
+// Interval k (k = -1 .. T-1): records of step k+1 into the ring, refill the load stage with step
+// k+1+4, store the outputs of step k-1, then barrier k.
+template <int ST>
+__device__ __forceinline__ bool biox_interval(const BwdIo& c, int k, io_word_t (&raw)[FUSED_IO_STAGES][BWD_EPL_IN],
+                                              float* rin, const float* rout, const int* abort_flag) {
+  constexpr int L = FUSED_IO_STAGES;
+  if (k + 1 < c.T) bio_put(c, k + 1, raw[ST], rin);
+  bio_issue(c, min(k + 1 + L, c.T - 1), raw[ST]);  // unconditional (clamped), as in bio_interval
+  if (k >= 1) bio_store(c, k - 1, rout);
+  block_barrier();
+  return uniform_flag(*abort_flag);
+}
+
+__device__ __forceinline__ void biox_wave(BwdIo& c, float* rin, const float* rout, const int* abort_flag) {
+  constexpr int L = FUSED_IO_STAGES;
+  static_assert(L == 4, "the interval loop below is unrolled for four stages");
+  c.init();
+  io_word_t raw[L][BWD_EPL_IN];
+  if (c.T == 0) {
+    block_barrier();
+    return;
+  }
+  // stage (k+1) mod 4 holds step k+1
+  bio_issue(c, 0, raw[0]);
+  bio_issue(c, min(1, c.T - 1), raw[1]);
+  bio_issue(c, min(2, c.T - 1), raw[2]);
+  bio_issue(c, min(3, c.T - 1), raw[3]);
+  int k = -1;
+  for (; k + 3 <= c.T - 1; k += L) {
+    if (biox_interval<0>(c, k, raw, rin, rout, abort_flag)) return;
+    if (biox_interval<1>(c, k + 1, raw, rin, rout, abort_flag)) return;
+    if (biox_interval<2>(c, k + 2, raw, rin, rout, abort_flag)) return;
+    if (biox_interval<3>(c, k + 3, raw, rin, rout, abort_flag)) return;
+  }
+  if (k <= c.T - 1 && biox_interval<0>(c, k, raw, rin, rout, abort_flag)) return;
+  if (k + 1 <= c.T - 1 && biox_interval<1>(c, k + 1, raw, rin, rout, abort_flag)) return;
+  if (k + 2 <= c.T - 1 && biox_interval<2>(c, k + 2, raw, rin, rout, abort_flag)) return;
+  bio_store(c, c.T - 1, rout);  // after barrier T-1
+}
+
+// x + (x of the lane D places up in the 16-lane row; 0 past the row's end).
+template <int D>
+__device__ __forceinline__ float row_shl_add(float x) {
+  return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x100 + D, 0xF, 0xF, true));
+}
+
+// xbuf: [groups][2][W][BR][D] words. NCW * MTW = D / 16; KTW * 32 = G * D / W.
+template <int CELL, int NCW, int MTW, int KTW>
+__global__ void __launch_bounds__((NCW + 1) * 64, 1) fused_bwdx_kernel(FusedBwdArgs a) {
+  constexpr int G = cell_gates(CELL);
+  static_assert(NCW == 4 || NCW == 6 || NCW == 8, "compute waves");
+
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  __shared__ int s_abort;
+
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int col = lane & 15, quad = lane >> 4;
+  const int D = a.D, N = a.N, T = a.T, W = a.W, BR = a.BR;
+  const int GD = G * D;
+  const int TPH = D / 16;
+  const int KT = GD / 32;
+  const int UW = D / W;
+
+  const int die = blockIdx.x % a.n_xcd, slot = blockIdx.x / a.n_xcd;
+  const int group = (slot / W) * a.n_xcd + die;
+  const int w = slot % W;
+  if (group >= a.groups) return;
+  if (a.check_xcc && xcc_id() != (int)((a.xcc_of >> (4 * die)) & 0xFu)) {
+    if (threadIdx.x == 0) atomicOr(a.err, DEVERR_PLACEMENT);
+    return;
+  }
+  if (threadIdx.x == 0) s_abort = 0;
+
+  const int n = group % N, bblk = group / N;
+  const int b0 = bblk * BR;
+  const int nvalid = min(BR, a.B - b0);
+  const int u0 = w * UW;
+  const FusedBwdxLds lay = fused_bwdx_lds(KTW, BR, UW);
+  constexpr int SROW = fused_stage_row(KTW);
+  uint32_t* stage = reinterpret_cast<uint32_t*>(smem + lay.stage);
+  float* rin = reinterpret_cast<float*>(smem + lay.rin);
+  float* rout = reinterpret_cast<float*>(smem + lay.rout);
+  // both stages: rows of padding batch columns stay zero
+  for (int i = threadIdx.x; i < 2 * 16 * SROW; i += (NCW + 1) * 64) stage[i] = 0u;
+
+  if (wave == NCW) {
+    BwdIo c;
+    c.rec = reinterpret_cast<const char*>(a.rec);
+    c.dst = a.dstate;
+    c.in_row = (long long)N * D * BWD_REC;
+    c.in_step = (long long)a.Bs * N * D * BWD_REC;
+    c.in_base = ((long long)b0 * N + n) * D * BWD_REC + (long long)u0 * BWD_REC;
+    c.out_row = (long long)N * D * 2;
+    c.out_step = (long long)a.Bs * N * D * 2;
+    c.out_base = ((long long)b0 * N + n) * D * 2 + (long long)u0 * 2;
+    c.nvalid = nvalid;
+    c.U = UW;
+    c.T = T;
+    c.BR = BR;
+    c.lane = lane;
+    biox_wave(c, rin, rout, &s_abort);
+    return;
+  }
+
+  // ==================================================================== compute waves
+  // ---- R fragments: rows d of this wave's tiles, k = g*UW + e - u0 over the slice. Eight
+  // consecutive k stay inside one gate (UW is a multiple of 8), so each fragment is one 16-byte
+  // lane of the packed R (global k = g*D + e).
+  bf16x8_t Ra[MTW][KTW];
+  {
+    const u32x4_t* rp = reinterpret_cast<const u32x4_t*>(a.rpk) + (long long)n * TPH * KT * 64;
+    u32x4_t raw[MTW][KTW];
+#pragma unroll
+    for (int kk = 0; kk < KTW; ++kk) {
+      const int kl = kk * 32 + 8 * quad;
+      const int g = kl / UW, kg = g * D + u0 + (kl - g * UW);
+      const int ktg = kg >> 5, grp = (kg & 31) >> 3;
+#pragma unroll
+      for (int j = 0; j < MTW; ++j) {
+        const int tt = wave * MTW + j;
+        raw[j][kk] = rp[((long long)tt * KT + ktg) * 64 + grp * 16 + col];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < MTW; ++j)
+#pragma unroll
+      for (int kk = 0; kk < KTW; ++kk) Ra[j][kk] = __builtin_bit_cast(bf16x8_t, raw[j][kk]);
+  }
+
+  // ---- poll lanes: combination c (batch row r, unit pair p) in lanes 8c' .. 8c'+7, slot chunk j
+  // = lane & 7 (slots j, j+8, ...)
+  static_assert(BWDX_J == 8 && BWDX_CPW * BWDX_J == 64, "poll lane layout");
+  const int UP = UW / 2;
+  const int PW = (BR * UP + BWDX_CPW - 1) / BWDX_CPW;
+  const bool poller = wave < PW;
+  const int cmb = wave * BWDX_CPW + (lane >> 3), chunk = lane & 7;
+  const int pr = cmb / UP, pp2 = cmb - pr * UP;
+  const bool cv = poller && cmb < BR * UP && pr < nvalid;
+  const int xpar = W * BR * D;  // words per parity
+  uint32_t* const xb = a.xbuf + (long long)group * 2 * xpar;
+  uint32_t off[BWDX_NP];  // 64-bit word offsets from the parity's base
+  bool pv[BWDX_NP];
+#pragma unroll
+  for (int e = 0; e < BWDX_NP; ++e) {
+    const int ws = chunk + BWDX_J * e;
+    pv[e] = cv && ws < W;
+    off[e] = pv[e] ? (uint32_t)((ws * BR * D + pr * D + u0 + 2 * pp2) >> 1) : 0u;
+  }
+  float cr[2] = {0.0f, 0.0f};  // LSTM dc, GRU dh carried to the next step, for the pair
+
+  // Step 0 has no dh_R: publish zero partials with tag 0 (parity 1), polled like any other step.
+  if (col < nvalid) {
+#pragma unroll
+    for (int j = 0; j < MTW; ++j) {
+      const int d0 = 16 * (wave * MTW + j) + 4 * quad;
+      *reinterpret_cast<u32x4_t*>(xb + xpar + (w * BR + col) * D + d0) = u32x4_t{0u, 0u, 0u, 0u};
+    }
+  }
+  block_barrier();  // barrier -1
+
+  for (int s = 0; s < T; ++s) {
+    // ---- A. poll this workgroup's units in every slot, add the partials, apply the step
+    if (poller) {
+      // this step's records of the lane's two units (in the ring since barrier s-1)
+      const bool mathlane = cv && chunk == 0;
+      f32x4_t rc[2][2];
+      {
+        const float* rr = rin + ((s & 1) * BR + (mathlane ? pr : 0)) * UW * BWD_REC + (mathlane ? 2 * pp2 : 0) * BWD_REC;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          rc[i][0] = *reinterpret_cast<const f32x4_t*>(rr + i * BWD_REC);
+          rc[i][1] = *reinterpret_cast<const f32x4_t*>(rr + i * BWD_REC + 4);
+        }
+      }
+      const uint32_t tag = (uint32_t)s & 0xFFFFu;
+      const uint64_t* src = reinterpret_cast<const uint64_t*>(xb + ((s - 1) & 1) * xpar);
+      uint64_t v[BWDX_NP];
+      long long t_first = 0;
+      int spins = 0;
+      bool ok = false;
+      if (s > 0) __builtin_amdgcn_s_sleep(FRNN_BWDX_SLEEP0);
+      while (true) {
+#pragma unroll
+        for (int e = 0; e < BWDX_NP; ++e) v[e] = __hip_atomic_load(src + off[e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        bool mine = true;
+#pragma unroll
+        for (int e = 0; e < BWDX_NP; ++e) {
+          const uint32_t lo = (uint32_t)v[e], hi = (uint32_t)(v[e] >> 32);
+          if (pv[e] && (((lo ^ tag) | (hi ^ tag)) & 0xFFFFu) != 0) mine = false;
+        }
+        if (__all(mine)) {
+          ok = true;
+          break;
+        }
+        if ((++spins & 63) == 0) {
+          const long long now = (long long)wall_clock64();
+          if (t_first == 0) t_first = now;
+          if (now - t_first > a.timeout_ticks ||
+              uniform_flag(__hip_atomic_load(a.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))) {
+            if (lane == 0) atomicOr(a.err, DEVERR_TIMEOUT);
+            s_abort = 1;  // every wave leaves after the next barrier
+            break;
+          }
+        }
+      }
+      if (ok) {
+        float s0 = 0.0f, s1 = 0.0f;
+#pragma unroll
+        for (int e = 0; e < BWDX_NP; ++e) {
+          if (pv[e]) {
+            s0 += __uint_as_float((uint32_t)v[e] & 0xFFFF0000u);
+            s1 += __uint_as_float((uint32_t)(v[e] >> 32) & 0xFFFF0000u);
+          }
+        }
+        // lane 8c' gathers the eight chunks of its combination: x[p] += x[p + d], d = 4, 2, 1
+        // (row shifts; lanes past the 16-lane row read 0, and only lanes 8c' use the result)
+        s0 = row_shl_add<1>(row_shl_add<2>(row_shl_add<4>(s0)));
+        s1 = row_shl_add<1>(row_shl_add<2>(row_shl_add<4>(s1)));
+        if (mathlane) {
+          const float dhr[2] = {s0, s1};
+          float da[G][2], dh[2], dc[2];
+#pragma unroll
+          for (int i = 0; i < 2; ++i) {
+            const f32x4_t r0 = rc[i][0];
+            const f32x4_t r1 = rc[i][1];
+            if constexpr (CELL == CELL_LSTM) {
+              dh[i] = dhr[i] + r1[2];
+              dc[i] = cr[i] + r1[3] + dh[i] * r0[0];
+              da[0][i] = dc[i] * r0[1];
+              da[1][i] = dc[i] * r0[2];
+              da[2 % G][i] = dc[i] * r0[3];
+              da[3 % G][i] = dh[i] * r1[0];
+              cr[i] = dc[i] * r1[1];
+            } else if constexpr (CELL == CELL_GRU) {
+              dh[i] = dhr[i] + r1[0] + cr[i];
+              dc[i] = 0.0f;
+              da[0][i] = dh[i] * r0[0];
+              da[1 % G][i] = dh[i] * r0[1];
+              da[2 % G][i] = dh[i] * r0[2];
+              cr[i] = dh[i] * r0[3];
+            } else {
+              dh[i] = dhr[i] + r0[1];
+              dc[i] = 0.0f;
+              da[0][i] = dh[i] * r0[0];
+            }
+          }
+          uint32_t* sg = stage + ((s & 1) * 16 + pr) * SROW;
+#pragma unroll
+          for (int g = 0; g < G; ++g)
+            sg[(g * UW + 2 * pp2) >> 1] = (uint32_t)f2bf(da[g][0]) | ((uint32_t)f2bf(da[g][1]) << 16);
+          *reinterpret_cast<f32x4_t*>(rout + ((s & 1) * BR + pr) * UW * 2 + 4 * pp2) = f32x4_t{dh[0], dc[0], dh[1], dc[1]};
+        }
+      }
+    }
+    block_barrier();  // barrier s
+
+    // ---- B. the slice's da times the R columns of the slice, for every row d; publish
+    f32x4_t acc[MTW];
+#pragma unroll
+    for (int j = 0; j < MTW; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    // the stage reads go out before the abort flag is looked at (they are harmless if it is set)
+    const uint32_t* sg = stage + (s & 1) * 16 * SROW;
+    bf16x8_t bks[KTW];
+#pragma unroll
+    for (int kk = 0; kk < KTW; ++kk) bks[kk] = *reinterpret_cast<const bf16x8_t*>(sg + col * SROW + kk * 16 + 4 * quad);
+    if (uniform_flag(s_abort)) return;
+#pragma unroll
+    for (int kk = 0; kk < KTW; ++kk) {
+      const bf16x8_t bk = bks[kk];
+#pragma unroll
+      for (int j = 0; j < MTW; ++j) acc[j] = mfma_bf16(Ra[j][kk], bk, acc[j]);
+    }
+    if (col < nvalid) {
+      const uint32_t wtag = (uint32_t)(s + 1) & 0xFFFFu;
+      uint32_t* dst = xb + (s & 1) * xpar + (w * BR + col) * D;
+#pragma unroll
+      for (int j = 0; j < MTW; ++j) {
+        u32x4_t wv;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) wv[i] = ((uint32_t)f2bf(acc[j][i]) << 16) | wtag;
+        *reinterpret_cast<u32x4_t*>(dst + 16 * (wave * MTW + j) + 4 * quad) = wv;
+      }
+    }
+    // Keep the exchange stores ahead of the next step's polling in program order.
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  }
+}
+
+}  // namespace frnn

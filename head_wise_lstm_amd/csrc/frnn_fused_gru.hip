@@ -15,7 +15,16 @@ const FusedVariant kTable[] = {FRNN_FUSED_DESIGNS(FRNN_FV)};
 const FusedBwdVariant kBwdTable[] = {FRNN_FUSED_BWD_GRU(FRNN_FBV)};
 #undef FRNN_FBV
 
+#define FRNN_FBXV(NCW, MTW, KTW) \
+  {CELL_GRU, NCW, MTW, KTW, &fused_bwdx_kernel<CELL_GRU, NCW, MTW, KTW>},
+const FusedBwdxVariant kBwdxTable[] = {FRNN_FUSED_BWDX_GRU(FRNN_FBXV)};
+#undef FRNN_FBXV
+
 }  // namespace
+
+FusedBwdxTable fused_bwdx_table_gru() {
+  return FusedBwdxTable{kBwdxTable, (int)(sizeof(kBwdxTable) / sizeof(kBwdxTable[0]))};
+}
 
 FusedBwdTable fused_bwd_table_gru() { return FusedBwdTable{kBwdTable, (int)(sizeof(kBwdTable) / sizeof(kBwdTable[0]))}; }
 

@@ -15,7 +15,16 @@ const FusedVariant kTable[] = {FRNN_FUSED_DESIGNS(FRNN_FV)};
 const FusedBwdVariant kBwdTable[] = {FRNN_FUSED_BWD_LSTM(FRNN_FBV)};
 #undef FRNN_FBV
 
+#define FRNN_FBXV(NCW, MTW, KTW) \
+  {CELL_LSTM, NCW, MTW, KTW, &fused_bwdx_kernel<CELL_LSTM, NCW, MTW, KTW>},
+const FusedBwdxVariant kBwdxTable[] = {FRNN_FUSED_BWDX_LSTM(FRNN_FBXV)};
+#undef FRNN_FBXV
+
 }  // namespace
+
+FusedBwdxTable fused_bwdx_table_lstm() {
+  return FusedBwdxTable{kBwdxTable, (int)(sizeof(kBwdxTable) / sizeof(kBwdxTable[0]))};
+}
 
 FusedBwdTable fused_bwd_table_lstm() { return FusedBwdTable{kBwdTable, (int)(sizeof(kBwdTable) / sizeof(kBwdTable[0]))}; }
 

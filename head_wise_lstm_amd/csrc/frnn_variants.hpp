@@ -75,4 +75,29 @@ FusedBwdTable fused_bwd_table_lstm();
 FusedBwdTable fused_bwd_table_elman();
 FusedBwdTable fused_bwd_table_gru();
 
+// The partial-sum backward design, per cell: X(NCW, MTW, KTW) with NCW * MTW = D / 16 row tiles
+// and KTW * 32 = G * D / W (the workgroup's unit slice with all its gates).
+#define FRNN_FUSED_BWDX_LSTM(X)                                                                       \
+  X(8, 6, 3) X(6, 8, 3) X(8, 4, 2) X(8, 4, 4) X(4, 8, 2) X(8, 2, 1) X(8, 2, 2) X(8, 2, 4) \
+  X(4, 4, 2) X(4, 4, 4) X(8, 1, 1) X(8, 1, 2) X(8, 1, 4) X(4, 2, 1) X(4, 2, 2) X(4, 2, 4) X(4, 1, 1) \
+  X(4, 1, 2) X(4, 1, 4) X(6, 1, 2) X(6, 1, 4)
+#define FRNN_FUSED_BWDX_GRU(X) \
+  X(8, 6, 3) X(8, 4, 3) X(8, 2, 3) X(4, 4, 3) X(8, 1, 3) X(4, 2, 3) X(4, 1, 3) X(6, 1, 3)
+#define FRNN_FUSED_BWDX_ELMAN(X)                                                                      \
+  X(8, 6, 1) X(8, 4, 1) X(8, 2, 1) X(4, 4, 1) X(8, 1, 1) X(4, 2, 1) X(8, 1, 2) X(4, 2, 2) X(4, 1, 1)
+
+struct FusedBwdxVariant {
+  int cell, ncw, mtw, ktw;
+  fused_bwd_fn fn;
+};
+
+struct FusedBwdxTable {
+  const FusedBwdxVariant* v;
+  int n;
+};
+
+FusedBwdxTable fused_bwdx_table_lstm();
+FusedBwdxTable fused_bwdx_table_elman();
+FusedBwdxTable fused_bwdx_table_gru();
+
 }  // namespace frnn

@@ -221,12 +221,25 @@ def test_bwd_validation_and_workspace(lib):
 @pytest.mark.skipif(torch.cuda.is_available(), reason="planner model of a 256-CU, 8-die device (no GPU here)")
 def test_fused_bwd_planner(lib):
     """The fused backward splits a head's rows into 16-unit tiles over the workgroups of one die."""
+    # the partial-sum design where it has a plan: 32 workgroups of 24 units each, K = 4 x 24
     s = hw.frnn_bwd_plan_str(D(B=16, T=1024, N=1, Dm=768), 1)
-    assert "design=die-local" in s and "BR=2 " in s and "W=24 " in s and "NCW=8 KS=8 MTW=2 KTW=12" in s
+    assert "design=die-local-partials" in s and "BR=2 " in s and "W=32 " in s and "NCW=8 KS=1 MTW=6 KTW=3" in s
     s = hw.frnn_bwd_plan_str(D(B=16, T=1024, N=1, Dm=768, cell=2), 1)
-    assert "cell=gru" in s and "W=24 " in s and "KTW=9" in s
+    assert "design=die-local-partials" in s and "cell=gru" in s and "W=24 " in s and "KTW=3" in s
     s = hw.frnn_bwd_plan_str(D(B=8, T=1024, N=3, Dm=256), 1)
-    assert "design=die-local" in s
+    assert "design=die-local-partials" in s
+    # it needs more launches than the da exchange for twelve 64-unit Elman heads of 64 rows
+    s = hw.frnn_bwd_plan_str(D(B=64, T=8, N=12, Dm=64, cell=1), 1)
+    assert "design=die-local " in s and "chunks=2 " in s
+    # the da-exchange design, pinned: head split 24 ways, K = 4 x 768 split over 8 waves
+    os.environ["FRNN_FUSED_BWD_PX"] = "0"
+    try:
+        s = hw.frnn_bwd_plan_str(D(B=16, T=1024, N=1, Dm=768), 1)
+        assert "design=die-local " in s and "BR=2 " in s and "W=24 " in s and "NCW=8 KS=8 MTW=2 KTW=12" in s
+        s = hw.frnn_bwd_plan_str(D(B=16, T=1024, N=1, Dm=768, cell=2), 1)
+        assert "cell=gru" in s and "W=24 " in s and "KTW=9" in s
+    finally:
+        del os.environ["FRNN_FUSED_BWD_PX"]
     for (B, N, Dm, cell) in [(16, 1, 768, 0), (8, 3, 256, 0), (5, 2, 64, 0), (9, 2, 256, 2), (7, 2, 128, 1)]:
         s = hw.frnn_bwd_plan_str(D(B=B, T=8, N=N, Dm=Dm, cell=cell), 1)
         grid = int(re.search(r"grid=(\d+)", s).group(1))

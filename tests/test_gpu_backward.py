@@ -7,6 +7,7 @@ Bar, per gradient tensor X (dWx, dR, db, dstates0): max|X_gpu - X_oracle| <= tol
 max|X_oracle|), tol = 1e-4 for fp32 inputs and 3e-2 for bf16 inputs (the forward's bars, taken
 relative to the tensor's scale: dR and db are sums over all B*T steps and grow with them).
 """
+import os
 import sys
 
 import numpy as np
@@ -38,7 +39,30 @@ def _log(msg):
     sys.stdout.flush()
 
 
-def run_bwd_case(w, path="alternating"):
+class _env:
+    """Set environment variables (planner overrides) for the duration of a block."""
+
+    def __init__(self, env):
+        self.env = {k: str(v) for k, v in (env or {}).items()}
+
+    def __enter__(self):
+        self.old = {k: os.environ.get(k) for k in self.env}
+        os.environ.update(self.env)
+
+    def __exit__(self, *exc):
+        for k, v in self.old.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+
+
+def run_bwd_case(w, path="alternating", env=None):
+    with _env(env):
+        return _run_bwd_case(w, path)
+
+
+def _run_bwd_case(w, path):
     hw = _hw()
     x = fi.make_inputs(w)
     ct = fi.backward_cotangents(w)
@@ -116,6 +140,46 @@ def test_bwd_full(name, path):
     run_bwd_case(w, path)
 
 
+# Both fused backward designs on the small cases: the partial-sum design (the planner's choice
+# where it has one) and the da-exchange design, pinned with FRNN_FUSED_BWD_PX.
+@pytest.mark.parametrize("px", [1, 0])
+@pytest.mark.parametrize("w", [x for x in SMALL if x.dtype == torch.bfloat16], ids=lambda w: w.name)
+def test_bwd_small_each_design(w, px):
+    with _env({"FRNN_FUSED_BWD_PX": px}):
+        plan = _fused_plan_or_skip(w)
+    assert ("die-local-partials" in plan) == bool(px), plan
+    run_bwd_case(w, "fused", env={"FRNN_FUSED_BWD_PX": px})
+
+
+# The partial-sum design forced onto shapes and splits the planner would not pick: several rows
+# per group, a ragged last block, units per workgroup from 8 to 64, every cell.
+PX_FORCED = [
+    (fi.HeadwiseWorkload("px_lstm_D256_W16_BR4", "lstm", torch.bfloat16, B=7, T=9, N=2, D=256, seed=281, s0_var=1.0),
+     {"FRNN_FUSED_BWD_W": 16, "FRNN_FUSED_BWD_BR": 4}),
+    (fi.HeadwiseWorkload("px_lstm_D768_BR3", "lstm", torch.bfloat16, B=7, T=6, N=1, D=768, seed=282, s0_var=1.0),
+     {"FRNN_FUSED_BWD_W": 32, "FRNN_FUSED_BWD_BR": 3}),
+    (fi.HeadwiseWorkload("px_lstm_D128_W16", "lstm", torch.bfloat16, B=5, T=8, N=2, D=128, seed=283, s0_var=1.0),
+     {"FRNN_FUSED_BWD_W": 16, "FRNN_FUSED_BWD_BR": 2}),
+    (fi.HeadwiseWorkload("px_lstm_D768_6waves", "lstm", torch.bfloat16, B=4, T=7, N=1, D=768, seed=284, s0_var=1.0),
+     {"FRNN_FUSED_BWD_W": 32, "FRNN_FUSED_BWD_NCW": 6}),
+    (fi.HeadwiseWorkload("px_gru_D256_W8_BR3", "gru", torch.bfloat16, B=8, T=9, N=2, D=256, seed=285, s0_var=1.0),
+     {"FRNN_FUSED_BWD_W": 8, "FRNN_FUSED_BWD_BR": 3}),
+    (fi.HeadwiseWorkload("px_elman_D128_W2", "elman", torch.bfloat16, B=5, T=10, N=2, D=128, seed=286, s0_var=1.0),
+     {"FRNN_FUSED_BWD_W": 2, "FRNN_FUSED_BWD_BR": 2}),
+    (fi.HeadwiseWorkload("px_elman_D768", "elman", torch.bfloat16, B=6, T=8, N=1, D=768, seed=287, s0_var=1.0),
+     {"FRNN_FUSED_BWD_W": 24, "FRNN_FUSED_BWD_BR": 3}),
+]
+
+
+@pytest.mark.parametrize("w,env", PX_FORCED, ids=lambda x: getattr(x, "name", ""))
+def test_bwd_partials_forced(w, env):
+    env = dict(env, FRNN_FUSED_BWD_PX=1)
+    with _env(env):
+        plan = _fused_plan_or_skip(w)
+    assert "die-local-partials" in plan and f"W={env['FRNN_FUSED_BWD_W']} " in plan, plan
+    run_bwd_case(w, "fused", env=env)
+
+
 @pytest.mark.timeout(300)
 @pytest.mark.parametrize("cell", ["lstm", "gru", "elman"])
 def test_bwd_long_sequence_past_tag_wrap(cell):
@@ -126,17 +190,24 @@ def test_bwd_long_sequence_past_tag_wrap(cell):
     run_bwd_case(w, "fused")
 
 
-@pytest.mark.parametrize("w,chunks", [
-    (fi.HeadwiseWorkload("bwd_gru_chunks_B40", "gru", torch.bfloat16, B=40, T=8, N=1, D=768, seed=251, s0_var=1.0), 3),
-    (fi.HeadwiseWorkload("bwd_lstm_chunks_B40", "lstm", torch.bfloat16, B=40, T=6, N=1, D=768, seed=252, s0_var=1.0), 3),
-    (fi.HeadwiseWorkload("bwd_elman_chunks_B64_N12", "elman", torch.bfloat16, B=64, T=16, N=12, D=64, seed=253,
-                         s0_var=1.0), 2),
+_CH_GRU = fi.HeadwiseWorkload("bwd_gru_chunks_B40", "gru", torch.bfloat16, B=40, T=8, N=1, D=768, seed=251, s0_var=1.0)
+_CH_LSTM = fi.HeadwiseWorkload("bwd_lstm_chunks_B40", "lstm", torch.bfloat16, B=40, T=6, N=1, D=768, seed=252,
+                               s0_var=1.0)
+_CH_ELMAN = fi.HeadwiseWorkload("bwd_elman_chunks_B64_N12", "elman", torch.bfloat16, B=64, T=16, N=12, D=64, seed=253,
+                                s0_var=1.0)
+
+
+@pytest.mark.parametrize("w,px,chunks", [
+    (_CH_GRU, 0, 3), (_CH_LSTM, 0, 3), (_CH_ELMAN, 0, 2),
+    (_CH_GRU, 1, 2), (_CH_LSTM, 1, 2), (_CH_ELMAN, 1, 4),
 ], ids=lambda x: getattr(x, "name", str(x)))
-def test_bwd_fused_chunks(w, chunks):
-    """A batch whose groups cannot all be co-resident runs the fused serial part in chunks of rows."""
-    plan = _fused_plan_or_skip(w)
-    assert f"chunks={chunks} " in plan, plan
-    run_bwd_case(w, "fused")
+def test_bwd_fused_chunks(w, px, chunks):
+    """A batch whose groups cannot all be co-resident runs the fused serial part in chunks of rows
+    (both designs)."""
+    with _env({"FRNN_FUSED_BWD_PX": px}):
+        plan = _fused_plan_or_skip(w)
+    assert f"chunks={chunks} " in plan and ("die-local-partials" in plan) == bool(px), plan
+    run_bwd_case(w, "fused", env={"FRNN_FUSED_BWD_PX": px})
 
 
 def test_bwd_fused_matches_alternating():
