@@ -71,8 +71,12 @@ def _run_bwd_case(w, path):
     _log(f"bwd case {w.name} cell={w.cell} B={w.B} T={w.T} N={w.N} D={w.D} path={path}")
     if path == "fused":
         _log("  plan: " + hw.frnn_bwd_plan_str(hw._desc(w.B, w.T, w.N, w.D, w.cell, w.dtype), "fused"))
-    st, last = hw.frnn_fwd(g(x["Wx"]), g(x["R"]), g(x["b"]), g(x["states0"]), cell=w.cell, path="fused"
-                           if w.dtype == torch.bfloat16 or w.D <= 64 else "alternating")
+    try:  # the forward on the fused path where it has a design
+        hw.frnn_plan_str(hw._desc(w.B, w.T, w.N, w.D, w.cell, w.dtype), "fused")
+        fwd_path = "fused"
+    except hw.FrnnError:
+        fwd_path = "alternating"
+    st, last = hw.frnn_fwd(g(x["Wx"]), g(x["R"]), g(x["b"]), g(x["states0"]), cell=w.cell, path=fwd_path)
     grads = hw.frnn_bwd(g(x["Wx"]), g(x["R"]), g(x["b"]), g(x["states0"]), st, g(ct["dstates"]), g(ct["dlast"]),
                         cell=w.cell, path=path)
     torch.cuda.synchronize()
@@ -178,6 +182,26 @@ def test_bwd_partials_forced(w, env):
         plan = _fused_plan_or_skip(w)
     assert "die-local-partials" in plan and f"W={env['FRNN_FUSED_BWD_W']} " in plan, plan
     run_bwd_case(w, "fused", env=env)
+
+
+# Extreme shapes (as in the forward tests): D = 1024, many narrow heads, wide batches.
+BWD_EXTREME = [
+    fi.HeadwiseWorkload("bwd_lstm_D1024", "lstm", torch.bfloat16, B=2, T=6, N=1, D=1024, seed=301, s0_var=1.0),
+    fi.HeadwiseWorkload("bwd_gru_D1024", "gru", torch.bfloat16, B=3, T=5, N=1, D=1024, seed=302, s0_var=1.0),
+    fi.HeadwiseWorkload("bwd_lstm_N48_D32", "lstm", torch.bfloat16, B=3, T=9, N=48, D=32, seed=303, s0_var=1.0),
+    fi.HeadwiseWorkload("bwd_elman_N40_D64", "elman", torch.bfloat16, B=5, T=9, N=40, D=64, seed=304, s0_var=1.0),
+    fi.HeadwiseWorkload("bwd_lstm_B300_D64", "lstm", torch.bfloat16, B=300, T=5, N=1, D=64, seed=305, s0_var=1.0),
+    fi.HeadwiseWorkload("bwd_gru_B130_N2_D256", "gru", torch.bfloat16, B=130, T=5, N=2, D=256, seed=306,
+                        s0_var=1.0),
+]
+
+
+@pytest.mark.parametrize("path", ["alternating", "fused"])
+@pytest.mark.parametrize("w", BWD_EXTREME, ids=lambda w: w.name)
+def test_bwd_extreme_shapes(w, path):
+    if path == "fused":
+        _fused_plan_or_skip(w)
+    run_bwd_case(w, path)
 
 
 @pytest.mark.timeout(300)

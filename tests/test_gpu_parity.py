@@ -253,6 +253,32 @@ def test_long_sequence_past_tag_wrap(cell, env):
     run_case(w, "fused", env=env)
 
 
+# Extreme shapes: the widest head the boundary takes (D = 1024; no fused design, alternating
+# only), many narrow heads, and batches far past one launch's co-resident rows.
+EXTREME = [
+    fi.HeadwiseWorkload("lstm_D1024", "lstm", torch.bfloat16, B=2, T=6, N=1, D=1024, seed=291, s0_var=1.0),
+    fi.HeadwiseWorkload("gru_D1024", "gru", torch.bfloat16, B=3, T=6, N=1, D=1024, seed=292, s0_var=1.0),
+    fi.HeadwiseWorkload("elman_D1024", "elman", torch.bfloat16, B=3, T=7, N=1, D=1024, seed=293, s0_var=1.0),
+    fi.HeadwiseWorkload("lstm_N48_D32", "lstm", torch.bfloat16, B=3, T=9, N=48, D=32, seed=294, s0_var=1.0),
+    fi.HeadwiseWorkload("elman_N40_D64", "elman", torch.bfloat16, B=5, T=9, N=40, D=64, seed=295, s0_var=1.0),
+    fi.HeadwiseWorkload("lstm_B300_D64", "lstm", torch.bfloat16, B=300, T=5, N=1, D=64, seed=296, s0_var=1.0),
+    fi.HeadwiseWorkload("gru_B130_N2_D256", "gru", torch.bfloat16, B=130, T=5, N=2, D=256, seed=297, s0_var=1.0),
+]
+
+
+@pytest.mark.parametrize("path", ["alternating", "fused"])
+@pytest.mark.parametrize("w", EXTREME, ids=lambda w: w.name)
+def test_extreme_shapes(w, path):
+    hw = _hw()
+    if path == "fused":
+        try:
+            hw.frnn_plan_str(hw._desc(w.B, w.T, w.N, w.D, w.cell, w.dtype), "fused")
+        except hw.FrnnError as e:
+            assert e.status == -2 and w.D == 1024, (w.name, e)
+            pytest.skip("no fused forward design for D = 1024 (the alternating path takes it)")
+    run_case(w, path)
+
+
 def test_repeat_calls_reuse_workspace():
     """Back-to-back calls on one workspace: the exchange buffer holds the previous call's tags."""
     hw = _hw()
