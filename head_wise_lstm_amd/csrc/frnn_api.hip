@@ -339,6 +339,13 @@ hipError_t launch_fill(void* p, size_t bytes, hipStream_t st, uint32_t value = 0
 template <typename E>
 void launch_transpose(const E* src, long long lds, int K, int Nc, E* dst, long long ldd, hipStream_t st) {
   if (K <= 0 || Nc <= 0) return;
+  if (sizeof(E) == 2 && lds % 4 == 0 && ldd % 4 == 0 && !(reinterpret_cast<uintptr_t>(src) & 7) &&
+      !(reinterpret_cast<uintptr_t>(dst) & 7)) {
+    const int ty = (int)std::min<long long>(((long long)K + 63) / 64, 65535);
+    hipLaunchKernelGGL(transpose_b16_kernel, dim3((Nc + 63) / 64, ty), dim3(256), 0, st,
+                       reinterpret_cast<const uint16_t*>(src), lds, K, Nc, reinterpret_cast<uint16_t*>(dst), ldd);
+    return;
+  }
   const int ty = (int)std::min<long long>(((long long)K + 31) / 32, 65535);
   hipLaunchKernelGGL(transpose_kernel<E>, dim3((Nc + 31) / 32, ty), dim3(256), 0, st, src, lds, K, Nc, dst, ldd);
 }
@@ -827,11 +834,17 @@ int run_backward(const BwdProblem& q, int path, const FusedBwdPlan& fbp, const D
   char* daT = base + L.daT;
   float* tmp = reinterpret_cast<float*>(base + L.tmp);
   float* hr = reinterpret_cast<float*>(base + L.hr);
-  // carried gradients start at zero; da's rows past T*B stay zero for the dR GEMM
+  // carried gradients start at zero
   if (launch_fill(base + L.zeros, 256, st) != hipSuccess ||
-      launch_fill(a.dhpart, (size_t)BWD_KS * BND * 4, st) != hipSuccess || launch_fill(a.carry, (size_t)BND * 4, st) != hipSuccess ||
-      launch_fill(a.da, (size_t)N * Kp * G * D * elt, st) != hipSuccess)
+      launch_fill(a.dhpart, (size_t)BWD_KS * BND * 4, st) != hipSuccess || launch_fill(a.carry, (size_t)BND * 4, st) != hipSuccess)
     return FRNN_EHIP;
+  // da's rows past T*B (padding to whole k-tiles of every dR part) must read zero
+  if ((size_t)Kp > (size_t)T * B) {
+    for (int n = 0; n < N; ++n)
+      if (launch_fill(static_cast<char*>(a.da) + ((size_t)n * Kp + (size_t)T * B) * G * D * elt,
+                      ((size_t)Kp - (size_t)T * B) * G * D * elt, st) != hipSuccess)
+        return FRNN_EHIP;
+  }
   // 1. h_{t-1} for every step, R^T, and h.R for every step
   hipLaunchKernelGGL(bwd_hprev_kernel, dim3((unsigned)std::min<long long>(((long long)N * Kp * D + 255) / 256, 65536)),
                      dim3(256), 0, st, a);

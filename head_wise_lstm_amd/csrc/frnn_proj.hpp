@@ -59,6 +59,58 @@ __global__ void __launch_bounds__(256) transpose_kernel(const E* src, long long 
   }
 }
 
+// dst[j][k] = src[k][j] for 16-bit elements on 64 x 64 tiles: every global access is 4
+// consecutive elements (8 bytes) of a row, so a wave moves 512 contiguous-in-rows bytes per
+// instruction instead of 128. Needs src, dst 8-byte aligned and lds, ldd multiples of 4; tiles
+// that cross the K or Nc edge move element by element. Grid (ceil(Nc/64), min(ceil(K/64), 65535)).
+__global__ void __launch_bounds__(256) transpose_b16_kernel(const uint16_t* src, long long lds, int K, int Nc,
+                                                            uint16_t* dst, long long ldd) {
+  __shared__ __attribute__((aligned(16))) uint16_t s[64][68];
+  const int n0 = blockIdx.x * 64;
+  const int t = threadIdx.x, r = t >> 4, c4 = (t & 15) * 4;  // row r + 16 i, 4 elements from c4
+  for (int kb = blockIdx.y; kb * 64 < K; kb += gridDim.y) {
+    const int k0 = kb * 64;
+    const bool full = k0 + 64 <= K && n0 + 64 <= Nc;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int k = k0 + r + 16 * i;
+      uint2 v;
+      if (full) {
+        v = *reinterpret_cast<const uint2*>(src + (long long)k * lds + n0 + c4);
+      } else {
+        uint16_t e[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int n = n0 + c4 + q;
+          e[q] = (k < K && n < Nc) ? src[(long long)k * lds + n] : (uint16_t)0;
+        }
+        v.x = (uint32_t)e[0] | ((uint32_t)e[1] << 16);
+        v.y = (uint32_t)e[2] | ((uint32_t)e[3] << 16);
+      }
+      *reinterpret_cast<uint2*>(&s[r + 16 * i][c4]) = v;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int j = r + 16 * i;  // output row (input column n0 + j), 4 elements from k0 + c4
+      uint2 v;
+      v.x = (uint32_t)s[c4][j] | ((uint32_t)s[c4 + 1][j] << 16);
+      v.y = (uint32_t)s[c4 + 2][j] | ((uint32_t)s[c4 + 3][j] << 16);
+      const int n = n0 + j;
+      if (full) {
+        *reinterpret_cast<uint2*>(dst + (long long)n * ldd + k0 + c4) = v;
+      } else if (n < Nc) {
+        const uint16_t e[4] = {(uint16_t)(v.x & 0xFFFFu), (uint16_t)(v.x >> 16), (uint16_t)(v.y & 0xFFFFu),
+                               (uint16_t)(v.y >> 16)};
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (k0 + c4 + q < K) dst[(long long)n * ldd + k0 + c4 + q] = e[q];
+      }
+    }
+    __syncthreads();
+  }
+}
+
 // dst[j][k] = bf16(src[k][j]) for fp32 src (as transpose_kernel, rounding to nearest even).
 __global__ void __launch_bounds__(256) transpose_f32_bf16_kernel(const float* src, long long lds, int K, int Nc,
                                                                  uint16_t* dst, long long ldd) {
