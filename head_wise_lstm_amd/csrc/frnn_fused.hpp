@@ -20,9 +20,10 @@
 // h exchange between the W workgroups of a group (W > 1): every group is placed on one
 // accelerator die (XCD), whose L2 is shared by its 32 CUs. A new h value travels as a 32-bit word
 // (bf16 << 16 | step tag) written with a plain store (CU caches are write-through to the die's L2)
-// and is read back with 64-bit agent-scope atomic loads, which bypass the reader's CU cache. Every
-// 32-bit half carries its own tag, so a reader needs no flag, fence or second round trip: a word
-// is either the current step's or it is polled again. Two parities of the buffer alternate by
+// and is read back with 8- or 16-byte loads that bypass the reader's CU cache (cache policy sc1,
+// the coherence of an agent-scope atomic load). Every 32-bit word carries its own tag, so a reader
+// needs no flag, fence or second round trip: a word is either the current step's or it is polled
+// again, and a wide load that sees words of two steps is just polled again. Two parities of the buffer alternate by
 // step. Placement is checked against the hardware XCC id; a workgroup on the wrong die reports an
 // error instead of computing. Every wait is bounded by a wall-clock limit.
 //
@@ -130,6 +131,13 @@ constexpr int FUSED_PART_ROW = 65;  // f32x4 entries per wave's packed partials 
 // Most batch rows per group a die-local design takes.
 __host__ __device__ constexpr int fused_max_br(int ks, int mtw) {
   return ks > 1 ? (fused_brp(ks, mtw) < FUSED_DIE_MAX_BR ? fused_brp(ks, mtw) : FUSED_DIE_MAX_BR) : FUSED_DIE_MAX_BR;
+}
+
+// Words (units) one lane polls per load: 16 bytes where that takes fewer loads per lane than 8
+// bytes (measured: D=768 B=16, 1.32 -> 1.21 us per step), else 8 (wider loads on fewer lanes
+// measured 1-3 % slower where the count of loads is the same).
+__host__ __device__ constexpr int fused_poll_words(int ks, int mtw, int ktw) {
+  return (fused_max_br(ks, mtw) * ktw * 16 + 63) / 64 > (fused_max_br(ks, mtw) * ktw * 8 + 63) / 64 ? 4 : 2;
 }
 
 // Byte offsets of the LDS regions (identical on host and device).
@@ -611,45 +619,62 @@ __global__ void __launch_bounds__((NCW + 1) * 64, 1) fused_fwd_kernel(FusedArgs 
       }
     } else if constexpr (!F32) {
       // Poll this wave's K range (KTW k-tiles of 32 units) for the group's nvalid rows with all
-      // 64 lanes, a few 64-bit words each; once every word carries this step's tag they are
-      // unpacked into the wave's LDS stage, from which the MFMA B fragments are read. (Taking
-      // k-tiles as they complete, in order, measured slower: the longer rounds poll less often.)
+      // 64 lanes, PW words (PW units) per lane and load, with loads that bypass the CU cache
+      // (the coherence of an agent-scope atomic load). Each 32-bit word carries its own tag, so
+      // a load that sees some words of this step and some of the last is simply polled again.
+      // Once every word carries this step's tag the values are unpacked into the wave's LDS
+      // stage, from which the MFMA B fragments are read.
       const int pp = (t - 1) & 1;
       const uint32_t tag = (uint32_t)t & 0xFFFFu;
-      constexpr int WPR = KTW * 16;                                // 64-bit words per row
-      constexpr int NP = (fused_max_br(KS, MTW) * WPR + 63) / 64;  // words per lane (upper bound)
+      constexpr int PW = fused_poll_words(KS, MTW, KTW);
+      constexpr int WPR = KTW * 32 / PW;                            // loads per row
+      constexpr int NP = (fused_max_br(KS, MTW) * WPR + 63) / 64;  // loads per lane (bound)
       constexpr int SROW = fused_stage_row(KTW);
+      typedef uint32_t pw_t __attribute__((ext_vector_type(PW)));
       uint32_t* stage = reinterpret_cast<uint32_t*>(smem + lay.h) + wave * 16 * SROW;
-      const uint64_t* src = reinterpret_cast<const uint64_t*>(xb + pp * xpar) + ks * WPR;
+      const __amdgpu_buffer_rsrc_t xr =
+          __builtin_amdgcn_make_buffer_rsrc(xb, (short)0, 2 * xpar * 4, 0x00020000);
+      const int soff = pp * xpar * 4;
       const int nw = nvalid * WPR;
-      // Every round re-reads all of the lane's words (a word, once current, stays current until
-      // this workgroup has published its own h of this step), and a lane without a word re-reads
-      // word 0, so that no load sits under a lane mask or depends on the last round.
-      uint32_t off[NP];
+      // A lane without a load of its own re-reads the first one and checks nothing, so that no
+      // load sits under a lane mask and the check needs no branch.
+      int voff[NP], sidx[NP];
+      uint32_t tmask[NP];
 #pragma unroll
       for (int e = 0; e < NP; ++e) {
         const int wi = lane + 64 * e, r = wi / WPR, wr = wi - r * WPR;
-        off[e] = wi < nw ? (uint32_t)(r * (D / 2) + wr) : 0u;  // 32-bit offsets from a uniform base
+        const bool ok = wi < nw;
+        voff[e] = ((ok ? r * D + wr * PW : 0) + ks * KTW * 32) * 4;
+        tmask[e] = ok ? 0xFFFFu : 0u;
+        sidx[e] = ok ? r * SROW + wr * (PW / 2) : -1;
       }
-      uint64_t v[NP];
+      pw_t v[NP];
       long long t_first = 0;
       int spins = 0;
       // nothing can have arrived yet (a store takes a few hundred ns to show on another CU)
       if (t > 0) __builtin_amdgcn_s_sleep(FRNN_POLL_SLEEP0);
       while (true) {
 #pragma unroll
-        for (int e = 0; e < NP; ++e) v[e] = __hip_atomic_load(src + off[e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        bool ok = true;
+        for (int e = 0; e < NP; ++e) {
+          if constexpr (PW == 4) v[e] = __builtin_amdgcn_raw_buffer_load_b128(xr, voff[e], soff, 16);
+          else v[e] = __builtin_amdgcn_raw_buffer_load_b64(xr, voff[e], soff, 16);
+        }
+        uint32_t bad = 0;
 #pragma unroll
         for (int e = 0; e < NP; ++e) {
-          const uint32_t lo = (uint32_t)v[e], hi = (uint32_t)(v[e] >> 32);
-          if (lane + 64 * e < nw && (((lo ^ tag) | (hi ^ tag)) & 0xFFFFu) != 0) ok = false;
+          uint32_t x = 0;
+#pragma unroll
+          for (int i = 0; i < PW; ++i) x |= v[e][i] ^ tag;
+          bad |= x & tmask[e];
         }
-        if (__all(ok)) {
+        if (__all(bad == 0)) {
 #pragma unroll
           for (int e = 0; e < NP; ++e) {
-            const int wi = lane + 64 * e, r = wi / WPR, wr = wi - r * WPR;
-            if (wi < nw) stage[r * SROW + wr] = pack_hi((uint32_t)v[e], (uint32_t)(v[e] >> 32));
+            if (sidx[e] < 0) continue;
+            if constexpr (PW == 4)
+              *reinterpret_cast<uint2*>(stage + sidx[e]) = make_uint2(pack_hi(v[e][0], v[e][1]), pack_hi(v[e][2], v[e][3]));
+            else
+              stage[sidx[e]] = pack_hi(v[e][0], v[e][1]);
           }
           break;
         }
