@@ -91,12 +91,19 @@ struct FusedArgs {
   } while (0)
 #endif
 
-constexpr int FUSED_IO_STAGES = 4;   // Wx steps in flight in the I/O wave
+constexpr int FUSED_IO_STAGES = 4;   // record steps in flight in the backward's I/O wave
 // max 64-bit Wx words (and output pairs) one I/O lane moves per step: the die-local design moves
 // few (its workgroups own few units), the single-workgroup design a whole head's rows (an Elman
 // head has a quarter of an LSTM head's Wx and half its outputs). Every slot costs a load per step.
 __host__ __device__ constexpr int fused_epl(bool local, int ncw, int cell) {
   return !local ? 2 : (cell == CELL_ELMAN ? 2 : (ncw == 4 ? 8 : 4));
+}
+
+// Wx steps in flight in the forward's I/O wave: eight where a lane moves at most two words a step
+// (measured against four: Elman B=64 N=12 D=64 0.432 -> 0.394 us per step, LSTM B=16 D=768
+// 1.223 -> 1.200), four where it moves more (eight stages of those spill registers).
+__host__ __device__ constexpr int fused_io_stages(bool local, int ncw, int cell) {
+  return fused_epl(local, ncw, cell) <= 2 ? 8 : 4;
 }
 
 __host__ __device__ constexpr int fused_hpad(bool f32) { return f32 ? 4 : 8; }
@@ -342,16 +349,15 @@ __device__ __forceinline__ void io_store(const IoCtx& c, const IoDesc<CELL, NCW,
 
 // One ring stage: interval k writes Wx of step k+1-G0 into LDS (and refills the stage with step
 // k+1-G0+L), stores the outputs of step k-1-G0, then joins the step's barrier.
-template <int CELL, int NCW, int KS, int MTW, int EPL, int G0, int ST>
+template <int CELL, int NCW, int KS, int MTW, int EPL, int G0, int L, int ST>
 __device__ __forceinline__ bool io_interval(const IoCtx& c, const IoDesc<CELL, NCW, KS, MTW, EPL>& d, int k,
-                                            io_word_t (&raw)[FUSED_IO_STAGES][EPL], f32x4_t* wxs,
+                                            io_word_t (&raw)[L][EPL], f32x4_t* wxs,
                                             const f32x4_t* outs, const int* abort_flag) {
-  constexpr int L = FUSED_IO_STAGES;
   const int s_wx = k + 1 - G0;
   if (s_wx >= 0 && s_wx < c.T) io_put<CELL, NCW, KS, MTW, EPL>(c, d, s_wx, raw[ST], wxs);
   // Every interval issues the same loads (outside the range the step is clamped and the reload
   // is never used), so that the compiler can count the loads in flight on every path and wait
-  // for the one four intervals back only.
+  // for the one L intervals back only.
   io_issue<CELL, NCW, KS, MTW, EPL>(c, d, min(max(s_wx + L, 0), c.T - 1), raw[ST]);
   const int s_out = k - 1 - G0;
   if (s_out >= 0 && s_out < c.T) io_store<CELL, NCW, KS, MTW, EPL>(c, d, s_out, outs);
@@ -359,40 +365,47 @@ __device__ __forceinline__ bool io_interval(const IoCtx& c, const IoDesc<CELL, N
   return uniform_flag(*abort_flag);
 }
 
-// The I/O wave: runs barriers -1 .. T in step with the compute waves (see the kernel).
-template <int CELL, int NCW, int KS, int MTW, int EPL, int G0>
+// Intervals k + J .. k + L - 1 (TAIL: only those up to T). Interval k + j uses stage
+// (j - G0) mod L, which holds the Wx step that interval writes. Returns true on abort.
+template <int CELL, int NCW, int KS, int MTW, int EPL, int G0, int L, int J, bool TAIL>
+__device__ __forceinline__ bool io_intervals(const IoCtx& c, const IoDesc<CELL, NCW, KS, MTW, EPL>& d, int k,
+                                             io_word_t (&raw)[L][EPL], f32x4_t* wxs, const f32x4_t* outs,
+                                             const int* abort_flag) {
+  if constexpr (J < L) {
+    constexpr int ST = ((J - G0) % L + L) % L;
+    if (TAIL && k + J > c.T) return false;
+    if (io_interval<CELL, NCW, KS, MTW, EPL, G0, L, ST>(c, d, k + J, raw, wxs, outs, abort_flag)) return true;
+    return io_intervals<CELL, NCW, KS, MTW, EPL, G0, L, J + 1, TAIL>(c, d, k, raw, wxs, outs, abort_flag);
+  }
+  return false;
+}
+
+// The I/O wave: runs barriers -1 .. T in step with the compute waves (see the kernel), with L
+// Wx steps in flight.
+template <int CELL, int NCW, int KS, int MTW, int EPL, int G0, int L>
 __device__ __forceinline__ void io_wave(const IoCtx& c, f32x4_t* wxs, const f32x4_t* outs, const int* abort_flag) {
-  constexpr int L = FUSED_IO_STAGES;
-  static_assert(L == 4, "the interval loop below is unrolled for four stages");
   IoDesc<CELL, NCW, KS, MTW, EPL> d;
   d.init(c);
   io_word_t raw[L][EPL];
-  // k runs -1 .. T; the stage of the Wx step written in interval k is (k + 1 - G0) mod 4, and
-  // stage s first holds step s. The first loads go out in the stage order of intervals -1, 0, 1,
-  // 2, as they do in the loop, so that the loop is entered with the same loads in flight.
-  constexpr int S0 = ((0 - G0) % L + L) % L, S1 = ((1 - G0) % L + L) % L;
-  constexpr int S2 = ((2 - G0) % L + L) % L, S3 = ((3 - G0) % L + L) % L;
   if (c.T == 0) {  // intervals -1 and 0: the compute waves' two barriers, nothing to move
     block_barrier();
     block_barrier();
     return;
   }
-  io_issue<CELL, NCW, KS, MTW, EPL>(c, d, min(S0, c.T - 1), raw[S0]);
-  io_issue<CELL, NCW, KS, MTW, EPL>(c, d, min(S1, c.T - 1), raw[S1]);
-  io_issue<CELL, NCW, KS, MTW, EPL>(c, d, min(S2, c.T - 1), raw[S2]);
-  io_issue<CELL, NCW, KS, MTW, EPL>(c, d, min(S3, c.T - 1), raw[S3]);
-  // Whole groups of four intervals in the loop (no exit inside the body, so every path into an
-  // interval has the same loads in flight), then at most three more.
-  int k = -1;
-  for (; k + 3 <= c.T; k += L) {
-    if (io_interval<CELL, NCW, KS, MTW, EPL, G0, S0>(c, d, k, raw, wxs, outs, abort_flag)) return;
-    if (io_interval<CELL, NCW, KS, MTW, EPL, G0, S1>(c, d, k + 1, raw, wxs, outs, abort_flag)) return;
-    if (io_interval<CELL, NCW, KS, MTW, EPL, G0, S2>(c, d, k + 2, raw, wxs, outs, abort_flag)) return;
-    if (io_interval<CELL, NCW, KS, MTW, EPL, G0, S3>(c, d, k + 3, raw, wxs, outs, abort_flag)) return;
+  // k runs -1 .. T; the stage of the Wx step written in interval k is (k + 1 - G0) mod L, and
+  // stage s first holds step s. The first loads go out in the stage order of intervals -1 ..
+  // L - 2, as they do in the loop, so that the loop is entered with the same loads in flight.
+#pragma unroll
+  for (int j = 0; j < L; ++j) {
+    const int st = ((j - G0) % L + L) % L;
+    io_issue<CELL, NCW, KS, MTW, EPL>(c, d, min(st, c.T - 1), raw[st]);
   }
-  if (k <= c.T && io_interval<CELL, NCW, KS, MTW, EPL, G0, S0>(c, d, k, raw, wxs, outs, abort_flag)) return;
-  if (k + 1 <= c.T && io_interval<CELL, NCW, KS, MTW, EPL, G0, S1>(c, d, k + 1, raw, wxs, outs, abort_flag)) return;
-  if (k + 2 <= c.T && io_interval<CELL, NCW, KS, MTW, EPL, G0, S2>(c, d, k + 2, raw, wxs, outs, abort_flag)) return;
+  // Whole groups of L intervals in the loop (no exit inside the body, so every path into an
+  // interval has the same loads in flight), then at most L - 1 more.
+  int k = -1;
+  for (; k + L - 1 <= c.T; k += L)
+    if (io_intervals<CELL, NCW, KS, MTW, EPL, G0, L, 0, false>(c, d, k, raw, wxs, outs, abort_flag)) return;
+  if (io_intervals<CELL, NCW, KS, MTW, EPL, G0, L, 0, true>(c, d, k, raw, wxs, outs, abort_flag)) return;
   if (G0 == 1 && c.T >= 1) io_store<CELL, NCW, KS, MTW, EPL>(c, d, c.T - 1, outs);
 }
 
@@ -490,7 +503,7 @@ __global__ void __launch_bounds__((NCW + 1) * 64, 1) fused_fwd_kernel(FusedArgs 
     c.U_wg = U_wg;
     c.u_base = u_base;
     c.lane = lane;
-    io_wave<CELL, NCW, KS, MTW, fused_epl(LOCAL, NCW, CELL), G0>(c, wxs, outs, &s_abort);
+    io_wave<CELL, NCW, KS, MTW, fused_epl(LOCAL, NCW, CELL), G0, fused_io_stages(LOCAL, NCW, CELL)>(c, wxs, outs, &s_abort);
     return;
   }
 
@@ -689,6 +702,8 @@ __global__ void __launch_bounds__((NCW + 1) * 64, 1) fused_fwd_kernel(FusedArgs 
           }
         }
       }
+      FRNN_TRACE(7);
+      FRNN_TRACE_RT(7);
 #pragma unroll
       for (int kk = 0; kk < KTW; ++kk) {
         const bf16x8_t bk = *reinterpret_cast<const bf16x8_t*>(stage + col * SROW + kk * 16 + 4 * quad);
