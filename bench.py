@@ -52,15 +52,19 @@ def kernel_sources_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def _counter_mean(csv_path: str, name_part: str) -> tuple:
-    """Mean Counter_Value (KiB per dispatch) over the dispatches of the kernels whose name holds name_part."""
+def _counter_mean(csv_path: str, name_part: str, last: int = 0) -> tuple:
+    """Mean Counter_Value (KiB per dispatch) over the dispatches of the kernels whose name holds
+    name_part (only the last `last` of them, in dispatch order, when last > 0)."""
     import csv
-    vals, names = [], set()
+    rows = []
     with open(csv_path, newline="") as f:
         for row in csv.DictReader(f):
             if name_part in row["Kernel_Name"]:
-                vals.append(float(row["Counter_Value"]))
-                names.add(row["Kernel_Name"])
+                rows.append(row)
+    if last:
+        rows = sorted(rows, key=lambda r: int(r.get("Dispatch_Id", 0)))[-last:]
+    vals = [float(r["Counter_Value"]) for r in rows]
+    names = {r["Kernel_Name"] for r in rows}
     if not vals:
         raise SystemExit(f"{csv_path}: no dispatch of a kernel named like {name_part!r}")
     return sum(vals) / len(vals), len(vals), sorted(names)
@@ -76,8 +80,10 @@ def write_traffic(args) -> None:
     else:
         kname = "fused_fwd_kernel" if args.path == "fused" else "alt_gemm_kernel"
     true_kib = args.copy_mib * 1024.0
-    fc, _, _ = _counter_mean(fetch_copy_csv, "copyBuffer")
-    wc, _, _ = _counter_mean(write_copy_csv, "copyBuffer")
+    # the calibration copies are the last five copies of their run (a benchmark run with
+    # --also-copy first copies its inputs to the device with the same copy kernel)
+    fc, _, _ = _counter_mean(fetch_copy_csv, "copyBuffer", last=5)
+    wc, _, _ = _counter_mean(write_copy_csv, "copyBuffer", last=5)
     fk, nf, names = _counter_mean(fetch_csv, kname)
     wk, nw, _ = _counter_mean(write_csv, kname)
     ff, wf = true_kib / fc, true_kib / wc
@@ -131,6 +137,21 @@ def cpu_baseline(w, sample_T: int, backward: bool = False):
             "us_per_timestep": dt / sample_T * 1e6}
 
 
+def calibration_copies(mib: int) -> None:
+    """Five plain device-to-device copies of `mib` MiB (the known-size kernel the HBM counters are
+    scaled by)."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.randn(n, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_mib": mib, "launches": 5,
+                      "bytes_read_per_launch": n * 4, "bytes_written_per_launch": n * 4}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -146,6 +167,9 @@ def main():
                     help="only run a plain device copy of MIB MiB (read MIB, write MIB), five times, for "
                          "scaling the HBM byte counters, and exit")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--also-copy", type=int, default=0, metavar="MIB",
+                    help="after the benchmark, run the --copy-calibration copies in the same process, so that "
+                         "one rocprofv3 counter pass records both")
     ap.add_argument("--write-traffic", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "FETCH_COPY_CSV", "WRITE_COPY_CSV"),
                     help="only turn rocprofv3 FETCH_SIZE / WRITE_SIZE counter files of this workload and of "
                          "--copy-calibration into the --traffic-json entry, and exit (no GPU needed)")
@@ -164,14 +188,7 @@ def main():
     import torch
 
     if args.copy_calibration:
-        n = args.copy_calibration * (1 << 20) // 4
-        src = torch.randn(n, device="cuda:0")
-        dst = torch.empty_like(src)
-        for _ in range(5):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        print(json.dumps({"copy_calibration_mib": args.copy_calibration, "launches": 5,
-                          "bytes_read_per_launch": n * 4, "bytes_written_per_launch": n * 4}))
+        calibration_copies(args.copy_calibration)
         return
 
     import frnn_inputs as fi
@@ -302,6 +319,8 @@ def main():
     if not args.no_cpu_baseline and isinstance(w, fi.HeadwiseWorkload):
         res["cpu_baseline"] = cpu_baseline(w, min(args.cpu_sample_T or w.T, w.T), backward=args.backward)
     print(json.dumps(res), flush=True)
+    if args.also_copy:
+        calibration_copies(args.also_copy)
 
 
 if __name__ == "__main__":
