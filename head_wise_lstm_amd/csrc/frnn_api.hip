@@ -533,7 +533,7 @@ struct FusedBwdPlan {
 // The partial-sum design: workgroup w owns units [w*UW, (w+1)*UW) of a head with all their
 // gates. Constraints: UW a multiple of 8 (an A fragment stays inside one gate) with G*UW a
 // multiple of 32 (whole k-tiles), at most BWDX_MAX_W workgroups (the pollers' words per lane),
-// the (row, unit pair) combinations within the compute waves' pollers, the I/O wave's limits and
+// the (row, unit quad) combinations within the compute waves' pollers, the I/O wave's limits and
 // an instantiated (waves, tiles, k-tiles) design. Same preference order as the da design.
 bool plan_fused_bwdx(int B, int N, int D, int cell, const DevInfo& di, FusedBwdPlan* out) {
   const int G = gates_of(cell);
@@ -563,7 +563,7 @@ bool plan_fused_bwdx(int B, int N, int D, int cell, const DevInfo& di, FusedBwdP
         if (force_ncw && ncw != force_ncw) continue;
         if (TPH % ncw) continue;
         const int mtw = TPH / ncw, ktw = G * UW / 32;
-        if (BR * (UW / 2) > BWDX_CPW * ncw) continue;
+        if (BR * (UW / 4) > BWDX_CPW * ncw) continue;
         const FusedBwdxVariant* v = find_fused_bwdx(cell, ncw, mtw, ktw);
         if (!v) continue;
         if (found && chunks >= best.chunks) continue;

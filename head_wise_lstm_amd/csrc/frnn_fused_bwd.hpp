@@ -438,8 +438,9 @@ namespace frnn {
 // read their units' words from all W slots (D words a row per workgroup, a quarter of the da
 // exchange of the LSTM design above for G = 4) and add them in fp32.
 //
-// Per step s: poll waves (the first PW compute waves, eight (row, unit pair) combinations each,
-// eight slot chunks per combination in adjacent lanes, summed by three DPP row shifts) poll,
+// Per step s: poll waves (the first PW compute waves, four (row, unit quad) combinations each,
+// sixteen slot chunks per combination in one 16-lane row, two 16-byte loads per lane, summed by
+// four DPP row shifts) poll,
 // apply the step (its records read from LDS before the poll) and write da into the
 // stage of parity s (bf16 B fragments [batch row][k], k = g*UW + unit) and (dh, dc) into the output
 // ring; the step's barrier; every compute wave multiplies the stage by its R fragments and
@@ -448,9 +449,9 @@ namespace frnn {
 // The I/O wave puts the records of step k+1 into the ring in interval k (the step is applied
 // before the barrier) and stores the outputs of step k-1.
 
-constexpr int BWDX_CPW = 8;  // (row, unit pair) combinations per poll wave
-constexpr int BWDX_J = 8;    // slot chunks per combination (lanes = CPW * J = 64)
-constexpr int BWDX_NP = 4;   // 64-bit words per lane and round: W <= BWDX_J * BWDX_NP
+constexpr int BWDX_CPW = 4;  // (row, unit quad) combinations per poll wave
+constexpr int BWDX_J = 16;   // slot chunks per combination (lanes = CPW * J = 64)
+constexpr int BWDX_NP = 2;   // 16-byte loads per lane and round: W <= BWDX_J * BWDX_NP
 constexpr int BWDX_MAX_W = BWDX_J * BWDX_NP;
 // s_sleep units (64 clocks) before a step's first poll round (see FRNN_POLL_SLEEP0)
 #ifndef FRNN_BWDX_SLEEP0
@@ -599,26 +600,31 @@ __global__ void __launch_bounds__((NCW + 1) * 64, 1) fused_bwdx_kernel(FusedBwdA
       for (int kk = 0; kk < KTW; ++kk) Ra[j][kk] = __builtin_bit_cast(bf16x8_t, raw[j][kk]);
   }
 
-  // ---- poll lanes: combination c (batch row r, unit pair p) in lanes 8c' .. 8c'+7, slot chunk j
-  // = lane & 7 (slots j, j+8, ...)
-  static_assert(BWDX_J == 8 && BWDX_CPW * BWDX_J == 64, "poll lane layout");
-  const int UP = UW / 2;
-  const int PW = (BR * UP + BWDX_CPW - 1) / BWDX_CPW;
+  // ---- poll lanes: combination c (batch row r, unit quad q) in lanes 16c' .. 16c'+15, slot chunk
+  // j = lane & 15 (slots j and j+16), one 16-byte load (the quad's four words) per slot
+  static_assert(BWDX_J == 16 && BWDX_CPW * BWDX_J == 64, "poll lane layout");
+  const int UQ = UW / 4;
+  const int PW = (BR * UQ + BWDX_CPW - 1) / BWDX_CPW;
   const bool poller = wave < PW;
-  const int cmb = wave * BWDX_CPW + (lane >> 3), chunk = lane & 7;
-  const int pr = cmb / UP, pp2 = cmb - pr * UP;
-  const bool cv = poller && cmb < BR * UP && pr < nvalid;
+  const int cmb = wave * BWDX_CPW + (lane >> 4), chunk = lane & 15;
+  const int pr = cmb / UQ, pq = cmb - pr * UQ;
+  const bool cv = poller && cmb < BR * UQ && pr < nvalid;
   const int xpar = W * BR * D;  // words per parity
   uint32_t* const xb = a.xbuf + (long long)group * 2 * xpar;
-  uint32_t off[BWDX_NP];  // 64-bit word offsets from the parity's base
-  bool pv[BWDX_NP];
+  // byte offsets from the parity's base; a lane without a slot re-reads offset 0 and neither
+  // checks nor adds what it reads (no load under a lane mask, no branch in the check or the sum)
+  int off[BWDX_NP];
+  uint32_t tmask[BWDX_NP], vmask[BWDX_NP];
 #pragma unroll
   for (int e = 0; e < BWDX_NP; ++e) {
     const int ws = chunk + BWDX_J * e;
-    pv[e] = cv && ws < W;
-    off[e] = pv[e] ? (uint32_t)((ws * BR * D + pr * D + u0 + 2 * pp2) >> 1) : 0u;
+    const bool pv = cv && ws < W;
+    off[e] = pv ? (ws * BR * D + pr * D + u0 + 4 * pq) * 4 : 0;
+    tmask[e] = pv ? 0xFFFFu : 0u;
+    vmask[e] = pv ? 0xFFFF0000u : 0u;
   }
-  float cr[2] = {0.0f, 0.0f};  // LSTM dc, GRU dh carried to the next step, for the pair
+  const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(xb, (short)0, 2 * xpar * 4, 0x00020000);
+  float cr[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // LSTM dc, GRU dh carried to the next step, for the quad
 
   // Step 0 has no dh_R: publish zero partials with tag 0 (parity 1), polled like any other step.
   if (col < nvalid) {
@@ -633,34 +639,35 @@ __global__ void __launch_bounds__((NCW + 1) * 64, 1) fused_bwdx_kernel(FusedBwdA
   for (int s = 0; s < T; ++s) {
     // ---- A. poll this workgroup's units in every slot, add the partials, apply the step
     if (poller) {
-      // this step's records of the lane's two units (in the ring since barrier s-1)
+      // this step's records of the lane's four units (in the ring since barrier s-1)
       const bool mathlane = cv && chunk == 0;
-      f32x4_t rc[2][2];
+      f32x4_t rc[4][2];
       {
-        const float* rr = rin + ((s & 1) * BR + (mathlane ? pr : 0)) * UW * BWD_REC + (mathlane ? 2 * pp2 : 0) * BWD_REC;
+        const float* rr = rin + ((s & 1) * BR + (mathlane ? pr : 0)) * UW * BWD_REC + (mathlane ? 4 * pq : 0) * BWD_REC;
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
+        for (int i = 0; i < 4; ++i) {
           rc[i][0] = *reinterpret_cast<const f32x4_t*>(rr + i * BWD_REC);
           rc[i][1] = *reinterpret_cast<const f32x4_t*>(rr + i * BWD_REC + 4);
         }
       }
       const uint32_t tag = (uint32_t)s & 0xFFFFu;
-      const uint64_t* src = reinterpret_cast<const uint64_t*>(xb + ((s - 1) & 1) * xpar);
-      uint64_t v[BWDX_NP];
+      // 16-byte loads that bypass the CU cache (cache policy sc1, the coherence of an agent-scope
+      // atomic load); every 32-bit word carries its own tag, so a load that sees words of two
+      // steps is simply polled again
+      const int soff = ((s - 1) & 1) * xpar * 4;
+      u32x4_t v[BWDX_NP];
       long long t_first = 0;
       int spins = 0;
       bool ok = false;
       if (s > 0) __builtin_amdgcn_s_sleep(FRNN_BWDX_SLEEP0);
       while (true) {
 #pragma unroll
-        for (int e = 0; e < BWDX_NP; ++e) v[e] = __hip_atomic_load(src + off[e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        bool mine = true;
+        for (int e = 0; e < BWDX_NP; ++e) v[e] = __builtin_amdgcn_raw_buffer_load_b128(xr, off[e], soff, 16);
+        uint32_t bad = 0;
 #pragma unroll
-        for (int e = 0; e < BWDX_NP; ++e) {
-          const uint32_t lo = (uint32_t)v[e], hi = (uint32_t)(v[e] >> 32);
-          if (pv[e] && (((lo ^ tag) | (hi ^ tag)) & 0xFFFFu) != 0) mine = false;
-        }
-        if (__all(mine)) {
+        for (int e = 0; e < BWDX_NP; ++e)
+          bad |= ((v[e][0] ^ tag) | (v[e][1] ^ tag) | (v[e][2] ^ tag) | (v[e][3] ^ tag)) & tmask[e];
+        if (__all(bad == 0)) {
           ok = true;
           break;
         }
@@ -676,27 +683,24 @@ __global__ void __launch_bounds__((NCW + 1) * 64, 1) fused_bwdx_kernel(FusedBwdA
         }
       }
       if (ok) {
-        float s0 = 0.0f, s1 = 0.0f;
+        float sum[4];
 #pragma unroll
-        for (int e = 0; e < BWDX_NP; ++e) {
-          if (pv[e]) {
-            s0 += __uint_as_float((uint32_t)v[e] & 0xFFFF0000u);
-            s1 += __uint_as_float((uint32_t)(v[e] >> 32) & 0xFFFF0000u);
-          }
+        for (int i = 0; i < 4; ++i) {
+          sum[i] = 0.0f;
+#pragma unroll
+          for (int e = 0; e < BWDX_NP; ++e) sum[i] += __uint_as_float(v[e][i] & vmask[e]);
+          // lane 16c' gathers the sixteen chunks of its combination: x[p] += x[p + d], d = 8, 4,
+          // 2, 1 (row shifts; lanes past the 16-lane row read 0, and only lanes 16c' use it)
+          sum[i] = row_shl_add<1>(row_shl_add<2>(row_shl_add<4>(row_shl_add<8>(sum[i]))));
         }
-        // lane 8c' gathers the eight chunks of its combination: x[p] += x[p + d], d = 4, 2, 1
-        // (row shifts; lanes past the 16-lane row read 0, and only lanes 8c' use the result)
-        s0 = row_shl_add<1>(row_shl_add<2>(row_shl_add<4>(s0)));
-        s1 = row_shl_add<1>(row_shl_add<2>(row_shl_add<4>(s1)));
         if (mathlane) {
-          const float dhr[2] = {s0, s1};
-          float da[G][2], dh[2], dc[2];
+          float da[G][4], dh[4], dc[4];
 #pragma unroll
-          for (int i = 0; i < 2; ++i) {
+          for (int i = 0; i < 4; ++i) {
             const f32x4_t r0 = rc[i][0];
             const f32x4_t r1 = rc[i][1];
             if constexpr (CELL == CELL_LSTM) {
-              dh[i] = dhr[i] + r1[2];
+              dh[i] = sum[i] + r1[2];
               dc[i] = cr[i] + r1[3] + dh[i] * r0[0];
               da[0][i] = dc[i] * r0[1];
               da[1][i] = dc[i] * r0[2];
@@ -704,14 +708,14 @@ __global__ void __launch_bounds__((NCW + 1) * 64, 1) fused_bwdx_kernel(FusedBwdA
               da[3 % G][i] = dh[i] * r1[0];
               cr[i] = dc[i] * r1[1];
             } else if constexpr (CELL == CELL_GRU) {
-              dh[i] = dhr[i] + r1[0] + cr[i];
+              dh[i] = sum[i] + r1[0] + cr[i];
               dc[i] = 0.0f;
               da[0][i] = dh[i] * r0[0];
               da[1 % G][i] = dh[i] * r0[1];
               da[2 % G][i] = dh[i] * r0[2];
               cr[i] = dh[i] * r0[3];
             } else {
-              dh[i] = dhr[i] + r0[1];
+              dh[i] = sum[i] + r0[1];
               dc[i] = 0.0f;
               da[0][i] = dh[i] * r0[0];
             }
@@ -719,8 +723,12 @@ __global__ void __launch_bounds__((NCW + 1) * 64, 1) fused_bwdx_kernel(FusedBwdA
           uint32_t* sg = stage + ((s & 1) * 16 + pr) * SROW;
 #pragma unroll
           for (int g = 0; g < G; ++g)
-            sg[(g * UW + 2 * pp2) >> 1] = (uint32_t)f2bf(da[g][0]) | ((uint32_t)f2bf(da[g][1]) << 16);
-          *reinterpret_cast<f32x4_t*>(rout + ((s & 1) * BR + pr) * UW * 2 + 4 * pp2) = f32x4_t{dh[0], dc[0], dh[1], dc[1]};
+            *reinterpret_cast<uint2*>(sg + ((g * UW + 4 * pq) >> 1)) =
+                make_uint2((uint32_t)f2bf(da[g][0]) | ((uint32_t)f2bf(da[g][1]) << 16),
+                           (uint32_t)f2bf(da[g][2]) | ((uint32_t)f2bf(da[g][3]) << 16));
+          float* ro = rout + ((s & 1) * BR + pr) * UW * 2 + 8 * pq;
+          *reinterpret_cast<f32x4_t*>(ro) = f32x4_t{dh[0], dc[0], dh[1], dc[1]};
+          *reinterpret_cast<f32x4_t*>(ro + 4) = f32x4_t{dh[2], dc[2], dh[3], dc[3]};
         }
       }
     }
