@@ -206,6 +206,81 @@ __device__ __forceinline__ void row_reduce(f32x4_t& x) {
 __device__ __forceinline__ bool uniform_flag(int v) { return __builtin_amdgcn_readfirstlane(v) != 0; }
 
 
+// Poll the exchange words of one compute wave's K range (KTW k-tiles of 32 words from word k0 of
+// each row, rows row_words apart) for rows 0 .. nvalid-1, with all 64 lanes and PW words per lane
+// and load (PW = fused_poll_words), until every word carries `tag`; then unpack the values (the
+// words' high halves) into the wave's LDS stage, row r at r * fused_stage_row(KTW) words, two
+// bf16 per word, from which the MFMA B fragments are read. The loads bypass the CU cache (cache
+// policy sc1, the coherence of an agent-scope atomic load). Each 32-bit word carries its own tag,
+// so a load that sees some words of this step and some of the last is simply polled again. A
+// lane without a load of its own re-reads the first one and checks nothing, so that no load sits
+// under a lane mask and the check needs no branch. Every wait is bounded: past timeout_ticks of
+// the wall clock, or once another workgroup has raised an error, the wave records a timeout and
+// sets *abort_flag (every wave then leaves after the next barrier).
+template <int KS, int MTW, int KTW>
+__device__ __forceinline__ void poll_stage(const uint32_t* xbase, int xbytes, int soff, int row_words, int k0,
+                                           int nvalid, uint32_t tag, bool first_step, uint32_t* stage, int lane,
+                                           long long timeout_ticks, int* err, int* abort_flag) {
+  constexpr int PW = fused_poll_words(KS, MTW, KTW);
+  constexpr int WPR = KTW * 32 / PW;                            // loads per row
+  constexpr int NP = (fused_max_br(KS, MTW) * WPR + 63) / 64;  // loads per lane (bound)
+  constexpr int SROW = fused_stage_row(KTW);
+  typedef uint32_t pw_t __attribute__((ext_vector_type(PW)));
+  const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(xbase), (short)0, xbytes, 0x00020000);
+  const int nw = nvalid * WPR;
+  int voff[NP], sidx[NP];
+  uint32_t tmask[NP];
+#pragma unroll
+  for (int e = 0; e < NP; ++e) {
+    const int wi = lane + 64 * e, r = wi / WPR, wr = wi - r * WPR;
+    const bool ok = wi < nw;
+    voff[e] = ((ok ? r * row_words + wr * PW : 0) + k0) * 4;
+    tmask[e] = ok ? 0xFFFFu : 0u;
+    sidx[e] = ok ? r * SROW + wr * (PW / 2) : -1;
+  }
+  pw_t v[NP];
+  long long t_first = 0;
+  int spins = 0;
+  // nothing can have arrived yet (a store takes a few hundred ns to show on another CU)
+  if (!first_step) __builtin_amdgcn_s_sleep(FRNN_POLL_SLEEP0);
+  while (true) {
+#pragma unroll
+    for (int e = 0; e < NP; ++e) {
+      if constexpr (PW == 4) v[e] = __builtin_amdgcn_raw_buffer_load_b128(xr, voff[e], soff, 16);
+      else v[e] = __builtin_amdgcn_raw_buffer_load_b64(xr, voff[e], soff, 16);
+    }
+    uint32_t bad = 0;
+#pragma unroll
+    for (int e = 0; e < NP; ++e) {
+      uint32_t x = 0;
+#pragma unroll
+      for (int i = 0; i < PW; ++i) x |= v[e][i] ^ tag;
+      bad |= x & tmask[e];
+    }
+    if (__all(bad == 0)) {
+#pragma unroll
+      for (int e = 0; e < NP; ++e) {
+        if (sidx[e] < 0) continue;
+        if constexpr (PW == 4)
+          *reinterpret_cast<uint2*>(stage + sidx[e]) = make_uint2(pack_hi(v[e][0], v[e][1]), pack_hi(v[e][2], v[e][3]));
+        else
+          stage[sidx[e]] = pack_hi(v[e][0], v[e][1]);
+      }
+      return;
+    }
+    if ((++spins & 63) == 0) {
+      const long long now = (long long)wall_clock64();
+      if (t_first == 0) t_first = now;
+      if (now - t_first > timeout_ticks ||
+          uniform_flag(__hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))) {
+        if (lane == 0) atomicOr(err, DEVERR_TIMEOUT);
+        *abort_flag = 1;
+        return;
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------- I/O wave
 // Everything the I/O wave needs, as plain values (no reference to the kernel argument).
 struct IoCtx {
@@ -631,82 +706,15 @@ __global__ void __launch_bounds__((NCW + 1) * 64, 1) fused_fwd_kernel(FusedArgs 
         }
       }
     } else if constexpr (!F32) {
-      // Poll this wave's K range (KTW k-tiles of 32 units) for the group's nvalid rows with all
-      // 64 lanes, PW words (PW units) per lane and load, with loads that bypass the CU cache
-      // (the coherence of an agent-scope atomic load). Each 32-bit word carries its own tag, so
-      // a load that sees some words of this step and some of the last is simply polled again.
-      // Once every word carries this step's tag the values are unpacked into the wave's LDS
-      // stage, from which the MFMA B fragments are read.
-      const int pp = (t - 1) & 1;
-      const uint32_t tag = (uint32_t)t & 0xFFFFu;
-      constexpr int PW = fused_poll_words(KS, MTW, KTW);
-      constexpr int WPR = KTW * 32 / PW;                            // loads per row
-      constexpr int NP = (fused_max_br(KS, MTW) * WPR + 63) / 64;  // loads per lane (bound)
-      constexpr int SROW = fused_stage_row(KTW);
-      typedef uint32_t pw_t __attribute__((ext_vector_type(PW)));
-      uint32_t* stage = reinterpret_cast<uint32_t*>(smem + lay.h) + wave * 16 * SROW;
-      const __amdgpu_buffer_rsrc_t xr =
-          __builtin_amdgcn_make_buffer_rsrc(xb, (short)0, 2 * xpar * 4, 0x00020000);
-      const int soff = pp * xpar * 4;
-      const int nw = nvalid * WPR;
-      // A lane without a load of its own re-reads the first one and checks nothing, so that no
-      // load sits under a lane mask and the check needs no branch.
-      int voff[NP], sidx[NP];
-      uint32_t tmask[NP];
-#pragma unroll
-      for (int e = 0; e < NP; ++e) {
-        const int wi = lane + 64 * e, r = wi / WPR, wr = wi - r * WPR;
-        const bool ok = wi < nw;
-        voff[e] = ((ok ? r * D + wr * PW : 0) + ks * KTW * 32) * 4;
-        tmask[e] = ok ? 0xFFFFu : 0u;
-        sidx[e] = ok ? r * SROW + wr * (PW / 2) : -1;
-      }
-      pw_t v[NP];
-      long long t_first = 0;
-      int spins = 0;
-      // nothing can have arrived yet (a store takes a few hundred ns to show on another CU)
-      if (t > 0) __builtin_amdgcn_s_sleep(FRNN_POLL_SLEEP0);
-      while (true) {
-#pragma unroll
-        for (int e = 0; e < NP; ++e) {
-          if constexpr (PW == 4) v[e] = __builtin_amdgcn_raw_buffer_load_b128(xr, voff[e], soff, 16);
-          else v[e] = __builtin_amdgcn_raw_buffer_load_b64(xr, voff[e], soff, 16);
-        }
-        uint32_t bad = 0;
-#pragma unroll
-        for (int e = 0; e < NP; ++e) {
-          uint32_t x = 0;
-#pragma unroll
-          for (int i = 0; i < PW; ++i) x |= v[e][i] ^ tag;
-          bad |= x & tmask[e];
-        }
-        if (__all(bad == 0)) {
-#pragma unroll
-          for (int e = 0; e < NP; ++e) {
-            if (sidx[e] < 0) continue;
-            if constexpr (PW == 4)
-              *reinterpret_cast<uint2*>(stage + sidx[e]) = make_uint2(pack_hi(v[e][0], v[e][1]), pack_hi(v[e][2], v[e][3]));
-            else
-              stage[sidx[e]] = pack_hi(v[e][0], v[e][1]);
-          }
-          break;
-        }
-        if ((++spins & 63) == 0) {
-          const long long now = (long long)wall_clock64();
-          if (t_first == 0) t_first = now;
-          if (now - t_first > a.timeout_ticks ||
-              uniform_flag(__hip_atomic_load(a.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))) {
-            if (lane == 0) atomicOr(a.err, DEVERR_TIMEOUT);
-            s_abort = 1;  // every wave leaves after the next barrier
-            break;
-          }
-        }
-      }
+      // this wave's K range of h_{t-1}, polled into the wave's LDS stage
+      uint32_t* stage = reinterpret_cast<uint32_t*>(smem + lay.h) + wave * 16 * fused_stage_row(KTW);
+      poll_stage<KS, MTW, KTW>(xb, 2 * xpar * 4, ((t - 1) & 1) * xpar * 4, D, ks * KTW * 32, nvalid,
+                               (uint32_t)t & 0xFFFFu, t == 0, stage, lane, a.timeout_ticks, a.err, &s_abort);
       FRNN_TRACE(7);
       FRNN_TRACE_RT(7);
 #pragma unroll
       for (int kk = 0; kk < KTW; ++kk) {
-        const bf16x8_t bk = *reinterpret_cast<const bf16x8_t*>(stage + col * SROW + kk * 16 + 4 * quad);
+        const bf16x8_t bk = *reinterpret_cast<const bf16x8_t*>(stage + col * fused_stage_row(KTW) + kk * 16 + 4 * quad);
 #pragma unroll
         for (int j = 0; j < MTW; ++j) acc[j] = mfma_bf16(Ra[j][kk], bk, acc[j]);
       }

@@ -290,51 +290,10 @@ __global__ void __launch_bounds__((NCW + 1) * 64, 1) fused_bwd_kernel(FusedBwdAr
 #pragma unroll
     for (int j = 0; j < MTW; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     {
-      const int pp = (s - 1) & 1;
-      const uint32_t tag = (uint32_t)s & 0xFFFFu;
-      constexpr int WPR = KTW * 16;                                // 64-bit words per row
-      constexpr int NP = (fused_max_br(KS, MTW) * WPR + 63) / 64;  // words per lane (upper bound)
+      // this wave's K range of the step before's da, polled into the wave's LDS stage
       uint32_t* stage = reinterpret_cast<uint32_t*>(smem + lay.stage) + wave * 16 * SROW;
-      const uint64_t* src = reinterpret_cast<const uint64_t*>(xb + pp * xpar) + ks * WPR;
-      const int nw = nvalid * WPR;
-      uint32_t off[NP];
-#pragma unroll
-      for (int e = 0; e < NP; ++e) {
-        const int wi = lane + 64 * e, r = wi / WPR, wr = wi - r * WPR;
-        off[e] = wi < nw ? (uint32_t)(r * (GD / 2) + wr) : 0u;
-      }
-      uint64_t v[NP];
-      long long t_first = 0;
-      int spins = 0;
-      if (s > 0) __builtin_amdgcn_s_sleep(FRNN_POLL_SLEEP0);
-      while (true) {
-#pragma unroll
-        for (int e = 0; e < NP; ++e) v[e] = __hip_atomic_load(src + off[e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        bool ok = true;
-#pragma unroll
-        for (int e = 0; e < NP; ++e) {
-          const uint32_t lo = (uint32_t)v[e], hi = (uint32_t)(v[e] >> 32);
-          if (lane + 64 * e < nw && (((lo ^ tag) | (hi ^ tag)) & 0xFFFFu) != 0) ok = false;
-        }
-        if (__all(ok)) {
-#pragma unroll
-          for (int e = 0; e < NP; ++e) {
-            const int wi = lane + 64 * e, r = wi / WPR, wr = wi - r * WPR;
-            if (wi < nw) stage[r * SROW + wr] = pack_hi((uint32_t)v[e], (uint32_t)(v[e] >> 32));
-          }
-          break;
-        }
-        if ((++spins & 63) == 0) {
-          const long long now = (long long)wall_clock64();
-          if (t_first == 0) t_first = now;
-          if (now - t_first > a.timeout_ticks ||
-              uniform_flag(__hip_atomic_load(a.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))) {
-            if (lane == 0) atomicOr(a.err, DEVERR_TIMEOUT);
-            s_abort = 1;  // every wave leaves after the next barrier
-            break;
-          }
-        }
-      }
+      poll_stage<KS, MTW, KTW>(xb, 2 * xpar * 4, ((s - 1) & 1) * xpar * 4, GD, ks * KTW * 32, nvalid,
+                               (uint32_t)s & 0xFFFFu, s == 0, stage, lane, a.timeout_ticks, a.err, &s_abort);
 #pragma unroll
       for (int kk = 0; kk < KTW; ++kk) {
         const bf16x8_t bk = *reinterpret_cast<const bf16x8_t*>(stage + col * SROW + kk * 16 + 4 * quad);
