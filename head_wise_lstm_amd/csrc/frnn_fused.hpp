@@ -124,6 +124,7 @@ struct FusedLds {
 #define FRNN_POLL_SLEEP0 5
 #endif
 
+
 // Batch rows per group of the die-local design (bounds the polling registers).
 constexpr int FUSED_DIE_MAX_BR = 4;
 
@@ -214,7 +215,7 @@ __device__ __forceinline__ bool uniform_flag(int v) { return __builtin_amdgcn_re
 // policy sc1, the coherence of an agent-scope atomic load). Each 32-bit word carries its own tag,
 // so a load that sees some words of this step and some of the last is simply polled again. A
 // lane without a load of its own re-reads the first one and checks nothing, so that no load sits
-// under a lane mask and the check needs no branch. Every wait is bounded: past timeout_ticks of
+// under a lane mask and neither the check nor the unpacking needs a branch. Every wait is bounded: past timeout_ticks of
 // the wall clock, or once another workgroup has raised an error, the wave records a timeout and
 // sets *abort_flag (every wave then leaves after the next barrier).
 template <int KS, int MTW, int KTW>
@@ -236,7 +237,10 @@ __device__ __forceinline__ void poll_stage(const uint32_t* xbase, int xbytes, in
     const bool ok = wi < nw;
     voff[e] = ((ok ? r * row_words + wr * PW : 0) + k0) * 4;
     tmask[e] = ok ? 0xFFFFu : 0u;
-    sidx[e] = ok ? r * SROW + wr * (PW / 2) : -1;
+    // a lane without a load writes its (unused) values into the padding words at the end of a
+    // stage row, which no fragment read touches, so that the writes need no branch (measured
+    // 1.213 -> 1.202 us per step at LSTM B=16 D=768)
+    sidx[e] = ok ? r * SROW + wr * (PW / 2) : (lane & 15) * SROW + KTW * 16;
   }
   pw_t v[NP];
   long long t_first = 0;
@@ -260,7 +264,6 @@ __device__ __forceinline__ void poll_stage(const uint32_t* xbase, int xbytes, in
     if (__all(bad == 0)) {
 #pragma unroll
       for (int e = 0; e < NP; ++e) {
-        if (sidx[e] < 0) continue;
         if constexpr (PW == 4)
           *reinterpret_cast<uint2*>(stage + sidx[e]) = make_uint2(pack_hi(v[e][0], v[e][1]), pack_hi(v[e][2], v[e][3]));
         else
