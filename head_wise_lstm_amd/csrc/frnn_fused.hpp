@@ -438,7 +438,8 @@ __device__ __forceinline__ bool io_interval(const IoCtx& c, const IoDesc<CELL, N
   // for the one L intervals back only.
   io_issue<CELL, NCW, KS, MTW, EPL>(c, d, min(max(s_wx + L, 0), c.T - 1), raw[ST]);
   const int s_out = k - 1 - G0;
-  if (s_out >= 0 && s_out < c.T) io_store<CELL, NCW, KS, MTW, EPL>(c, d, s_out, outs);
+  // (single-workgroup designs, G0 == 0: the compute waves store the states themselves)
+  if (G0 == 1 && s_out >= 0 && s_out < c.T) io_store<CELL, NCW, KS, MTW, EPL>(c, d, s_out, outs);
   block_barrier();
   return uniform_flag(*abort_flag);
 }
@@ -795,10 +796,16 @@ __global__ void __launch_bounds__((NCW + 1) * 64, 1) fused_fwd_kernel(FusedArgs 
         if (LOCAL) {
           if constexpr (F32) hbuf_f[((t & 1) * 16 + col) * HS + u] = h;
           else hbuf_b[((t & 1) * 16 + col) * HS + u] = f2bf(h);
-        } else if (colv) {
-          xb[(t & 1) * xpar + col * D + u] = ((uint32_t)f2bf(h) << 16) | wtag;
+          // no global load is ever waited for in these waves, so the state stores cost no wait
+          if (colv) {
+            const long long o = bcol * a.out_sb + (long long)t * a.out_st + (long long)n * D + u;
+            if (a.out_h) a.out_h[o] = h;
+            if (CELL == CELL_LSTM && a.out_c) a.out_c[o] = c;
+          }
+        } else {
+          if (colv) xb[(t & 1) * xpar + col * D + u] = ((uint32_t)f2bf(h) << 16) | wtag;
+          outs[ri] = f32x4_t{h, c, 0.f, 0.f};
         }
-        outs[ri] = f32x4_t{h, c, 0.f, 0.f};
         hlast[q][0] = h;
       } else {
         float h[4];
@@ -812,13 +819,18 @@ __global__ void __launch_bounds__((NCW + 1) * 64, 1) fused_fwd_kernel(FusedArgs 
             u16x4_t hv = {f2bf(h[0]), f2bf(h[1]), f2bf(h[2]), f2bf(h[3])};
             *reinterpret_cast<u16x4_t*>(&hbuf_b[((t & 1) * 16 + col) * HS + u]) = hv;
           }
-        } else if (colv) {
-          u32x4_t wv;
+          if (colv && a.out_h)
+            *reinterpret_cast<f32x4_t*>(a.out_h + bcol * a.out_sb + (long long)t * a.out_st + (long long)n * D + u) =
+                f32x4_t{h[0], h[1], h[2], h[3]};
+        } else {
+          if (colv) {
+            u32x4_t wv;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) wv[i] = ((uint32_t)f2bf(h[i]) << 16) | wtag;
-          *reinterpret_cast<u32x4_t*>(xb + ((t & 1) * xpar + col * D + u)) = wv;
+            for (int i = 0; i < 4; ++i) wv[i] = ((uint32_t)f2bf(h[i]) << 16) | wtag;
+            *reinterpret_cast<u32x4_t*>(xb + ((t & 1) * xpar + col * D + u)) = wv;
+          }
+          outs[ri] = f32x4_t{h[0], h[1], h[2], h[3]};
         }
-        outs[ri] = f32x4_t{h[0], h[1], h[2], h[3]};
 #pragma unroll
         for (int i = 0; i < 4; ++i) hlast[q][i] = h[i];
       }
