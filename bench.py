@@ -152,6 +152,68 @@ def calibration_copies(mib: int) -> None:
                       "bytes_read_per_launch": n * 4, "bytes_written_per_launch": n * 4}), flush=True)
 
 
+def sweep_designs(spec: str, T: int) -> None:
+    """Pin every fused forward design through the planner's FRNN_FUSED_W / BR / NCW / KS variables,
+    time each distinct design the planner accepts (the best of three calls after one warm-up,
+    HIP events), and print its planner prediction beside the measurement; `pick` marks the design
+    the planner chooses unpinned."""
+    import re
+    import torch
+    import frnn_inputs as fi
+    import head_wise_lstm_amd as hw
+    cell, B, N, D = spec.split(",")
+    B, N, D = int(B), int(N), int(D)
+    pins = ["FRNN_FUSED_W", "FRNN_FUSED_BR", "FRNN_FUSED_NCW", "FRNN_FUSED_KS"]
+    dev = torch.device("cuda:0")
+    w = fi.HeadwiseWorkload("sweep", cell, torch.bfloat16, B=B, T=T, N=N, D=D, seed=0, s0_var=None)
+    g = {k: (v.to(dev) if v is not None else None) for k, v in fi.make_inputs(w).items()}
+    desc = hw._desc(B, T, N, D, cell, torch.bfloat16)
+
+    def clear():
+        for k in pins:
+            os.environ.pop(k, None)
+
+    def design(plan):
+        m = dict(re.findall(r"(\w+)=(\S+)", plan))
+        return ({"design": plan.split()[1].split("=")[1], **{k: int(m[k]) for k in
+                 ("BR", "W", "NCW", "KS", "MTW", "KTW", "chunks")}}, float(m["predicted_us"]))
+
+    def us_per_step():
+        hw.frnn_fwd(g["Wx"], g["R"], g["b"], g["states0"], cell=cell, path="fused")
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            hw.frnn_fwd(g["Wx"], g["R"], g["b"], g["states0"], cell=cell, path="fused")
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return 1000.0 * min(ts) / T
+
+    clear()
+    pick, _ = design(hw.frnn_plan_str(desc))
+    combos = [(1, br, ncw, 0) for br in range(1, 17) for ncw in (4, 8)]
+    combos += [(W, br, ncw, ks) for W in range(2, 33) for br in range(1, 5)
+               for ncw, ks in ((4, 1), (4, 2), (4, 4), (6, 6), (8, 2), (8, 4), (8, 8))]
+    seen = []
+    for W, br, ncw, ks in combos:
+        clear()
+        os.environ.update({"FRNN_FUSED_W": str(W), "FRNN_FUSED_BR": str(br), "FRNN_FUSED_NCW": str(ncw)})
+        if ks:
+            os.environ["FRNN_FUSED_KS"] = str(ks)
+        try:
+            d, pred = design(hw.frnn_plan_str(desc))
+        except hw.FrnnError:
+            continue
+        if d in seen:
+            continue
+        seen.append(d)
+        print(json.dumps({"shape": f"{cell}_B{B}_T{T}_N{N}_D{D}", **d, "predicted_us_per_call": pred,
+                          "us_per_step": us_per_step(), "pick": d == pick}), flush=True)
+    clear()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -167,6 +229,10 @@ def main():
                     help="only run a plain device copy of MIB MiB (read MIB, write MIB), five times, for "
                          "scaling the HBM byte counters, and exit")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sweep-designs", default="", metavar="CELL,B,N,D",
+                    help="time every fused forward design the planner can be pinned to on this head-wise shape "
+                         "(bf16, seeded inputs, --sweep-T steps) and print one JSON line per design")
+    ap.add_argument("--sweep-T", type=int, default=512)
     ap.add_argument("--also-copy", type=int, default=0, metavar="MIB",
                     help="after the benchmark, run the --copy-calibration copies in the same process, so that "
                          "one rocprofv3 counter pass records both")
@@ -189,6 +255,9 @@ def main():
 
     if args.copy_calibration:
         calibration_copies(args.copy_calibration)
+        return
+    if args.sweep_designs:
+        sweep_designs(args.sweep_designs, args.sweep_T)
         return
 
     import frnn_inputs as fi
