@@ -176,19 +176,20 @@ int env_int(const char* name, int dflt) {
   return std::atoi(s);
 }
 
-// Predicted time of one step of the fused kernel (µs), fitted by least squares to 61 measured
-// die-local designs on ten shapes (LSTM, GRU, Elman; D 128-768; B 4-32): a base for the exchange,
-// the barrier and the gates, plus each compute wave's MFMA chain (MTW*KTW tiles) and its poll
-// loads per lane per round (fitted when every load was 8 bytes; a design whose rows take fewer
-// loads at 16 bytes polls with those, and the term counts them). The single-workgroup design has no
-// exchange: its base is lower and its chain runs over the whole K.
-constexpr double kStepBaseDie = 0.731, kStepBaseLocal = 0.37, kStepPerMfma = 0.0184, kStepPerPollWord = 0.0637;
+// Predicted time of one step of the fused kernel (µs). Die-local design: fitted by least squares
+// to 129 measured die-local designs on twelve shapes (LSTM, GRU, Elman; D 64-768; B 4-64; the
+// kernels with 16-byte exchange polls): a base for the exchange, the barrier and the gates, plus
+// each compute wave's MFMA chain (MTW*KTW tiles), its poll loads per lane and round, and the
+// number of compute waves (more waves meet at every barrier and split the K-sum exchange). The
+// single-workgroup design has no exchange: its base is lower and its chain runs over the whole K.
+constexpr double kStepBaseDie = 0.700, kStepPerMfma = 0.0164, kStepPerPollLoad = 0.0141, kStepPerWave = 0.0181;
+constexpr double kStepBaseLocal = 0.37, kStepPerMfmaLocal = 0.0184;
 constexpr double kLaunchUs = 15.0;  // R packing, fills and the launch of one chunk
 
-double step_cost(bool local, int br, int ks, int mtw, int ktw) {
-  if (local) return kStepBaseLocal + kStepPerMfma * mtw * ktw;
+double step_cost(bool local, int br, int ncw, int ks, int mtw, int ktw) {
+  if (local) return kStepBaseLocal + kStepPerMfmaLocal * mtw * ktw;
   const int np = (br * ktw * 32 / fused_poll_words(ks, mtw, ktw) + 63) / 64;
-  return kStepBaseDie + kStepPerMfma * mtw * ktw + kStepPerPollWord * np;
+  return kStepBaseDie + kStepPerMfma * mtw * ktw + kStepPerPollLoad * np + kStepPerWave * ncw;
 }
 
 // Choose the fused design by integer constraint search. The variables are:
@@ -223,7 +224,7 @@ int plan_fused(const Problem& p, const DevInfo& di, FusedPlan* out) {
     fp.chunks = (int)((p.B + bmax - 1) / bmax);
     fp.Bc = (int)(((long long)p.B + fp.chunks - 1) / fp.chunks);
     fp.groups = p.N * ((fp.Bc + fp.BR - 1) / fp.BR);
-    fp.cost_us = fp.chunks * (T * step_cost(fp.local, fp.BR, fp.ks, fp.mtw, fp.ktw) + kLaunchUs);
+    fp.cost_us = fp.chunks * (T * step_cost(fp.local, fp.BR, fp.ncw, fp.ks, fp.mtw, fp.ktw) + kLaunchUs);
     if (!fp.local) {
       const int per_die = (fp.groups + di.n_xcd - 1) / di.n_xcd;
       fp.slots = per_die * fp.W;

@@ -135,9 +135,10 @@ def test_planner_choices_for_the_workloads(lib):
     assert "die-local" in s and "BR=2 " in s and "groups=8 " in s and "W=32 " in s
     # R^T of a 32-CU slice (147 KB) must stay in registers: a K split over 6 or 8 compute waves
     assert "NCW=8 KS=8 MTW=6 KTW=3" in s and "chunks=1 " in s
-    # LSTM D=256 B=8 N=3: two rows per group (the fewest that fit), twelve groups of 16 workgroups
+    # LSTM D=256 B=8 N=3: four rows per group, six groups of 32 workgroups (one tile each), four
+    # compute waves (the step model charges every compute wave at the barrier)
     s = plan(D(B=8, T=1024, N=3, Dm=256), 1)
-    assert "die-local" in s and "BR=2 " in s and "groups=12 " in s and "W=16 " in s
+    assert "die-local" in s and "BR=4 " in s and "groups=6 " in s and "W=32 " in s and "NCW=4 KS=4" in s
     # Elman D=64: a whole head per workgroup, four batch rows each so that 192 workgroups fill the CUs
     s = plan(D(B=64, T=2048, N=12, Dm=64, cell=1), 1)
     assert "workgroup-local" in s and "BR=4 " in s and "groups=192 " in s
