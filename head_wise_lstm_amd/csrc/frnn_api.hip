@@ -249,9 +249,11 @@ int plan_fused(const Problem& p, const DevInfo& di, FusedPlan* out) {
       // a long per-wave MFMA chain makes the die-local split faster (measured); keep the design
       // for heads whose chain is short
       if (mtw * KT > 64 && force_w != 1) continue;
+      // the I/O wave moves at most 64 * epl words of Wx per step (the compute waves store the
+      // states themselves in this design)
       const int epl = fused_epl(true, ncw, p.cell);
       const int words_per_row = G * p.D / (p.wx_f32 ? 2 : 4);
-      const int br_cap = std::min(16, std::min(64 * epl / words_per_row, 64 * epl * 2 / p.D));
+      const int br_cap = std::min(16, 64 * epl / words_per_row);
       for (int br = 1; br <= br_cap; ++br) {
         if (force_br && br != force_br) continue;
         FusedPlan fp;

@@ -557,10 +557,22 @@ __global__ void __launch_bounds__((NCW + 1) * 64, 1) fused_fwd_kernel(FusedArgs 
       const int c = idx / D, k = idx - c * D;
       float v = 0.0f;
       if (a.s0_h && c < nvalid) v = ld_f(a.s0_h, (long long)(b0 + c) * a.s0_sb + (long long)n * D + k, a.s0_f32);
-      if (F32) hbuf_f[(1 * 16 + c) * HS + k] = v;
-      else hbuf_b[(1 * 16 + c) * HS + k] = f2bf(v);
+      if (F32) {
+        hbuf_f[(1 * 16 + c) * HS + k] = v;
+        hbuf_f[c * HS + k] = 0.0f;
+      } else {
+        hbuf_b[(1 * 16 + c) * HS + k] = f2bf(v);
+        hbuf_b[c * HS + k] = 0;
+      }
     }
   }
+  // A whole Elman head with at most four batch rows: only columns 0-3 of the MFMA result are
+  // real, so before the gates the four units of lane (quad, column b) move to lanes (quad,
+  // 4 i + b), one unit per lane, and a quarter of the transcendentals remain on the chain. It pays
+  // where a wave gates two or more tiles (Elman D=128: 0.565 -> 0.512 us per step); with one tile
+  // the scattered 4-byte state stores cost more than the transcendentals saved (D=64: 0.306 ->
+  // 0.312), so that design keeps a lane's four units.
+  const bool narrow = (CELL == CELL_ELMAN) && LOCAL && !F32 && MTW >= 2 && a.BR <= 4;
 
   const int u_base = tile0 * UPT;                   // first hidden unit of this workgroup
   const int U_wg = min(MT_WG * UPT, D - u_base);    // its hidden units (the last tiles may be idle)
@@ -809,6 +821,21 @@ __global__ void __launch_bounds__((NCW + 1) * 64, 1) fused_fwd_kernel(FusedArgs 
           outs[ri] = f32x4_t{h, c, 0.f, 0.f};
         }
         hlast[q][0] = h;
+      } else if (CELL == CELL_ELMAN && LOCAL && !F32 && MTW >= 2 && narrow) {
+        f32x4_t y;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) y[i] = pre[q][i] + wx4[i] + bia[q][i];
+        // lane 16 quad + 4 i + b takes component i of lane 16 quad + b (row shifts by 4 i, written
+        // only into bank i of each 16-lane row)
+        float x = y[0];
+        x = __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(y[1]), 0x114, 0xF, 0x2, false));
+        x = __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(y[2]), 0x118, 0xF, 0x4, false));
+        x = __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(y[3]), 0x11C, 0xF, 0x8, false));
+        const float hv = tanh_f(x);
+        const int bb = col & 3, u1 = gu[q] + (col >> 2);
+        hbuf_b[((t & 1) * 16 + bb) * HS + u1] = f2bf(hv);
+        if (bb < nvalid && a.out_h) a.out_h[(long long)(b0 + bb) * a.out_sb + (long long)t * a.out_st + (long long)n * D + u1] = hv;
+        hlast[q][0] = hv;
       } else {
         float h[4];
 #pragma unroll
@@ -845,7 +872,13 @@ __global__ void __launch_bounds__((NCW + 1) * 64, 1) fused_fwd_kernel(FusedArgs 
   }
   block_barrier();  // barrier T: the last step's outputs are in LDS for the I/O wave
   // last_states: the state after the last step, straight from registers
-  if (T > 0 && colv) {
+  if (T > 0 && narrow) {
+    const int bb = col & 3;
+#pragma unroll
+    for (int q = 0; q < GT; ++q)
+      if (gval[q] && bb < nvalid && a.last_h)
+        a.last_h[(long long)(b0 + bb) * a.last_sb + (long long)n * D + gu[q] + (col >> 2)] = hlast[q][0];
+  } else if (T > 0 && colv) {
 #pragma unroll
     for (int q = 0; q < GT; ++q) {
       if (!gval[q]) continue;

@@ -176,6 +176,36 @@ def test_forced_die_local(w, env):
     run_case(w, "fused", env=env)
 
 
+# A whole Elman head per workgroup with at most four batch rows and two tiles per wave: the gates
+# run one unit per lane after a DPP move (the lane's four units spread over four lanes). Ragged
+# last block (B=7 in blocks of 3), full blocks of 4, and an initial state.
+NARROW = [
+    (fi.HeadwiseWorkload("elman_narrow_D128_BR3", "elman", torch.bfloat16, B=7, T=9, N=2, D=128, seed=135, s0_var=1.0),
+     {"FRNN_FUSED_W": 1, "FRNN_FUSED_BR": 3}),
+    (fi.HeadwiseWorkload("elman_narrow_D128_BR4", "elman", torch.bfloat16, B=8, T=11, N=3, D=128, seed=136),
+     {"FRNN_FUSED_W": 1, "FRNN_FUSED_BR": 4}),
+    (fi.HeadwiseWorkload("elman_narrow_D128_BR1", "elman", torch.bfloat16, B=2, T=5, N=1, D=128, seed=137, s0_var=1.0),
+     {"FRNN_FUSED_W": 1, "FRNN_FUSED_BR": 1}),
+]
+
+
+@pytest.mark.parametrize("w,env", NARROW, ids=lambda x: getattr(x, "name", ""))
+def test_forced_narrow_elman(w, env):
+    hw = _hw()
+    old = {k: os.environ.get(k) for k in env}
+    os.environ.update({k: str(v) for k, v in env.items()})
+    try:
+        plan = hw.frnn_plan_str(hw._desc(w.B, w.T, w.N, w.D, w.cell, w.dtype), "fused")
+    finally:
+        for k, v in old.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+    assert "workgroup-local" in plan and f"BR={env['FRNN_FUSED_BR']} " in plan and "MTW=2 KTW=4" in plan, plan
+    run_case(w, "fused", env=env)
+
+
 @pytest.mark.parametrize("cell", ["lstm", "gru"])
 def test_fused_batch_chunks(cell):
     """A batch that does not fit co-resident runs as several launches over chunks of rows: the
