@@ -7,13 +7,14 @@
 // units. W workgroups share a group, each owning MT_WG consecutive tiles; their R^T
 // fragments stay in VGPRs for all T steps (the page's "weights kept in registers").
 //
-// Waves. Four compute waves run MFMA v_mfma_f32_16x16x32_bf16 with
+// Waves. Four to eight compute waves run MFMA v_mfma_f32_16x16x32_bf16 with
 //   A = R^T tile (16 rows x 32 k), B = h^T (32 k x 16 batch columns), D = pre-activations,
 // so that lane l ends up holding all four gates of unit (4*tile + l/16) for batch column l%16:
 // the gate math needs no cross-lane traffic. With KS > 1 the compute waves split K and add the
-// partial sums through LDS. A fifth wave does all other global-memory traffic: it streams Wx
-// several steps ahead into an LDS ring and writes the state outputs from an LDS ring two steps
-// behind. On gfx9 a wave's vector-memory counter retires in issue order, so keeping those
+// partial sums through LDS. One more wave does the other global-memory traffic: it streams Wx
+// several steps ahead into an LDS ring and, in the die-local design, writes the state outputs
+// from an LDS ring two steps behind (in the single-workgroup design the compute waves, which
+// never wait on a global load there, store the states themselves). On gfx9 a wave's vector-memory counter retires in issue order, so keeping those
 // long-latency accesses out of the compute waves keeps them off the serial chain: a compute wave
 // only ever waits on its own exchange traffic. One workgroup barrier per step orders the rings.
 //
@@ -92,9 +93,10 @@ struct FusedArgs {
 #endif
 
 constexpr int FUSED_IO_STAGES = 4;   // record steps in flight in the backward's I/O wave
-// max 64-bit Wx words (and output pairs) one I/O lane moves per step: the die-local design moves
-// few (its workgroups own few units), the single-workgroup design a whole head's rows (an Elman
-// head has a quarter of an LSTM head's Wx and half its outputs). Every slot costs a load per step.
+// max 64-bit Wx words (and, in the die-local design, output pairs) one I/O lane moves per step:
+// the die-local design moves few (its workgroups own few units), the single-workgroup design a
+// whole head's rows of Wx (an Elman head has a quarter of an LSTM head's). Every slot costs a load
+// per step.
 __host__ __device__ constexpr int fused_epl(bool local, int ncw, int cell) {
   return !local ? 2 : (cell == CELL_ELMAN ? 2 : (ncw == 4 ? 8 : 4));
 }
