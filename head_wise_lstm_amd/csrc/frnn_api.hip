@@ -258,7 +258,7 @@ int plan_fused(const Problem& p, const DevInfo& di, FusedPlan* out) {
         if (force_br && br != force_br) continue;
         FusedPlan fp;
         fp.v = v; fp.local = 1; fp.W = 1; fp.BR = br; fp.ncw = ncw; fp.ks = 1; fp.mtw = mtw; fp.ktw = KT;
-        fp.lds = (size_t)fused_lds(true, p.r_f32, ncw, 1, mtw, p.D).total;
+        fp.lds = (size_t)fused_lds(true, p.r_f32, ncw, 1, mtw, p.D, p.cell).total;
         consider(fp, di.cus);
       }
     }
@@ -287,7 +287,7 @@ int plan_fused(const Problem& p, const DevInfo& di, FusedPlan* out) {
           FusedPlan fp;
           fp.v = v; fp.local = 0; fp.W = W; fp.BR = BR; fp.ncw = ncw; fp.ks = ks; fp.mtw = mtw; fp.ktw = ktw;
           fp.n_xcd = di.n_xcd;
-          fp.lds = (size_t)fused_lds(false, false, ncw, ks, mtw, p.D).total;
+          fp.lds = (size_t)fused_lds(false, false, ncw, ks, mtw, p.D, p.cell).total;
           consider(fp, (slots_per_die / W) * di.n_xcd);
         }
       }

@@ -118,8 +118,16 @@ __host__ __device__ constexpr int fused_gt(int ncw, int ks, int mtw) {
 __host__ __device__ constexpr int fused_threads(int ncw) { return (ncw + 1) * 64; }
 
 struct FusedLds {
-  int h, part, wx, out, total;
+  int h, part, wx, out, dma, total;
 };
+
+// A whole bf16 Elman head per workgroup streams Wx straight into LDS (global_load_lds): a ring of
+// FUSED_DMA_STAGES steps, each slot FUSED_DMA_NE x 64 dwords in load order (dword i of load e at
+// slot + 4 (64 e + i): row b, units 2j, 2j+1 at dword b * D/2 + j). Nothing is held in registers
+// across steps, so no wait of the I/O wave covers more than the one step it needs.
+constexpr int FUSED_DMA_STAGES = 16;
+constexpr int FUSED_DMA_NE = 4;  // loads per step (a row is D/2 dwords; BR * D <= 512 here)
+__host__ __device__ constexpr bool fused_dma(bool local, bool f32, int cell) { return local && !f32 && cell == CELL_ELMAN; }
 
 // s_sleep units (64 clocks) before a step's first poll round. Polls compete with the stores
 // they wait for; holding back the first, certainly useless, round measured best at 4-6 units
@@ -156,7 +164,7 @@ __host__ __device__ constexpr int fused_poll_words(int ks, int mtw, int ktw) {
 // Words (32-bit, two bf16 units each) per row of a compute wave's poll stage, padded by 16 bytes.
 __host__ __device__ constexpr int fused_stage_row(int ktw) { return ktw * 16 + 4; }
 
-__host__ __device__ inline FusedLds fused_lds(bool local, bool f32, int ncw, int ks, int mtw, int D) {
+__host__ __device__ inline FusedLds fused_lds(bool local, bool f32, int ncw, int ks, int mtw, int D, int cell) {
   FusedLds L;
   const int gt = fused_gt(ncw, ks, mtw);
   const int mt_wg = mtw * (ncw / ks);
@@ -168,7 +176,8 @@ __host__ __device__ inline FusedLds fused_lds(bool local, bool f32, int ncw, int
   const int pbytes = (!local && ks > 1) ? 2 * ncw * FUSED_PART_ROW * 16 : 0;
   L.wx = L.part + pbytes;
   L.out = L.wx + 2 * ncw * gt * 1024;
-  L.total = L.out + 2 * ncw * gt * 1024;
+  L.dma = L.out + 2 * ncw * gt * 1024;
+  L.total = L.dma + (fused_dma(local, f32, cell) ? FUSED_DMA_STAGES * FUSED_DMA_NE * 256 : 0);
   return L;
 }
 
@@ -492,6 +501,54 @@ __device__ __forceinline__ void io_wave(const IoCtx& c, f32x4_t* wxs, const f32x
   if (G0 == 1 && c.T >= 1) io_store<CELL, NCW, KS, MTW, EPL>(c, d, c.T - 1, outs);
 }
 
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
+
+// s_waitcnt immediate (gfx9 encoding) that waits until at most n vector-memory operations remain
+// (expcnt and lgkmcnt left alone).
+__host__ __device__ constexpr int vmcnt_imm(int n) { return (n & 0xF) | (7 << 4) | (0xF << 8) | ((n >> 4) << 14); }
+
+// The I/O wave of a single-workgroup bf16 Elman design (see FUSED_DMA_STAGES). It runs barriers
+// -1 .. T with the compute waves. Interval k issues the loads of step k - 1 + L into the slot of
+// step k - 1 (read by the compute waves during step k - 1, before barrier k - 1), then waits for
+// the loads of step k + 1, issued L - 2 intervals earlier, and joins barrier k: the compute waves
+// read step k + 1's slot after it. Every interval issues the same FUSED_DMA_NE loads (steps are
+// clamped; lanes without a dword reload the first one into a slot position nobody reads), so a
+// constant count of loads stays in flight. It touches no LDS itself and uses a plain s_barrier,
+// so no wait of the compiler's joins its own. Single-workgroup designs never set the abort flag.
+__device__ __forceinline__ void io_wave_dma(const char* wxb, long long wx_sb, long long wx_st, int b0, int nvalid,
+                                            int n, int D, int T, int lane, char* ring) {
+  constexpr int L = FUSED_DMA_STAGES, NE = FUSED_DMA_NE;
+  const int dpr = D / 2;  // dwords per batch row
+  long long goff[NE];
+#pragma unroll
+  for (int e = 0; e < NE; ++e) {
+    const int wi = lane + 64 * e, r = wi / dpr, j = wi - r * dpr;
+    goff[e] = r < nvalid ? ((long long)(b0 + r) * wx_sb + (long long)n * D) * 2 + 4LL * j
+                         : ((long long)b0 * wx_sb + (long long)n * D) * 2;
+  }
+  const long long step_bytes = wx_st * 2;
+  auto issue = [&](int s) {
+    const int sc = min(max(s, 0), T - 1);
+    char* slot = ring + (s & (L - 1)) * NE * 256;
+#pragma unroll
+    for (int e = 0; e < NE; ++e)
+      __builtin_amdgcn_global_load_lds((glb_void_t*)(wxb + goff[e] + sc * step_bytes), (lds_void_t*)(slot + 256 * e), 4, 0, 0);
+  };
+  if (T == 0) {
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_s_barrier();
+    return;
+  }
+  for (int s = 0; s <= L - 3; ++s) issue(s);
+  for (int k = -1; k <= T; ++k) {
+    issue(k - 1 + L);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm((L - 2) * NE));
+    __builtin_amdgcn_s_barrier();
+  }
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // no load may land after the workgroup has ended
+}
+
 template <int CELL, bool F32, bool LOCAL, int NCW, int KS, int MTW, int KTW>
 __global__ void __launch_bounds__((NCW + 1) * 64, 1) fused_fwd_kernel(FusedArgs a) {
   constexpr int NT = (NCW + 1) * 64;
@@ -538,7 +595,7 @@ __global__ void __launch_bounds__((NCW + 1) * 64, 1) fused_fwd_kernel(FusedArgs 
   const int b0 = bblk * a.BR;
   const int nvalid = min(a.BR, a.B - b0);
   const int tile0 = w * MT_WG;
-  const FusedLds lay = fused_lds(LOCAL, F32, NCW, KS, MTW, D);
+  const FusedLds lay = fused_lds(LOCAL, F32, NCW, KS, MTW, D, CELL);
   constexpr int HPAD = fused_hpad(F32);
   const int HS = D + HPAD;  // row stride of the LDS h buffer (elements)
   float* hbuf_f = reinterpret_cast<float*>(smem + lay.h);
@@ -579,6 +636,14 @@ __global__ void __launch_bounds__((NCW + 1) * 64, 1) fused_fwd_kernel(FusedArgs 
   const int u_base = tile0 * UPT;                   // first hidden unit of this workgroup
   const int U_wg = min(MT_WG * UPT, D - u_base);    // its hidden units (the last tiles may be idle)
 
+  constexpr bool DMA = fused_dma(LOCAL, F32, CELL);
+  char* const dring = smem + lay.dma;
+  if constexpr (DMA) {
+    if (wave == NCW) {
+      io_wave_dma(reinterpret_cast<const char*>(a.Wx), a.wx_sb, a.wx_st, b0, nvalid, n, D, T, lane, dring);
+      return;
+    }
+  }
   if (wave == NCW) {
     IoCtx c;
     c.wxb = reinterpret_cast<const char*>(a.Wx);
@@ -704,7 +769,17 @@ __global__ void __launch_bounds__((NCW + 1) * 64, 1) fused_fwd_kernel(FusedArgs 
     // Wx of this step (the ring slot t & 1, written by the I/O wave before the barrier that
     // precedes the gating): read as early as that barrier allows
     f32x4_t wxq[GT];
-    if (LOCAL) {
+    if constexpr (DMA) {
+      // four units of row col from the DMA ring: two dwords (rows past nvalid read the last row)
+      const uint32_t* slot = reinterpret_cast<const uint32_t*>(dring + (t & (FUSED_DMA_STAGES - 1)) * FUSED_DMA_NE * 256);
+      const int rb = min(col, nvalid - 1);
+#pragma unroll
+      for (int q = 0; q < GT; ++q) {
+        const uint2 w = *reinterpret_cast<const uint2*>(slot + rb * (D / 2) + (gval[q] ? gu[q] / 2 : 0));
+        wxq[q] = f32x4_t{__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xFFFF0000u), __uint_as_float(w.y << 16),
+                         __uint_as_float(w.y & 0xFFFF0000u)};
+      }
+    } else if (LOCAL) {
 #pragma unroll
       for (int q = 0; q < GT; ++q) wxq[q] = wxs[(((t & 1) * NCW + wave) * GT + q) * 64 + lane];
     }
