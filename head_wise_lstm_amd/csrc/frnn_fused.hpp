@@ -104,8 +104,9 @@ __host__ __device__ constexpr int fused_epl(bool local, int ncw, int cell) {
 // Wx steps in flight in the forward's I/O wave: eight where a lane moves at most two words a step
 // (measured against four: Elman B=64 N=12 D=64 0.432 -> 0.394 us per step, LSTM B=16 D=768
 // 1.223 -> 1.200), four where it moves more (eight stages of those spill registers).
-// A whole Elman head per workgroup streams the most Wx per step of compute: sixteen steps in
-// flight there (Elman B=64 N=12 D=64: 0.317 -> 0.305 us per step against eight).
+// (A whole bf16 Elman head per workgroup streams Wx through its own LDS ring instead, see
+// FUSED_DMA_STAGES; the register ring of sixteen steps measured 0.317 -> 0.305 us per step there
+// against eight, and remains for fp32 Elman heads.)
 __host__ __device__ constexpr int fused_io_stages(bool local, int ncw, int cell) {
   return (local && cell == CELL_ELMAN) ? 16 : fused_epl(local, ncw, cell) <= 2 ? 8 : 4;
 }
