@@ -628,11 +628,9 @@ __global__ void __launch_bounds__((NCW + 1) * 64, 1) fused_fwd_kernel(FusedArgs 
   }
   // A whole Elman head with at most four batch rows: only columns 0-3 of the MFMA result are
   // real, so before the gates the four units of lane (quad, column b) move to lanes (quad,
-  // 4 i + b), one unit per lane, and a quarter of the transcendentals remain on the chain. It pays
-  // where a wave gates two or more tiles (Elman D=128: 0.565 -> 0.512 us per step); with one tile
-  // the scattered 4-byte state stores cost more than the transcendentals saved (D=64: 0.306 ->
-  // 0.312), so that design keeps a lane's four units.
-  const bool narrow = (CELL == CELL_ELMAN) && LOCAL && !F32 && MTW >= 2 && a.BR <= 4;
+  // 4 i + b), one unit per lane, and a quarter of the transcendentals remain on the chain
+  // (Elman D=128: 0.565 -> 0.512 us per step; B=16 N=12 D=64: 0.299 -> 0.287).
+  const bool narrow = (CELL == CELL_ELMAN) && LOCAL && !F32 && a.BR <= 4;
 
   const int u_base = tile0 * UPT;                   // first hidden unit of this workgroup
   const int U_wg = min(MT_WG * UPT, D - u_base);    // its hidden units (the last tiles may be idle)
@@ -899,7 +897,7 @@ __global__ void __launch_bounds__((NCW + 1) * 64, 1) fused_fwd_kernel(FusedArgs 
           outs[ri] = f32x4_t{h, c, 0.f, 0.f};
         }
         hlast[q][0] = h;
-      } else if (CELL == CELL_ELMAN && LOCAL && !F32 && MTW >= 2 && narrow) {
+      } else if (CELL == CELL_ELMAN && LOCAL && !F32 && narrow) {
         f32x4_t y;
 #pragma unroll
         for (int i = 0; i < 4; ++i) y[i] = pre[q][i] + wx4[i] + bia[q][i];
