@@ -354,6 +354,18 @@ void launch_transpose(const E* src, long long lds, int K, int Nc, E* dst, long l
   hipLaunchKernelGGL(transpose_kernel<E>, dim3((Nc + 31) / 32, ty), dim3(256), 0, st, src, lds, K, Nc, dst, ldd);
 }
 
+// Launch of the bf16 GEMM of ProjArgs: with bf16 A whose rows (and Bt's, and the parts' offsets)
+// start on 16-byte boundaries, the kernel that loads its tiles straight into LDS; otherwise the
+// register-staged one (fp32 A is rounded as it is staged). FRNN_PROJ_DMA=0 pins the latter.
+void launch_proj(const ProjArgs& pa, dim3 grid, hipStream_t st) {
+  if (pa.M <= 0 || pa.Nc <= 0) return;
+  const bool aligned = reinterpret_cast<uintptr_t>(pa.A) % 16 == 0 && reinterpret_cast<uintptr_t>(pa.Bt) % 16 == 0 &&
+                       pa.lda % 8 == 0 && pa.ldb % 8 == 0 && pa.a_z % 8 == 0 && pa.b_z % 8 == 0;
+  if (pa.a_f32) hipLaunchKernelGGL(proj_gemm_kernel<true>, grid, dim3(256), 0, st, pa);
+  else if (aligned && env_int("FRNN_PROJ_DMA", 1)) hipLaunchKernelGGL(proj_gemm_dma_kernel, grid, dim3(256), 0, st, pa);
+  else hipLaunchKernelGGL(proj_gemm_kernel<false>, grid, dim3(256), 0, st, pa);
+}
+
 // C[M][Nc] = A[M][K] . Bt[Nc][K]^T in fp32, for parts z = 0 .. parts-1 at once (A, Bt and C
 // offset by z * a_z, b_z, c_z elements): the tiled MFMA kernel for bf16 operands, the plain fp32
 // MFMA kernel for fp32 ones. K is a multiple of 32.
@@ -378,8 +390,7 @@ hipError_t launch_gemm(bool f32, int M, int Nc, int K, const void* A, long long 
   pa.C = C; pa.ldc = ldc;
   pa.a_z = a_z; pa.b_z = b_z; pa.c_z = c_z;
   const dim3 pgrid(((Nc + PJ_BN - 1) / PJ_BN) * ((M + PJ_BM - 1) / PJ_BM), parts);
-  if (a_f32) hipLaunchKernelGGL(proj_gemm_kernel<true>, pgrid, dim3(256), 0, st, pa);  // A rounded to bf16 as staged
-  else hipLaunchKernelGGL(proj_gemm_kernel<false>, pgrid, dim3(256), 0, st, pa);
+  launch_proj(pa, pgrid, st);
   return hipGetLastError();
 }
 
@@ -1241,8 +1252,7 @@ int frnn_lstm_stack_fwd(int L, int T, int B, int I, int H, int path, const void*
     pa.ldc = 4 * H;
     launch_transpose<uint16_t>(reinterpret_cast<const uint16_t*>(Wi[l]), pa.Nc, pa.K, pa.Nc, wit, pa.K, st);
     const dim3 pgrid(((pa.Nc + PJ_BN - 1) / PJ_BN) * ((pa.M + PJ_BM - 1) / PJ_BM));
-    if (pa.a_f32) hipLaunchKernelGGL(proj_gemm_kernel<true>, pgrid, dim3(256), 0, st, pa);
-    else hipLaunchKernelGGL(proj_gemm_kernel<false>, pgrid, dim3(256), 0, st, pa);
+    launch_proj(pa, pgrid, st);
     if (hipGetLastError() != hipSuccess) return FRNN_EHIP;
     // recurrence with Wh [H, 4H] read through strides: R[g][0][d][e] = Wh[d][g*H + e]
     Problem p;
@@ -1389,8 +1399,7 @@ int frnn_lstm_stack_bwd(int L, int T, int B, int I, int H, int path, const void*
     pa.ldc = 4 * H;
     launch_transpose<uint16_t>(reinterpret_cast<const uint16_t*>(Wi[l]), 4 * H, in, 4 * H, wit, in, st);
     const dim3 pgrid(((pa.Nc + PJ_BN - 1) / PJ_BN) * ((pa.M + PJ_BM - 1) / PJ_BM));
-    if (pa.a_f32) hipLaunchKernelGGL(proj_gemm_kernel<true>, pgrid, dim3(256), 0, st, pa);
-    else hipLaunchKernelGGL(proj_gemm_kernel<false>, pgrid, dim3(256), 0, st, pa);
+    launch_proj(pa, pgrid, st);
     if (hipGetLastError() != hipSuccess) return FRNN_EHIP;
     Problem p;
     std::memset(&p, 0, sizeof(p));

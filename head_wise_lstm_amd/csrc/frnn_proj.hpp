@@ -8,6 +8,7 @@
 // (8 x 4 tiles of v_mfma_f32_16x16x32_bf16, 32 accumulators), which keeps LDS traffic at about
 // 96 bytes per clock per CU. K goes 32 at a time through two LDS buffers: the next step's global
 // loads are in flight in registers while the current step's MFMAs run, one barrier per step.
+// With bf16 A, proj_gemm_dma_kernel loads the same tiles straight into a three-stage LDS ring.
 #pragma once
 
 #include <type_traits>
@@ -252,6 +253,118 @@ __global__ void __launch_bounds__(256, 2) proj_gemm_kernel(ProjArgs p) {
 #undef PJ_GLOAD
 #undef PJ_LSTORE
   // Epilogue: lane (col, quad) holds rows 4*quad + r of column col of every 16 x 16 tile.
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int gn = n0 + wn * 64 + j * 16 + col;
+    if (gn >= p.Nc) continue;
+    const float bias = (p.b1 ? bf2f(p.b1[gn]) : 0.0f) + (p.b2 ? bf2f(p.b2[gn]) : 0.0f);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const long long gm = m0 + wm * 128 + i * 16 + 4 * quad + r;
+        if (gm < p.M) p.C[gm * p.ldc + gn] = acc[i][j][r] + bias;
+      }
+    }
+  }
+}
+
+// bf16 A only: the same tiles and wave layout, with the operands loaded straight from memory into
+// a ring of PD_STAGES LDS stages (16-byte global_load_lds), so that two K steps are in flight
+// without staging registers. One load instruction of a wave fills 1 KB of LDS, lane l at byte
+// 16 l: 16 rows of 64 bytes (32 k). Lane l therefore fetches row l / 4 of its 16-row block and the
+// 16-byte chunk that belongs at position l % 4, where chunk c of row r sits at position
+// c ^ ((r / 4) % 4): the 16 rows that a fragment read touches at one chunk then fall on 16
+// different 16-byte bank groups. Rows past the end load the last row: only outputs that are never
+// stored depend on them. A and Bt rows must start on 16-byte boundaries.
+constexpr int PD_STAGES = 3;
+constexpr int PD_A_BYTES = PJ_BM * PJ_BK * 2, PD_B_BYTES = PJ_BN * PJ_BK * 2;
+constexpr int PD_STAGE_BYTES = PD_A_BYTES + PD_B_BYTES;  // 24 KB: two workgroups fit a CU with 3 stages
+constexpr int PD_A_LOADS = PJ_BM / 16 / 4, PD_B_LOADS = PJ_BN / 16 / 4;  // per wave and stage: 4 and 2
+constexpr int PD_LOADS = PD_A_LOADS + PD_B_LOADS;
+
+typedef __attribute__((address_space(3))) void pd_lds_t;
+typedef __attribute__((address_space(1))) void pd_glb_t;
+
+// s_waitcnt immediate (gfx9 encoding) that waits until at most n vector-memory operations and no
+// LDS operation remain (expcnt left alone).
+__host__ __device__ constexpr int pd_vmcnt(int n) { return (n & 0xF) | (7 << 4) | ((n >> 4) << 14); }
+
+__global__ void __launch_bounds__(256, 2) proj_gemm_dma_kernel(ProjArgs p) {
+  __shared__ __attribute__((aligned(1024))) char ring[PD_STAGES * PD_STAGE_BYTES];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int col = lane & 15, quad = lane >> 4;
+  const int wm = wave >> 1, wn = wave & 1;
+  if (blockIdx.y) {
+    p.A = reinterpret_cast<const char*>(p.A) + blockIdx.y * p.a_z * 2;
+    p.Bt += blockIdx.y * p.b_z;
+    p.C += blockIdx.y * p.c_z;
+  }
+  const int ntn = (p.Nc + PJ_BN - 1) / PJ_BN;
+  const int L = blockIdx.x, G = gridDim.x;
+  const int tile = (G % PJ_DIES == 0) ? (L % PJ_DIES) * (G / PJ_DIES) + L / PJ_DIES : L;
+  const long long m0 = (long long)(tile / ntn) * PJ_BM;
+  const int n0 = (tile % ntn) * PJ_BN;
+
+  // this lane's source rows: A blocks 4 wave + e, B blocks 2 wave + e; the chunk for position lane % 4
+  const int brow = lane >> 2, chunk = (lane & 3) ^ ((lane >> 4) & 3);
+  const char* asrc[PD_A_LOADS];
+  const char* bsrc[PD_B_LOADS];
+#pragma unroll
+  for (int e = 0; e < PD_A_LOADS; ++e) {
+    const long long r0 = m0 + 16 * (PD_A_LOADS * wave + e) + brow, r = r0 < p.M ? r0 : p.M - 1;
+    asrc[e] = reinterpret_cast<const char*>(p.A) + (r * p.lda + 8 * chunk) * 2;
+  }
+#pragma unroll
+  for (int e = 0; e < PD_B_LOADS; ++e) {
+    const long long r0 = (long long)n0 + 16 * (PD_B_LOADS * wave + e) + brow, r = r0 < p.Nc ? r0 : p.Nc - 1;
+    bsrc[e] = reinterpret_cast<const char*>(p.Bt + r * p.ldb + 8 * chunk);
+  }
+  auto issue = [&](int kt) {
+    char* st = ring + (kt % PD_STAGES) * PD_STAGE_BYTES;
+    const int kb = kt * PJ_BK * 2;
+#pragma unroll
+    for (int e = 0; e < PD_A_LOADS; ++e)
+      __builtin_amdgcn_global_load_lds((pd_glb_t*)(asrc[e] + kb), (pd_lds_t*)(st + 1024 * (PD_A_LOADS * wave + e)), 16,
+                                       0, 0);
+#pragma unroll
+    for (int e = 0; e < PD_B_LOADS; ++e)
+      __builtin_amdgcn_global_load_lds((pd_glb_t*)(bsrc[e] + kb),
+                                       (pd_lds_t*)(st + PD_A_BYTES + 1024 * (PD_B_LOADS * wave + e)), 16, 0, 0);
+  };
+  // fragment (row col of a 16-row block, k 8 quad .. 8 quad + 7)
+  const int foff = col * 64 + ((quad ^ (col >> 2)) & 3) * 16;
+
+  f32x4_t acc[8][4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const int nk = p.K / PJ_BK;
+  if (nk > 0) issue(0);
+  if (nk > 1) issue(1);
+  for (int kt = 0; kt < nk; ++kt) {
+    // wait for this wave's loads of step kt and its reads of step kt - 1, then for every wave's:
+    // after the barrier step kt's stage is complete and step kt - 1's slot is free for step kt + 2
+    asm volatile("" ::: "memory");
+    if (kt + 1 < nk) __builtin_amdgcn_s_waitcnt(pd_vmcnt(PD_LOADS));
+    else __builtin_amdgcn_s_waitcnt(pd_vmcnt(0));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (kt + 2 < nk) issue(kt + 2);
+    const char* st = ring + (kt % PD_STAGES) * PD_STAGE_BYTES;
+    bf16x8_t bfr[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      bfr[j] = *reinterpret_cast<const bf16x8_t*>(st + PD_A_BYTES + 1024 * (wn * 4 + j) + foff);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const bf16x8_t af = *reinterpret_cast<const bf16x8_t*>(st + 1024 * (wm * 8 + i) + foff);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = mfma_bf16(af, bfr[j], acc[i][j]);
+    }
+  }
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int gn = n0 + wn * 64 + j * 16 + col;

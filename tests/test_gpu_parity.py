@@ -339,16 +339,25 @@ def test_full_workload(name, path):
     run_case(fi.get_workload(name), path, pairs=FULL_PAIRS[name])
 
 
-def _stack_case(w, path, rows):
+def _stack_case(w, path, rows, env=None):
     hw = _hw()
     x = fi.make_inputs(w)
     dev = torch.device("cuda:0")
-    _log(f"stack case {w.name} L={w.L} T={w.T} B={w.B} I={w.I} H={w.H} path={path}")
+    _log(f"stack case {w.name} L={w.L} T={w.T} B={w.B} I={w.I} H={w.H} path={path} env={env}")
     g = lambda t: None if t is None else t.to(dev)
-    out, hn, cn = hw.frnn_lstm_stack_fwd(g(x["x"]), [g(t) for t in x["Wi"]], [g(t) for t in x["Wh"]],
-                                         [g(t) for t in x["b_ih"]], [g(t) for t in x["b_hh"]], g(x["h0"]), g(x["c0"]),
-                                         path=path)
-    torch.cuda.synchronize()
+    old = {k: os.environ.get(k) for k in (env or {})}
+    os.environ.update({k: str(v) for k, v in (env or {}).items()})
+    try:
+        out, hn, cn = hw.frnn_lstm_stack_fwd(g(x["x"]), [g(t) for t in x["Wi"]], [g(t) for t in x["Wh"]],
+                                             [g(t) for t in x["b_ih"]], [g(t) for t in x["b_hh"]], g(x["h0"]),
+                                             g(x["c0"]), path=path)
+        torch.cuda.synchronize()
+    finally:
+        for k, v in old.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
     f = fi.to_f64
     sel = lambda a, axis: np.take(a, rows, axis=axis)
     ro, rh, rc = oracle.lstm_stack_p3(sel(f(x["x"]), 1), [f(t) for t in x["Wi"]], [f(t) for t in x["Wh"]],
@@ -369,6 +378,11 @@ STACK_SMALL = fi.StackWorkload("stack_small", torch.bfloat16, L=2, T=19, B=10, I
 @pytest.mark.parametrize("path", ["fused", "alternating"])
 def test_stack_small(path):
     _stack_case(STACK_SMALL, path, list(range(STACK_SMALL.B)))
+
+
+def test_stack_small_register_staged_projection():
+    # the first layer's bf16 projection through the register-staged GEMM instead of the LDS-DMA one
+    _stack_case(STACK_SMALL, "fused", list(range(STACK_SMALL.B)), env={"FRNN_PROJ_DMA": 0})
 
 
 @pytest.mark.parametrize("path", ["fused", "alternating"])
