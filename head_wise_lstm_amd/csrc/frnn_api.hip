@@ -361,9 +361,16 @@ void launch_proj(const ProjArgs& pa, dim3 grid, hipStream_t st) {
   if (pa.M <= 0 || pa.Nc <= 0) return;
   const bool aligned = reinterpret_cast<uintptr_t>(pa.A) % 16 == 0 && reinterpret_cast<uintptr_t>(pa.Bt) % 16 == 0 &&
                        pa.lda % 8 == 0 && pa.ldb % 8 == 0 && pa.a_z % 8 == 0 && pa.b_z % 8 == 0;
-  if (pa.a_f32) hipLaunchKernelGGL(proj_gemm_kernel<true>, grid, dim3(256), 0, st, pa);
-  else if (aligned && env_int("FRNN_PROJ_DMA", 1)) hipLaunchKernelGGL(proj_gemm_dma_kernel, grid, dim3(256), 0, st, pa);
-  else hipLaunchKernelGGL(proj_gemm_kernel<false>, grid, dim3(256), 0, st, pa);
+  const bool dma = !pa.a_f32 && aligned && env_int("FRNN_PROJ_DMA", 1);
+  if (pa.nt) {
+    if (pa.a_f32) hipLaunchKernelGGL((proj_gemm_kernel<true, true>), grid, dim3(256), 0, st, pa);
+    else if (dma) hipLaunchKernelGGL(proj_gemm_dma_kernel<true>, grid, dim3(256), 0, st, pa);
+    else hipLaunchKernelGGL((proj_gemm_kernel<false, true>), grid, dim3(256), 0, st, pa);
+  } else {
+    if (pa.a_f32) hipLaunchKernelGGL((proj_gemm_kernel<true, false>), grid, dim3(256), 0, st, pa);
+    else if (dma) hipLaunchKernelGGL(proj_gemm_dma_kernel<false>, grid, dim3(256), 0, st, pa);
+    else hipLaunchKernelGGL((proj_gemm_kernel<false, false>), grid, dim3(256), 0, st, pa);
+  }
 }
 
 // C[M][Nc] = A[M][K] . Bt[Nc][K]^T in fp32, for parts z = 0 .. parts-1 at once (A, Bt and C
@@ -389,6 +396,7 @@ hipError_t launch_gemm(bool f32, int M, int Nc, int K, const void* A, long long 
   pa.b1 = nullptr; pa.b2 = nullptr;
   pa.C = C; pa.ldc = ldc;
   pa.a_z = a_z; pa.b_z = b_z; pa.c_z = c_z;
+  pa.nt = 1;  // every caller's product is read by a streaming kernel
   const dim3 pgrid(((Nc + PJ_BN - 1) / PJ_BN) * ((M + PJ_BM - 1) / PJ_BM), parts);
   launch_proj(pa, pgrid, st);
   return hipGetLastError();
@@ -1246,6 +1254,7 @@ int frnn_lstm_stack_fwd(int L, int T, int B, int I, int H, int path, const void*
     pa.Bt = wit;
     pa.ldb = pa.K;
     pa.a_z = pa.b_z = pa.c_z = 0;
+    pa.nt = 0;  // the recurrence reads Wx next: left where its loads find it soonest
     pa.b1 = b_ih ? reinterpret_cast<const uint16_t*>(b_ih[l]) : nullptr;
     pa.b2 = b_hh ? reinterpret_cast<const uint16_t*>(b_hh[l]) : nullptr;
     pa.C = wx;
@@ -1393,6 +1402,7 @@ int frnn_lstm_stack_bwd(int L, int T, int B, int I, int H, int path, const void*
     pa.Bt = wit;
     pa.ldb = in;
     pa.a_z = pa.b_z = pa.c_z = 0;
+    pa.nt = 0;  // the recurrence reads Wx next: left where its loads find it soonest
     pa.b1 = b_ih ? reinterpret_cast<const uint16_t*>(b_ih[l]) : nullptr;
     pa.b2 = b_hh ? reinterpret_cast<const uint16_t*>(b_hh[l]) : nullptr;
     pa.C = layer_wx(l);

@@ -29,7 +29,15 @@ struct ProjArgs {
   float* C;
   long long ldc;
   long long a_z, b_z, c_z;  // element offsets of A, Bt and C per blockIdx.y (independent parts)
+  int nt;  // 1: C by streaming stores (read later by a streaming kernel, not by a recurrence)
 };
+
+// (a compile-time choice: with a run-time one the compiler merges both stores into the plain one)
+template <bool NT>
+__device__ __forceinline__ void proj_put(float* c, float v) {
+  if constexpr (NT) __builtin_nontemporal_store(v, c);
+  else *c = v;
+}
 
 constexpr int PJ_BM = 256, PJ_BN = 128, PJ_BK = 32;
 constexpr int PJ_DIES = 8;  // accelerator dies (XCDs) of an MI355X
@@ -182,7 +190,7 @@ __device__ __forceinline__ void proj_store8(uint16_t* dst, const Stage8<F32>& st
 }
 
 // AF32: A is fp32. Two workgroups per CU: while one waits for its loads, the other multiplies.
-template <bool AF32>
+template <bool AF32, bool NT>
 __global__ void __launch_bounds__(256, 2) proj_gemm_kernel(ProjArgs p) {
   // two stages of A (256 x 32) and B (128 x 32), rows padded to PJ_LS
   __shared__ __attribute__((aligned(16))) uint16_t As[2][PJ_BM * PJ_LS];
@@ -263,7 +271,7 @@ __global__ void __launch_bounds__(256, 2) proj_gemm_kernel(ProjArgs p) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const long long gm = m0 + wm * 128 + i * 16 + 4 * quad + r;
-        if (gm < p.M) p.C[gm * p.ldc + gn] = acc[i][j][r] + bias;
+        if (gm < p.M) proj_put<NT>(&p.C[gm * p.ldc + gn], acc[i][j][r] + bias);
       }
     }
   }
@@ -290,6 +298,7 @@ typedef __attribute__((address_space(1))) void pd_glb_t;
 // LDS operation remain (expcnt left alone).
 __host__ __device__ constexpr int pd_vmcnt(int n) { return (n & 0xF) | (7 << 4) | ((n >> 4) << 14); }
 
+template <bool NT>
 __global__ void __launch_bounds__(256, 2) proj_gemm_dma_kernel(ProjArgs p) {
   __shared__ __attribute__((aligned(1024))) char ring[PD_STAGES * PD_STAGE_BYTES];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -365,6 +374,7 @@ __global__ void __launch_bounds__(256, 2) proj_gemm_dma_kernel(ProjArgs p) {
       for (int j = 0; j < 4; ++j) acc[i][j] = mfma_bf16(af, bfr[j], acc[i][j]);
     }
   }
+  // epilogue as in proj_gemm_kernel
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int gn = n0 + wn * 64 + j * 16 + col;
@@ -375,7 +385,7 @@ __global__ void __launch_bounds__(256, 2) proj_gemm_dma_kernel(ProjArgs p) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const long long gm = m0 + wm * 128 + i * 16 + 4 * quad + r;
-        if (gm < p.M) p.C[gm * p.ldc + gn] = acc[i][j][r] + bias;
+        if (gm < p.M) proj_put<NT>(&p.C[gm * p.ldc + gn], acc[i][j][r] + bias);
       }
     }
   }
