@@ -20,6 +20,10 @@ The arithmetic lives in ``frnn_oracle.c`` (plain C, double precision, OpenMP ove
   pinned head-wise forward and backward and library matmuls for the projections.
 * ``lstm_stack_p3`` -- "5.3 LSTM", MyLSTM.set_weights and MyLSTM.forward: time loop outermost,
   layers inside it, bias = bias_ih + bias_hh, Wi stored [in, 4H], Wh stored [H, 4H].
+* ``lstm_stack_dirs`` -- the same cell with one or two directions per layer, layer by layer. The
+  page's MyLSTM takes ``bidirectional`` and copies "_reverse" weights but its forward never uses
+  them; the reading (torch.nn.LSTM's): direction 1 runs the layer's input from the last step to
+  the first with its own weights, and a layer's output is [h of direction 0, h of direction 1].
 
 Pins (tests/test_oracle_pins.py): closed forms (R = 0 geometric gating, saturated forget gate,
 Elman and GRU scalar iterations) computed independently at 50 significant digits, GRU closed forms
@@ -90,6 +94,12 @@ class Oracle:
         lib.oracle_lstm_stack_p3.restype = ctypes.c_int
         lib.oracle_lstm_stack_p3.argtypes = [
             ctypes.c_long, ctypes.c_long, ctypes.c_long, ctypes.c_long, ctypes.c_long,
+            dp, ctypes.POINTER(dp), ctypes.POINTER(dp), ctypes.POINTER(dp), ctypes.POINTER(dp),
+            dp, dp, dp, dp, dp,
+        ]
+        lib.oracle_lstm_stack_dirs.restype = ctypes.c_int
+        lib.oracle_lstm_stack_dirs.argtypes = [
+            ctypes.c_long, ctypes.c_long, ctypes.c_long, ctypes.c_long, ctypes.c_long, ctypes.c_long,
             dp, ctypes.POINTER(dp), ctypes.POINTER(dp), ctypes.POINTER(dp), ctypes.POINTER(dp),
             dp, dp, dp, dp, dp,
         ]
@@ -186,6 +196,40 @@ class Oracle:
         return out, hn, cn
 
 
+    def lstm_stack_dirs(self, x, Wi, Wh, b_ih, b_hh, h0=None, c0=None, dirs: int = 1):
+        """Multi-layer LSTM with ``dirs`` (1 or 2) directions per layer, in float64.
+
+        x [T,B,I]; Wi, Wh, b_ih, b_hh: lists of L*dirs entries, layer l direction k at l*dirs + k
+        ([in,4H] with in = I for l = 0 else dirs*H, [H,4H], [4H], [4H]; a bias may be None);
+        h0, c0 [L*dirs,B,H] or None. Returns (out [T,B,dirs*H], hn, cn [L*dirs,B,H]).
+        """
+        x = _f64(x)
+        T, B, I = x.shape
+        if dirs not in (1, 2) or len(Wi) % dirs:
+            raise ValueError("dirs must be 1 or 2, with dirs weights per layer")
+        L = len(Wi) // dirs
+        H = Wh[0].shape[0]
+        Wi = [_f64(w) for w in Wi]
+        Wh = [_f64(w) for w in Wh]
+        b_ih = [np.zeros(4 * H) if v is None else _f64(v) for v in b_ih]
+        b_hh = [np.zeros(4 * H) if v is None else _f64(v) for v in b_hh]
+        for j in range(L * dirs):
+            if Wi[j].shape != ((I if j < dirs else dirs * H), 4 * H) or Wh[j].shape != (H, 4 * H):
+                raise ValueError("weight shape mismatch")
+        h0, c0 = _f64(h0), _f64(c0)
+        out = np.empty((T, B, dirs * H))
+        hn = np.empty((L * dirs, B, H))
+        cn = np.empty((L * dirs, B, H))
+        arr = ctypes.POINTER(ctypes.c_double) * (L * dirs)
+        rc = self.lib.oracle_lstm_stack_dirs(
+            L, dirs, T, B, I, H, _ptr(x), arr(*[_ptr(w) for w in Wi]), arr(*[_ptr(w) for w in Wh]),
+            arr(*[_ptr(v) for v in b_ih]), arr(*[_ptr(v) for v in b_hh]), _ptr(h0), _ptr(c0),
+            _ptr(out), _ptr(hn), _ptr(cn))
+        if rc != 0:
+            raise RuntimeError("oracle_lstm_stack_dirs failed")
+        return out, hn, cn
+
+
 def lstm_stack_bwd(orc, x, Wi, Wh, b_ih, b_hh, h0=None, c0=None, dout=None, dhn=None, dcn=None):
     """Backward of the plain multi-layer LSTM of "5.3 LSTM" in float64: the gradients of
     L = sum(dout * out) + sum(dhn * hn) + sum(dcn * cn) with respect to x, Wi[l], Wh[l],
@@ -260,6 +304,10 @@ def headwise_bwd(*args, **kwargs):
 
 def lstm_stack_p3(*args, **kwargs):
     return default().lstm_stack_p3(*args, **kwargs)
+
+
+def lstm_stack_dirs(*args, **kwargs):
+    return default().lstm_stack_dirs(*args, **kwargs)
 
 
 def lstm_stack_bwd_p3(*args, **kwargs):

@@ -424,3 +424,88 @@ int oracle_lstm_stack_p3(long L, long T, long B, long I, long H, const double* x
   free(bias);
   return failed ? -1 : 0;
 }
+
+/*
+ * Multi-layer LSTM with one or two directions per layer. 5.3 LSTM (MyLSTM.__init__) takes a
+ * `bidirectional` flag and set_weights copies the "_reverse" weights of each layer, but the page's
+ * forward never uses them. The reading taken (the one of torch.nn.LSTM, whose state_dict names
+ * the page copies): direction 1 of a layer is the same cell with its own weights, run over the
+ * layer's input sequence from the last step to the first; the layer's output at step t is the
+ * concatenation [h of direction 0 at t, h of direction 1 at t]; layer l >= 1 takes that
+ * 2H-wide output as its input. With one direction this is the page's forward in layer-major
+ * order.
+ *   x   [T,B,I] input sequence
+ *   Wi[j] [in_l, 4H] (in_0 = I, in_l = dirs*H), Wh[j] [H, 4H], b_ih[j], b_hh[j] [4H],
+ *         for layer l and direction k at j = l*dirs + k; the bias used is b_ih + b_hh
+ *   h0, c0 [L*dirs,B,H] or NULL for zeros
+ *   out [T,B,dirs*H] the top layer's output at every step; hn, cn [L*dirs,B,H] the state each
+ *       direction ends in (direction 1: after consuming step 0). NULL: not written.
+ * Each layer runs whole before the next; each direction runs its own time loop. Batch rows are
+ * independent and run in parallel.
+ */
+int oracle_lstm_stack_dirs(long L, long dirs, long T, long B, long I, long H, const double* x,
+                           const double* const* Wi, const double* const* Wh, const double* const* b_ih,
+                           const double* const* b_hh, const double* h0, const double* c0, double* out,
+                           double* hn, double* cn) {
+  if (L <= 0 || (dirs != 1 && dirs != 2) || B <= 0 || I <= 0 || H <= 0 || T < 0) return -1;
+  const long H4 = 4 * H, W = dirs * H;  /* W: width of a layer's output */
+  int failed = 0;
+
+#pragma omp parallel for schedule(dynamic, 1)
+  for (long bi = 0; bi < B; ++bi) {
+    double* prev = (double*)malloc(sizeof(double) * (T > 0 ? T : 1) * W);  /* layer input, l >= 1 */
+    double* cur = (double*)malloc(sizeof(double) * (T > 0 ? T : 1) * W);   /* layer output */
+    double* h = (double*)malloc(sizeof(double) * H);
+    double* c = (double*)malloc(sizeof(double) * H);
+    double* ifgo = (double*)malloc(sizeof(double) * H4);
+    if (!prev || !cur || !h || !c || !ifgo) {
+      failed = 1;
+      free(prev); free(cur); free(h); free(c); free(ifgo);
+      continue;
+    }
+    for (long l = 0; l < L; ++l) {
+      const long K = (l == 0) ? I : W;
+      for (long k = 0; k < dirs; ++k) {
+        const long j = l * dirs + k;
+        for (long e = 0; e < H; ++e) {
+          h[e] = h0 ? h0[(j * B + bi) * H + e] : 0.0;
+          c[e] = c0 ? c0[(j * B + bi) * H + e] : 0.0;
+        }
+        for (long s = 0; s < T; ++s) {
+          const long t = (k == 0) ? s : T - 1 - s;  /* direction 1 walks the sequence backwards */
+          const double* in = (l == 0) ? x + (t * B + bi) * I : prev + t * W;
+          for (long q = 0; q < H4; ++q) ifgo[q] = b_ih[j][q] + b_hh[j][q];
+          for (long d = 0; d < K; ++d) {
+            const double v = in[d];
+            const double* row = Wi[j] + d * H4;
+            for (long q = 0; q < H4; ++q) ifgo[q] += v * row[q];
+          }
+          for (long d = 0; d < H; ++d) {
+            const double v = h[d];
+            const double* row = Wh[j] + d * H4;
+            for (long q = 0; q < H4; ++q) ifgo[q] += v * row[q];
+          }
+          for (long e = 0; e < H; ++e) {
+            const double ig = sigmoid(ifgo[0 * H + e]);
+            const double fg = sigmoid(ifgo[1 * H + e]);
+            const double gg = tanh(ifgo[2 * H + e]);
+            const double og = sigmoid(ifgo[3 * H + e]);
+            c[e] = fg * c[e] + ig * gg;
+            h[e] = og * tanh(c[e]);
+            cur[t * W + k * H + e] = h[e];
+          }
+        }
+        for (long e = 0; e < H; ++e) {
+          if (hn) hn[(j * B + bi) * H + e] = h[e];
+          if (cn) cn[(j * B + bi) * H + e] = c[e];
+        }
+      }
+      double* sw = prev; prev = cur; cur = sw;  /* this layer's output is the next one's input */
+    }
+    if (out)
+      for (long t = 0; t < T; ++t)
+        for (long q = 0; q < W; ++q) out[(t * B + bi) * W + q] = prev[t * W + q];
+    free(prev); free(cur); free(h); free(c); free(ifgo);
+  }
+  return failed ? -1 : 0;
+}

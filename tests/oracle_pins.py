@@ -14,7 +14,9 @@ Kinds of pin:
 * invariants: heads independent (= one wide head with block-diagonal R), batch permutation,
   continuation through last_states, T = 0, state bounds, row subsets;
 * two formulations: the page's time-major multi-layer loop against a layer-major composition of
-  head-wise runs.
+  head-wise runs, and against the layer-by-layer formulation the bidirectional stack uses;
+* the bidirectional reading (torch.nn.LSTM(bidirectional=True) in float64, a time-reversed
+  one-direction run, layer composition).
 """
 from __future__ import annotations
 
@@ -499,6 +501,95 @@ def pin_layer_major(orc):
         np.testing.assert_allclose(last[0, :, 0, 0], hn[l], rtol=0, atol=1e-12)
         np.testing.assert_allclose(last[1, :, 0, 0], cn[l], rtol=0, atol=1e-12)
     np.testing.assert_allclose(inp, out, rtol=0, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------- bidirectional
+def _torch_stack_weights(m, L, dirs):
+    """The "5.3 LSTM" page's weight reading of a torch.nn.LSTM state_dict (weight_ih_l{k}.T,
+    weight_hh_l{k}.T, bias_ih_l{k}, bias_hh_l{k}, and the "_reverse" ones of direction 1), in the
+    oracle's order l * dirs + k."""
+    sd = m.state_dict()
+    sfx = ["", "_reverse"][:dirs]
+    names = [(l, s) for l in range(L) for s in sfx]
+    Wi = [sd[f"weight_ih_l{l}{s}"].numpy().T for l, s in names]
+    Wh = [sd[f"weight_hh_l{l}{s}"].numpy().T for l, s in names]
+    bi = [sd[f"bias_ih_l{l}{s}"].numpy() for l, s in names]
+    bh = [sd[f"bias_hh_l{l}{s}"].numpy() for l, s in names]
+    return Wi, Wh, bi, bh
+
+
+def pin_torch_lstm_bidirectional(orc):
+    """torch.nn.LSTM(bidirectional=True) in float64: two layers of two directions, initial
+    states, outputs [T,B,2H] and final states [L*2,B,H] in its (layer, direction) order."""
+    T, B, I, H, L = 7, 3, 5, 4, 2
+    torch.manual_seed(23)
+    m = torch.nn.LSTM(I, H, num_layers=L, bidirectional=True, dtype=torch.float64)
+    rng = np.random.default_rng(23)
+    x = rng.normal(size=(T, B, I))
+    h0 = rng.normal(size=(2 * L, B, H))
+    c0 = rng.normal(size=(2 * L, B, H))
+    with torch.no_grad():
+        ref, (rh, rc) = m(torch.from_numpy(x), (torch.from_numpy(h0), torch.from_numpy(c0)))
+    Wi, Wh, bi, bh = _torch_stack_weights(m, L, 2)
+    out, hn, cn = orc.lstm_stack_dirs(x, Wi, Wh, bi, bh, h0, c0, dirs=2)
+    np.testing.assert_allclose(out, ref.numpy(), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(hn, rh.numpy(), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(cn, rc.numpy(), rtol=0, atol=1e-12)
+
+
+def pin_stack_one_direction_is_the_page_loop(orc):
+    """With one direction, the layer-by-layer formulation equals the page's time-major loop."""
+    T, B, I, H, L = 8, 2, 6, 4, 3
+    rng = np.random.default_rng(24)
+    x = rng.normal(size=(T, B, I))
+    Wi = [rng.normal(size=((I if l == 0 else H), 4 * H)) * 0.5 for l in range(L)]
+    Wh = [rng.normal(size=(H, 4 * H)) * 0.5 for _ in range(L)]
+    bi = [rng.normal(size=4 * H) * 0.3 for _ in range(L)]
+    bh = [rng.normal(size=4 * H) * 0.3 for _ in range(L)]
+    h0 = rng.normal(size=(L, B, H))
+    c0 = rng.normal(size=(L, B, H))
+    a = orc.lstm_stack_p3(x, Wi, Wh, bi, bh, h0, c0)
+    b = orc.lstm_stack_dirs(x, Wi, Wh, bi, bh, h0, c0, dirs=1)
+    for u, v in zip(a, b):
+        np.testing.assert_allclose(v, u, rtol=0, atol=1e-13)
+
+
+def pin_bidirectional_reverse_is_flipped_forward(orc):
+    """Direction 1 of a layer equals a one-direction run over the time-reversed sequence with the
+    reverse weights, reversed back; direction 0 equals a plain one-direction run."""
+    T, B, I, H = 9, 3, 5, 4
+    rng = np.random.default_rng(25)
+    x = rng.normal(size=(T, B, I))
+    Wi = [rng.normal(size=(I, 4 * H)) * 0.5 for _ in range(2)]
+    Wh = [rng.normal(size=(H, 4 * H)) * 0.5 for _ in range(2)]
+    bi = [rng.normal(size=4 * H) * 0.3 for _ in range(2)]
+    bh = [rng.normal(size=4 * H) * 0.3 for _ in range(2)]
+    h0 = rng.normal(size=(2, B, H))
+    c0 = rng.normal(size=(2, B, H))
+    out, hn, cn = orc.lstm_stack_dirs(x, Wi, Wh, bi, bh, h0, c0, dirs=2)
+    f_out, f_hn, f_cn = orc.lstm_stack_p3(x, Wi[:1], Wh[:1], bi[:1], bh[:1], h0[:1], c0[:1])
+    r_out, r_hn, r_cn = orc.lstm_stack_p3(x[::-1].copy(), Wi[1:], Wh[1:], bi[1:], bh[1:], h0[1:], c0[1:])
+    np.testing.assert_allclose(out[:, :, :H], f_out, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(out[:, :, H:], r_out[::-1], rtol=0, atol=1e-13)
+    np.testing.assert_allclose(hn, np.concatenate([f_hn, r_hn]), rtol=0, atol=1e-13)
+    np.testing.assert_allclose(cn, np.concatenate([f_cn, r_cn]), rtol=0, atol=1e-13)
+
+
+def pin_bidirectional_layers_compose(orc):
+    """Two bidirectional layers equal one bidirectional layer fed the other's [T,B,2H] output."""
+    T, B, I, H = 6, 2, 3, 4
+    rng = np.random.default_rng(26)
+    x = rng.normal(size=(T, B, I))
+    Wi = [rng.normal(size=(I, 4 * H)) * 0.5 for _ in range(2)] + [rng.normal(size=(2 * H, 4 * H)) * 0.5 for _ in range(2)]
+    Wh = [rng.normal(size=(H, 4 * H)) * 0.5 for _ in range(4)]
+    bi = [rng.normal(size=4 * H) * 0.3 for _ in range(4)]
+    bh = [rng.normal(size=4 * H) * 0.3 for _ in range(4)]
+    out, hn, cn = orc.lstm_stack_dirs(x, Wi, Wh, bi, bh, dirs=2)
+    o0, hn0, cn0 = orc.lstm_stack_dirs(x, Wi[:2], Wh[:2], bi[:2], bh[:2], dirs=2)
+    o1, hn1, cn1 = orc.lstm_stack_dirs(o0, Wi[2:], Wh[2:], bi[2:], bh[2:], dirs=2)
+    np.testing.assert_allclose(out, o1, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(hn, np.concatenate([hn0, hn1]), rtol=0, atol=1e-13)
+    np.testing.assert_allclose(cn, np.concatenate([cn0, cn1]), rtol=0, atol=1e-13)
 
 
 # ----------------------------------------------------------------------------- backward

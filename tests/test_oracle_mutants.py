@@ -61,6 +61,15 @@ MUTANTS = {
                           "const double* in = (l == 0) ? x + (t * B + bi) * I : h + l * H;"),
     "stack_wh_layer0": ("const double* row = Wh[l] + k * H4;", "const double* row = Wh[0] + k * H4;"),
     "stack_gate_blocks": ("const double gg = tanh(ifgo[2 * H + e]);", "const double gg = tanh(ifgo[3 * H + e]);"),
+    "dirs_reverse_not_reversed": ("const long t = (k == 0) ? s : T - 1 - s;", "const long t = s;"),
+    "dirs_concat_swapped": ("cur[t * W + k * H + e] = h[e];", "cur[t * W + (dirs - 1 - k) * H + e] = h[e];"),
+    "dirs_reverse_uses_forward_weights": ("const long j = l * dirs + k;", "const long j = l * dirs;"),
+    "dirs_next_layer_sees_direction0_only": ("const long K = (l == 0) ? I : W;", "const long K = (l == 0) ? I : H;"),
+    "dirs_hn_direction_major": ("if (hn) hn[(j * B + bi) * H + e] = h[e];", "if (hn) hn[((k * L + l) * B + bi) * H + e] = h[e];"),
+    "dirs_bias_hh_dropped": ("for (long q = 0; q < H4; ++q) ifgo[q] = b_ih[j][q] + b_hh[j][q];",
+                             "for (long q = 0; q < H4; ++q) ifgo[q] = b_ih[j][q];"),
+    "dirs_c_not_carried": ("c[e] = fg * c[e] + ig * gg;\n            h[e] = og * tanh(c[e]);\n            cur",
+                           "c[e] = ig * gg;\n            h[e] = og * tanh(c[e]);\n            cur"),
 }
 
 
