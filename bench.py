@@ -23,8 +23,10 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "LSTM fwd µs/timestep + achieved TFLOP/s (% MFMA bf16 peak), B=16 N=1 D=768"
-PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, at the 2.4 GHz peak engine clock
+PEAK_SCLK_MHZ = 2400.0
 PEAK_HBM_GBS = 8000.0
+WS_RING_BYTES = 512 << 20   # workspaces of the timed calls: each call its own where they fit
 
 
 def headwise_flops(w) -> float:
@@ -137,6 +139,73 @@ def cpu_baseline(w, sample_T: int, backward: bool = False):
             "us_per_timestep": dt / sample_T * 1e6}
 
 
+def measured_copy_gbs(mib: int = 256, reps: int = 10):
+    """Bandwidth of a plain device-to-device copy of `mib` MiB (read + write bytes over the HIP-event
+    time, the best of `reps`): the HBM roof this device reaches with a streaming kernel."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.randn(n, device="cuda:0")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    best = float("inf")
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        best = min(best, e0.elapsed_time(e1))
+    del src, dst
+    return 2.0 * n * 4 / (best / 1e3) / 1e9
+
+
+def engine_clock_under_load(step, seconds: float = 0.3):
+    """The GPU engine clock (MHz) while `step` runs back to back: amd-smi's current graphics clock,
+    sampled every few ms on the host while a queue of calls keeps the device busy (the median of
+    the samples). None when amd-smi's Python module is not usable."""
+    import threading
+
+    import torch
+    try:
+        import amdsmi
+        amdsmi.amdsmi_init()
+        handle = amdsmi.amdsmi_get_processor_handles()[torch.cuda.current_device()]
+        amdsmi.amdsmi_get_clock_info(handle, amdsmi.AmdSmiClkType.GFX)
+    except Exception:
+        return None
+    samples, done = [], threading.Event()
+
+    def sample():
+        while not done.is_set():
+            try:
+                samples.append(float(amdsmi.amdsmi_get_clock_info(handle, amdsmi.AmdSmiClkType.GFX)["clk"]))
+            except Exception:
+                pass
+            time.sleep(0.003)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    step()
+    e1.record()
+    torch.cuda.synchronize()
+    n = max(1, int(seconds / max(e0.elapsed_time(e1) / 1e3, 1e-6)))
+    for _ in range(n):
+        step()
+    th = threading.Thread(target=sample)
+    th.start()
+    torch.cuda.synchronize()
+    done.set()
+    th.join()
+    try:
+        amdsmi.amdsmi_shut_down()
+    except Exception:
+        pass
+    if len(samples) < 3:
+        return None
+    samples.sort()
+    return samples[len(samples) // 2]
+
+
 def calibration_copies(mib: int) -> None:
     """Five plain device-to-device copies of `mib` MiB (the known-size kernel the HBM counters are
     scaled by)."""
@@ -214,6 +283,14 @@ def sweep_designs(spec: str, T: int) -> None:
     clear()
 
 
+def ws_ring(nbytes: int, steps: int, dev):
+    """Workspaces for the timed calls: one per call where they fit in WS_RING_BYTES (each call's
+    error word then survives until it is checked), else as many as fit, at least one."""
+    import torch
+    k = max(1, min(steps, WS_RING_BYTES // max(nbytes, 1)))
+    return [torch.empty(nbytes, dtype=torch.uint8, device=dev) for _ in range(k)]
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -229,6 +306,8 @@ def main():
                     help="only run a plain device copy of MIB MiB (read MIB, write MIB), five times, for "
                          "scaling the HBM byte counters, and exit")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-roofs", action="store_true",
+                    help="skip the engine-clock sample and the copy-bandwidth measurement after the timed region")
     ap.add_argument("--sweep-designs", default="", metavar="CELL,B,N,D",
                     help="time every fused forward design the planner can be pinned to on this head-wise shape "
                          "(bf16, seeded inputs, --sweep-T steps) and print one JSON line per design")
@@ -279,24 +358,24 @@ def main():
     if isinstance(w, fi.HeadwiseWorkload):
         G, S = w.G, w.S
         desc = hw._desc(w.B, w.T, w.N, w.D, w.cell, w.dtype)
-        ws = torch.empty(hw.frnn_workspace_bytes(desc, args.path), dtype=torch.uint8, device=dev)
+        wss = ws_ring(hw.frnn_workspace_bytes(desc, args.path), args.steps, dev)
         out = (torch.empty((S, w.B, w.T, w.N, w.D), dtype=torch.float32, device=dev),
                torch.empty((S, w.B, 1, w.N, w.D), dtype=torch.float32, device=dev))
         plan = hw.frnn_plan_str(desc, args.path)
 
-        def step():
-            hw.frnn_fwd(g["Wx"], g["R"], g["b"], g["states0"], cell=w.cell, path=args.path, out=out, workspace=ws,
-                        check=False)
+        def step(i=0):
+            hw.frnn_fwd(g["Wx"], g["R"], g["b"], g["states0"], cell=w.cell, path=args.path, out=out,
+                        workspace=wss[i % len(wss)], check=False)
         flops = headwise_flops(w)
         if args.backward:
             fwd_st, _ = hw.frnn_fwd(g["Wx"], g["R"], g["b"], g["states0"], cell=w.cell, path="fused")
             ct = {k: v.to(dev) for k, v in fi.backward_cotangents(w).items()}
-            ws = torch.empty(hw.frnn_bwd_workspace_bytes(desc, args.path), dtype=torch.uint8, device=dev)
+            wss = ws_ring(hw.frnn_bwd_workspace_bytes(desc, args.path), args.steps, dev)
             plan = hw.frnn_bwd_plan_str(desc, args.path)
 
-            def step():
+            def step(i=0):
                 hw.frnn_bwd(g["Wx"], g["R"], g["b"], g["states0"], fwd_st, ct["dstates"], ct["dlast"], cell=w.cell,
-                            path=args.path, workspace=ws, check=False)
+                            path=args.path, workspace=wss[i % len(wss)], check=False)
             # the serial contraction (da . R^T per step), the h.R recompute and the dR GEMM
             flops = 2.0 * headwise_flops(w) + 2.0 * (w.D + 1) * w.G * w.D * w.B * w.T * w.N
         elt = 2 if w.dtype == torch.bfloat16 else 4
@@ -307,51 +386,58 @@ def main():
                   "plan": plan, "pass": "backward" if args.backward else "forward"}
         dtype = "bf16" if w.dtype == torch.bfloat16 else "f32"
     else:
-        ws = torch.empty(hw.frnn_lstm_stack_workspace_bytes(w.L, w.T, w.B, w.I, w.H, args.path), dtype=torch.uint8,
-                         device=dev)
-        out = (torch.empty((w.T, w.B, w.H), dtype=torch.float32, device=dev),
-               torch.empty((w.L, w.B, w.H), dtype=torch.float32, device=dev),
-               torch.empty((w.L, w.B, w.H), dtype=torch.float32, device=dev))
+        dirs = getattr(w, "dirs", 1)
+        wss = ws_ring(hw.frnn_lstm_stack_workspace_bytes(w.L, w.T, w.B, w.I, w.H, args.path, dirs), args.steps, dev)
+        out = (torch.empty((w.T, w.B, dirs * w.H), dtype=torch.float32, device=dev),
+               torch.empty((w.L * dirs, w.B, w.H), dtype=torch.float32, device=dev),
+               torch.empty((w.L * dirs, w.B, w.H), dtype=torch.float32, device=dev))
 
-        def step():
+        def step(i=0):
             hw.frnn_lstm_stack_fwd(g["x"], g["Wi"], g["Wh"], g["b_ih"], g["b_hh"], g["h0"], g["c0"], path=args.path,
-                                   out=out, workspace=ws, check=False)
-        flops = 2.0 * w.B * 4 * w.H * w.H * w.T * w.L  # recurrent contraction of all layers
+                                   out=out, workspace=wss[i % len(wss)], check=False, bidirectional=dirs == 2)
+        flops = 2.0 * w.B * 4 * w.H * w.H * w.T * w.L * dirs  # recurrent contraction of all layers and directions
         if args.backward:
             ct = {k: v.to(dev) for k, v in fi.stack_cotangents(w).items()}
-            ws = torch.empty(hw.frnn_lstm_stack_bwd_workspace_bytes(w.L, w.T, w.B, w.I, w.H, args.path),
-                             dtype=torch.uint8, device=dev)
+            wss = ws_ring(hw.frnn_lstm_stack_bwd_workspace_bytes(w.L, w.T, w.B, w.I, w.H, args.path), args.steps, dev)
 
-            def step():
+            def step(i=0):
                 hw.frnn_lstm_stack_bwd(g["x"], g["Wi"], g["Wh"], g["b_ih"], g["b_hh"], g["h0"], g["c0"], ct["dout"],
-                                       ct["dhn"], ct["dcn"], path=args.path, workspace=ws, check=False)
+                                       ct["dhn"], ct["dcn"], path=args.path, workspace=wss[i % len(wss)], check=False)
             # forward again (recurrent contraction) + per layer the serial da.R^T, the h.R recompute
             # and the dR GEMM; the projections' GEMMs (forward, dWi, dX) are reported separately
             flops = 4.0 * flops
         nbytes = 0.0
         timesteps = w.T * w.L
-        config = {"workload": w.name, "L": w.L, "T": w.T, "B": w.B, "I": w.I, "H": w.H, "path": args.path,
-                  "projection_gflop": (3.0 if args.backward else 1.0) * 2.0 * w.T * w.B * 4 * w.H *
-                  (w.I + w.H * (w.L - 1)) / 1e9,
+        config = {"workload": w.name, "L": w.L, "dirs": dirs, "T": w.T, "B": w.B, "I": w.I, "H": w.H, "path": args.path,
+                  "projection_gflop": (3.0 if args.backward else 1.0) * 2.0 * w.T * w.B * 4 * w.H * dirs *
+                  (w.I + dirs * w.H * (w.L - 1)) / 1e9,
                   "pass": "backward" if args.backward else "forward"}
         if args.backward:  # each layer's serial part: the head-wise backward of one head of H units
             config["plan"] = hw.frnn_bwd_plan_str(hw._desc(w.B, w.T, 1, w.H, "lstm", w.dtype), args.path)
         dtype = "bf16"
 
-    for _ in range(args.warmup):
-        step()
-    hw.frnn_check(ws)
+    for i in range(args.warmup):
+        step(i)
+    for ws in wss:
+        hw.frnn_check(ws)
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # one event between consecutive calls: the whole region's time and every call's own
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     t0 = time.perf_counter()
-    e0.record(stream)
-    for _ in range(args.steps):
-        step()
-    e1.record(stream)
+    ev[0].record(stream)
+    for i in range(args.steps):
+        step(i)
+        ev[i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    hw.frnn_check(ws)
-    ms = e0.elapsed_time(e1) / args.steps
+    # each call's device-side error word (a bounded wait that ran out, a workgroup on the wrong die)
+    for ws in wss:
+        hw.frnn_check(ws)
+    ms = ev[0].elapsed_time(ev[-1]) / args.steps
+    per_call = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps))
+    ms_median = per_call[len(per_call) // 2] if len(per_call) % 2 else 0.5 * (per_call[len(per_call) // 2 - 1] +
+                                                                                per_call[len(per_call) // 2])
+    ms_min = per_call[0]
     sec = ms / 1e3
     tflops = flops / sec / 1e12
     roof = {"bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
@@ -361,6 +447,11 @@ def main():
                         "frnn::bwd_gate_kernel+bwd_dh_kernel (+ GEMMs)") if args.backward else
                        "frnn::fused_fwd_kernel" if args.path == "fused" else "frnn::alt_gemm_kernel+alt_gate_kernel"),
             "per_launch_flop": flops, "launch_ms": ms}
+    if not args.no_roofs:
+        clk = engine_clock_under_load(step)
+        roof["engine_clock_mhz"] = clk
+        roof["frac_at_measured_clock"] = None if not clk else tflops / (PEAK_BF16_TFLOPS * clk / PEAK_SCLK_MHZ)
+        roof["measured_copy_gbs"] = measured_copy_gbs()
     if nbytes and not args.backward:
         roof["algorithmic_bytes"] = nbytes
         roof["hbm_frac"] = nbytes / sec / 1e9 / PEAK_HBM_GBS
@@ -384,6 +475,9 @@ def main():
            "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "dtype": dtype, "data": "synthetic (seeded, shapes and distributions of the workload)",
            "config": config, "us_per_timestep": ms * 1e3 / timesteps,
+           "ms_per_call_median": ms_median, "ms_per_call_min": ms_min,
+           "us_per_timestep_median": ms_median * 1e3 / timesteps, "us_per_timestep_min": ms_min * 1e3 / timesteps,
+           "calls_error_checked": min(len(wss), args.steps),
            "pct_mfma_bf16_peak": 100.0 * tflops / PEAK_BF16_TFLOPS, "wall_s_timed": wall, "roofline": roof}
     if not args.no_cpu_baseline and isinstance(w, fi.HeadwiseWorkload):
         res["cpu_baseline"] = cpu_baseline(w, min(args.cpu_sample_T or w.T, w.T), backward=args.backward)

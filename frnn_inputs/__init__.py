@@ -46,7 +46,8 @@ class HeadwiseWorkload:
 
 @dataclass(frozen=True)
 class StackWorkload:
-    """Plain multi-layer LSTM with input projection: x[T,B,I], Wi[in,4H], Wh[H,4H], b_ih, b_hh."""
+    """Plain multi-layer LSTM with input projection and one or two directions per layer: x[T,B,I],
+    per layer and direction Wi[in,4H] (in = I, or dirs*H above layer 0), Wh[H,4H], b_ih, b_hh."""
     name: str
     dtype: torch.dtype
     L: int
@@ -58,6 +59,7 @@ class StackWorkload:
     x_var: float = 1.0
     w_bound: Optional[float] = None    # None -> 1/sqrt(H)
     zero_init: bool = True
+    dirs: int = 1
 
 
 # The five workloads the recurrence is measured and checked on.
@@ -78,6 +80,13 @@ WORKLOADS = {
 }
 
 HEADLINE = "lstm_bf16_B16_T1024_N1_D768"
+
+# The two-layer LSTM workload's shape with both directions per layer (reading A21: the "5.3 LSTM"
+# page's bidirectional flag and reverse weights): torch.nn.LSTM's init bound 1/sqrt(H).
+BIDIR_WORKLOADS = {
+    "lstm2bi_bf16_T512_B32_I512_H512": StackWorkload(
+        "lstm2bi_bf16_T512_B32_I512_H512", torch.bfloat16, L=2, T=512, B=32, I=512, H=512, seed=5, dirs=2),
+}
 
 # The GRU cell (named in the FlashRNN cell list) on the shapes of the LSTM workloads above: the
 # headline shape, the three-head shape with random initial state, and a small fp32 case.
@@ -137,28 +146,33 @@ def stack_cotangents(w: StackWorkload):
 
 
 def stack_inputs(w: StackWorkload):
-    """Return dict(x, Wi[], Wh[], b_ih[], b_hh[], h0, c0) of CPU tensors in ``w.dtype``."""
+    """Return dict(x, Wi[], Wh[], b_ih[], b_hh[], h0, c0) of CPU tensors in ``w.dtype``; the weight
+    lists hold L*dirs entries, layer l direction k at l*dirs + k, drawn in that order."""
     g = torch.Generator(device="cpu")
     g.manual_seed(w.seed)
     bound = (1.0 / math.sqrt(w.H)) if w.w_bound is None else w.w_bound
     x = _normal(g, (w.T, w.B, w.I), w.x_var).to(w.dtype)
     Wi, Wh, bih, bhh = [], [], [], []
     for l in range(w.L):
-        fan_in = w.I if l == 0 else w.H
-        Wi.append(_uniform(g, (fan_in, 4 * w.H), bound).to(w.dtype))
-        Wh.append(_uniform(g, (w.H, 4 * w.H), bound).to(w.dtype))
-        bih.append(_uniform(g, (4 * w.H,), bound).to(w.dtype))
-        bhh.append(_uniform(g, (4 * w.H,), bound).to(w.dtype))
+        for _ in range(w.dirs):
+            fan_in = w.I if l == 0 else w.dirs * w.H
+            Wi.append(_uniform(g, (fan_in, 4 * w.H), bound).to(w.dtype))
+            Wh.append(_uniform(g, (w.H, 4 * w.H), bound).to(w.dtype))
+            bih.append(_uniform(g, (4 * w.H,), bound).to(w.dtype))
+            bhh.append(_uniform(g, (4 * w.H,), bound).to(w.dtype))
     h0 = c0 = None
     if not w.zero_init:
-        h0 = _normal(g, (w.L, w.B, w.H), 1.0).to(w.dtype)
-        c0 = _normal(g, (w.L, w.B, w.H), 1.0).to(w.dtype)
+        h0 = _normal(g, (w.L * w.dirs, w.B, w.H), 1.0).to(w.dtype)
+        c0 = _normal(g, (w.L * w.dirs, w.B, w.H), 1.0).to(w.dtype)
     return {"x": x, "Wi": Wi, "Wh": Wh, "b_ih": bih, "b_hh": bhh, "h0": h0, "c0": c0}
 
 
 def get_workload(name: str):
-    """A named workload from WORKLOADS or GRU_WORKLOADS."""
-    return WORKLOADS[name] if name in WORKLOADS else GRU_WORKLOADS[name]
+    """A named workload from WORKLOADS, GRU_WORKLOADS or BIDIR_WORKLOADS."""
+    for table in (WORKLOADS, GRU_WORKLOADS, BIDIR_WORKLOADS):
+        if name in table:
+            return table[name]
+    raise KeyError(name)
 
 
 def make_inputs(name_or_workload):

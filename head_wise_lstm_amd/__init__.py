@@ -20,6 +20,7 @@ __all__ = [
     "frnn_abi_version", "frnn_status_str", "frnn_workspace_bytes", "frnn_plan_str", "frnn_fwd",
     "frnn_check", "frnn_lstm_stack_workspace_bytes", "frnn_lstm_stack_fwd", "frnn_bwd_workspace_bytes",
     "frnn_bwd_plan_str", "frnn_bwd", "flashrnn", "frnn_lstm_stack_bwd_workspace_bytes", "frnn_lstm_stack_bwd",
+    "frnn_init",
 ]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -43,8 +44,9 @@ class FrnnError(RuntimeError):
 
 
 class Desc(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_int32) for n in
-                ("B", "T", "N", "D", "cell", "in_dtype", "out_dtype", "reserved")]
+    """frnn_desc: sizes, cell, dtypes, then element strides (0 = the dense default)."""
+    _fields_ = ([(n, ctypes.c_int32) for n in ("B", "T", "N", "D", "cell", "in_dtype", "out_dtype", "reserved")]
+                + [(n, ctypes.c_int64) for n in ("wx_sb", "wx_st", "st_ss", "st_sb", "st_st", "r_sg", "r_sn", "r_sd")])
 
 
 _lib = None
@@ -67,6 +69,8 @@ def load():
     dptr = ctypes.POINTER(Desc)
     lib.frnn_abi_version.restype = i32
     lib.frnn_abi_version.argtypes = []
+    lib.frnn_init.restype = i32
+    lib.frnn_init.argtypes = []
     lib.frnn_status_str.restype = ctypes.c_char_p
     lib.frnn_status_str.argtypes = [i32]
     lib.frnn_workspace_bytes.restype = i32
@@ -84,16 +88,16 @@ def load():
     lib.frnn_bwd.restype = i32
     lib.frnn_bwd.argtypes = [dptr, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.frnn_lstm_stack_workspace_bytes.restype = i32
-    lib.frnn_lstm_stack_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, ctypes.POINTER(sz)]
+    lib.frnn_lstm_stack_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32, ctypes.POINTER(sz)]
     lib.frnn_lstm_stack_bwd_workspace_bytes.restype = i32
-    lib.frnn_lstm_stack_bwd_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, ctypes.POINTER(sz)]
+    lib.frnn_lstm_stack_bwd_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32, ctypes.POINTER(sz)]
     lib.frnn_lstm_stack_bwd.restype = i32
-    lib.frnn_lstm_stack_bwd.argtypes = [i32, i32, i32, i32, i32, i32, vp, ctypes.POINTER(vp), ctypes.POINTER(vp),
+    lib.frnn_lstm_stack_bwd.argtypes = [i32, i32, i32, i32, i32, i32, i32, vp, ctypes.POINTER(vp), ctypes.POINTER(vp),
                                         ctypes.POINTER(vp), ctypes.POINTER(vp), vp, vp, vp, vp, vp, vp,
                                         ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.POINTER(vp),
                                         ctypes.POINTER(vp), vp, vp, vp, sz, vp]
     lib.frnn_lstm_stack_fwd.restype = i32
-    lib.frnn_lstm_stack_fwd.argtypes = [i32, i32, i32, i32, i32, i32, vp, ctypes.POINTER(vp), ctypes.POINTER(vp),
+    lib.frnn_lstm_stack_fwd.argtypes = [i32, i32, i32, i32, i32, i32, i32, vp, ctypes.POINTER(vp), ctypes.POINTER(vp),
                                         ctypes.POINTER(vp), ctypes.POINTER(vp), vp, vp, vp, vp, vp, vp, sz, vp]
     _lib = lib
     return lib
@@ -101,6 +105,25 @@ def load():
 
 def frnn_abi_version() -> int:
     return load().frnn_abi_version()
+
+
+_initialised = set()
+
+
+def frnn_init(device=None) -> None:
+    """frnn_init() on ``device`` (default: torch's current device), once per device: the one call
+    that allocates device memory and waits for the device. Every compute wrapper below calls it
+    for its tensors' device before its first call there."""
+    idx = torch.cuda.current_device() if device is None else torch.device(device).index
+    if idx is None:
+        idx = torch.cuda.current_device()
+    if idx in _initialised:
+        return
+    with torch.cuda.device(idx):
+        rc = load().frnn_init()
+    if rc != FRNN_OK:
+        raise FrnnError(rc, "frnn_init")
+    _initialised.add(idx)
 
 
 def frnn_status_str(status: int) -> str:
@@ -148,15 +171,35 @@ def frnn_check(workspace: torch.Tensor, stream=None) -> None:
         raise FrnnError(rc, "frnn_check")
 
 
-def _check_tensor(t, name, shape, dtype, device):
+def _check_tensor(t, name, shape, dtype, device, dense_inner=None):
+    """Check device, dtype and shape. Without ``dense_inner`` the tensor must be contiguous; with
+    it, only its last ``dense_inner`` dimensions must be dense, and its strides are returned."""
     if t is None:
-        return
+        return None
     if not isinstance(t, torch.Tensor) or t.device != device or t.dtype != dtype:
         raise ValueError(f"{name}: expected a {dtype} tensor on {device}")
     if tuple(t.shape) != tuple(shape):
         raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
-    if not t.is_contiguous():
-        raise ValueError(f"{name}: must be contiguous")
+    if dense_inner is None:
+        if not t.is_contiguous():
+            raise ValueError(f"{name}: must be contiguous")
+        return None
+    st, expect = t.stride(), 1
+    for k in range(t.dim() - 1, t.dim() - 1 - dense_inner, -1):
+        if t.shape[k] > 1 and st[k] != expect:
+            raise ValueError(f"{name}: its last {dense_inner} dimensions must be dense")
+        expect *= t.shape[k]
+    return st
+
+
+def _set_strides(desc: Desc, wx=None, st=None, r=None) -> None:
+    """Element strides of strided views into the description (None keeps the dense default)."""
+    if wx is not None:
+        desc.wx_sb, desc.wx_st = wx[0], wx[1]
+    if st is not None:
+        desc.st_ss, desc.st_sb, desc.st_st = st[0], st[1], st[2]
+    if r is not None:
+        desc.r_sg, desc.r_sn, desc.r_sd = r[0], r[1], r[2]
 
 
 def frnn_fwd(Wx: torch.Tensor, R: torch.Tensor, b: Optional[torch.Tensor] = None,
@@ -179,8 +222,8 @@ def frnn_fwd(Wx: torch.Tensor, R: torch.Tensor, b: Optional[torch.Tensor] = None
     dev, dt = Wx.device, Wx.dtype
     if G_ != G or dt not in _DTYPES:
         raise ValueError("Wx: wrong gate count or dtype")
-    _check_tensor(Wx, "Wx", (B, T, G, N, D), dt, dev)
-    _check_tensor(R, "R", (G, N, D, D), dt, dev)
+    wx_st = _check_tensor(Wx, "Wx", (B, T, G, N, D), dt, dev, dense_inner=3)
+    r_st = _check_tensor(R, "R", (G, N, D, D), dt, dev, dense_inner=1)
     _check_tensor(b, "b", (G, N, D), dt, dev)
     _check_tensor(states, "states", (S, B, 1, N, D), dt, dev)
     desc = _desc(B, T, N, D, cell, dt)
@@ -190,13 +233,15 @@ def frnn_fwd(Wx: torch.Tensor, R: torch.Tensor, b: Optional[torch.Tensor] = None
         last = torch.empty((S, B, 1, N, D), dtype=torch.float32, device=dev)
     else:
         st_out, last = out
-        _check_tensor(st_out, "out[0]", (S, B, T, N, D), torch.float32, dev)
         _check_tensor(last, "out[1]", (S, B, 1, N, D), torch.float32, dev)
+    st_st = _check_tensor(st_out, "out[0]", (S, B, T, N, D), torch.float32, dev, dense_inner=2)
+    _set_strides(desc, wx_st, st_st, r_st)
     need = frnn_workspace_bytes(desc, p)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     elif workspace.numel() < need or workspace.device != dev:
         raise ValueError("workspace too small")
+    frnn_init(dev)
     rc = load().frnn_fwd(ctypes.byref(desc), p, _ptr(Wx), _ptr(R), _ptr(b), _ptr(states), _ptr(st_out),
                          _ptr(last), _ptr(workspace), workspace.numel(), _stream_handle(dev))
     if rc != FRNN_OK:
@@ -237,17 +282,25 @@ def frnn_bwd(Wx: torch.Tensor, R: torch.Tensor, b: Optional[torch.Tensor], state
     dev, dt = Wx.device, Wx.dtype
     if G_ != G or dt not in _DTYPES:
         raise ValueError("Wx: wrong gate count or dtype")
-    _check_tensor(R, "R", (G, N, D, D), dt, dev)
+    wx_st = _check_tensor(Wx, "Wx", (B, T, G, N, D), dt, dev, dense_inner=3)
+    r_st = _check_tensor(R, "R", (G, N, D, D), dt, dev, dense_inner=1)
     _check_tensor(b, "b", (G, N, D), dt, dev)
     _check_tensor(states0, "states0", (S, B, 1, N, D), dt, dev)
-    _check_tensor(states, "states", (S, B, T, N, D), torch.float32, dev)
-    _check_tensor(dstates, "dstates", (S, B, T, N, D), torch.float32, dev)
+    st_st = _check_tensor(states, "states", (S, B, T, N, D), torch.float32, dev, dense_inner=2)
+    if dstates is not None and dstates.stride() != states.stride():
+        # dstates is read with the states' strides
+        ds = torch.empty_strided(states.shape, states.stride(), dtype=torch.float32, device=dev)
+        ds.copy_(dstates)
+        dstates = ds
+    _check_tensor(dstates, "dstates", (S, B, T, N, D), torch.float32, dev, dense_inner=2)
     _check_tensor(dlast, "dlast", (S, B, 1, N, D), torch.float32, dev)
     desc = _desc(B, T, N, D, cell, dt)
+    _set_strides(desc, wx_st, st_st, r_st)
     p = _path(path)
     f = torch.float32
-    dWx = torch.empty((B, T, G, N, D), dtype=f, device=dev)
-    dR = torch.empty((G, N, D, D), dtype=f, device=dev)
+    # dWx and dR take the layouts (strides) of Wx and R
+    dWx = torch.empty_strided((B, T, G, N, D), Wx.stride(), dtype=f, device=dev)
+    dR = torch.empty_strided((G, N, D, D), R.stride(), dtype=f, device=dev)
     db = torch.empty((G, N, D), dtype=f, device=dev)
     ds0 = torch.empty((S, B, 1, N, D), dtype=f, device=dev)
     need = frnn_bwd_workspace_bytes(desc, p)
@@ -255,6 +308,7 @@ def frnn_bwd(Wx: torch.Tensor, R: torch.Tensor, b: Optional[torch.Tensor], state
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     elif workspace.numel() < need or workspace.device != dev:
         raise ValueError("workspace too small")
+    frnn_init(dev)
     rc = load().frnn_bwd(ctypes.byref(desc), p, _ptr(Wx), _ptr(R), _ptr(b), _ptr(states0), _ptr(states),
                          _ptr(dstates), _ptr(dlast), _ptr(dWx), _ptr(dR), _ptr(db), _ptr(ds0), _ptr(workspace),
                          workspace.numel(), _stream_handle(dev))
@@ -267,10 +321,10 @@ def frnn_bwd(Wx: torch.Tensor, R: torch.Tensor, b: Optional[torch.Tensor], state
 
 class _FlashRNNFunction(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, Wx, R, b, states0, cell, path, bwd_path):
-        states, last = frnn_fwd(Wx, R, b, states0, cell=cell, path=path)
+    def forward(ctx, Wx, R, b, states0, cell, path, bwd_path, check):
+        states, last = frnn_fwd(Wx, R, b, states0, cell=cell, path=path, check=check)
         ctx.save_for_backward(Wx, R, b, states0, states)
-        ctx.cell, ctx.bwd_path = cell, bwd_path
+        ctx.cell, ctx.bwd_path, ctx.check = cell, bwd_path, check
         return states, last
 
     @staticmethod
@@ -278,17 +332,20 @@ class _FlashRNNFunction(torch.autograd.Function):
         Wx, R, b, states0, states = ctx.saved_tensors
         c = lambda t: None if t is None else t.float().contiguous()
         dWx, dR, db, ds0 = frnn_bwd(Wx, R, b, states0, states, c(dstates), c(dlast), cell=ctx.cell,
-                                    path=ctx.bwd_path)
+                                    path=ctx.bwd_path, check=ctx.check)
         cast = lambda g, like: None if like is None else g.to(like.dtype)
-        return cast(dWx, Wx), cast(dR, R), cast(db, b), cast(ds0, states0), None, None, None
+        return cast(dWx, Wx), cast(dR, R), cast(db, b), cast(ds0, states0), None, None, None, None
 
 
 def flashrnn(Wx: torch.Tensor, R: torch.Tensor, b: Optional[torch.Tensor] = None,
-             states: Optional[torch.Tensor] = None, cell: str = "lstm", path="fused", bwd_path=None):
+             states: Optional[torch.Tensor] = None, cell: str = "lstm", path="fused", bwd_path=None,
+             check: bool = False):
     """Differentiable head-wise forward (the FlashRNN page's functional call): returns (states,
     last_states) like frnn_fwd; torch autograd runs frnn_bwd for the gradients of Wx, R, b and the
     initial states (cast to their dtypes). bwd_path None: the fused backward where this build has
-    a design for the shape and dtype, else the alternating one (both are HIP paths)."""
+    a design for the shape and dtype, else the alternating one (both are HIP paths). Neither pass
+    waits for the stream unless ``check`` is set (then each waits and raises on a device-side
+    error, as frnn_check does)."""
     if bwd_path is None:
         B, T, _, N, D = Wx.shape
         try:
@@ -298,12 +355,12 @@ def flashrnn(Wx: torch.Tensor, R: torch.Tensor, b: Optional[torch.Tensor] = None
             if e.status != -2:
                 raise
             bwd_path = "alternating"
-    return _FlashRNNFunction.apply(Wx, R, b, states, cell, path, bwd_path)
+    return _FlashRNNFunction.apply(Wx, R, b, states, cell, path, bwd_path, check)
 
 
-def frnn_lstm_stack_workspace_bytes(L, T, B, I, H, path="fused") -> int:
+def frnn_lstm_stack_workspace_bytes(L, T, B, I, H, path="fused", dirs: int = 1) -> int:
     n = ctypes.c_size_t(0)
-    rc = load().frnn_lstm_stack_workspace_bytes(L, T, B, I, H, _path(path), ctypes.byref(n))
+    rc = load().frnn_lstm_stack_workspace_bytes(L, dirs, T, B, I, H, _path(path), ctypes.byref(n))
     if rc != FRNN_OK:
         raise FrnnError(rc, "frnn_lstm_stack_workspace_bytes")
     return n.value
@@ -313,40 +370,49 @@ def frnn_lstm_stack_fwd(x: torch.Tensor, Wi: Sequence[torch.Tensor], Wh: Sequenc
                         b_ih: Sequence[Optional[torch.Tensor]], b_hh: Sequence[Optional[torch.Tensor]],
                         h0: Optional[torch.Tensor] = None, c0: Optional[torch.Tensor] = None, path="fused",
                         out: Optional[Sequence[torch.Tensor]] = None, workspace: Optional[torch.Tensor] = None,
-                        check: bool = True):
-    """Multi-layer LSTM with input projection: (out [T,B,H], hn [L,B,H], cn [L,B,H]), fp32.
+                        check: bool = True, bidirectional: bool = False):
+    """Multi-layer LSTM with input projection: (out [T,B,dirs*H], hn [L*dirs,B,H], cn [L*dirs,B,H]), fp32.
 
-    x [T,B,I]; Wi[l] [in,4H]; Wh[l] [H,4H]; b_ih[l], b_hh[l] [4H] or None; h0, c0 [L,B,H] or None;
-    every tensor bfloat16 on one device.
+    x [T,B,I]; per layer l and direction k (index l*dirs + k, dirs = 2 when ``bidirectional``):
+    Wi [in,4H] (in = I for l = 0, else dirs*H); Wh [H,4H]; b_ih, b_hh [4H] or None; h0, c0
+    [L*dirs,B,H] or None; every tensor bfloat16 on one device. Direction 1 runs the sequence
+    backwards; a layer's output is [h of direction 0, h of direction 1] at each step.
     """
     T, B, I = x.shape
-    L = len(Wi)
+    dirs = 2 if bidirectional else 1
+    if len(Wi) % dirs or len(Wh) != len(Wi) or len(b_ih) != len(Wi) or len(b_hh) != len(Wi):
+        raise ValueError("one Wi, Wh, b_ih and b_hh per layer and direction")
+    L = len(Wi) // dirs
     H = Wh[0].shape[0]
     dev, bf = x.device, torch.bfloat16
     _check_tensor(x, "x", (T, B, I), bf, dev)
-    for l in range(L):
-        _check_tensor(Wi[l], f"Wi[{l}]", ((I if l == 0 else H), 4 * H), bf, dev)
-        _check_tensor(Wh[l], f"Wh[{l}]", (H, 4 * H), bf, dev)
-        _check_tensor(b_ih[l], f"b_ih[{l}]", (4 * H,), bf, dev)
-        _check_tensor(b_hh[l], f"b_hh[{l}]", (4 * H,), bf, dev)
-    _check_tensor(h0, "h0", (L, B, H), bf, dev)
-    _check_tensor(c0, "c0", (L, B, H), bf, dev)
+    for j in range(L * dirs):
+        _check_tensor(Wi[j], f"Wi[{j}]", ((I if j < dirs else dirs * H), 4 * H), bf, dev)
+        _check_tensor(Wh[j], f"Wh[{j}]", (H, 4 * H), bf, dev)
+        _check_tensor(b_ih[j], f"b_ih[{j}]", (4 * H,), bf, dev)
+        _check_tensor(b_hh[j], f"b_hh[{j}]", (4 * H,), bf, dev)
+    _check_tensor(h0, "h0", (L * dirs, B, H), bf, dev)
+    _check_tensor(c0, "c0", (L * dirs, B, H), bf, dev)
     p = _path(path)
     if out is None:
-        o = torch.empty((T, B, H), dtype=torch.float32, device=dev)
-        hn = torch.empty((L, B, H), dtype=torch.float32, device=dev)
-        cn = torch.empty((L, B, H), dtype=torch.float32, device=dev)
+        o = torch.empty((T, B, dirs * H), dtype=torch.float32, device=dev)
+        hn = torch.empty((L * dirs, B, H), dtype=torch.float32, device=dev)
+        cn = torch.empty((L * dirs, B, H), dtype=torch.float32, device=dev)
     else:
         o, hn, cn = out
-    need = frnn_lstm_stack_workspace_bytes(L, T, B, I, H, p)
+        _check_tensor(o, "out[0]", (T, B, dirs * H), torch.float32, dev)
+        _check_tensor(hn, "out[1]", (L * dirs, B, H), torch.float32, dev)
+        _check_tensor(cn, "out[2]", (L * dirs, B, H), torch.float32, dev)
+    need = frnn_lstm_stack_workspace_bytes(L, T, B, I, H, p, dirs)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     elif workspace.numel() < need:
         raise ValueError("workspace too small")
-    arr = ctypes.c_void_p * L
+    frnn_init(dev)
+    arr = ctypes.c_void_p * (L * dirs)
+    ptrs = lambda ts: arr(*[0 if t is None else t.data_ptr() for t in ts])
     rc = load().frnn_lstm_stack_fwd(
-        L, T, B, I, H, p, _ptr(x), arr(*[w.data_ptr() for w in Wi]), arr(*[w.data_ptr() for w in Wh]),
-        arr(*[0 if v is None else v.data_ptr() for v in b_ih]), arr(*[0 if v is None else v.data_ptr() for v in b_hh]),
+        L, dirs, T, B, I, H, p, _ptr(x), ptrs(Wi), ptrs(Wh), ptrs(b_ih), ptrs(b_hh),
         _ptr(h0), _ptr(c0), _ptr(o), _ptr(hn), _ptr(cn), _ptr(workspace), workspace.numel(), _stream_handle(dev))
     if rc != FRNN_OK:
         raise FrnnError(rc, "frnn_lstm_stack_fwd")
@@ -355,9 +421,9 @@ def frnn_lstm_stack_fwd(x: torch.Tensor, Wi: Sequence[torch.Tensor], Wh: Sequenc
     return o, hn, cn
 
 
-def frnn_lstm_stack_bwd_workspace_bytes(L, T, B, I, H, path="fused") -> int:
+def frnn_lstm_stack_bwd_workspace_bytes(L, T, B, I, H, path="fused", dirs: int = 1) -> int:
     n = ctypes.c_size_t(0)
-    rc = load().frnn_lstm_stack_bwd_workspace_bytes(L, T, B, I, H, _path(path), ctypes.byref(n))
+    rc = load().frnn_lstm_stack_bwd_workspace_bytes(L, dirs, T, B, I, H, _path(path), ctypes.byref(n))
     if rc != FRNN_OK:
         raise FrnnError(rc, "frnn_lstm_stack_bwd_workspace_bytes")
     return n.value
@@ -399,10 +465,11 @@ def frnn_lstm_stack_bwd(x: torch.Tensor, Wi: Sequence[torch.Tensor], Wh: Sequenc
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     elif workspace.numel() < need:
         raise ValueError("workspace too small")
+    frnn_init(dev)
     arr = ctypes.c_void_p * L
     ptrs = lambda ts: arr(*[0 if t is None else t.data_ptr() for t in ts])
     rc = load().frnn_lstm_stack_bwd(
-        L, T, B, I, H, p, _ptr(x), ptrs(Wi), ptrs(Wh), ptrs(b_ih), ptrs(b_hh), _ptr(h0), _ptr(c0), _ptr(dout),
+        L, 1, T, B, I, H, p, _ptr(x), ptrs(Wi), ptrs(Wh), ptrs(b_ih), ptrs(b_hh), _ptr(h0), _ptr(c0), _ptr(dout),
         _ptr(dhn), _ptr(dcn), _ptr(dx), ptrs(dWi), ptrs(dWh), ptrs(dbi), ptrs(dbh), _ptr(dh0), _ptr(dc0),
         _ptr(workspace), workspace.numel(), _stream_handle(dev))
     if rc != FRNN_OK:

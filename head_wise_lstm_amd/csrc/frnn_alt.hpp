@@ -23,13 +23,14 @@ struct AltArgs {
   const void* s0_h;
   const void* s0_c;
   int s0_f32;
-  long long s0_sb;
+  long long s0_sb, s0_sn;  // element strides of the initial states for b and n
   float* out_h;
   float* out_c;
   long long out_sb, out_st;
   float* last_h;
   float* last_c;
-  long long last_sb;
+  long long last_sb, last_sn;
+  int rev_n0;  // heads n >= rev_n0 run backwards in time: step t reads Wx and writes states at T-1-t
   void* rpack;    // packed R fragments: [N][TPH][KT][64][8 bf16] or [N][TPH][KT][64] fp32
   float* rh;      // h.R per step: LSTM, GRU [B][N][D][4]; Elman [B][N][D]
   void* hcur;     // current h, MFMA operand type: [N][B][D]
@@ -45,7 +46,7 @@ __global__ void __launch_bounds__(256) alt_init_kernel(AltArgs a) {
     const long long r = idx / a.D;
     const int n = (int)(r % a.N);
     const int b = (int)(r / a.N);
-    const long long s = (long long)b * a.s0_sb + (long long)n * a.D + d;
+    const long long s = (long long)b * a.s0_sb + (long long)n * a.s0_sn + d;
     const float h = a.s0_h ? ld_f(a.s0_h, s, a.s0_f32) : 0.0f;
     const float c = a.cell == CELL_GRU ? h : a.s0_c ? ld_f(a.s0_c, s, a.s0_f32) : 0.0f;
     const long long hi = ((long long)n * a.B + b) * a.D + d;
@@ -128,8 +129,9 @@ __global__ void __launch_bounds__(256) alt_gate_kernel(AltArgs a, int t) {
   const int n = (int)(r % a.N);
   const long long b = r / a.N;
   const int N = a.N, D = a.D;
-  const long long wbase = b * a.wx_sb + (long long)t * a.wx_st;
-  const long long o = b * a.out_sb + (long long)t * a.out_st + (long long)n * D + u;
+  const int tt = n >= a.rev_n0 ? a.T - 1 - t : t;  // the head's time direction
+  const long long wbase = b * a.wx_sb + (long long)tt * a.wx_st;
+  const long long o = b * a.out_sb + (long long)tt * a.out_st + (long long)n * D + u;
   const bool rf = a.r_is_f32;
   float h, c = 0.0f;
   if (a.cell == CELL_LSTM) {
@@ -166,7 +168,7 @@ __global__ void __launch_bounds__(256) alt_gate_kernel(AltArgs a, int t) {
   if (a.out_h) a.out_h[o] = h;
   if (a.out_c && a.cell == CELL_LSTM) a.out_c[o] = c;
   if (t == a.T - 1) {
-    const long long lo = b * a.last_sb + (long long)n * D + u;
+    const long long lo = b * a.last_sb + (long long)n * a.last_sn + u;
     if (a.last_h) a.last_h[lo] = h;
     if (a.last_c && a.cell == CELL_LSTM) a.last_c[lo] = c;
   }

@@ -34,6 +34,25 @@ __global__ void __launch_bounds__(256) copy_init_kernel(const void* s0, int s0_f
     dst[i] = s0 ? ld_f(s0, i, s0_f32) : 0.0f;
 }
 
+// Both biases of a bidirectional layer in the projection's column order [gate][direction][unit]:
+// out[j] from b_ih, out[4*dirs*H + j] from b_hh (bf16, a NULL bias reads as zeros).
+struct StackBiasArgs {
+  int H, dirs;
+  const uint16_t* bi[2];
+  const uint16_t* bh[2];
+  uint16_t* out;
+};
+
+__global__ void __launch_bounds__(256) stack_bias_kernel(StackBiasArgs a) {
+  const int G4 = 4 * a.H * a.dirs;
+  const int j = blockIdx.x * 256 + threadIdx.x;
+  if (j >= G4) return;
+  const int g = j / (a.dirs * a.H), r = j - g * a.dirs * a.H, n = r / a.H, e = r - n * a.H;
+  const int src = g * a.H + e;
+  a.out[j] = a.bi[n] ? a.bi[n][src] : (uint16_t)0;
+  a.out[G4 + j] = a.bh[n] ? a.bh[n][src] : (uint16_t)0;
+}
+
 // Records the hardware die id of each workgroup (used once to learn the dispatch pattern).
 __global__ void xcc_map_kernel(int* out) {
   if (threadIdx.x == 0) out[blockIdx.x] = xcc_id();
@@ -58,42 +77,58 @@ struct DevInfo {
 std::mutex g_dev_mu;
 std::vector<DevInfo> g_dev;
 
-int get_devinfo(DevInfo* out) {
+int raise_lds_limits();
+
+// Learns the facts of the current device once (frnn_init): its architecture, CU count and wall
+// clock, and how workgroups are dealt to dies: a grid of one workgroup per CU records the die id
+// of each. The fused designs need the pattern to be periodic in the workgroup index.
+int init_device() {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return FRNN_ENODEVICE;
   std::lock_guard<std::mutex> lk(g_dev_mu);
   if ((int)g_dev.size() <= dev) g_dev.resize(dev + 1);
   DevInfo& di = g_dev[dev];
-  if (!di.ok) {
-    hipDeviceProp_t p;
-    if (hipGetDeviceProperties(&p, dev) != hipSuccess) return FRNN_ENODEVICE;
-    if (std::strncmp(p.gcnArchName, "gfx950", 6) != 0) return FRNN_ENODEVICE;
-    di.device = dev;
-    di.cus = p.multiProcessorCount;
-    int khz = 0;
-    if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) == hipSuccess && khz > 0) di.wall_khz = khz;
-    // Learn how workgroups are dealt to dies: run a grid of one workgroup per CU and read the
-    // die id of each. The fused design needs the pattern to be periodic in the workgroup index.
-    di.n_xcd = std::max(1, std::min(kMaxDies, di.cus / 32));
-    const int nb = di.cus;
-    int* d_map = nullptr;
-    std::vector<int> map(nb, -1);
-    if (hipMalloc(&d_map, sizeof(int) * nb) != hipSuccess) return FRNN_EHIP;
-    hipLaunchKernelGGL(xcc_map_kernel, dim3(nb), dim3(64), 0, 0, d_map);
-    hipError_t e = hipDeviceSynchronize();
-    if (e == hipSuccess) e = hipMemcpy(map.data(), d_map, sizeof(int) * nb, hipMemcpyDeviceToHost);
-    (void)hipFree(d_map);
-    if (e != hipSuccess) return FRNN_EHIP;
-    di.periodic = true;
-    for (int d = 0; d < di.n_xcd; ++d) di.xcc_of[d] = map[d];
-    for (int b = 0; b < nb; ++b)
-      if (map[b] != map[b % di.n_xcd]) di.periodic = false;
-    for (int d = 0; d < di.n_xcd; ++d)
-      for (int d2 = 0; d2 < d; ++d2)
-        if (di.xcc_of[d] == di.xcc_of[d2]) di.periodic = false;
-    di.ok = true;
-  }
-  *out = di;
+  if (di.ok) return FRNN_OK;
+  hipDeviceProp_t p;
+  if (hipGetDeviceProperties(&p, dev) != hipSuccess) return FRNN_ENODEVICE;
+  if (std::strncmp(p.gcnArchName, "gfx950", 6) != 0) return FRNN_ENODEVICE;
+  DevInfo nd;
+  nd.device = dev;
+  nd.cus = p.multiProcessorCount;
+  int khz = 0;
+  if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) == hipSuccess && khz > 0) nd.wall_khz = khz;
+  nd.n_xcd = std::max(1, std::min(kMaxDies, nd.cus / 32));
+  const int nb = nd.cus;
+  int* d_map = nullptr;
+  std::vector<int> map(nb, -1);
+  if (hipMalloc(&d_map, sizeof(int) * nb) != hipSuccess) return FRNN_EHIP;
+  hipLaunchKernelGGL(xcc_map_kernel, dim3(nb), dim3(64), 0, 0, d_map);
+  hipError_t e = hipDeviceSynchronize();
+  if (e == hipSuccess) e = hipMemcpy(map.data(), d_map, sizeof(int) * nb, hipMemcpyDeviceToHost);
+  (void)hipFree(d_map);
+  if (e != hipSuccess) return FRNN_EHIP;
+  nd.periodic = true;
+  for (int d = 0; d < nd.n_xcd; ++d) nd.xcc_of[d] = map[d];
+  for (int b = 0; b < nb; ++b)
+    if (map[b] != map[b % nd.n_xcd]) nd.periodic = false;
+  for (int d = 0; d < nd.n_xcd; ++d)
+    for (int d2 = 0; d2 < d; ++d2)
+      if (nd.xcc_of[d] == nd.xcc_of[d2]) nd.periodic = false;
+  const int rc = raise_lds_limits();
+  if (rc != FRNN_OK) return rc;
+  nd.ok = true;
+  di = nd;
+  return FRNN_OK;
+}
+
+// The facts frnn_init() learned for the current device (a host-side lookup: no device call
+// beyond asking which device is current).
+int get_devinfo(DevInfo* out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return FRNN_ENODEVICE;
+  std::lock_guard<std::mutex> lk(g_dev_mu);
+  if ((int)g_dev.size() <= dev || !g_dev[dev].ok) return FRNN_ENOINIT;
+  *out = g_dev[dev];
   return FRNN_OK;
 }
 
@@ -135,6 +170,43 @@ const FusedBwdxVariant* find_fused_bwdx(int cell, int ncw, int mtw, int ktw) {
   return nullptr;
 }
 
+// Raises the dynamic-LDS limit of every persistent kernel to what its design uses (frnn_init), so
+// that a compute call makes no attribute call. A design's head width is fixed by its k-tiles, so
+// its LDS is known here exactly as the planner computes it.
+constexpr int kMaxLds = 160 * 1024;
+
+int raise_lds_limits() {
+  auto raise = [](const void* fn, int bytes) {
+    if (bytes <= 48 * 1024) return true;
+    return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, std::min(bytes, kMaxLds)) == hipSuccess;
+  };
+  for (const FusedTable& t : {fused_table_lstm(), fused_table_elman(), fused_table_gru()}) {
+    for (int i = 0; i < t.n; ++i) {
+      const FusedVariant& v = t.v[i];
+      const int D = v.ks * v.ktw * (v.f32 ? 4 : 32);
+      if (!raise(reinterpret_cast<const void*>(v.fn), fused_lds(v.local, v.f32, v.ncw, v.ks, v.mtw, D, v.cell).total))
+        return FRNN_EHIP;
+    }
+  }
+  for (const FusedBwdTable& t : {fused_bwd_table_lstm(), fused_bwd_table_elman(), fused_bwd_table_gru()}) {
+    for (int i = 0; i < t.n; ++i) {
+      const FusedBwdVariant& v = t.v[i];
+      const int U = (v.ncw / v.ks) * v.mtw * 16;
+      if (!raise(reinterpret_cast<const void*>(v.fn), fused_bwd_lds(v.ncw, v.ks, v.ktw, FUSED_DIE_MAX_BR, U).total))
+        return FRNN_EHIP;
+    }
+  }
+  for (const FusedBwdxTable& t : {fused_bwdx_table_lstm(), fused_bwdx_table_elman(), fused_bwdx_table_gru()}) {
+    for (int i = 0; i < t.n; ++i) {
+      const FusedBwdxVariant& v = t.v[i];
+      const int UW = v.ktw * 32 / cell_gates(v.cell);
+      if (!raise(reinterpret_cast<const void*>(v.fn), fused_bwdx_lds(v.ktw, FUSED_DIE_MAX_BR, UW).total))
+        return FRNN_EHIP;
+    }
+  }
+  return FRNN_OK;
+}
+
 // ----------------------------------------------------------------------------- problem
 struct Problem {
   int B, T, N, D, cell;
@@ -148,13 +220,14 @@ struct Problem {
   const void* s0_h;
   const void* s0_c;
   int s0_f32;
-  long long s0_sb;
+  long long s0_sb, s0_sn;
   float* out_h;
   float* out_c;
   long long out_sb, out_st;
   float* last_h;
   float* last_c;
-  long long last_sb;
+  long long last_sb, last_sn;
+  int rev_n0;  // heads n >= rev_n0 run backwards in time (N: none)
 };
 
 // Gates stored in Wx, R and b; rows per unit in a tile of packed R^T (see cell_slots).
@@ -441,9 +514,6 @@ int run_recurrence(const Problem& p, int path, int* err, void* scratch, hipStrea
     char* xw = base + rbytes;
     if (!p.r_f32 && launch_rpack(p, base, st) != hipSuccess) return FRNN_EHIP;
     const void* fn = reinterpret_cast<const void*>(fp.v->fn);
-    if (fp.lds > 48 * 1024) {
-      if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)fp.lds) != hipSuccess) return FRNN_EHIP;
-    }
     const size_t wx_elt = p.wx_f32 ? 4 : 2, s0_elt = p.s0_f32 ? 4 : 2;
     // the batch in chunks of at most Bc rows, one launch each (rows never interact)
     for (int b0 = 0; b0 < p.B; b0 += fp.Bc) {
@@ -462,26 +532,24 @@ int run_recurrence(const Problem& p, int path, int* err, void* scratch, hipStrea
       a.check_xcc = fp.local ? 0 : 1;
       a.xcc_of = 0;
       for (int d = 0; d < kMaxDies; ++d) a.xcc_of |= (uint32_t)(di.xcc_of[d] & 0xF) << (4 * d);
-      a.Wx = reinterpret_cast<const char*>(p.Wx) + (size_t)b0 * p.wx_sb * wx_elt;
+      a.Wx = reinterpret_cast<const char*>(p.Wx) + (long long)b0 * p.wx_sb * (long long)wx_elt;
       a.wx_f32 = p.wx_f32; a.wx_sb = p.wx_sb; a.wx_st = p.wx_st;
       a.R = p.R; a.r_sg = p.r_sg; a.r_sn = p.r_sn; a.r_sd = p.r_sd; a.bias = p.bias;
-      a.s0_h = p.s0_h ? reinterpret_cast<const char*>(p.s0_h) + (size_t)b0 * p.s0_sb * s0_elt : nullptr;
-      a.s0_c = p.s0_c ? reinterpret_cast<const char*>(p.s0_c) + (size_t)b0 * p.s0_sb * s0_elt : nullptr;
-      a.s0_f32 = p.s0_f32; a.s0_sb = p.s0_sb;
-      a.out_h = p.out_h ? p.out_h + (size_t)b0 * p.out_sb : nullptr;
-      a.out_c = p.out_c ? p.out_c + (size_t)b0 * p.out_sb : nullptr;
+      a.s0_h = p.s0_h ? reinterpret_cast<const char*>(p.s0_h) + (long long)b0 * p.s0_sb * (long long)s0_elt : nullptr;
+      a.s0_c = p.s0_c ? reinterpret_cast<const char*>(p.s0_c) + (long long)b0 * p.s0_sb * (long long)s0_elt : nullptr;
+      a.s0_f32 = p.s0_f32; a.s0_sb = p.s0_sb; a.s0_sn = p.s0_sn;
+      a.out_h = p.out_h ? p.out_h + (long long)b0 * p.out_sb : nullptr;
+      a.out_c = p.out_c ? p.out_c + (long long)b0 * p.out_sb : nullptr;
       a.out_sb = p.out_sb; a.out_st = p.out_st;
-      a.last_h = p.last_h ? p.last_h + (size_t)b0 * p.last_sb : nullptr;
-      a.last_c = p.last_c ? p.last_c + (size_t)b0 * p.last_sb : nullptr;
-      a.last_sb = p.last_sb;
+      a.last_h = p.last_h ? p.last_h + (long long)b0 * p.last_sb : nullptr;
+      a.last_c = p.last_c ? p.last_c + (long long)b0 * p.last_sb : nullptr;
+      a.last_sb = p.last_sb; a.last_sn = p.last_sn;
+      a.rev_n0 = p.rev_n0;
       a.rpack = base;
       a.xbuf = reinterpret_cast<uint32_t*>(xw);
       a.err = err;
       a.timeout_ticks = (long long)env_int("FRNN_TIMEOUT_MS", 2000) * di.wall_khz;
-#ifdef FRNN_PHASE_TRACE
-      if (const char* tp = std::getenv("FRNN_TRACE_PTR")) a.trace = reinterpret_cast<long long*>(std::strtoull(tp, nullptr, 0));
-      a.trace_slots = env_int("FRNN_TRACE_SLOTS", 0);  // no slot, no trace store
-#endif
+      a.stall_step = env_int("FRNN_TEST_STALL_STEP", -1);
       void* args[] = {&a};
       hipError_t e;
       if (fp.local) {
@@ -503,9 +571,10 @@ int run_recurrence(const Problem& p, int path, int* err, void* scratch, hipStrea
   a.B = p.B; a.T = p.T; a.N = p.N; a.D = p.D; a.cell = p.cell; a.r_is_f32 = p.r_f32;
   a.Wx = p.Wx; a.wx_f32 = p.wx_f32; a.wx_sb = p.wx_sb; a.wx_st = p.wx_st;
   a.R = p.R; a.r_sg = p.r_sg; a.r_sn = p.r_sn; a.r_sd = p.r_sd; a.bias = p.bias;
-  a.s0_h = p.s0_h; a.s0_c = p.s0_c; a.s0_f32 = p.s0_f32; a.s0_sb = p.s0_sb;
+  a.s0_h = p.s0_h; a.s0_c = p.s0_c; a.s0_f32 = p.s0_f32; a.s0_sb = p.s0_sb; a.s0_sn = p.s0_sn;
   a.out_h = p.out_h; a.out_c = p.out_c; a.out_sb = p.out_sb; a.out_st = p.out_st;
-  a.last_h = p.last_h; a.last_c = p.last_c; a.last_sb = p.last_sb;
+  a.last_h = p.last_h; a.last_c = p.last_c; a.last_sb = p.last_sb; a.last_sn = p.last_sn;
+  a.rev_n0 = p.rev_n0;
   char* q = base;
   a.rpack = q; q += align256((size_t)GS * p.N * p.D * p.D * elt);
   a.rh = reinterpret_cast<float*>(q); q += align256((size_t)p.B * p.N * p.D * GS * 4);
@@ -760,8 +829,6 @@ int run_fused_bwd(int cell, const BwdArgs& a, const FusedBwdPlan& fp, const DevI
   float* dstate = reinterpret_cast<float*>(base + L.dstate);
   launch_bwd_cell_kernel(kBwdRecord, cell, false, a.wx_f32, dim3(pgrid), dim3(256), st, a, 0, rec);
   const void* fn = reinterpret_cast<const void*>(fp.fn);
-  if (fp.lds > 48 * 1024 && hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)fp.lds) != hipSuccess)
-    return FRNN_EHIP;
   // the batch in chunks of at most Bc rows, one launch each (rows never interact)
   for (int b0 = 0; b0 < a.B; b0 += fp.Bc) {
     const int Bch = std::min(fp.Bc, a.B - b0);
@@ -781,6 +848,7 @@ int run_fused_bwd(int cell, const BwdArgs& a, const FusedBwdPlan& fp, const DevI
     f.xbuf = reinterpret_cast<uint32_t*>(base + L.xbuf);
     f.err = reinterpret_cast<int*>(base - kErrBytes);
     f.timeout_ticks = (long long)env_int("FRNN_TIMEOUT_MS", 2000) * di.wall_khz;
+    f.stall_step = env_int("FRNN_TEST_STALL_STEP", -1);
     void* args[] = {&f};
     const hipError_t e = hipLaunchCooperativeKernel(fn, dim3(grid), dim3(fused_threads(fp.ncw)), args, (unsigned)fp.lds, st);
     if (e == hipErrorCooperativeLaunchTooLarge) return FRNN_ENORESIDENT;
@@ -938,6 +1006,25 @@ int run_backward(const BwdProblem& q, int path, const FusedBwdPlan& fbp, const D
 
 bool misaligned(const void* p) { return p && (reinterpret_cast<uintptr_t>(p) & 15u); }
 
+// Element strides of a description, its dense defaults filled in where it gives 0.
+struct Strides {
+  long long wx_sb, wx_st, st_ss, st_sb, st_st, r_sg, r_sn, r_sd;
+};
+
+Strides strides_of(const frnn_desc* d) {
+  const long long T = d->T, N = d->N, D = d->D, B = d->B, G = gates_of(d->cell);
+  Strides s;
+  s.wx_sb = d->wx_sb ? d->wx_sb : T * G * N * D;
+  s.wx_st = d->wx_st ? d->wx_st : G * N * D;
+  s.st_ss = d->st_ss ? d->st_ss : B * T * N * D;
+  s.st_sb = d->st_sb ? d->st_sb : T * N * D;
+  s.st_st = d->st_st ? d->st_st : N * D;
+  s.r_sg = d->r_sg ? d->r_sg : N * D * D;
+  s.r_sn = d->r_sn ? d->r_sn : D * D;
+  s.r_sd = d->r_sd ? d->r_sd : D;
+  return s;
+}
+
 int validate_desc(const frnn_desc* d, int path) {
   if (!d) return FRNN_EINVAL;
   if (d->reserved != 0) return FRNN_EINVAL;
@@ -948,6 +1035,14 @@ int validate_desc(const frnn_desc* d, int path) {
   if (path != FRNN_PATH_ALTERNATING && path != FRNN_PATH_FUSED) return FRNN_EINVAL;
   const long long elems = (long long)d->B * d->T * gates_of(d->cell) * d->N * d->D;
   if (elems < 0 || elems > (1LL << 40)) return FRNN_EINVAL;
+  // strides: Wx and states rows and steps keep 8-byte (bf16) / 16-byte (fp32) alignment of the
+  // kernels' vector accesses; R's are offsets and must not be negative; every offset fits in 2^40
+  for (long long v : {d->wx_sb, d->wx_st, d->st_ss, d->st_sb, d->st_st}) {
+    if (v % 4 != 0) return FRNN_EINVAL;
+    if (v > (1LL << 40) || v < -(1LL << 40)) return FRNN_EINVAL;
+  }
+  for (long long v : {d->r_sg, d->r_sn, d->r_sd})
+    if (v < 0 || v > (1LL << 40)) return FRNN_EINVAL;
   if (d->out_dtype != FRNN_F32) return FRNN_EUNSUPPORTED;
   if (d->D % 32 != 0 || d->D > 1024) return FRNN_EUNSUPPORTED;
   return FRNN_OK;
@@ -957,25 +1052,26 @@ Problem problem_from_desc(const frnn_desc* d, const void* Wx, const void* R, con
                           void* states, void* last) {
   Problem p;
   std::memset(&p, 0, sizeof(p));
-  const int G = gates_of(d->cell);
-  const long long B = d->B, T = d->T, N = d->N, D = d->D;
+  const long long B = d->B, N = d->N, D = d->D;
   const int f32 = d->in_dtype == FRNN_F32;
   const size_t elt = f32 ? 4 : 2;
+  const Strides s = strides_of(d);
   p.B = d->B; p.T = d->T; p.N = d->N; p.D = d->D; p.cell = d->cell; p.r_f32 = f32;
-  p.Wx = Wx; p.wx_f32 = f32; p.wx_sb = T * G * N * D; p.wx_st = (long long)G * N * D;
-  p.R = R; p.r_sg = N * D * D; p.r_sn = D * D; p.r_sd = D;
+  p.Wx = Wx; p.wx_f32 = f32; p.wx_sb = s.wx_sb; p.wx_st = s.wx_st;
+  p.R = R; p.r_sg = s.r_sg; p.r_sn = s.r_sn; p.r_sd = s.r_sd;
   p.bias = b;
   p.s0_h = s0;
   p.s0_c = (s0 && d->cell == FRNN_CELL_LSTM) ? reinterpret_cast<const char*>(s0) + (size_t)B * N * D * elt : nullptr;
-  p.s0_f32 = f32; p.s0_sb = N * D;
+  p.s0_f32 = f32; p.s0_sb = N * D; p.s0_sn = D;
   float* st = reinterpret_cast<float*>(states);
   p.out_h = st;
-  p.out_c = (st && d->cell == FRNN_CELL_LSTM) ? st + B * T * N * D : nullptr;
-  p.out_sb = T * N * D; p.out_st = N * D;
+  p.out_c = (st && d->cell == FRNN_CELL_LSTM) ? st + s.st_ss : nullptr;
+  p.out_sb = s.st_sb; p.out_st = s.st_st;
   float* ls = reinterpret_cast<float*>(last);
   p.last_h = ls;
   p.last_c = (ls && d->cell == FRNN_CELL_LSTM) ? ls + B * N * D : nullptr;
-  p.last_sb = N * D;
+  p.last_sb = N * D; p.last_sn = D;
+  p.rev_n0 = d->N;
   return p;
 }
 
@@ -985,6 +1081,8 @@ Problem problem_from_desc(const frnn_desc* d, const void* Wx, const void* R, con
 extern "C" {
 
 int frnn_abi_version(void) { return FRNN_ABI_VERSION; }
+
+int frnn_init(void) { return init_device(); }
 
 const char* frnn_status_str(int s) {
   switch (s) {
@@ -997,6 +1095,7 @@ const char* frnn_status_str(int s) {
     case FRNN_ETIMEOUT: return "a bounded inter-workgroup wait ran out on the device";
     case FRNN_EPLACEMENT: return "a workgroup ran on a different accelerator die than planned";
     case FRNN_ENODEVICE: return "no usable gfx950 device";
+    case FRNN_ENOINIT: return "frnn_init() has not prepared the current device";
     default: return "unknown status";
   }
 }
@@ -1127,25 +1226,26 @@ int frnn_bwd(const frnn_desc* d, int path, const void* Wx, const void* R, const 
     if (db && launch_fill(db, (size_t)G * N * D * 4, st) != hipSuccess) return FRNN_EHIP;
     return hipGetLastError() == hipSuccess ? FRNN_OK : FRNN_EHIP;
   }
+  const Strides sd = strides_of(d);
   BwdProblem q;
   std::memset(&q, 0, sizeof(q));
   q.B = B; q.T = T; q.N = N; q.D = D; q.cell = d->cell; q.f32 = f32; q.wx_f32 = f32;
-  q.Wx = Wx; q.wx_sb = (long long)T * G * N * D; q.wx_st = (long long)G * N * D;
-  q.R = R; q.r_sg = (long long)N * D * D; q.r_sn = (long long)D * D; q.r_sd = D;
+  q.Wx = Wx; q.wx_sb = sd.wx_sb; q.wx_st = sd.wx_st;
+  q.R = R; q.r_sg = sd.r_sg; q.r_sn = sd.r_sn; q.r_sd = sd.r_sd;
   q.bias = b;
   q.s0_h = states0;
   q.s0_c = (states0 && S == 2) ? reinterpret_cast<const char*>(states0) + (size_t)BND * elt : nullptr;
   q.s0_sb = (long long)N * D;
   const float* stf = reinterpret_cast<const float*>(states);
-  q.st_h = stf; q.st_c = S == 2 ? stf + (long long)B * T * N * D : nullptr;
-  q.st_sb = (long long)T * N * D; q.st_st = (long long)N * D;
+  q.st_h = stf; q.st_c = S == 2 ? stf + sd.st_ss : nullptr;
+  q.st_sb = sd.st_sb; q.st_st = sd.st_st;
   const float* dsf = reinterpret_cast<const float*>(dstates);
-  q.ds_h = dsf; q.ds_c = (dsf && S == 2) ? dsf + (long long)B * T * N * D : nullptr;
+  q.ds_h = dsf; q.ds_c = (dsf && S == 2) ? dsf + sd.st_ss : nullptr;
   const float* dlf = reinterpret_cast<const float*>(dlast);
   q.dl_h = dlf; q.dl_c = (dlf && S == 2) ? dlf + BND : nullptr;
   q.last_sb = (long long)N * D;
   q.dWx = reinterpret_cast<float*>(dWx);
-  q.dR = reinterpret_cast<float*>(dR); q.dr_sg = (long long)N * D * D; q.dr_sn = (long long)D * D; q.dr_sd = D;
+  q.dR = reinterpret_cast<float*>(dR); q.dr_sg = sd.r_sg; q.dr_sn = sd.r_sn; q.dr_sd = sd.r_sd;
   q.db = reinterpret_cast<float*>(db);
   q.ds0_h = reinterpret_cast<float*>(dstates0);
   q.ds0_c = (dstates0 && S == 2) ? reinterpret_cast<float*>(dstates0) + BND : nullptr;
@@ -1168,40 +1268,65 @@ int frnn_bwd_plan_str(const frnn_desc* d, int path, char* buf, size_t cap) {
   return FRNN_OK;
 }
 
-static int validate_stack(int L, int T, int B, int I, int H, int path) {
+static int validate_stack(int L, int dirs, int T, int B, int I, int H, int path) {
   if (L < 1 || T < 0 || B < 1 || I < 1 || H < 1) return FRNN_EINVAL;
+  if (dirs != 1 && dirs != 2) return FRNN_EINVAL;
   if (path != FRNN_PATH_ALTERNATING && path != FRNN_PATH_FUSED) return FRNN_EINVAL;
-  if ((long long)T * B * 4 * H > (1LL << 40)) return FRNN_EINVAL;
+  if ((long long)T * B * 4 * H * dirs > (1LL << 40)) return FRNN_EINVAL;
   if (H % 32 != 0 || H > 1024) return FRNN_EUNSUPPORTED;
   return FRNN_OK;
 }
 
-static size_t stack_ws_bytes(int L, int T, int B, int I, int H, int path) {
-  size_t s = kErrBytes;
-  s += align256((size_t)T * B * 4 * H * 4);           // projected inputs of one layer, fp32
-  s += align256((size_t)std::max(I, H) * 4 * H * 2);  // Wi of one layer transposed, bf16
-  if (L > 1) s += align256((size_t)T * B * H * 4);    // h sequence handed to the next layer, fp32
-  s += rec_scratch_bytes(B, 1, H, FRNN_CELL_LSTM, 0, path);
-  return s;
+// Workspace of frnn_lstm_stack_fwd after the error word.
+struct StackLayout {
+  size_t wx, wit, bias, hseq, rcopy, rec, total;
+};
+
+static StackLayout stack_layout(int L, int dirs, int T, int B, int I, int H, int path) {
+  const size_t G4 = (size_t)4 * H * dirs;  // projected columns of one layer
+  StackLayout S;
+  size_t q = 0;
+  S.wx = q;    q += align256((size_t)T * B * G4 * 4);                        // projected inputs, fp32
+  S.wit = q;   q += align256((size_t)std::max(I, dirs * H) * G4 * 2);        // Wi transposed, bf16
+  S.bias = q;  q += dirs > 1 ? align256(2 * G4 * 2) : 0;                     // both biases in column order
+  S.hseq = q;  q += L > 1 ? align256((size_t)T * B * dirs * H * 4) : 0;      // h sequence for the next layer
+  S.rcopy = q; q += dirs > 1 ? align256((size_t)dirs * H * 4 * H * 2) : 0;   // both Wh side by side
+  S.rec = q;   q += rec_scratch_bytes(B, dirs, H, FRNN_CELL_LSTM, 0, path);
+  S.total = q;
+  return S;
 }
 
-int frnn_lstm_stack_workspace_bytes(int L, int T, int B, int I, int H, int path, size_t* bytes) {
-  const int rc = validate_stack(L, T, B, I, H, path);
+int frnn_lstm_stack_workspace_bytes(int L, int dirs, int T, int B, int I, int H, int path, size_t* bytes) {
+  const int rc = validate_stack(L, dirs, T, B, I, H, path);
   if (rc != FRNN_OK) return rc;
   if (!bytes) return FRNN_EINVAL;
-  *bytes = stack_ws_bytes(L, T, B, I, H, path);
+  *bytes = kErrBytes + stack_layout(L, dirs, T, B, I, H, path).total;
   return FRNN_OK;
 }
 
-int frnn_lstm_stack_fwd(int L, int T, int B, int I, int H, int path, const void* x, const void* const* Wi,
+// The layer's projection operand: Bt rows (the projected columns) in the order [gate][direction][unit],
+// so that the projection comes out as the head-wise Wx [T][B][G][dirs][H] with one head per
+// direction. Row g*dirs*H + n*H + e is column g*H + e of Wi of direction n.
+static void stack_transpose_wi(const void* const* Wi, int l, int dirs, int in, int H, uint16_t* wit, hipStream_t st) {
+  if (dirs == 1) {
+    launch_transpose<uint16_t>(reinterpret_cast<const uint16_t*>(Wi[l]), 4LL * H, in, 4 * H, wit, in, st);
+    return;
+  }
+  for (int n = 0; n < dirs; ++n)
+    for (int g = 0; g < 4; ++g)
+      launch_transpose<uint16_t>(reinterpret_cast<const uint16_t*>(Wi[l * dirs + n]) + (size_t)g * H, 4LL * H, in, H,
+                                 wit + ((size_t)g * dirs * H + (size_t)n * H) * in, in, st);
+}
+
+int frnn_lstm_stack_fwd(int L, int dirs, int T, int B, int I, int H, int path, const void* x, const void* const* Wi,
                         const void* const* Wh, const void* const* b_ih, const void* const* b_hh, const void* h0,
                         const void* c0, void* out, void* hn, void* cn, void* workspace, size_t workspace_bytes,
                         void* stream) {
-  int rc = validate_stack(L, T, B, I, H, path);
+  int rc = validate_stack(L, dirs, T, B, I, H, path);
   if (rc != FRNN_OK) return rc;
   if (!Wi || !Wh) return FRNN_EINVAL;
   if (T > 0 && !x) return FRNN_EINVAL;
-  for (int l = 0; l < L; ++l) {
+  for (int l = 0; l < L * dirs; ++l) {
     if (!Wi[l] || !Wh[l]) return FRNN_EINVAL;
     if (misaligned(Wi[l]) || misaligned(Wh[l])) return FRNN_EINVAL;
     if (b_ih && misaligned(b_ih[l])) return FRNN_EINVAL;
@@ -1210,44 +1335,43 @@ int frnn_lstm_stack_fwd(int L, int T, int B, int I, int H, int path, const void*
   if (misaligned(x) || misaligned(h0) || misaligned(c0) || misaligned(out) || misaligned(hn) || misaligned(cn) ||
       misaligned(workspace))
     return FRNN_EINVAL;
-  if (!workspace || workspace_bytes < stack_ws_bytes(L, T, B, I, H, path)) return FRNN_EWORKSPACE;
+  const StackLayout SL = stack_layout(L, dirs, T, B, I, H, path);
+  if (!workspace || workspace_bytes < kErrBytes + SL.total) return FRNN_EWORKSPACE;
   DevInfo di;
   rc = get_devinfo(&di);
   if (rc != FRNN_OK) return rc;
   // the per-layer recurrence plan must exist before anything is enqueued
   Problem probe;
   std::memset(&probe, 0, sizeof(probe));
-  probe.B = B; probe.T = T; probe.N = 1; probe.D = H; probe.cell = FRNN_CELL_LSTM; probe.r_f32 = 0; probe.wx_f32 = 1;
+  probe.B = B; probe.T = T; probe.N = dirs; probe.D = H; probe.cell = FRNN_CELL_LSTM; probe.r_f32 = 0; probe.wx_f32 = 1;
   if (path == FRNN_PATH_FUSED) {
     FusedPlan fp;
     rc = plan_fused(probe, di, &fp);
     if (rc != FRNN_OK) return rc;
   }
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  char* base = reinterpret_cast<char*>(workspace);
+  char* base = reinterpret_cast<char*>(workspace) + kErrBytes;
   if (launch_fill(workspace, kErrBytes, st) != hipSuccess) return FRNN_EHIP;
-  char* q = base + kErrBytes;
-  float* wx = reinterpret_cast<float*>(q);
-  q += align256((size_t)T * B * 4 * H * 4);
-  uint16_t* wit = reinterpret_cast<uint16_t*>(q);
-  q += align256((size_t)std::max(I, H) * 4 * H * 2);
-  float* hseq = nullptr;
-  if (L > 1) { hseq = reinterpret_cast<float*>(q); q += align256((size_t)T * B * H * 4); }
-  void* rws = q;
-  const long long LBH = (long long)B * H;
+  float* wx = reinterpret_cast<float*>(base + SL.wx);
+  uint16_t* wit = reinterpret_cast<uint16_t*>(base + SL.wit);
+  uint16_t* biasp = reinterpret_cast<uint16_t*>(base + SL.bias);
+  float* hseq = L > 1 ? reinterpret_cast<float*>(base + SL.hseq) : nullptr;
+  uint16_t* rcopy = reinterpret_cast<uint16_t*>(base + SL.rcopy);
+  void* rws = base + SL.rec;
+  const long long LBH = (long long)B * H, G4 = 4LL * H * dirs;
+  if (T == 0) {  // the final states are the initial ones
+    const long long n = (long long)L * dirs * LBH;
+    const unsigned g = (unsigned)std::min<long long>((n + 255) / 256, 4096);
+    if (hn) hipLaunchKernelGGL(copy_init_kernel, dim3(g), dim3(256), 0, st, h0, 0, reinterpret_cast<float*>(hn), n);
+    if (cn) hipLaunchKernelGGL(copy_init_kernel, dim3(g), dim3(256), 0, st, c0, 0, reinterpret_cast<float*>(cn), n);
+    return hipGetLastError() == hipSuccess ? FRNN_OK : FRNN_EHIP;
+  }
   for (int l = 0; l < L; ++l) {
-    float* last_h = hn ? reinterpret_cast<float*>(hn) + l * LBH : nullptr;
-    float* last_c = cn ? reinterpret_cast<float*>(cn) + l * LBH : nullptr;
-    const void* s0h = h0 ? reinterpret_cast<const uint16_t*>(h0) + l * LBH : nullptr;
-    const void* s0c = c0 ? reinterpret_cast<const uint16_t*>(c0) + l * LBH : nullptr;
-    if (T == 0) {
-      if (last_h) hipLaunchKernelGGL(copy_init_kernel, dim3((unsigned)((LBH + 255) / 256)), dim3(256), 0, st, s0h, 0, last_h, LBH);
-      if (last_c) hipLaunchKernelGGL(copy_init_kernel, dim3((unsigned)((LBH + 255) / 256)), dim3(256), 0, st, s0c, 0, last_c, LBH);
-      continue;
-    }
-    // projection of the layer's whole input sequence: rows m = t*B + b
+    const int in = (l == 0) ? I : dirs * H;
+    const long long soff = (long long)l * dirs * LBH;  // this layer's [dirs][B][H] block of h0 / hn
+    // projection of the layer's whole input sequence, rows m = t*B + b, columns [gate][direction][unit]
     ProjArgs pa;
-    pa.M = T * B; pa.Nc = 4 * H; pa.K = (l == 0) ? I : H;
+    pa.M = T * B; pa.Nc = (int)G4; pa.K = in;
     pa.A = (l == 0) ? x : hseq;
     pa.a_f32 = (l == 0) ? 0 : 1;
     pa.lda = pa.K;
@@ -1255,26 +1379,54 @@ int frnn_lstm_stack_fwd(int L, int T, int B, int I, int H, int path, const void*
     pa.ldb = pa.K;
     pa.a_z = pa.b_z = pa.c_z = 0;
     pa.nt = 0;  // the recurrence reads Wx next: left where its loads find it soonest
-    pa.b1 = b_ih ? reinterpret_cast<const uint16_t*>(b_ih[l]) : nullptr;
-    pa.b2 = b_hh ? reinterpret_cast<const uint16_t*>(b_hh[l]) : nullptr;
+    if (dirs == 1) {
+      pa.b1 = b_ih ? reinterpret_cast<const uint16_t*>(b_ih[l]) : nullptr;
+      pa.b2 = b_hh ? reinterpret_cast<const uint16_t*>(b_hh[l]) : nullptr;
+    } else {
+      StackBiasArgs ba;
+      ba.H = H; ba.dirs = dirs;
+      for (int n = 0; n < 2; ++n) {
+        ba.bi[n] = b_ih ? reinterpret_cast<const uint16_t*>(b_ih[l * dirs + n]) : nullptr;
+        ba.bh[n] = b_hh ? reinterpret_cast<const uint16_t*>(b_hh[l * dirs + n]) : nullptr;
+      }
+      ba.out = biasp;
+      hipLaunchKernelGGL(stack_bias_kernel, dim3((unsigned)((G4 + 255) / 256)), dim3(256), 0, st, ba);
+      pa.b1 = biasp;
+      pa.b2 = biasp + G4;
+    }
     pa.C = wx;
-    pa.ldc = 4 * H;
-    launch_transpose<uint16_t>(reinterpret_cast<const uint16_t*>(Wi[l]), pa.Nc, pa.K, pa.Nc, wit, pa.K, st);
+    pa.ldc = G4;
+    stack_transpose_wi(Wi, l, dirs, in, H, wit, st);
     const dim3 pgrid(((pa.Nc + PJ_BN - 1) / PJ_BN) * ((pa.M + PJ_BM - 1) / PJ_BM));
     launch_proj(pa, pgrid, st);
     if (hipGetLastError() != hipSuccess) return FRNN_EHIP;
-    // recurrence with Wh [H, 4H] read through strides: R[g][0][d][e] = Wh[d][g*H + e]
+    // recurrence, one head per direction: R[g][n][d][e] = Wh of direction n at [d][g*H + e], read
+    // in place for one direction, from a side-by-side copy for two
     Problem p;
     std::memset(&p, 0, sizeof(p));
-    p.B = B; p.T = T; p.N = 1; p.D = H; p.cell = FRNN_CELL_LSTM; p.r_f32 = 0;
-    p.Wx = wx; p.wx_f32 = 1; p.wx_sb = 4LL * H; p.wx_st = 4LL * H * B;
-    p.R = Wh[l]; p.r_sg = H; p.r_sn = 0; p.r_sd = 4LL * H;
+    p.B = B; p.T = T; p.N = dirs; p.D = H; p.cell = FRNN_CELL_LSTM; p.r_f32 = 0;
+    p.Wx = wx; p.wx_f32 = 1; p.wx_sb = G4; p.wx_st = G4 * B;
+    if (dirs == 1) {
+      p.R = Wh[l]; p.r_sn = 0;
+    } else {
+      const long long wh = (long long)H * 4 * H;
+      for (int n = 0; n < dirs; ++n)
+        if (hipMemcpyAsync(rcopy + n * wh, Wh[l * dirs + n], (size_t)wh * 2, hipMemcpyDeviceToDevice, st) != hipSuccess)
+          return FRNN_EHIP;
+      p.R = rcopy; p.r_sn = wh;
+    }
+    p.r_sg = H; p.r_sd = 4LL * H;
     p.bias = nullptr;
-    p.s0_h = s0h; p.s0_c = s0c; p.s0_f32 = 0; p.s0_sb = H;
+    p.s0_h = h0 ? reinterpret_cast<const uint16_t*>(h0) + soff : nullptr;
+    p.s0_c = c0 ? reinterpret_cast<const uint16_t*>(c0) + soff : nullptr;
+    p.s0_f32 = 0; p.s0_sb = H; p.s0_sn = LBH;
     p.out_h = (l == L - 1) ? reinterpret_cast<float*>(out) : hseq;
     p.out_c = nullptr;
-    p.out_sb = H; p.out_st = (long long)B * H;
-    p.last_h = last_h; p.last_c = last_c; p.last_sb = H;
+    p.out_sb = (long long)dirs * H; p.out_st = (long long)B * dirs * H;
+    p.last_h = hn ? reinterpret_cast<float*>(hn) + soff : nullptr;
+    p.last_c = cn ? reinterpret_cast<float*>(cn) + soff : nullptr;
+    p.last_sb = H; p.last_sn = LBH;
+    p.rev_n0 = 1;  // the second direction's head runs backwards in time
     rc = run_recurrence(p, path, reinterpret_cast<int*>(workspace), rws, st);
     if (rc != FRNN_OK) return rc;
   }
@@ -1308,21 +1460,24 @@ static StackBwdLayout stack_bwd_layout(int L, int T, int B, int I, int H, int pa
   return S;
 }
 
-int frnn_lstm_stack_bwd_workspace_bytes(int L, int T, int B, int I, int H, int path, size_t* bytes) {
-  const int rc = validate_stack(L, T, B, I, H, path);
+int frnn_lstm_stack_bwd_workspace_bytes(int L, int dirs, int T, int B, int I, int H, int path, size_t* bytes) {
+  const int rc = validate_stack(L, dirs, T, B, I, H, path);
+  if (rc != FRNN_OK) return rc;
+  if (dirs != 1) return FRNN_EUNSUPPORTED;
   if (rc != FRNN_OK) return rc;
   if (!bytes) return FRNN_EINVAL;
   *bytes = kErrBytes + stack_bwd_layout(L, T, B, I, H, path).total;
   return FRNN_OK;
 }
 
-int frnn_lstm_stack_bwd(int L, int T, int B, int I, int H, int path, const void* x, const void* const* Wi,
+int frnn_lstm_stack_bwd(int L, int dirs, int T, int B, int I, int H, int path, const void* x, const void* const* Wi,
                         const void* const* Wh, const void* const* b_ih, const void* const* b_hh, const void* h0,
                         const void* c0, const void* dout, const void* dhn, const void* dcn, void* dx,
                         void* const* dWi, void* const* dWh, void* const* db_ih, void* const* db_hh, void* dh0,
                         void* dc0, void* workspace, size_t workspace_bytes, void* stream) {
-  int rc = validate_stack(L, T, B, I, H, path);
+  int rc = validate_stack(L, dirs, T, B, I, H, path);
   if (rc != FRNN_OK) return rc;
+  if (dirs != 1) return FRNN_EUNSUPPORTED;
   if (!Wi || !Wh) return FRNN_EINVAL;
   if (T > 0 && !x) return FRNN_EINVAL;
   for (int l = 0; l < L; ++l) {
@@ -1418,7 +1573,7 @@ int frnn_lstm_stack_bwd(int L, int T, int B, int I, int H, int path, const void*
     p.R = Wh[l]; p.r_sg = H; p.r_sn = 0; p.r_sd = 4LL * H;
     p.s0_h = h0 ? reinterpret_cast<const uint16_t*>(h0) + l * LBH : nullptr;
     p.s0_c = c0 ? reinterpret_cast<const uint16_t*>(c0) + l * LBH : nullptr;
-    p.s0_f32 = 0; p.s0_sb = H;
+    p.s0_f32 = 0; p.s0_sb = H; p.s0_sn = H; p.last_sn = H; p.rev_n0 = 1;
     p.out_h = layer_h(l); p.out_c = layer_h(l) + TB * H;
     p.out_sb = H; p.out_st = (long long)B * H;
     rc = run_recurrence(p, path, err, base + SL.rec, st);

@@ -55,42 +55,19 @@ struct FusedArgs {
   const void* s0_h;
   const void* s0_c;
   int s0_f32;
-  long long s0_sb;  // element stride of the initial states for b; [N][D] packed inside
+  long long s0_sb, s0_sn;  // element strides of the initial states for b and n; units dense
   float* out_h;
   float* out_c;
   long long out_sb, out_st;  // element strides of the state outputs for b and t
   float* last_h;
   float* last_c;
-  long long last_sb;
+  long long last_sb, last_sn;
+  int rev_n0;  // heads n >= rev_n0 run backwards in time: step t reads Wx and writes states at T-1-t
   uint32_t* xbuf;  // exchange words [groups][2][BR][D]
   int* err;
   long long timeout_ticks;  // bound of every wait, in wall-clock (100 MHz) ticks
-  long long* trace;         // phase timestamps (only in builds with FRNN_PHASE_TRACE), or null
-  int trace_slots;          // slots of 4096 x 8 timestamps the trace buffer holds
+  int stall_step;           // a failure-handling test's hook: this step publishes a stale tag (-1: none)
 };
-
-#ifdef FRNN_PHASE_TRACE
-// Shader-clock timestamp of phase `ph` of step t, recorded by lane 0 of compute wave 0 of the
-// first and the last workgroup; at most 4096 steps. FRNN_TRACE_RT records the wall clock
-// (100 MHz, common to all CUs) for the workgroups 0, n_xcd, 2 n_xcd, ... (slots 2, 3, ...).
-#define FRNN_TRACE(ph)                                                                          \
-  do {                                                                                          \
-    if (a.trace && a.trace_slots >= 2 && lane == 0 && wave == 0 && (blockIdx.x == 0 || blockIdx.x == gridDim.x - 1) && t < 4096) \
-      a.trace[((blockIdx.x == 0 ? 0 : 1) * 4096 + t) * 8 + (ph)] = (long long)clock64();       \
-  } while (0)
-#define FRNN_TRACE_RT(ph)                                                                       \
-  do {                                                                                          \
-    if (a.trace && lane == 0 && wave == 0 && blockIdx.x % a.n_xcd == 0 && 2 + (int)blockIdx.x / a.n_xcd < a.trace_slots && t < 4096) \
-      a.trace[((2 + blockIdx.x / a.n_xcd) * 4096 + t) * 8 + (ph)] = (long long)wall_clock64();  \
-  } while (0)
-#else
-#define FRNN_TRACE(ph) \
-  do {                 \
-  } while (0)
-#define FRNN_TRACE_RT(ph) \
-  do {                    \
-  } while (0)
-#endif
 
 constexpr int FUSED_IO_STAGES = 4;   // record steps in flight in the backward's I/O wave
 // max 64-bit Wx words (and, in the die-local design, output pairs) one I/O lane moves per step:
@@ -616,7 +593,7 @@ __global__ void __launch_bounds__((NCW + 1) * 64, 1) fused_fwd_kernel(FusedArgs 
     for (int idx = threadIdx.x; idx < 16 * D; idx += NT) {
       const int c = idx / D, k = idx - c * D;
       float v = 0.0f;
-      if (a.s0_h && c < nvalid) v = ld_f(a.s0_h, (long long)(b0 + c) * a.s0_sb + (long long)n * D + k, a.s0_f32);
+      if (a.s0_h && c < nvalid) v = ld_f(a.s0_h, (long long)(b0 + c) * a.s0_sb + (long long)n * a.s0_sn + k, a.s0_f32);
       if (F32) {
         hbuf_f[(1 * 16 + c) * HS + k] = v;
         hbuf_f[c * HS + k] = 0.0f;
@@ -635,24 +612,32 @@ __global__ void __launch_bounds__((NCW + 1) * 64, 1) fused_fwd_kernel(FusedArgs 
   const int u_base = tile0 * UPT;                   // first hidden unit of this workgroup
   const int U_wg = min(MT_WG * UPT, D - u_base);    // its hidden units (the last tiles may be idle)
 
+  // Time direction of this head: a head that runs backwards reads Wx and writes its states
+  // from step T-1 down, through the same strides negated.
+  const bool rev = n >= a.rev_n0;
+  const long long wx_st = rev ? -a.wx_st : a.wx_st, out_st = rev ? -a.out_st : a.out_st;
+  const char* const wx0 = reinterpret_cast<const char*>(a.Wx) + (rev ? (long long)(T - 1) * a.wx_st * (a.wx_f32 ? 4 : 2) : 0);
+  float* const out_h = a.out_h ? a.out_h + (rev ? (long long)(T - 1) * a.out_st : 0) : nullptr;
+  float* const out_c = a.out_c ? a.out_c + (rev ? (long long)(T - 1) * a.out_st : 0) : nullptr;
+
   constexpr bool DMA = fused_dma(LOCAL, F32, CELL);
   char* const dring = smem + lay.dma;
   if constexpr (DMA) {
     if (wave == NCW) {
-      io_wave_dma(reinterpret_cast<const char*>(a.Wx), a.wx_sb, a.wx_st, b0, nvalid, n, D, T, lane, dring);
+      io_wave_dma(wx0, a.wx_sb, wx_st, b0, nvalid, n, D, T, lane, dring);
       return;
     }
   }
   if (wave == NCW) {
     IoCtx c;
-    c.wxb = reinterpret_cast<const char*>(a.Wx);
+    c.wxb = wx0;
     c.wx_f32 = a.wx_f32;
     c.wx_sb = a.wx_sb;
-    c.wx_st = a.wx_st;
-    c.out_h = a.out_h;
-    c.out_c = a.out_c;
+    c.wx_st = wx_st;
+    c.out_h = out_h;
+    c.out_c = out_c;
     c.out_sb = a.out_sb;
-    c.out_st = a.out_st;
+    c.out_st = out_st;
     c.b0 = b0;
     c.nvalid = nvalid;
     c.n = n;
@@ -737,9 +722,9 @@ __global__ void __launch_bounds__((NCW + 1) * 64, 1) fused_fwd_kernel(FusedArgs 
         }
       }
       if (CELL == CELL_LSTM && a.s0_c && colv)
-        creg[q] = ld_f(a.s0_c, bcol * a.s0_sb + (long long)n * D + gu[q], a.s0_f32);
+        creg[q] = ld_f(a.s0_c, bcol * a.s0_sb + (long long)n * a.s0_sn + gu[q], a.s0_f32);
       if (CELL == CELL_GRU && a.s0_h && colv)
-        creg[q] = ld_f(a.s0_h, bcol * a.s0_sb + (long long)n * D + gu[q], a.s0_f32);
+        creg[q] = ld_f(a.s0_h, bcol * a.s0_sb + (long long)n * a.s0_sn + gu[q], a.s0_f32);
     }
   }
   block_barrier();  // barrier -1
@@ -756,7 +741,7 @@ __global__ void __launch_bounds__((NCW + 1) * 64, 1) fused_fwd_kernel(FusedArgs 
 #pragma unroll
       for (int i = 0; i < (QUAD ? 1 : 4); ++i) {
         const int u = gu[q] + i;
-        const float h0 = a.s0_h ? ld_f(a.s0_h, bcol * a.s0_sb + (long long)n * D + u, a.s0_f32) : 0.0f;
+        const float h0 = a.s0_h ? ld_f(a.s0_h, bcol * a.s0_sb + (long long)n * a.s0_sn + u, a.s0_f32) : 0.0f;
         xb[xpar + col * D + u] = (uint32_t)f2bf(h0) << 16;
       }
     }
@@ -764,7 +749,6 @@ __global__ void __launch_bounds__((NCW + 1) * 64, 1) fused_fwd_kernel(FusedArgs 
   float hlast[GT][4];         // h of the last step, written out after the loop
 
   for (int t = 0; t < T; ++t) {
-    FRNN_TRACE(0);
     // Wx of this step (the ring slot t & 1, written by the I/O wave before the barrier that
     // precedes the gating): read as early as that barrier allows
     f32x4_t wxq[GT];
@@ -804,18 +788,13 @@ __global__ void __launch_bounds__((NCW + 1) * 64, 1) fused_fwd_kernel(FusedArgs 
       uint32_t* stage = reinterpret_cast<uint32_t*>(smem + lay.h) + wave * 16 * fused_stage_row(KTW);
       poll_stage<KS, MTW, KTW>(xb, 2 * xpar * 4, ((t - 1) & 1) * xpar * 4, D, ks * KTW * 32, nvalid,
                                (uint32_t)t & 0xFFFFu, t == 0, stage, lane, a.timeout_ticks, a.err, &s_abort);
-      FRNN_TRACE(7);
-      FRNN_TRACE_RT(7);
 #pragma unroll
       for (int kk = 0; kk < KTW; ++kk) {
         const bf16x8_t bk = *reinterpret_cast<const bf16x8_t*>(stage + col * fused_stage_row(KTW) + kk * 16 + 4 * quad);
 #pragma unroll
         for (int j = 0; j < MTW; ++j) acc[j] = mfma_bf16(Ra[j][kk], bk, acc[j]);
       }
-      FRNN_TRACE(6);
-      FRNN_TRACE_RT(6);
     }
-    FRNN_TRACE(1);
 
     // ---- 3. (die-local design) the step's barrier; K-split partial sums through LDS.
     f32x4_t pre[GT];
@@ -837,9 +816,7 @@ __global__ void __launch_bounds__((NCW + 1) * 64, 1) fused_fwd_kernel(FusedArgs 
       f32x4_t P = acc[0];
       pack_tiles<BRP, 1, MTW>(P, acc);
       part[(pp * NCW + wave) * FUSED_PART_ROW + lane] = P;
-      FRNN_TRACE(2);
       block_barrier();
-      FRNN_TRACE(3);
       // the reads go out before the abort flag is looked at (they are harmless if it is set)
 #pragma unroll
       for (int q = 0; q < GT; ++q) wxq[q] = wxs[(((t & 1) * NCW + wave) * GT + q) * 64 + lane];
@@ -857,9 +834,11 @@ __global__ void __launch_bounds__((NCW + 1) * 64, 1) fused_fwd_kernel(FusedArgs 
       for (int q = 0; q < GT; ++q) row_reduce<BRP, KS * BRP>(pre[q]);
     }
 
-    FRNN_TRACE(4);
     // ---- 4. gates, state update, exchange; outputs go to the LDS ring for the I/O wave.
-    const uint32_t wtag = (uint32_t)(t + 1) & 0xFFFFu;
+    // The step the host names in stall_step (a failure-handling test; -1 in every normal call)
+    // publishes the tag of step t - 1, which no consumer polls for, so that their bounded waits
+    // run out and every workgroup leaves through the abort path.
+    const uint32_t wtag = (uint32_t)(t + 1 - (t == a.stall_step ? 2 : 0)) & 0xFFFFu;
 #pragma unroll
     for (int q = 0; q < GT; ++q) {
       if (!gval[q]) continue;
@@ -888,9 +867,9 @@ __global__ void __launch_bounds__((NCW + 1) * 64, 1) fused_fwd_kernel(FusedArgs 
           else hbuf_b[((t & 1) * 16 + col) * HS + u] = f2bf(h);
           // no global load is ever waited for in these waves, so the state stores cost no wait
           if (colv) {
-            const long long o = bcol * a.out_sb + (long long)t * a.out_st + (long long)n * D + u;
-            if (a.out_h) a.out_h[o] = h;
-            if (CELL == CELL_LSTM && a.out_c) a.out_c[o] = c;
+            const long long o = bcol * a.out_sb + (long long)t * out_st + (long long)n * D + u;
+            if (out_h) out_h[o] = h;
+            if (CELL == CELL_LSTM && out_c) out_c[o] = c;
           }
         } else {
           if (colv) xb[(t & 1) * xpar + col * D + u] = ((uint32_t)f2bf(h) << 16) | wtag;
@@ -910,7 +889,7 @@ __global__ void __launch_bounds__((NCW + 1) * 64, 1) fused_fwd_kernel(FusedArgs 
         const float hv = tanh_f(x);
         const int bb = col & 3, u1 = gu[q] + (col >> 2);
         hbuf_b[((t & 1) * 16 + bb) * HS + u1] = f2bf(hv);
-        if (bb < nvalid && a.out_h) a.out_h[(long long)(b0 + bb) * a.out_sb + (long long)t * a.out_st + (long long)n * D + u1] = hv;
+        if (bb < nvalid && out_h) out_h[(long long)(b0 + bb) * a.out_sb + (long long)t * out_st + (long long)n * D + u1] = hv;
         hlast[q][0] = hv;
       } else {
         float h[4];
@@ -924,8 +903,8 @@ __global__ void __launch_bounds__((NCW + 1) * 64, 1) fused_fwd_kernel(FusedArgs 
             u16x4_t hv = {f2bf(h[0]), f2bf(h[1]), f2bf(h[2]), f2bf(h[3])};
             *reinterpret_cast<u16x4_t*>(&hbuf_b[((t & 1) * 16 + col) * HS + u]) = hv;
           }
-          if (colv && a.out_h)
-            *reinterpret_cast<f32x4_t*>(a.out_h + bcol * a.out_sb + (long long)t * a.out_st + (long long)n * D + u) =
+          if (colv && out_h)
+            *reinterpret_cast<f32x4_t*>(out_h + bcol * a.out_sb + (long long)t * out_st + (long long)n * D + u) =
                 f32x4_t{h[0], h[1], h[2], h[3]};
         } else {
           if (colv) {
@@ -940,8 +919,6 @@ __global__ void __launch_bounds__((NCW + 1) * 64, 1) fused_fwd_kernel(FusedArgs 
         for (int i = 0; i < 4; ++i) hlast[q][i] = h[i];
       }
     }
-    FRNN_TRACE(5);
-    FRNN_TRACE_RT(5);
     // Keep the exchange stores ahead of the next step's polling in program order.
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     if (LOCAL) block_barrier();
@@ -953,12 +930,12 @@ __global__ void __launch_bounds__((NCW + 1) * 64, 1) fused_fwd_kernel(FusedArgs 
 #pragma unroll
     for (int q = 0; q < GT; ++q)
       if (gval[q] && bb < nvalid && a.last_h)
-        a.last_h[(long long)(b0 + bb) * a.last_sb + (long long)n * D + gu[q] + (col >> 2)] = hlast[q][0];
+        a.last_h[(long long)(b0 + bb) * a.last_sb + (long long)n * a.last_sn + gu[q] + (col >> 2)] = hlast[q][0];
   } else if (T > 0 && colv) {
 #pragma unroll
     for (int q = 0; q < GT; ++q) {
       if (!gval[q]) continue;
-      const long long lo = bcol * a.last_sb + (long long)n * D + gu[q];
+      const long long lo = bcol * a.last_sb + (long long)n * a.last_sn + gu[q];
       if constexpr (QUAD) {
         if (a.last_h) a.last_h[lo] = hlast[q][0];
         if (CELL == CELL_LSTM && a.last_c) a.last_c[lo] = creg[q];

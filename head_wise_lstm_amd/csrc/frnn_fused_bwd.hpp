@@ -46,6 +46,7 @@ struct FusedBwdArgs {
   uint32_t* xbuf;    // [groups][2][BR][G*D] exchange words
   int* err;
   long long timeout_ticks;
+  int stall_step;    // a failure-handling test's hook: this step publishes a stale tag (-1: none)
 };
 
 struct FusedBwdLds {
@@ -332,7 +333,9 @@ __global__ void __launch_bounds__((NCW + 1) * 64, 1) fused_bwd_kernel(FusedBwdAr
 
     // ---- 4. the linear step for the lane's four units; da out through the exchange, (dh, dc)
     // to the output ring
-    const uint32_t wtag = (uint32_t)(s + 1) & 0xFFFFu;
+    // (the step the host names in stall_step publishes the tag of step s - 1, which no one polls
+    // for: its consumers' bounded waits run out; -1 in every normal call)
+    const uint32_t wtag = (uint32_t)(s + 1 - (s == a.stall_step ? 2 : 0)) & 0xFFFFu;
     if (colv) {
 #pragma unroll
       for (int q = 0; q < GT; ++q) {
@@ -710,7 +713,8 @@ __global__ void __launch_bounds__((NCW + 1) * 64, 1) fused_bwdx_kernel(FusedBwdA
       for (int j = 0; j < MTW; ++j) acc[j] = mfma_bf16(Ra[j][kk], bk, acc[j]);
     }
     if (col < nvalid) {
-      const uint32_t wtag = (uint32_t)(s + 1) & 0xFFFFu;
+      // (stall_step: a stale tag, as in the da design)
+      const uint32_t wtag = (uint32_t)(s + 1 - (s == a.stall_step ? 2 : 0)) & 0xFFFFu;
       uint32_t* dst = xb + (s & 1) * xpar + (w * BR + col) * D;
 #pragma unroll
       for (int j = 0; j < MTW; ++j) {

@@ -24,9 +24,13 @@
  * never interact.
  *
  * Conventions shared by every entry point:
- *  - All tensor arguments are DEVICE pointers owned by the caller; the library never allocates,
- *    frees or synchronises them. Work is enqueued on `stream` (a hipStream_t passed as void*;
- *    NULL = the default stream) and runs asynchronously.
+ *  - frnn_init() prepares the current device once (the only call that allocates device memory or
+ *    waits for the device, apart from frnn_check). Every compute entry point (frnn_fwd, frnn_bwd,
+ *    frnn_lstm_stack_fwd, frnn_lstm_stack_bwd) only enqueues kernels: it never allocates, frees or
+ *    synchronises, so it may be called under stream capture. On a device frnn_init() has not
+ *    prepared it returns FRNN_ENOINIT.
+ *  - All tensor arguments are DEVICE pointers owned by the caller. Work is enqueued on `stream`
+ *    (a hipStream_t passed as void*; NULL = the default stream) and runs asynchronously.
  *  - Arguments are validated on the host before anything is enqueued; on any error nothing is
  *    enqueued and a negative frnn_status is returned.
  *  - The workspace is caller-owned device memory of at least the size the matching
@@ -35,7 +39,9 @@
  *  - Errors that can only be seen on the device (a bounded wait that ran out, a workgroup that
  *    landed on an unexpected accelerator die) are written into the workspace and reported by
  *    frnn_check() after the stream has reached the call.
- *  - Tensors are dense, row-major, with the layouts stated below, and 16-byte aligned.
+ *  - Tensors are row-major with the layouts stated below, and 16-byte aligned. frnn_desc may give
+ *    element strides for Wx, states and R (a time-major Wx, a [D, G*D] weight read in place);
+ *    the other tensors are dense.
  */
 #ifndef FRNN_H
 #define FRNN_H
@@ -47,7 +53,7 @@
 extern "C" {
 #endif
 
-#define FRNN_ABI_VERSION 1
+#define FRNN_ABI_VERSION 2
 
 /* Status codes (0 = success). */
 enum {
@@ -59,7 +65,8 @@ enum {
   FRNN_EHIP = -5,            /* a HIP runtime call failed */
   FRNN_ETIMEOUT = -6,        /* (frnn_check) a bounded inter-workgroup wait ran out */
   FRNN_EPLACEMENT = -7,      /* (frnn_check) a workgroup ran on another die than planned */
-  FRNN_ENODEVICE = -8        /* no usable gfx950 device */
+  FRNN_ENODEVICE = -8,       /* no usable gfx950 device */
+  FRNN_ENOINIT = -9          /* frnn_init() has not prepared the current device */
 };
 
 /* Cells (FlashRNN cell names "lstm", "elman" and "gru"). */
@@ -76,8 +83,18 @@ enum { FRNN_F32 = 0, FRNN_BF16 = 1 };
  *               workgroups sharing a head exchange h through the die-local L2 every step. */
 enum { FRNN_PATH_ALTERNATING = 0, FRNN_PATH_FUSED = 1 };
 
-/* Problem description for frnn_fwd. G and S follow from `cell` (LSTM: 4, 2; Elman: 1, 1;
- * GRU: 3, 1). */
+/* Problem description for frnn_fwd and frnn_bwd. G and S follow from `cell` (LSTM: 4, 2;
+ * Elman: 1, 1; GRU: 3, 1).
+ *
+ * Strides are counted in elements of the tensor's own dtype; 0 selects the dense default given in
+ * brackets. Inside a (batch row, step) slice Wx stays dense as [G, N, D] and states as [N, D]; in R
+ * the unit axis e is contiguous. The FlashRNN usage example's layouts are the defaults; a strided
+ * Wx lets a caller pass a time-major projection [T, B, G*N*D] (wx_sb = G*N*D, wx_st = B*G*N*D)
+ * and a strided R the "5.3 LSTM" page's recurrent weight Wh [D, 4D] in place (N = 1, r_sg = D,
+ * r_sd = 4D). Wx and states strides may be negative (a time- or batch-reversed view, the pointer
+ * then addressing element [0, 0, ...]); their magnitudes must be multiples of 4. R strides must be
+ * non-negative. Output views must not overlap themselves. frnn_bwd reads dstates with the states
+ * strides, writes dWx with the Wx strides and dR with the R strides. */
 typedef struct frnn_desc {
   int32_t B;          /* batch size, >= 1 */
   int32_t T;          /* sequence length, >= 0 */
@@ -87,10 +104,25 @@ typedef struct frnn_desc {
   int32_t in_dtype;   /* dtype of Wx, R, b, states0: FRNN_F32 or FRNN_BF16 */
   int32_t out_dtype;  /* dtype of states and last_states: FRNN_F32 (the only one supported) */
   int32_t reserved;   /* must be 0 */
+  int64_t wx_sb;      /* Wx between batch rows             [T*G*N*D] */
+  int64_t wx_st;      /* Wx between steps                  [G*N*D]   */
+  int64_t st_ss;      /* states between h and c (LSTM)     [B*T*N*D] */
+  int64_t st_sb;      /* states between batch rows         [T*N*D]   */
+  int64_t st_st;      /* states between steps              [N*D]     */
+  int64_t r_sg;       /* R between gates                   [N*D*D]   */
+  int64_t r_sn;       /* R between heads                   [D*D]     */
+  int64_t r_sd;       /* R between rows d (the input unit) [D]       */
 } frnn_desc;
 
 /* ABI version of the loaded library (FRNN_ABI_VERSION). */
 int frnn_abi_version(void);
+
+/* Prepares the current HIP device: checks that it is a gfx950 part, learns how the hardware deals
+ * workgroups to accelerator dies (one probe kernel on a 1 KB buffer it allocates and frees, then a
+ * device synchronisation) and raises the LDS limit of the persistent kernels. Call it once per
+ * device before the first compute call on that device, outside stream capture; later calls
+ * return at once. Thread-safe. Returns FRNN_OK, FRNN_ENODEVICE or FRNN_EHIP. */
+int frnn_init(void);
 
 /* Static, human-readable text for a status code. */
 const char* frnn_status_str(int status);
@@ -131,10 +163,15 @@ int frnn_fwd(const frnn_desc* d, int path, const void* Wx, const void* R, const 
  *   db          [G, N, D]         fp32, written, or NULL
  *   dstates0    [S, B, 1, N, D]   fp32, written, or NULL
  * The contractions take bf16 operands (fp32 for fp32 inputs) with fp32 accumulation, like the
- * forward. T == 0: dstates0 = dlast, dR = db = 0. Only FRNN_PATH_ALTERNATING is offered (per
- * step: a pointwise kernel and an MFMA kernel; before the steps one GEMM recomputes h.R for all
- * of them, after them one GEMM forms dR and db); FRNN_PATH_FUSED returns FRNN_EUNSUPPORTED. The
- * workspace grows with T (it holds every step's h.R and gradient).
+ * forward. T == 0: dstates0 = dlast, dR = db = 0. Both paths first recompute h.R for every step
+ * with one MFMA GEMM per head and end with one GEMM per head that forms dR and db; they differ in
+ * the serial part, t = T-1 .. 0:
+ *   FRNN_PATH_ALTERNATING: per step, a pointwise kernel and an MFMA kernel (2*T launches);
+ *   FRNN_PATH_FUSED: one persistent cooperative launch (bf16 inputs), in which the workgroups of
+ *     a head exchange the gradient reaching h through R every step, the forward's die-local
+ *     design with h and R^T exchanged. Shapes this build has no fused design for return
+ *     FRNN_EUNSUPPORTED (frnn_bwd_plan_str says which design a shape gets).
+ * The workspace grows with T (it holds every step's h.R and gradient).
  */
 int frnn_bwd(const frnn_desc* d, int path, const void* Wx, const void* R, const void* b,
              const void* states0, const void* states, const void* dstates, const void* dlast,
@@ -148,34 +185,41 @@ int frnn_bwd_workspace_bytes(const frnn_desc* d, int path, size_t* bytes);
 int frnn_bwd_plan_str(const frnn_desc* d, int path, char* buf, size_t cap);
 
 /*
- * Plain multi-layer unidirectional LSTM with input projection ("5.3 LSTM": MyLSTM.set_weights,
- * MyLSTM.forward). Per layer l and step t:
- *   gates = in_t . Wi[l] + h . Wh[l] + (b_ih[l] + b_hh[l]),   column blocks i | f | g | o of width H
- *   c = f*c + i*g, h = o*tanh(c);   in_t = x[t] for l = 0, else layer l-1's new h at step t.
- * Layouts (bf16 unless stated):
+ * Plain multi-layer LSTM with input projection ("5.3 LSTM": MyLSTM.set_weights, MyLSTM.forward),
+ * one direction or two (dirs = 1 or 2). Per layer l, direction k and step t:
+ *   gates = in_t . Wi[l,k] + h . Wh[l,k] + (b_ih[l,k] + b_hh[l,k]),   column blocks i | f | g | o of width H
+ *   c = f*c + i*g, h = o*tanh(c)
+ * Direction 0 runs t = 0 .. T-1. Direction 1 (dirs = 2) is the same cell with its own weights run
+ * over the sequence backwards, t = T-1 .. 0 (the page stores these "_reverse" weights; the reading
+ * is torch.nn.LSTM's bidirectional layer). in_t = x[t] for l = 0, else layer l-1's output at step t,
+ * the concatenation [h of direction 0, h of direction 1] at that step. Weights are indexed
+ * [l * dirs + k]. Layouts (bf16 unless stated):
  *   x          [T, B, I]
- *   Wi[l]      [I, 4H] for l = 0, [H, 4H] for l >= 1   (array of L device pointers, host array)
- *   Wh[l]      [H, 4H]                                 (host array of L device pointers)
- *   b_ih[l], b_hh[l]  [4H]                             (host arrays; an entry may be NULL = 0)
- *   h0, c0     [L, B, H] or NULL (zeros)
- *   out        [T, B, H]  fp32, top layer's h at every step (NULL = not written)
- *   hn, cn     [L, B, H]  fp32, final states (NULL = not written)
+ *   Wi[l,k]    [I, 4H] for l = 0, [dirs*H, 4H] for l >= 1   (host array of L*dirs device pointers)
+ *   Wh[l,k]    [H, 4H]                                      (host array of L*dirs device pointers)
+ *   b_ih[l,k], b_hh[l,k]  [4H]                              (host arrays; an entry may be NULL = 0)
+ *   h0, c0     [L*dirs, B, H] or NULL (zeros)
+ *   out        [T, B, dirs*H]  fp32, the top layer's output at every step (NULL = not written)
+ *   hn, cn     [L*dirs, B, H]  fp32, final states (direction 1: after step t = 0) (NULL = not written)
  * The layers run in layer-major order (all T steps of layer 0, then layer 1), which gives the
  * same result as the page's time-major order because layer l at step t depends only on layer
- * l-1 at step t and layer l at step t-1. Each layer's projection over all T runs as one MFMA
- * GEMM before its recurrence.
+ * l-1's outputs and on its own previous step. Each layer's projection over all T, both
+ * directions at once, runs as one MFMA GEMM before its recurrence; the two directions' recurrences
+ * run as two heads of one launch.
  */
-int frnn_lstm_stack_fwd(int L, int T, int B, int I, int H, int path, const void* x,
+int frnn_lstm_stack_fwd(int L, int dirs, int T, int B, int I, int H, int path, const void* x,
                         const void* const* Wi, const void* const* Wh, const void* const* b_ih,
                         const void* const* b_hh, const void* h0, const void* c0, void* out,
                         void* hn, void* cn, void* workspace, size_t workspace_bytes,
                         void* stream);
 
 /* Workspace bytes frnn_lstm_stack_fwd needs (grows with T: it holds the projected inputs). */
-int frnn_lstm_stack_workspace_bytes(int L, int T, int B, int I, int H, int path, size_t* bytes);
+int frnn_lstm_stack_workspace_bytes(int L, int dirs, int T, int B, int I, int H, int path,
+                                    size_t* bytes);
 
 /*
- * Backward of frnn_lstm_stack_fwd: for the loss
+ * Backward of frnn_lstm_stack_fwd for one direction (dirs = 1; dirs = 2 returns
+ * FRNN_EUNSUPPORTED): for the loss
  *     L = sum(dout * out) + sum(dhn * hn) + sum(dcn * cn)
  * it writes the gradients of x, Wi[l], Wh[l], b_ih[l], b_hh[l], h0 and c0 ("5.3 LSTM"'s
  * parameters; the chain rule of its cell and projection, the pages printing no gradients).
@@ -189,7 +233,7 @@ int frnn_lstm_stack_workspace_bytes(int L, int T, int B, int I, int H, int path,
  * as R through strides), dWi = X^T . dWx and dX = dWx . Wi^T (MFMA GEMMs, bf16 operands, fp32
  * accumulation). T == 0: dh0 = dhn, dc0 = dcn, the weight gradients are zero.
  */
-int frnn_lstm_stack_bwd(int L, int T, int B, int I, int H, int path, const void* x,
+int frnn_lstm_stack_bwd(int L, int dirs, int T, int B, int I, int H, int path, const void* x,
                         const void* const* Wi, const void* const* Wh, const void* const* b_ih,
                         const void* const* b_hh, const void* h0, const void* c0, const void* dout,
                         const void* dhn, const void* dcn, void* dx, void* const* dWi,
@@ -197,7 +241,8 @@ int frnn_lstm_stack_bwd(int L, int T, int B, int I, int H, int path, const void*
                         void* dc0, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Workspace bytes frnn_lstm_stack_bwd needs (grows with T and L). */
-int frnn_lstm_stack_bwd_workspace_bytes(int L, int T, int B, int I, int H, int path, size_t* bytes);
+int frnn_lstm_stack_bwd_workspace_bytes(int L, int dirs, int T, int B, int I, int H, int path,
+                                        size_t* bytes);
 
 /* Waits for `stream`, then reads the device-side error word of the last call that used
  * `workspace` (FRNN_OK, FRNN_ETIMEOUT, FRNN_EPLACEMENT, or FRNN_EHIP if the wait failed). */

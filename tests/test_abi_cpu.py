@@ -47,14 +47,17 @@ def test_abi_version_and_status_strings(lib):
     m = re.search(r"#define FRNN_ABI_VERSION (\d+)", open(HEADER).read())
     assert hw.frnn_abi_version() == int(m.group(1))
     for code in ("FRNN_OK", "FRNN_EINVAL", "FRNN_EUNSUPPORTED", "FRNN_EWORKSPACE", "FRNN_ENORESIDENT", "FRNN_EHIP",
-                 "FRNN_ETIMEOUT", "FRNN_EPLACEMENT", "FRNN_ENODEVICE"):
+                 "FRNN_ETIMEOUT", "FRNN_EPLACEMENT", "FRNN_ENODEVICE", "FRNN_ENOINIT"):
         s = hw.frnn_status_str(header_enum(code))
         assert s and s != "unknown status"
     assert hw.frnn_status_str(12345) == "unknown status"
 
 
-def D(B=2, T=3, N=1, Dm=64, cell=0, ind=1, outd=0, res=0):
-    return hw.Desc(B, T, N, Dm, cell, ind, outd, res)
+def D(B=2, T=3, N=1, Dm=64, cell=0, ind=1, outd=0, res=0, **strides):
+    d = hw.Desc(B, T, N, Dm, cell, ind, outd, res)
+    for k, v in strides.items():
+        setattr(d, k, v)
+    return d
 
 
 def ws_bytes(desc, path):
@@ -76,6 +79,27 @@ def test_workspace_bytes_validation(lib, desc, code):
     for path in (0, 1):
         assert ws_bytes(desc, path)[0] == code
     assert ws_bytes(D(), 3)[0] == EINVAL
+
+
+def test_desc_layout_matches_header(lib):
+    # 8 int32 fields, then 8 int64 strides: 96 bytes, the strides 8-byte aligned from byte 32
+    assert ctypes.sizeof(hw.Desc) == 96 and hw.Desc.wx_sb.offset == 32 and hw.Desc.r_sd.offset == 88
+    text = open(HEADER).read()
+    body = text[text.index("typedef struct frnn_desc {"):text.index("} frnn_desc;")]
+    names = re.findall(r"int(?:32|64)_t\s+(\w+);", body)
+    assert names == [f[0] for f in hw.Desc._fields_]
+
+
+@pytest.mark.parametrize("strides,code", [
+    (dict(wx_sb=6), EINVAL), (dict(wx_st=-2), EINVAL), (dict(st_st=3), EINVAL), (dict(st_sb=-4 * 7), 0),
+    (dict(wx_st=-4 * 64), 0), (dict(r_sd=-64), EINVAL), (dict(r_sg=-1), EINVAL), (dict(r_sd=65), 0),
+    (dict(r_sg=64, r_sd=256, r_sn=0), 0), (dict(wx_sb=1 << 41), EINVAL), (dict(st_ss=4 * 999), 0),
+])
+def test_desc_stride_validation(lib, strides, code):
+    """Wx and states strides may be negative but keep multiples of 4 elements; R strides are
+    non-negative element offsets of any value."""
+    for path in (0, 1):
+        assert ws_bytes(D(**strides), path)[0] == code
 
 
 def test_workspace_bytes_independent_of_T(lib):
@@ -105,15 +129,23 @@ def test_fwd_rejects_before_any_device_call(lib):
 def test_stack_validation(lib):
     n = ctypes.c_size_t(0)
     g = lib.frnn_lstm_stack_workspace_bytes
-    assert g(2, 512, 32, 512, 512, 1, ctypes.byref(n)) == 0 and n.value > 512 * 32 * 2048 * 4
-    assert g(0, 512, 32, 512, 512, 1, ctypes.byref(n)) == EINVAL
-    assert g(2, 512, 32, 512, 500, 1, ctypes.byref(n)) == EUNSUP
-    arr = ctypes.c_void_p * 2
+    assert g(2, 1, 512, 32, 512, 512, 1, ctypes.byref(n)) == 0 and n.value > 512 * 32 * 2048 * 4
+    one = n.value
+    assert g(2, 2, 512, 32, 512, 512, 1, ctypes.byref(n)) == 0 and n.value > 2 * 512 * 32 * 2048 * 4 > one
+    assert g(0, 1, 512, 32, 512, 512, 1, ctypes.byref(n)) == EINVAL
+    assert g(2, 3, 512, 32, 512, 512, 1, ctypes.byref(n)) == EINVAL   # one or two directions
+    assert g(2, 0, 512, 32, 512, 512, 1, ctypes.byref(n)) == EINVAL
+    assert g(2, 1, 512, 32, 512, 500, 1, ctypes.byref(n)) == EUNSUP
+    assert lib.frnn_lstm_stack_bwd_workspace_bytes(2, 2, 512, 32, 512, 512, 1, ctypes.byref(n)) == EUNSUP
+    arr = ctypes.c_void_p * 4
     p = ctypes.c_void_p(0x100000)
-    ptrs = arr(0x100000, 0x100000)
+    ptrs = arr(0x100000, 0x100000, 0x100000, 0x100000)
     f = lib.frnn_lstm_stack_fwd
-    assert f(2, 4, 2, 64, 64, 1, p, None, ptrs, None, None, None, None, p, p, p, p, 1 << 30, None) == EINVAL
-    assert f(2, 4, 2, 64, 64, 1, p, ptrs, ptrs, None, None, None, None, p, p, p, p, 16, None) == EWS
+    assert f(2, 1, 4, 2, 64, 64, 1, p, None, ptrs, None, None, None, None, p, p, p, p, 1 << 30, None) == EINVAL
+    assert f(2, 1, 4, 2, 64, 64, 1, p, ptrs, ptrs, None, None, None, None, p, p, p, p, 16, None) == EWS
+    assert f(2, 2, 4, 2, 64, 64, 1, p, ptrs, ptrs, None, None, None, None, p, p, p, p, 16, None) == EWS
+    odd = arr(0x100000, 0x100000, 0x100000, 0x100004)   # the fourth (layer 1, direction 1) misaligned
+    assert f(2, 2, 4, 2, 64, 64, 1, p, ptrs, odd, None, None, None, None, p, p, p, p, 1 << 30, None) == EINVAL
 
 
 @pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-device answer")
@@ -122,6 +154,40 @@ def test_valid_call_without_device_reports_no_device(lib):
     p = ctypes.c_void_p(0x100000)
     need = ws_bytes(d, 1)[1]
     assert lib.frnn_fwd(ctypes.byref(d), 1, p, p, None, None, p, p, p, need, None) == header_enum("FRNN_ENODEVICE")
+    assert lib.frnn_init() == header_enum("FRNN_ENODEVICE")
+
+
+def _function_bodies(src):
+    """Top-level function bodies of a C++ source: {name: body text} (brace matching)."""
+    out = {}
+    for m in re.finditer(r"^[A-Za-z_][\w:<>,\s\*&]*?\b(\w+)\s*\([^;{]*\)\s*(?:const\s*)?\{", src, re.M):
+        i, depth = m.end(), 1
+        while depth and i < len(src):
+            depth += {"{": 1, "}": -1}.get(src[i], 0)
+            i += 1
+        out.setdefault(m.group(1), "")
+        out[m.group(1)] += src[m.end():i]
+    return out
+
+
+def test_compute_entry_points_never_allocate_or_wait():
+    """Only frnn_init (through init_device) and frnn_check may allocate, free or wait for the
+    device; every other function of the library's sources only enqueues work."""
+    csrc = os.path.join(ROOT, "head_wise_lstm_amd", "csrc")
+    banned = re.compile(r"\b(hipMalloc\w*|hipFree\w*|hipHostMalloc|hipDeviceSynchronize|hipStreamSynchronize|"
+                        r"hipEventSynchronize|hipMemcpy|hipMemset|hipMallocAsync|hipFuncSetAttribute)\s*\(")
+    allowed = {"init_device", "frnn_check", "raise_lds_limits"}
+    seen = set()
+    for fn in sorted(os.listdir(csrc)):
+        if not fn.endswith((".hip", ".hpp")):
+            continue
+        src = open(os.path.join(csrc, fn)).read()
+        src = re.sub(r"//[^\n]*", "", src)
+        for name, body in _function_bodies(src).items():
+            for m in banned.finditer(body):
+                seen.add((name, m.group(1)))
+                assert name in allowed, f"{fn}: {name} calls {m.group(1)}"
+    assert ("init_device", "hipMalloc") in seen and ("frnn_check", "hipStreamSynchronize") in seen
 
 
 def plan(desc, path):

@@ -4,8 +4,11 @@ The GPU runs its own forward, then the backward from the states it returned; the
 both in fp64 on the same stored inputs and the same seeded cotangents (dstates, dlast ~ N(0,1)).
 
 Bar, per gradient tensor X (dWx, dR, db, dstates0): max|X_gpu - X_oracle| <= tol * max(1,
-max|X_oracle|), tol = 1e-4 for fp32 inputs and 3e-2 for bf16 inputs (the forward's bars, taken
-relative to the tensor's scale: dR and db are sums over all B*T steps and grow with them).
+max|X_oracle|), relative to the tensor's scale because dR and db are sums over all B*T steps and
+grow with them. tol = 1e-2 for bf16 inputs: the contractions take bf16 copies of h and of the
+gradient of the gate pre-activations (unit roundoff 2^-9, about 2e-3, on each operand), so an
+element carries a few units of it relative to the largest element; 1e-2 is five. tol = 1e-5 for
+fp32 inputs, a few hundred fp32 units for sums over up to B*T*D terms.
 """
 import os
 import sys
@@ -19,7 +22,7 @@ import oracle
 
 pytestmark = pytest.mark.gpu
 
-TOL = {torch.float32: 1e-4, torch.bfloat16: 3e-2}
+TOL = {torch.float32: 1e-5, torch.bfloat16: 1e-2}
 
 
 def _hw():
@@ -306,7 +309,7 @@ def _stack_bwd_case(w, path):
             scale = max(1.0, float(np.abs(r).max()))
             rel = float(np.abs(a - r).max()) / scale
             worst = max(worst, rel)
-            assert rel <= 3e-2, f"{name}[{k}]: max abs err / scale {rel}"
+            assert rel <= TOL[torch.bfloat16], f"{name}[{k}]: max abs err / scale {rel}"
     _log(f"  worst max|err| / scale = {worst:.3e}")
 
 
@@ -323,3 +326,37 @@ def test_stack_bwd_small(path):
 def test_stack_bwd_full():
     # the float64 oracle takes about a minute at this size (every gradient depends on every step)
     _stack_bwd_case(fi.WORKLOADS["lstm2_bf16_T512_B32_I512_H512"], "fused")
+
+
+@pytest.mark.parametrize("path", ["alternating", "fused"])
+def test_bwd_strided_views(path):
+    """frnn_bwd on a time-major Wx view, the recurrent weight Wh [D, 4D] read in place as R, and
+    time-major states: dWx comes back with Wx's strides and dR with R's, equal to the oracle's
+    gradients of the same values laid out densely."""
+    hw = _hw()
+    B, T, D = 6, 13, 128
+    w = fi.HeadwiseWorkload("bwd_strided", "lstm", torch.bfloat16, B=B, T=T, N=1, D=D, seed=241, s0_var=1.0)
+    x = fi.make_inputs(w)
+    ct = fi.backward_cotangents(w)
+    dev = torch.device("cuda:0")
+    Wx_view = x["Wx"].permute(1, 0, 2, 3, 4).contiguous().to(dev).permute(1, 0, 2, 3, 4)
+    Wh = x["R"][:, 0].permute(1, 0, 2).reshape(D, 4 * D).contiguous().to(dev)
+    R_view = Wh.view(D, 4, D).permute(1, 0, 2).unsqueeze(1)
+    st_tm = torch.empty((2, T, B, 1, D), dtype=torch.float32, device=dev)
+    last = torch.empty((2, B, 1, 1, D), dtype=torch.float32, device=dev)
+    b, s0 = x["b"].to(dev), x["states0"].to(dev)
+    _log(f"bwd strided case path={path}")
+    st_view = st_tm.permute(0, 2, 1, 3, 4)
+    hw.frnn_fwd(Wx_view, R_view, b, s0, cell="lstm", path="fused", out=(st_view, last))
+    grads = hw.frnn_bwd(Wx_view, R_view, b, s0, st_view, ct["dstates"].to(dev), ct["dlast"].to(dev), cell="lstm",
+                        path=path)
+    assert grads[0].stride() == Wx_view.stride() and grads[1].stride() == R_view.stride()
+    f = fi.to_f64
+    ref = oracle.headwise_bwd("lstm", f(x["Wx"]), f(x["R"]), f(x["b"]), f(x["states0"]), f(ct["dstates"]),
+                              f(ct["dlast"]))
+    for name, gv, rv in zip(("dWx", "dR", "db", "dstates0"), grads, ref):
+        gv = gv.double().cpu().numpy()
+        scale = max(1.0, float(np.abs(rv).max()))
+        rel = float(np.abs(gv - rv).max()) / scale
+        _log(f"  {name}: rel={rel:.2e}")
+        assert rel <= TOL[torch.bfloat16], name

@@ -4,6 +4,7 @@ Tolerances (max abs error on h and c): 1e-4 for fp32 inputs, 3e-2 for bf16 input
 accumulation. Every case, the full-size workloads in the launch configuration the benchmark times
 included, compares every (batch, head) row element by element.
 """
+import ctypes
 import math
 import os
 import sys
@@ -341,6 +342,9 @@ def test_full_workload(name, path):
 
 
 def _stack_case(w, path, rows, env=None):
+    if w.dirs > 1:
+        return _stack_dirs_case(w, path, rows, env)
+
     hw = _hw()
     x = fi.make_inputs(w)
     dev = torch.device("cuda:0")
@@ -390,3 +394,142 @@ def test_stack_small_register_staged_projection():
 def test_stack_full(path):
     w = fi.WORKLOADS["lstm2_bf16_T512_B32_I512_H512"]
     _stack_case(w, path, list(range(w.B)))
+
+
+def _stack_dirs_case(w, path, rows, env=None):
+    """Multi-layer LSTM with two directions per layer against the oracle's layer-by-layer loops."""
+    hw = _hw()
+    x = fi.make_inputs(w)
+    dev = torch.device("cuda:0")
+    _log(f"bidirectional stack case {w.name} L={w.L} T={w.T} B={w.B} I={w.I} H={w.H} path={path} env={env}")
+    g = lambda t: None if t is None else t.to(dev)
+    old = {k: os.environ.get(k) for k in (env or {})}
+    os.environ.update({k: str(v) for k, v in (env or {}).items()})
+    try:
+        out, hn, cn = hw.frnn_lstm_stack_fwd(g(x["x"]), [g(t) for t in x["Wi"]], [g(t) for t in x["Wh"]],
+                                             [g(t) for t in x["b_ih"]], [g(t) for t in x["b_hh"]], g(x["h0"]),
+                                             g(x["c0"]), path=path, bidirectional=True)
+        torch.cuda.synchronize()
+    finally:
+        for k, v in old.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+    f = fi.to_f64
+    sel = lambda a, axis: np.take(a, rows, axis=axis)
+    ro, rh, rc = oracle.lstm_stack_dirs(sel(f(x["x"]), 1), [f(t) for t in x["Wi"]], [f(t) for t in x["Wh"]],
+                                        [f(t) for t in x["b_ih"]], [f(t) for t in x["b_hh"]],
+                                        None if x["h0"] is None else sel(f(x["h0"]), 1),
+                                        None if x["c0"] is None else sel(f(x["c0"]), 1), dirs=2)
+    go = sel(out.double().cpu().numpy(), 1)
+    gh = sel(hn.double().cpu().numpy(), 1)
+    gc = sel(cn.double().cpu().numpy(), 1)
+    assert go.shape == ro.shape and gh.shape == rh.shape
+    e = max(np.abs(go - ro).max(), np.abs(gh - rh).max(), np.abs(gc - rc).max())
+    _log(f"  max|err| out/hn/cn = {e:.3e}")
+    assert np.isfinite(e) and e <= 3e-2
+
+
+STACK_BIDIR_SMALL = fi.StackWorkload("stack_bidir_small", torch.bfloat16, L=2, T=19, B=10, I=96, H=128, seed=162,
+                                     zero_init=False, dirs=2)
+
+
+@pytest.mark.parametrize("path", ["fused", "alternating"])
+def test_stack_bidirectional_small(path):
+    _stack_case(STACK_BIDIR_SMALL, path, list(range(STACK_BIDIR_SMALL.B)))
+
+
+@pytest.mark.parametrize("path", ["fused", "alternating"])
+def test_stack_bidirectional_three_layers(path):
+    w = fi.StackWorkload("stack_bidir_l3", torch.bfloat16, L=3, T=7, B=5, I=64, H=64, seed=163, zero_init=False,
+                         dirs=2)
+    _stack_case(w, path, list(range(w.B)))
+
+
+@pytest.mark.parametrize("path", ["fused", "alternating"])
+def test_stack_bidirectional_full(path):
+    w = fi.get_workload("lstm2bi_bf16_T512_B32_I512_H512")
+    _stack_case(w, path, list(range(w.B)))
+
+
+def test_stack_bidirectional_t0():
+    hw = _hw()
+    w = fi.StackWorkload("bidir_t0", torch.bfloat16, L=2, T=0, B=3, I=32, H=32, seed=164, zero_init=False, dirs=2)
+    x = {k: v for k, v in fi.make_inputs(w).items()}
+    g = lambda t: None if t is None else t.cuda()
+    out, hn, cn = hw.frnn_lstm_stack_fwd(g(x["x"]), [g(t) for t in x["Wi"]], [g(t) for t in x["Wh"]],
+                                         [g(t) for t in x["b_ih"]], [g(t) for t in x["b_hh"]], g(x["h0"]), g(x["c0"]),
+                                         path="fused", bidirectional=True)
+    torch.testing.assert_close(hn.cpu(), x["h0"].float(), rtol=0, atol=0)
+    torch.testing.assert_close(cn.cpu(), x["c0"].float(), rtol=0, atol=0)
+
+
+# ------------------------------------------------------------------ strided views (frnn_desc strides)
+def test_strided_time_major_wx_and_wh_view():
+    """A time-major projection [T,B,G*N*D] passed as Wx, the "5.3 LSTM" recurrent weight Wh [D,4D]
+    read in place as R, and time-major states out, on both paths, against the oracle on the same
+    values laid out densely."""
+    hw = _hw()
+    B, T, D = 6, 11, 128
+    w = fi.HeadwiseWorkload("strided", "lstm", torch.bfloat16, B=B, T=T, N=1, D=D, seed=171, s0_var=1.0)
+    x = fi.make_inputs(w)
+    dev = torch.device("cuda:0")
+    wx_tm = x["Wx"].permute(1, 0, 2, 3, 4).contiguous().to(dev)        # [T,B,G,1,D]
+    Wx_view = wx_tm.permute(1, 0, 2, 3, 4)                            # [B,T,G,1,D], strides (G*D, B*G*D, ...)
+    Wh = x["R"][:, 0].permute(1, 0, 2).reshape(D, 4 * D).contiguous().to(dev)   # Wh[d, g*D + e] = R[g,0,d,e]
+    R_view = Wh.view(D, 4, D).permute(1, 0, 2).unsqueeze(1)           # [4,1,D,D], strides (D, *, 4D, 1)
+    assert not Wx_view.is_contiguous() and not R_view.is_contiguous()
+    ref, ref_last = oracle.headwise_fwd("lstm", fi.to_f64(x["Wx"]), fi.to_f64(x["R"]), fi.to_f64(x["b"]),
+                                        fi.to_f64(x["states0"]))
+    for path in ("fused", "alternating"):
+        st_tm = torch.empty((2, T, B, 1, D), dtype=torch.float32, device=dev)
+        last = torch.empty((2, B, 1, 1, D), dtype=torch.float32, device=dev)
+        _log(f"strided case path={path}")
+        hw.frnn_fwd(Wx_view, R_view, x["b"].to(dev), x["states0"].to(dev), cell="lstm", path=path,
+                    out=(st_tm.permute(0, 2, 1, 3, 4), last))
+        got = st_tm.permute(0, 2, 1, 3, 4).double().cpu().numpy()
+        err = np.abs(got - ref).max()
+        err_last = np.abs(last.double().cpu().numpy() - ref_last).max()
+        _log(f"  max|err| states={err:.3e} last={err_last:.3e}")
+        assert err <= 3e-2 and err_last <= 3e-2
+
+
+def _desc_ptr_call(hw, d, path, Wx, R, b, s0, st, last):
+    ws = torch.empty(hw.frnn_workspace_bytes(d, path), dtype=torch.uint8, device="cuda")
+    hw.frnn_init()
+    p = lambda t: None if t is None else ctypes.c_void_p(t)
+    rc = hw.load().frnn_fwd(ctypes.byref(d), hw._path(path), p(Wx), p(R), p(b), p(s0), p(st), p(last),
+                            ctypes.c_void_p(ws.data_ptr()), ws.numel(), hw._stream_handle(torch.device("cuda:0")))
+    assert rc == 0, hw.frnn_status_str(rc)
+    hw.frnn_check(ws)
+
+
+@pytest.mark.parametrize("path", ["fused", "alternating"])
+def test_negative_strides_time_reversed(path):
+    """Negative strides through the C ABI: Wx read backwards in time (the pointer at step 0 of the
+    view, which is the stored sequence's last step) and states written backwards, equal the
+    forward over the reversed sequence."""
+    hw = _hw()
+    B, T, N, D = 5, 9, 2, 64
+    w = fi.HeadwiseWorkload("negstride", "lstm", torch.bfloat16, B=B, T=T, N=N, D=D, seed=172, s0_var=1.0)
+    x = fi.make_inputs(w)
+    dev = torch.device("cuda:0")
+    stored = x["Wx"].flip(1).contiguous().to(dev)                      # the sequence stored last step first
+    R, b, s0 = x["R"].to(dev), x["b"].to(dev), x["states0"].to(dev)
+    st = torch.full((2, B, T, N, D), float("nan"), dtype=torch.float32, device=dev)
+    last = torch.empty((2, B, 1, N, D), dtype=torch.float32, device=dev)
+    d = hw._desc(B, T, N, D, "lstm", torch.bfloat16)
+    G = 4
+    d.wx_sb, d.wx_st = T * G * N * D, -G * N * D
+    d.st_ss, d.st_sb, d.st_st = B * T * N * D, T * N * D, -N * D
+    wx0 = stored.data_ptr() + (T - 1) * G * N * D * 2                 # element [0, 0] of the reversed view
+    st0 = st.data_ptr() + (T - 1) * N * D * 4
+    _desc_ptr_call(hw, d, path, wx0, R.data_ptr(), b.data_ptr(), s0.data_ptr(), st0, last.data_ptr())
+    got = st.flip(2).double().cpu().numpy()                            # written backwards: flip to time order
+    ref, ref_last = oracle.headwise_fwd("lstm", fi.to_f64(x["Wx"]), fi.to_f64(x["R"]), fi.to_f64(x["b"]),
+                                        fi.to_f64(x["states0"]))
+    err = np.abs(got - ref).max()
+    _log(f"  negative strides {path}: max|err| states={err:.3e}")
+    assert np.all(np.isfinite(got)) and err <= 3e-2
+    assert np.abs(last.double().cpu().numpy() - ref_last).max() <= 3e-2

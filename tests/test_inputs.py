@@ -53,3 +53,15 @@ def test_gru_workloads_shapes():
     x = fi.make_inputs("gru_f32_B2_T16_N1_D32")
     assert tuple(x["Wx"].shape) == (2, 16, 3, 1, 32) and tuple(x["R"].shape) == (3, 1, 32, 32)
     assert tuple(x["b"].shape) == (3, 1, 32) and tuple(x["states0"].shape) == (1, 2, 1, 1, 32)
+
+
+def test_bidirectional_stack_workload():
+    w = fi.get_workload("lstm2bi_bf16_T512_B32_I512_H512")
+    assert w.dirs == 2 and (w.L, w.T, w.B, w.I, w.H) == (2, 512, 32, 512, 512)
+    x = fi.make_inputs(w)
+    assert len(x["Wi"]) == len(x["Wh"]) == len(x["b_ih"]) == len(x["b_hh"]) == 4
+    assert [tuple(t.shape) for t in x["Wi"]] == [(512, 2048), (512, 2048), (1024, 2048), (1024, 2048)]
+    # one direction: the same draws as before the direction count existed
+    one = fi.StackWorkload("one", torch.bfloat16, L=2, T=3, B=2, I=8, H=32, seed=9)
+    a = fi.make_inputs(one)
+    assert [tuple(t.shape) for t in a["Wi"]] == [(8, 128), (32, 128)]
