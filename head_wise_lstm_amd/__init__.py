@@ -20,7 +20,7 @@ __all__ = [
     "frnn_abi_version", "frnn_status_str", "frnn_workspace_bytes", "frnn_plan_str", "frnn_fwd",
     "frnn_check", "frnn_lstm_stack_workspace_bytes", "frnn_lstm_stack_fwd", "frnn_bwd_workspace_bytes",
     "frnn_bwd_plan_str", "frnn_bwd", "flashrnn", "frnn_lstm_stack_bwd_workspace_bytes", "frnn_lstm_stack_bwd",
-    "frnn_init",
+    "frnn_init", "frnn_fwd_noalloc",
 ]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -81,6 +81,8 @@ def load():
     lib.frnn_fwd.argtypes = [dptr, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.frnn_check.restype = i32
     lib.frnn_check.argtypes = [vp, vp]
+    lib.frnn_fwd_noalloc.restype = i32
+    lib.frnn_fwd_noalloc.argtypes = [dptr, i32, vp, vp, vp, vp, vp, vp, vp]
     lib.frnn_bwd_workspace_bytes.restype = i32
     lib.frnn_bwd_workspace_bytes.argtypes = [dptr, i32, ctypes.POINTER(sz)]
     lib.frnn_bwd_plan_str.restype = i32
@@ -248,6 +250,40 @@ def frnn_fwd(Wx: torch.Tensor, R: torch.Tensor, b: Optional[torch.Tensor] = None
         raise FrnnError(rc, "frnn_fwd")
     if check:
         frnn_check(workspace)
+    return st_out, last
+
+
+def frnn_fwd_noalloc(Wx: torch.Tensor, R: torch.Tensor, b: Optional[torch.Tensor], states: Optional[torch.Tensor],
+                     out: Sequence[torch.Tensor], cell: str = "lstm", path="fused", check: bool = True):
+    """frnn_fwd into the caller's ``out`` = (states [S,B,T,N,D], last_states [S,B,1,N,D]) fp32, with
+    the library's own per-device array as the workspace: the call allocates nothing (for callers
+    that cannot). Calls on one device share the array and must not overlap. Returns ``out``."""
+    if cell not in _GATES_STATES:
+        raise ValueError(f"unknown cell {cell!r}")
+    G, S = _GATES_STATES[cell]
+    B, T, G_, N, D = Wx.shape
+    dev, dt = Wx.device, Wx.dtype
+    if G_ != G or dt not in _DTYPES:
+        raise ValueError("Wx: wrong gate count or dtype")
+    wx_st = _check_tensor(Wx, "Wx", (B, T, G, N, D), dt, dev, dense_inner=3)
+    r_st = _check_tensor(R, "R", (G, N, D, D), dt, dev, dense_inner=1)
+    _check_tensor(b, "b", (G, N, D), dt, dev)
+    _check_tensor(states, "states", (S, B, 1, N, D), dt, dev)
+    st_out, last = out
+    st_st = _check_tensor(st_out, "out[0]", (S, B, T, N, D), torch.float32, dev, dense_inner=2)
+    _check_tensor(last, "out[1]", (S, B, 1, N, D), torch.float32, dev)
+    desc = _desc(B, T, N, D, cell, dt)
+    _set_strides(desc, wx_st, st_st, r_st)
+    frnn_init(dev)
+    stream = _stream_handle(dev)
+    rc = load().frnn_fwd_noalloc(ctypes.byref(desc), _path(path), _ptr(Wx), _ptr(R), _ptr(b), _ptr(states),
+                                 _ptr(st_out), _ptr(last), stream)
+    if rc != FRNN_OK:
+        raise FrnnError(rc, "frnn_fwd_noalloc")
+    if check:
+        rc = load().frnn_check(None, stream)
+        if rc != FRNN_OK:
+            raise FrnnError(rc, "frnn_check")
     return st_out, last
 
 

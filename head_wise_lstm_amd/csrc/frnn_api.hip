@@ -61,6 +61,12 @@ __global__ void xcc_map_kernel(int* out) {
 constexpr size_t kErrBytes = 256;
 constexpr int kMaxDies = 8;
 
+// The workspace of frnn_fwd_noalloc: one array per device, held until the process ends. Host code
+// never uses this name as an address (on the host it is a stand-in); init_device() looks up the
+// device address of the current device's copy once and every use goes through that pointer.
+constexpr size_t kScratchBytes = FRNN_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // ----------------------------------------------------------------------------- device facts
@@ -72,6 +78,7 @@ struct DevInfo {
   bool periodic = true;
   int xcc_of[kMaxDies] = {0, 1, 2, 3, 4, 5, 6, 7};
   long long wall_khz = 100000;
+  void* scratch = nullptr;  // device address of this device's `scratch` array
 };
 
 std::mutex g_dev_mu;
@@ -116,6 +123,7 @@ int init_device() {
       if (nd.xcc_of[d] == nd.xcc_of[d2]) nd.periodic = false;
   const int rc = raise_lds_limits();
   if (rc != FRNN_OK) return rc;
+  if (hipGetSymbolAddress(&nd.scratch, HIP_SYMBOL(scratch)) != hipSuccess || !nd.scratch) return FRNN_EHIP;
   nd.ok = true;
   di = nd;
   return FRNN_OK;
@@ -1165,8 +1173,27 @@ int frnn_fwd(const frnn_desc* d, int path, const void* Wx, const void* R, const 
   return run_recurrence(p, path, reinterpret_cast<int*>(workspace), reinterpret_cast<char*>(workspace) + kErrBytes, st);
 }
 
+int frnn_fwd_noalloc(const frnn_desc* d, int path, const void* Wx, const void* R, const void* b, const void* states0,
+                     void* states, void* last_states, void* stream) {
+  const int rc = validate_desc(d, path);
+  if (rc != FRNN_OK) return rc;
+  const size_t need = kErrBytes + rec_scratch_bytes(d->B, d->N, d->D, d->cell, d->in_dtype == FRNN_F32, path);
+  if (need > kScratchBytes) return FRNN_EWORKSPACE;
+  DevInfo di;
+  const int drc = get_devinfo(&di);
+  if (drc != FRNN_OK) return drc;
+  // frnn_fwd on the array: it clears the error word and fills the exchange words at the start of
+  // the call, so nothing of an earlier call's contents is read
+  return frnn_fwd(d, path, Wx, R, b, states0, states, last_states, di.scratch, kScratchBytes, stream);
+}
+
 int frnn_check(const void* workspace, void* stream) {
-  if (!workspace) return FRNN_EINVAL;
+  if (!workspace) {  // the error word of frnn_fwd_noalloc's array on the current device
+    DevInfo di;
+    const int rc = get_devinfo(&di);
+    if (rc != FRNN_OK) return rc;
+    workspace = di.scratch;
+  }
   if (hipStreamSynchronize(reinterpret_cast<hipStream_t>(stream)) != hipSuccess) return FRNN_EHIP;
   int word = 0;
   if (hipMemcpy(&word, workspace, sizeof(int), hipMemcpyDeviceToHost) != hipSuccess) return FRNN_EHIP;

@@ -245,8 +245,26 @@ int frnn_lstm_stack_bwd_workspace_bytes(int L, int dirs, int T, int B, int I, in
                                         size_t* bytes);
 
 /* Waits for `stream`, then reads the device-side error word of the last call that used
- * `workspace` (FRNN_OK, FRNN_ETIMEOUT, FRNN_EPLACEMENT, or FRNN_EHIP if the wait failed). */
+ * `workspace` (FRNN_OK, FRNN_ETIMEOUT, FRNN_EPLACEMENT, or FRNN_EHIP if the wait failed).
+ * workspace == NULL reads the word of frnn_fwd_noalloc's array on the current device. */
 int frnn_check(const void* workspace, void* stream);
+
+/* Bytes of the device array frnn_fwd_noalloc uses as its workspace (one per device). */
+#define FRNN_NOALLOC_SCRATCH_BYTES (8u << 20)
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): frnn_fwd with the workspace replaced by a device array
+ * the library holds, FRNN_NOALLOC_SCRATCH_BYTES per device, until the process ends (frnn_init()
+ * looks its address up once per device). The call allocates nothing and frees nothing; it
+ * returns FRNN_EWORKSPACE when the problem needs more than that (frnn_workspace_bytes says how
+ * much) and FRNN_ENOINIT before frnn_init(). Every call on a device shares that device's array and
+ * clears what it reads (the error word, the exchange words) at its start, so two calls that may
+ * overlap on one device, on any streams, race and must not be made; frnn_check(NULL, stream)
+ * reads the array's error word after the last call.
+ */
+int frnn_fwd_noalloc(const frnn_desc* d, int path, const void* Wx, const void* R, const void* b,
+                     const void* states0, void* states, void* last_states, void* stream);
 
 /* Description of the launch frnn_fwd would make for `d` on `path` (for logs and tests):
  * writes up to `cap` bytes of text into `buf`. Returns FRNN_OK or a negative status. */

@@ -332,3 +332,20 @@ def test_planner_cost_model_and_chunks(lib):
         return float(re.search(r"predicted_us=([0-9.]+)", plan(desc, 1)).group(1))
     assert pred(D(B=16, T=2048, N=1, Dm=768)) > pred(D(B=16, T=1024, N=1, Dm=768))
     assert pred(D(B=64, T=1024, N=1, Dm=768)) > 3.5 * pred(D(B=16, T=1024, N=1, Dm=768))
+
+
+def test_noalloc_entry_refuses_problems_beyond_its_array(lib):
+    """frnn_fwd_noalloc's array holds FRNN_NOALLOC_SCRATCH_BYTES; a larger problem is refused with
+    FRNN_EWORKSPACE before any device call, a fitting one reaches the device lookup."""
+    m = re.search(r"#define FRNN_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", open(HEADER).read())
+    cap = int(m.group(1)) << int(m.group(2))
+    f = lib.frnn_fwd_noalloc
+    p = ctypes.c_void_p(0x100000)
+    big = D(B=64, T=8, N=4, Dm=1024)
+    assert ws_bytes(big, 1)[1] > cap
+    assert f(ctypes.byref(big), 1, p, p, None, None, p, p, None) == EWS
+    small = D(B=16, T=8, N=1, Dm=768)  # the headline shape fits
+    assert ws_bytes(small, 1)[1] <= cap and ws_bytes(small, 0)[1] <= cap
+    assert f(ctypes.byref(D(B=0)), 1, p, p, None, None, p, p, None) == EINVAL
+    if not torch.cuda.is_available():
+        assert f(ctypes.byref(small), 1, p, p, None, None, p, p, None) == header_enum("FRNN_ENODEVICE")
