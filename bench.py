@@ -160,10 +160,11 @@ def measured_copy_gbs(mib: int = 256, reps: int = 10):
     return 2.0 * n * 4 / (best / 1e3) / 1e9
 
 
-def engine_clock_under_load(step, seconds: float = 0.3):
+def engine_clock_under_load(step, seconds: float = 1.5, settle: float = 0.5):
     """The GPU engine clock (MHz) while `step` runs back to back: amd-smi's current graphics clock,
-    sampled every few ms on the host while a queue of calls keeps the device busy (the median of
-    the samples). None when amd-smi's Python module is not usable."""
+    sampled every 20 ms on the host while a queue of `seconds` of calls keeps the device busy,
+    leaving out the first `settle` seconds (the clock ramps up and the firmware's figure lags);
+    the median of the samples. None when amd-smi's Python module is not usable."""
     import threading
 
     import torch
@@ -177,22 +178,25 @@ def engine_clock_under_load(step, seconds: float = 0.3):
     samples, done = [], threading.Event()
 
     def sample():
+        t0 = time.perf_counter()
         while not done.is_set():
             try:
-                samples.append(float(amdsmi.amdsmi_get_clock_info(handle, amdsmi.AmdSmiClkType.GFX)["clk"]))
+                clk = float(amdsmi.amdsmi_get_clock_info(handle, amdsmi.AmdSmiClkType.GFX)["clk"])
+                if time.perf_counter() - t0 >= settle:
+                    samples.append(clk)
             except Exception:
                 pass
-            time.sleep(0.003)
+            time.sleep(0.02)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     step()
     e1.record()
     torch.cuda.synchronize()
     n = max(1, int(seconds / max(e0.elapsed_time(e1) / 1e3, 1e-6)))
-    for _ in range(n):
-        step()
     th = threading.Thread(target=sample)
     th.start()
+    for _ in range(n):
+        step()
     torch.cuda.synchronize()
     done.set()
     th.join()

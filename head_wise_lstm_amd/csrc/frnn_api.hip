@@ -142,6 +142,21 @@ int get_devinfo(DevInfo* out) {
 
 DevInfo default_devinfo() { return DevInfo(); }
 
+// Launch of a persistent kernel whose workgroups wait on each other (bounded waits): every
+// workgroup must be resident at once. The planner keeps the grid within one workgroup per CU; this
+// checks on the host that the kernel's registers and LDS allow that many (hipOccupancy is a host
+// query), then makes a plain launch. The hardware deals workgroups to dies round-robin in a plain
+// launch too (the probe of init_device is one). A cooperative launch is not used: nothing here
+// needs its grid-wide barrier, and every profiled process that made one ended in a segmentation
+// fault inside exit(), after the profiler's own teardown, while processes with plain launches only
+// exited normally.
+int launch_resident(const void* fn, int grid, int threads, size_t lds, void** args, int cus, hipStream_t st) {
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, threads, lds) != hipSuccess) return FRNN_EHIP;
+  if ((long long)per_cu * cus < grid) return FRNN_ENORESIDENT;
+  return hipLaunchKernel(fn, dim3(grid), dim3(threads), args, lds, st) == hipSuccess ? FRNN_OK : FRNN_EHIP;
+}
+
 // ----------------------------------------------------------------------------- kernel tables
 const FusedVariant* find_fused(int cell, int f32, int local, int ncw, int ks, int mtw, int ktw) {
   const FusedTable t = cell == FRNN_CELL_LSTM ? fused_table_lstm()
@@ -200,7 +215,7 @@ int raise_lds_limits() {
     for (int i = 0; i < t.n; ++i) {
       const FusedBwdVariant& v = t.v[i];
       const int U = (v.ncw / v.ks) * v.mtw * 16;
-      if (!raise(reinterpret_cast<const void*>(v.fn), fused_bwd_lds(v.ncw, v.ks, v.ktw, FUSED_DIE_MAX_BR, U).total))
+      if (!raise(reinterpret_cast<const void*>(v.fn), fused_bwd_lds(v.ncw, v.ks, v.mtw, v.ktw, FUSED_DIE_MAX_BR, U).total))
         return FRNN_EHIP;
     }
   }
@@ -332,7 +347,7 @@ int plan_fused(const Problem& p, const DevInfo& di, FusedPlan* out) {
       if (mtw * KT > 64 && force_w != 1) continue;
       // the I/O wave moves at most 64 * epl words of Wx per step (the compute waves store the
       // states themselves in this design)
-      const int epl = fused_epl(true, ncw, p.cell);
+      const int epl = fused_epl(true, ncw, p.cell, 1, mtw);
       const int words_per_row = G * p.D / (p.wx_f32 ? 2 : 4);
       const int br_cap = std::min(16, 64 * epl / words_per_row);
       for (int br = 1; br <= br_cap; ++br) {
@@ -363,7 +378,7 @@ int plan_fused(const Problem& p, const DevInfo& di, FusedPlan* out) {
           const FusedVariant* v = find_fused(p.cell, 0, 0, ncw, ks, mtw, ktw);
           if (!v || BR > fused_max_br(ks, mtw)) continue;
           // the I/O wave moves at most 64 * epl words of Wx and as many output pairs per step
-          const int epl = fused_epl(false, ncw, p.cell);
+          const int epl = fused_epl(false, ncw, p.cell, ks, mtw);
           if (BR * G * u_wg / (p.wx_f32 ? 2 : 4) > 64 * epl || BR * u_wg / 2 > 64 * epl) continue;
           FusedPlan fp;
           fp.v = v; fp.local = 0; fp.W = W; fp.BR = BR; fp.ncw = ncw; fp.ks = ks; fp.mtw = mtw; fp.ktw = ktw;
@@ -559,14 +574,12 @@ int run_recurrence(const Problem& p, int path, int* err, void* scratch, hipStrea
       a.timeout_ticks = (long long)env_int("FRNN_TIMEOUT_MS", 2000) * di.wall_khz;
       a.stall_step = env_int("FRNN_TEST_STALL_STEP", -1);
       void* args[] = {&a};
-      hipError_t e;
       if (fp.local) {
-        e = hipLaunchKernel(fn, dim3(grid), dim3(fused_threads(fp.ncw)), args, fp.lds, st);
+        if (hipLaunchKernel(fn, dim3(grid), dim3(fused_threads(fp.ncw)), args, fp.lds, st) != hipSuccess) return FRNN_EHIP;
       } else {
-        e = hipLaunchCooperativeKernel(fn, dim3(grid), dim3(fused_threads(fp.ncw)), args, (unsigned)fp.lds, st);
-        if (e == hipErrorCooperativeLaunchTooLarge) return FRNN_ENORESIDENT;
+        const int lrc = launch_resident(fn, grid, fused_threads(fp.ncw), fp.lds, args, di.cus, st);
+        if (lrc != FRNN_OK) return lrc;
       }
-      if (e != hipSuccess) return FRNN_EHIP;
     }
     return FRNN_OK;
   }
@@ -741,7 +754,7 @@ int plan_fused_bwd_da(int B, int N, int D, int cell, const DevInfo& di, FusedBwd
         fp.v = v; fp.fn = v->fn; fp.W = W; fp.BR = BR; fp.groups = groups; fp.ncw = ncw; fp.ks = ks; fp.mtw = mtw;
         fp.ktw = ktw; fp.n_xcd = di.n_xcd; fp.slots = per_die * W; fp.grid = fp.slots * di.n_xcd; fp.U = U;
         fp.chunks = chunks; fp.Bc = Bc;
-        fp.lds = (size_t)fused_bwd_lds(ncw, ks, ktw, BR, U).total;
+        fp.lds = (size_t)fused_bwd_lds(ncw, ks, mtw, ktw, BR, U).total;
         best = fp;
         found = true;
         break;
@@ -858,9 +871,8 @@ int run_fused_bwd(int cell, const BwdArgs& a, const FusedBwdPlan& fp, const DevI
     f.timeout_ticks = (long long)env_int("FRNN_TIMEOUT_MS", 2000) * di.wall_khz;
     f.stall_step = env_int("FRNN_TEST_STALL_STEP", -1);
     void* args[] = {&f};
-    const hipError_t e = hipLaunchCooperativeKernel(fn, dim3(grid), dim3(fused_threads(fp.ncw)), args, (unsigned)fp.lds, st);
-    if (e == hipErrorCooperativeLaunchTooLarge) return FRNN_ENORESIDENT;
-    if (e != hipSuccess) return FRNN_EHIP;
+    const int lrc = launch_resident(fn, grid, fused_threads(fp.ncw), fp.lds, args, di.cus, st);
+    if (lrc != FRNN_OK) return lrc;
   }
   if (cell == FRNN_CELL_LSTM) hipLaunchKernelGGL((bwd_post_kernel<CELL_LSTM, false>), dim3(pgrid), dim3(256), 0, st, a, rec, dstate);
   else if (cell == FRNN_CELL_GRU) hipLaunchKernelGGL((bwd_post_kernel<CELL_GRU, false>), dim3(pgrid), dim3(256), 0, st, a, rec, dstate);

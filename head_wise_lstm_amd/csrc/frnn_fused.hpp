@@ -71,11 +71,12 @@ struct FusedArgs {
 
 constexpr int FUSED_IO_STAGES = 4;   // record steps in flight in the backward's I/O wave
 // max 64-bit Wx words (and, in the die-local design, output pairs) one I/O lane moves per step:
-// the die-local design moves few (its workgroups own few units), the single-workgroup design a
+// the die-local design moves few (its workgroups own few units: two words, four where a workgroup
+// owns eight or more tiles, so that four batch rows of fp32 Wx fit), the single-workgroup design a
 // whole head's rows of Wx (an Elman head has a quarter of an LSTM head's). Every slot costs a load
 // per step.
-__host__ __device__ constexpr int fused_epl(bool local, int ncw, int cell) {
-  return !local ? 2 : (cell == CELL_ELMAN ? 2 : (ncw == 4 ? 8 : 4));
+__host__ __device__ constexpr int fused_epl(bool local, int ncw, int cell, int ks, int mtw) {
+  return !local ? ((ncw / ks) * mtw >= 8 ? 4 : 2) : (cell == CELL_ELMAN ? 2 : (ncw == 4 ? 8 : 4));
 }
 
 // Wx steps in flight in the forward's I/O wave: eight where a lane moves at most two words a step
@@ -84,8 +85,8 @@ __host__ __device__ constexpr int fused_epl(bool local, int ncw, int cell) {
 // (A whole bf16 Elman head per workgroup streams Wx through its own LDS ring instead, see
 // FUSED_DMA_STAGES; the register ring of sixteen steps measured 0.317 -> 0.305 us per step there
 // against eight, and remains for fp32 Elman heads.)
-__host__ __device__ constexpr int fused_io_stages(bool local, int ncw, int cell) {
-  return (local && cell == CELL_ELMAN) ? 16 : fused_epl(local, ncw, cell) <= 2 ? 8 : 4;
+__host__ __device__ constexpr int fused_io_stages(bool local, int ncw, int cell, int ks, int mtw) {
+  return (local && cell == CELL_ELMAN) ? 16 : fused_epl(local, ncw, cell, ks, mtw) <= 2 ? 8 : 4;
 }
 
 __host__ __device__ constexpr int fused_hpad(bool f32) { return f32 ? 4 : 8; }
@@ -125,7 +126,12 @@ constexpr int FUSED_DIE_MAX_BR = 4;
 __host__ __device__ constexpr int fused_brp(int ks, int mtw) {
   return (ks * 4 <= 16 && mtw * 4 <= 16) ? 4 : (ks * 2 <= 16 && mtw * 2 <= 16) ? 2 : 1;
 }
-constexpr int FUSED_PART_ROW = 65;  // f32x4 entries per wave's packed partials (one of padding)
+// f32x4 entries per wave's row of packed partials: 64 and BRP of padding. The gather that follows
+// the barrier reads, for 16-lane row c = k2 * BRP + cc, entry k2 * row + cc: with a row of 64 + BRP
+// entries that is 64 k2 + c, so consecutive lanes read consecutive 16-byte entries modulo the 256
+// words of a full row set and no two lanes of a read share a bank (with 65 entries lanes
+// (k2, cc + 1) and (k2 + 1, cc) met on one bank when BRP = 2).
+__host__ __device__ constexpr int fused_part_row(int ks, int mtw) { return 64 + fused_brp(ks, mtw); }
 // Most batch rows per group a die-local design takes.
 __host__ __device__ constexpr int fused_max_br(int ks, int mtw) {
   return ks > 1 ? (fused_brp(ks, mtw) < FUSED_DIE_MAX_BR ? fused_brp(ks, mtw) : FUSED_DIE_MAX_BR) : FUSED_DIE_MAX_BR;
@@ -151,7 +157,7 @@ __host__ __device__ inline FusedLds fused_lds(bool local, bool f32, int ncw, int
   // LOCAL: the h buffer; die-local: each compute wave's poll stage, 16 rows
   const int hbytes = local ? 2 * 16 * (D + fused_hpad(f32)) * (f32 ? 4 : 2) : ncw * 16 * fused_stage_row(ktw) * 4;
   L.part = (hbytes + 15) & ~15;
-  const int pbytes = (!local && ks > 1) ? 2 * ncw * FUSED_PART_ROW * 16 : 0;
+  const int pbytes = (!local && ks > 1) ? 2 * ncw * fused_part_row(ks, mtw) * 16 : 0;
   L.wx = L.part + pbytes;
   L.out = L.wx + 2 * ncw * gt * 1024;
   L.dma = L.out + 2 * ncw * gt * 1024;
@@ -647,7 +653,7 @@ __global__ void __launch_bounds__((NCW + 1) * 64, 1) fused_fwd_kernel(FusedArgs 
     c.U_wg = U_wg;
     c.u_base = u_base;
     c.lane = lane;
-    io_wave<CELL, NCW, KS, MTW, fused_epl(LOCAL, NCW, CELL), G0, fused_io_stages(LOCAL, NCW, CELL)>(c, wxs, outs, &s_abort);
+    io_wave<CELL, NCW, KS, MTW, fused_epl(LOCAL, NCW, CELL, KS, MTW), G0, fused_io_stages(LOCAL, NCW, CELL, KS, MTW)>(c, wxs, outs, &s_abort);
     return;
   }
 
@@ -812,10 +818,11 @@ __global__ void __launch_bounds__((NCW + 1) * 64, 1) fused_fwd_kernel(FusedArgs 
       // after the barrier one read gathers, for each tile this wave gates, the KS partials of
       // its columns (source k2, column c at row position k2*BRP + c), and row_reduce adds them
       constexpr int BRP = fused_brp(KS, MTW);
+      constexpr int PROW = fused_part_row(KS, MTW);
       const int pp = t & 1;
       f32x4_t P = acc[0];
       pack_tiles<BRP, 1, MTW>(P, acc);
-      part[(pp * NCW + wave) * FUSED_PART_ROW + lane] = P;
+      part[(pp * NCW + wave) * PROW + lane] = P;
       block_barrier();
       // the reads go out before the abort flag is looked at (they are harmless if it is set)
 #pragma unroll
@@ -827,7 +834,7 @@ __global__ void __launch_bounds__((NCW + 1) * 64, 1) fused_fwd_kernel(FusedArgs 
         const int tq = wave + NCW * q;
         const int msq = tq / MTW, jq = tq - msq * MTW;
         if (gval[q] && k2 < KS)
-          pre[q] = part[(pp * NCW + msq * KS + k2) * FUSED_PART_ROW + quad * 16 + jq * BRP + cc];
+          pre[q] = part[(pp * NCW + msq * KS + k2) * PROW + quad * 16 + jq * BRP + cc];
       }
       if (uniform_flag(s_abort)) return;
 #pragma unroll

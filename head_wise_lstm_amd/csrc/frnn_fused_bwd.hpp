@@ -53,12 +53,12 @@ struct FusedBwdLds {
   int stage, part, rin, rout, total;
 };
 
-__host__ __device__ inline FusedBwdLds fused_bwd_lds(int ncw, int ks, int ktw, int BR, int U) {
+__host__ __device__ inline FusedBwdLds fused_bwd_lds(int ncw, int ks, int mtw, int ktw, int BR, int U) {
   FusedBwdLds L;
   L.stage = 0;
   const int sbytes = ncw * 16 * fused_stage_row(ktw) * 4;
   L.part = (sbytes + 15) & ~15;
-  const int pbytes = ks > 1 ? 2 * ncw * FUSED_PART_ROW * 16 : 0;
+  const int pbytes = ks > 1 ? 2 * ncw * fused_part_row(ks, mtw) * 16 : 0;
   L.rin = L.part + pbytes;
   L.rout = L.rin + 2 * BR * U * BWD_REC * 4;
   L.total = L.rout + 2 * BR * U * 2 * 4;
@@ -201,7 +201,7 @@ __global__ void __launch_bounds__((NCW + 1) * 64, 1) fused_bwd_kernel(FusedBwdAr
   const int tile0 = w * MT_WG;
   const int u_base = tile0 * 16;
   const int U = MT_WG * 16;  // units of this workgroup (the planner divides the head evenly)
-  const FusedBwdLds lay = fused_bwd_lds(NCW, KS, KTW, a.BR, U);
+  const FusedBwdLds lay = fused_bwd_lds(NCW, KS, MTW, KTW, a.BR, U);
   constexpr int SROW = fused_stage_row(KTW);
   f32x4_t* part = reinterpret_cast<f32x4_t*>(smem + lay.part);
   float* rin = reinterpret_cast<float*>(smem + lay.rin);
@@ -315,7 +315,7 @@ __global__ void __launch_bounds__((NCW + 1) * 64, 1) fused_bwd_kernel(FusedBwdAr
       const int pp = s & 1;
       f32x4_t P = acc[0];
       pack_tiles<BRP, 1, MTW>(P, acc);
-      part[(pp * NCW + wave) * FUSED_PART_ROW + lane] = P;
+      part[(pp * NCW + wave) * fused_part_row(KS, MTW) + lane] = P;
       block_barrier();
       const int k2 = col / BRP, cc = col - k2 * BRP;
 #pragma unroll
@@ -324,7 +324,7 @@ __global__ void __launch_bounds__((NCW + 1) * 64, 1) fused_bwd_kernel(FusedBwdAr
         const int tq = wave + NCW * q;
         const int msq = tq / MTW, jq = tq - msq * MTW;
         if (gval[q] && k2 < KS)
-          pre[q] = part[(pp * NCW + msq * KS + k2) * FUSED_PART_ROW + quad * 16 + jq * BRP + cc];
+          pre[q] = part[(pp * NCW + msq * KS + k2) * fused_part_row(KS, MTW) + quad * 16 + jq * BRP + cc];
       }
       if (uniform_flag(s_abort)) return;
 #pragma unroll

@@ -32,7 +32,7 @@ struct FusedTable {
   X(false, false, 4, 2, 2, 2) X(false, false, 4, 1, 1, 1) X(false, false, 4, 1, 1, 2)              \
   X(false, false, 8, 8, 6, 3) X(false, false, 8, 8, 4, 2) X(false, false, 8, 8, 2, 1)              \
   X(false, false, 6, 6, 6, 4) X(false, false, 4, 4, 6, 6) X(false, false, 8, 8, 8, 2)              \
-  X(false, false, 4, 4, 8, 4) X(false, false, 8, 8, 4, 1)                                          \
+  X(false, false, 4, 4, 8, 4) X(false, false, 8, 8, 4, 1) X(false, false, 8, 4, 4, 4)              \
   /* single-workgroup design (bf16) */                                                             \
   X(false, true, 4, 1, 1, 1) X(false, true, 4, 1, 2, 1) X(false, true, 4, 1, 1, 2)                 \
   X(false, true, 4, 1, 4, 2) X(false, true, 4, 1, 6, 3) X(false, true, 4, 1, 2, 4)                 \

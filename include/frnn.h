@@ -79,8 +79,9 @@ enum { FRNN_F32 = 0, FRNN_BF16 = 1 };
  * gfx950):
  *  ALTERNATING: per step, one MFMA kernel computes h.R for every head and one coalesced
  *               pointwise kernel applies the gates; 2*T launches on `stream`.
- *  FUSED:       one persistent cooperative launch; R stays in registers for all T steps; the
- *               workgroups sharing a head exchange h through the die-local L2 every step. */
+ *  FUSED:       one persistent launch (all workgroups resident at once); R stays in registers
+ *               for all T steps; the workgroups sharing a head exchange h through the die-local
+ *               L2 every step. */
 enum { FRNN_PATH_ALTERNATING = 0, FRNN_PATH_FUSED = 1 };
 
 /* Problem description for frnn_fwd and frnn_bwd. G and S follow from `cell` (LSTM: 4, 2;
@@ -167,7 +168,7 @@ int frnn_fwd(const frnn_desc* d, int path, const void* Wx, const void* R, const 
  * with one MFMA GEMM per head and end with one GEMM per head that forms dR and db; they differ in
  * the serial part, t = T-1 .. 0:
  *   FRNN_PATH_ALTERNATING: per step, a pointwise kernel and an MFMA kernel (2*T launches);
- *   FRNN_PATH_FUSED: one persistent cooperative launch (bf16 inputs), in which the workgroups of
+ *   FRNN_PATH_FUSED: one persistent launch (bf16 inputs), in which the workgroups of
  *     a head exchange the gradient reaching h through R every step, the forward's die-local
  *     design with h and R^T exchanged. Shapes this build has no fused design for return
  *     FRNN_EUNSUPPORTED (frnn_bwd_plan_str says which design a shape gets).

@@ -132,7 +132,7 @@ FORCED = [
     (fi.HeadwiseWorkload("lstm_D512_W16_4waves", "lstm", torch.bfloat16, B=3, T=6, N=1, D=512, seed=127, s0_var=1.0),
      {"FRNN_FUSED_W": 16, "FRNN_FUSED_NCW": 4, "FRNN_FUSED_BR": 2}),
     (fi.HeadwiseWorkload("lstm_D512_W16_8waves", "lstm", torch.bfloat16, B=5, T=5, N=1, D=512, seed=128, s0_var=1.0),
-     {"FRNN_FUSED_W": 16, "FRNN_FUSED_NCW": 8, "FRNN_FUSED_BR": 2}),
+     {"FRNN_FUSED_W": 16, "FRNN_FUSED_NCW": 8, "FRNN_FUSED_KS": 8, "FRNN_FUSED_BR": 2}),
     (fi.HeadwiseWorkload("lstm_D256_W16_8waves", "lstm", torch.bfloat16, B=5, T=7, N=2, D=256, seed=129, s0_var=1.0),
      {"FRNN_FUSED_W": 16, "FRNN_FUSED_NCW": 8, "FRNN_FUSED_BR": 2}),
     (fi.HeadwiseWorkload("gru_forced_W4", "gru", torch.bfloat16, B=7, T=9, N=3, D=64, seed=130, s0_var=1.0),
@@ -143,6 +143,11 @@ FORCED = [
      {"FRNN_FUSED_NCW": 6, "FRNN_FUSED_BR": 2}),
     (fi.HeadwiseWorkload("gru_D512_W16_4waves", "gru", torch.bfloat16, B=3, T=6, N=1, D=512, seed=134, s0_var=1.0),
      {"FRNN_FUSED_W": 16, "FRNN_FUSED_NCW": 4, "FRNN_FUSED_BR": 2}),
+    # eight compute waves over a four-way K split (two waves per K range): four rows per group
+    (fi.HeadwiseWorkload("lstm_D512_W16_8waves_KS4", "lstm", torch.bfloat16, B=7, T=6, N=2, D=512, seed=135,
+                         s0_var=1.0), {"FRNN_FUSED_W": 16, "FRNN_FUSED_NCW": 8, "FRNN_FUSED_KS": 4, "FRNN_FUSED_BR": 4}),
+    (fi.HeadwiseWorkload("gru_D512_W16_8waves_KS4", "gru", torch.bfloat16, B=5, T=6, N=1, D=512, seed=136,
+                         s0_var=1.0), {"FRNN_FUSED_W": 16, "FRNN_FUSED_NCW": 8, "FRNN_FUSED_KS": 4, "FRNN_FUSED_BR": 4}),
 ]
 
 # the design each forced case must get (compute waves, K split, tiles and k-tiles per wave)
@@ -155,6 +160,8 @@ FORCED_PLAN = {
     "gru_D768_8waves": "NCW=8 KS=8 MTW=6 KTW=3",
     "gru_D768_6waves": "NCW=6 KS=6 MTW=6 KTW=4",
     "gru_D512_W16_4waves": "NCW=4 KS=4 MTW=8 KTW=4",
+    "lstm_D512_W16_8waves_KS4": "NCW=8 KS=4 MTW=4 KTW=4",
+    "gru_D512_W16_8waves_KS4": "NCW=8 KS=4 MTW=4 KTW=4",
 }
 
 
