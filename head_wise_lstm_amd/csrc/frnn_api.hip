@@ -60,6 +60,7 @@ __global__ void xcc_map_kernel(int* out) {
 
 constexpr size_t kErrBytes = 256;
 constexpr int kMaxDies = 8;
+constexpr size_t kCtrBytes = 256;  // per-die workgroup counters after a launch's exchange words
 
 // The workspace of frnn_fwd_noalloc: one array per device, held until the process ends. Host code
 // never uses this name as an address (on the host it is a stand-in); init_device() looks up the
@@ -401,8 +402,8 @@ size_t rec_scratch_bytes(int B, int N, int D, int cell, int r_f32, int path) {
   const size_t elt = r_f32 ? 4 : 2;
   size_t s = align256((size_t)GS * N * D * D * elt);  // packed R
   if (path == FRNN_PATH_FUSED) {
-    // exchange words: groups * BR <= N * (B + 15) rows, two parities
-    return s + align256((size_t)2 * N * (B + 15) * D * 4);
+    // exchange words: groups * BR <= N * (B + 15) rows, two parities; the per-die counters
+    return s + align256((size_t)2 * N * (B + 15) * D * 4) + kCtrBytes;
   }
   s += align256((size_t)B * N * D * GS * 4);   // h.R
   s += align256((size_t)N * B * D * elt);      // current h
@@ -545,14 +546,15 @@ int run_recurrence(const Problem& p, int path, int* err, void* scratch, hipStrea
       int grid = groups;
       if (!fp.local) grid = ((groups + fp.n_xcd - 1) / fp.n_xcd) * fp.W * fp.n_xcd;
       // exchange words start with tag 0xFFFF, which no step before 65535 polls for (by then
-      // every word has been overwritten)
+      // every word has been overwritten); the per-die counters after them start at 0xFFFF too
       const size_t xbytes = fp.local ? 0 : (size_t)groups * 2 * fp.BR * p.D * 4;
-      if (launch_fill(xw, xbytes, st, 0xFFFFu) != hipSuccess) return FRNN_EHIP;
+      if (!fp.local && launch_fill(xw, xbytes + kCtrBytes, st, 0xFFFFu) != hipSuccess) return FRNN_EHIP;
       FusedArgs a;
       std::memset(&a, 0, sizeof(a));
       a.B = Bch; a.T = p.T; a.N = p.N; a.D = p.D;
       a.BR = fp.BR; a.groups = groups; a.W = fp.W; a.n_xcd = fp.n_xcd;
-      a.check_xcc = fp.local ? 0 : 1;
+      a.slots = fp.local ? 0 : grid / fp.n_xcd;
+      a.ctr = reinterpret_cast<uint32_t*>(xw + xbytes);
       a.xcc_of = 0;
       for (int d = 0; d < kMaxDies; ++d) a.xcc_of |= (uint32_t)(di.xcc_of[d] & 0xF) << (4 * d);
       a.Wx = reinterpret_cast<const char*>(p.Wx) + (long long)b0 * p.wx_sb * (long long)wx_elt;
@@ -789,7 +791,7 @@ BwdLayout bwd_layout(int B, int T, int N, int D, int cell, int f32, int path) {
     // exchange words: groups * BR <= N * (B + 3) rows (BR <= 4), two parities, G*D words a row
     // (da design) or W*D words a row (partial-sum design, W <= BWDX_MAX_W)
     L.xbuf = q;
-    q += align256((size_t)2 * N * (B + FUSED_DIE_MAX_BR - 1) * std::max<size_t>(G, BWDX_MAX_W) * D * 4);
+    q += align256((size_t)2 * N * (B + FUSED_DIE_MAX_BR - 1) * std::max<size_t>(G, BWDX_MAX_W) * D * 4) + kCtrBytes;
   }
   L.total = q;
   return L;
@@ -856,11 +858,12 @@ int run_fused_bwd(int cell, const BwdArgs& a, const FusedBwdPlan& fp, const DevI
     const int groups = a.N * ((Bch + fp.BR - 1) / fp.BR);
     const int grid = ((groups + fp.n_xcd - 1) / fp.n_xcd) * fp.W * fp.n_xcd;
     const size_t xbytes = (size_t)groups * 2 * fp.BR * (fp.px ? fp.W : gates_of(cell)) * a.D * 4;
-    if (launch_fill(base + L.xbuf, xbytes, st, 0xFFFFu) != hipSuccess) return FRNN_EHIP;
+    if (launch_fill(base + L.xbuf, xbytes + kCtrBytes, st, 0xFFFFu) != hipSuccess) return FRNN_EHIP;
     FusedBwdArgs f;
     std::memset(&f, 0, sizeof(f));
     f.B = Bch; f.Bs = a.B; f.T = a.T; f.N = a.N; f.D = a.D;
-    f.BR = fp.BR; f.groups = groups; f.W = fp.W; f.n_xcd = fp.n_xcd; f.check_xcc = 1;
+    f.BR = fp.BR; f.groups = groups; f.W = fp.W; f.n_xcd = fp.n_xcd; f.slots = grid / fp.n_xcd;
+    f.ctr = reinterpret_cast<uint32_t*>(base + L.xbuf + xbytes);
     f.xcc_of = 0;
     for (int k = 0; k < kMaxDies; ++k) f.xcc_of |= (uint32_t)(di.xcc_of[k] & 0xF) << (4 * k);
     f.rpk = a.rpk;

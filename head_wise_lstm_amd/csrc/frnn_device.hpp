@@ -53,6 +53,32 @@ __device__ __forceinline__ int xcc_id() {
   return (int)(__builtin_amdgcn_s_getreg((20) | (0 << 6) | (15 << 11)) & 0xFu);
 }
 
+// Position of this workgroup in a die-local launch, as (slot * n_xcd + die): the die is the index in
+// xcc_of (four bits per die) of the hardware XCC the workgroup runs on, the slot its rank among the
+// launch's workgroups on that die, drawn from the die's counter in ctr (which the host fills with
+// 0xFFFF before the launch). Groups are then formed from the workgroups that really share a die,
+// whatever order the hardware deals them in. -1 (after recording a placement error) for an XCC
+// missing from xcc_of or a die that received more than `slots` workgroups. Every thread of the
+// workgroup calls it: it contains a workgroup barrier.
+__device__ __forceinline__ int die_position(uint32_t xcc_of, int n_xcd, uint32_t* ctr, int slots, int* err) {
+  __shared__ int s_pos;
+  if (threadIdx.x == 0) {
+    const int x = xcc_id();
+    int d = -1;
+    for (int k = 0; k < n_xcd; ++k)
+      if ((int)((xcc_of >> (4 * k)) & 0xFu) == x) d = k;
+    int pos = -1;
+    if (d >= 0) {
+      const int s = (int)(atomicAdd(ctr + d, 1u) - 0xFFFFu);
+      if (s >= 0 && s < slots) pos = s * n_xcd + d;
+    }
+    if (pos < 0) atomicOr(err, DEVERR_PLACEMENT);
+    s_pos = pos;
+  }
+  __syncthreads();
+  return s_pos;
+}
+
 // Pack the high halves of two 32-bit exchange words (bf16 << 16 | tag) into one bf16 pair.
 __device__ __forceinline__ uint32_t pack_hi(uint32_t lo_word, uint32_t hi_word) {
   return __builtin_amdgcn_perm(hi_word, lo_word, 0x07060302u);

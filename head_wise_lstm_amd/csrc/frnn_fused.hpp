@@ -42,9 +42,10 @@ struct FusedArgs {
   int BR;       // batch rows per group (1..16)
   int groups;   // N * ceil(B / BR)
   int W;        // workgroups per group (1 for the LDS-local design)
-  int n_xcd;    // dies the grid is spread over: workgroup index = slot * n_xcd + die
-  int check_xcc;
-  uint32_t xcc_of;  // expected hardware XCC id of die slot d in bits [4d, 4d+4)
+  int n_xcd;    // dies the grid is spread over (die-local design: slots workgroups on each)
+  int slots;
+  uint32_t xcc_of;  // hardware XCC id of die d in bits [4d, 4d+4)
+  uint32_t* ctr;    // per-die workgroup counters (filled with 0xFFFF before the launch)
   const void* Wx;
   int wx_f32;
   long long wx_sb, wx_st;  // element strides of Wx for b and t; [G][N][D] packed inside
@@ -563,14 +564,12 @@ __global__ void __launch_bounds__((NCW + 1) * 64, 1) fused_fwd_kernel(FusedArgs 
     group = blockIdx.x;
     w = 0;
   } else {
-    const int die = blockIdx.x % a.n_xcd, slot = blockIdx.x / a.n_xcd;
+    // the group is formed from the workgroups that landed on one die (see die_position)
+    const int pos = die_position(a.xcc_of, a.n_xcd, a.ctr, a.slots, a.err);
+    if (pos < 0) return;
+    const int die = pos % a.n_xcd, slot = pos / a.n_xcd;
     group = (slot / a.W) * a.n_xcd + die;
     w = slot % a.W;
-    if (group >= a.groups) return;
-    if (a.check_xcc && xcc_id() != (int)((a.xcc_of >> (4 * die)) & 0xFu)) {
-      if (threadIdx.x == 0) atomicOr(a.err, DEVERR_PLACEMENT);
-      return;
-    }
   }
   if (group >= a.groups) return;
   if (threadIdx.x == 0) s_abort = 0;

@@ -38,8 +38,9 @@ constexpr int BWD_EPL_OUT = 2;  // 64-bit (dh, dc) words one I/O lane moves per 
 struct FusedBwdArgs {
   int B, T, N, D;    // B: the rows of this launch (a chunk of the batch)
   int Bs;            // rows of the record and output arrays (their step stride)
-  int BR, groups, W, n_xcd, check_xcc;
-  uint32_t xcc_of;
+  int BR, groups, W, n_xcd, slots;  // slots: workgroups on each of the n_xcd dies
+  uint32_t xcc_of;   // hardware XCC id of die d in bits [4d, 4d+4)
+  uint32_t* ctr;     // per-die workgroup counters (filled with 0xFFFF before the launch)
   const void* rpk;   // R as A fragments: [N][D/16][G*D/32][64] x 8 bf16 (bwd_rpack_kernel)
   const float* rec;  // [T][B][N][D][BWD_REC], indexed by the kernel step s
   float* dstate;     // [T][B][N][D][2]: (dh, dc) of kernel step s
@@ -185,14 +186,13 @@ __global__ void __launch_bounds__((NCW + 1) * 64, 1) fused_bwd_kernel(FusedBwdAr
   const int TPH = D / 16;     // row tiles of a head
   const int KT = GD / 32;     // k-tiles of a head
 
-  const int die = blockIdx.x % a.n_xcd, slot = blockIdx.x / a.n_xcd;
+  // the group is formed from the workgroups that landed on one die (see die_position)
+  const int pos = die_position(a.xcc_of, a.n_xcd, a.ctr, a.slots, a.err);
+  if (pos < 0) return;
+  const int die = pos % a.n_xcd, slot = pos / a.n_xcd;
   const int group = (slot / a.W) * a.n_xcd + die;
   const int w = slot % a.W;
   if (group >= a.groups) return;
-  if (a.check_xcc && xcc_id() != (int)((a.xcc_of >> (4 * die)) & 0xFu)) {
-    if (threadIdx.x == 0) atomicOr(a.err, DEVERR_PLACEMENT);
-    return;
-  }
   if (threadIdx.x == 0) s_abort = 0;
 
   const int n = group % N, bblk = group / N;
@@ -496,14 +496,13 @@ __global__ void __launch_bounds__((NCW + 1) * 64, 1) fused_bwdx_kernel(FusedBwdA
   const int KT = GD / 32;
   const int UW = D / W;
 
-  const int die = blockIdx.x % a.n_xcd, slot = blockIdx.x / a.n_xcd;
+  // the group is formed from the workgroups that landed on one die (see die_position)
+  const int pos = die_position(a.xcc_of, a.n_xcd, a.ctr, a.slots, a.err);
+  if (pos < 0) return;
+  const int die = pos % a.n_xcd, slot = pos / a.n_xcd;
   const int group = (slot / W) * a.n_xcd + die;
   const int w = slot % W;
   if (group >= a.groups) return;
-  if (a.check_xcc && xcc_id() != (int)((a.xcc_of >> (4 * die)) & 0xFu)) {
-    if (threadIdx.x == 0) atomicOr(a.err, DEVERR_PLACEMENT);
-    return;
-  }
   if (threadIdx.x == 0) s_abort = 0;
 
   const int n = group % N, bblk = group / N;
