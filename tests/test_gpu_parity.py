@@ -73,7 +73,10 @@ def run_case(w, path, pairs=None, env=None):
     assert np.all(np.isfinite(got_s))
     err = np.abs(got_s - ref_s).max() if got_s.size else 0.0
     err_last = np.abs(gl_s - rl_s).max()
-    _log(f"  max|err| states={err:.3e} last={err_last:.3e}")
+    sax = 0 if pairs is None else 1  # the state axis (h, c)
+    err_h = np.abs(np.take(got_s, 0, sax) - np.take(ref_s, 0, sax)).max() if got_s.size else 0.0
+    err_c = np.abs(np.take(got_s, 1, sax) - np.take(ref_s, 1, sax)).max() if got_s.size and w.S == 2 else 0.0
+    _log(f"  max|err| states={err:.3e} (h {err_h:.3e}, c {err_c:.3e}) last={err_last:.3e}")
     tol = TOL[w.dtype]
     assert err <= tol, f"states max abs err {err} > {tol}"
     assert err_last <= tol
