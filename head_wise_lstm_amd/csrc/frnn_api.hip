@@ -638,7 +638,8 @@ struct BwdLayout {
 struct FusedBwdPlan {
   const FusedBwdVariant* v = nullptr;
   int px = 0;                  // 1: the partial-sum design (fused_bwdx_kernel), 0: the da exchange
-  fused_bwd_fn fn = nullptr;   // the kernel of either design
+  int local = 0;               // 1: the single-workgroup fp32 design (fused_bwd_local_kernel)
+  fused_bwd_fn fn = nullptr;   // the kernel of the design
   int W = 0, BR = 0, groups = 0, ncw = 0, ks = 0, mtw = 0, ktw = 0, n_xcd = 1, slots = 0, grid = 0, U = 0;
   int chunks = 1, Bc = 0;  // the batch runs as `chunks` launches of at most Bc rows
   size_t lds = 0;
@@ -700,8 +701,32 @@ int plan_fused_bwd_da(int B, int N, int D, int cell, const DevInfo& di, FusedBwd
 
 // The partial-sum design where it has a plan with no more launches than the da design, else the
 // da design. FRNN_FUSED_BWD_DESIGN=da / px pins one.
+// fp32 operands: the single-workgroup design, a head and BR batch rows per workgroup (as many rows
+// as the I/O wave's limits allow), the batch in chunks when the groups exceed the CUs.
+int plan_fused_bwd_local(int B, int N, int D, int cell, const DevInfo& di, FusedBwdPlan* out) {
+  const fused_bwd_fn fn = cell == FRNN_CELL_LSTM ? fused_bwd_local_lstm(D)
+                          : cell == FRNN_CELL_GRU ? fused_bwd_local_gru(D)
+                                                  : fused_bwd_local_elman(D);
+  if (!fn || D / 16 > BWDL_NCW) return FRNN_EUNSUPPORTED;
+  const int G = gates_of(cell);
+  FusedBwdPlan fp;
+  fp.local = 1; fp.fn = fn; fp.W = 1; fp.ncw = BWDL_NCW; fp.ks = 1; fp.mtw = 1; fp.ktw = G * D / 4;
+  fp.BR = std::max(1, std::min(B, fused_bwdl_max_br(D)));
+  const long long bmax = (long long)fp.BR * std::max(1, di.cus / N);
+  if (di.cus < N) return FRNN_EUNSUPPORTED;
+  fp.chunks = (int)((B + bmax - 1) / bmax);
+  fp.Bc = (B + fp.chunks - 1) / fp.chunks;
+  fp.groups = N * ((fp.Bc + fp.BR - 1) / fp.BR);
+  fp.grid = fp.groups;
+  fp.n_xcd = 1; fp.U = D;
+  fp.lds = (size_t)fused_bwdl_lds(G, D, fp.BR).total;
+  *out = fp;
+  return FRNN_OK;
+}
+
 int plan_fused_bwd(int B, int N, int D, int cell, int f32, const DevInfo& di, FusedBwdPlan* out) {
-  if (f32 || !di.periodic || D % 32 != 0) return FRNN_EUNSUPPORTED;
+  if (f32) return plan_fused_bwd_local(B, N, D, cell, di, out);
+  if (!di.periodic || D % 32 != 0) return FRNN_EUNSUPPORTED;
   const int design = env_int("FRNN_FUSED_BWD_PX", -1);  // 1: partial sums only, 0: da exchange only
   FusedBwdPlan px, da;
   const bool has_px = design != 0 && plan_fused_bwdx(B, N, D, cell, di, &px);
@@ -801,9 +826,10 @@ std::string bwd_plan_string(const frnn_desc* d, int path, const FusedBwdPlan* fp
   char buf[512];
   if (path == FRNN_PATH_FUSED && fp) {
     std::snprintf(buf, sizeof(buf),
-                  "backward path=fused design=%s cell=%s dtype=bf16 B=%d T=%d N=%d D=%d BR=%d groups=%d W=%d "
+                  "backward path=fused design=%s cell=%s dtype=%s B=%d T=%d N=%d D=%d BR=%d groups=%d W=%d "
                   "NCW=%d KS=%d MTW=%d KTW=%d dies=%d slots/die=%d grid=%d lds=%zu chunks=%d rows/chunk=%d",
-                  fp->px ? "die-local-partials" : "die-local", cell_name(d->cell), d->B, d->T, d->N, d->D, fp->BR, fp->groups, fp->W, fp->ncw, fp->ks, fp->mtw,
+                  fp->local ? "workgroup-local" : fp->px ? "die-local-partials" : "die-local", cell_name(d->cell),
+                  d->in_dtype == FRNN_F32 ? "f32" : "bf16", d->B, d->T, d->N, d->D, fp->BR, fp->groups, fp->W, fp->ncw, fp->ks, fp->mtw,
                   fp->ktw, fp->n_xcd, fp->slots, fp->grid, fp->lds, fp->chunks, fp->Bc);
     return std::string(buf);
   }
@@ -850,12 +876,27 @@ int run_fused_bwd(int cell, const BwdArgs& a, const FusedBwdPlan& fp, const DevI
   const unsigned pgrid = (unsigned)((total + 255) / 256);
   float* rec = reinterpret_cast<float*>(base + L.rec);
   float* dstate = reinterpret_cast<float*>(base + L.dstate);
-  launch_bwd_cell_kernel(kBwdRecord, cell, false, a.wx_f32, dim3(pgrid), dim3(256), st, a, 0, rec);
+  const bool f32 = a.f32 != 0;
+  launch_bwd_cell_kernel(kBwdRecord, cell, f32, a.wx_f32, dim3(pgrid), dim3(256), st, a, 0, rec);
   const void* fn = reinterpret_cast<const void*>(fp.fn);
   // the batch in chunks of at most Bc rows, one launch each (rows never interact)
   for (int b0 = 0; b0 < a.B; b0 += fp.Bc) {
     const int Bch = std::min(fp.Bc, a.B - b0);
     const int groups = a.N * ((Bch + fp.BR - 1) / fp.BR);
+    if (fp.local) {  // single-workgroup design: a workgroup per group, no exchange, no placement
+      FusedBwdArgs f;
+      std::memset(&f, 0, sizeof(f));
+      f.B = Bch; f.Bs = a.B; f.T = a.T; f.N = a.N; f.D = a.D;
+      f.BR = fp.BR; f.groups = groups; f.W = 1; f.n_xcd = 1;
+      f.rpk = a.rpk;
+      f.rec = rec + (size_t)b0 * a.N * a.D * BWD_REC;
+      f.dstate = dstate + (size_t)b0 * a.N * a.D * 2;
+      f.err = reinterpret_cast<int*>(base - kErrBytes);
+      f.stall_step = -1;
+      void* args[] = {&f};
+      if (hipLaunchKernel(fn, dim3(groups), dim3((BWDL_NCW + 1) * 64), args, fp.lds, st) != hipSuccess) return FRNN_EHIP;
+      continue;
+    }
     const int grid = ((groups + fp.n_xcd - 1) / fp.n_xcd) * fp.W * fp.n_xcd;
     const size_t xbytes = (size_t)groups * 2 * fp.BR * (fp.px ? fp.W : gates_of(cell)) * a.D * 4;
     if (launch_fill(base + L.xbuf, xbytes + kCtrBytes, st, 0xFFFFu) != hipSuccess) return FRNN_EHIP;
@@ -877,9 +918,15 @@ int run_fused_bwd(int cell, const BwdArgs& a, const FusedBwdPlan& fp, const DevI
     const int lrc = launch_resident(fn, grid, fused_threads(fp.ncw), fp.lds, args, di.cus, st);
     if (lrc != FRNN_OK) return lrc;
   }
-  if (cell == FRNN_CELL_LSTM) hipLaunchKernelGGL((bwd_post_kernel<CELL_LSTM, false>), dim3(pgrid), dim3(256), 0, st, a, rec, dstate);
-  else if (cell == FRNN_CELL_GRU) hipLaunchKernelGGL((bwd_post_kernel<CELL_GRU, false>), dim3(pgrid), dim3(256), 0, st, a, rec, dstate);
-  else hipLaunchKernelGGL((bwd_post_kernel<CELL_ELMAN, false>), dim3(pgrid), dim3(256), 0, st, a, rec, dstate);
+  if (f32) {
+    if (cell == FRNN_CELL_LSTM) hipLaunchKernelGGL((bwd_post_kernel<CELL_LSTM, true>), dim3(pgrid), dim3(256), 0, st, a, rec, dstate);
+    else if (cell == FRNN_CELL_GRU) hipLaunchKernelGGL((bwd_post_kernel<CELL_GRU, true>), dim3(pgrid), dim3(256), 0, st, a, rec, dstate);
+    else hipLaunchKernelGGL((bwd_post_kernel<CELL_ELMAN, true>), dim3(pgrid), dim3(256), 0, st, a, rec, dstate);
+  } else {
+    if (cell == FRNN_CELL_LSTM) hipLaunchKernelGGL((bwd_post_kernel<CELL_LSTM, false>), dim3(pgrid), dim3(256), 0, st, a, rec, dstate);
+    else if (cell == FRNN_CELL_GRU) hipLaunchKernelGGL((bwd_post_kernel<CELL_GRU, false>), dim3(pgrid), dim3(256), 0, st, a, rec, dstate);
+    else hipLaunchKernelGGL((bwd_post_kernel<CELL_ELMAN, false>), dim3(pgrid), dim3(256), 0, st, a, rec, dstate);
+  }
   return hipGetLastError() == hipSuccess ? FRNN_OK : FRNN_EHIP;
 }
 
@@ -983,7 +1030,8 @@ int run_backward(const BwdProblem& q, int path, const FusedBwdPlan& fbp, const D
     rc = run_fused_bwd(q.cell, a, fbp, di, base, L, st);
     if (rc != FRNN_OK) return rc;
     // the gradient that reaches the initial state through R: one more contraction, of step 0's da
-    hipLaunchKernelGGL(bwd_dh_kernel<false>, hgrid, dim3(256), 0, st, a, 0);
+    if (f32) hipLaunchKernelGGL(bwd_dh_kernel<true>, hgrid, dim3(256), 0, st, a, 0);
+    else hipLaunchKernelGGL(bwd_dh_kernel<false>, hgrid, dim3(256), 0, st, a, 0);
   }
   for (int t = (path == FRNN_PATH_FUSED ? -1 : T - 1); t >= 0; --t) {
     const dim3 g64((unsigned)((BND + 63) / 64)), b64(64);
@@ -1221,7 +1269,6 @@ int frnn_bwd_workspace_bytes(const frnn_desc* d, int path, size_t* bytes) {
   const int rc = validate_desc(d, path);
   if (rc != FRNN_OK) return rc;
   if (!bytes) return FRNN_EINVAL;
-  if (path == FRNN_PATH_FUSED && d->in_dtype == FRNN_F32) return FRNN_EUNSUPPORTED;
   *bytes = kErrBytes + bwd_layout(d->B, d->T, d->N, d->D, d->cell, d->in_dtype == FRNN_F32, path).total;
   return FRNN_OK;
 }
@@ -1231,7 +1278,6 @@ int frnn_bwd(const frnn_desc* d, int path, const void* Wx, const void* R, const 
              void* dstates0, void* workspace, size_t workspace_bytes, void* stream) {
   int rc = validate_desc(d, path);
   if (rc != FRNN_OK) return rc;
-  if (path == FRNN_PATH_FUSED && d->in_dtype == FRNN_F32) return FRNN_EUNSUPPORTED;
   if ((long long)((d->B + 15) / 16) * d->N > 65535) return FRNN_EUNSUPPORTED;  // dh kernel grid
   if (d->T > 0 && (!Wx || !R || !states)) return FRNN_EINVAL;
   for (const void* p : {Wx, R, b, states0, states, dstates, dlast, (const void*)dWx, (const void*)dR, (const void*)db,

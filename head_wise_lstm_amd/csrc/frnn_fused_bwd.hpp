@@ -729,3 +729,152 @@ __global__ void __launch_bounds__((NCW + 1) * 64, 1) fused_bwdx_kernel(FusedBwdA
 }
 
 }  // namespace frnn
+
+namespace frnn {
+
+// ============================================================================ single-workgroup fp32 design
+// fp32 operands for heads of at most 64 units: a whole head (and a block of BR batch rows) per
+// workgroup, so the step's da stays in LDS (two parities) as the next step's B operand: no
+// exchange, no bounded wait. Each compute wave owns one 16-row tile of R's rows d, resident in
+// VGPRs, with k = (g, e) over G*D in the fp32 MFMA's k-tiles of four (v_mfma_f32_16x16x4_f32, A = R
+// packed by bwd_rpack_kernel, B = da^T). Lane l of the result holds dh_R of units 4*(l/16)..+3 of
+// its tile for batch column l%16, as in the die-local design, and applies the same linear step.
+// The I/O wave streams the records in and (dh, dc) out exactly as there (one barrier per step).
+constexpr int BWDL_NCW = 4;
+__host__ __device__ constexpr int fused_bwdl_row(int G, int D) { return G * D + 4; }  // floats per da row
+
+struct FusedBwdlLds {
+  int da, rin, rout, total;
+};
+
+__host__ __device__ inline FusedBwdlLds fused_bwdl_lds(int G, int D, int BR) {
+  FusedBwdlLds L;
+  L.da = 0;
+  L.rin = 2 * 16 * fused_bwdl_row(G, D) * 4;
+  L.rout = L.rin + 2 * BR * D * BWD_REC * 4;
+  L.total = L.rout + 2 * BR * D * 2 * 4;
+  return L;
+}
+
+// Largest batch rows per group: the I/O wave moves at most 64 * BWD_EPL_IN record words and
+// 64 * BWD_EPL_OUT output words per step (a head's D units per row).
+__host__ __device__ constexpr int fused_bwdl_max_br(int D) {
+  return (64 * BWD_EPL_IN * 2 / BWD_REC / D) < (64 * BWD_EPL_OUT / D) ? (64 * BWD_EPL_IN * 2 / BWD_REC / D)
+                                                                       : (64 * BWD_EPL_OUT / D);
+}
+
+template <int CELL, int KT>
+__global__ void __launch_bounds__((BWDL_NCW + 1) * 64, 1) fused_bwd_local_kernel(FusedBwdArgs a) {
+  constexpr int G = cell_gates(CELL);
+  constexpr int NCW = BWDL_NCW;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  __shared__ int s_abort;
+
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int col = lane & 15, quad = lane >> 4;
+  const int D = a.D, N = a.N, T = a.T;
+  const int TPH = D / 16;  // row tiles of a head (at most NCW)
+  const int group = blockIdx.x;
+  if (group >= a.groups) return;
+  if (threadIdx.x == 0) s_abort = 0;
+  const int n = group % N, bblk = group / N;
+  const int b0 = bblk * a.BR;
+  const int nvalid = min(a.BR, a.B - b0);
+  const FusedBwdlLds lay = fused_bwdl_lds(G, D, a.BR);
+  const int ROW = fused_bwdl_row(G, D);
+  float* dab = reinterpret_cast<float*>(smem + lay.da);
+  float* rin = reinterpret_cast<float*>(smem + lay.rin);
+  float* rout = reinterpret_cast<float*>(smem + lay.rout);
+  // both parities of da start at zero: step 0 has no dh_R, and rows of padding batch columns
+  // are never written
+  for (int i = threadIdx.x; i < 2 * 16 * ROW; i += (NCW + 1) * 64) dab[i] = 0.0f;
+
+  if (wave == NCW) {
+    BwdIo c;
+    c.rec = reinterpret_cast<const char*>(a.rec);
+    c.dst = a.dstate;
+    c.in_row = (long long)N * D * BWD_REC;
+    c.in_step = (long long)a.Bs * N * D * BWD_REC;
+    c.in_base = ((long long)b0 * N + n) * D * BWD_REC;
+    c.out_row = (long long)N * D * 2;
+    c.out_step = (long long)a.Bs * N * D * 2;
+    c.out_base = ((long long)b0 * N + n) * D * 2;
+    c.nvalid = nvalid;
+    c.U = D;
+    c.T = T;
+    c.BR = a.BR;
+    c.lane = lane;
+    bio_wave(c, rin, rout, &s_abort);
+    return;
+  }
+
+  // ==================================================================== compute waves
+  const bool colv = col < nvalid;
+  const int tt = wave;  // the wave's tile of R's rows
+  const bool tv = tt < TPH;
+  float Ra[KT];
+  {
+    const float* rp = reinterpret_cast<const float*>(a.rpk) + ((long long)n * TPH + min(tt, TPH - 1)) * KT * 64 + lane;
+#pragma unroll
+    for (int kk = 0; kk < KT; ++kk) Ra[kk] = tv ? rp[(long long)kk * 64] : 0.0f;
+  }
+  const int gu = 16 * tt + 4 * quad;  // the lane's first unit
+  float cr[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // LSTM dc, GRU dh carried to the next kernel step
+  block_barrier();  // barrier -1
+
+  for (int s = 0; s < T; ++s) {
+    block_barrier();  // barrier s: the step before's da and this step's records are in LDS
+    if (uniform_flag(s_abort)) return;
+    if (tv) {  // (uniform in the wave; every wave reaches every barrier)
+      // ---- dh_R = sum over k of R[d][k] da[k] for this wave's 16 rows d, all batch columns
+      f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+      const float* bp = dab + ((s + 1) & 1) * 16 * ROW + col * ROW + quad;
+#pragma unroll
+      for (int kk = 0; kk < KT; kk += 2) {
+        acc0 = mfma_f32(Ra[kk], bp[kk * 4], acc0);
+        if (kk + 1 < KT) acc1 = mfma_f32(Ra[kk + 1], bp[(kk + 1) * 4], acc1);
+      }
+      const f32x4_t pre = acc0 + acc1;
+      if (colv) {
+        // ---- the linear step for the lane's four units; da into this step's parity, (dh, dc) out
+        const float* rr = rin + ((s & 1) * a.BR + col) * D * BWD_REC + gu * BWD_REC;
+        float* ro = rout + ((s & 1) * a.BR + col) * D * 2 + gu * 2;
+        float da[G][4], dh[4], dc[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const f32x4_t r0 = *reinterpret_cast<const f32x4_t*>(rr + i * BWD_REC);
+          const f32x4_t r1 = *reinterpret_cast<const f32x4_t*>(rr + i * BWD_REC + 4);
+          if constexpr (CELL == CELL_LSTM) {
+            dh[i] = pre[i] + r1[2];
+            dc[i] = cr[i] + r1[3] + dh[i] * r0[0];
+            da[0][i] = dc[i] * r0[1];
+            da[1][i] = dc[i] * r0[2];
+            da[2 % G][i] = dc[i] * r0[3];
+            da[3 % G][i] = dh[i] * r1[0];
+            cr[i] = dc[i] * r1[1];
+          } else if constexpr (CELL == CELL_GRU) {
+            dh[i] = pre[i] + r1[0] + cr[i];
+            dc[i] = 0.0f;
+            da[0][i] = dh[i] * r0[0];
+            da[1 % G][i] = dh[i] * r0[1];
+            da[2 % G][i] = dh[i] * r0[2];
+            cr[i] = dh[i] * r0[3];
+          } else {
+            dh[i] = pre[i] + r0[1];
+            dc[i] = 0.0f;
+            da[0][i] = dh[i] * r0[0];
+          }
+        }
+        float* dw = dab + (s & 1) * 16 * ROW + col * ROW + gu;
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+          *reinterpret_cast<f32x4_t*>(dw + g * D) = f32x4_t{da[g][0], da[g][1], da[g][2], da[g][3]};
+        *reinterpret_cast<f32x4_t*>(ro) = f32x4_t{dh[0], dc[0], dh[1], dc[1]};
+        *reinterpret_cast<f32x4_t*>(ro + 4) = f32x4_t{dh[2], dc[2], dh[3], dc[3]};
+      }
+    }
+  }
+  block_barrier();  // barrier T: the last step's outputs are in LDS for the I/O wave
+}
+
+}  // namespace frnn

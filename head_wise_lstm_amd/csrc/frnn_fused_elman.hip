@@ -28,6 +28,12 @@ FusedBwdxTable fused_bwdx_table_elman() {
 
 FusedBwdTable fused_bwd_table_elman() { return FusedBwdTable{kBwdTable, (int)(sizeof(kBwdTable) / sizeof(kBwdTable[0]))}; }
 
+fused_bwd_fn fused_bwd_local_elman(int D) {
+  if (D == 32) return &fused_bwd_local_kernel<CELL_ELMAN, 1 * 32 / 4>;
+  if (D == 64) return &fused_bwd_local_kernel<CELL_ELMAN, 1 * 64 / 4>;
+  return nullptr;
+}
+
 FusedTable fused_table_elman() { return FusedTable{kTable, (int)(sizeof(kTable) / sizeof(kTable[0]))}; }
 
 }  // namespace frnn

@@ -28,6 +28,12 @@ FusedBwdxTable fused_bwdx_table_gru() {
 
 FusedBwdTable fused_bwd_table_gru() { return FusedBwdTable{kBwdTable, (int)(sizeof(kBwdTable) / sizeof(kBwdTable[0]))}; }
 
+fused_bwd_fn fused_bwd_local_gru(int D) {
+  if (D == 32) return &fused_bwd_local_kernel<CELL_GRU, 3 * 32 / 4>;
+  if (D == 64) return &fused_bwd_local_kernel<CELL_GRU, 3 * 64 / 4>;
+  return nullptr;
+}
+
 FusedTable fused_table_gru() { return FusedTable{kTable, (int)(sizeof(kTable) / sizeof(kTable[0]))}; }
 
 }  // namespace frnn

@@ -100,4 +100,10 @@ FusedBwdxTable fused_bwdx_table_lstm();
 FusedBwdxTable fused_bwdx_table_elman();
 FusedBwdxTable fused_bwdx_table_gru();
 
+// The single-workgroup fp32 backward (fused_bwd_local_kernel) of a cell for heads of D units,
+// D = 32 or 64 (its k-tiles, G*D/4, are a template parameter), or null for any other D.
+fused_bwd_fn fused_bwd_local_lstm(int D);
+fused_bwd_fn fused_bwd_local_elman(int D);
+fused_bwd_fn fused_bwd_local_gru(int D);
+
 }  // namespace frnn
