@@ -26,7 +26,7 @@ METRIC = "LSTM fwd µs/timestep + achieved TFLOP/s (% MFMA bf16 peak), B=16 N=1 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, at the 2.4 GHz peak engine clock
 PEAK_SCLK_MHZ = 2400.0
 PEAK_HBM_GBS = 8000.0
-WS_RING_BYTES = 512 << 20   # workspaces of the timed calls: each call its own where they fit
+WS_RING_BYTES = 24 << 30   # workspaces of the timed calls: each call its own where they fit (288 GB of HBM)
 
 
 def headwise_flops(w) -> float:
