@@ -630,7 +630,7 @@ size_t bwd_kp(int T, int B) {
 }
 
 struct BwdLayout {
-  size_t zeros, hprev, hprevT, rt, rpk, hr, da, daT, tmp, dhpart, carry, rec, dstate, xbuf, total;
+  size_t zeros, hprev, hprevT, rt, rpk, rpk32, hr, da, daT, tmp, dhpart, carry, rec, dstate, xbuf, total;
 };
 
 // Fused backward design: groups of BR batch rows of one head on one die, W workgroups each owning
@@ -699,9 +699,7 @@ bool plan_fused_bwdx(int B, int N, int D, int cell, const DevInfo& di, FusedBwdP
 
 int plan_fused_bwd_da(int B, int N, int D, int cell, const DevInfo& di, FusedBwdPlan* out);
 
-// The partial-sum design where it has a plan with no more launches than the da design, else the
-// da design. FRNN_FUSED_BWD_DESIGN=da / px pins one.
-// fp32 operands: the single-workgroup design, a head and BR batch rows per workgroup (as many rows
+// The single-workgroup design, a head and BR batch rows per workgroup (as many rows
 // as the I/O wave's limits allow), the batch in chunks when the groups exceed the CUs.
 int plan_fused_bwd_local(int B, int N, int D, int cell, const DevInfo& di, FusedBwdPlan* out) {
   const fused_bwd_fn fn = cell == FRNN_CELL_LSTM ? fused_bwd_local_lstm(D)
@@ -724,10 +722,19 @@ int plan_fused_bwd_local(int B, int N, int D, int cell, const DevInfo& di, Fused
   return FRNN_OK;
 }
 
+// fp32 operands take the single-workgroup design. bf16 operands take the partial-sum design where
+// it has a plan with no more launches than the da design, else the da design; heads that neither
+// die-local design tiles (a head of 32 units, say) run the single-workgroup design on fp32
+// fragments of R, and so do Elman heads of at most 64 units, where it measured 17-22 % faster than
+// either die-local design (B x N from 16 x 1 to 256 x 4, T = 512; LSTM and GRU heads of 64 units
+// keep the die-local designs, which measured up to 1.7x faster there). FRNN_FUSED_BWD_PX pins a
+// design: 1 the partial sums, 0 the da exchange, 2 the single workgroup.
 int plan_fused_bwd(int B, int N, int D, int cell, int f32, const DevInfo& di, FusedBwdPlan* out) {
   if (f32) return plan_fused_bwd_local(B, N, D, cell, di, out);
-  if (!di.periodic || D % 32 != 0) return FRNN_EUNSUPPORTED;
-  const int design = env_int("FRNN_FUSED_BWD_PX", -1);  // 1: partial sums only, 0: da exchange only
+  const int design = env_int("FRNN_FUSED_BWD_PX", -1);
+  if (design == 2) return plan_fused_bwd_local(B, N, D, cell, di, out);
+  if (design < 0 && cell == FRNN_CELL_ELMAN && plan_fused_bwd_local(B, N, D, cell, di, out) == FRNN_OK) return FRNN_OK;
+  if (!di.periodic || D % 32 != 0) return design < 0 ? plan_fused_bwd_local(B, N, D, cell, di, out) : FRNN_EUNSUPPORTED;
   FusedBwdPlan px, da;
   const bool has_px = design != 0 && plan_fused_bwdx(B, N, D, cell, di, &px);
   const bool has_da = design != 1 && plan_fused_bwd_da(B, N, D, cell, di, &da) == FRNN_OK;
@@ -739,7 +746,7 @@ int plan_fused_bwd(int B, int N, int D, int cell, int f32, const DevInfo& di, Fu
     *out = da;
     return FRNN_OK;
   }
-  return FRNN_EUNSUPPORTED;
+  return design < 0 ? plan_fused_bwd_local(B, N, D, cell, di, out) : FRNN_EUNSUPPORTED;
 }
 
 int plan_fused_bwd_da(int B, int N, int D, int cell, const DevInfo& di, FusedBwdPlan* out) {
@@ -809,8 +816,10 @@ BwdLayout bwd_layout(int B, int T, int N, int D, int cell, int f32, int path) {
   L.tmp = q;    q += align256((size_t)BWD_DR_PARTS * N * (D + 1) * G * D * 4);
   L.dhpart = q; q += align256((size_t)BWD_KS * B * N * D * 4);
   L.carry = q;  q += align256((size_t)B * N * D * 4);
-  L.rec = L.dstate = L.xbuf = q;
+  L.rec = L.dstate = L.xbuf = L.rpk32 = q;
   if (path == FRNN_PATH_FUSED) {
+    // R as fp32 fragments for the single-workgroup design on bf16 inputs (heads of at most 64)
+    L.rpk32 = q;  q += (!f32 && D <= 64) ? align256((size_t)N * G * D * D * 4) : 0;
     L.rec = q;    q += align256((size_t)T * B * N * D * BWD_REC * 4);
     L.dstate = q; q += align256((size_t)T * B * N * D * 2 * 4);
     // exchange words: groups * BR <= N * (B + 3) rows (BR <= 4), two parities, G*D words a row
@@ -879,6 +888,14 @@ int run_fused_bwd(int cell, const BwdArgs& a, const FusedBwdPlan& fp, const DevI
   const bool f32 = a.f32 != 0;
   launch_bwd_cell_kernel(kBwdRecord, cell, f32, a.wx_f32, dim3(pgrid), dim3(256), st, a, 0, rec);
   const void* fn = reinterpret_cast<const void*>(fp.fn);
+  // the single-workgroup design multiplies on the fp32 MFMA: bf16 R widened into fp32 fragments
+  const void* rpk_local = a.rpk;
+  if (fp.local && !f32) {
+    const long long np = (long long)a.N * (a.D / 16) * (gates_of(cell) * a.D / 4) * 64;
+    hipLaunchKernelGGL(bwd_rpack_kernel, dim3((unsigned)std::min<long long>((np + 255) / 256, 65536)), dim3(256), 0, st, a,
+                       (void*)(base + L.rpk32), 1);
+    rpk_local = base + L.rpk32;
+  }
   // the batch in chunks of at most Bc rows, one launch each (rows never interact)
   for (int b0 = 0; b0 < a.B; b0 += fp.Bc) {
     const int Bch = std::min(fp.Bc, a.B - b0);
@@ -888,7 +905,7 @@ int run_fused_bwd(int cell, const BwdArgs& a, const FusedBwdPlan& fp, const DevI
       std::memset(&f, 0, sizeof(f));
       f.B = Bch; f.Bs = a.B; f.T = a.T; f.N = a.N; f.D = a.D;
       f.BR = fp.BR; f.groups = groups; f.W = 1; f.n_xcd = 1;
-      f.rpk = a.rpk;
+      f.rpk = rpk_local;
       f.rec = rec + (size_t)b0 * a.N * a.D * BWD_REC;
       f.dstate = dstate + (size_t)b0 * a.N * a.D * 2;
       f.err = reinterpret_cast<int*>(base - kErrBytes);
@@ -1023,7 +1040,7 @@ int run_backward(const BwdProblem& q, int path, const FusedBwdPlan& fbp, const D
   {
     const long long np = (long long)N * (D / 16) * (G * D / (f32 ? 4 : 32)) * 64;
     hipLaunchKernelGGL(bwd_rpack_kernel, dim3((unsigned)std::min<long long>((np + 255) / 256, 65536)), dim3(256), 0, st, a,
-                       (void*)(base + L.rpk));
+                       (void*)(base + L.rpk), 0);
   }
   const dim3 hgrid(D / 16, a.ks, ((B + 15) / 16) * N);
   if (path == FRNN_PATH_FUSED) {

@@ -33,6 +33,7 @@ struct FusedTable {
   X(false, false, 8, 8, 6, 3) X(false, false, 8, 8, 4, 2) X(false, false, 8, 8, 2, 1)              \
   X(false, false, 6, 6, 6, 4) X(false, false, 4, 4, 6, 6) X(false, false, 8, 8, 8, 2)              \
   X(false, false, 4, 4, 8, 4) X(false, false, 8, 8, 4, 1) X(false, false, 8, 4, 4, 4)              \
+  X(false, false, 8, 8, 2, 4)                                                                      \
   /* single-workgroup design (bf16) */                                                             \
   X(false, true, 4, 1, 1, 1) X(false, true, 4, 1, 2, 1) X(false, true, 4, 1, 1, 2)                 \
   X(false, true, 4, 1, 4, 2) X(false, true, 4, 1, 6, 3) X(false, true, 4, 1, 2, 4)                 \
@@ -58,11 +59,11 @@ struct FusedBwdTable {
   int n;
 };
 
-// D = 768 (head split 24 ways), 512, 256, 128 and 64
+// D = 768 (head split 24 ways), 512, 256, 128, 96 and 64
 #define FRNN_FUSED_BWD_LSTM(X)                                                          \
   X(8, 8, 2, 12) X(6, 6, 2, 16) X(8, 8, 2, 8) X(8, 8, 1, 8) X(8, 8, 2, 4) X(4, 4, 2, 8) \
   X(8, 8, 1, 4) X(4, 4, 1, 8) X(8, 8, 1, 2) X(4, 4, 1, 4) X(8, 8, 2, 2) X(4, 4, 2, 4)   \
-  X(4, 4, 1, 2) X(4, 4, 2, 2) X(4, 2, 1, 4)
+  X(4, 4, 1, 2) X(4, 4, 2, 2) X(4, 2, 1, 4) X(4, 4, 1, 3)
 #define FRNN_FUSED_BWD_GRU(X)                                                           \
   X(8, 8, 2, 9) X(6, 6, 2, 12) X(8, 8, 2, 6) X(8, 8, 1, 6) X(8, 8, 2, 3) X(6, 6, 2, 4)  \
   X(8, 8, 1, 3) X(6, 6, 1, 4) X(6, 6, 1, 2) X(6, 6, 2, 2) X(4, 4, 2, 3) X(6, 6, 1, 1)   \

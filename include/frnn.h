@@ -79,9 +79,10 @@ enum { FRNN_F32 = 0, FRNN_BF16 = 1 };
  * gfx950):
  *  ALTERNATING: per step, one MFMA kernel computes h.R for every head and one coalesced
  *               pointwise kernel applies the gates; 2*T launches on `stream`.
- *  FUSED:       one persistent launch (all workgroups resident at once); R stays in registers
- *               for all T steps; the workgroups sharing a head exchange h through the die-local
- *               L2 every step. */
+ *  FUSED:       one persistent launch for all T steps (per chunk of batch rows where the batch
+ *               exceeds one launch); R stays in registers. The workgroups sharing a head, all
+ *               resident on one die, exchange h through that die's L2 every step; a head small
+ *               enough for one workgroup keeps h in LDS. */
 enum { FRNN_PATH_ALTERNATING = 0, FRNN_PATH_FUSED = 1 };
 
 /* Problem description for frnn_fwd and frnn_bwd. G and S follow from `cell` (LSTM: 4, 2;
@@ -168,10 +169,14 @@ int frnn_fwd(const frnn_desc* d, int path, const void* Wx, const void* R, const 
  * with one MFMA GEMM per head and end with one GEMM per head that forms dR and db; they differ in
  * the serial part, t = T-1 .. 0:
  *   FRNN_PATH_ALTERNATING: per step, a pointwise kernel and an MFMA kernel (2*T launches);
- *   FRNN_PATH_FUSED: one persistent launch (bf16 inputs), in which the workgroups of
- *     a head exchange the gradient reaching h through R every step, the forward's die-local
- *     design with h and R^T exchanged. Shapes this build has no fused design for return
- *     FRNN_EUNSUPPORTED (frnn_bwd_plan_str says which design a shape gets).
+ *   FRNN_PATH_FUSED: one launch for all T steps (per chunk of batch rows where the batch
+ *     exceeds one launch). Either the workgroups of one die share a head and exchange the
+ *     gradient reaching h through R every step (bf16 inputs; the forward's die-local design
+ *     with h and R^T exchanged), or one workgroup holds a whole head of 32 or 64 units and
+ *     keeps that gradient in LDS, multiplying on the fp32 MFMA (fp32 inputs, bf16 Elman heads,
+ *     and bf16 heads no die-local design tiles). Shapes this build has no fused design for (a
+ *     head of 1024 units with three or four gates, say) return FRNN_EUNSUPPORTED before any
+ *     launch; frnn_bwd_plan_str says which design a shape gets.
  * The workspace grows with T (it holds every step's h.R and gradient).
  */
 int frnn_bwd(const frnn_desc* d, int path, const void* Wx, const void* R, const void* b,

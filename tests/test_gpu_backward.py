@@ -147,14 +147,19 @@ def test_bwd_full(name, path):
     run_bwd_case(w, path)
 
 
-# Both fused backward designs on the small cases: the partial-sum design (the planner's choice
-# where it has one) and the da-exchange design, pinned with FRNN_FUSED_BWD_PX.
-@pytest.mark.parametrize("px", [1, 0])
-@pytest.mark.parametrize("w", [x for x in SMALL if x.dtype == torch.bfloat16], ids=lambda w: w.name)
+# Every fused backward design on the small bf16 cases, pinned with FRNN_FUSED_BWD_PX: the
+# partial-sum design (the planner's choice where it has one), the da-exchange design, and, for
+# heads of at most 64 units, the single-workgroup design on fp32 fragments of R (the planner's
+# choice for heads neither die-local design tiles).
+_DESIGN_NAME = {1: "die-local-partials", 0: "design=die-local ", 2: "workgroup-local"}
+
+
+@pytest.mark.parametrize("w,px", [(x, px) for x in SMALL if x.dtype == torch.bfloat16 for px in (1, 0, 2)
+                                  if px != 2 or x.D <= 64], ids=lambda x: f"px{x}" if isinstance(x, int) else x.name)
 def test_bwd_small_each_design(w, px):
     with _env({"FRNN_FUSED_BWD_PX": px}):
         plan = _fused_plan_or_skip(w)
-    assert ("die-local-partials" in plan) == bool(px), plan
+    assert _DESIGN_NAME[px] in plan + " ", plan
     run_bwd_case(w, "fused", env={"FRNN_FUSED_BWD_PX": px})
 
 
@@ -197,14 +202,33 @@ BWD_EXTREME = [
     fi.HeadwiseWorkload("bwd_gru_B130_N2_D256", "gru", torch.bfloat16, B=130, T=5, N=2, D=256, seed=306,
                         s0_var=1.0),
 ]
+# A head of 1024 units with four gate rows: R (8 MB bf16) is half of a die's register file, more
+# than the workgroups of a die-local backward design can hold beside their working registers.
+BWD_NO_FUSED_DESIGN = {"bwd_lstm_D1024", "bwd_gru_D1024"}
 
 
-@pytest.mark.parametrize("path", ["alternating", "fused"])
-@pytest.mark.parametrize("w", BWD_EXTREME, ids=lambda w: w.name)
+@pytest.mark.parametrize("w,path", [(w, p) for w in BWD_EXTREME for p in ("alternating", "fused")
+                                    if not (p == "fused" and w.name in BWD_NO_FUSED_DESIGN)],
+                         ids=lambda x: x if isinstance(x, str) else x.name)
 def test_bwd_extreme_shapes(w, path):
-    if path == "fused":
-        _fused_plan_or_skip(w)
     run_bwd_case(w, path)
+
+
+@pytest.mark.parametrize("w", [w for w in BWD_EXTREME if w.name in BWD_NO_FUSED_DESIGN], ids=lambda w: w.name)
+def test_fused_bwd_rejects_heads_without_a_design(w):
+    """The fused backward reports FRNN_EUNSUPPORTED for a head it has no design for, from the
+    planner and from the compute call."""
+    hw = _hw()
+    desc = hw._desc(w.B, w.T, w.N, w.D, w.cell, w.dtype)
+    with pytest.raises(hw.FrnnError) as ei:
+        hw.frnn_bwd_plan_str(desc, "fused")
+    assert ei.value.status == -2
+    x = {k: (v.cuda() if v is not None else None) for k, v in fi.make_inputs(w).items()}
+    ct = {k: (v.cuda() if v is not None else None) for k, v in fi.backward_cotangents(w).items()}
+    st, _ = hw.frnn_fwd(x["Wx"], x["R"], x["b"], x["states0"], cell=w.cell, path="alternating")
+    with pytest.raises(hw.FrnnError) as ei:
+        hw.frnn_bwd(x["Wx"], x["R"], x["b"], x["states0"], st, ct["dstates"], ct["dlast"], cell=w.cell, path="fused")
+    assert ei.value.status == -2
 
 
 @pytest.mark.timeout(300)
@@ -212,9 +236,11 @@ def test_bwd_extreme_shapes(w, path):
 def test_bwd_long_sequence_past_tag_wrap(cell):
     """65,600 steps: the fused backward's 16-bit step tags wrap (every step checked)."""
     w = fi.HeadwiseWorkload(f"bwd_{cell}_long", cell, torch.bfloat16, B=3, T=65600, N=1, D=64, seed=272, s0_var=1.0)
-    plan = _fused_plan_or_skip(w)
+    env = {"FRNN_FUSED_BWD_PX": 1}  # a die-local design (an Elman head of 64 units takes the single workgroup)
+    with _env(env):
+        plan = _fused_plan_or_skip(w)
     assert "die-local" in plan, plan
-    run_bwd_case(w, "fused")
+    run_bwd_case(w, "fused", env=env)
 
 
 _CH_GRU = fi.HeadwiseWorkload("bwd_gru_chunks_B40", "gru", torch.bfloat16, B=40, T=8, N=1, D=768, seed=251, s0_var=1.0)
@@ -226,14 +252,14 @@ _CH_ELMAN = fi.HeadwiseWorkload("bwd_elman_chunks_B64_N12", "elman", torch.bfloa
 
 @pytest.mark.parametrize("w,px,chunks", [
     (_CH_GRU, 0, 3), (_CH_LSTM, 0, 3), (_CH_ELMAN, 0, 2),
-    (_CH_GRU, 1, 2), (_CH_LSTM, 1, 2), (_CH_ELMAN, 1, 4),
+    (_CH_GRU, 1, 2), (_CH_LSTM, 1, 2), (_CH_ELMAN, 1, 4), (_CH_ELMAN, 2, 2),
 ], ids=lambda x: getattr(x, "name", str(x)))
 def test_bwd_fused_chunks(w, px, chunks):
-    """A batch whose groups cannot all be co-resident runs the fused serial part in chunks of rows
-    (both designs)."""
+    """A batch whose groups exceed one launch runs the fused serial part in chunks of rows (every
+    design)."""
     with _env({"FRNN_FUSED_BWD_PX": px}):
         plan = _fused_plan_or_skip(w)
-    assert f"chunks={chunks} " in plan and ("die-local-partials" in plan) == bool(px), plan
+    assert f"chunks={chunks} " in plan and _DESIGN_NAME[px] in plan + " ", plan
     run_bwd_case(w, "fused", env={"FRNN_FUSED_BWD_PX": px})
 
 

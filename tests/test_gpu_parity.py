@@ -294,8 +294,10 @@ def test_long_sequence_past_tag_wrap(cell, env):
     run_case(w, "fused", env=env)
 
 
-# Extreme shapes: the widest head the boundary takes (D = 1024; no fused design, alternating
-# only), many narrow heads, and batches far past one launch's co-resident rows.
+# Extreme shapes: the widest head the boundary takes (D = 1024), many narrow heads, and batches
+# far past one launch's co-resident rows. A head of 1024 units has a fused design for the Elman
+# cell only: four gate rows of 1024 x 1024 bf16 (8 MB) are half of a die's register file, more
+# than its 32 workgroups can hold beside their working registers.
 EXTREME = [
     fi.HeadwiseWorkload("lstm_D1024", "lstm", torch.bfloat16, B=2, T=6, N=1, D=1024, seed=291, s0_var=1.0),
     fi.HeadwiseWorkload("gru_D1024", "gru", torch.bfloat16, B=3, T=6, N=1, D=1024, seed=292, s0_var=1.0),
@@ -305,19 +307,33 @@ EXTREME = [
     fi.HeadwiseWorkload("lstm_B300_D64", "lstm", torch.bfloat16, B=300, T=5, N=1, D=64, seed=296, s0_var=1.0),
     fi.HeadwiseWorkload("gru_B130_N2_D256", "gru", torch.bfloat16, B=130, T=5, N=2, D=256, seed=297, s0_var=1.0),
 ]
+NO_FUSED_DESIGN = {"lstm_D1024", "gru_D1024"}
 
 
-@pytest.mark.parametrize("path", ["alternating", "fused"])
-@pytest.mark.parametrize("w", EXTREME, ids=lambda w: w.name)
+@pytest.mark.parametrize("w,path", [(w, p) for w in EXTREME for p in ("alternating", "fused")
+                                    if not (p == "fused" and w.name in NO_FUSED_DESIGN)],
+                         ids=lambda x: x if isinstance(x, str) else x.name)
 def test_extreme_shapes(w, path):
-    hw = _hw()
-    if path == "fused":
-        try:
-            hw.frnn_plan_str(hw._desc(w.B, w.T, w.N, w.D, w.cell, w.dtype), "fused")
-        except hw.FrnnError as e:
-            assert e.status == -2 and w.D == 1024, (w.name, e)
-            pytest.skip("no fused forward design for D = 1024 (the alternating path takes it)")
     run_case(w, path)
+
+
+@pytest.mark.parametrize("w", [w for w in EXTREME if w.name in NO_FUSED_DESIGN], ids=lambda w: w.name)
+def test_fused_rejects_heads_without_a_design(w):
+    """The fused path reports FRNN_EUNSUPPORTED for a head it has no design for, from the planner
+    and from the compute call, and leaves the outputs as they were."""
+    hw = _hw()
+    desc = hw._desc(w.B, w.T, w.N, w.D, w.cell, w.dtype)
+    with pytest.raises(hw.FrnnError) as ei:
+        hw.frnn_plan_str(desc, "fused")
+    assert ei.value.status == -2
+    x = {k: (v.cuda() if v is not None else None) for k, v in fi.make_inputs(w).items()}
+    S = 2 if w.cell == "lstm" else 1
+    out = (torch.full((S, w.B, w.T, w.N, w.D), 7.0, device="cuda"), torch.full((S, w.B, 1, w.N, w.D), 7.0, device="cuda"))
+    with pytest.raises(hw.FrnnError) as ei:
+        hw.frnn_fwd(x["Wx"], x["R"], x["b"], x["states0"], cell=w.cell, path="fused", out=out)
+    assert ei.value.status == -2
+    torch.cuda.synchronize()
+    assert bool((out[0] == 7.0).all()) and bool((out[1] == 7.0).all())
 
 
 def test_repeat_calls_reuse_workspace():
