@@ -80,7 +80,7 @@ def write_traffic(args) -> None:
     if args.backward:
         kname = "fused_bwd" if args.path == "fused" else "bwd_dh_kernel"  # either fused backward design
     else:
-        kname = "fused_fwd_kernel" if args.path == "fused" else "alt_gemm_kernel"
+        kname = "fused_fwd_kernel" if args.path == "fused" else "alt_step_kernel"
     true_kib = args.copy_mib * 1024.0
     # the calibration copies are the last five copies of their run (a benchmark run with
     # --also-copy first copies its inputs to the device with the same copy kernel)
@@ -447,9 +447,10 @@ def main():
     roof = {"bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": tflops / PEAK_BF16_TFLOPS, "traffic": None,
             "kernel": ((("frnn::fused_bwdx_kernel" if "die-local-partials" in str(config.get("plan", "")) else
+                         "frnn::fused_bwd_local_kernel" if "workgroup-local" in str(config.get("plan", "")) else
                          "frnn::fused_bwd_kernel") + " (+ GEMMs, records)" if args.path == "fused" else
                         "frnn::bwd_gate_kernel+bwd_dh_kernel (+ GEMMs)") if args.backward else
-                       "frnn::fused_fwd_kernel" if args.path == "fused" else "frnn::alt_gemm_kernel+alt_gate_kernel"),
+                       "frnn::fused_fwd_kernel" if args.path == "fused" else "frnn::alt_step_kernel"),
             "per_launch_flop": flops, "launch_ms": ms}
     if not args.no_roofs:
         clk = engine_clock_under_load(step)

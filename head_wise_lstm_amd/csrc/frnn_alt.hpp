@@ -1,10 +1,14 @@
-// Alternating forward recurrence for gfx950: per step, one MFMA kernel computes h.R for all heads
-// and batch rows, then one coalesced pointwise kernel applies the gates. R is packed once per call
-// into MFMA-fragment order, so every per-step operand load is a contiguous 1 KiB per wave.
+// Alternating forward recurrence for gfx950: per step one launch, the MFMA contraction h.R for
+// all heads and batch rows with the gates as its epilogue; the step's synchronisation is the
+// kernel boundary, and R is re-read (from L2) every step, so any head size runs. R is packed once
+// per call into MFMA-fragment order, so every per-step operand load is a contiguous 1 KiB per wave.
+// h alternates between two buffers: step t reads one and writes the other, so a workgroup that
+// has finished its units cannot overwrite h that another workgroup of the same step still reads.
 //
 // Tiles follow the fused design: a 16-row tile of R^T holds the four gate rows of four units
 // (LSTM; GRU with a zero fourth row) or sixteen units (Elman); lane l of the MFMA result holds
-// rows 4*(l/16)+i of batch column l%16.
+// rows 4*(l/16)+i of batch column l%16, so after the K split's sum a lane holds every gate of its
+// unit (or four units of the Elman cell) and gates without cross-lane traffic.
 #pragma once
 
 #include "frnn_device.hpp"
@@ -32,12 +36,11 @@ struct AltArgs {
   long long last_sb, last_sn;
   int rev_n0;  // heads n >= rev_n0 run backwards in time: step t reads Wx and writes states at T-1-t
   void* rpack;    // packed R fragments: [N][TPH][KT][64][8 bf16] or [N][TPH][KT][64] fp32
-  float* rh;      // h.R per step: LSTM, GRU [B][N][D][4]; Elman [B][N][D]
-  void* hcur;     // current h, MFMA operand type: [N][B][D]
+  void* hbuf[2];  // h, MFMA operand type, [N][B][D] each: step t reads hbuf[t & 1], writes the other
   float* ccur;    // current c (LSTM) or h in fp32 (GRU): [B][N][D]
 };
 
-// Initial state into the working buffers: hcur[n][b][d] (operand type), ccur[b][n][d] (the
+// Initial state into the working buffers: hbuf[0][n][b][d] (operand type), ccur[b][n][d] (the
 // LSTM's c, the GRU's h).
 __global__ void __launch_bounds__(256) alt_init_kernel(AltArgs a) {
   const long long total = (long long)a.B * a.N * a.D;
@@ -50,131 +53,141 @@ __global__ void __launch_bounds__(256) alt_init_kernel(AltArgs a) {
     const float h = a.s0_h ? ld_f(a.s0_h, s, a.s0_f32) : 0.0f;
     const float c = a.cell == CELL_GRU ? h : a.s0_c ? ld_f(a.s0_c, s, a.s0_f32) : 0.0f;
     const long long hi = ((long long)n * a.B + b) * a.D + d;
-    if (a.r_is_f32) reinterpret_cast<float*>(a.hcur)[hi] = h;
-    else reinterpret_cast<uint16_t*>(a.hcur)[hi] = f2bf(h);
+    if (a.r_is_f32) reinterpret_cast<float*>(a.hbuf[0])[hi] = h;
+    else reinterpret_cast<uint16_t*>(a.hbuf[0])[hi] = f2bf(h);
     a.ccur[idx] = c;
   }
 }
 
-// Per step: grid (TPH, ceil(B/16), N), one R^T tile per workgroup. The 4 waves take the tile's
-// k-tiles 4 apart (wave w: w, w+4, ...), each with two accumulators, so that every wave has a
-// quarter of the fragment loads in flight at once; the four partial sums meet in LDS.
+// Step t: grid (TPH, ceil(B/16), N), one R^T tile per workgroup. The 4 waves take the tile's
+// k-tiles 4 apart (wave w: w, w+4, ...), each with two accumulators and all its loads in flight at
+// once; the four partial sums meet in LDS, and wave 0 adds Wx and the bias (loaded before the
+// contraction), applies the gates and writes the step's states.
 template <bool F32>
-__global__ void __launch_bounds__(256) alt_gemm_kernel(AltArgs a) {
+__global__ void __launch_bounds__(256) alt_step_kernel(AltArgs a, int t) {
   __shared__ f32x4_t part[4][64];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int col = lane & 15, quad = lane >> 4;
   const int GS = cell_slots(a.cell);
-  const int TPH = GS * a.D / 16;
+  const int N = a.N, D = a.D;
+  const int TPH = GS * D / 16;
   const int tt = blockIdx.x;
   const int b0 = blockIdx.y * 16;
   const int n = blockIdx.z;
   const int KW = F32 ? 4 : 32;
-  const int KT = a.D / KW;
+  const int KT = D / KW;
   const bool colv = b0 + col < a.B;
-  f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-  if constexpr (F32) {
-    const float* rp = reinterpret_cast<const float*>(a.rpack) + ((long long)n * TPH + tt) * KT * 64 + lane;
-    const float* hp = reinterpret_cast<const float*>(a.hcur) + ((long long)n * a.B + b0 + col) * a.D + quad;
-    int kt = wave;
-    for (; kt + 4 < KT; kt += 8) {
-      const float a0 = rp[(long long)kt * 64], a1 = rp[(long long)(kt + 4) * 64];
-      const float h0 = colv ? hp[kt * 4] : 0.0f, h1 = colv ? hp[(kt + 4) * 4] : 0.0f;
-      acc0 = mfma_f32(a0, h0, acc0);
-      acc1 = mfma_f32(a1, h1, acc1);
-    }
-    if (kt < KT) acc0 = mfma_f32(rp[(long long)kt * 64], colv ? hp[kt * 4] : 0.0f, acc0);
-  } else {
-    const u32x4_t* rp = reinterpret_cast<const u32x4_t*>(a.rpack) + ((long long)n * TPH + tt) * KT * 64 + lane;
-    const uint16_t* hp = reinterpret_cast<const uint16_t*>(a.hcur) + ((long long)n * a.B + b0 + col) * a.D + 8 * quad;
-    int kt = wave;
-    for (; kt + 4 < KT; kt += 8) {
-      const u32x4_t a0 = rp[(long long)kt * 64], a1 = rp[(long long)(kt + 4) * 64];
-      u32x4_t h0 = {0u, 0u, 0u, 0u}, h1 = {0u, 0u, 0u, 0u};
-      if (colv) {
-        h0 = *reinterpret_cast<const u32x4_t*>(hp + kt * 32);
-        h1 = *reinterpret_cast<const u32x4_t*>(hp + (kt + 4) * 32);
+  const void* hin = a.hbuf[t & 1];
+  void* hout = a.hbuf[(t + 1) & 1];
+  const bool rf = F32;
+
+  // ---- the epilogue's inputs (wave 0): Wx, bias and the carried state do not depend on h, so
+  // their loads go out first and their latency hides behind the contraction's
+  const long long b = b0 + col;
+  const int ts = n >= a.rev_n0 ? a.T - 1 - t : t;  // the head's time direction
+  const long long wbase = b * a.wx_sb + (long long)ts * a.wx_st;
+  const long long sbase = (b * N + n) * D;  // ccur
+  const int ue = GS == 4 ? 4 * tt + quad : 16 * tt + 4 * quad;  // the lane's (first) unit
+  float pin[4] = {0.f, 0.f, 0.f, 0.f}, cprev = 0.0f;  // Wx + bias per gate (LSTM, GRU) or unit (Elman)
+  float bn = 0.0f;                                    // GRU: the candidate's bias, added inside r (.)
+  if (wave == 0 && colv) {
+    if (GS == 4) {
+      const int G = cell_gates(a.cell);
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        if (g >= G) continue;
+        const long long off = (long long)(g * N + n) * D + ue;
+        const float bb = a.bias ? ld_f(a.bias, off, rf) : 0.0f;
+        const float wx = ld_f(a.Wx, wbase + off, a.wx_f32);
+        if (a.cell == CELL_GRU && g == 2) { pin[g] = wx; bn = bb; }
+        else pin[g] = wx + bb;
       }
-      acc0 = mfma_bf16(__builtin_bit_cast(bf16x8_t, a0), __builtin_bit_cast(bf16x8_t, h0), acc0);
-      acc1 = mfma_bf16(__builtin_bit_cast(bf16x8_t, a1), __builtin_bit_cast(bf16x8_t, h1), acc1);
+      cprev = a.ccur[sbase + ue];
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const long long off = (long long)n * D + ue + i;
+        pin[i] = ld_f(a.Wx, wbase + off, a.wx_f32) + (a.bias ? ld_f(a.bias, off, rf) : 0.0f);
+      }
     }
-    if (kt < KT) {
-      u32x4_t h0 = {0u, 0u, 0u, 0u};
-      if (colv) h0 = *reinterpret_cast<const u32x4_t*>(hp + kt * 32);
-      acc0 = mfma_bf16(__builtin_bit_cast(bf16x8_t, rp[(long long)kt * 64]), __builtin_bit_cast(bf16x8_t, h0), acc0);
+  }
+
+  // ---- the contraction: wave w takes k-tiles w, w+4, ...; all of a batch of KB k-tiles' loads
+  // (R fragments and h) go out before the first MFMA, so the wave waits for memory once per batch
+  // (one batch for every bf16 head up to D = 1024)
+  constexpr int KB = F32 ? 16 : 8;
+  typedef typename std::conditional<F32, float, bf16x8_t>::type frag_t;
+  f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+  for (int k0 = wave; k0 < KT; k0 += 4 * KB) {
+    frag_t ra[KB], hb[KB];
+#pragma unroll
+    for (int j = 0; j < KB; ++j) {
+      const int kt = k0 + 4 * j;
+      const bool kv = kt < KT;
+      if constexpr (F32) {
+        const float* rp = reinterpret_cast<const float*>(a.rpack) + ((long long)n * TPH + tt) * KT * 64 + lane;
+        const float* hp = reinterpret_cast<const float*>(hin) + ((long long)n * a.B + b0 + col) * D + quad;
+        ra[j] = kv ? rp[(long long)kt * 64] : 0.0f;
+        hb[j] = (kv && colv) ? hp[kt * 4] : 0.0f;
+      } else {
+        const u32x4_t* rp = reinterpret_cast<const u32x4_t*>(a.rpack) + ((long long)n * TPH + tt) * KT * 64 + lane;
+        const uint16_t* hp = reinterpret_cast<const uint16_t*>(hin) + ((long long)n * a.B + b0 + col) * D + 8 * quad;
+        u32x4_t rv = {0u, 0u, 0u, 0u}, hv = {0u, 0u, 0u, 0u};
+        if (kv) rv = rp[(long long)kt * 64];
+        if (kv && colv) hv = *reinterpret_cast<const u32x4_t*>(hp + kt * 32);
+        ra[j] = __builtin_bit_cast(bf16x8_t, rv);
+        hb[j] = __builtin_bit_cast(bf16x8_t, hv);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < KB; j += 2) {
+      if (k0 + 4 * j >= KT) break;  // (uniform in the wave)
+      if constexpr (F32) {
+        acc0 = mfma_f32(ra[j], hb[j], acc0);
+        acc1 = mfma_f32(ra[j + 1], hb[j + 1], acc1);
+      } else {
+        acc0 = mfma_bf16(ra[j], hb[j], acc0);
+        acc1 = mfma_bf16(ra[j + 1], hb[j + 1], acc1);
+      }
     }
   }
   part[wave][lane] = acc0 + acc1;
   __syncthreads();
   if (wave != 0 || !colv) return;
   const f32x4_t s = (part[0][lane] + part[1][lane]) + (part[2][lane] + part[3][lane]);
-  const long long b = b0 + col;
-  if (GS == 4) {
-    const int u = 4 * tt + quad;
-    *reinterpret_cast<f32x4_t*>(a.rh + ((b * a.N + n) * a.D + u) * 4) = s;
-  } else {
-    const int u = 16 * tt + 4 * quad;
-    *reinterpret_cast<f32x4_t*>(a.rh + (b * a.N + n) * a.D + u) = s;
-  }
-}
 
-// Per step: one thread per (b, n, unit); consecutive threads take consecutive units, so the Wx,
-// bias, state and output accesses of a wave are contiguous.
-__global__ void __launch_bounds__(256) alt_gate_kernel(AltArgs a, int t) {
-  const long long total = (long long)a.B * a.N * a.D;
-  const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= total) return;
-  const int u = (int)(idx % a.D);
-  const long long r = idx / a.D;
-  const int n = (int)(r % a.N);
-  const long long b = r / a.N;
-  const int N = a.N, D = a.D;
-  const int tt = n >= a.rev_n0 ? a.T - 1 - t : t;  // the head's time direction
-  const long long wbase = b * a.wx_sb + (long long)tt * a.wx_st;
-  const long long o = b * a.out_sb + (long long)tt * a.out_st + (long long)n * D + u;
-  const bool rf = a.r_is_f32;
-  float h, c = 0.0f;
-  if (a.cell == CELL_LSTM) {
-    const f32x4_t rh = *reinterpret_cast<const f32x4_t*>(a.rh + idx * 4);
-    float pre[4];
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const long long off = (long long)(g * N + n) * D + u;
-      pre[g] = rh[g] + ld_f(a.Wx, wbase + off, a.wx_f32) + (a.bias ? ld_f(a.bias, off, rf) : 0.0f);
+  // ---- the epilogue: gates of this lane's unit(s) for batch row b; the step's states out
+  const long long obase = b * a.out_sb + (long long)ts * a.out_st + (long long)n * D;
+  const long long hbase = ((long long)n * a.B + b) * D;  // hbuf
+  const long long lbase = b * a.last_sb + (long long)n * a.last_sn;
+  const bool last = t == a.T - 1;
+  auto put_h = [&](int u, float h) {
+    if (rf) reinterpret_cast<float*>(hout)[hbase + u] = h;
+    else reinterpret_cast<uint16_t*>(hout)[hbase + u] = f2bf(h);
+    if (a.out_h) a.out_h[obase + u] = h;
+    if (last && a.last_h) a.last_h[lbase + u] = h;
+  };
+  if (GS == 4) {
+    if (a.cell == CELL_LSTM) {
+      const float ig = sigmoid_f(s[0] + pin[0]), fg = sigmoid_f(s[1] + pin[1]);
+      const float zg = tanh_f(s[2] + pin[2]), og = sigmoid_f(s[3] + pin[3]);
+      const float c = fg * cprev + ig * zg;
+      a.ccur[sbase + ue] = c;
+      put_h(ue, og * tanh_f(c));
+      if (a.out_c) a.out_c[obase + ue] = c;
+      if (last && a.last_c) a.last_c[lbase + ue] = c;
+    } else {  // GRU: the reset gate scales the candidate's recurrent part (h.R_n + b_n), not its Wx
+      const float rg = sigmoid_f(s[0] + pin[0]);
+      const float zg = sigmoid_f(s[1] + pin[1]);
+      const float ng = tanh_f(pin[2] + rg * (s[2] + bn));
+      const float h = ng + zg * (cprev - ng);  // (1 - z) n + z h
+      a.ccur[sbase + ue] = h;
+      put_h(ue, h);
     }
-    const float ig = sigmoid_f(pre[0]), fg = sigmoid_f(pre[1]), zg = tanh_f(pre[2]), og = sigmoid_f(pre[3]);
-    c = fg * a.ccur[idx] + ig * zg;
-    a.ccur[idx] = c;
-    h = og * tanh_f(c);
-  } else if (a.cell == CELL_GRU) {
-    // the reset gate scales the candidate's recurrent part (h.R_n + b_n), not its Wx
-    const f32x4_t rh = *reinterpret_cast<const f32x4_t*>(a.rh + idx * 4);
-    float wx[3], bb[3];
+  } else {  // Elman: rows 4 quad .. +3 of the tile are four units
 #pragma unroll
-    for (int g = 0; g < 3; ++g) {
-      const long long off = (long long)(g * N + n) * D + u;
-      wx[g] = ld_f(a.Wx, wbase + off, a.wx_f32);
-      bb[g] = a.bias ? ld_f(a.bias, off, rf) : 0.0f;
-    }
-    const float rg = sigmoid_f(rh[0] + wx[0] + bb[0]);
-    const float zg = sigmoid_f(rh[1] + wx[1] + bb[1]);
-    const float ng = tanh_f(wx[2] + rg * (rh[2] + bb[2]));
-    h = ng + zg * (a.ccur[idx] - ng);  // (1 - z) n + z h
-    a.ccur[idx] = h;
-  } else {
-    const long long off = (long long)n * D + u;
-    h = tanh_f(a.rh[idx] + ld_f(a.Wx, wbase + off, a.wx_f32) + (a.bias ? ld_f(a.bias, off, rf) : 0.0f));
+    for (int i = 0; i < 4; ++i) put_h(ue + i, tanh_f(s[i] + pin[i]));
   }
-  if (a.out_h) a.out_h[o] = h;
-  if (a.out_c && a.cell == CELL_LSTM) a.out_c[o] = c;
-  if (t == a.T - 1) {
-    const long long lo = b * a.last_sb + (long long)n * a.last_sn + u;
-    if (a.last_h) a.last_h[lo] = h;
-    if (a.last_c && a.cell == CELL_LSTM) a.last_c[lo] = c;
-  }
-  const long long hi = ((long long)n * a.B + b) * D + u;
-  if (rf) reinterpret_cast<float*>(a.hcur)[hi] = h;
-  else reinterpret_cast<uint16_t*>(a.hcur)[hi] = f2bf(h);
 }
 
 }  // namespace frnn

@@ -405,8 +405,7 @@ size_t rec_scratch_bytes(int B, int N, int D, int cell, int r_f32, int path) {
     // exchange words: groups * BR <= N * (B + 15) rows, two parities; the per-die counters
     return s + align256((size_t)2 * N * (B + 15) * D * 4) + kCtrBytes;
   }
-  s += align256((size_t)B * N * D * GS * 4);   // h.R
-  s += align256((size_t)N * B * D * elt);      // current h
+  s += 2 * align256((size_t)N * B * D * elt);  // h, two buffers
   s += align256((size_t)B * N * D * 4);        // current c
   return s;
 }
@@ -515,9 +514,9 @@ std::string plan_string(const Problem& p, int path, const FusedPlan* fp) {
   } else {
     const int TPH = slots_of(p.cell) * p.D / 16;
     std::snprintf(buf, sizeof(buf),
-                  "alternating cell=%s dtype=%s B=%d T=%d N=%d D=%d gemm_grid=(%d,%d,%d) gate_grid=%lld launches=%d",
+                  "alternating cell=%s dtype=%s B=%d T=%d N=%d D=%d step_grid=(%d,%d,%d) launches=%d",
                   cell_name(p.cell), p.r_f32 ? "f32" : "bf16", p.B, p.T, p.N, p.D,
-                  TPH, (p.B + 15) / 16, p.N, ((long long)p.B * p.N * p.D + 255) / 256, 2 * p.T + 2);
+                  TPH, (p.B + 15) / 16, p.N, p.T + 2);
   }
   return std::string(buf);
 }
@@ -600,19 +599,17 @@ int run_recurrence(const Problem& p, int path, int* err, void* scratch, hipStrea
   a.rev_n0 = p.rev_n0;
   char* q = base;
   a.rpack = q; q += align256((size_t)GS * p.N * p.D * p.D * elt);
-  a.rh = reinterpret_cast<float*>(q); q += align256((size_t)p.B * p.N * p.D * GS * 4);
-  a.hcur = q; q += align256((size_t)p.N * p.B * p.D * elt);
+  a.hbuf[0] = q; q += align256((size_t)p.N * p.B * p.D * elt);
+  a.hbuf[1] = q; q += align256((size_t)p.N * p.B * p.D * elt);
   a.ccur = reinterpret_cast<float*>(q);
   const int TPH = GS * p.D / 16;
   if (launch_rpack(p, a.rpack, st) != hipSuccess) return FRNN_EHIP;
   const long long nstate = (long long)p.B * p.N * p.D;
   hipLaunchKernelGGL(alt_init_kernel, dim3((unsigned)std::min<long long>((nstate + 255) / 256, 4096)), dim3(256), 0, st, a);
   const dim3 ggrid(TPH, (p.B + 15) / 16, p.N);
-  const dim3 tgrid((unsigned)((nstate + 255) / 256));
   for (int t = 0; t < p.T; ++t) {
-    if (p.r_f32) hipLaunchKernelGGL(alt_gemm_kernel<true>, ggrid, dim3(256), 0, st, a);
-    else hipLaunchKernelGGL(alt_gemm_kernel<false>, ggrid, dim3(256), 0, st, a);
-    hipLaunchKernelGGL(alt_gate_kernel, tgrid, dim3(256), 0, st, a, t);
+    if (p.r_f32) hipLaunchKernelGGL(alt_step_kernel<true>, ggrid, dim3(256), 0, st, a, t);
+    else hipLaunchKernelGGL(alt_step_kernel<false>, ggrid, dim3(256), 0, st, a, t);
   }
   return hipGetLastError() == hipSuccess ? FRNN_OK : FRNN_EHIP;
 }
