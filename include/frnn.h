@@ -77,8 +77,9 @@ enum { FRNN_F32 = 0, FRNN_BF16 = 1 };
 
 /* Kernel designs (the FlashRNN page's "alternating" and "fused" variants, re-designed for
  * gfx950):
- *  ALTERNATING: per step, one MFMA kernel computes h.R for every head and one coalesced
- *               pointwise kernel applies the gates; 2*T launches on `stream`.
+ *  ALTERNATING: per step one launch on `stream`: an MFMA kernel computes h.R for every head,
+ *               R read from memory, and applies the gates in its epilogue (T launches); any
+ *               head size runs.
  *  FUSED:       one persistent launch for all T steps (per chunk of batch rows where the batch
  *               exceeds one launch); R stays in registers. The workgroups sharing a head, all
  *               resident on one die, exchange h through that die's L2 every step; a head small

@@ -16,8 +16,9 @@ The arithmetic lives in ``frnn_oracle.c`` (plain C, double precision, OpenMP ove
 * ``headwise_bwd`` -- back-propagation through time of ``headwise_fwd``: the gradients of
   sum(dstates * states) + sum(dlast * last_states) with respect to Wx, R, b and states0. The pages
   print no gradient formulas; the C source writes out the chain rule of the cell equations.
-* ``lstm_stack_bwd`` -- the gradients of the multi-layer LSTM, composed layer by layer of the
-  pinned head-wise forward and backward and library matmuls for the projections.
+* ``lstm_stack_bwd`` -- the gradients of the multi-layer LSTM (one or two directions per layer),
+  composed layer by layer of the pinned head-wise forward and backward and library matmuls for the
+  projections.
 * ``lstm_stack_p3`` -- "5.3 LSTM", MyLSTM.set_weights and MyLSTM.forward: time loop outermost,
   layers inside it, bias = bias_ih + bias_hh, Wi stored [in, 4H], Wh stored [H, 4H].
 * ``lstm_stack_dirs`` -- the same cell with one or two directions per layer, layer by layer. The
@@ -229,59 +230,83 @@ class Oracle:
             raise RuntimeError("oracle_lstm_stack_dirs failed")
         return out, hn, cn
 
+    def lstm_stack_bwd(self, x, Wi, Wh, b_ih, b_hh, h0=None, c0=None, dout=None, dhn=None, dcn=None,
+                       dirs: int = 1):
+        """Backward of the multi-layer LSTM (``dirs`` = 1: "5.3 LSTM"; 2: reading A21's two
+        directions per layer) in float64: the gradients of L = sum(dout * out) + sum(dhn * hn) +
+        sum(dcn * cn) with respect to x, Wi[j], Wh[j], b_ih[j], b_hh[j], h0 and c0, with j = l * dirs
+        + k for layer l, direction k (shapes as for lstm_stack_dirs).
 
-def lstm_stack_bwd(orc, x, Wi, Wh, b_ih, b_hh, h0=None, c0=None, dout=None, dhn=None, dcn=None):
-    """Backward of the plain multi-layer LSTM of "5.3 LSTM" in float64: the gradients of
-    L = sum(dout * out) + sum(dhn * hn) + sum(dcn * cn) with respect to x, Wi[l], Wh[l],
-    b_ih[l], b_hh[l], h0 and c0.
+        Composed of steps already pinned on their own, layer by layer (layer-major order, equal to the
+        page's time-major loop; reading A13): per layer and direction, the projection Wx = X.Wi + b_ih
+        + b_hh (a library matmul) of the layer's input X in the direction's own time order (direction
+        1 takes the sequence from the last step to the first), the head-wise forward and backward
+        (headwise_fwd / headwise_bwd with R[g,0,d,e] = Wh[d, g*H + e]), then dWi = X^T.dWx,
+        db_ih = db_hh = sum dWx, and the direction's part of dX = dWx.Wi^T, put back in time order;
+        the layer's dX is the sum over its directions. The layer output's gradient for direction k
+        is columns k*H .. k*H + H - 1 of the gradient reaching it. Returns (dx, dWi[], dWh[],
+        db_ih[], db_hh[], dh0, dc0).
+        """
+        x = _f64(x)
+        T, B, I = x.shape
+        if dirs not in (1, 2) or len(Wi) % dirs:
+            raise ValueError("dirs must be 1 or 2, with dirs weights per layer")
+        L = len(Wi) // dirs
+        H = Wh[0].shape[0]
+        J = L * dirs
+        Wi = [_f64(w) for w in Wi]
+        Wh = [_f64(w) for w in Wh]
+        b_ih = [np.zeros(4 * H) if v is None else _f64(v) for v in b_ih]
+        b_hh = [np.zeros(4 * H) if v is None else _f64(v) for v in b_hh]
+        h0 = np.zeros((J, B, H)) if h0 is None else _f64(h0)
+        c0 = np.zeros((J, B, H)) if c0 is None else _f64(c0)
 
-    Composed of steps already pinned on their own, layer by layer (layer-major order, equal to the
-    page's time-major loop; reading A13): per layer, the projection Wx = X.Wi + b_ih + b_hh (a
-    library matmul), the head-wise forward and backward (oracle_headwise_fwd / _bwd with
-    R[g,0,d,e] = Wh[d, g*H + e]), then dWi = X^T.dWx, db_ih = db_hh = sum dWx and dX = dWx.Wi^T,
-    dX being the gradient of the layer below's h sequence. Returns (dx, dWi[], dWh[], db_ih[],
-    db_hh[], dh0, dc0).
-    """
-    x = _f64(x)
-    T, B, I = x.shape
-    L = len(Wi)
-    H = Wh[0].shape[0]
-    Wi = [_f64(w) for w in Wi]
-    Wh = [_f64(w) for w in Wh]
-    b_ih = [np.zeros(4 * H) if v is None else _f64(v) for v in b_ih]
-    b_hh = [np.zeros(4 * H) if v is None else _f64(v) for v in b_hh]
-    h0 = np.zeros((L, B, H)) if h0 is None else _f64(h0)
-    c0 = np.zeros((L, B, H)) if c0 is None else _f64(c0)
-    # forward, keeping every layer's input sequence and projection
-    X, Wxs, Rs, s0s = [x], [], [], []
-    for l in range(L):
-        proj = X[l] @ Wi[l] + (b_ih[l] + b_hh[l])                      # [T,B,4H]
-        Wx = proj.reshape(T, B, 4, 1, H).transpose(1, 0, 2, 3, 4)     # [B,T,4,1,H]
-        R = Wh[l].reshape(H, 4, H).transpose(1, 0, 2)[:, None]        # R[g,0,d,e] = Wh[d, gH+e]
-        s0 = np.stack([h0[l], c0[l]])[:, :, None, None, :]            # [2,B,1,1,H]
-        st, _ = orc.headwise_fwd("lstm", Wx, R, None, s0)
-        Wxs.append(Wx); Rs.append(R); s0s.append(s0)
-        X.append(st[0, :, :, 0].transpose(1, 0, 2))                  # [T,B,H]
-    dX = np.zeros((T, B, H)) if dout is None else _f64(dout)
-    dWi, dWh, dbi, dbh = [None] * L, [None] * L, [None] * L, [None] * L
-    dh0, dc0 = np.zeros((L, B, H)), np.zeros((L, B, H))
-    for l in range(L - 1, -1, -1):
-        dstates = np.zeros((2, B, T, 1, H))
-        dstates[0, :, :, 0] = dX.transpose(1, 0, 2)
-        dlast = np.zeros((2, B, 1, 1, H))
-        if dhn is not None:
-            dlast[0, :, 0, 0] = _f64(dhn)[l]
-        if dcn is not None:
-            dlast[1, :, 0, 0] = _f64(dcn)[l]
-        dWx, dR, _, ds0 = orc.headwise_bwd("lstm", Wxs[l], Rs[l], None, s0s[l], dstates, dlast)
-        dproj = dWx[:, :, :, 0].transpose(1, 0, 2, 3).reshape(T, B, 4 * H)  # [T,B,4H]
-        dWh[l] = dR[:, 0].transpose(1, 0, 2).reshape(H, 4 * H)            # dWh[d, gH+e] = dR[g,0,d,e]
-        dWi[l] = X[l].reshape(T * B, -1).T @ dproj.reshape(T * B, 4 * H)
-        dbi[l] = dproj.reshape(T * B, 4 * H).sum(axis=0)
-        dbh[l] = dbi[l].copy()
-        dh0[l], dc0[l] = ds0[0, :, 0, 0], ds0[1, :, 0, 0]
-        dX = dproj @ Wi[l].T                                              # [T,B,in]
-    return dX, dWi, dWh, dbi, dbh, dh0, dc0
+        def order(a, k):  # a [T, ...] in direction k's time order (and back: the map is its own inverse)
+            return a if k == 0 else a[::-1]
+
+        # forward, keeping every layer's input sequence and every direction's projection
+        X, Wxs, Rs, s0s = [x], [None] * J, [None] * J, [None] * J
+        for l in range(L):
+            outs = []
+            for k in range(dirs):
+                j = l * dirs + k
+                proj = order(X[l], k) @ Wi[j] + (b_ih[j] + b_hh[j])          # [T,B,4H], own time order
+                Wxs[j] = proj.reshape(T, B, 4, 1, H).transpose(1, 0, 2, 3, 4)  # [B,T,4,1,H]
+                Rs[j] = Wh[j].reshape(H, 4, H).transpose(1, 0, 2)[:, None]      # R[g,0,d,e] = Wh[d, gH+e]
+                s0s[j] = np.stack([h0[j], c0[j]])[:, :, None, None, :]         # [2,B,1,1,H]
+                st, _ = self.headwise_fwd("lstm", Wxs[j], Rs[j], None, s0s[j])
+                outs.append(order(st[0, :, :, 0].transpose(1, 0, 2), k))      # [T,B,H] in time order
+            X.append(np.concatenate(outs, axis=2))                           # [T,B,dirs*H]
+        dX = np.zeros((T, B, dirs * H)) if dout is None else _f64(dout)
+        dWi, dWh, dbi, dbh = [None] * J, [None] * J, [None] * J, [None] * J
+        dh0, dc0 = np.zeros((J, B, H)), np.zeros((J, B, H))
+        for l in range(L - 1, -1, -1):
+            dXin = np.zeros(X[l].shape)
+            for k in range(dirs):
+                j = l * dirs + k
+                dstates = np.zeros((2, B, T, 1, H))
+                dstates[0, :, :, 0] = order(dX[:, :, k * H:(k + 1) * H], k).transpose(1, 0, 2)
+                dlast = np.zeros((2, B, 1, 1, H))
+                if dhn is not None:
+                    dlast[0, :, 0, 0] = _f64(dhn)[j]
+                if dcn is not None:
+                    dlast[1, :, 0, 0] = _f64(dcn)[j]
+                dWx, dR, _, ds0 = self.headwise_bwd("lstm", Wxs[j], Rs[j], None, s0s[j], dstates, dlast)
+                dproj = dWx[:, :, :, 0].transpose(1, 0, 2, 3).reshape(T, B, 4 * H)  # [T,B,4H], own order
+                dWh[j] = dR[:, 0].transpose(1, 0, 2).reshape(H, 4 * H)            # dWh[d, gH+e] = dR[g,0,d,e]
+                Xk = order(X[l], k)
+                dWi[j] = Xk.reshape(T * B, -1).T @ dproj.reshape(T * B, 4 * H)
+                dbi[j] = dproj.reshape(T * B, 4 * H).sum(axis=0)
+                dbh[j] = dbi[j].copy()
+                dh0[j], dc0[j] = ds0[0, :, 0, 0], ds0[1, :, 0, 0]
+                dXin += order(dproj @ Wi[j].T, k)                                 # [T,B,in], time order
+            dX = dXin
+        return dX, dWi, dWh, dbi, dbh, dh0, dc0
+
+
+def lstm_stack_bwd(orc, *args, **kwargs):
+    """``orc.lstm_stack_bwd(...)`` (kept as a function for callers that pass the oracle)."""
+    return orc.lstm_stack_bwd(*args, **kwargs)
 
 
 _default = None

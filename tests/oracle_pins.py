@@ -2,7 +2,8 @@
 
 Every pin takes an ``oracle.Oracle`` and raises AssertionError when the oracle disagrees. The same
 pins run against the real oracle (tests/test_oracle_pins.py) and against deliberately broken copies
-of its C source (tests/test_oracle_mutants.py), which must each fail at least one pin.
+of its C source and of its Python-composed multi-layer backward (tests/test_oracle_mutants.py),
+which must each fail at least one pin.
 
 Kinds of pin:
 * golden fixtures (tests/golden/*.txt): closed forms and hand-stepped scalar recurrences evaluated
@@ -16,7 +17,10 @@ Kinds of pin:
 * two formulations: the page's time-major multi-layer loop against a layer-major composition of
   head-wise runs, and against the layer-by-layer formulation the bidirectional stack uses;
 * the bidirectional reading (torch.nn.LSTM(bidirectional=True) in float64, a time-reversed
-  one-direction run, layer composition).
+  one-direction run, layer composition);
+* the backward: torch autograd through float64 torch layers (head-wise cells with identity input
+  weights, the one- and two-direction multi-layer LSTM), central finite differences of the pinned
+  forwards, linearity in the cotangent, T = 0.
 """
 from __future__ import annotations
 
@@ -746,7 +750,6 @@ def pin_bwd_torch_lstm_stack(orc):
     """The multi-layer backward equals torch autograd through a float64 two-layer torch.nn.LSTM
     (the module whose state_dict the "5.3 LSTM" page reads), for every gradient: x, Wi, Wh,
     both biases, h0 and c0."""
-    import oracle as _o
     T, B, I, H, L = 6, 3, 5, 4, 2
     m = _torch_lstm(I, H, L, 71)
     rng = np.random.default_rng(71)
@@ -767,7 +770,7 @@ def pin_bwd_torch_lstm_stack(orc):
     Wh = [sd[f"weight_hh_l{l}"].numpy().T for l in range(L)]
     bi = [sd[f"bias_ih_l{l}"].numpy() for l in range(L)]
     bh = [sd[f"bias_hh_l{l}"].numpy() for l in range(L)]
-    dx, dWi, dWh, dbi, dbh, dh0, dc0 = _o.lstm_stack_bwd(orc, x, Wi, Wh, bi, bh, h0, c0, dout, dhn, dcn)
+    dx, dWi, dWh, dbi, dbh, dh0, dc0 = orc.lstm_stack_bwd(x, Wi, Wh, bi, bh, h0, c0, dout, dhn, dcn)
     np.testing.assert_allclose(dx, xt.grad.numpy(), rtol=0, atol=1e-12)
     np.testing.assert_allclose(dh0, h0t.grad.numpy(), rtol=0, atol=1e-12)
     np.testing.assert_allclose(dc0, c0t.grad.numpy(), rtol=0, atol=1e-12)
@@ -777,5 +780,74 @@ def pin_bwd_torch_lstm_stack(orc):
         np.testing.assert_allclose(dbi[l], getattr(m, f"bias_ih_l{l}").grad.numpy(), rtol=0, atol=1e-12)
         np.testing.assert_allclose(dbh[l], getattr(m, f"bias_hh_l{l}").grad.numpy(), rtol=0, atol=1e-12)
 
+
+
+def pin_bwd_torch_lstm_stack_bidirectional(orc):
+    """The two-direction multi-layer backward equals torch autograd through a float64 two-layer
+    torch.nn.LSTM(bidirectional=True) (reading A21), for every gradient: x, the Wi, Wh and both
+    biases of each (layer, direction), h0 and c0 in its (layer, direction) order."""
+    T, B, I, H, L = 6, 3, 5, 4, 2
+    torch.manual_seed(73)
+    m = torch.nn.LSTM(I, H, num_layers=L, bidirectional=True, dtype=torch.float64)
+    rng = np.random.default_rng(73)
+    x = rng.normal(size=(T, B, I))
+    h0 = rng.normal(size=(2 * L, B, H)) * 0.5
+    c0 = rng.normal(size=(2 * L, B, H)) * 0.5
+    dout = rng.normal(size=(T, B, 2 * H))
+    dhn = rng.normal(size=(2 * L, B, H))
+    dcn = rng.normal(size=(2 * L, B, H))
+    xt = torch.tensor(x, requires_grad=True)
+    h0t = torch.tensor(h0, requires_grad=True)
+    c0t = torch.tensor(c0, requires_grad=True)
+    out, (hn, cn) = m(xt, (h0t, c0t))
+    loss = (out * torch.from_numpy(dout)).sum() + (hn * torch.from_numpy(dhn)).sum() + (cn * torch.from_numpy(dcn)).sum()
+    loss.backward()
+    Wi, Wh, bi, bh = _torch_stack_weights(m, L, 2)
+    dx, dWi, dWh, dbi, dbh, dh0, dc0 = orc.lstm_stack_bwd(x, Wi, Wh, bi, bh, h0, c0, dout, dhn, dcn, dirs=2)
+    np.testing.assert_allclose(dx, xt.grad.numpy(), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dh0, h0t.grad.numpy(), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dc0, c0t.grad.numpy(), rtol=0, atol=1e-12)
+    names = [(l, s) for l in range(L) for s in ("", "_reverse")]
+    for j, (l, s) in enumerate(names):
+        np.testing.assert_allclose(dWi[j], getattr(m, f"weight_ih_l{l}{s}").grad.numpy().T, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(dWh[j], getattr(m, f"weight_hh_l{l}{s}").grad.numpy().T, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(dbi[j], getattr(m, f"bias_ih_l{l}{s}").grad.numpy(), rtol=0, atol=1e-12)
+        np.testing.assert_allclose(dbh[j], getattr(m, f"bias_hh_l{l}{s}").grad.numpy(), rtol=0, atol=1e-12)
+
+
+def pin_bwd_stack_bidirectional_finite_differences(orc):
+    """Every gradient entry of a tiny two-direction two-layer stack against central differences of
+    the pinned two-direction forward (lstm_stack_dirs)."""
+    T, B, I, H, L = 3, 2, 2, 2, 2
+    rng = np.random.default_rng(79)
+    x = rng.normal(size=(T, B, I))
+    Wi = [rng.normal(size=((I if j < 2 else 2 * H), 4 * H)) * 0.6 for j in range(2 * L)]
+    Wh = [rng.normal(size=(H, 4 * H)) * 0.6 for _ in range(2 * L)]
+    bi = [rng.normal(size=4 * H) * 0.3 for _ in range(2 * L)]
+    bh = [rng.normal(size=4 * H) * 0.3 for _ in range(2 * L)]
+    h0 = rng.normal(size=(2 * L, B, H)) * 0.5
+    c0 = rng.normal(size=(2 * L, B, H)) * 0.5
+    dout = rng.normal(size=(T, B, 2 * H))
+    dhn = rng.normal(size=(2 * L, B, H))
+    dcn = rng.normal(size=(2 * L, B, H))
+
+    def loss():
+        out, hn, cn = orc.lstm_stack_dirs(x, Wi, Wh, bi, bh, h0, c0, dirs=2)
+        return float((out * dout).sum() + (hn * dhn).sum() + (cn * dcn).sum())
+
+    grads = orc.lstm_stack_bwd(x, Wi, Wh, bi, bh, h0, c0, dout, dhn, dcn, dirs=2)
+    targets = [(x, grads[0])] + list(zip(Wi, grads[1])) + list(zip(Wh, grads[2])) + list(zip(bi, grads[3])) + \
+        list(zip(bh, grads[4])) + [(h0, grads[5]), (c0, grads[6])]
+    eps = 1e-6
+    for arr, g in targets:
+        flat, gf = arr.reshape(-1), np.asarray(g).reshape(-1)
+        for i in range(flat.size):
+            v = flat[i]
+            flat[i] = v + eps
+            lp = loss()
+            flat[i] = v - eps
+            lm = loss()
+            flat[i] = v
+            assert abs((lp - lm) / (2 * eps) - gf[i]) <= 1e-7 * max(1.0, abs(gf[i])), (arr.shape, i)
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -2,9 +2,12 @@
 
 This shows the pins are sharp enough to catch a dropped term, a wrong sign, a wrong index or a
 transposed operand. The mutants are compiled on the CPU into a temporary folder; the real oracle
-is untouched."""
+is untouched. The multi-layer backward, composed in Python, gets the same treatment: mutated
+copies of its source replace the method in a subclass of the oracle."""
+import inspect
 import os
 import subprocess
+import textwrap
 
 import pytest
 
@@ -82,6 +85,39 @@ def test_mutant_is_caught(name, tmp_path):
     lib = str(tmp_path / f"liboracle_{name}.so")
     oracle.build(source=str(src), out=lib)
     mutant = oracle.Oracle(lib)
+    caught_by = None
+    for pin in ALL_PINS:
+        try:
+            pin(mutant)
+        except (AssertionError, RuntimeError, ValueError):
+            caught_by = pin.__name__
+            break
+    assert caught_by, f"mutant {name} passed every pin"
+
+
+STACK_BWD_SRC = textwrap.dedent(inspect.getsource(oracle.Oracle.lstm_stack_bwd))
+
+PY_MUTANTS = {
+    "stack_bwd_reverse_dx_not_flipped": ("dXin += order(dproj @ Wi[j].T, k)", "dXin += dproj @ Wi[j].T"),
+    "stack_bwd_reverse_input_not_flipped": ("Xk = order(X[l], k)", "Xk = X[l]"),
+    "stack_bwd_dout_columns_swapped": ("order(dX[:, :, k * H:(k + 1) * H], k)",
+                                       "order(dX[:, :, (dirs - 1 - k) * H:(dirs - k) * H], k)"),
+    "stack_bwd_reverse_uses_forward_wi": ("dXin += order(dproj @ Wi[j].T, k)", "dXin += order(dproj @ Wi[l * dirs].T, k)"),
+    "stack_bwd_dhn_direction_major": ("dlast[0, :, 0, 0] = _f64(dhn)[j]", "dlast[0, :, 0, 0] = _f64(dhn)[k * L + l]"),
+    "stack_bwd_db_hh_zero": ("dbh[j] = dbi[j].copy()", "dbh[j] = 0.0 * dbi[j]"),
+    "stack_bwd_dx_one_direction": ("dXin += order(", "dXin = order("),
+    "stack_bwd_dcn_dropped": ("dlast[1, :, 0, 0] = _f64(dcn)[j]", "dlast[1, :, 0, 0] = 0.0"),
+    "stack_bwd_forward_input_not_flipped": ("proj = order(X[l], k) @ Wi[j]", "proj = X[l] @ Wi[j]"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(PY_MUTANTS))
+def test_stack_bwd_mutant_is_caught(name):
+    old, new = PY_MUTANTS[name]
+    assert STACK_BWD_SRC.count(old) >= 1, f"mutation anchor for {name} not found in lstm_stack_bwd"
+    ns = dict(vars(oracle))
+    exec(compile(STACK_BWD_SRC.replace(old, new), f"<mutant {name}>", "exec"), ns)
+    mutant = type("MutantOracle", (oracle.Oracle,), {"lstm_stack_bwd": ns["lstm_stack_bwd"]})()
     caught_by = None
     for pin in ALL_PINS:
         try:
