@@ -402,11 +402,13 @@ def main():
         flops = 2.0 * w.B * 4 * w.H * w.H * w.T * w.L * dirs  # recurrent contraction of all layers and directions
         if args.backward:
             ct = {k: v.to(dev) for k, v in fi.stack_cotangents(w).items()}
-            wss = ws_ring(hw.frnn_lstm_stack_bwd_workspace_bytes(w.L, w.T, w.B, w.I, w.H, args.path), args.steps, dev)
+            wss = ws_ring(hw.frnn_lstm_stack_bwd_workspace_bytes(w.L, w.T, w.B, w.I, w.H, args.path, dirs), args.steps,
+                          dev)
 
             def step(i=0):
                 hw.frnn_lstm_stack_bwd(g["x"], g["Wi"], g["Wh"], g["b_ih"], g["b_hh"], g["h0"], g["c0"], ct["dout"],
-                                       ct["dhn"], ct["dcn"], path=args.path, workspace=wss[i % len(wss)], check=False)
+                                       ct["dhn"], ct["dcn"], path=args.path, workspace=wss[i % len(wss)], check=False,
+                                       bidirectional=dirs == 2)
             # forward again (recurrent contraction) + per layer the serial da.R^T, the h.R recompute
             # and the dR GEMM; the projections' GEMMs (forward, dWi, dX) are reported separately
             flops = 4.0 * flops

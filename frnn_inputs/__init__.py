@@ -135,13 +135,13 @@ def backward_cotangents(w: HeadwiseWorkload):
 
 
 def stack_cotangents(w: StackWorkload):
-    """Gradients of the multi-layer forward's outputs: dout [T,B,H], dhn and dcn [L,B,H], float32
-    ~N(0,1), drawn in that order from a generator seeded with seed + 1000."""
+    """Gradients of the multi-layer forward's outputs: dout [T,B,dirs*H], dhn and dcn [L*dirs,B,H],
+    float32 ~N(0,1), drawn in that order from a generator seeded with seed + 1000."""
     g = torch.Generator(device="cpu")
     g.manual_seed(w.seed + 1000)
-    dout = _normal(g, (w.T, w.B, w.H), 1.0)
-    dhn = _normal(g, (w.L, w.B, w.H), 1.0)
-    dcn = _normal(g, (w.L, w.B, w.H), 1.0)
+    dout = _normal(g, (w.T, w.B, w.dirs * w.H), 1.0)
+    dhn = _normal(g, (w.L * w.dirs, w.B, w.H), 1.0)
+    dcn = _normal(g, (w.L * w.dirs, w.B, w.H), 1.0)
     return {"dout": dout, "dhn": dhn, "dcn": dcn}
 
 

@@ -470,42 +470,49 @@ def frnn_lstm_stack_bwd(x: torch.Tensor, Wi: Sequence[torch.Tensor], Wh: Sequenc
                         h0: Optional[torch.Tensor] = None, c0: Optional[torch.Tensor] = None,
                         dout: Optional[torch.Tensor] = None, dhn: Optional[torch.Tensor] = None,
                         dcn: Optional[torch.Tensor] = None, path="fused", workspace: Optional[torch.Tensor] = None,
-                        check: bool = True):
-    """Backward of frnn_lstm_stack_fwd: (dx [T,B,I], dWi[], dWh[], db_ih[], db_hh[], dh0, dc0 [L,B,H]), fp32,
-    for the loss sum(dout * out) + sum(dhn * hn) + sum(dcn * cn); dout [T,B,H], dhn, dcn [L,B,H] fp32 or None."""
+                        check: bool = True, bidirectional: bool = False):
+    """Backward of frnn_lstm_stack_fwd: (dx [T,B,I], dWi[], dWh[], db_ih[], db_hh[], dh0, dc0 [L*dirs,B,H]),
+    fp32, for the loss sum(dout * out) + sum(dhn * hn) + sum(dcn * cn); dout [T,B,dirs*H], dhn, dcn
+    [L*dirs,B,H] fp32 or None. The weight lists hold L*dirs entries, layer l direction k at
+    l*dirs + k (dirs = 2 with ``bidirectional``), as for frnn_lstm_stack_fwd."""
     T, B, I = x.shape
-    L = len(Wi)
+    dirs = 2 if bidirectional else 1
+    if len(Wi) % dirs:
+        raise ValueError("two directions need two weights per layer")
+    J = len(Wi)
+    L = J // dirs
     H = Wh[0].shape[0]
     dev, bf, f = x.device, torch.bfloat16, torch.float32
     _check_tensor(x, "x", (T, B, I), bf, dev)
-    for l in range(L):
-        _check_tensor(Wi[l], f"Wi[{l}]", ((I if l == 0 else H), 4 * H), bf, dev)
-        _check_tensor(Wh[l], f"Wh[{l}]", (H, 4 * H), bf, dev)
-        _check_tensor(b_ih[l], f"b_ih[{l}]", (4 * H,), bf, dev)
-        _check_tensor(b_hh[l], f"b_hh[{l}]", (4 * H,), bf, dev)
-    _check_tensor(h0, "h0", (L, B, H), bf, dev)
-    _check_tensor(c0, "c0", (L, B, H), bf, dev)
-    _check_tensor(dout, "dout", (T, B, H), f, dev)
-    _check_tensor(dhn, "dhn", (L, B, H), f, dev)
-    _check_tensor(dcn, "dcn", (L, B, H), f, dev)
+    ins = [(I if j < dirs else dirs * H) for j in range(J)]
+    for j in range(J):
+        _check_tensor(Wi[j], f"Wi[{j}]", (ins[j], 4 * H), bf, dev)
+        _check_tensor(Wh[j], f"Wh[{j}]", (H, 4 * H), bf, dev)
+        _check_tensor(b_ih[j], f"b_ih[{j}]", (4 * H,), bf, dev)
+        _check_tensor(b_hh[j], f"b_hh[{j}]", (4 * H,), bf, dev)
+    _check_tensor(h0, "h0", (J, B, H), bf, dev)
+    _check_tensor(c0, "c0", (J, B, H), bf, dev)
+    _check_tensor(dout, "dout", (T, B, dirs * H), f, dev)
+    _check_tensor(dhn, "dhn", (J, B, H), f, dev)
+    _check_tensor(dcn, "dcn", (J, B, H), f, dev)
     p = _path(path)
     dx = torch.empty((T, B, I), dtype=f, device=dev)
-    dWi = [torch.empty(((I if l == 0 else H), 4 * H), dtype=f, device=dev) for l in range(L)]
-    dWh = [torch.empty((H, 4 * H), dtype=f, device=dev) for _ in range(L)]
-    dbi = [torch.empty((4 * H,), dtype=f, device=dev) for _ in range(L)]
-    dbh = [torch.empty((4 * H,), dtype=f, device=dev) for _ in range(L)]
-    dh0 = torch.empty((L, B, H), dtype=f, device=dev)
-    dc0 = torch.empty((L, B, H), dtype=f, device=dev)
-    need = frnn_lstm_stack_bwd_workspace_bytes(L, T, B, I, H, p)
+    dWi = [torch.empty((ins[j], 4 * H), dtype=f, device=dev) for j in range(J)]
+    dWh = [torch.empty((H, 4 * H), dtype=f, device=dev) for _ in range(J)]
+    dbi = [torch.empty((4 * H,), dtype=f, device=dev) for _ in range(J)]
+    dbh = [torch.empty((4 * H,), dtype=f, device=dev) for _ in range(J)]
+    dh0 = torch.empty((J, B, H), dtype=f, device=dev)
+    dc0 = torch.empty((J, B, H), dtype=f, device=dev)
+    need = frnn_lstm_stack_bwd_workspace_bytes(L, T, B, I, H, p, dirs)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     elif workspace.numel() < need:
         raise ValueError("workspace too small")
     frnn_init(dev)
-    arr = ctypes.c_void_p * L
+    arr = ctypes.c_void_p * J
     ptrs = lambda ts: arr(*[0 if t is None else t.data_ptr() for t in ts])
     rc = load().frnn_lstm_stack_bwd(
-        L, 1, T, B, I, H, p, _ptr(x), ptrs(Wi), ptrs(Wh), ptrs(b_ih), ptrs(b_hh), _ptr(h0), _ptr(c0), _ptr(dout),
+        L, dirs, T, B, I, H, p, _ptr(x), ptrs(Wi), ptrs(Wh), ptrs(b_ih), ptrs(b_hh), _ptr(h0), _ptr(c0), _ptr(dout),
         _ptr(dhn), _ptr(dcn), _ptr(dx), ptrs(dWi), ptrs(dWh), ptrs(dbi), ptrs(dbh), _ptr(dh0), _ptr(dc0),
         _ptr(workspace), workspace.numel(), _stream_handle(dev))
     if rc != FRNN_OK:

@@ -34,6 +34,17 @@ __global__ void __launch_bounds__(256) copy_init_kernel(const void* s0, int s0_f
     dst[i] = s0 ? ld_f(s0, i, s0_f32) : 0.0f;
 }
 
+// dst[r][c] = src[r][c] for r < rows, c < cols (bf16, row strides sld and dld elements): places
+// one matrix beside another, e.g. two directions' Wi side by side along K.
+__global__ void __launch_bounds__(256) copy_rows_b16_kernel(const uint16_t* src, long long sld, int rows, int cols,
+                                                            uint16_t* dst, long long dld) {
+  const long long n = (long long)rows * cols;
+  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long long)gridDim.x * 256) {
+    const long long r = i / cols, c = i - r * cols;
+    dst[r * dld + c] = src[r * sld + c];
+  }
+}
+
 // Both biases of a bidirectional layer in the projection's column order [gate][direction][unit]:
 // out[j] from b_ih, out[4*dirs*H + j] from b_hh (bf16, a NULL bias reads as zeros).
 struct StackBiasArgs {
@@ -1538,23 +1549,27 @@ int frnn_lstm_stack_fwd(int L, int dirs, int T, int B, int I, int H, int path, c
 // ----------------------------------------------------------------------------- stack backward
 // Workspace of frnn_lstm_stack_bwd (after the error word).
 struct StackBwdLayout {
-  size_t wx, st, wit, dwx, dx, xt, dwxt, parts, db, rec, bwd, total;
+  size_t wx, st, wit, dwx, dx, xt, dwxt, parts, db, wicat, rec, bwd, total;
   BwdLayout bl;
 };
 
-static StackBwdLayout stack_bwd_layout(int L, int T, int B, int I, int H, int path) {
+// Every layer keeps its projection [T][B][dirs][4H] and its states, h and c each [T][B][dirs*H]
+// (direction k at columns k*H), in time order for both directions.
+static StackBwdLayout stack_bwd_layout(int L, int dirs, int T, int B, int I, int H, int path) {
   StackBwdLayout S;
-  const size_t TB = (size_t)T * B, IH = (size_t)std::max(I, H), Kp = bwd_kp(T, B);
+  const size_t TB = (size_t)T * B, IH = (size_t)std::max(I, dirs * H), Kp = bwd_kp(T, B);
+  const size_t G4 = (size_t)dirs * 4 * H;
   size_t q = 0;
-  S.wx = q;    q += align256((size_t)L * TB * 4 * H * 4);      // every layer's projection, fp32 [T][B][4H]
-  S.st = q;    q += align256((size_t)L * 2 * TB * H * 4);      // every layer's h and c, fp32 [T][B][H]
-  S.wit = q;   q += align256(IH * 4 * H * 2);                  // Wi transposed for the projection GEMM
-  S.dwx = q;   q += align256(TB * 4 * H * 4);                  // dWx of the layer at hand
-  S.dx = q;    q += align256(2 * TB * IH * 4);                 // dX of the layer above / at hand
-  S.xt = q;    q += align256(IH * Kp * 2);                     // the layer's input, transposed, bf16
-  S.dwxt = q;  q += align256((size_t)4 * H * Kp * 2);          // dWx transposed, bf16
+  S.wx = q;    q += align256((size_t)L * TB * G4 * 4);            // every layer's projection, fp32
+  S.st = q;    q += align256((size_t)L * 2 * TB * dirs * H * 4);  // every layer's h and c, fp32
+  S.wit = q;   q += align256(IH * 4 * H * 2);                     // one direction's Wi transposed
+  S.dwx = q;   q += align256(TB * G4 * 4);                        // dWx of the layer at hand
+  S.dx = q;    q += align256(2 * TB * IH * 4);                    // dX of the layer above / at hand
+  S.xt = q;    q += align256(IH * Kp * 2);                        // the layer's input, transposed, bf16
+  S.dwxt = q;  q += align256((size_t)4 * H * Kp * 2);             // one direction's dWx transposed, bf16
   S.parts = q; q += align256((size_t)BWD_DR_PARTS * IH * 4 * H * 4);  // K parts of dWi
   S.db = q;    q += align256((size_t)4 * H * 4);
+  S.wicat = q; q += dirs > 1 ? align256(IH * G4 * 2) : 0;         // both directions' Wi side by side along K
   S.rec = q;   q += align256(rec_scratch_bytes(B, 1, H, FRNN_CELL_LSTM, 0, path));  // forward recurrence
   S.bl = bwd_layout(B, T, 1, H, FRNN_CELL_LSTM, 0, path);
   S.bwd = q;   q += align256(S.bl.total);
@@ -1565,10 +1580,8 @@ static StackBwdLayout stack_bwd_layout(int L, int T, int B, int I, int H, int pa
 int frnn_lstm_stack_bwd_workspace_bytes(int L, int dirs, int T, int B, int I, int H, int path, size_t* bytes) {
   const int rc = validate_stack(L, dirs, T, B, I, H, path);
   if (rc != FRNN_OK) return rc;
-  if (dirs != 1) return FRNN_EUNSUPPORTED;
-  if (rc != FRNN_OK) return rc;
   if (!bytes) return FRNN_EINVAL;
-  *bytes = kErrBytes + stack_bwd_layout(L, T, B, I, H, path).total;
+  *bytes = kErrBytes + stack_bwd_layout(L, dirs, T, B, I, H, path).total;
   return FRNN_OK;
 }
 
@@ -1579,25 +1592,26 @@ int frnn_lstm_stack_bwd(int L, int dirs, int T, int B, int I, int H, int path, c
                         void* dc0, void* workspace, size_t workspace_bytes, void* stream) {
   int rc = validate_stack(L, dirs, T, B, I, H, path);
   if (rc != FRNN_OK) return rc;
-  if (dirs != 1) return FRNN_EUNSUPPORTED;
   if (!Wi || !Wh) return FRNN_EINVAL;
   if (T > 0 && !x) return FRNN_EINVAL;
-  for (int l = 0; l < L; ++l) {
-    if (!Wi[l] || !Wh[l] || misaligned(Wi[l]) || misaligned(Wh[l])) return FRNN_EINVAL;
-    if ((b_ih && misaligned(b_ih[l])) || (b_hh && misaligned(b_hh[l]))) return FRNN_EINVAL;
-    if ((dWi && misaligned(dWi[l])) || (dWh && misaligned(dWh[l])) || (db_ih && misaligned(db_ih[l])) ||
-        (db_hh && misaligned(db_hh[l])))
+  const int J = L * dirs;  // (layer, direction) pairs, j = l * dirs + k
+  for (int j = 0; j < J; ++j) {
+    if (!Wi[j] || !Wh[j] || misaligned(Wi[j]) || misaligned(Wh[j])) return FRNN_EINVAL;
+    if ((b_ih && misaligned(b_ih[j])) || (b_hh && misaligned(b_hh[j]))) return FRNN_EINVAL;
+    if ((dWi && misaligned(dWi[j])) || (dWh && misaligned(dWh[j])) || (db_ih && misaligned(db_ih[j])) ||
+        (db_hh && misaligned(db_hh[j])))
       return FRNN_EINVAL;
   }
   for (const void* p : {x, h0, c0, dout, dhn, dcn, (const void*)dx, (const void*)dh0, (const void*)dc0,
                         (const void*)workspace})
     if (misaligned(p)) return FRNN_EINVAL;
-  const StackBwdLayout SL = stack_bwd_layout(L, T, B, I, H, path);
+  const StackBwdLayout SL = stack_bwd_layout(L, dirs, T, B, I, H, path);
   if (!workspace || workspace_bytes < kErrBytes + SL.total) return FRNN_EWORKSPACE;
   DevInfo di;
   rc = get_devinfo(&di);
   if (rc != FRNN_OK) return rc;
-  // both recurrences' plans must exist before anything is enqueued
+  // both recurrences' plans must exist before anything is enqueued (every direction of every layer
+  // is one head of H units)
   Problem probe;
   std::memset(&probe, 0, sizeof(probe));
   probe.B = B; probe.T = T; probe.N = 1; probe.D = H; probe.cell = FRNN_CELL_LSTM; probe.r_f32 = 0; probe.wx_f32 = 1;
@@ -1612,18 +1626,20 @@ int frnn_lstm_stack_bwd(int L, int dirs, int T, int B, int I, int H, int path, c
   char* base = reinterpret_cast<char*>(workspace) + kErrBytes;
   if (launch_fill(workspace, kErrBytes, st) != hipSuccess) return FRNN_EHIP;
   const long long TB = (long long)T * B, LBH = (long long)B * H;
+  const long long DH = (long long)dirs * H, G4 = 4LL * dirs * H;  // a layer's output and projection widths
   const int Kp = (int)bwd_kp(T, B);
+  auto in_of = [&](int l) { return l == 0 ? I : (int)DH; };
   auto fill_out = [&](void* p, size_t bytes) { return p ? launch_fill(p, bytes, st) : hipSuccess; };
   if (T == 0) {  // the final states are the initial ones; nothing else receives a gradient
-    for (int l = 0; l < L; ++l) {
-      const int in = (l == 0) ? I : H;
-      if ((dWi && fill_out(dWi[l], (size_t)in * 4 * H * 4) != hipSuccess) ||
-          (dWh && fill_out(dWh[l], (size_t)H * 4 * H * 4) != hipSuccess) ||
-          (db_ih && fill_out(db_ih[l], (size_t)4 * H * 4) != hipSuccess) ||
-          (db_hh && fill_out(db_hh[l], (size_t)4 * H * 4) != hipSuccess))
+    for (int j = 0; j < J; ++j) {
+      const int in = in_of(j / dirs);
+      if ((dWi && fill_out(dWi[j], (size_t)in * 4 * H * 4) != hipSuccess) ||
+          (dWh && fill_out(dWh[j], (size_t)H * 4 * H * 4) != hipSuccess) ||
+          (db_ih && fill_out(db_ih[j], (size_t)4 * H * 4) != hipSuccess) ||
+          (db_hh && fill_out(db_hh[j], (size_t)4 * H * 4) != hipSuccess))
         return FRNN_EHIP;
     }
-    const long long n = (long long)L * LBH;
+    const long long n = (long long)J * LBH;
     const unsigned g = (unsigned)std::min<long long>((n + 255) / 256, 4096);
     if (dh0) {
       if (dhn) hipLaunchKernelGGL(copy_init_kernel, dim3(g), dim3(256), 0, st, dhn, 1, reinterpret_cast<float*>(dh0), n);
@@ -1639,102 +1655,134 @@ int frnn_lstm_stack_bwd(int L, int dirs, int T, int B, int I, int H, int path, c
   float* st_all = reinterpret_cast<float*>(base + SL.st);
   uint16_t* wit = reinterpret_cast<uint16_t*>(base + SL.wit);
   float* dwx = reinterpret_cast<float*>(base + SL.dwx);
-  float* dxb[2] = {reinterpret_cast<float*>(base + SL.dx),
-                   reinterpret_cast<float*>(base + SL.dx) + (size_t)TB * std::max(I, H)};
+  const long long IH = std::max<long long>(I, DH);
+  float* dxb[2] = {reinterpret_cast<float*>(base + SL.dx), reinterpret_cast<float*>(base + SL.dx) + TB * IH};
   uint16_t* xt = reinterpret_cast<uint16_t*>(base + SL.xt);
   uint16_t* dwxt = reinterpret_cast<uint16_t*>(base + SL.dwxt);
   float* parts = reinterpret_cast<float*>(base + SL.parts);
   float* dbt = reinterpret_cast<float*>(base + SL.db);
+  uint16_t* wicat = reinterpret_cast<uint16_t*>(base + SL.wicat);
   int* err = reinterpret_cast<int*>(workspace);
-  auto layer_wx = [&](int l) { return wx_all + (size_t)l * TB * 4 * H; };
-  auto layer_h = [&](int l) { return st_all + (size_t)l * 2 * TB * H; };
-  // 1. the forward again, keeping every layer's projection and states (time-major)
+  auto layer_wx = [&](int l) { return wx_all + (size_t)l * TB * G4; };
+  auto layer_h = [&](int l) { return st_all + (size_t)l * 2 * TB * DH; };
+  auto layer_c = [&](int l) { return layer_h(l) + TB * DH; };
+  // 1. the forward again, keeping every layer's projection and states (time-major, time order);
+  // direction 1 is a head that runs backwards in time over the same buffers
   for (int l = 0; l < L; ++l) {
-    const int in = (l == 0) ? I : H;
-    ProjArgs pa;
-    pa.M = (int)TB; pa.Nc = 4 * H; pa.K = in;
-    pa.A = (l == 0) ? x : (const void*)layer_h(l - 1);
-    pa.a_f32 = (l == 0) ? 0 : 1;
-    pa.lda = in;
-    pa.Bt = wit;
-    pa.ldb = in;
-    pa.a_z = pa.b_z = pa.c_z = 0;
-    pa.nt = 0;  // the recurrence reads Wx next: left where its loads find it soonest
-    pa.b1 = b_ih ? reinterpret_cast<const uint16_t*>(b_ih[l]) : nullptr;
-    pa.b2 = b_hh ? reinterpret_cast<const uint16_t*>(b_hh[l]) : nullptr;
-    pa.C = layer_wx(l);
-    pa.ldc = 4 * H;
-    launch_transpose<uint16_t>(reinterpret_cast<const uint16_t*>(Wi[l]), 4 * H, in, 4 * H, wit, in, st);
-    const dim3 pgrid(((pa.Nc + PJ_BN - 1) / PJ_BN) * ((pa.M + PJ_BM - 1) / PJ_BM));
-    launch_proj(pa, pgrid, st);
-    if (hipGetLastError() != hipSuccess) return FRNN_EHIP;
-    Problem p;
-    std::memset(&p, 0, sizeof(p));
-    p.B = B; p.T = T; p.N = 1; p.D = H; p.cell = FRNN_CELL_LSTM; p.r_f32 = 0;
-    p.Wx = layer_wx(l); p.wx_f32 = 1; p.wx_sb = 4LL * H; p.wx_st = 4LL * H * B;
-    p.R = Wh[l]; p.r_sg = H; p.r_sn = 0; p.r_sd = 4LL * H;
-    p.s0_h = h0 ? reinterpret_cast<const uint16_t*>(h0) + l * LBH : nullptr;
-    p.s0_c = c0 ? reinterpret_cast<const uint16_t*>(c0) + l * LBH : nullptr;
-    p.s0_f32 = 0; p.s0_sb = H; p.s0_sn = H; p.last_sn = H; p.rev_n0 = 1;
-    p.out_h = layer_h(l); p.out_c = layer_h(l) + TB * H;
-    p.out_sb = H; p.out_st = (long long)B * H;
-    rc = run_recurrence(p, path, err, base + SL.rec, st);
-    if (rc != FRNN_OK) return rc;
+    const int in = in_of(l);
+    for (int k = 0; k < dirs; ++k) {
+      const int j = l * dirs + k;
+      ProjArgs pa;
+      pa.M = (int)TB; pa.Nc = 4 * H; pa.K = in;
+      pa.A = (l == 0) ? x : (const void*)layer_h(l - 1);
+      pa.a_f32 = (l == 0) ? 0 : 1;
+      pa.lda = in;
+      pa.Bt = wit;
+      pa.ldb = in;
+      pa.a_z = pa.b_z = pa.c_z = 0;
+      pa.nt = 0;  // the recurrence reads Wx next: left where its loads find it soonest
+      pa.b1 = b_ih ? reinterpret_cast<const uint16_t*>(b_ih[j]) : nullptr;
+      pa.b2 = b_hh ? reinterpret_cast<const uint16_t*>(b_hh[j]) : nullptr;
+      pa.C = layer_wx(l) + (size_t)k * 4 * H;
+      pa.ldc = G4;
+      launch_transpose<uint16_t>(reinterpret_cast<const uint16_t*>(Wi[j]), 4 * H, in, 4 * H, wit, in, st);
+      const dim3 pgrid(((pa.Nc + PJ_BN - 1) / PJ_BN) * ((pa.M + PJ_BM - 1) / PJ_BM));
+      launch_proj(pa, pgrid, st);
+      if (hipGetLastError() != hipSuccess) return FRNN_EHIP;
+      Problem p;
+      std::memset(&p, 0, sizeof(p));
+      p.B = B; p.T = T; p.N = 1; p.D = H; p.cell = FRNN_CELL_LSTM; p.r_f32 = 0;
+      p.Wx = layer_wx(l) + (size_t)k * 4 * H; p.wx_f32 = 1; p.wx_sb = G4; p.wx_st = G4 * B;
+      p.R = Wh[j]; p.r_sg = H; p.r_sn = 0; p.r_sd = 4LL * H;
+      p.s0_h = h0 ? reinterpret_cast<const uint16_t*>(h0) + j * LBH : nullptr;
+      p.s0_c = c0 ? reinterpret_cast<const uint16_t*>(c0) + j * LBH : nullptr;
+      p.s0_f32 = 0; p.s0_sb = H; p.s0_sn = H; p.last_sn = H;
+      p.rev_n0 = k == 1 ? 0 : 1;  // direction 1: the head runs from step T-1 down
+      p.out_h = layer_h(l) + (size_t)k * H; p.out_c = layer_c(l) + (size_t)k * H;
+      p.out_sb = DH; p.out_st = DH * B;
+      rc = run_recurrence(p, path, err, base + SL.rec, st);
+      if (rc != FRNN_OK) return rc;
+    }
   }
-  // 2. the layers from the top: the recurrence's backward, then the projection's
+  // 2. the layers from the top: per direction the recurrence's backward, then the projection's;
+  // direction 1 sees its sequences through views that run from step T-1 down (negative time strides)
   for (int l = L - 1; l >= 0; --l) {
-    const int in = (l == 0) ? I : H;
-    BwdProblem q;
-    std::memset(&q, 0, sizeof(q));
-    q.B = B; q.T = T; q.N = 1; q.D = H; q.cell = FRNN_CELL_LSTM; q.f32 = 0; q.wx_f32 = 1;
-    q.Wx = layer_wx(l); q.wx_sb = 4LL * H; q.wx_st = 4LL * H * B;
-    q.R = Wh[l]; q.r_sg = H; q.r_sn = 0; q.r_sd = 4LL * H;
-    q.s0_h = h0 ? reinterpret_cast<const uint16_t*>(h0) + l * LBH : nullptr;
-    q.s0_c = c0 ? reinterpret_cast<const uint16_t*>(c0) + l * LBH : nullptr;
-    q.s0_sb = H;
-    q.st_h = layer_h(l); q.st_c = layer_h(l) + TB * H; q.st_sb = H; q.st_st = (long long)B * H;
-    q.ds_h = (l == L - 1) ? reinterpret_cast<const float*>(dout) : dxb[(l + 1) & 1];
-    q.dl_h = dhn ? reinterpret_cast<const float*>(dhn) + l * LBH : nullptr;
-    q.dl_c = dcn ? reinterpret_cast<const float*>(dcn) + l * LBH : nullptr;
-    q.last_sb = H;
-    q.dWx = dwx;
-    q.dR = dWh ? reinterpret_cast<float*>(dWh[l]) : nullptr;
-    q.dr_sg = H; q.dr_sn = 0; q.dr_sd = 4LL * H;
-    q.db = dbt;  // the bias is folded into Wx: db_ih = db_hh = sum of dWx, which the dR GEMM's ones row gives
-    q.ds0_h = dh0 ? reinterpret_cast<float*>(dh0) + l * LBH : nullptr;
-    q.ds0_c = dc0 ? reinterpret_cast<float*>(dc0) + l * LBH : nullptr;
-    rc = run_backward(q, path, fbp, di, base + SL.bwd, SL.bl, st);
-    if (rc != FRNN_OK) return rc;
-    const long long nb = 4LL * H;
-    if (db_ih && db_ih[l])
-      hipLaunchKernelGGL(copy_init_kernel, dim3((unsigned)((nb + 255) / 256)), dim3(256), 0, st, dbt, 1,
-                         reinterpret_cast<float*>(db_ih[l]), nb);
-    if (db_hh && db_hh[l])
-      hipLaunchKernelGGL(copy_init_kernel, dim3((unsigned)((nb + 255) / 256)), dim3(256), 0, st, dbt, 1,
-                         reinterpret_cast<float*>(db_hh[l]), nb);
-    // dWi = X^T . dWx over K = T*B (bf16 operands, K split in parts summed in order)
-    if (dWi && dWi[l]) {
-      if (launch_fill(xt, (size_t)in * Kp * 2, st) != hipSuccess || launch_fill(dwxt, (size_t)4 * H * Kp * 2, st) != hipSuccess)
-        return FRNN_EHIP;
+    const int in = in_of(l);
+    const float* dup = (l == L - 1) ? reinterpret_cast<const float*>(dout) : dxb[(l + 1) & 1];  // [T][B][dirs*H]
+    if (dWi) {  // the layer's input, transposed once for both directions' dWi
+      if (launch_fill(xt, (size_t)in * Kp * 2, st) != hipSuccess) return FRNN_EHIP;
       const int ty = (int)std::min<long long>((TB + 31) / 32, 65535);
       if (l == 0) launch_transpose<uint16_t>(reinterpret_cast<const uint16_t*>(x), in, (int)TB, in, xt, Kp, st);
       else hipLaunchKernelGGL(transpose_f32_bf16_kernel, dim3((in + 31) / 32, ty), dim3(256), 0, st, layer_h(l - 1),
                               (long long)in, (int)TB, in, xt, (long long)Kp);
-      hipLaunchKernelGGL(transpose_f32_bf16_kernel, dim3((4 * H + 31) / 32, ty), dim3(256), 0, st, dwx, 4LL * H, (int)TB,
-                         4 * H, dwxt, (long long)Kp);
-      const int kpart = Kp / BWD_DR_PARTS;
-      const long long ptot = (long long)in * 4 * H;
-      if (launch_gemm(false, in, 4 * H, kpart, xt, Kp, dwxt, Kp, parts, 4LL * H, st, BWD_DR_PARTS, kpart, kpart, ptot) !=
-          hipSuccess)
-        return FRNN_EHIP;
-      hipLaunchKernelGGL(sum_parts_kernel, dim3((unsigned)std::min<long long>((ptot + 255) / 256, 65536)), dim3(256), 0, st,
-                         parts, BWD_DR_PARTS, ptot, reinterpret_cast<float*>(dWi[l]));
     }
-    // dX = dWx . Wi^T: the gradient of the layer below's h sequence, or of x
+    for (int k = 0; k < dirs; ++k) {
+      const int j = l * dirs + k;
+      const bool rev = k == 1;
+      const long long wst = G4 * B, sst = DH * B;  // time strides of Wx / dWx and of the states / their gradients
+      const long long w0 = (long long)k * 4 * H + (rev ? (T - 1) * wst : 0);
+      const long long s0 = (long long)k * H + (rev ? (T - 1) * sst : 0);
+      BwdProblem q;
+      std::memset(&q, 0, sizeof(q));
+      q.B = B; q.T = T; q.N = 1; q.D = H; q.cell = FRNN_CELL_LSTM; q.f32 = 0; q.wx_f32 = 1;
+      q.Wx = layer_wx(l) + w0; q.wx_sb = G4; q.wx_st = rev ? -wst : wst;
+      q.R = Wh[j]; q.r_sg = H; q.r_sn = 0; q.r_sd = 4LL * H;
+      q.s0_h = h0 ? reinterpret_cast<const uint16_t*>(h0) + j * LBH : nullptr;
+      q.s0_c = c0 ? reinterpret_cast<const uint16_t*>(c0) + j * LBH : nullptr;
+      q.s0_sb = H;
+      q.st_h = layer_h(l) + s0; q.st_c = layer_c(l) + s0; q.st_sb = DH; q.st_st = rev ? -sst : sst;
+      q.ds_h = dup ? dup + s0 : nullptr;
+      q.dl_h = dhn ? reinterpret_cast<const float*>(dhn) + j * LBH : nullptr;
+      q.dl_c = dcn ? reinterpret_cast<const float*>(dcn) + j * LBH : nullptr;
+      q.last_sb = H;
+      q.dWx = dwx + w0;  // the layout (and views) of Wx
+      q.dR = dWh ? reinterpret_cast<float*>(dWh[j]) : nullptr;
+      q.dr_sg = H; q.dr_sn = 0; q.dr_sd = 4LL * H;
+      q.db = dbt;  // the bias is folded into Wx: db_ih = db_hh = sum of dWx, which the dR GEMM's ones row gives
+      q.ds0_h = dh0 ? reinterpret_cast<float*>(dh0) + j * LBH : nullptr;
+      q.ds0_c = dc0 ? reinterpret_cast<float*>(dc0) + j * LBH : nullptr;
+      rc = run_backward(q, path, fbp, di, base + SL.bwd, SL.bl, st);
+      if (rc != FRNN_OK) return rc;
+      const long long nb = 4LL * H;
+      if (db_ih && db_ih[j])
+        hipLaunchKernelGGL(copy_init_kernel, dim3((unsigned)((nb + 255) / 256)), dim3(256), 0, st, dbt, 1,
+                           reinterpret_cast<float*>(db_ih[j]), nb);
+      if (db_hh && db_hh[j])
+        hipLaunchKernelGGL(copy_init_kernel, dim3((unsigned)((nb + 255) / 256)), dim3(256), 0, st, dbt, 1,
+                           reinterpret_cast<float*>(db_hh[j]), nb);
+      // dWi = X^T . dWx over K = T*B (bf16 operands, K split in parts summed in order); the sum over
+      // the steps does not depend on their order, so both directions use the time-order buffers
+      if (dWi && dWi[j]) {
+        if (launch_fill(dwxt, (size_t)4 * H * Kp * 2, st) != hipSuccess) return FRNN_EHIP;
+        const int ty = (int)std::min<long long>((TB + 31) / 32, 65535);
+        hipLaunchKernelGGL(transpose_f32_bf16_kernel, dim3((4 * H + 31) / 32, ty), dim3(256), 0, st,
+                           dwx + (size_t)k * 4 * H, G4, (int)TB, 4 * H, dwxt, (long long)Kp);
+        const int kpart = Kp / BWD_DR_PARTS;
+        const long long ptot = (long long)in * 4 * H;
+        if (launch_gemm(false, in, 4 * H, kpart, xt, Kp, dwxt, Kp, parts, 4LL * H, st, BWD_DR_PARTS, kpart, kpart, ptot) !=
+            hipSuccess)
+          return FRNN_EHIP;
+        hipLaunchKernelGGL(sum_parts_kernel, dim3((unsigned)std::min<long long>((ptot + 255) / 256, 65536)), dim3(256), 0,
+                           st, parts, BWD_DR_PARTS, ptot, reinterpret_cast<float*>(dWi[j]));
+      }
+    }
+    // dX = sum over directions of dWx_k . Wi_k^T: the gradient of the layer below's h sequence, or
+    // of x; one GEMM over K = dirs*4H with the directions' Wi side by side
     float* dxo = (l == 0) ? reinterpret_cast<float*>(dx) : dxb[l & 1];
-    if (dxo && launch_gemm(false, (int)TB, in, 4 * H, dwx, 4LL * H, Wi[l], 4LL * H, dxo, in, st, 1, 0, 0, 0, true) !=
-                   hipSuccess)
-      return FRNN_EHIP;
+    if (dxo) {
+      const void* wcat = Wi[l * dirs];
+      if (dirs > 1) {
+        for (int k = 0; k < dirs; ++k) {
+          const long long n = (long long)in * 4 * H;
+          hipLaunchKernelGGL(copy_rows_b16_kernel, dim3((unsigned)std::min<long long>((n + 255) / 256, 65536)), dim3(256),
+                             0, st, reinterpret_cast<const uint16_t*>(Wi[l * dirs + k]), 4LL * H, in, 4 * H,
+                             wicat + (size_t)k * 4 * H, G4);
+        }
+        wcat = wicat;
+      }
+      if (launch_gemm(false, (int)TB, in, (int)G4, dwx, G4, wcat, G4, dxo, in, st, 1, 0, 0, 0, true) != hipSuccess)
+        return FRNN_EHIP;
+    }
   }
   return hipGetLastError() == hipSuccess ? FRNN_OK : FRNN_EHIP;
 }

@@ -225,20 +225,23 @@ int frnn_lstm_stack_workspace_bytes(int L, int dirs, int T, int B, int I, int H,
                                     size_t* bytes);
 
 /*
- * Backward of frnn_lstm_stack_fwd for one direction (dirs = 1; dirs = 2 returns
- * FRNN_EUNSUPPORTED): for the loss
+ * Backward of frnn_lstm_stack_fwd, with one or two directions per layer (dirs as there; reading
+ * of two directions: torch.nn.LSTM(bidirectional=True), whose state_dict "5.3 LSTM" reads): for
+ * the loss
  *     L = sum(dout * out) + sum(dhn * hn) + sum(dcn * cn)
- * it writes the gradients of x, Wi[l], Wh[l], b_ih[l], b_hh[l], h0 and c0 ("5.3 LSTM"'s
- * parameters; the chain rule of its cell and projection, the pages printing no gradients).
+ * it writes the gradients of x, Wi[j], Wh[j], b_ih[j], b_hh[j], h0 and c0 ("5.3 LSTM"'s
+ * parameters, j = l * dirs + k for layer l, direction k; the chain rule of its cell and
+ * projection, the pages printing no gradients).
  * Inputs as for frnn_lstm_stack_fwd (bf16), plus (fp32, each may be NULL = zeros):
- *   dout [T, B, H],   dhn, dcn [L, B, H]
+ *   dout [T, B, dirs*H],   dhn, dcn [L*dirs, B, H]
  * Outputs (fp32; a NULL pointer, or a NULL array, is not written):
- *   dx [T, B, I];  dWi[l] [in, 4H];  dWh[l] [H, 4H];  db_ih[l], db_hh[l] [4H] (equal: both biases
- *   enter as their sum);  dh0, dc0 [L, B, H]
+ *   dx [T, B, I];  dWi[j] [in, 4H] (in = I for layer 0, else dirs*H);  dWh[j] [H, 4H];
+ *   db_ih[j], db_hh[j] [4H] (equal: both biases enter as their sum);  dh0, dc0 [L*dirs, B, H]
  * The call runs the forward again, keeping every layer's projection and states in the workspace,
- * then per layer from the top: the head-wise backward (frnn_bwd's kernels on `path`, with Wh read
- * as R through strides), dWi = X^T . dWx and dX = dWx . Wi^T (MFMA GEMMs, bf16 operands, fp32
- * accumulation). T == 0: dh0 = dhn, dc0 = dcn, the weight gradients are zero.
+ * then per layer from the top and per direction: the head-wise backward (frnn_bwd's kernels on
+ * `path`, with Wh read as R through strides, direction 1 through views that run from the last
+ * step to the first), dWi = X^T . dWx, then dX = sum over directions of dWx . Wi^T (MFMA GEMMs,
+ * bf16 operands, fp32 accumulation). T == 0: dh0 = dhn, dc0 = dcn, the weight gradients are zero.
  */
 int frnn_lstm_stack_bwd(int L, int dirs, int T, int B, int I, int H, int path, const void* x,
                         const void* const* Wi, const void* const* Wh, const void* const* b_ih,

@@ -137,7 +137,11 @@ def test_stack_validation(lib):
     assert g(2, 3, 512, 32, 512, 512, 1, ctypes.byref(n)) == EINVAL   # one or two directions
     assert g(2, 0, 512, 32, 512, 512, 1, ctypes.byref(n)) == EINVAL
     assert g(2, 1, 512, 32, 512, 500, 1, ctypes.byref(n)) == EUNSUP
-    assert lib.frnn_lstm_stack_bwd_workspace_bytes(2, 2, 512, 32, 512, 512, 1, ctypes.byref(n)) == EUNSUP
+    assert lib.frnn_lstm_stack_bwd_workspace_bytes(2, 1, 512, 32, 512, 512, 1, ctypes.byref(n)) == 0
+    bwd_one = n.value
+    assert lib.frnn_lstm_stack_bwd_workspace_bytes(2, 2, 512, 32, 512, 512, 1, ctypes.byref(n)) == 0
+    assert n.value > bwd_one   # both directions' projections and states
+    assert lib.frnn_lstm_stack_bwd_workspace_bytes(2, 3, 512, 32, 512, 512, 1, ctypes.byref(n)) == EINVAL
     arr = ctypes.c_void_p * 4
     p = ctypes.c_void_p(0x100000)
     ptrs = arr(0x100000, 0x100000, 0x100000, 0x100000)

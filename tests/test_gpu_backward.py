@@ -315,15 +315,15 @@ def _stack_bwd_case(w, path):
     ct = fi.stack_cotangents(w)
     dev = torch.device("cuda:0")
     g = lambda t: None if t is None else t.to(dev)
-    _log(f"stack bwd case {w.name} L={w.L} T={w.T} B={w.B} I={w.I} H={w.H} path={path}")
+    _log(f"stack bwd case {w.name} L={w.L} dirs={w.dirs} T={w.T} B={w.B} I={w.I} H={w.H} path={path}")
     got = hw.frnn_lstm_stack_bwd(g(x["x"]), [g(t) for t in x["Wi"]], [g(t) for t in x["Wh"]],
                                  [g(t) for t in x["b_ih"]], [g(t) for t in x["b_hh"]], g(x["h0"]), g(x["c0"]),
-                                 g(ct["dout"]), g(ct["dhn"]), g(ct["dcn"]), path=path)
+                                 g(ct["dout"]), g(ct["dhn"]), g(ct["dcn"]), path=path, bidirectional=w.dirs == 2)
     torch.cuda.synchronize()
     f = fi.to_f64
-    ref = oracle.lstm_stack_bwd_p3(f(x["x"]), [f(t) for t in x["Wi"]], [f(t) for t in x["Wh"]],
-                                   [f(t) for t in x["b_ih"]], [f(t) for t in x["b_hh"]], f(x["h0"]), f(x["c0"]),
-                                   f(ct["dout"]), f(ct["dhn"]), f(ct["dcn"]))
+    ref = oracle.default().lstm_stack_bwd(f(x["x"]), [f(t) for t in x["Wi"]], [f(t) for t in x["Wh"]],
+                                          [f(t) for t in x["b_ih"]], [f(t) for t in x["b_hh"]], f(x["h0"]),
+                                          f(x["c0"]), f(ct["dout"]), f(ct["dhn"]), f(ct["dcn"]), dirs=w.dirs)
     names = ("dx", "dWi", "dWh", "db_ih", "db_hh", "dh0", "dc0")
     worst = 0.0
     for name, gv, rv in zip(names, got, ref):
@@ -352,6 +352,23 @@ def test_stack_bwd_small(path):
 def test_stack_bwd_full():
     # the float64 oracle takes about a minute at this size (every gradient depends on every step)
     _stack_bwd_case(fi.WORKLOADS["lstm2_bf16_T512_B32_I512_H512"], "fused")
+
+
+# Two directions per layer (reading A21): direction 1 runs the backward through views that go from
+# the last step to the first, and each layer's dX sums both directions'.
+STACK_BWD_BIDIR = fi.StackWorkload("stack_bwd_bidir", torch.bfloat16, L=2, T=17, B=6, I=64, H=96, seed=262,
+                                   zero_init=False, dirs=2)
+
+
+@pytest.mark.parametrize("path", ["alternating", "fused"])
+def test_stack_bwd_bidirectional(path):
+    _stack_bwd_case(STACK_BWD_BIDIR, path)
+
+
+@pytest.mark.timeout(900)
+def test_stack_bwd_bidirectional_full():
+    # the float64 oracle runs each direction of each layer forward and backward: about two minutes
+    _stack_bwd_case(fi.get_workload("lstm2bi_bf16_T512_B32_I512_H512"), "fused")
 
 
 @pytest.mark.parametrize("path", ["alternating", "fused"])
