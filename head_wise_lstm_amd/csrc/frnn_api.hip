@@ -839,6 +839,14 @@ BwdLayout bwd_layout(int B, int T, int N, int D, int cell, int f32, int path) {
   return L;
 }
 
+// The alternating backward's step in one launch (bwd_step_kernel: each workgroup contracts a whole
+// K = G*D) where K is short, else two (bwd_gate_kernel, then bwd_dh_kernel split over K); the
+// crossover measured between G*D = 1024 and 2048. FRNN_ALT_BWD_ONE_LAUNCH=0/1 pins either.
+bool bwd_one_launch(int G, int D) {
+  const int pin = env_int("FRNN_ALT_BWD_ONE_LAUNCH", -1);
+  return pin >= 0 ? pin != 0 : G * D <= 1024;
+}
+
 std::string bwd_plan_string(const frnn_desc* d, int path, const FusedBwdPlan* fp = nullptr) {
   char buf[512];
   if (path == FRNN_PATH_FUSED && fp) {
@@ -857,17 +865,18 @@ std::string bwd_plan_string(const frnn_desc* d, int path, const FusedBwdPlan* fp
                 "step_launches=%d",
                 path == FRNN_PATH_FUSED ? "fused" : "alternating", cell_name(d->cell),
                 d->in_dtype == FRNN_F32 ? "f32" : "bf16", d->B, d->T, d->N, d->D, (long long)d->T * d->B, G * d->D,
-                d->D, d->D + 1, G * d->D, Kp, 2 * d->T);
+                d->D, d->D + 1, G * d->D, Kp, path == FRNN_PATH_FUSED ? 1 : bwd_one_launch(G, d->D) ? d->T : 2 * d->T);
   return std::string(buf);
 }
 
-// Launch bwd_gate_kernel (step t) or bwd_record_kernel (rec) instantiated for the cell, the
-// operand dtype and the Wx dtype.
-enum BwdCellKernel { kBwdGate, kBwdRecord };
+// Launch bwd_gate_kernel or bwd_step_kernel (step t) or bwd_record_kernel (rec) instantiated for
+// the cell, the operand dtype and the Wx dtype.
+enum BwdCellKernel { kBwdGate, kBwdStep, kBwdRecord };
 
 template <int CELL, bool F32, bool WXF32>
 void launch_bwd_cell_kernel_t(BwdCellKernel k, dim3 grid, dim3 block, hipStream_t st, const BwdArgs& a, int t, float* rec) {
   if (k == kBwdGate) hipLaunchKernelGGL((bwd_gate_kernel<CELL, F32, WXF32>), grid, block, 0, st, a, t);
+  else if (k == kBwdStep) hipLaunchKernelGGL((bwd_step_kernel<CELL, F32, WXF32>), grid, block, 0, st, a, t);
   else hipLaunchKernelGGL((bwd_record_kernel<CELL, F32, WXF32>), grid, block, 0, st, a, rec);
 }
 
@@ -1054,16 +1063,26 @@ int run_backward(const BwdProblem& q, int path, const FusedBwdPlan& fbp, const D
   if (path == FRNN_PATH_FUSED) {
     rc = run_fused_bwd(q.cell, a, fbp, di, base, L, st);
     if (rc != FRNN_OK) return rc;
-    // the gradient that reaches the initial state through R: one more contraction, of step 0's da
-    if (f32) hipLaunchKernelGGL(bwd_dh_kernel<true>, hgrid, dim3(256), 0, st, a, 0);
-    else hipLaunchKernelGGL(bwd_dh_kernel<false>, hgrid, dim3(256), 0, st, a, 0);
-  }
-  for (int t = (path == FRNN_PATH_FUSED ? -1 : T - 1); t >= 0; --t) {
+  } else if (bwd_one_launch(G, D)) {
+    // one launch per step: the contraction of step t+1's da with R^T, the step's gradients as its
+    // epilogue
+    const dim3 tgrid(D / 16, 1, ((B + 15) / 16) * N);
+    for (int t = T - 1; t >= 0; --t)
+      launch_bwd_cell_kernel(kBwdStep, q.cell, f32, a.wx_f32, tgrid, dim3(BWD_STEP_WAVES * 64), st, a, t, nullptr);
+  } else {
+    // per step: the step's gradients, then their contraction with R^T (in K-split parts) for the
+    // step before
     const dim3 g64((unsigned)((BND + 63) / 64)), b64(64);
-    launch_bwd_cell_kernel(kBwdGate, q.cell, f32, a.wx_f32, g64, b64, st, a, t, nullptr);
-    if (f32) hipLaunchKernelGGL(bwd_dh_kernel<true>, hgrid, dim3(256), 0, st, a, t);
-    else hipLaunchKernelGGL(bwd_dh_kernel<false>, hgrid, dim3(256), 0, st, a, t);
+    for (int t = T - 1; t >= 0; --t) {
+      launch_bwd_cell_kernel(kBwdGate, q.cell, f32, a.wx_f32, g64, b64, st, a, t, nullptr);
+      if (t == 0) break;  // step 0's contraction is the one below
+      if (f32) hipLaunchKernelGGL(bwd_dh_kernel<true>, hgrid, dim3(256), 0, st, a, t);
+      else hipLaunchKernelGGL(bwd_dh_kernel<false>, hgrid, dim3(256), 0, st, a, t);
+    }
   }
+  // the gradient that reaches the initial state through R: one more contraction, of step 0's da
+  if (f32) hipLaunchKernelGGL(bwd_dh_kernel<true>, hgrid, dim3(256), 0, st, a, 0);
+  else hipLaunchKernelGGL(bwd_dh_kernel<false>, hgrid, dim3(256), 0, st, a, 0);
   hipLaunchKernelGGL(bwd_final_kernel, dim3(sgrid), dim3(256), 0, st, a);
   if (hipGetLastError() != hipSuccess) return FRNN_EHIP;
   // 3. dR and db: per head, [D+1 rows: h^T and ones] x [G*D columns of da], over K = T*B

@@ -83,21 +83,20 @@ __global__ void __launch_bounds__(256) bwd_hprev_kernel(BwdArgs a) {
   }
 }
 
-// Step t of the serial part: one thread per (b, n, unit), consecutive threads on consecutive
-// units. Reads the recomputed h.R, Wx, bias and the forward states of the step, adds the
-// incoming gradients, and writes dWx, da (operand type, for the dh kernel and dR) and the carry.
+// The coefficients of step t for one (b, n, unit): everything the backward of the step needs
+// that does not depend on the gradient arriving from later steps (the gates from the recomputed
+// h.R, Wx and the bias, the states, and the gradients of the step's own outputs). The record
+// layout (two f32x4) is the fused serial part's (frnn_fused_bwd.hpp):
+//   LSTM: r0 = (o tanh'(c), z i', c_prev f', i z'), r1 = (tanh(c) o', f, dstates_h, dstates_c)
+//   GRU:  r0 = (c3 q r', (h_prev - n) z', c3 r, z), r1 = (dstates_h, c3), c3 = (1 - z) n'
+//   Elman: r0 = (1 - h^2, dstates_h)
+// (x' the derivative of the gate's nonlinearity at its value; dstates includes last_states'
+// gradient at t = T-1).
 template <int CELL, bool F32, bool WXF32>
-__global__ void __launch_bounds__(64) bwd_gate_kernel(BwdArgs a, int t) {
+__device__ __forceinline__ void bwd_coeffs(const BwdArgs& a, int t, int b, int n, int u, f32x4_t& r0, f32x4_t& r1) {
   constexpr int G = cell_gates(CELL);
   typedef typename std::conditional<F32, float, uint16_t>::type op_t;
   typedef typename std::conditional<WXF32, float, uint16_t>::type wx_t;
-  const long long total = (long long)a.B * a.N * a.D;
-  const long long idx = (long long)blockIdx.x * 64 + threadIdx.x;
-  if (idx >= total) return;
-  const int u = (int)(idx % a.D);
-  const long long r = idx / a.D;
-  const int n = (int)(r % a.N);
-  const int b = (int)(r / a.N);
   const int N = a.N, D = a.D;
   const long long tb = (long long)t * a.B + b;
   const float* hr = a.hr + ((long long)n * a.T * a.B + tb) * G * D + u;
@@ -121,114 +120,6 @@ __global__ void __launch_bounds__(64) bwd_gate_kernel(BwdArgs a, int t) {
     if constexpr (WXF32) return v;
     else return bf2f(v);
   };
-  float pre[G], wx[G], bb[G], dp[BWD_KS];
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    pre[g] = hr[(long long)g * D];
-    wx[g] = fw(wxp[wbase + (long long)g * N * D]);
-    bb[g] = f(bp[hb ? (long long)(g * N + n) * D + u : 0]);
-  }
-  const long long BND = (long long)a.B * N * D;
-#pragma unroll
-  for (int k = 0; k < BWD_KS; ++k) dp[k] = a.dhpart[(k < a.ks ? k * BND : 0) + idx];
-  float dh = dsh[hds ? sidx : 0] + dlh[hdl ? lidx : 0];
-#pragma unroll
-  for (int k = 0; k < BWD_KS; ++k) dh += k < a.ks ? dp[k] : 0.0f;
-  float dw[G], dav[G];
-  if constexpr (CELL == CELL_LSTM) {
-    const bool hdc = a.ds_c != nullptr, hlc = a.dl_c != nullptr && t == a.T - 1, hs0 = a.s0_c != nullptr;
-    const float* dsc = hdc ? a.ds_c : a.zeros;
-    const float* dlc = hlc ? a.dl_c : a.zeros;
-    const op_t* s0c = hs0 ? reinterpret_cast<const op_t*>(a.s0_c) : zop;
-    const float ct = a.st_c[sidx];
-    const float cprev = a.st_c[t > 0 ? sidx - a.st_st : sidx];
-    const float c0 = f(s0c[hs0 ? s0idx : 0]);
-    const float cp = t > 0 ? cprev : c0;
-    const float dc = a.carry[idx] + dsc[hdc ? sidx : 0] + dlc[hlc ? lidx : 0];
-    const float ig = sigmoid_f(pre[0] + wx[0] + bb[0]);
-    const float fg = sigmoid_f(pre[1] + wx[1] + bb[1]);
-    const float zg = tanh_f(pre[2] + wx[2] + bb[2]);
-    const float og = sigmoid_f(pre[3] + wx[3] + bb[3]);
-    const float tc = tanh_f(ct);
-    const float dct = dc + dh * og * (1.0f - tc * tc);
-    dw[0] = dct * zg * ig * (1.0f - ig);
-    dw[1] = dct * cp * fg * (1.0f - fg);
-    dw[2] = dct * ig * (1.0f - zg * zg);
-    dw[3] = dh * tc * og * (1.0f - og);
-    a.carry[idx] = dct * fg;
-#pragma unroll
-    for (int g = 0; g < 4; ++g) dav[g] = dw[g];
-  } else if constexpr (CELL == CELL_GRU) {
-    const bool hs0 = a.s0_h != nullptr;
-    const op_t* s0h = hs0 ? reinterpret_cast<const op_t*>(a.s0_h) : zop;
-    const float hprev = a.st_h[t > 0 ? sidx - a.st_st : sidx];
-    const float h0 = f(s0h[hs0 ? s0idx : 0]);
-    const float hp = t > 0 ? hprev : h0;
-    dh += a.carry[idx];
-    const float rg = sigmoid_f(pre[0] + wx[0] + bb[0]);
-    const float zg = sigmoid_f(pre[1] + wx[1] + bb[1]);
-    const float q = pre[2] + bb[2];
-    const float ng = tanh_f(wx[2] + rg * q);
-    const float dq = dh * (1.0f - zg) * (1.0f - ng * ng);
-    dw[0] = dq * q * rg * (1.0f - rg);
-    dw[1] = dh * (hp - ng) * zg * (1.0f - zg);
-    dw[2] = dq;
-    dav[0] = dw[0];
-    dav[1] = dw[1];
-    dav[2] = dq * rg;
-    a.carry[idx] = dh * zg;
-  } else {
-    const float ht = a.st_h[sidx];
-    dw[0] = dh * (1.0f - ht * ht);
-    dav[0] = dw[0];
-  }
-  if (a.dWx) {
-#pragma unroll
-    for (int g = 0; g < G; ++g) a.dWx[wbase + (long long)g * N * D] = dw[g];
-  }
-  const long long drow = ((long long)n * a.Kp + tb) * G * D + u;
-#pragma unroll
-  for (int g = 0; g < G; ++g) st_op(a.da, drow + (long long)g * D, dav[g], F32);
-}
-
-// Coefficient records of every step, for the fused serial part (layout: frnn_fused_bwd.hpp): one
-// thread per (t, b, n, unit); record index s = T-1-t. The gradients of the step's outputs (and of
-// last_states at t = T-1) ride along.
-template <int CELL, bool F32, bool WXF32>
-__global__ void __launch_bounds__(256) bwd_record_kernel(BwdArgs a, float* rec) {
-  constexpr int G = cell_gates(CELL);
-  typedef typename std::conditional<F32, float, uint16_t>::type op_t;
-  typedef typename std::conditional<WXF32, float, uint16_t>::type wx_t;
-  const long long total = (long long)a.T * a.B * a.N * a.D;
-  const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= total) return;
-  const int u = (int)(idx % a.D);
-  long long r = idx / a.D;
-  const int n = (int)(r % a.N);
-  r /= a.N;
-  const int b = (int)(r % a.B);
-  const int t = (int)(r / a.B);
-  const int N = a.N, D = a.D;
-  const long long tb = (long long)t * a.B + b;
-  const float* hr = a.hr + ((long long)n * a.T * a.B + tb) * G * D + u;
-  const long long wbase = (long long)b * a.wx_sb + (long long)t * a.wx_st + (long long)n * D + u;
-  const long long sidx = (long long)b * a.st_sb + (long long)t * a.st_st + (long long)n * D + u;
-  const long long lidx = (long long)b * a.last_sb + (long long)n * D + u;
-  const long long s0idx = (long long)b * a.s0_sb + (long long)n * D + u;
-  const op_t* zop = reinterpret_cast<const op_t*>(a.zeros);
-  const wx_t* wxp = reinterpret_cast<const wx_t*>(a.Wx);
-  const bool hb = a.bias != nullptr, hds = a.ds_h != nullptr, hdl = a.dl_h != nullptr && t == a.T - 1;
-  const op_t* bp = hb ? reinterpret_cast<const op_t*>(a.bias) : zop;
-  const float* dsh = hds ? a.ds_h : a.zeros;
-  const float* dlh = hdl ? a.dl_h : a.zeros;
-  auto f = [](op_t v) -> float {
-    if constexpr (F32) return v;
-    else return bf2f(v);
-  };
-  auto fw = [](wx_t v) -> float {
-    if constexpr (WXF32) return v;
-    else return bf2f(v);
-  };
   float pre[G], wx[G], bb[G];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
@@ -237,7 +128,6 @@ __global__ void __launch_bounds__(256) bwd_record_kernel(BwdArgs a, float* rec) 
     bb[g] = f(bp[hb ? (long long)(g * N + n) * D + u : 0]);
   }
   const float ds_h = dsh[hds ? sidx : 0] + dlh[hdl ? lidx : 0];
-  f32x4_t r0, r1;
   if constexpr (CELL == CELL_LSTM) {
     const bool hdc = a.ds_c != nullptr, hlc = a.dl_c != nullptr && t == a.T - 1, hs0 = a.s0_c != nullptr;
     const float* dsc = hdc ? a.ds_c : a.zeros;
@@ -273,17 +163,12 @@ __global__ void __launch_bounds__(256) bwd_record_kernel(BwdArgs a, float* rec) 
     r0 = f32x4_t{1.0f - ht * ht, ds_h, 0.0f, 0.0f};
     r1 = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
   }
-  const long long s = (long long)(a.T - 1 - t);
-  f32x4_t* out = reinterpret_cast<f32x4_t*>(rec + ((((s * a.B + b) * N + n) * D + u) * 8));
-  out[0] = r0;
-  out[1] = r1;
 }
 
-// dWx, the dR operand da and (at t = 0) the carries from the fused serial part's (dh, dc) and the
-// records: one thread per (t, b, n, unit).
-template <int CELL, bool F32>
-__global__ void __launch_bounds__(256) bwd_post_kernel(BwdArgs a, const float* rec, const float* dstate) {
-  constexpr int G = cell_gates(CELL);
+// Coefficient records of every step, for the fused serial part: one thread per (t, b, n, unit);
+// record index s = T-1-t.
+template <int CELL, bool F32, bool WXF32>
+__global__ void __launch_bounds__(256) bwd_record_kernel(BwdArgs a, float* rec) {
   const long long total = (long long)a.T * a.B * a.N * a.D;
   const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
   if (idx >= total) return;
@@ -293,13 +178,22 @@ __global__ void __launch_bounds__(256) bwd_post_kernel(BwdArgs a, const float* r
   r /= a.N;
   const int b = (int)(r % a.B);
   const int t = (int)(r / a.B);
-  const int N = a.N, D = a.D;
+  f32x4_t r0, r1;
+  bwd_coeffs<CELL, F32, WXF32>(a, t, b, n, u, r0, r1);
   const long long s = (long long)(a.T - 1 - t);
-  const long long ri = ((s * a.B + b) * N + n) * D + u;
-  const f32x4_t r0 = reinterpret_cast<const f32x4_t*>(rec)[ri * 2];
-  const f32x4_t r1 = reinterpret_cast<const f32x4_t*>(rec)[ri * 2 + 1];
-  const float2 st = reinterpret_cast<const float2*>(dstate)[ri];
-  const float dh = st.x, dc = st.y;
+  f32x4_t* out = reinterpret_cast<f32x4_t*>(rec + ((((s * a.B + b) * a.N + n) * a.D + u) * 8));
+  out[0] = r0;
+  out[1] = r1;
+}
+
+// The gradients of step t for one (b, n, unit) from its coefficients and the gradients reaching
+// its state: dh (h_t) and, for the LSTM, dc (c_t, everything included). Writes dWx and the dR
+// operand da; returns the gradient carried to step t-1 past R (LSTM: dc . f; GRU: dh . z; Elman: 0).
+template <int CELL, bool F32>
+__device__ __forceinline__ float bwd_apply(const BwdArgs& a, int t, int b, int n, int u, f32x4_t r0, f32x4_t r1,
+                                           float dh, float dc) {
+  constexpr int G = cell_gates(CELL);
+  const int N = a.N, D = a.D;
   float dw[G], dav[G];
   float carry = 0.0f;
   if constexpr (CELL == CELL_LSTM) {
@@ -330,7 +224,165 @@ __global__ void __launch_bounds__(256) bwd_post_kernel(BwdArgs a, const float* r
   const long long drow = ((long long)n * a.Kp + (long long)t * a.B + b) * G * D + u;
 #pragma unroll
   for (int g = 0; g < G; ++g) st_op(a.da, drow + (long long)g * D, dav[g], F32);
+  return carry;
+}
+
+// dWx, the dR operand da and (at t = 0) the carries from the fused serial part's (dh, dc) and the
+// records: one thread per (t, b, n, unit).
+template <int CELL, bool F32>
+__global__ void __launch_bounds__(256) bwd_post_kernel(BwdArgs a, const float* rec, const float* dstate) {
+  const long long total = (long long)a.T * a.B * a.N * a.D;
+  const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= total) return;
+  const int u = (int)(idx % a.D);
+  long long r = idx / a.D;
+  const int n = (int)(r % a.N);
+  r /= a.N;
+  const int b = (int)(r % a.B);
+  const int t = (int)(r / a.B);
+  const int N = a.N, D = a.D;
+  const long long s = (long long)(a.T - 1 - t);
+  const long long ri = ((s * a.B + b) * N + n) * D + u;
+  const f32x4_t r0 = reinterpret_cast<const f32x4_t*>(rec)[ri * 2];
+  const f32x4_t r1 = reinterpret_cast<const f32x4_t*>(rec)[ri * 2 + 1];
+  const float2 st = reinterpret_cast<const float2*>(dstate)[ri];
+  const float carry = bwd_apply<CELL, F32>(a, t, b, n, u, r0, r1, st.x, st.y);
   if (t == 0) a.carry[((long long)b * N + n) * D + u] = carry;
+}
+
+// Step t of the alternating serial part, one thread per (b, n, unit), consecutive threads on
+// consecutive units: the gradient reaching h_t through R (the K-split parts that step t+1's
+// bwd_dh_kernel left in dhpart) plus the step's own, then the step's coefficients (bwd_coeffs) and
+// gradients (bwd_apply): dWx, da and the carry.
+template <int CELL, bool F32, bool WXF32>
+__global__ void __launch_bounds__(64) bwd_gate_kernel(BwdArgs a, int t) {
+  const long long total = (long long)a.B * a.N * a.D;
+  const long long idx = (long long)blockIdx.x * 64 + threadIdx.x;
+  if (idx >= total) return;
+  const int u = (int)(idx % a.D);
+  const long long r = idx / a.D;
+  const int n = (int)(r % a.N);
+  const int b = (int)(r / a.N);
+  const long long BND = total;
+  float dp[BWD_KS];
+#pragma unroll
+  for (int k = 0; k < BWD_KS; ++k) dp[k] = a.dhpart[(k < a.ks ? k * BND : 0) + idx];
+  const float cin = CELL != CELL_ELMAN ? a.carry[idx] : 0.0f;
+  f32x4_t r0, r1;
+  bwd_coeffs<CELL, F32, WXF32>(a, t, b, n, u, r0, r1);
+  float dhr = 0.0f;
+#pragma unroll
+  for (int k = 0; k < BWD_KS; ++k) dhr += k < a.ks ? dp[k] : 0.0f;
+  float dh, dc = 0.0f;
+  if constexpr (CELL == CELL_LSTM) {
+    dh = dhr + r1[2];
+    dc = cin + r1[3] + dh * r0[0];
+  } else if constexpr (CELL == CELL_GRU) {
+    dh = dhr + r1[0] + cin;
+  } else {
+    dh = dhr + r0[1];
+  }
+  const float carry = bwd_apply<CELL, F32>(a, t, b, n, u, r0, r1, dh, dc);
+  if (CELL != CELL_ELMAN) a.carry[idx] = carry;
+}
+
+// Step t of the alternating serial part in one launch: the contraction dhr = da_{t+1} . R^T for
+// one 16-unit tile of d and 16 batch columns (grid (D/16, 1, ceil(B/16)*N); skipped at t = T-1,
+// where nothing reaches h through R), then, as its epilogue, the step's backward for the tile's 16
+// units of the 16 batch columns (bwd_coeffs, then bwd_apply). The tile's result puts units
+// 4*(l/16)..+3 of batch column l%16 in lane l. The 16 waves take the k-tiles of K = G*D 16 apart,
+// issue all of a batch of fragment loads before its MFMAs, and meet in LDS. da_{t+1} and da_t are
+// different rows of the da buffer, and each carry belongs to one lane, so no workgroup overwrites
+// what another of the same launch still reads.
+//
+// Against bwd_gate_kernel + bwd_dh_kernel (two launches per step) it trades a launch for a whole K
+// of R and da per workgroup (G*D*64 bytes): the planner takes it where G*D <= 1024 (ms per call,
+// one launch / two: LSTM B=8 N=3 D=256 6.02 / 7.69, Elman B=64 N=12 D=64 14.44 / 16.94, LSTM fp32
+// D=32 0.119 / 0.148), and the two launches above (LSTM D=768 9.80 / 7.85, GRU D=768 8.05 / 7.50,
+// the two-layer LSTM's H=512 14.57 / 14.25).
+constexpr int BWD_STEP_WAVES = 16;
+
+template <int CELL, bool F32, bool WXF32>
+__global__ void __launch_bounds__(BWD_STEP_WAVES * 64) bwd_step_kernel(BwdArgs a, int t) {
+  constexpr int NW = BWD_STEP_WAVES;
+  __shared__ f32x4_t part[NW][64];
+  constexpr int G = cell_gates(CELL);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int col = lane & 15, quad = lane >> 4;
+  const int D = a.D;
+  const int dt = blockIdx.x;
+  const int nbb = (a.B + 15) / 16;
+  const int n = blockIdx.z / nbb, b0 = (blockIdx.z % nbb) * 16;
+  const bool colv = b0 + col < a.B;
+  // the epilogue's inputs first (waves 0-3, unit 4*(l/16) + wave of lane l): they do not depend on
+  // the contraction, so their loads and transcendentals overlap it
+  const bool epi = wave < 4 && colv;
+  const int ue = dt * 16 + 4 * quad + (wave & 3);
+  const long long cidx = ((long long)(b0 + col) * a.N + n) * D + ue;
+  f32x4_t r0 = {0.f, 0.f, 0.f, 0.f}, r1 = {0.f, 0.f, 0.f, 0.f};
+  float cin = 0.0f;
+  if (epi) {
+    bwd_coeffs<CELL, F32, WXF32>(a, t, b0 + col, n, ue, r0, r1);
+    if (CELL != CELL_ELMAN) cin = a.carry[cidx];
+  }
+  f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+  if (t + 1 < a.T) {
+    constexpr int KW = F32 ? 4 : 32;
+    constexpr int KB = F32 ? 16 : 8;
+    typedef typename std::conditional<F32, float, bf16x8_t>::type frag_t;
+    const int KT = G * D / KW;
+    const long long drow = ((long long)n * a.Kp + (long long)(t + 1) * a.B + b0 + col) * G * D;
+    const long long rbase = (((long long)n * (D / 16) + dt) * KT) * 64 + lane;
+    for (int k0 = wave; k0 < KT; k0 += NW * KB) {
+      frag_t ra[KB], db[KB];
+#pragma unroll
+      for (int j = 0; j < KB; ++j) {
+        const int k = k0 + NW * j;
+        const bool kv = k < KT;
+        if constexpr (F32) {
+          ra[j] = kv ? reinterpret_cast<const float*>(a.rpk)[rbase + (long long)k * 64] : 0.0f;
+          db[j] = (kv && colv) ? reinterpret_cast<const float*>(a.da)[drow + k * KW + quad] : 0.0f;
+        } else {
+          u32x4_t rv = {0u, 0u, 0u, 0u}, dv = {0u, 0u, 0u, 0u};
+          if (kv) rv = reinterpret_cast<const u32x4_t*>(a.rpk)[rbase + (long long)k * 64];
+          if (kv && colv) dv = *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const uint16_t*>(a.da) + drow + k * KW + 8 * quad);
+          ra[j] = __builtin_bit_cast(bf16x8_t, rv);
+          db[j] = __builtin_bit_cast(bf16x8_t, dv);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < KB; j += 2) {
+        if (k0 + NW * j >= KT) break;  // (uniform in the wave)
+        if constexpr (F32) {
+          acc0 = mfma_f32(ra[j], db[j], acc0);
+          acc1 = mfma_f32(ra[j + 1], db[j + 1], acc1);
+        } else {
+          acc0 = mfma_bf16(ra[j], db[j], acc0);
+          acc1 = mfma_bf16(ra[j + 1], db[j + 1], acc1);
+        }
+      }
+    }
+  }
+  part[wave][lane] = acc0 + acc1;
+  __syncthreads();
+  // the epilogue: wave i < 4 takes unit 4*(l/16) + i of lane l, so that a lane's loads and stores
+  // are those of one element (one lane handling four units in turn would wait for each unit's
+  // stores before the next unit's loads: on gfx9 a wave's memory counter retires both in order)
+  if (!epi) return;
+  float dhr = 0.0f;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) dhr += reinterpret_cast<const float*>(&part[w][lane])[wave];
+  float dh, dc = 0.0f;
+  if constexpr (CELL == CELL_LSTM) {
+    dh = dhr + r1[2];
+    dc = cin + r1[3] + dh * r0[0];
+  } else if constexpr (CELL == CELL_GRU) {
+    dh = dhr + r1[0] + cin;
+  } else {
+    dh = dhr + r0[1];
+  }
+  const float carry = bwd_apply<CELL, F32>(a, t, b0 + col, n, ue, r0, r1, dh, dc);
+  if (CELL != CELL_ELMAN) a.carry[cidx] = carry;
 }
 
 // R in the dh kernel's A-fragment order: [N][D/16 row tiles][G*D/KW k-tiles][64 lanes] x (8 bf16

@@ -147,6 +147,21 @@ def test_bwd_full(name, path):
     run_bwd_case(w, path)
 
 
+# Both forms of the alternating backward's step, pinned with FRNN_ALT_BWD_ONE_LAUNCH: one launch
+# (the contraction with the step's gradients as its epilogue; the choice for G*D <= 1024) and two
+# (the gradients, then the K-split contraction).
+@pytest.mark.parametrize("one", [1, 0])
+@pytest.mark.parametrize("w", [x for x in SMALL if x.name in ("bwd_lstm_bf16_ragged_D64", "bwd_gru_bf16_D256",
+                                                                "bwd_elman_bf16_D128", "bwd_lstm_f32_D32")],
+                         ids=lambda w: w.name)
+def test_bwd_alternating_each_form(w, one):
+    hw = _hw()
+    with _env({"FRNN_ALT_BWD_ONE_LAUNCH": one}):
+        plan = hw.frnn_bwd_plan_str(hw._desc(w.B, w.T, w.N, w.D, w.cell, w.dtype), "alternating")
+    assert f"step_launches={w.T if one else 2 * w.T}" in plan, plan
+    run_bwd_case(w, "alternating", env={"FRNN_ALT_BWD_ONE_LAUNCH": one})
+
+
 # Every fused backward design on the small bf16 cases, pinned with FRNN_FUSED_BWD_PX: the
 # partial-sum design (the planner's choice where it has one), the da-exchange design, and, for
 # heads of at most 64 units, the single-workgroup design on fp32 fragments of R (the planner's
