@@ -289,13 +289,23 @@ int env_int(const char* name, int dflt) {
 // kernels with 16-byte exchange polls): a base for the exchange, the barrier and the gates, plus
 // each compute wave's MFMA chain (MTW*KTW tiles), its poll loads per lane and round, and the
 // number of compute waves (more waves meet at every barrier and split the K-sum exchange). The
-// single-workgroup design has no exchange: its base is lower and its chain runs over the whole K.
+// single-workgroup design has no exchange; its chain runs over the whole K. Fitted by least squares
+// to 76 measured single-workgroup designs on eleven shapes (LSTM, GRU, Elman; D 32-128; B 16-64;
+// N 2-12; RMS 37 ns against 265 for a base shared by the cells): a base per cell (what the I/O wave
+// streams and the gates cost: the LSTM's four gates of Wx, five transcendentals and two states a
+// unit, the GRU's three, three and one, the Elman head's one gate through its DMA ring), the MFMA
+// chain, and the batch rows (the states the compute waves store, the Wx words the I/O wave loads).
 constexpr double kStepBaseDie = 0.700, kStepPerMfma = 0.0164, kStepPerPollLoad = 0.0141, kStepPerWave = 0.0181;
-constexpr double kStepBaseLocal = 0.37, kStepPerMfmaLocal = 0.0184;
+constexpr double kStepBaseLocalLstm = 0.440, kStepBaseLocalGru = 0.281, kStepBaseLocalElman = 0.161;
+constexpr double kStepPerMfmaLocal = 0.0513, kStepPerRowLocal = 0.0145;
 constexpr double kLaunchUs = 15.0;  // R packing, fills and the launch of one chunk
 
-double step_cost(bool local, int br, int ncw, int ks, int mtw, int ktw) {
-  if (local) return kStepBaseLocal + kStepPerMfmaLocal * mtw * ktw;
+double step_cost(bool local, int cell, int br, int ncw, int ks, int mtw, int ktw) {
+  if (local) {
+    const double base = cell == FRNN_CELL_LSTM ? kStepBaseLocalLstm : cell == FRNN_CELL_GRU ? kStepBaseLocalGru
+                                                                                           : kStepBaseLocalElman;
+    return base + kStepPerMfmaLocal * mtw * ktw + kStepPerRowLocal * br;
+  }
   const int np = (br * ktw * 32 / fused_poll_words(ks, mtw, ktw) + 63) / 64;
   return kStepBaseDie + kStepPerMfma * mtw * ktw + kStepPerPollLoad * np + kStepPerWave * ncw;
 }
@@ -332,7 +342,7 @@ int plan_fused(const Problem& p, const DevInfo& di, FusedPlan* out) {
     fp.chunks = (int)((p.B + bmax - 1) / bmax);
     fp.Bc = (int)(((long long)p.B + fp.chunks - 1) / fp.chunks);
     fp.groups = p.N * ((fp.Bc + fp.BR - 1) / fp.BR);
-    fp.cost_us = fp.chunks * (T * step_cost(fp.local, fp.BR, fp.ncw, fp.ks, fp.mtw, fp.ktw) + kLaunchUs);
+    fp.cost_us = fp.chunks * (T * step_cost(fp.local, p.cell, fp.BR, fp.ncw, fp.ks, fp.mtw, fp.ktw) + kLaunchUs);
     if (!fp.local) {
       const int per_die = (fp.groups + di.n_xcd - 1) / di.n_xcd;
       fp.slots = per_die * fp.W;

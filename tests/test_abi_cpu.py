@@ -213,6 +213,13 @@ def test_planner_choices_for_the_workloads(lib):
     # Elman D=64: a whole head per workgroup, four batch rows each so that 192 workgroups fill the CUs
     s = plan(D(B=64, T=2048, N=12, Dm=64, cell=1), 1)
     assert "workgroup-local" in s and "BR=4 " in s and "groups=192 " in s
+    # twelve LSTM heads of 64 units at B=16: a die-local design of four workgroups a head (measured
+    # 0.81 us per step against 0.96 for a whole head per workgroup, whose I/O wave streams four
+    # gates of Wx); the Elman and GRU heads of that shape keep the single-workgroup design
+    s = plan(D(B=16, T=512, N=12, Dm=64), 1)
+    assert "design=die-local " in s and "BR=4 " in s and "W=4 " in s
+    assert "workgroup-local" in plan(D(B=16, T=512, N=12, Dm=64, cell=1), 1)
+    assert "workgroup-local" in plan(D(B=16, T=512, N=12, Dm=64, cell=2), 1)
     # fp32 LSTM D=32
     s = plan(D(B=2, T=16, N=1, Dm=32, ind=0), 1)
     assert "workgroup-local" in s and "dtype=f32" in s
@@ -252,7 +259,8 @@ def test_gru_cell_accepted_and_sized(lib):
 @pytest.mark.skipif(torch.cuda.is_available(), reason="planner model of a 256-CU, 8-die device (no GPU here)")
 def test_planner_gru_matches_lstm_tiles(lib):
     """A GRU head has as many 16-row tiles as an LSTM head of the same width, so it gets the same
-    design on the same shape."""
+    design on these shapes (the predicted time differs: the single-workgroup step model has a base
+    per cell)."""
     for (B, N, Dm) in [(16, 1, 768), (8, 3, 256), (2, 1, 32), (64, 12, 64)]:
         for ind in (0, 1):
             try:
@@ -263,7 +271,8 @@ def test_planner_gru_matches_lstm_tiles(lib):
                 continue
             sg = plan(D(B=B, T=8, N=N, Dm=Dm, cell=2, ind=ind), 1)
             assert "cell=gru" in sg
-            assert sg.replace("cell=gru", "cell=lstm") == sl
+            strip = lambda x: re.sub(r" predicted_us=\S+", "", x)
+            assert strip(sg.replace("cell=gru", "cell=lstm")) == strip(sl)
 
 
 def test_bwd_validation_and_workspace(lib):
