@@ -10,6 +10,7 @@ gradient of the gate pre-activations (unit roundoff 2^-9, about 2e-3, on each op
 element carries a few units of it relative to the largest element; 1e-2 is five. tol = 1e-5 for
 fp32 inputs, a few hundred fp32 units for sums over up to B*T*D terms.
 """
+import ctypes
 import os
 import sys
 
@@ -384,6 +385,56 @@ def test_stack_bwd_bidirectional(path):
 def test_stack_bwd_bidirectional_full():
     # the float64 oracle runs each direction of each layer forward and backward: about two minutes
     _stack_bwd_case(fi.get_workload("lstm2bi_bf16_T512_B32_I512_H512"), "fused")
+
+
+@pytest.mark.parametrize("cell", ["lstm", "gru"])
+@pytest.mark.parametrize("path", ["alternating", "fused"])
+def test_bwd_negative_strides_time_reversed(path, cell):
+    """frnn_bwd through the C ABI over views that run backwards in time (negative step strides,
+    the pointers at step 0 of each view, which is the stored sequence's last step): Wx, the states,
+    their gradients and dWx. Equals the oracle's backward of the time-order sequence."""
+    hw = _hw()
+    B, T, N, D = 5, 11, 2, 64
+    G, S = {"lstm": (4, 2), "gru": (3, 1)}[cell]
+    w = fi.HeadwiseWorkload(f"bwd_negstride_{cell}", cell, torch.bfloat16, B=B, T=T, N=N, D=D, seed=243, s0_var=1.0)
+    x = fi.make_inputs(w)
+    ct = fi.backward_cotangents(w)
+    dev = torch.device("cuda:0")
+    Wx, R, b, s0 = x["Wx"].to(dev), x["R"].to(dev), x["b"].to(dev), x["states0"].to(dev)
+    st, _ = hw.frnn_fwd(Wx, R, b, s0, cell=cell, path="fused")           # time order
+    wx_rev = Wx.flip(1).contiguous()                                     # stored last step first
+    st_rev = st.flip(2).contiguous()
+    ds_rev = ct["dstates"].to(dev).flip(2).contiguous()
+    dl = ct["dlast"].to(dev).contiguous()
+    dwx_rev = torch.full((B, T, G, N, D), float("nan"), dtype=torch.float32, device=dev)
+    dR = torch.empty((G, N, D, D), dtype=torch.float32, device=dev)
+    db = torch.empty((G, N, D), dtype=torch.float32, device=dev)
+    ds0 = torch.empty((S, B, 1, N, D), dtype=torch.float32, device=dev)
+    d = hw._desc(B, T, N, D, cell, torch.bfloat16)
+    d.wx_sb, d.wx_st = T * G * N * D, -G * N * D
+    d.st_ss, d.st_sb, d.st_st = B * T * N * D, T * N * D, -N * D
+    wx0 = wx_rev.data_ptr() + (T - 1) * G * N * D * 2                    # element [0, 0] of each reversed view
+    st0 = st_rev.data_ptr() + (T - 1) * N * D * 4
+    ds0p = ds_rev.data_ptr() + (T - 1) * N * D * 4
+    dwx0 = dwx_rev.data_ptr() + (T - 1) * G * N * D * 4
+    ws = torch.empty(hw.frnn_bwd_workspace_bytes(d, path), dtype=torch.uint8, device=dev)
+    hw.frnn_init()
+    p = ctypes.c_void_p
+    _log(f"bwd negative strides case cell={cell} path={path}")
+    rc = hw.load().frnn_bwd(ctypes.byref(d), hw._path(path), p(wx0), p(R.data_ptr()), p(b.data_ptr()), p(s0.data_ptr()),
+                            p(st0), p(ds0p), p(dl.data_ptr()), p(dwx0), p(dR.data_ptr()), p(db.data_ptr()),
+                            p(ds0.data_ptr()), p(ws.data_ptr()), ws.numel(), hw._stream_handle(dev))
+    assert rc == 0, hw.frnn_status_str(rc)
+    hw.frnn_check(ws)
+    f = fi.to_f64
+    ref = oracle.headwise_bwd(cell, f(x["Wx"]), f(x["R"]), f(x["b"]), f(x["states0"]), f(ct["dstates"]), f(ct["dlast"]))
+    got = (dwx_rev.flip(1), dR, db, ds0)
+    for name, gv, rv in zip(("dWx", "dR", "db", "dstates0"), got, ref):
+        gv = gv.double().cpu().numpy()
+        scale = max(1.0, float(np.abs(rv).max()))
+        err = float(np.abs(gv - rv).max())
+        _log(f"  {name}: err={err:.3e} scale={scale:.3g}")
+        assert np.all(np.isfinite(gv)) and err <= TOL[torch.bfloat16] * scale, name
 
 
 @pytest.mark.parametrize("path", ["alternating", "fused"])
