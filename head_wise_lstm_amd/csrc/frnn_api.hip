@@ -170,17 +170,24 @@ int launch_resident(const void* fn, int grid, int threads, size_t lds, void** ar
 }
 
 // ----------------------------------------------------------------------------- kernel tables
-const FusedVariant* find_fused(int cell, int f32, int local, int ncw, int ks, int mtw, int ktw) {
+// The instantiated design with these variables and R^T wholly in VGPRs (ktl = 0), or, with
+// ktl < 0, the one that keeps the fewest k-tiles of it in LDS.
+const FusedVariant* find_fused(int cell, int f32, int local, int ncw, int ks, int mtw, int ktw, int ktl = 0) {
   const FusedTable t = cell == FRNN_CELL_LSTM ? fused_table_lstm()
                        : cell == FRNN_CELL_GRU ? fused_table_gru()
                                                : fused_table_elman();
+  const FusedVariant* best = nullptr;
   for (int i = 0; i < t.n; ++i) {
     const FusedVariant& v = t.v[i];
-    if (v.cell == cell && v.f32 == f32 && v.local == local && v.ncw == ncw && v.ks == ks && v.mtw == mtw &&
-        v.ktw == ktw)
-      return &v;
+    if (v.cell != cell || v.f32 != f32 || v.local != local || v.ncw != ncw || v.ks != ks || v.mtw != mtw ||
+        v.ktw != ktw)
+      continue;
+    if (ktl >= 0 ? v.ktl == ktl : (v.ktl > 0 && (!best || v.ktl < best->ktl))) {
+      if (ktl >= 0) return &v;
+      best = &v;
+    }
   }
-  return nullptr;
+  return best;
 }
 
 const FusedBwdVariant* find_fused_bwd(int cell, int ncw, int ks, int mtw, int ktw) {
@@ -219,7 +226,7 @@ int raise_lds_limits() {
     for (int i = 0; i < t.n; ++i) {
       const FusedVariant& v = t.v[i];
       const int D = v.ks * v.ktw * (v.f32 ? 4 : 32);
-      if (!raise(reinterpret_cast<const void*>(v.fn), fused_lds(v.local, v.f32, v.ncw, v.ks, v.mtw, D, v.cell).total))
+      if (!raise(reinterpret_cast<const void*>(v.fn), fused_lds(v.local, v.f32, v.ncw, v.ks, v.mtw, D, v.cell, v.ktl).total))
         return FRNN_EHIP;
     }
   }
@@ -273,6 +280,7 @@ const char* cell_name(int cell) { return cell == FRNN_CELL_LSTM ? "lstm" : cell 
 struct FusedPlan {
   const FusedVariant* v = nullptr;
   int local = 0, W = 1, BR = 16, groups = 0, ncw = 4, ks = 1, mtw = 0, ktw = 0, n_xcd = 1, slots = 0, grid = 0;
+  int ktl = 0;             // k-tiles per compute wave whose R^T fragments live in LDS
   int chunks = 1, Bc = 0;  // the batch runs as `chunks` launches of at most Bc rows
   double cost_us = 0.0;    // predicted time of the whole call
   size_t lds = 0;
@@ -298,16 +306,19 @@ int env_int(const char* name, int dflt) {
 constexpr double kStepBaseDie = 0.700, kStepPerMfma = 0.0164, kStepPerPollLoad = 0.0141, kStepPerWave = 0.0181;
 constexpr double kStepBaseLocalLstm = 0.440, kStepBaseLocalGru = 0.281, kStepBaseLocalElman = 0.161;
 constexpr double kStepPerMfmaLocal = 0.0513, kStepPerRowLocal = 0.0145;
+// A die-local design with part of R^T in LDS reads MTW*KTL fragments (1 KB each) from LDS per wave
+// and step, the CU's eight compute waves sharing the LDS port: its step adds this per fragment.
+constexpr double kStepPerRLds = 0.027;
 constexpr double kLaunchUs = 15.0;  // R packing, fills and the launch of one chunk
 
-double step_cost(bool local, int cell, int br, int ncw, int ks, int mtw, int ktw) {
+double step_cost(bool local, int cell, int br, int ncw, int ks, int mtw, int ktw, int ktl = 0) {
   if (local) {
     const double base = cell == FRNN_CELL_LSTM ? kStepBaseLocalLstm : cell == FRNN_CELL_GRU ? kStepBaseLocalGru
                                                                                            : kStepBaseLocalElman;
     return base + kStepPerMfmaLocal * mtw * ktw + kStepPerRowLocal * br;
   }
   const int np = (br * ktw * 32 / fused_poll_words(ks, mtw, ktw) + 63) / 64;
-  return kStepBaseDie + kStepPerMfma * mtw * ktw + kStepPerPollLoad * np + kStepPerWave * ncw;
+  return kStepBaseDie + kStepPerMfma * mtw * ktw + kStepPerPollLoad * np + kStepPerWave * ncw + kStepPerRLds * mtw * ktl;
 }
 
 // Choose the fused design by integer constraint search. The variables are:
@@ -342,7 +353,7 @@ int plan_fused(const Problem& p, const DevInfo& di, FusedPlan* out) {
     fp.chunks = (int)((p.B + bmax - 1) / bmax);
     fp.Bc = (int)(((long long)p.B + fp.chunks - 1) / fp.chunks);
     fp.groups = p.N * ((fp.Bc + fp.BR - 1) / fp.BR);
-    fp.cost_us = fp.chunks * (T * step_cost(fp.local, p.cell, fp.BR, fp.ncw, fp.ks, fp.mtw, fp.ktw) + kLaunchUs);
+    fp.cost_us = fp.chunks * (T * step_cost(fp.local, p.cell, fp.BR, fp.ncw, fp.ks, fp.mtw, fp.ktw, fp.ktl) + kLaunchUs);
     if (!fp.local) {
       const int per_die = (fp.groups + di.n_xcd - 1) / di.n_xcd;
       fp.slots = per_die * fp.W;
@@ -397,7 +408,9 @@ int plan_fused(const Problem& p, const DevInfo& di, FusedPlan* out) {
           const int ms = ncw / ks;
           if (mt_wg % ms || KT % ks) continue;
           const int mtw = mt_wg / ms, ktw = KT / ks;
+          // R^T wholly in registers where a design holds it, else in part in LDS
           const FusedVariant* v = find_fused(p.cell, 0, 0, ncw, ks, mtw, ktw);
+          if (!v) v = find_fused(p.cell, 0, 0, ncw, ks, mtw, ktw, -1);
           if (!v || BR > fused_max_br(ks, mtw)) continue;
           // the I/O wave moves at most 64 * epl words of Wx and as many output pairs per step
           const int epl = fused_epl(false, ncw, p.cell, ks, mtw);
@@ -405,7 +418,9 @@ int plan_fused(const Problem& p, const DevInfo& di, FusedPlan* out) {
           FusedPlan fp;
           fp.v = v; fp.local = 0; fp.W = W; fp.BR = BR; fp.ncw = ncw; fp.ks = ks; fp.mtw = mtw; fp.ktw = ktw;
           fp.n_xcd = di.n_xcd;
-          fp.lds = (size_t)fused_lds(false, false, ncw, ks, mtw, p.D, p.cell).total;
+          fp.ktl = v->ktl;
+          fp.lds = (size_t)fused_lds(false, false, ncw, ks, mtw, p.D, p.cell, v->ktl).total;
+          if (fp.lds > (size_t)kMaxLds) continue;
           consider(fp, (slots_per_die / W) * di.n_xcd);
         }
       }
@@ -527,11 +542,12 @@ std::string plan_string(const Problem& p, int path, const FusedPlan* fp) {
   char buf[512];
   if (path == FRNN_PATH_FUSED && fp) {
     std::snprintf(buf, sizeof(buf),
-                  "fused design=%s cell=%s dtype=%s B=%d T=%d N=%d D=%d BR=%d groups=%d W=%d NCW=%d KS=%d MTW=%d KTW=%d "
+                  "fused design=%s cell=%s dtype=%s B=%d T=%d N=%d D=%d BR=%d groups=%d W=%d NCW=%d KS=%d MTW=%d KTW=%d%s "
                   "dies=%d slots/die=%d grid=%d lds=%zu chunks=%d rows/chunk=%d predicted_us=%.1f",
                   fp->local ? "workgroup-local" : "die-local", cell_name(p.cell),
                   p.r_f32 ? "f32" : "bf16", p.B, p.T, p.N, p.D, fp->BR, fp->groups, fp->W, fp->ncw, fp->ks, fp->mtw, fp->ktw,
-                  fp->n_xcd, fp->slots, fp->grid, fp->lds, fp->chunks, fp->Bc, fp->cost_us);
+                  fp->ktl > 0 ? (" KTL=" + std::to_string(fp->ktl)).c_str() : "", fp->n_xcd, fp->slots, fp->grid, fp->lds,
+                  fp->chunks, fp->Bc, fp->cost_us);
   } else {
     const int TPH = slots_of(p.cell) * p.D / 16;
     std::snprintf(buf, sizeof(buf),

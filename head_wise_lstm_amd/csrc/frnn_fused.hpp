@@ -98,7 +98,7 @@ __host__ __device__ constexpr int fused_gt(int ncw, int ks, int mtw) {
 __host__ __device__ constexpr int fused_threads(int ncw) { return (ncw + 1) * 64; }
 
 struct FusedLds {
-  int h, part, wx, out, dma, total;
+  int h, part, wx, out, dma, r, total;
 };
 
 // A whole bf16 Elman head per workgroup streams Wx straight into LDS (global_load_lds): a ring of
@@ -149,7 +149,10 @@ __host__ __device__ constexpr int fused_poll_words(int ks, int mtw, int ktw) {
 // Words (32-bit, two bf16 units each) per row of a compute wave's poll stage, padded by 16 bytes.
 __host__ __device__ constexpr int fused_stage_row(int ktw) { return ktw * 16 + 4; }
 
-__host__ __device__ inline FusedLds fused_lds(bool local, bool f32, int ncw, int ks, int mtw, int D, int cell) {
+// ktl: k-tiles per compute wave whose R^T fragments live in LDS instead of VGPRs (a head too wide
+// for the die's registers), 1 KB per (wave, tile, k-tile) after the other regions.
+__host__ __device__ inline FusedLds fused_lds(bool local, bool f32, int ncw, int ks, int mtw, int D, int cell,
+                                              int ktl = 0) {
   FusedLds L;
   const int gt = fused_gt(ncw, ks, mtw);
   const int mt_wg = mtw * (ncw / ks);
@@ -162,7 +165,8 @@ __host__ __device__ inline FusedLds fused_lds(bool local, bool f32, int ncw, int
   L.wx = L.part + pbytes;
   L.out = L.wx + 2 * ncw * gt * 1024;
   L.dma = L.out + 2 * ncw * gt * 1024;
-  L.total = L.dma + (fused_dma(local, f32, cell) ? FUSED_DMA_STAGES * FUSED_DMA_NE * 256 : 0);
+  L.r = L.dma + (fused_dma(local, f32, cell) ? FUSED_DMA_STAGES * FUSED_DMA_NE * 256 : 0);
+  L.total = L.r + ncw * mtw * ktl * 1024;
   return L;
 }
 
@@ -534,7 +538,7 @@ __device__ __forceinline__ void io_wave_dma(const char* wxb, long long wx_sb, lo
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // no load may land after the workgroup has ended
 }
 
-template <int CELL, bool F32, bool LOCAL, int NCW, int KS, int MTW, int KTW>
+template <int CELL, bool F32, bool LOCAL, int NCW, int KS, int MTW, int KTW, int KTL = 0>
 __global__ void __launch_bounds__((NCW + 1) * 64, 1) fused_fwd_kernel(FusedArgs a) {
   constexpr int NT = (NCW + 1) * 64;
   constexpr int MS = NCW / KS;
@@ -549,6 +553,9 @@ __global__ void __launch_bounds__((NCW + 1) * 64, 1) fused_fwd_kernel(FusedArgs 
   static_assert((NCW == 4 || NCW == 6 || NCW == 8) && NCW % KS == 0, "compute waves / K split");
   static_assert(!(F32 && !LOCAL), "fp32 runs only in the workgroup-local design");
   static_assert(!(LOCAL && KS != 1), "the workgroup-local design does not split K");
+  // the last KTL of a wave's KTW k-tiles keep their R^T fragments in LDS (die-local bf16 only)
+  static_assert(KTL == 0 || (!LOCAL && !F32 && KTL < KTW), "R^T in LDS: die-local bf16 designs");
+  constexpr int KTR = KTW - KTL;  // k-tiles whose fragments stay in VGPRs
   typedef typename std::conditional<F32, float, bf16x8_t>::type frag_t;
 
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -578,7 +585,7 @@ __global__ void __launch_bounds__((NCW + 1) * 64, 1) fused_fwd_kernel(FusedArgs 
   const int b0 = bblk * a.BR;
   const int nvalid = min(a.BR, a.B - b0);
   const int tile0 = w * MT_WG;
-  const FusedLds lay = fused_lds(LOCAL, F32, NCW, KS, MTW, D, CELL);
+  const FusedLds lay = fused_lds(LOCAL, F32, NCW, KS, MTW, D, CELL, KTL);
   constexpr int HPAD = fused_hpad(F32);
   const int HS = D + HPAD;  // row stride of the LDS h buffer (elements)
   float* hbuf_f = reinterpret_cast<float*>(smem + lay.h);
@@ -665,7 +672,9 @@ __global__ void __launch_bounds__((NCW + 1) * 64, 1) fused_fwd_kernel(FusedArgs 
   // ---- R^T fragments, resident for the whole sequence. bf16: 16 contiguous bytes per lane from
   // the packed copy, all loads in flight at once (tiles past the head read its last tile and are
   // zeroed).
-  frag_t Ra[MTW][KTW];
+  frag_t Ra[MTW][KTR];
+  // the LDS-resident fragments of this wave: [tile j][k-tile kk - KTR][64 lanes], 16 bytes a lane
+  u32x4_t* const rl = reinterpret_cast<u32x4_t*>(smem + lay.r) + (long long)wave * MTW * (KTL > 0 ? KTL : 1) * 64;
   if constexpr (F32) {
 #pragma unroll
     for (int j = 0; j < MTW; ++j) {
@@ -685,21 +694,34 @@ __global__ void __launch_bounds__((NCW + 1) * 64, 1) fused_fwd_kernel(FusedArgs 
   } else {
     const int KT = D / 32;
     const u32x4_t* rp = reinterpret_cast<const u32x4_t*>(a.rpack) + (long long)n * TPH * KT * 64 + lane;
-    u32x4_t raw[MTW][KTW];
+    u32x4_t raw[MTW][KTR];
 #pragma unroll
     for (int j = 0; j < MTW; ++j) {
       const int tt = min(tile0 + ms * MTW + j, TPH - 1);
 #pragma unroll
-      for (int kk = 0; kk < KTW; ++kk) raw[j][kk] = rp[((long long)tt * KT + ks * KTW + kk) * 64];
+      for (int kk = 0; kk < KTR; ++kk) raw[j][kk] = rp[((long long)tt * KT + ks * KTW + kk) * 64];
     }
 #pragma unroll
     for (int j = 0; j < MTW; ++j) {
       const bool tv = tile0 + ms * MTW + j < TPH;
 #pragma unroll
-      for (int kk = 0; kk < KTW; ++kk) {
+      for (int kk = 0; kk < KTR; ++kk) {
         u32x4_t v = raw[j][kk];
         if (!tv) v = u32x4_t{0u, 0u, 0u, 0u};
         Ra[j][kk] = __builtin_bit_cast(bf16x8_t, v);
+      }
+    }
+    if constexpr (KTL > 0) {  // the rest go to LDS, read back every step (the first barrier orders them)
+#pragma unroll
+      for (int j = 0; j < MTW; ++j) {
+        const int tr = tile0 + ms * MTW + j;
+        const int tt = min(tr, TPH - 1);
+#pragma unroll
+        for (int kk = KTR; kk < KTW; ++kk) {
+          u32x4_t v = rp[((long long)tt * KT + ks * KTW + kk) * 64];
+          if (tr >= TPH) v = u32x4_t{0u, 0u, 0u, 0u};
+          rl[(j * KTL + (kk - KTR)) * 64 + lane] = v;
+        }
       }
     }
   }
@@ -797,7 +819,16 @@ __global__ void __launch_bounds__((NCW + 1) * 64, 1) fused_fwd_kernel(FusedArgs 
       for (int kk = 0; kk < KTW; ++kk) {
         const bf16x8_t bk = *reinterpret_cast<const bf16x8_t*>(stage + col * fused_stage_row(KTW) + kk * 16 + 4 * quad);
 #pragma unroll
-        for (int j = 0; j < MTW; ++j) acc[j] = mfma_bf16(Ra[j][kk], bk, acc[j]);
+        for (int j = 0; j < MTW; ++j) {
+          if constexpr (KTL > 0) {
+            if (kk >= KTR) {
+              const bf16x8_t ak = __builtin_bit_cast(bf16x8_t, rl[(j * KTL + (kk - KTR)) * 64 + lane]);
+              acc[j] = mfma_bf16(ak, bk, acc[j]);
+              continue;
+            }
+          }
+          acc[j] = mfma_bf16(Ra[j][kk < KTR ? kk : 0], bk, acc[j]);
+        }
       }
     }
 

@@ -6,7 +6,7 @@ namespace frnn {
 namespace {
 
 #define FRNN_FV(F32, LOCAL, NCW, KS, MTW, KTW) \
-  {CELL_ELMAN, F32, LOCAL, NCW, KS, MTW, KTW, &fused_fwd_kernel<CELL_ELMAN, F32, LOCAL, NCW, KS, MTW, KTW>},
+  {CELL_ELMAN, F32, LOCAL, NCW, KS, MTW, KTW, 0, &fused_fwd_kernel<CELL_ELMAN, F32, LOCAL, NCW, KS, MTW, KTW>},
 const FusedVariant kTable[] = {FRNN_FUSED_DESIGNS(FRNN_FV)};
 #undef FRNN_FV
 

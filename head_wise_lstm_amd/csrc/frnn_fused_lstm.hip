@@ -6,9 +6,12 @@ namespace frnn {
 namespace {
 
 #define FRNN_FV(F32, LOCAL, NCW, KS, MTW, KTW) \
-  {CELL_LSTM, F32, LOCAL, NCW, KS, MTW, KTW, &fused_fwd_kernel<CELL_LSTM, F32, LOCAL, NCW, KS, MTW, KTW>},
-const FusedVariant kTable[] = {FRNN_FUSED_DESIGNS(FRNN_FV)};
+  {CELL_LSTM, F32, LOCAL, NCW, KS, MTW, KTW, 0, &fused_fwd_kernel<CELL_LSTM, F32, LOCAL, NCW, KS, MTW, KTW>},
+#define FRNN_FVL(NCW, KS, MTW, KTW, KTL) \
+  {CELL_LSTM, false, false, NCW, KS, MTW, KTW, KTL, &fused_fwd_kernel<CELL_LSTM, false, false, NCW, KS, MTW, KTW, KTL>},
+const FusedVariant kTable[] = {FRNN_FUSED_DESIGNS(FRNN_FV) FRNN_FUSED_RLDS_DESIGNS(FRNN_FVL)};
 #undef FRNN_FV
+#undef FRNN_FVL
 
 #define FRNN_FBV(NCW, KS, MTW, KTW) \
   {CELL_LSTM, NCW, KS, MTW, KTW, &fused_bwd_kernel<CELL_LSTM, NCW, KS, MTW, KTW>},

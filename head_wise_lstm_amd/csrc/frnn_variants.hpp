@@ -12,6 +12,7 @@ typedef void (*fused_fn)(FusedArgs);
 
 struct FusedVariant {
   int cell, f32, local, ncw, ks, mtw, ktw;
+  int ktl;  // k-tiles per compute wave whose R^T fragments live in LDS (0: all in VGPRs)
   fused_fn fn;
 };
 
@@ -41,6 +42,12 @@ struct FusedTable {
   /* single-workgroup design (fp32) */                                                             \
   X(true, true, 4, 1, 2, 8) X(true, true, 4, 1, 1, 8) X(true, true, 4, 1, 4, 16)                   \
   X(true, true, 4, 1, 1, 16)
+
+// Die-local bf16 designs that keep part of R^T in LDS: X(NCW, KS, MTW, KTW, KTL), the last KTL of a
+// wave's KTW k-tiles in LDS. A head of 1024 units with four gate rows (8 MB of bf16 R^T over the 32
+// workgroups of a die, 256 KB each) fits the registers of no design here: eight compute waves x
+// eight tiles x three k-tiles in VGPRs (96 registers a lane), the fourth k-tile in LDS (64 KB).
+#define FRNN_FUSED_RLDS_DESIGNS(X) X(8, 8, 8, 4, 1)
 
 FusedTable fused_table_lstm();
 FusedTable fused_table_elman();

@@ -81,9 +81,10 @@ enum { FRNN_F32 = 0, FRNN_BF16 = 1 };
  *               R read from memory, and applies the gates in its epilogue (T launches); any
  *               head size runs.
  *  FUSED:       one persistent launch for all T steps (per chunk of batch rows where the batch
- *               exceeds one launch); R stays in registers. The workgroups sharing a head, all
- *               resident on one die, exchange h through that die's L2 every step; a head small
- *               enough for one workgroup keeps h in LDS. */
+ *               exceeds one launch); R stays in registers (a quarter of it in LDS for LSTM
+ *               and GRU heads of 1024 units, too wide for a die's registers). The workgroups
+ *               sharing a head, all resident on one die, exchange h through that die's L2 every
+ *               step; a head small enough for one workgroup keeps h in LDS. */
 enum { FRNN_PATH_ALTERNATING = 0, FRNN_PATH_FUSED = 1 };
 
 /* Problem description for frnn_fwd and frnn_bwd. G and S follow from `cell` (LSTM: 4, 2;

@@ -294,10 +294,9 @@ def test_long_sequence_past_tag_wrap(cell, env):
     run_case(w, "fused", env=env)
 
 
-# Extreme shapes: the widest head the boundary takes (D = 1024), many narrow heads, and batches
-# far past one launch's co-resident rows. A head of 1024 units has a fused design for the Elman
-# cell only: four gate rows of 1024 x 1024 bf16 (8 MB) are half of a die's register file, more
-# than its 32 workgroups can hold beside their working registers.
+# Extreme shapes: the widest head the boundary takes (D = 1024; the LSTM and GRU heads' fused
+# design keeps a quarter of R^T in LDS, since four gate rows of 1024 x 1024 bf16 are half of a
+# die's register file), many narrow heads, and batches far past one launch's co-resident rows.
 EXTREME = [
     fi.HeadwiseWorkload("lstm_D1024", "lstm", torch.bfloat16, B=2, T=6, N=1, D=1024, seed=291, s0_var=1.0),
     fi.HeadwiseWorkload("gru_D1024", "gru", torch.bfloat16, B=3, T=6, N=1, D=1024, seed=292, s0_var=1.0),
@@ -307,17 +306,39 @@ EXTREME = [
     fi.HeadwiseWorkload("lstm_B300_D64", "lstm", torch.bfloat16, B=300, T=5, N=1, D=64, seed=296, s0_var=1.0),
     fi.HeadwiseWorkload("gru_B130_N2_D256", "gru", torch.bfloat16, B=130, T=5, N=2, D=256, seed=297, s0_var=1.0),
 ]
-NO_FUSED_DESIGN = {"lstm_D1024", "gru_D1024"}
 
 
-@pytest.mark.parametrize("w,path", [(w, p) for w in EXTREME for p in ("alternating", "fused")
-                                    if not (p == "fused" and w.name in NO_FUSED_DESIGN)],
-                         ids=lambda x: x if isinstance(x, str) else x.name)
+@pytest.mark.parametrize("path", ["alternating", "fused"])
+@pytest.mark.parametrize("w", EXTREME, ids=lambda w: w.name)
 def test_extreme_shapes(w, path):
+    if path == "fused" and w.D == 1024 and w.cell != "elman":
+        hw = _hw()
+        assert "KTL=1" in hw.frnn_plan_str(hw._desc(w.B, w.T, w.N, w.D, w.cell, w.dtype), "fused")
     run_case(w, path)
 
 
-@pytest.mark.parametrize("w", [w for w in EXTREME if w.name in NO_FUSED_DESIGN], ids=lambda w: w.name)
+def test_d1024_lds_design_full_launch():
+    """Heads of 1024 units on the design that keeps a quarter of R^T in LDS, at 16 batch rows (8
+    groups of 2 rows, one per die, the whole chip) over 64 steps, LSTM and GRU, against the oracle
+    row by row."""
+    for cell, seed in (("lstm", 331), ("gru", 332)):
+        w = fi.HeadwiseWorkload(f"{cell}_D1024_B16", cell, torch.bfloat16, B=16, T=64, N=1, D=1024, seed=seed,
+                                s0_var=1.0)
+        hw = _hw()
+        plan = hw.frnn_plan_str(hw._desc(w.B, w.T, w.N, w.D, w.cell, w.dtype), "fused")
+        assert "KTL=1" in plan and "groups=8 " in plan, plan
+        run_case(w, "fused")
+
+
+# fp32 heads wider than 64 units have no fused design (the single-workgroup fp32 design holds a
+# head of at most 64 units; the die-local designs are bf16).
+NO_FUSED_DESIGN = [
+    fi.HeadwiseWorkload("lstm_f32_D128", "lstm", torch.float32, B=2, T=5, N=1, D=128, seed=298, s0_var=1.0),
+    fi.HeadwiseWorkload("gru_f32_D256", "gru", torch.float32, B=3, T=4, N=2, D=256, seed=299, s0_var=1.0),
+]
+
+
+@pytest.mark.parametrize("w", NO_FUSED_DESIGN, ids=lambda w: w.name)
 def test_fused_rejects_heads_without_a_design(w):
     """The fused path reports FRNN_EUNSUPPORTED for a head it has no design for, from the planner
     and from the compute call, and leaves the outputs as they were."""
@@ -334,6 +355,7 @@ def test_fused_rejects_heads_without_a_design(w):
     assert ei.value.status == -2
     torch.cuda.synchronize()
     assert bool((out[0] == 7.0).all()) and bool((out[1] == 7.0).all())
+    run_case(w, "alternating")  # the alternating path takes the shape
 
 
 def test_repeat_calls_reuse_workspace():
