@@ -102,6 +102,17 @@ GRU_WORKLOADS = {
         b_var=0.1),
 }
 
+# The headline shape with heads of 1024 units (the widest head the fused designs cover), LSTM and
+# GRU.
+WIDE_WORKLOADS = {
+    "lstm_bf16_B16_T1024_N1_D1024": HeadwiseWorkload(
+        "lstm_bf16_B16_T1024_N1_D1024", "lstm", torch.bfloat16, B=16, T=1024, N=1, D=1024, seed=13,
+        b_var=0.1),
+    "gru_bf16_B16_T1024_N1_D1024": HeadwiseWorkload(
+        "gru_bf16_B16_T1024_N1_D1024", "gru", torch.bfloat16, B=16, T=1024, N=1, D=1024, seed=14,
+        b_var=0.1),
+}
+
 
 def _normal(g: torch.Generator, shape, var: float) -> torch.Tensor:
     return torch.randn(shape, generator=g, dtype=torch.float32) * math.sqrt(var)
@@ -168,8 +179,8 @@ def stack_inputs(w: StackWorkload):
 
 
 def get_workload(name: str):
-    """A named workload from WORKLOADS, GRU_WORKLOADS or BIDIR_WORKLOADS."""
-    for table in (WORKLOADS, GRU_WORKLOADS, BIDIR_WORKLOADS):
+    """A named workload from WORKLOADS, GRU_WORKLOADS, WIDE_WORKLOADS or BIDIR_WORKLOADS."""
+    for table in (WORKLOADS, GRU_WORKLOADS, WIDE_WORKLOADS, BIDIR_WORKLOADS):
         if name in table:
             return table[name]
     raise KeyError(name)

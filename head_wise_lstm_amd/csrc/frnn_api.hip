@@ -201,15 +201,21 @@ const FusedBwdVariant* find_fused_bwd(int cell, int ncw, int ks, int mtw, int kt
   return nullptr;
 }
 
-const FusedBwdxVariant* find_fused_bwdx(int cell, int ncw, int mtw, int ktw) {
+// ktl < 0: the design with the fewest k-tiles of R in LDS.
+const FusedBwdxVariant* find_fused_bwdx(int cell, int ncw, int mtw, int ktw, int ktl = -1) {
   const FusedBwdxTable t = cell == FRNN_CELL_LSTM ? fused_bwdx_table_lstm()
                            : cell == FRNN_CELL_GRU ? fused_bwdx_table_gru()
                                                    : fused_bwdx_table_elman();
+  const FusedBwdxVariant* best = nullptr;
   for (int i = 0; i < t.n; ++i) {
     const FusedBwdxVariant& v = t.v[i];
-    if (v.cell == cell && v.ncw == ncw && v.mtw == mtw && v.ktw == ktw) return &v;
+    if (v.cell != cell || v.ncw != ncw || v.mtw != mtw || v.ktw != ktw) continue;
+    if (ktl >= 0 ? v.ktl == ktl : (!best || v.ktl < best->ktl)) {
+      if (ktl >= 0) return &v;
+      best = &v;
+    }
   }
-  return nullptr;
+  return best;
 }
 
 // Raises the dynamic-LDS limit of every persistent kernel to what its design uses (frnn_init), so
@@ -242,7 +248,7 @@ int raise_lds_limits() {
     for (int i = 0; i < t.n; ++i) {
       const FusedBwdxVariant& v = t.v[i];
       const int UW = v.ktw * 32 / cell_gates(v.cell);
-      if (!raise(reinterpret_cast<const void*>(v.fn), fused_bwdx_lds(v.ktw, FUSED_DIE_MAX_BR, UW).total))
+      if (!raise(reinterpret_cast<const void*>(v.fn), fused_bwdx_lds(v.ktw, FUSED_DIE_MAX_BR, UW, v.ncw, v.mtw, v.ktl).total))
         return FRNN_EHIP;
     }
   }
@@ -675,6 +681,7 @@ struct FusedBwdPlan {
   int local = 0;               // 1: the single-workgroup fp32 design (fused_bwd_local_kernel)
   fused_bwd_fn fn = nullptr;   // the kernel of the design
   int W = 0, BR = 0, groups = 0, ncw = 0, ks = 0, mtw = 0, ktw = 0, n_xcd = 1, slots = 0, grid = 0, U = 0;
+  int ktl = 0;             // k-tiles of R per compute wave kept in LDS (partial-sum design)
   int chunks = 1, Bc = 0;  // the batch runs as `chunks` launches of at most Bc rows
   size_t lds = 0;
 };
@@ -716,11 +723,13 @@ bool plan_fused_bwdx(int B, int N, int D, int cell, const DevInfo& di, FusedBwdP
         const FusedBwdxVariant* v = find_fused_bwdx(cell, ncw, mtw, ktw);
         if (!v) continue;
         if (found && chunks >= best.chunks) continue;
+        const size_t lds = (size_t)fused_bwdx_lds(ktw, BR, UW, ncw, mtw, v->ktl).total;
+        if (lds > (size_t)kMaxLds) continue;
         FusedBwdPlan fp;
         fp.px = 1; fp.fn = v->fn; fp.W = W; fp.BR = BR; fp.groups = groups; fp.ncw = ncw; fp.ks = 1; fp.mtw = mtw;
-        fp.ktw = ktw; fp.n_xcd = di.n_xcd; fp.slots = per_die * W; fp.grid = fp.slots * di.n_xcd; fp.U = UW;
-        fp.chunks = chunks; fp.Bc = Bc;
-        fp.lds = (size_t)fused_bwdx_lds(ktw, BR, UW).total;
+        fp.ktw = ktw; fp.ktl = v->ktl; fp.n_xcd = di.n_xcd; fp.slots = per_die * W; fp.grid = fp.slots * di.n_xcd;
+        fp.U = UW; fp.chunks = chunks; fp.Bc = Bc;
+        fp.lds = lds;
         best = fp;
         found = true;
         break;
@@ -878,10 +887,11 @@ std::string bwd_plan_string(const frnn_desc* d, int path, const FusedBwdPlan* fp
   if (path == FRNN_PATH_FUSED && fp) {
     std::snprintf(buf, sizeof(buf),
                   "backward path=fused design=%s cell=%s dtype=%s B=%d T=%d N=%d D=%d BR=%d groups=%d W=%d "
-                  "NCW=%d KS=%d MTW=%d KTW=%d dies=%d slots/die=%d grid=%d lds=%zu chunks=%d rows/chunk=%d",
+                  "NCW=%d KS=%d MTW=%d KTW=%d%s dies=%d slots/die=%d grid=%d lds=%zu chunks=%d rows/chunk=%d",
                   fp->local ? "workgroup-local" : fp->px ? "die-local-partials" : "die-local", cell_name(d->cell),
                   d->in_dtype == FRNN_F32 ? "f32" : "bf16", d->B, d->T, d->N, d->D, fp->BR, fp->groups, fp->W, fp->ncw, fp->ks, fp->mtw,
-                  fp->ktw, fp->n_xcd, fp->slots, fp->grid, fp->lds, fp->chunks, fp->Bc);
+                  fp->ktw, fp->ktl > 0 ? (" KTL=" + std::to_string(fp->ktl)).c_str() : "", fp->n_xcd, fp->slots, fp->grid,
+                  fp->lds, fp->chunks, fp->Bc);
     return std::string(buf);
   }
   const int G = gates_of(d->cell);

@@ -421,15 +421,18 @@ constexpr int BWDX_MAX_W = BWDX_J * BWDX_NP;
 #endif
 
 struct FusedBwdxLds {
-  int stage, rin, rout, total;
+  int stage, rin, rout, r, total;
 };
 
-__host__ __device__ inline FusedBwdxLds fused_bwdx_lds(int ktw, int BR, int U) {
+// ktl: k-tiles of R per compute wave kept in LDS (ncw waves of mtw row tiles, 1 KB per tile and
+// k-tile) rather than in VGPRs.
+__host__ __device__ inline FusedBwdxLds fused_bwdx_lds(int ktw, int BR, int U, int ncw = 0, int mtw = 0, int ktl = 0) {
   FusedBwdxLds L;
   L.stage = 0;
   L.rin = 2 * 16 * fused_stage_row(ktw) * 4;
   L.rout = L.rin + 2 * BR * U * BWD_REC * 4;
-  L.total = L.rout + 2 * BR * U * 2 * 4;
+  L.r = L.rout + 2 * BR * U * 2 * 4;
+  L.total = L.r + ncw * mtw * ktl * 1024;
   return L;
 }
 
@@ -479,11 +482,14 @@ __device__ __forceinline__ float row_shl_add(float x) {
   return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x100 + D, 0xF, 0xF, true));
 }
 
-// xbuf: [groups][2][W][BR][D] words. NCW * MTW = D / 16; KTW * 32 = G * D / W.
-template <int CELL, int NCW, int MTW, int KTW>
+// xbuf: [groups][2][W][BR][D] words. NCW * MTW = D / 16; KTW * 32 = G * D / W; the last KTL of
+// a wave's KTW k-tiles keep their R fragments in LDS.
+template <int CELL, int NCW, int MTW, int KTW, int KTL = 0>
 __global__ void __launch_bounds__((NCW + 1) * 64, 1) fused_bwdx_kernel(FusedBwdArgs a) {
   constexpr int G = cell_gates(CELL);
   static_assert(NCW == 4 || NCW == 6 || NCW == 8, "compute waves");
+  static_assert(KTL >= 0 && KTL < KTW, "R k-tiles in LDS");
+  constexpr int KTR = KTW - KTL;  // k-tiles whose fragments stay in VGPRs
 
   extern __shared__ __attribute__((aligned(16))) char smem[];
   __shared__ int s_abort;
@@ -509,7 +515,7 @@ __global__ void __launch_bounds__((NCW + 1) * 64, 1) fused_bwdx_kernel(FusedBwdA
   const int b0 = bblk * BR;
   const int nvalid = min(BR, a.B - b0);
   const int u0 = w * UW;
-  const FusedBwdxLds lay = fused_bwdx_lds(KTW, BR, UW);
+  const FusedBwdxLds lay = fused_bwdx_lds(KTW, BR, UW, NCW, MTW, KTL);
   constexpr int SROW = fused_stage_row(KTW);
   uint32_t* stage = reinterpret_cast<uint32_t*>(smem + lay.stage);
   float* rin = reinterpret_cast<float*>(smem + lay.rin);
@@ -539,8 +545,11 @@ __global__ void __launch_bounds__((NCW + 1) * 64, 1) fused_bwdx_kernel(FusedBwdA
   // ==================================================================== compute waves
   // ---- R fragments: rows d of this wave's tiles, k = g*UW + e - u0 over the slice. Eight
   // consecutive k stay inside one gate (UW is a multiple of 8), so each fragment is one 16-byte
-  // lane of the packed R (global k = g*D + e).
-  bf16x8_t Ra[MTW][KTW];
+  // lane of the packed R (global k = g*D + e). The fragments of k-tiles KTR.. go to LDS, one
+  // region per wave ([tile j][k-tile kk - KTR][64 lanes], 16 bytes a lane), and are read back every
+  // step by the wave that wrote them.
+  bf16x8_t Ra[MTW][KTR];
+  u32x4_t* const rl = reinterpret_cast<u32x4_t*>(smem + lay.r) + wave * MTW * (KTL > 0 ? KTL : 1) * 64;
   {
     const u32x4_t* rp = reinterpret_cast<const u32x4_t*>(a.rpk) + (long long)n * TPH * KT * 64;
     u32x4_t raw[MTW][KTW];
@@ -556,9 +565,12 @@ __global__ void __launch_bounds__((NCW + 1) * 64, 1) fused_bwdx_kernel(FusedBwdA
       }
     }
 #pragma unroll
-    for (int j = 0; j < MTW; ++j)
+    for (int j = 0; j < MTW; ++j) {
 #pragma unroll
-      for (int kk = 0; kk < KTW; ++kk) Ra[j][kk] = __builtin_bit_cast(bf16x8_t, raw[j][kk]);
+      for (int kk = 0; kk < KTR; ++kk) Ra[j][kk] = __builtin_bit_cast(bf16x8_t, raw[j][kk]);
+#pragma unroll
+      for (int kk = KTR; kk < KTW; ++kk) rl[(j * KTL + (kk - KTR)) * 64 + lane] = raw[j][kk];
+    }
   }
 
   // ---- poll lanes: combination c (batch row r, unit quad q) in lanes 16c' .. 16c'+15, slot chunk
@@ -602,9 +614,13 @@ __global__ void __launch_bounds__((NCW + 1) * 64, 1) fused_bwdx_kernel(FusedBwdA
     if (poller) {
       // this step's records of the lane's four units (in the ring since barrier s-1)
       const bool mathlane = cv && chunk == 0;
+      const float* rr = rin + ((s & 1) * BR + (mathlane ? pr : 0)) * UW * BWD_REC + (mathlane ? 4 * pq : 0) * BWD_REC;
       f32x4_t rc[4][2];
-      {
-        const float* rr = rin + ((s & 1) * BR + (mathlane ? pr : 0)) * UW * BWD_REC + (mathlane ? 4 * pq : 0) * BWD_REC;
+      // The records go out before the poll (their latency hidden behind it) unless R k-tiles live
+      // in LDS: those designs hold up to 96 VGPRs of R, and 32 registers of records held through
+      // the poll would push values out to scratch. They read each unit's records where they are
+      // used, after the poll.
+      if constexpr (KTL == 0) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           rc[i][0] = *reinterpret_cast<const f32x4_t*>(rr + i * BWD_REC);
@@ -658,8 +674,14 @@ __global__ void __launch_bounds__((NCW + 1) * 64, 1) fused_bwdx_kernel(FusedBwdA
           float da[G][4], dh[4], dc[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const f32x4_t r0 = rc[i][0];
-            const f32x4_t r1 = rc[i][1];
+            f32x4_t r0, r1;
+            if constexpr (KTL > 0) {
+              r0 = *reinterpret_cast<const f32x4_t*>(rr + i * BWD_REC);
+              r1 = *reinterpret_cast<const f32x4_t*>(rr + i * BWD_REC + 4);
+            } else {
+              r0 = rc[i][0];
+              r1 = rc[i][1];
+            }
             if constexpr (CELL == CELL_LSTM) {
               dh[i] = sum[i] + r1[2];
               dc[i] = cr[i] + r1[3] + dh[i] * r0[0];
@@ -701,15 +723,25 @@ __global__ void __launch_bounds__((NCW + 1) * 64, 1) fused_bwdx_kernel(FusedBwdA
     for (int j = 0; j < MTW; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     // the stage reads go out before the abort flag is looked at (they are harmless if it is set)
     const uint32_t* sg = stage + (s & 1) * 16 * SROW;
-    bf16x8_t bks[KTW];
+    // (designs with R k-tiles in LDS read each k-tile's operand where it is used)
+    constexpr int KB = KTL > 0 ? 1 : KTW;
+    bf16x8_t bks[KB];
 #pragma unroll
-    for (int kk = 0; kk < KTW; ++kk) bks[kk] = *reinterpret_cast<const bf16x8_t*>(sg + col * SROW + kk * 16 + 4 * quad);
+    for (int kk = 0; kk < KB; ++kk) bks[kk] = *reinterpret_cast<const bf16x8_t*>(sg + col * SROW + kk * 16 + 4 * quad);
     if (uniform_flag(s_abort)) return;
 #pragma unroll
     for (int kk = 0; kk < KTW; ++kk) {
-      const bf16x8_t bk = bks[kk];
+      const bf16x8_t bk = kk < KB ? bks[kk < KB ? kk : 0] : *reinterpret_cast<const bf16x8_t*>(sg + col * SROW + kk * 16 + 4 * quad);
 #pragma unroll
-      for (int j = 0; j < MTW; ++j) acc[j] = mfma_bf16(Ra[j][kk], bk, acc[j]);
+      for (int j = 0; j < MTW; ++j) {
+        if constexpr (KTL > 0) {
+          if (kk >= KTR) {
+            acc[j] = mfma_bf16(__builtin_bit_cast(bf16x8_t, rl[(j * KTL + (kk - KTR)) * 64 + lane]), bk, acc[j]);
+            continue;
+          }
+        }
+        acc[j] = mfma_bf16(Ra[j][kk < KTR ? kk : 0], bk, acc[j]);
+      }
     }
     if (col < nvalid) {
       // (stall_step: a stale tag, as in the da design)

@@ -16,7 +16,7 @@ const FusedBwdVariant kBwdTable[] = {FRNN_FUSED_BWD_ELMAN(FRNN_FBV)};
 #undef FRNN_FBV
 
 #define FRNN_FBXV(NCW, MTW, KTW) \
-  {CELL_ELMAN, NCW, MTW, KTW, &fused_bwdx_kernel<CELL_ELMAN, NCW, MTW, KTW>},
+  {CELL_ELMAN, NCW, MTW, KTW, 0, &fused_bwdx_kernel<CELL_ELMAN, NCW, MTW, KTW>},
 const FusedBwdxVariant kBwdxTable[] = {FRNN_FUSED_BWDX_ELMAN(FRNN_FBXV)};
 #undef FRNN_FBXV
 

@@ -19,9 +19,12 @@ const FusedBwdVariant kBwdTable[] = {FRNN_FUSED_BWD_GRU(FRNN_FBV)};
 #undef FRNN_FBV
 
 #define FRNN_FBXV(NCW, MTW, KTW) \
-  {CELL_GRU, NCW, MTW, KTW, &fused_bwdx_kernel<CELL_GRU, NCW, MTW, KTW>},
-const FusedBwdxVariant kBwdxTable[] = {FRNN_FUSED_BWDX_GRU(FRNN_FBXV)};
+  {CELL_GRU, NCW, MTW, KTW, 0, &fused_bwdx_kernel<CELL_GRU, NCW, MTW, KTW>},
+#define FRNN_FBXVL(NCW, MTW, KTW, KTL) \
+  {CELL_GRU, NCW, MTW, KTW, KTL, &fused_bwdx_kernel<CELL_GRU, NCW, MTW, KTW, KTL>},
+const FusedBwdxVariant kBwdxTable[] = {FRNN_FUSED_BWDX_GRU(FRNN_FBXV) FRNN_FUSED_BWDX_RLDS_GRU(FRNN_FBXVL)};
 #undef FRNN_FBXV
+#undef FRNN_FBXVL
 
 }  // namespace
 

@@ -19,9 +19,12 @@ const FusedBwdVariant kBwdTable[] = {FRNN_FUSED_BWD_LSTM(FRNN_FBV)};
 #undef FRNN_FBV
 
 #define FRNN_FBXV(NCW, MTW, KTW) \
-  {CELL_LSTM, NCW, MTW, KTW, &fused_bwdx_kernel<CELL_LSTM, NCW, MTW, KTW>},
-const FusedBwdxVariant kBwdxTable[] = {FRNN_FUSED_BWDX_LSTM(FRNN_FBXV)};
+  {CELL_LSTM, NCW, MTW, KTW, 0, &fused_bwdx_kernel<CELL_LSTM, NCW, MTW, KTW>},
+#define FRNN_FBXVL(NCW, MTW, KTW, KTL) \
+  {CELL_LSTM, NCW, MTW, KTW, KTL, &fused_bwdx_kernel<CELL_LSTM, NCW, MTW, KTW, KTL>},
+const FusedBwdxVariant kBwdxTable[] = {FRNN_FUSED_BWDX_LSTM(FRNN_FBXV) FRNN_FUSED_BWDX_RLDS_LSTM(FRNN_FBXVL)};
 #undef FRNN_FBXV
+#undef FRNN_FBXVL
 
 }  // namespace
 

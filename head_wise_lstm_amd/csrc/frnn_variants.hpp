@@ -93,9 +93,15 @@ FusedBwdTable fused_bwd_table_gru();
   X(8, 6, 3) X(8, 4, 3) X(8, 2, 3) X(4, 4, 3) X(8, 1, 3) X(4, 2, 3) X(4, 1, 3) X(6, 1, 3)
 #define FRNN_FUSED_BWDX_ELMAN(X)                                                                      \
   X(8, 6, 1) X(8, 4, 1) X(8, 2, 1) X(4, 4, 1) X(8, 1, 1) X(4, 2, 1) X(8, 1, 2) X(4, 2, 2) X(4, 1, 1)
+// Partial-sum designs X(NCW, MTW, KTW, KTL) that keep the last KTL of a wave's k-tiles of R in LDS:
+// heads of 1024 units, whose slice of R (32 units with all their gates, all 1024 rows) fits the
+// VGPRs of no design without spilling (nine waves leave 168 VGPRs a lane). LSTM: two of four
+// k-tiles in LDS (with one, the step's MFMA phase spills); GRU: one of three.
+#define FRNN_FUSED_BWDX_RLDS_LSTM(X) X(8, 8, 4, 2)
+#define FRNN_FUSED_BWDX_RLDS_GRU(X) X(8, 8, 3, 1)
 
 struct FusedBwdxVariant {
-  int cell, ncw, mtw, ktw;
+  int cell, ncw, mtw, ktw, ktl;
   fused_bwd_fn fn;
 };
 

@@ -176,9 +176,10 @@ int frnn_fwd(const frnn_desc* d, int path, const void* Wx, const void* R, const 
  *     gradient reaching h through R every step (bf16 inputs; the forward's die-local design
  *     with h and R^T exchanged), or one workgroup holds a whole head of 32 or 64 units and
  *     keeps that gradient in LDS, multiplying on the fp32 MFMA (fp32 inputs, bf16 Elman heads,
- *     and bf16 heads no die-local design tiles). Shapes this build has no fused design for (a
- *     head of 1024 units with three or four gates, say) return FRNN_EUNSUPPORTED before any
- *     launch; frnn_bwd_plan_str says which design a shape gets.
+ *     and bf16 heads no die-local design tiles). LSTM and GRU heads of 1024 units keep part of
+ *     R in LDS. Shapes this build has no fused design for (fp32 heads wider than 64 units, say)
+ *     return FRNN_EUNSUPPORTED before any launch; frnn_bwd_plan_str says which design a shape
+ *     gets.
  * The workspace grows with T (it holds every step's h.R and gradient).
  */
 int frnn_bwd(const frnn_desc* d, int path, const void* Wx, const void* R, const void* b,

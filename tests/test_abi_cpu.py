@@ -309,6 +309,13 @@ def test_fused_bwd_planner(lib):
     assert "design=die-local-partials" in s and "cell=gru" in s and "W=24 " in s and "KTW=3" in s
     s = hw.frnn_bwd_plan_str(D(B=8, T=1024, N=3, Dm=256), 1)
     assert "design=die-local-partials" in s
+    # heads of 1024 units: 32 units a workgroup with part of their R in LDS (LSTM two of four
+    # k-tiles, GRU one of three)
+    s = hw.frnn_bwd_plan_str(D(B=16, T=1024, N=1, Dm=1024), 1)
+    assert "design=die-local-partials" in s and "W=32 " in s and "NCW=8 KS=1 MTW=8 KTW=4 KTL=2 " in s, s
+    s = hw.frnn_bwd_plan_str(D(B=16, T=1024, N=1, Dm=1024, cell=2), 1)
+    assert "design=die-local-partials" in s and "W=32 " in s and "NCW=8 KS=1 MTW=8 KTW=3 KTL=1 " in s, s
+    assert "KTL" not in hw.frnn_bwd_plan_str(D(B=16, T=1024, N=1, Dm=768), 1)
     # twelve 64-unit Elman heads of 64 rows: the single-workgroup design
     s = hw.frnn_bwd_plan_str(D(B=64, T=8, N=12, Dm=64, cell=1), 1)
     assert "design=workgroup-local " in s and "BR=2 " in s
@@ -332,7 +339,8 @@ def test_fused_bwd_planner(lib):
         assert "cell=gru" in s and "W=24 " in s and "KTW=9" in s
     finally:
         del os.environ["FRNN_FUSED_BWD_PX"]
-    for (B, N, Dm, cell) in [(16, 1, 768, 0), (8, 3, 256, 0), (5, 2, 64, 0), (9, 2, 256, 2), (7, 2, 128, 1)]:
+    for (B, N, Dm, cell) in [(16, 1, 768, 0), (8, 3, 256, 0), (5, 2, 64, 0), (9, 2, 256, 2), (7, 2, 128, 1),
+                             (16, 1, 1024, 0), (40, 1, 1024, 2)]:
         s = hw.frnn_bwd_plan_str(D(B=B, T=8, N=N, Dm=Dm, cell=cell), 1)
         grid = int(re.search(r"grid=(\d+)", s).group(1))
         slots = int(re.search(r"slots/die=(\d+)", s).group(1))

@@ -218,19 +218,44 @@ BWD_EXTREME = [
     fi.HeadwiseWorkload("bwd_gru_B130_N2_D256", "gru", torch.bfloat16, B=130, T=5, N=2, D=256, seed=306,
                         s0_var=1.0),
 ]
-# A head of 1024 units with four gate rows: R (8 MB bf16) is half of a die's register file, more
-# than the workgroups of a die-local backward design can hold beside their working registers.
-BWD_NO_FUSED_DESIGN = {"bwd_lstm_D1024", "bwd_gru_D1024"}
+# fp32 heads wider than 64 units have no fused backward design (the single-workgroup fp32 design
+# holds a head of at most 64 units; the die-local designs are bf16).
+BWD_NO_FUSED_DESIGN = [
+    fi.HeadwiseWorkload("bwd_lstm_f32_D128", "lstm", torch.float32, B=2, T=5, N=1, D=128, seed=307, s0_var=1.0),
+    fi.HeadwiseWorkload("bwd_gru_f32_D256", "gru", torch.float32, B=3, T=4, N=2, D=256, seed=308, s0_var=1.0),
+]
 
 
-@pytest.mark.parametrize("w,path", [(w, p) for w in BWD_EXTREME for p in ("alternating", "fused")
-                                    if not (p == "fused" and w.name in BWD_NO_FUSED_DESIGN)],
+@pytest.mark.parametrize("w,path", [(w, p) for w in BWD_EXTREME for p in ("alternating", "fused")],
                          ids=lambda x: x if isinstance(x, str) else x.name)
 def test_bwd_extreme_shapes(w, path):
+    if path == "fused" and w.D == 1024:
+        hw = _hw()
+        plan = hw.frnn_bwd_plan_str(hw._desc(w.B, w.T, w.N, w.D, w.cell, w.dtype), "fused")
+        assert "die-local-partials" in plan and ("KTL=2" if w.cell == "lstm" else "KTL=1") in plan, plan
     run_bwd_case(w, path)
 
 
-@pytest.mark.parametrize("w", [w for w in BWD_EXTREME if w.name in BWD_NO_FUSED_DESIGN], ids=lambda w: w.name)
+def test_bwd_d1024_lds_design_full_launch():
+    """Heads of 1024 units on the partial-sum design that keeps part of R in LDS (LSTM: two of a
+    wave's four k-tiles; GRU: one of three), at 16 batch rows (8 groups of 2 rows, one per die, the
+    whole chip) over 48 steps, against the oracle."""
+    for cell, seed, ktl in (("lstm", 333, 2), ("gru", 334, 1)):
+        w = fi.HeadwiseWorkload(f"bwd_{cell}_D1024_B16", cell, torch.bfloat16, B=16, T=48, N=1, D=1024, seed=seed,
+                                s0_var=1.0)
+        hw = _hw()
+        plan = hw.frnn_bwd_plan_str(hw._desc(w.B, w.T, w.N, w.D, w.cell, w.dtype), "fused")
+        assert f"KTL={ktl} " in plan and "groups=8 " in plan and "W=32 " in plan, plan
+        run_bwd_case(w, "fused")
+
+
+def test_bwd_alternating_no_fused_design():
+    """The heads the fused backward rejects run on the alternating path, against the oracle."""
+    for w in BWD_NO_FUSED_DESIGN:
+        run_bwd_case(w, "alternating")
+
+
+@pytest.mark.parametrize("w", BWD_NO_FUSED_DESIGN, ids=lambda w: w.name)
 def test_fused_bwd_rejects_heads_without_a_design(w):
     """The fused backward reports FRNN_EUNSUPPORTED for a head it has no design for, from the
     planner and from the compute call."""
