@@ -249,6 +249,18 @@ def test_bwd_d1024_lds_design_full_launch():
         run_bwd_case(w, "fused")
 
 
+def test_bwd_d1024_lds_design_chunks():
+    """Heads of 1024 units, 40 batch rows: two launches of 20 rows (7 groups of 3 rows) on the
+    designs with R partly in LDS, LSTM and GRU, against the oracle."""
+    for cell, seed in (("lstm", 335), ("gru", 336)):
+        w = fi.HeadwiseWorkload(f"bwd_{cell}_D1024_B40", cell, torch.bfloat16, B=40, T=5, N=1, D=1024, seed=seed,
+                                s0_var=1.0)
+        hw = _hw()
+        plan = hw.frnn_bwd_plan_str(hw._desc(w.B, w.T, w.N, w.D, w.cell, w.dtype), "fused")
+        assert "KTL=" in plan and "chunks=2 " in plan, plan
+        run_bwd_case(w, "fused")
+
+
 def test_bwd_alternating_no_fused_design():
     """The heads the fused backward rejects run on the alternating path, against the oracle."""
     for w in BWD_NO_FUSED_DESIGN:
