@@ -793,6 +793,9 @@ __global__ void __launch_bounds__((NCW + 1) * 64, 1) fused_fwd_kernel(FusedArgs 
 #pragma unroll
       for (int q = 0; q < GT; ++q) wxq[q] = wxs[(((t & 1) * NCW + wave) * GT + q) * 64 + lane];
     }
+    // Keep those reads here, ahead of the MFMAs: the compiler would otherwise sink them into the
+    // gating branch that uses them, after the MFMAs, and put their LDS latency on the step's chain.
+    if (LOCAL) asm volatile("" ::: "memory");
     // ---- 1+2. h_{t-1} as the B operand, multiplied on MFMA as each k-tile becomes available.
     f32x4_t acc[MTW];
 #pragma unroll
