@@ -304,14 +304,17 @@ int env_int(const char* name, int dflt) {
 // each compute wave's MFMA chain (MTW*KTW tiles), its poll loads per lane and round, and the
 // number of compute waves (more waves meet at every barrier and split the K-sum exchange). The
 // single-workgroup design has no exchange; its chain runs over the whole K. Fitted by least squares
-// to 76 measured single-workgroup designs on eleven shapes (LSTM, GRU, Elman; D 32-128; B 16-64;
-// N 2-12; RMS 37 ns against 265 for a base shared by the cells): a base per cell (what the I/O wave
-// streams and the gates cost: the LSTM's four gates of Wx, five transcendentals and two states a
-// unit, the GRU's three, three and one, the Elman head's one gate through its DMA ring), the MFMA
-// chain, and the batch rows (the states the compute waves store, the Wx words the I/O wave loads).
+// to 110 measured single-workgroup designs on thirteen shapes (LSTM, GRU, Elman; D 32-128; B
+// 16-128; N 2-12; RMS 33 ns): a base per cell (what the I/O wave streams and the gates cost: the
+// LSTM's four gates of Wx, five transcendentals and two states a unit, the GRU's three, three and
+// one, the Elman head's one gate through its DMA ring), the MFMA chain, and two batch-row terms:
+// one growing with the rows (the states the compute waves store, the Wx words the I/O wave loads)
+// and one falling with them, fitted to the measurement that one row a workgroup runs slower than
+// two to four on every swept shape (with a row term alone the model picked one row and lost up to
+// 7 % against the best design; with both, its worst pick over 28 shapes loses 4.4 %).
 constexpr double kStepBaseDie = 0.700, kStepPerMfma = 0.0164, kStepPerPollLoad = 0.0141, kStepPerWave = 0.0181;
-constexpr double kStepBaseLocalLstm = 0.440, kStepBaseLocalGru = 0.281, kStepBaseLocalElman = 0.161;
-constexpr double kStepPerMfmaLocal = 0.0513, kStepPerRowLocal = 0.0145;
+constexpr double kStepBaseLocalLstm = 0.356, kStepBaseLocalGru = 0.157, kStepBaseLocalElman = 0.075;
+constexpr double kStepPerMfmaLocal = 0.0495, kStepPerRowLocal = 0.0193, kStepPerInvRowLocal = 0.079;
 // A die-local design with part of R^T in LDS reads MTW*KTL fragments (1 KB each) from LDS per wave
 // and step, the CU's eight compute waves sharing the LDS port: its step adds this per fragment.
 constexpr double kStepPerRLds = 0.027;
@@ -321,7 +324,7 @@ double step_cost(bool local, int cell, int br, int ncw, int ks, int mtw, int ktw
   if (local) {
     const double base = cell == FRNN_CELL_LSTM ? kStepBaseLocalLstm : cell == FRNN_CELL_GRU ? kStepBaseLocalGru
                                                                                            : kStepBaseLocalElman;
-    return base + kStepPerMfmaLocal * mtw * ktw + kStepPerRowLocal * br;
+    return base + kStepPerMfmaLocal * mtw * ktw + kStepPerRowLocal * br + kStepPerInvRowLocal / br;
   }
   const int np = (br * ktw * 32 / fused_poll_words(ks, mtw, ktw) + 63) / 64;
   return kStepBaseDie + kStepPerMfma * mtw * ktw + kStepPerPollLoad * np + kStepPerWave * ncw + kStepPerRLds * mtw * ktl;
