@@ -717,7 +717,9 @@ bool plan_fused_bwdx(int B, int N, int D, int cell, const DevInfo& di, FusedBwdP
       const int Bc = (B + chunks - 1) / chunks;
       const int groups = N * ((Bc + BR - 1) / BR);
       const int per_die = (groups + di.n_xcd - 1) / di.n_xcd;
-      if (BR * UW * BWD_REC / 2 > 64 * BWD_EPL_IN || BR * UW > 64 * BWD_EPL_OUT) continue;
+      // a step's records fill at most one slot of the I/O wave's LDS ring; its outputs, two
+      // 8-byte words per I/O lane
+      if (BR * UW * BWD_REC * 4 > BWDX_SLOT || BR * UW > 64 * BWD_EPL_OUT) continue;
       for (const int ncw : cand) {
         if (force_ncw && ncw != force_ncw) continue;
         if (TPH % ncw) continue;

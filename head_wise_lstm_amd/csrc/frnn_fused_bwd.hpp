@@ -408,8 +408,9 @@ namespace frnn {
 // ring; the step's barrier; every compute wave multiplies the stage by its R fragments and
 // publishes. The stage has two parities: a workgroup's pollers wait only for the waves that own
 // their units, so another wave may still read the stage of step s while step s+1 is written.
-// The I/O wave puts the records of step k+1 into the ring in interval k (the step is applied
-// before the barrier) and stores the outputs of step k-1.
+// The I/O wave loads the records of step k+1 into the LDS ring with LDS-direct loads, landed by
+// barrier k (the step is applied before the barrier); the lanes that apply the step store its
+// (dh, dc) themselves.
 
 constexpr int BWDX_CPW = 4;  // (row, unit quad) combinations per poll wave
 constexpr int BWDX_J = 16;   // slot chunks per combination (lanes = CPW * J = 64)
@@ -420,8 +421,14 @@ constexpr int BWDX_MAX_W = BWDX_J * BWDX_NP;
 #define FRNN_BWDX_SLEEP0 FRNN_POLL_SLEEP0
 #endif
 
+// The record ring: BWDX_RING slots of BWDX_SLOT bytes, each filled by BWDX_NE 16-byte LDS-direct
+// loads per I/O lane and step; a group's records of one step (BR * U * BWD_REC floats) fit a slot.
+constexpr int BWDX_RING = 4;
+constexpr int BWDX_NE = 4;
+constexpr int BWDX_SLOT = 64 * 16 * BWDX_NE;
+
 struct FusedBwdxLds {
-  int stage, rin, rout, r, total;
+  int stage, rin, r, total;
 };
 
 // ktl: k-tiles of R per compute wave kept in LDS (ncw waves of mtw row tiles, 1 KB per tile and
@@ -429,51 +436,73 @@ struct FusedBwdxLds {
 __host__ __device__ inline FusedBwdxLds fused_bwdx_lds(int ktw, int BR, int U, int ncw = 0, int mtw = 0, int ktl = 0) {
   FusedBwdxLds L;
   L.stage = 0;
-  L.rin = 2 * 16 * fused_stage_row(ktw) * 4;
-  L.rout = L.rin + 2 * BR * U * BWD_REC * 4;
-  L.r = L.rout + 2 * BR * U * 2 * 4;
+  L.rin = 2 * 16 * fused_stage_row(ktw) * 4;  // a multiple of 16 bytes, as the ring's loads need
+  L.r = L.rin + BWDX_RING * BWDX_SLOT;
   L.total = L.r + ncw * mtw * ktl * 1024;
+  (void)BR;
+  (void)U;
   return L;
 }
 
-// Interval k (k = -1 .. T-1): records of step k+1 into the ring, refill the load stage with step
-// k+1+4, store the outputs of step k-1, then barrier k.
-template <int ST>
-__device__ __forceinline__ bool biox_interval(const BwdIo& c, int k, io_word_t (&raw)[FUSED_IO_STAGES][BWD_EPL_IN],
-                                              float* rin, const float* rout, const int* abort_flag) {
-  constexpr int L = FUSED_IO_STAGES;
-  if (k + 1 < c.T) bio_put(c, k + 1, raw[ST], rin);
-  bio_issue(c, min(k + 1 + L, c.T - 1), raw[ST]);  // unconditional (clamped), as in bio_interval
-  if (k >= 1) bio_store(c, k - 1, rout);
-  block_barrier();
-  return uniform_flag(*abort_flag);
+// The partial-sum design's I/O wave: it only loads. A step's records come straight into a slot of
+// the LDS ring with 16-byte LDS-direct loads: lane l of load e writes slot bytes 1024 e + 16 l, so
+// chunk i = 64 e + l of the group's dense [row][U * BWD_REC] records lands where the compute waves
+// read it; a lane past the valid rows loads the first chunk again into a slot position no one
+// reads. Interval k (k = -1 .. T-1) issues the loads of step k + BWDX_RING - 1 (clamped to T - 1)
+// into its slot, whose last reader, step k - 1, finished before barrier k - 1; waits until the
+// loads of step k + 1, issued two intervals earlier, have landed; and joins barrier k, after which
+// the compute waves read step k + 1. Every interval issues the same four loads, so a constant
+// count of them stays in flight; the wave touches no LDS itself and no load result passes through
+// a register, so no wait of the compiler's joins in. Every exit waits for all loads, so that none
+// lands after the workgroup has ended.
+// A word of LDS read from inline asm, which waits for it in the same statement: a plain read would
+// make the compiler wait for every LDS-direct load in flight first (it cannot tell that they write
+// elsewhere), which would drain the ring each interval.
+__device__ __forceinline__ int lds_read_word(const int* p) {
+  const uint32_t off = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) int*)p;
+  int v;
+  asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(off) : "memory");
+  return v;
 }
 
-__device__ __forceinline__ void biox_wave(BwdIo& c, float* rin, const float* rout, const int* abort_flag) {
-  constexpr int L = FUSED_IO_STAGES;
-  static_assert(L == 4, "the interval loop below is unrolled for four stages");
-  c.init();
-  io_word_t raw[L][BWD_EPL_IN];
+struct BwdxDma {
+  const char* rec;                          // bytes
+  long long in_base, in_row, in_step;       // floats
+  int nvalid, U, T, lane;
+};
+
+__device__ __forceinline__ void biox_wave(const BwdxDma& c, char* ring, const int* abort_flag) {
+  constexpr int NS = BWDX_RING, NE = BWDX_NE;
+  static_assert(NS == 4, "the wait below counts the loads of the two intervals after a step's");
   if (c.T == 0) {
     block_barrier();
     return;
   }
-  // stage (k+1) mod 4 holds step k+1
-  bio_issue(c, 0, raw[0]);
-  bio_issue(c, min(1, c.T - 1), raw[1]);
-  bio_issue(c, min(2, c.T - 1), raw[2]);
-  bio_issue(c, min(3, c.T - 1), raw[3]);
-  int k = -1;
-  for (; k + 3 <= c.T - 1; k += L) {
-    if (biox_interval<0>(c, k, raw, rin, rout, abort_flag)) return;
-    if (biox_interval<1>(c, k + 1, raw, rin, rout, abort_flag)) return;
-    if (biox_interval<2>(c, k + 2, raw, rin, rout, abort_flag)) return;
-    if (biox_interval<3>(c, k + 3, raw, rin, rout, abort_flag)) return;
+  const int cpr = c.U * BWD_REC / 4;  // 16-byte chunks per row
+  long long goff[NE];
+#pragma unroll
+  for (int e = 0; e < NE; ++e) {
+    const int i = c.lane + 64 * e, r = i / cpr, w = i - r * cpr;
+    goff[e] = (r < c.nvalid ? c.in_base + r * c.in_row + 4 * w : c.in_base) * 4;
   }
-  if (k <= c.T - 1 && biox_interval<0>(c, k, raw, rin, rout, abort_flag)) return;
-  if (k + 1 <= c.T - 1 && biox_interval<1>(c, k + 1, raw, rin, rout, abort_flag)) return;
-  if (k + 2 <= c.T - 1 && biox_interval<2>(c, k + 2, raw, rin, rout, abort_flag)) return;
-  bio_store(c, c.T - 1, rout);  // after barrier T-1
+  const long long step_bytes = c.in_step * 4;
+  auto issue = [&](int s) {
+    const int sc = min(max(s, 0), c.T - 1);
+    char* slot = ring + (s & (NS - 1)) * BWDX_SLOT;
+#pragma unroll
+    for (int e = 0; e < NE; ++e)
+      __builtin_amdgcn_global_load_lds((glb_void_t*)(c.rec + goff[e] + sc * step_bytes), (lds_void_t*)(slot + 1024 * e),
+                                       16, 0, 0);
+  };
+  issue(0);  // steps 0 and 1, as intervals -3 and -2 would issue them
+  issue(1);
+  for (int k = -1; k < c.T; ++k) {
+    issue(k + NS - 1);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * NE));
+    __builtin_amdgcn_s_barrier();
+    if (uniform_flag(lds_read_word(abort_flag))) break;
+  }
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 }
 
 // x + (x of the lane D places up in the 16-lane row; 0 past the row's end).
@@ -518,27 +547,21 @@ __global__ void __launch_bounds__((NCW + 1) * 64, 1) fused_bwdx_kernel(FusedBwdA
   const FusedBwdxLds lay = fused_bwdx_lds(KTW, BR, UW, NCW, MTW, KTL);
   constexpr int SROW = fused_stage_row(KTW);
   uint32_t* stage = reinterpret_cast<uint32_t*>(smem + lay.stage);
-  float* rin = reinterpret_cast<float*>(smem + lay.rin);
-  float* rout = reinterpret_cast<float*>(smem + lay.rout);
+  char* const ring = smem + lay.rin;
   // both stages: rows of padding batch columns stay zero
   for (int i = threadIdx.x; i < 2 * 16 * SROW; i += (NCW + 1) * 64) stage[i] = 0u;
 
   if (wave == NCW) {
-    BwdIo c;
+    BwdxDma c;
     c.rec = reinterpret_cast<const char*>(a.rec);
-    c.dst = a.dstate;
     c.in_row = (long long)N * D * BWD_REC;
     c.in_step = (long long)a.Bs * N * D * BWD_REC;
     c.in_base = ((long long)b0 * N + n) * D * BWD_REC + (long long)u0 * BWD_REC;
-    c.out_row = (long long)N * D * 2;
-    c.out_step = (long long)a.Bs * N * D * 2;
-    c.out_base = ((long long)b0 * N + n) * D * 2 + (long long)u0 * 2;
     c.nvalid = nvalid;
     c.U = UW;
     c.T = T;
-    c.BR = BR;
     c.lane = lane;
-    biox_wave(c, rin, rout, &s_abort);
+    biox_wave(c, ring, &s_abort);
     return;
   }
 
@@ -614,7 +637,8 @@ __global__ void __launch_bounds__((NCW + 1) * 64, 1) fused_bwdx_kernel(FusedBwdA
     if (poller) {
       // this step's records of the lane's four units (in the ring since barrier s-1)
       const bool mathlane = cv && chunk == 0;
-      const float* rr = rin + ((s & 1) * BR + (mathlane ? pr : 0)) * UW * BWD_REC + (mathlane ? 4 * pq : 0) * BWD_REC;
+      const float* rr = reinterpret_cast<const float*>(ring + (s & (BWDX_RING - 1)) * BWDX_SLOT) +
+                        (mathlane ? pr : 0) * UW * BWD_REC + (mathlane ? 4 * pq : 0) * BWD_REC;
       f32x4_t rc[4][2];
       // The records go out before the poll (their latency hidden behind it) unless R k-tiles live
       // in LDS: those designs hold up to 96 VGPRs of R, and 32 registers of records held through
@@ -709,7 +733,10 @@ __global__ void __launch_bounds__((NCW + 1) * 64, 1) fused_bwdx_kernel(FusedBwdA
             *reinterpret_cast<uint2*>(sg + ((g * UW + 4 * pq) >> 1)) =
                 make_uint2((uint32_t)f2bf(da[g][0]) | ((uint32_t)f2bf(da[g][1]) << 16),
                            (uint32_t)f2bf(da[g][2]) | ((uint32_t)f2bf(da[g][3]) << 16));
-          float* ro = rout + ((s & 1) * BR + pr) * UW * 2 + 8 * pq;
+          // (dh, dc) of the four units, straight to memory: these waves' next wait on memory is
+          // the next step's poll, long after the stores have landed
+          float* ro = a.dstate + (long long)s * a.Bs * N * D * 2 + ((long long)(b0 + pr) * N + n) * D * 2 +
+                      (long long)(u0 + 4 * pq) * 2;
           *reinterpret_cast<f32x4_t*>(ro) = f32x4_t{dh[0], dc[0], dh[1], dc[1]};
           *reinterpret_cast<f32x4_t*>(ro + 4) = f32x4_t{dh[2], dc[2], dh[3], dc[3]};
         }
