@@ -798,36 +798,71 @@ namespace frnn {
 // VGPRs, with k = (g, e) over G*D in the fp32 MFMA's k-tiles of four (v_mfma_f32_16x16x4_f32, A = R
 // packed by bwd_rpack_kernel, B = da^T). Lane l of the result holds dh_R of units 4*(l/16)..+3 of
 // its tile for batch column l%16, as in the die-local design, and applies the same linear step.
-// The I/O wave streams the records in and (dh, dc) out exactly as there (one barrier per step).
+// The I/O wave streams the records into an LDS ring as the partial-sum design's does, and the
+// lanes that apply a step store its (dh, dc) (one barrier per step).
 constexpr int BWDL_NCW = 4;
 __host__ __device__ constexpr int fused_bwdl_row(int G, int D) { return G * D + 4; }  // floats per da row
 
 struct FusedBwdlLds {
-  int da, rin, rout, total;
+  int da, rin, total;
 };
 
+// The record ring has the partial-sum design's slots (a group's records of one step fit one).
 __host__ __device__ inline FusedBwdlLds fused_bwdl_lds(int G, int D, int BR) {
   FusedBwdlLds L;
   L.da = 0;
-  L.rin = 2 * 16 * fused_bwdl_row(G, D) * 4;
-  L.rout = L.rin + 2 * BR * D * BWD_REC * 4;
-  L.total = L.rout + 2 * BR * D * 2 * 4;
+  L.rin = 2 * 16 * fused_bwdl_row(G, D) * 4;  // a multiple of 16 bytes, as the ring's loads need
+  L.total = L.rin + BWDX_RING * BWDX_SLOT;
+  (void)BR;
   return L;
 }
 
-// Largest batch rows per group: the I/O wave moves at most 64 * BWD_EPL_IN record words and
-// 64 * BWD_EPL_OUT output words per step (a head's D units per row).
-__host__ __device__ constexpr int fused_bwdl_max_br(int D) {
-  return (64 * BWD_EPL_IN * 2 / BWD_REC / D) < (64 * BWD_EPL_OUT / D) ? (64 * BWD_EPL_IN * 2 / BWD_REC / D)
-                                                                       : (64 * BWD_EPL_OUT / D);
+// The single-workgroup design's I/O wave: the partial-sum design's load-only ring (see biox_wave)
+// on this design's schedule. The compute waves apply step s between barriers s and s + 1, so the
+// records of step s land by barrier s, and interval k issues step k + BWDX_RING - 2, whose slot's
+// last reader, step k - 2, finished at barrier k - 1. The design never aborts (it has no bounded
+// wait), so the wave joins every barrier, -1 .. T.
+__device__ __forceinline__ void biol_wave(const BwdxDma& c, char* ring) {
+  constexpr int NS = BWDX_RING, NE = BWDX_NE;
+  static_assert(NS == 4, "the wait below counts the loads of the two intervals after a step's");
+  if (c.T == 0) {
+    block_barrier();
+    block_barrier();
+    return;
+  }
+  const int cpr = c.U * BWD_REC / 4;  // 16-byte chunks per row
+  long long goff[NE];
+#pragma unroll
+  for (int e = 0; e < NE; ++e) {
+    const int i = c.lane + 64 * e, r = i / cpr, w = i - r * cpr;
+    goff[e] = (r < c.nvalid ? c.in_base + r * c.in_row + 4 * w : c.in_base) * 4;
+  }
+  const long long step_bytes = c.in_step * 4;
+  auto issue = [&](int s) {
+    const int sc = min(max(s, 0), c.T - 1);
+    char* slot = ring + (s & (NS - 1)) * BWDX_SLOT;
+#pragma unroll
+    for (int e = 0; e < NE; ++e)
+      __builtin_amdgcn_global_load_lds((glb_void_t*)(c.rec + goff[e] + sc * step_bytes), (lds_void_t*)(slot + 1024 * e),
+                                       16, 0, 0);
+  };
+  issue(0);  // step 0, as interval -2 would issue it
+  for (int k = -1; k <= c.T; ++k) {
+    issue(k + NS - 2);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * NE));
+    __builtin_amdgcn_s_barrier();
+  }
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 }
+
+// Largest batch rows per group: a step's records (D units a row) fill at most one ring slot.
+__host__ __device__ constexpr int fused_bwdl_max_br(int D) { return BWDX_SLOT / (D * BWD_REC * 4); }
 
 template <int CELL, int KT>
 __global__ void __launch_bounds__((BWDL_NCW + 1) * 64, 1) fused_bwd_local_kernel(FusedBwdArgs a) {
   constexpr int G = cell_gates(CELL);
   constexpr int NCW = BWDL_NCW;
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  __shared__ int s_abort;
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int col = lane & 15, quad = lane >> 4;
@@ -835,35 +870,28 @@ __global__ void __launch_bounds__((BWDL_NCW + 1) * 64, 1) fused_bwd_local_kernel
   const int TPH = D / 16;  // row tiles of a head (at most NCW)
   const int group = blockIdx.x;
   if (group >= a.groups) return;
-  if (threadIdx.x == 0) s_abort = 0;
   const int n = group % N, bblk = group / N;
   const int b0 = bblk * a.BR;
   const int nvalid = min(a.BR, a.B - b0);
   const FusedBwdlLds lay = fused_bwdl_lds(G, D, a.BR);
   const int ROW = fused_bwdl_row(G, D);
   float* dab = reinterpret_cast<float*>(smem + lay.da);
-  float* rin = reinterpret_cast<float*>(smem + lay.rin);
-  float* rout = reinterpret_cast<float*>(smem + lay.rout);
+  char* const ring = smem + lay.rin;
   // both parities of da start at zero: step 0 has no dh_R, and rows of padding batch columns
   // are never written
   for (int i = threadIdx.x; i < 2 * 16 * ROW; i += (NCW + 1) * 64) dab[i] = 0.0f;
 
   if (wave == NCW) {
-    BwdIo c;
+    BwdxDma c;
     c.rec = reinterpret_cast<const char*>(a.rec);
-    c.dst = a.dstate;
     c.in_row = (long long)N * D * BWD_REC;
     c.in_step = (long long)a.Bs * N * D * BWD_REC;
     c.in_base = ((long long)b0 * N + n) * D * BWD_REC;
-    c.out_row = (long long)N * D * 2;
-    c.out_step = (long long)a.Bs * N * D * 2;
-    c.out_base = ((long long)b0 * N + n) * D * 2;
     c.nvalid = nvalid;
     c.U = D;
     c.T = T;
-    c.BR = a.BR;
     c.lane = lane;
-    bio_wave(c, rin, rout, &s_abort);
+    biol_wave(c, ring);
     return;
   }
 
@@ -883,7 +911,6 @@ __global__ void __launch_bounds__((BWDL_NCW + 1) * 64, 1) fused_bwd_local_kernel
 
   for (int s = 0; s < T; ++s) {
     block_barrier();  // barrier s: the step before's da and this step's records are in LDS
-    if (uniform_flag(s_abort)) return;
     if (tv) {  // (uniform in the wave; every wave reaches every barrier)
       // ---- dh_R = sum over k of R[d][k] da[k] for this wave's 16 rows d, all batch columns
       f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
@@ -896,8 +923,10 @@ __global__ void __launch_bounds__((BWDL_NCW + 1) * 64, 1) fused_bwd_local_kernel
       const f32x4_t pre = acc0 + acc1;
       if (colv) {
         // ---- the linear step for the lane's four units; da into this step's parity, (dh, dc) out
-        const float* rr = rin + ((s & 1) * a.BR + col) * D * BWD_REC + gu * BWD_REC;
-        float* ro = rout + ((s & 1) * a.BR + col) * D * 2 + gu * 2;
+        const float* rr = reinterpret_cast<const float*>(ring + (s & (BWDX_RING - 1)) * BWDX_SLOT) + col * D * BWD_REC +
+                          gu * BWD_REC;
+        // (dh, dc) straight to memory: these waves never wait on memory
+        float* ro = a.dstate + (long long)s * a.Bs * N * D * 2 + ((long long)(b0 + col) * N + n) * D * 2 + gu * 2;
         float da[G][4], dh[4], dc[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -933,7 +962,7 @@ __global__ void __launch_bounds__((BWDL_NCW + 1) * 64, 1) fused_bwd_local_kernel
       }
     }
   }
-  block_barrier();  // barrier T: the last step's outputs are in LDS for the I/O wave
+  block_barrier();  // barrier T (the I/O wave joins barriers -1 .. T)
 }
 
 }  // namespace frnn
