@@ -18,9 +18,11 @@
 // dh_R of units 4*(l/16)..+3 of its tile for batch column l%16, applies the step to them, and
 // publishes their da (G words per unit, bf16 << 16 | step tag) through the die's L2; every
 // workgroup polls the da of the whole group (its K range per wave) as the next step's B operand.
-// A fifth kind of wave, the I/O wave, streams the step records into an LDS ring four steps ahead
-// and writes each step's (dh, dc) out of another ring. dWx and the dR operand are formed from
-// (dh, dc) afterwards, for all steps at once (bwd_post_kernel).
+// A fifth kind of wave, the I/O wave, streams the step records into an LDS ring ahead of the
+// steps (this design: four steps ahead through registers, and it writes each step's (dh, dc) out
+// of another ring; the partial-sum and single-workgroup designs below: LDS-direct loads, with
+// (dh, dc) stored by the lanes that compute them). dWx and the dR operand are formed from (dh,
+// dc) afterwards, for all steps at once (bwd_post_kernel).
 #pragma once
 
 #include "frnn_fused.hpp"
@@ -403,9 +405,9 @@ namespace frnn {
 // Per step s: poll waves (the first PW compute waves, four (row, unit quad) combinations each,
 // sixteen slot chunks per combination in one 16-lane row, two 16-byte loads per lane, summed by
 // four DPP row shifts) poll,
-// apply the step (its records read from LDS before the poll) and write da into the
-// stage of parity s (bf16 B fragments [batch row][k], k = g*UW + unit) and (dh, dc) into the output
-// ring; the step's barrier; every compute wave multiplies the stage by its R fragments and
+// apply the step (its records read from LDS, before the poll where the registers allow) and write
+// da into the stage of parity s (bf16 B fragments [batch row][k], k = g*UW + unit) and (dh, dc) to
+// memory; the step's barrier; every compute wave multiplies the stage by its R fragments and
 // publishes. The stage has two parities: a workgroup's pollers wait only for the waves that own
 // their units, so another wave may still read the stage of step s while step s+1 is written.
 // The I/O wave loads the records of step k+1 into the LDS ring with LDS-direct loads, landed by
