@@ -1082,7 +1082,7 @@ int run_backward(const BwdProblem& q, int path, const FusedBwdPlan& fbp, const D
         return FRNN_EHIP;
   }
   // 1. h_{t-1} for every step, R^T, and h.R for every step
-  hipLaunchKernelGGL(bwd_hprev_kernel, dim3((unsigned)std::min<long long>(((long long)N * Kp * D + 255) / 256, 65536)),
+  hipLaunchKernelGGL(bwd_hprev_kernel, dim3((unsigned)std::min<long long>(((long long)N * Kp * (D / 8) + 255) / 256, 65536)),
                      dim3(256), 0, st, a);
   for (int n = 0; n < N; ++n) {
     for (int g = 0; g < G; ++g) {
@@ -1152,7 +1152,7 @@ int run_backward(const BwdProblem& q, int path, const FusedBwdPlan& fbp, const D
                       tmp + (size_t)n * (D + 1) * G * D, (long long)G * D, st, parts, kpart, kpart, ptot) != hipSuccess)
         return FRNN_EHIP;
     }
-    const long long nt = ptot;
+    const long long nt = ptot / 4;
     hipLaunchKernelGGL(bwd_scatter_kernel, dim3((unsigned)std::min<long long>((nt + 255) / 256, 65536)), dim3(256), 0, st,
                        tmp, parts, N, D, G, q.dR, q.dr_sg, q.dr_sn, q.dr_sd, q.db);
   }

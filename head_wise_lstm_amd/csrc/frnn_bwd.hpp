@@ -65,21 +65,44 @@ __device__ __forceinline__ void st_op(void* p, long long i, float v, bool f32) {
 
 // hprev[n][t*B + b][d] = h_{t-1}[b][n][d] (the initial state for t = 0), in the operand type;
 // rows T*B .. Kp-1 are zero.
+// Eight consecutive d per thread (D is a multiple of 32): the index arithmetic once per eight
+// elements, and one 16-byte store of the bf16 operand (two of fp32).
 __global__ void __launch_bounds__(256) bwd_hprev_kernel(BwdArgs a) {
-  const long long total = (long long)a.N * a.Kp * a.D;
+  const int DC = a.D / 8;
+  const long long total = (long long)a.N * a.Kp * DC;
   const bool f32 = a.f32;
   for (long long idx = (long long)blockIdx.x * 256 + threadIdx.x; idx < total; idx += (long long)gridDim.x * 256) {
-    const int d = (int)(idx % a.D);
-    const long long r = idx / a.D;
+    const int d0 = (int)(idx % DC) * 8;
+    const long long r = idx / DC;
     const int row = (int)(r % a.Kp);
     const int n = (int)(r / a.Kp);
-    float v = 0.0f;
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = 0.0f;
     if (row < a.T * a.B) {
       const int t = row / a.B, b = row % a.B;
-      if (t > 0) v = a.st_h[(long long)b * a.st_sb + (long long)(t - 1) * a.st_st + (long long)n * a.D + d];
-      else if (a.s0_h) v = ld_f(a.s0_h, (long long)b * a.s0_sb + (long long)n * a.D + d, f32);
+      if (t > 0) {
+        const float* src = a.st_h + (long long)b * a.st_sb + (long long)(t - 1) * a.st_st + (long long)n * a.D + d0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = src[i];
+      } else if (a.s0_h) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = ld_f(a.s0_h, (long long)b * a.s0_sb + (long long)n * a.D + d0 + i, f32);
+      }
     }
-    st_op(a.hprev, idx, v, f32);
+    const long long o = r * a.D + d0;  // element index of the operand
+    if (f32) {
+      float4* dst = reinterpret_cast<float4*>(reinterpret_cast<float*>(a.hprev) + o);
+      dst[0] = make_float4(v[0], v[1], v[2], v[3]);
+      dst[1] = make_float4(v[4], v[5], v[6], v[7]);
+    } else {
+      uint4 w;
+      w.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
+      w.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
+      w.z = (uint32_t)f2bf(v[4]) | ((uint32_t)f2bf(v[5]) << 16);
+      w.w = (uint32_t)f2bf(v[6]) | ((uint32_t)f2bf(v[7]) << 16);
+      *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(a.hprev) + o) = w;
+    }
   }
 }
 
@@ -496,21 +519,30 @@ __global__ void __launch_bounds__(256) bwd_final_kernel(BwdArgs a) {
 // and db[g][n][e] = sum_p tmp[p][n][D][g*D + e]
 // (tmp: [parts][N][D+1][G*D] fp32, the K-split parts of the dR GEMM's output with its row of
 // ones), the parts added in order.
+// Four consecutive e per thread (one 16-byte load of each part; D is a multiple of 32, so the
+// four stay in one gate).
 __global__ void __launch_bounds__(256) bwd_scatter_kernel(const float* tmp, int parts, int N, int D, int G, float* dR,
                                                           long long dr_sg, long long dr_sn, long long dr_sd, float* db) {
   const long long total = (long long)N * (D + 1) * G * D;
-  for (long long idx = (long long)blockIdx.x * 256 + threadIdx.x; idx < total; idx += (long long)gridDim.x * 256) {
-    float v = 0.0f;
-    for (int p = 0; p < parts; ++p) v += tmp[p * total + idx];
-    const int col = (int)(idx % (G * D));
-    const long long r = idx / (G * D);
+  const int CPR = G * D / 4;  // chunks of four per row
+  for (long long idx = (long long)blockIdx.x * 256 + threadIdx.x; idx < total / 4; idx += (long long)gridDim.x * 256) {
+    f32x4_t v = {0.f, 0.f, 0.f, 0.f};
+    for (int p = 0; p < parts; ++p) v += *reinterpret_cast<const f32x4_t*>(tmp + p * total + 4 * idx);
+    const int col = (int)(idx % CPR) * 4;
+    const long long r = idx / CPR;
     const int d = (int)(r % (D + 1));
     const int n = (int)(r / (D + 1));
     const int g = col / D, e = col % D;
     if (d < D) {
-      if (dR) dR[(long long)g * dr_sg + (long long)n * dr_sn + (long long)d * dr_sd + e] = v;
+      if (dR) {
+        float* o = dR + (long long)g * dr_sg + (long long)n * dr_sn + (long long)d * dr_sd + e;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[i] = v[i];
+      }
     } else if (db) {
-      db[((long long)g * N + n) * D + e] = v;
+      float* o = db + ((long long)g * N + n) * D + e;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[i] = v[i];
     }
   }
 }
