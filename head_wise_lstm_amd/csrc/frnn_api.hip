@@ -252,6 +252,13 @@ int raise_lds_limits() {
         return FRNN_EHIP;
     }
   }
+  for (const int D : {32, 64}) {
+    const fused_bwd_fn fns[3] = {fused_bwd_local_lstm(D), fused_bwd_local_gru(D), fused_bwd_local_elman(D)};
+    const int gates[3] = {4, 3, 1};
+    for (int c = 0; c < 3; ++c)
+      if (fns[c] && !raise(reinterpret_cast<const void*>(fns[c]), fused_bwdl_lds(gates[c], D, fused_bwdl_max_br(D)).total))
+        return FRNN_EHIP;
+  }
   return FRNN_OK;
 }
 
@@ -480,19 +487,23 @@ hipError_t launch_fill(void* p, size_t bytes, hipStream_t st, uint32_t value = 0
   return hipGetLastError();
 }
 
-// dst[j][k] = src[k][j] (K rows of Nc elements, 2- or 4-byte elements).
+// dst[j][k] = src[k][j] (K rows of Nc elements, 2- or 4-byte elements), for mats matrices in one
+// launch, matrix z at src + z * src_z and dst + z * dst_z.
 template <typename E>
-void launch_transpose(const E* src, long long lds, int K, int Nc, E* dst, long long ldd, hipStream_t st) {
-  if (K <= 0 || Nc <= 0) return;
-  if (sizeof(E) == 2 && lds % 4 == 0 && ldd % 4 == 0 && !(reinterpret_cast<uintptr_t>(src) & 7) &&
-      !(reinterpret_cast<uintptr_t>(dst) & 7)) {
+void launch_transpose(const E* src, long long lds, int K, int Nc, E* dst, long long ldd, hipStream_t st, int mats = 1,
+                      long long src_z = 0, long long dst_z = 0) {
+  if (K <= 0 || Nc <= 0 || mats <= 0) return;
+  if (sizeof(E) == 2 && lds % 4 == 0 && ldd % 4 == 0 && src_z % 4 == 0 && dst_z % 4 == 0 &&
+      !(reinterpret_cast<uintptr_t>(src) & 7) && !(reinterpret_cast<uintptr_t>(dst) & 7)) {
     const int ty = (int)std::min<long long>(((long long)K + 63) / 64, 65535);
-    hipLaunchKernelGGL(transpose_b16_kernel, dim3((Nc + 63) / 64, ty), dim3(256), 0, st,
-                       reinterpret_cast<const uint16_t*>(src), lds, K, Nc, reinterpret_cast<uint16_t*>(dst), ldd);
+    hipLaunchKernelGGL(transpose_b16_kernel, dim3((Nc + 63) / 64, ty, mats), dim3(256), 0, st,
+                       reinterpret_cast<const uint16_t*>(src), lds, K, Nc, reinterpret_cast<uint16_t*>(dst), ldd, src_z,
+                       dst_z);
     return;
   }
   const int ty = (int)std::min<long long>(((long long)K + 31) / 32, 65535);
-  hipLaunchKernelGGL(transpose_kernel<E>, dim3((Nc + 31) / 32, ty), dim3(256), 0, st, src, lds, K, Nc, dst, ldd);
+  hipLaunchKernelGGL(transpose_kernel<E>, dim3((Nc + 31) / 32, ty, mats), dim3(256), 0, st, src, lds, K, Nc, dst, ldd,
+                     src_z, dst_z);
 }
 
 // Launch of the bf16 GEMM of ProjArgs: with bf16 A whose rows (and Bt's, and the parts' offsets)
@@ -501,7 +512,8 @@ void launch_transpose(const E* src, long long lds, int K, int Nc, E* dst, long l
 void launch_proj(const ProjArgs& pa, dim3 grid, hipStream_t st) {
   if (pa.M <= 0 || pa.Nc <= 0) return;
   const bool aligned = reinterpret_cast<uintptr_t>(pa.A) % 16 == 0 && reinterpret_cast<uintptr_t>(pa.Bt) % 16 == 0 &&
-                       pa.lda % 8 == 0 && pa.ldb % 8 == 0 && pa.a_z % 8 == 0 && pa.b_z % 8 == 0;
+                       pa.lda % 8 == 0 && pa.ldb % 8 == 0 && pa.a_z % 8 == 0 && pa.b_z % 8 == 0 &&
+                       pa.a_h % 8 == 0 && pa.b_h % 8 == 0;
   const bool dma = !pa.a_f32 && aligned && env_int("FRNN_PROJ_DMA", 1);
   if (pa.nt) {
     if (pa.a_f32) hipLaunchKernelGGL((proj_gemm_kernel<true, true>), grid, dim3(256), 0, st, pa);
@@ -514,19 +526,21 @@ void launch_proj(const ProjArgs& pa, dim3 grid, hipStream_t st) {
   }
 }
 
-// C[M][Nc] = A[M][K] . Bt[Nc][K]^T in fp32, for parts z = 0 .. parts-1 at once (A, Bt and C
-// offset by z * a_z, b_z, c_z elements): the tiled MFMA kernel for bf16 operands, the plain fp32
-// MFMA kernel for fp32 ones. K is a multiple of 32.
+// C[M][Nc] = A[M][K] . Bt[Nc][K]^T in fp32, for parts y = 0 .. parts-1 of heads z = 0 .. heads-1
+// at once (A, Bt and C offset by y * a_z + z * a_h, y * b_z + z * b_h, y * c_z + z * c_h
+// elements): the tiled MFMA kernel for bf16 operands, the plain fp32 MFMA kernel for fp32 ones. K
+// is a multiple of 32.
 hipError_t launch_gemm(bool f32, int M, int Nc, int K, const void* A, long long lda, const void* Bt, long long ldb,
                        float* C, long long ldc, hipStream_t st, int parts = 1, long long a_z = 0, long long b_z = 0,
-                       long long c_z = 0, bool a_f32 = false) {
+                       long long c_z = 0, bool a_f32 = false, int heads = 1, long long a_h = 0, long long b_h = 0,
+                       long long c_h = 0) {
   if (M <= 0 || Nc <= 0) return hipSuccess;
-  if (K % 32 != 0 || parts < 1) return hipErrorInvalidValue;
+  if (K % 32 != 0 || parts < 1 || heads < 1 || heads > 65535) return hipErrorInvalidValue;
   if (f32) {
     const long long tiles = (long long)((M + 15) / 16) * ((Nc + 15) / 16);
-    hipLaunchKernelGGL(gemm_f32_kernel, dim3((unsigned)((tiles + 3) / 4), parts), dim3(256), 0, st, M, Nc, K,
+    hipLaunchKernelGGL(gemm_f32_kernel, dim3((unsigned)((tiles + 3) / 4), parts, heads), dim3(256), 0, st, M, Nc, K,
                        reinterpret_cast<const float*>(A), lda, reinterpret_cast<const float*>(Bt), ldb, C, ldc, a_z, b_z,
-                       c_z);
+                       c_z, a_h, b_h, c_h);
     return hipGetLastError();
   }
   ProjArgs pa;
@@ -537,8 +551,9 @@ hipError_t launch_gemm(bool f32, int M, int Nc, int K, const void* A, long long 
   pa.b1 = nullptr; pa.b2 = nullptr;
   pa.C = C; pa.ldc = ldc;
   pa.a_z = a_z; pa.b_z = b_z; pa.c_z = c_z;
+  pa.a_h = a_h; pa.b_h = b_h; pa.c_h = c_h;
   pa.nt = 1;  // every caller's product is read by a streaming kernel
-  const dim3 pgrid(((Nc + PJ_BN - 1) / PJ_BN) * ((M + PJ_BM - 1) / PJ_BM), parts);
+  const dim3 pgrid(((Nc + PJ_BN - 1) / PJ_BN) * ((M + PJ_BM - 1) / PJ_BM), parts, heads);
   launch_proj(pa, pgrid, st);
   return hipGetLastError();
 }
@@ -663,13 +678,24 @@ int run_recurrence(const Problem& p, int path, int* err, void* scratch, hipStrea
 // ----------------------------------------------------------------------------- backward
 // Workspace of frnn_bwd after the error word (grows with T: it holds every step's h.R and da).
 // K split of the dR GEMM (K = T*B is long and its output small): the parts are summed by the
-// scatter kernel.
+// scatter kernel. The multi-layer backward's dWi GEMMs take BWD_DR_PARTS parts.
 constexpr int BWD_DR_PARTS = 8;
 
-// Rows of the (t, b) operand buffers: T*B padded to whole 32-wide k-tiles of every dR part.
-size_t bwd_kp(int T, int B) {
-  const size_t q = 32 * BWD_DR_PARTS;
+// Rows of the (t, b) operand buffers: T*B padded to whole 32-wide k-tiles of every one of P parts.
+size_t bwd_kp(int T, int B, int P = BWD_DR_PARTS) {
+  const size_t q = 32 * (size_t)P;
   return ((size_t)T * B + q - 1) / q * q;
+}
+
+// K parts of the head-wise dR GEMM (all heads in one launch): eight, doubled (up to 128) while the
+// output tiles of all heads times the parts stay under 512 workgroups and a part keeps at least
+// 512 of K. Many narrow heads have few output tiles each: twelve heads of 64 units have one 256 x
+// 128 tile each, so eight parts would leave the K = T*B sum to 96 workgroups.
+int bwd_dr_parts(int T, int B, int N, int D, int G) {
+  const long long tiles = (long long)N * ((D + 1 + PJ_BM - 1) / PJ_BM) * ((G * D + PJ_BN - 1) / PJ_BN);
+  int P = BWD_DR_PARTS;
+  while (P < 128 && tiles * P < 512 && (long long)T * B >= 1024LL * P) P *= 2;
+  return P;
 }
 
 struct BwdLayout {
@@ -850,7 +876,8 @@ int plan_fused_bwd_da(int B, int N, int D, int cell, const DevInfo& di, FusedBwd
 
 BwdLayout bwd_layout(int B, int T, int N, int D, int cell, int f32, int path) {
   const size_t G = gates_of(cell), elt = f32 ? 4 : 2;
-  const size_t Kp = bwd_kp(T, B);
+  const int P = bwd_dr_parts(T, B, N, D, (int)G);
+  const size_t Kp = bwd_kp(T, B, P);
   BwdLayout L;
   size_t q = 0;
   L.zeros = q;  q += 256;
@@ -861,7 +888,7 @@ BwdLayout bwd_layout(int B, int T, int N, int D, int cell, int f32, int path) {
   L.hr = q;     q += align256((size_t)N * T * B * G * D * 4);
   L.da = q;     q += align256((size_t)N * Kp * G * D * elt);
   L.daT = q;    q += align256((size_t)N * G * D * Kp * elt);
-  L.tmp = q;    q += align256((size_t)BWD_DR_PARTS * N * (D + 1) * G * D * 4);
+  L.tmp = q;    q += align256((size_t)P * N * (D + 1) * G * D * 4);
   L.dhpart = q; q += align256((size_t)BWD_KS * B * N * D * 4);
   L.carry = q;  q += align256((size_t)B * N * D * 4);
   L.rec = L.dstate = L.xbuf = L.rpk32 = q;
@@ -900,7 +927,7 @@ std::string bwd_plan_string(const frnn_desc* d, int path, const FusedBwdPlan* fp
     return std::string(buf);
   }
   const int G = gates_of(d->cell);
-  const long long Kp = (long long)bwd_kp(d->T, d->B);
+  const long long Kp = (long long)bwd_kp(d->T, d->B, bwd_dr_parts(d->T, d->B, d->N, d->D, G));
   std::snprintf(buf, sizeof(buf),
                 "backward path=%s cell=%s dtype=%s B=%d T=%d N=%d D=%d hr_gemm=%lldx%dx%d dR_gemm=%dx%dx%lld "
                 "step_launches=%d",
@@ -1044,7 +1071,8 @@ int run_backward(const BwdProblem& q, int path, const FusedBwdPlan& fbp, const D
   const size_t elt = f32 ? 4 : 2;
   const unsigned sgrid = (unsigned)((BND + 255) / 256);
   int rc = FRNN_OK;
-  const int Kp = (int)bwd_kp(T, B);
+  const int parts = bwd_dr_parts(T, B, N, D, G);
+  const int Kp = (int)bwd_kp(T, B, parts);
   BwdArgs a;
   std::memset(&a, 0, sizeof(a));
   a.B = B; a.T = T; a.N = N; a.D = D; a.cell = q.cell; a.f32 = f32; a.wx_f32 = f32 || q.wx_f32; a.Kp = Kp;
@@ -1084,16 +1112,24 @@ int run_backward(const BwdProblem& q, int path, const FusedBwdPlan& fbp, const D
   // 1. h_{t-1} for every step, R^T, and h.R for every step
   hipLaunchKernelGGL(bwd_hprev_kernel, dim3((unsigned)std::min<long long>(((long long)N * Kp * (D / 8) + 255) / 256, 65536)),
                      dim3(256), 0, st, a);
-  for (int n = 0; n < N; ++n) {
-    for (int g = 0; g < G; ++g) {
-      const size_t src = (size_t)g * a.r_sg + (size_t)n * a.r_sn, dst = ((size_t)n * G + g) * D * D;
-      if (f32) launch_transpose<uint32_t>(reinterpret_cast<const uint32_t*>(q.R) + src, a.r_sd, D, D, reinterpret_cast<uint32_t*>(rt) + dst, D, st);
-      else launch_transpose<uint16_t>(reinterpret_cast<const uint16_t*>(q.R) + src, a.r_sd, D, D, reinterpret_cast<uint16_t*>(rt) + dst, D, st);
-    }
-    if (launch_gemm(f32, T * B, G * D, D, base + L.hprev + (size_t)n * Kp * D * elt, D, rt + (size_t)n * G * D * D * elt, D,
-                    hr + (size_t)n * T * B * G * D, (long long)G * D, st) != hipSuccess)
-      return FRNN_EHIP;
+  // R_g^T of every (head, gate): one launch per gate over the heads, or per head over the gates,
+  // whichever makes fewer launches
+  const bool by_head = N >= G;
+  for (int i = 0; i < (by_head ? G : N); ++i) {
+    const int g = by_head ? i : 0, n = by_head ? 0 : i;
+    const size_t src = (size_t)g * a.r_sg + (size_t)n * a.r_sn, dst = ((size_t)n * G + g) * D * D;
+    const long long src_z = by_head ? a.r_sn : a.r_sg, dst_z = by_head ? (long long)G * D * D : (long long)D * D;
+    if (f32)
+      launch_transpose<uint32_t>(reinterpret_cast<const uint32_t*>(q.R) + src, a.r_sd, D, D,
+                                 reinterpret_cast<uint32_t*>(rt) + dst, D, st, by_head ? N : G, src_z, dst_z);
+    else
+      launch_transpose<uint16_t>(reinterpret_cast<const uint16_t*>(q.R) + src, a.r_sd, D, D,
+                                 reinterpret_cast<uint16_t*>(rt) + dst, D, st, by_head ? N : G, src_z, dst_z);
   }
+  // h.R of every head in one launch
+  if (launch_gemm(f32, T * B, G * D, D, base + L.hprev, D, rt, D, hr, (long long)G * D, st, 1, 0, 0, 0, false, N,
+                  (long long)Kp * D, (long long)G * D * D, (long long)T * B * G * D) != hipSuccess)
+    return FRNN_EHIP;
   // 2. the serial part (R packed once as the dh kernels' A fragments)
   {
     const long long np = (long long)N * (D / 16) * (G * D / (f32 ? 4 : 32)) * 64;
@@ -1128,30 +1164,29 @@ int run_backward(const BwdProblem& q, int path, const FusedBwdPlan& fbp, const D
   if (hipGetLastError() != hipSuccess) return FRNN_EHIP;
   // 3. dR and db: per head, [D+1 rows: h^T and ones] x [G*D columns of da], over K = T*B
   if (q.dR || q.db) {
-    for (int n = 0; n < N; ++n) {
-      const size_t hoff = (size_t)n * Kp * D, toff = (size_t)n * (D + 1) * Kp;
-      const size_t doff = (size_t)n * Kp * G * D, dtoff = (size_t)n * G * D * Kp;
-      if (f32) {
-        launch_transpose<uint32_t>(reinterpret_cast<const uint32_t*>(a.hprev) + hoff, D, Kp, D, reinterpret_cast<uint32_t*>(hT) + toff, Kp, st);
-        launch_transpose<uint32_t>(reinterpret_cast<const uint32_t*>(a.da) + doff, (long long)G * D, Kp, G * D,
-                                   reinterpret_cast<uint32_t*>(daT) + dtoff, Kp, st);
-      } else {
-        launch_transpose<uint16_t>(reinterpret_cast<const uint16_t*>(a.hprev) + hoff, D, Kp, D, reinterpret_cast<uint16_t*>(hT) + toff, Kp, st);
-        launch_transpose<uint16_t>(reinterpret_cast<const uint16_t*>(a.da) + doff, (long long)G * D, Kp, G * D,
-                                   reinterpret_cast<uint16_t*>(daT) + dtoff, Kp, st);
-      }
+    // h^T and da^T of every head, one launch each
+    const long long h_z = (long long)Kp * D, ht_z = (long long)(D + 1) * Kp;
+    const long long d_z = (long long)Kp * G * D, dt_z = (long long)G * D * Kp;
+    if (f32) {
+      launch_transpose<uint32_t>(reinterpret_cast<const uint32_t*>(a.hprev), D, Kp, D, reinterpret_cast<uint32_t*>(hT), Kp,
+                                 st, N, h_z, ht_z);
+      launch_transpose<uint32_t>(reinterpret_cast<const uint32_t*>(a.da), (long long)G * D, Kp, G * D,
+                                 reinterpret_cast<uint32_t*>(daT), Kp, st, N, d_z, dt_z);
+    } else {
+      launch_transpose<uint16_t>(reinterpret_cast<const uint16_t*>(a.hprev), D, Kp, D, reinterpret_cast<uint16_t*>(hT), Kp,
+                                 st, N, h_z, ht_z);
+      launch_transpose<uint16_t>(reinterpret_cast<const uint16_t*>(a.da), (long long)G * D, Kp, G * D,
+                                 reinterpret_cast<uint16_t*>(daT), Kp, st, N, d_z, dt_z);
     }
     hipLaunchKernelGGL(bwd_ones_row_kernel, dim3((unsigned)std::min<long long>(((long long)N * Kp + 255) / 256, 4096)),
                        dim3(256), 0, st, hT, N, D, Kp, f32);
-    // K split into BWD_DR_PARTS equal parts, computed in one launch per head and summed by the
-    // scatter kernel
-    const int parts = BWD_DR_PARTS, kpart = Kp / parts;
+    // K split into equal parts (bwd_dr_parts), all parts of all heads in one launch, summed in
+    // order by the scatter kernel
+    const int kpart = Kp / parts;
     const long long ptot = (long long)N * (D + 1) * G * D;
-    for (int n = 0; n < N; ++n) {
-      if (launch_gemm(f32, D + 1, G * D, kpart, hT + (size_t)n * (D + 1) * Kp * elt, Kp, daT + (size_t)n * G * D * Kp * elt, Kp,
-                      tmp + (size_t)n * (D + 1) * G * D, (long long)G * D, st, parts, kpart, kpart, ptot) != hipSuccess)
-        return FRNN_EHIP;
-    }
+    if (launch_gemm(f32, D + 1, G * D, kpart, hT, Kp, daT, Kp, tmp, (long long)G * D, st, parts, kpart, kpart, ptot, false,
+                    N, ht_z, dt_z, (long long)(D + 1) * G * D) != hipSuccess)
+      return FRNN_EHIP;
     const long long nt = ptot / 4;
     hipLaunchKernelGGL(bwd_scatter_kernel, dim3((unsigned)std::min<long long>((nt + 255) / 256, 65536)), dim3(256), 0, st,
                        tmp, parts, N, D, G, q.dR, q.dr_sg, q.dr_sn, q.dr_sd, q.db);
@@ -1551,6 +1586,7 @@ int frnn_lstm_stack_fwd(int L, int dirs, int T, int B, int I, int H, int path, c
     pa.Bt = wit;
     pa.ldb = pa.K;
     pa.a_z = pa.b_z = pa.c_z = 0;
+    pa.a_h = pa.b_h = pa.c_h = 0;
     pa.nt = 0;  // the recurrence reads Wx next: left where its loads find it soonest
     if (dirs == 1) {
       pa.b1 = b_ih ? reinterpret_cast<const uint16_t*>(b_ih[l]) : nullptr;
@@ -1740,6 +1776,7 @@ int frnn_lstm_stack_bwd(int L, int dirs, int T, int B, int I, int H, int path, c
       pa.Bt = wit;
       pa.ldb = in;
       pa.a_z = pa.b_z = pa.c_z = 0;
+      pa.a_h = pa.b_h = pa.c_h = 0;
       pa.nt = 0;  // the recurrence reads Wx next: left where its loads find it soonest
       pa.b1 = b_ih ? reinterpret_cast<const uint16_t*>(b_ih[j]) : nullptr;
       pa.b2 = b_hh ? reinterpret_cast<const uint16_t*>(b_hh[j]) : nullptr;

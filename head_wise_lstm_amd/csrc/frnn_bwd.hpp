@@ -561,10 +561,11 @@ __global__ void __launch_bounds__(256) bwd_ones_row_kernel(void* hT, int N, int 
 // wave on v_mfma_f32_16x16x4f32, operands read straight from memory (K a multiple of 4).
 __global__ void __launch_bounds__(256) gemm_f32_kernel(int M, int Nc, int K, const float* A, long long lda,
                                                        const float* Bt, long long ldb, float* C, long long ldc,
-                                                       long long a_z, long long b_z, long long c_z) {
-  A += blockIdx.y * a_z;  // part blockIdx.y of a batch of independent products
-  Bt += blockIdx.y * b_z;
-  C += blockIdx.y * c_z;
+                                                       long long a_z, long long b_z, long long c_z, long long a_h,
+                                                       long long b_h, long long c_h) {
+  A += blockIdx.y * a_z + blockIdx.z * a_h;  // part blockIdx.y of head blockIdx.z of a batch of products
+  Bt += blockIdx.y * b_z + blockIdx.z * b_h;
+  C += blockIdx.y * c_z + blockIdx.z * c_h;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int col = lane & 15, quad = lane >> 4;
   const int tn = (Nc + 15) / 16;

@@ -804,29 +804,35 @@ namespace frnn {
 // lanes that apply a step store its (dh, dc) (one barrier per step).
 constexpr int BWDL_NCW = 4;
 __host__ __device__ constexpr int fused_bwdl_row(int G, int D) { return G * D + 4; }  // floats per da row
+// The design's record ring: BWDX_RING slots of BWDL_SLOT bytes, BWDL_NE 16-byte LDS-direct loads
+// per I/O lane and step; twice the partial-sum design's slot, so that a 64-unit head takes four
+// batch rows a workgroup.
+constexpr int BWDL_NE = 8;
+constexpr int BWDL_SLOT = 64 * 16 * BWDL_NE;
 
 struct FusedBwdlLds {
   int da, rin, total;
 };
 
-// The record ring has the partial-sum design's slots (a group's records of one step fit one).
+// A group's records of one step fit one slot of the record ring.
 __host__ __device__ inline FusedBwdlLds fused_bwdl_lds(int G, int D, int BR) {
   FusedBwdlLds L;
   L.da = 0;
   L.rin = 2 * 16 * fused_bwdl_row(G, D) * 4;  // a multiple of 16 bytes, as the ring's loads need
-  L.total = L.rin + BWDX_RING * BWDX_SLOT;
+  L.total = L.rin + BWDX_RING * BWDL_SLOT;
   (void)BR;
   return L;
 }
 
 // The single-workgroup design's I/O wave: the partial-sum design's load-only ring (see biox_wave)
-// on this design's schedule. The compute waves apply step s between barriers s and s + 1, so the
+// with BWDL_NE loads per lane and step, on this design's schedule. The compute waves apply step s between barriers s and s + 1, so the
 // records of step s land by barrier s, and interval k issues step k + BWDX_RING - 2, whose slot's
 // last reader, step k - 2, finished at barrier k - 1. The design never aborts (it has no bounded
 // wait), so the wave joins every barrier, -1 .. T.
 __device__ __forceinline__ void biol_wave(const BwdxDma& c, char* ring) {
-  constexpr int NS = BWDX_RING, NE = BWDX_NE;
+  constexpr int NS = BWDX_RING, NE = BWDL_NE;
   static_assert(NS == 4, "the wait below counts the loads of the two intervals after a step's");
+  static_assert((NS - 2) * NE < 64, "vmcnt counts at most 63 operations");
   if (c.T == 0) {
     block_barrier();
     block_barrier();
@@ -842,7 +848,7 @@ __device__ __forceinline__ void biol_wave(const BwdxDma& c, char* ring) {
   const long long step_bytes = c.in_step * 4;
   auto issue = [&](int s) {
     const int sc = min(max(s, 0), c.T - 1);
-    char* slot = ring + (s & (NS - 1)) * BWDX_SLOT;
+    char* slot = ring + (s & (NS - 1)) * BWDL_SLOT;
 #pragma unroll
     for (int e = 0; e < NE; ++e)
       __builtin_amdgcn_global_load_lds((glb_void_t*)(c.rec + goff[e] + sc * step_bytes), (lds_void_t*)(slot + 1024 * e),
@@ -858,7 +864,7 @@ __device__ __forceinline__ void biol_wave(const BwdxDma& c, char* ring) {
 }
 
 // Largest batch rows per group: a step's records (D units a row) fill at most one ring slot.
-__host__ __device__ constexpr int fused_bwdl_max_br(int D) { return BWDX_SLOT / (D * BWD_REC * 4); }
+__host__ __device__ constexpr int fused_bwdl_max_br(int D) { return BWDL_SLOT / (D * BWD_REC * 4); }
 
 template <int CELL, int KT>
 __global__ void __launch_bounds__((BWDL_NCW + 1) * 64, 1) fused_bwd_local_kernel(FusedBwdArgs a) {
@@ -925,7 +931,7 @@ __global__ void __launch_bounds__((BWDL_NCW + 1) * 64, 1) fused_bwd_local_kernel
       const f32x4_t pre = acc0 + acc1;
       if (colv) {
         // ---- the linear step for the lane's four units; da into this step's parity, (dh, dc) out
-        const float* rr = reinterpret_cast<const float*>(ring + (s & (BWDX_RING - 1)) * BWDX_SLOT) + col * D * BWD_REC +
+        const float* rr = reinterpret_cast<const float*>(ring + (s & (BWDX_RING - 1)) * BWDL_SLOT) + col * D * BWD_REC +
                           gu * BWD_REC;
         // (dh, dc) straight to memory: these waves never wait on memory
         float* ro = a.dstate + (long long)s * a.Bs * N * D * 2 + ((long long)(b0 + col) * N + n) * D * 2 + gu * 2;

@@ -29,6 +29,7 @@ struct ProjArgs {
   float* C;
   long long ldc;
   long long a_z, b_z, c_z;  // element offsets of A, Bt and C per blockIdx.y (independent parts)
+  long long a_h, b_h, c_h;  // and per blockIdx.z (heads; a second batch dimension)
   int nt;  // 1: C by streaming stores (read later by a streaming kernel, not by a recurrence)
 };
 
@@ -44,11 +45,14 @@ constexpr int PJ_DIES = 8;  // accelerator dies (XCDs) of an MI355X
 constexpr int PJ_LS = PJ_BK + 8;  // LDS row stride (bf16): 80 bytes, spreads a fragment's rows over the banks
 
 // dst[j][k] = src[k][j] for k < K, j < Nc (src row stride lds, dst row stride ldd), 32 x 32 tiles
-// through LDS. Grid (ceil(Nc/32), min(ceil(K/32), 65535)); the y tiles repeat by gridDim.y.
+// through LDS. Grid (ceil(Nc/32), min(ceil(K/32), 65535), matrices); the y tiles repeat by
+// gridDim.y; matrix z starts src_z and dst_z elements further.
 template <typename E>
 __global__ void __launch_bounds__(256) transpose_kernel(const E* src, long long lds, int K, int Nc, E* dst,
-                                                        long long ldd) {
+                                                        long long ldd, long long src_z, long long dst_z) {
   __shared__ E s[32][33];
+  src += blockIdx.z * src_z;
+  dst += blockIdx.z * dst_z;
   const int n0 = blockIdx.x * 32;
   const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;  // 32 x 8
   for (int kb = blockIdx.y; kb * 32 < K; kb += gridDim.y) {
@@ -71,10 +75,14 @@ __global__ void __launch_bounds__(256) transpose_kernel(const E* src, long long 
 // dst[j][k] = src[k][j] for 16-bit elements on 64 x 64 tiles: every global access is 4
 // consecutive elements (8 bytes) of a row, so a wave moves 512 contiguous-in-rows bytes per
 // instruction instead of 128. Needs src, dst 8-byte aligned and lds, ldd multiples of 4; tiles
-// that cross the K or Nc edge move element by element. Grid (ceil(Nc/64), min(ceil(K/64), 65535)).
+// that cross the K or Nc edge move element by element. Grid (ceil(Nc/64), min(ceil(K/64), 65535),
+// matrices), matrix z starting src_z and dst_z elements further (multiples of 4).
 __global__ void __launch_bounds__(256) transpose_b16_kernel(const uint16_t* src, long long lds, int K, int Nc,
-                                                            uint16_t* dst, long long ldd) {
+                                                            uint16_t* dst, long long ldd, long long src_z,
+                                                            long long dst_z) {
   __shared__ __attribute__((aligned(16))) uint16_t s[64][68];
+  src += blockIdx.z * src_z;
+  dst += blockIdx.z * dst_z;
   const int n0 = blockIdx.x * 64;
   const int t = threadIdx.x, r = t >> 4, c4 = (t & 15) * 4;  // row r + 16 i, 4 elements from c4
   for (int kb = blockIdx.y; kb * 64 < K; kb += gridDim.y) {
@@ -198,10 +206,10 @@ __global__ void __launch_bounds__(256, 2) proj_gemm_kernel(ProjArgs p) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int col = lane & 15, quad = lane >> 4;
   const int wm = wave >> 1, wn = wave & 1;  // wave tile: rows wm*128 .., columns wn*64 ..
-  if (blockIdx.y) {  // part z of a batch of independent products
-    p.A = reinterpret_cast<const char*>(p.A) + blockIdx.y * p.a_z * (AF32 ? 4 : 2);
-    p.Bt += blockIdx.y * p.b_z;
-    p.C += blockIdx.y * p.c_z;
+  if (blockIdx.y || blockIdx.z) {  // part y of head z of a batch of independent products
+    p.A = reinterpret_cast<const char*>(p.A) + (blockIdx.y * p.a_z + blockIdx.z * p.a_h) * (AF32 ? 4 : 2);
+    p.Bt += blockIdx.y * p.b_z + blockIdx.z * p.b_h;
+    p.C += blockIdx.y * p.c_z + blockIdx.z * p.c_h;
   }
   // Die-aware tile order. Workgroups are dealt to the 8 dies round-robin by index, so the die of
   // workgroup L is L % 8. Tiles are numbered row-major (M tile, then N tile) and each die takes a
@@ -304,10 +312,10 @@ __global__ void __launch_bounds__(256, 2) proj_gemm_dma_kernel(ProjArgs p) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int col = lane & 15, quad = lane >> 4;
   const int wm = wave >> 1, wn = wave & 1;
-  if (blockIdx.y) {
-    p.A = reinterpret_cast<const char*>(p.A) + blockIdx.y * p.a_z * 2;
-    p.Bt += blockIdx.y * p.b_z;
-    p.C += blockIdx.y * p.c_z;
+  if (blockIdx.y || blockIdx.z) {
+    p.A = reinterpret_cast<const char*>(p.A) + (blockIdx.y * p.a_z + blockIdx.z * p.a_h) * 2;
+    p.Bt += blockIdx.y * p.b_z + blockIdx.z * p.b_h;
+    p.C += blockIdx.y * p.c_z + blockIdx.z * p.c_h;
   }
   const int ntn = (p.Nc + PJ_BN - 1) / PJ_BN;
   const int L = blockIdx.x, G = gridDim.x;

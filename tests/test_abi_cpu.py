@@ -316,9 +316,10 @@ def test_fused_bwd_planner(lib):
     s = hw.frnn_bwd_plan_str(D(B=16, T=1024, N=1, Dm=1024, cell=2), 1)
     assert "design=die-local-partials" in s and "W=32 " in s and "NCW=8 KS=1 MTW=8 KTW=3 KTL=1 " in s, s
     assert "KTL" not in hw.frnn_bwd_plan_str(D(B=16, T=1024, N=1, Dm=768), 1)
-    # twelve 64-unit Elman heads of 64 rows: the single-workgroup design
+    # twelve 64-unit Elman heads of 64 rows: the single-workgroup design, four rows a workgroup (a
+    # step's records of four 64-unit rows fill one 8 KB ring slot), all 192 groups in one launch
     s = hw.frnn_bwd_plan_str(D(B=64, T=8, N=12, Dm=64, cell=1), 1)
-    assert "design=workgroup-local " in s and "BR=2 " in s
+    assert "design=workgroup-local " in s and "BR=4 " in s and "groups=192 " in s and "chunks=1 " in s, s
     # the partial-sum design needs more launches than the da exchange there
     old = os.environ.get("FRNN_FUSED_BWD_PX")
     try:

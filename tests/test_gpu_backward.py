@@ -301,11 +301,15 @@ _CH_LSTM = fi.HeadwiseWorkload("bwd_lstm_chunks_B40", "lstm", torch.bfloat16, B=
                                s0_var=1.0)
 _CH_ELMAN = fi.HeadwiseWorkload("bwd_elman_chunks_B64_N12", "elman", torch.bfloat16, B=64, T=16, N=12, D=64, seed=253,
                                 s0_var=1.0)
+# the single-workgroup design takes four 64-unit rows a workgroup: 128 rows of twelve heads need two
+# launches of at most 21 groups of rows a head
+_CH_ELMAN_L = fi.HeadwiseWorkload("bwd_elman_chunks_B128_N12", "elman", torch.bfloat16, B=128, T=16, N=12, D=64,
+                                  seed=254, s0_var=1.0)
 
 
 @pytest.mark.parametrize("w,px,chunks", [
     (_CH_GRU, 0, 3), (_CH_LSTM, 0, 3), (_CH_ELMAN, 0, 2),
-    (_CH_GRU, 1, 2), (_CH_LSTM, 1, 2), (_CH_ELMAN, 1, 4), (_CH_ELMAN, 2, 2),
+    (_CH_GRU, 1, 2), (_CH_LSTM, 1, 2), (_CH_ELMAN, 1, 4), (_CH_ELMAN_L, 2, 2),
 ], ids=lambda x: getattr(x, "name", str(x)))
 def test_bwd_fused_chunks(w, px, chunks):
     """A batch whose groups exceed one launch runs the fused serial part in chunks of rows (every
