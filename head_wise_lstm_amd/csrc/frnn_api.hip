@@ -971,7 +971,17 @@ int run_fused_bwd(int cell, const BwdArgs& a, const FusedBwdPlan& fp, const DevI
   float* rec = reinterpret_cast<float*>(base + L.rec);
   float* dstate = reinterpret_cast<float*>(base + L.dstate);
   const bool f32 = a.f32 != 0;
-  launch_bwd_cell_kernel(kBwdRecord, cell, f32, a.wx_f32, dim3(pgrid), dim3(256), st, a, 0, rec);
+  // the single-workgroup design keeps an Elman cell's records compact (two coefficients) and
+  // stores its dWx and da itself
+  const bool compact = fp.local && cell == FRNN_CELL_ELMAN;
+  const int rec_f = compact ? 2 : BWD_REC;
+  if (compact) {
+    if (f32) hipLaunchKernelGGL((bwd_record_kernel<CELL_ELMAN, true, true, 2>), dim3(pgrid), dim3(256), 0, st, a, rec);
+    else if (a.wx_f32) hipLaunchKernelGGL((bwd_record_kernel<CELL_ELMAN, false, true, 2>), dim3(pgrid), dim3(256), 0, st, a, rec);
+    else hipLaunchKernelGGL((bwd_record_kernel<CELL_ELMAN, false, false, 2>), dim3(pgrid), dim3(256), 0, st, a, rec);
+  } else {
+    launch_bwd_cell_kernel(kBwdRecord, cell, f32, a.wx_f32, dim3(pgrid), dim3(256), st, a, 0, rec);
+  }
   const void* fn = reinterpret_cast<const void*>(fp.fn);
   // the single-workgroup design multiplies on the fp32 MFMA: bf16 R widened into fp32 fragments
   const void* rpk_local = a.rpk;
@@ -991,8 +1001,11 @@ int run_fused_bwd(int cell, const BwdArgs& a, const FusedBwdPlan& fp, const DevI
       f.B = Bch; f.Bs = a.B; f.T = a.T; f.N = a.N; f.D = a.D;
       f.BR = fp.BR; f.groups = groups; f.W = 1; f.n_xcd = 1;
       f.rpk = rpk_local;
-      f.rec = rec + (size_t)b0 * a.N * a.D * BWD_REC;
+      f.rec = rec + (size_t)b0 * a.N * a.D * rec_f;
       f.dstate = dstate + (size_t)b0 * a.N * a.D * 2;
+      f.bbase = b0;
+      f.dWx = a.dWx; f.wx_sb = a.wx_sb; f.wx_st = a.wx_st;
+      f.da = a.da; f.Kp = a.Kp; f.f32op = a.f32;
       f.err = reinterpret_cast<int*>(base - kErrBytes);
       f.stall_step = -1;
       void* args[] = {&f};
@@ -1020,7 +1033,10 @@ int run_fused_bwd(int cell, const BwdArgs& a, const FusedBwdPlan& fp, const DevI
     const int lrc = launch_resident(fn, grid, fused_threads(fp.ncw), fp.lds, args, di.cus, st);
     if (lrc != FRNN_OK) return lrc;
   }
-  if (f32) {
+  if (compact) {
+    // the serial kernel stored dWx and da; an Elman cell carries nothing to the step before, and
+    // the carries are zero from the start
+  } else if (f32) {
     if (cell == FRNN_CELL_LSTM) hipLaunchKernelGGL((bwd_post_kernel<CELL_LSTM, true>), dim3(pgrid), dim3(256), 0, st, a, rec, dstate);
     else if (cell == FRNN_CELL_GRU) hipLaunchKernelGGL((bwd_post_kernel<CELL_GRU, true>), dim3(pgrid), dim3(256), 0, st, a, rec, dstate);
     else hipLaunchKernelGGL((bwd_post_kernel<CELL_ELMAN, true>), dim3(pgrid), dim3(256), 0, st, a, rec, dstate);

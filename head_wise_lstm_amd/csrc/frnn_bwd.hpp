@@ -189,9 +189,11 @@ __device__ __forceinline__ void bwd_coeffs(const BwdArgs& a, int t, int b, int n
 }
 
 // Coefficient records of every step, for the fused serial part: one thread per (t, b, n, unit);
-// record index s = T-1-t.
-template <int CELL, bool F32, bool WXF32>
+// record index s = T-1-t. REC floats a record: 8 (both f32x4), or 2 for an Elman cell, whose
+// record is r0's first two (the single-workgroup design's compact records).
+template <int CELL, bool F32, bool WXF32, int REC = 8>
 __global__ void __launch_bounds__(256) bwd_record_kernel(BwdArgs a, float* rec) {
+  static_assert(REC == 8 || (REC == 2 && CELL == CELL_ELMAN), "compact records hold an Elman cell's two coefficients");
   const long long total = (long long)a.T * a.B * a.N * a.D;
   const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
   if (idx >= total) return;
@@ -204,9 +206,14 @@ __global__ void __launch_bounds__(256) bwd_record_kernel(BwdArgs a, float* rec) 
   f32x4_t r0, r1;
   bwd_coeffs<CELL, F32, WXF32>(a, t, b, n, u, r0, r1);
   const long long s = (long long)(a.T - 1 - t);
-  f32x4_t* out = reinterpret_cast<f32x4_t*>(rec + ((((s * a.B + b) * a.N + n) * a.D + u) * 8));
-  out[0] = r0;
-  out[1] = r1;
+  const long long ri = ((s * a.B + b) * a.N + n) * a.D + u;
+  if constexpr (REC == 2) {
+    reinterpret_cast<float2*>(rec)[ri] = make_float2(r0[0], r0[1]);
+  } else {
+    f32x4_t* out = reinterpret_cast<f32x4_t*>(rec + ri * 8);
+    out[0] = r0;
+    out[1] = r1;
+  }
 }
 
 // The gradients of step t for one (b, n, unit) from its coefficients and the gradients reaching

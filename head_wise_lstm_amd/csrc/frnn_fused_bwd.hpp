@@ -50,6 +50,13 @@ struct FusedBwdArgs {
   int* err;
   long long timeout_ticks;
   int stall_step;    // a failure-handling test's hook: this step publishes a stale tag (-1: none)
+  // the single-workgroup design on an Elman cell stores dWx and the dR operand da itself (as
+  // bwd_apply lays them out) instead of dh: row b of this launch is batch row bbase + b
+  int bbase;
+  float* dWx;        // [B,T,N,D] slices (or null)
+  long long wx_sb, wx_st;
+  void* da;          // [N][Kp][D] dR operand (fp32 where f32op, else bf16)
+  int Kp, f32op;
 };
 
 struct FusedBwdLds {
@@ -809,6 +816,10 @@ __host__ __device__ constexpr int fused_bwdl_row(int G, int D) { return G * D + 
 // batch rows a workgroup.
 constexpr int BWDL_NE = 8;
 constexpr int BWDL_SLOT = 64 * 16 * BWDL_NE;
+// Floats a record in this design: an Elman cell's two coefficients alone (compact records:
+// bwd_record_kernel with REC = 2), else BWD_REC. With an Elman cell the design also stores the
+// step's dWx and da itself, so no post kernel runs.
+__host__ __device__ constexpr int bwdl_rec(int cell) { return cell == CELL_ELMAN ? 2 : BWD_REC; }
 
 struct FusedBwdlLds {
   int da, rin, total;
@@ -825,12 +836,14 @@ __host__ __device__ inline FusedBwdlLds fused_bwdl_lds(int G, int D, int BR) {
 }
 
 // The single-workgroup design's I/O wave: the partial-sum design's load-only ring (see biox_wave)
-// with BWDL_NE loads per lane and step, on this design's schedule. The compute waves apply step s between barriers s and s + 1, so the
+// with NE loads per lane and step of records of REC floats, on this design's schedule. The compute waves apply step s between barriers s and s + 1, so the
 // records of step s land by barrier s, and interval k issues step k + BWDX_RING - 2, whose slot's
 // last reader, step k - 2, finished at barrier k - 1. The design never aborts (it has no bounded
 // wait), so the wave joins every barrier, -1 .. T.
+template <int NE, int REC>
 __device__ __forceinline__ void biol_wave(const BwdxDma& c, char* ring) {
-  constexpr int NS = BWDX_RING, NE = BWDL_NE;
+  constexpr int NS = BWDX_RING;
+  static_assert(NE * 64 * 16 <= BWDL_SLOT, "a step's loads fill at most one slot");
   static_assert(NS == 4, "the wait below counts the loads of the two intervals after a step's");
   static_assert((NS - 2) * NE < 64, "vmcnt counts at most 63 operations");
   if (c.T == 0) {
@@ -838,7 +851,7 @@ __device__ __forceinline__ void biol_wave(const BwdxDma& c, char* ring) {
     block_barrier();
     return;
   }
-  const int cpr = c.U * BWD_REC / 4;  // 16-byte chunks per row
+  const int cpr = c.U * REC / 4;  // 16-byte chunks per row
   long long goff[NE];
 #pragma unroll
   for (int e = 0; e < NE; ++e) {
@@ -863,13 +876,16 @@ __device__ __forceinline__ void biol_wave(const BwdxDma& c, char* ring) {
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 }
 
-// Largest batch rows per group: a step's records (D units a row) fill at most one ring slot.
+// Largest batch rows per group: a step's records (D units a row, BWD_REC floats a unit) fill at most
+// one ring slot; compact records then take a quarter of the slot's loads.
 __host__ __device__ constexpr int fused_bwdl_max_br(int D) { return BWDL_SLOT / (D * BWD_REC * 4); }
 
 template <int CELL, int KT>
 __global__ void __launch_bounds__((BWDL_NCW + 1) * 64, 1) fused_bwd_local_kernel(FusedBwdArgs a) {
   constexpr int G = cell_gates(CELL);
   constexpr int NCW = BWDL_NCW;
+  constexpr int REC = bwdl_rec(CELL);  // floats a record
+  constexpr bool DIRECT = CELL == CELL_ELMAN;  // dWx and da out, instead of (dh, dc)
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -892,14 +908,14 @@ __global__ void __launch_bounds__((BWDL_NCW + 1) * 64, 1) fused_bwd_local_kernel
   if (wave == NCW) {
     BwdxDma c;
     c.rec = reinterpret_cast<const char*>(a.rec);
-    c.in_row = (long long)N * D * BWD_REC;
-    c.in_step = (long long)a.Bs * N * D * BWD_REC;
-    c.in_base = ((long long)b0 * N + n) * D * BWD_REC;
+    c.in_row = (long long)N * D * REC;
+    c.in_step = (long long)a.Bs * N * D * REC;
+    c.in_base = ((long long)b0 * N + n) * D * REC;
     c.nvalid = nvalid;
     c.U = D;
     c.T = T;
     c.lane = lane;
-    biol_wave(c, ring);
+    biol_wave<BWDL_NE * REC / BWD_REC, REC>(c, ring);
     return;
   }
 
@@ -931,15 +947,25 @@ __global__ void __launch_bounds__((BWDL_NCW + 1) * 64, 1) fused_bwd_local_kernel
       const f32x4_t pre = acc0 + acc1;
       if (colv) {
         // ---- the linear step for the lane's four units; da into this step's parity, (dh, dc) out
-        const float* rr = reinterpret_cast<const float*>(ring + (s & (BWDX_RING - 1)) * BWDL_SLOT) + col * D * BWD_REC +
-                          gu * BWD_REC;
-        // (dh, dc) straight to memory: these waves never wait on memory
-        float* ro = a.dstate + (long long)s * a.Bs * N * D * 2 + ((long long)(b0 + col) * N + n) * D * 2 + gu * 2;
+        const float* rr = reinterpret_cast<const float*>(ring + (s & (BWDX_RING - 1)) * BWDL_SLOT) + col * D * REC +
+                          gu * REC;
+        // (dh, dc), or dWx and da, straight to memory: these waves never wait on memory
         float da[G][4], dh[4], dc[4];
+        f32x4_t rc[2];  // compact records: the four units' (r0[0], r0[1]) pairs
+        if constexpr (REC == 2) {
+          rc[0] = *reinterpret_cast<const f32x4_t*>(rr);
+          rc[1] = *reinterpret_cast<const f32x4_t*>(rr + 4);
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const f32x4_t r0 = *reinterpret_cast<const f32x4_t*>(rr + i * BWD_REC);
-          const f32x4_t r1 = *reinterpret_cast<const f32x4_t*>(rr + i * BWD_REC + 4);
+          f32x4_t r0, r1;
+          if constexpr (REC == 2) {
+            r0 = f32x4_t{rc[i >> 1][2 * (i & 1)], rc[i >> 1][2 * (i & 1) + 1], 0.0f, 0.0f};
+            r1 = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+          } else {
+            r0 = *reinterpret_cast<const f32x4_t*>(rr + i * REC);
+            r1 = *reinterpret_cast<const f32x4_t*>(rr + i * REC + 4);
+          }
           if constexpr (CELL == CELL_LSTM) {
             dh[i] = pre[i] + r1[2];
             dc[i] = cr[i] + r1[3] + dh[i] * r0[0];
@@ -965,8 +991,27 @@ __global__ void __launch_bounds__((BWDL_NCW + 1) * 64, 1) fused_bwd_local_kernel
 #pragma unroll
         for (int g = 0; g < G; ++g)
           *reinterpret_cast<f32x4_t*>(dw + g * D) = f32x4_t{da[g][0], da[g][1], da[g][2], da[g][3]};
-        *reinterpret_cast<f32x4_t*>(ro) = f32x4_t{dh[0], dc[0], dh[1], dc[1]};
-        *reinterpret_cast<f32x4_t*>(ro + 4) = f32x4_t{dh[2], dc[2], dh[3], dc[3]};
+        if constexpr (DIRECT) {
+          const long long bg = (long long)a.bbase + b0 + col, t = T - 1 - s;
+          if (a.dWx) {
+            float* dw = a.dWx + bg * a.wx_sb + t * a.wx_st + (long long)n * D + gu;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dw[i] = da[0][i];
+          }
+          const long long drow = ((long long)n * a.Kp + t * a.Bs + bg) * D + gu;
+          if (a.f32op) {
+            *reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(a.da) + drow) = f32x4_t{da[0][0], da[0][1], da[0][2], da[0][3]};
+          } else {
+            uint2 w;
+            w.x = (uint32_t)f2bf(da[0][0]) | ((uint32_t)f2bf(da[0][1]) << 16);
+            w.y = (uint32_t)f2bf(da[0][2]) | ((uint32_t)f2bf(da[0][3]) << 16);
+            *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.da) + drow) = w;
+          }
+        } else {
+          float* ro = a.dstate + (long long)s * a.Bs * N * D * 2 + ((long long)(b0 + col) * N + n) * D * 2 + gu * 2;
+          *reinterpret_cast<f32x4_t*>(ro) = f32x4_t{dh[0], dc[0], dh[1], dc[1]};
+          *reinterpret_cast<f32x4_t*>(ro + 4) = f32x4_t{dh[2], dc[2], dh[3], dc[3]};
+        }
       }
     }
   }

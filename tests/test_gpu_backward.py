@@ -116,6 +116,10 @@ SMALL = [
     fi.HeadwiseWorkload("bwd_elman_f32_D64", "elman", torch.float32, B=4, T=9, N=3, D=64, seed=209, s0_var=1.0),
     fi.HeadwiseWorkload("bwd_gru_f32_D32", "gru", torch.float32, B=3, T=11, N=2, D=32, seed=210, s0_var=1.0),
     fi.HeadwiseWorkload("bwd_lstm_bf16_T1", "lstm", torch.bfloat16, B=1, T=1, N=1, D=64, seed=211, s0_var=1.0),
+    # 32-unit Elman heads on the single-workgroup design: eight rows a workgroup (compact records),
+    # the second group of each head ragged (three rows)
+    fi.HeadwiseWorkload("bwd_elman_bf16_D32", "elman", torch.bfloat16, B=11, T=10, N=2, D=32, seed=212, s0_var=1.0),
+    fi.HeadwiseWorkload("bwd_elman_f32_D32", "elman", torch.float32, B=11, T=7, N=2, D=32, seed=213, s0_var=1.0),
 ]
 
 
@@ -166,12 +170,13 @@ def test_bwd_alternating_each_form(w, one):
 # Every fused backward design on the small bf16 cases, pinned with FRNN_FUSED_BWD_PX: the
 # partial-sum design (the planner's choice where it has one), the da-exchange design, and, for
 # heads of at most 64 units, the single-workgroup design on fp32 fragments of R (the planner's
-# choice for heads neither die-local design tiles).
+# choice for heads neither die-local design tiles). Heads of 32 units have only the last.
 _DESIGN_NAME = {1: "die-local-partials", 0: "design=die-local ", 2: "workgroup-local"}
 
 
 @pytest.mark.parametrize("w,px", [(x, px) for x in SMALL if x.dtype == torch.bfloat16 for px in (1, 0, 2)
-                                  if px != 2 or x.D <= 64], ids=lambda x: f"px{x}" if isinstance(x, int) else x.name)
+                                  if (px != 2 or x.D <= 64) and (px == 2 or x.D > 32)],
+                         ids=lambda x: f"px{x}" if isinstance(x, int) else x.name)
 def test_bwd_small_each_design(w, px):
     with _env({"FRNN_FUSED_BWD_PX": px}):
         plan = _fused_plan_or_skip(w)
