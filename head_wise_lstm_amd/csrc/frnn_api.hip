@@ -975,7 +975,15 @@ int run_fused_bwd(int cell, const BwdArgs& a, const FusedBwdPlan& fp, const DevI
   // stores its dWx and da itself
   const bool compact = fp.local && cell == FRNN_CELL_ELMAN;
   const int rec_f = compact ? 2 : BWD_REC;
-  if (compact) {
+  // ... or, where the states and their gradient sit in 16-byte aligned rows, none at all: its I/O
+  // wave loads h and ds_h themselves
+  auto al16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
+  const bool raw = compact && al16(a.st_h) && (!a.ds_h || al16(a.ds_h)) && (!a.dl_h || al16(a.dl_h)) &&
+                   a.st_sb % 4 == 0 && a.st_st % 4 == 0 && a.last_sb % 4 == 0 && a.D % 4 == 0 &&
+                   env_int("FRNN_BWD_ELMAN_RAW", 1) != 0;
+  if (raw) {
+    // no records
+  } else if (compact) {
     if (f32) hipLaunchKernelGGL((bwd_record_kernel<CELL_ELMAN, true, true, 2>), dim3(pgrid), dim3(256), 0, st, a, rec);
     else if (a.wx_f32) hipLaunchKernelGGL((bwd_record_kernel<CELL_ELMAN, false, true, 2>), dim3(pgrid), dim3(256), 0, st, a, rec);
     else hipLaunchKernelGGL((bwd_record_kernel<CELL_ELMAN, false, false, 2>), dim3(pgrid), dim3(256), 0, st, a, rec);
@@ -1006,6 +1014,9 @@ int run_fused_bwd(int cell, const BwdArgs& a, const FusedBwdPlan& fp, const DevI
       f.bbase = b0;
       f.dWx = a.dWx; f.wx_sb = a.wx_sb; f.wx_st = a.wx_st;
       f.da = a.da; f.Kp = a.Kp; f.f32op = a.f32;
+      f.raw = raw ? 1 : 0;
+      f.st_h = a.st_h; f.ds_h = a.ds_h; f.dl_h = a.dl_h; f.zeros = a.zeros;
+      f.st_sb = a.st_sb; f.st_st = a.st_st; f.last_sb = a.last_sb;
       f.err = reinterpret_cast<int*>(base - kErrBytes);
       f.stall_step = -1;
       void* args[] = {&f};

@@ -57,6 +57,16 @@ struct FusedBwdArgs {
   long long wx_sb, wx_st;
   void* da;          // [N][Kp][D] dR operand (fp32 where f32op, else bf16)
   int Kp, f32op;
+  // raw = 1: no records at all; the I/O wave loads each step's h and its state gradient ds_h
+  // straight from the forward's states and the caller's gradient (or the zero page), in rows of
+  // [h: D floats][ds_h: D floats], and the step's coefficients 1 - h^2 and ds_h (+ dl_h at the
+  // last time step) come from them (16-byte aligned rows and strides)
+  int raw;
+  const float* st_h;
+  const float* ds_h;  // (or null)
+  const float* dl_h;  // (or null)
+  const float* zeros; // 256 zero bytes
+  long long st_sb, st_st, last_sb;
 };
 
 struct FusedBwdLds {
@@ -876,6 +886,53 @@ __device__ __forceinline__ void biol_wave(const BwdxDma& c, char* ring) {
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 }
 
+// The raw-input form of the I/O wave above (an Elman cell's records replaced by their inputs): lane
+// chunk i = 64 e + lane is 16 bytes of row r = i / (D / 2), h where its chunk w < D / 4, else ds_h;
+// rows past the group's last load that row again. Step s reads time T - 1 - s.
+template <int NE>
+__device__ __forceinline__ void biol_raw_wave(const FusedBwdArgs& a, int n, int b0, int nvalid, int lane, char* ring) {
+  constexpr int NS = BWDX_RING;
+  static_assert(NE * 64 * 16 <= BWDL_SLOT, "a step's loads fill at most one slot");
+  const int T = a.T, D = a.D;
+  if (T == 0) {
+    block_barrier();
+    block_barrier();
+    return;
+  }
+  const int cpr = D / 2, hc = D / 4;  // 16-byte chunks a row, of them h's
+  const char* src[NE];
+  long long step[NE];  // bytes from one kernel step's source to the next (a step back in time)
+#pragma unroll
+  for (int e = 0; e < NE; ++e) {
+    const int i = lane + 64 * e, r = min(i / cpr, nvalid - 1), w = i % cpr;
+    const long long row = (long long)(a.bbase + b0 + r) * a.st_sb + (long long)(T - 1) * a.st_st + (long long)n * D;
+    if (w < hc) {
+      src[e] = reinterpret_cast<const char*>(a.st_h + row + 4 * w);
+      step[e] = -a.st_st * 4;
+    } else if (a.ds_h) {
+      src[e] = reinterpret_cast<const char*>(a.ds_h + row + 4 * (w - hc));
+      step[e] = -a.st_st * 4;
+    } else {
+      src[e] = reinterpret_cast<const char*>(a.zeros) + 16 * (w - hc);
+      step[e] = 0;
+    }
+  }
+  auto issue = [&](int s) {
+    const int sc = min(max(s, 0), T - 1);
+    char* slot = ring + (s & (NS - 1)) * BWDL_SLOT;
+#pragma unroll
+    for (int e = 0; e < NE; ++e)
+      __builtin_amdgcn_global_load_lds((glb_void_t*)(src[e] + sc * step[e]), (lds_void_t*)(slot + 1024 * e), 16, 0, 0);
+  };
+  issue(0);  // step 0, as interval -2 would issue it
+  for (int k = -1; k <= T; ++k) {
+    issue(k + NS - 2);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * NE));
+    __builtin_amdgcn_s_barrier();
+  }
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+}
+
 // Largest batch rows per group: a step's records (D units a row, BWD_REC floats a unit) fill at most
 // one ring slot; compact records then take a quarter of the slot's loads.
 __host__ __device__ constexpr int fused_bwdl_max_br(int D) { return BWDL_SLOT / (D * BWD_REC * 4); }
@@ -906,6 +963,10 @@ __global__ void __launch_bounds__((BWDL_NCW + 1) * 64, 1) fused_bwd_local_kernel
   for (int i = threadIdx.x; i < 2 * 16 * ROW; i += (NCW + 1) * 64) dab[i] = 0.0f;
 
   if (wave == NCW) {
+    if (DIRECT && a.raw) {
+      biol_raw_wave<BWDL_NE * REC / BWD_REC>(a, n, b0, nvalid, lane, ring);
+      return;
+    }
     BwdxDma c;
     c.rec = reinterpret_cast<const char*>(a.rec);
     c.in_row = (long long)N * D * REC;
@@ -931,6 +992,10 @@ __global__ void __launch_bounds__((BWDL_NCW + 1) * 64, 1) fused_bwd_local_kernel
   }
   const int gu = 16 * tt + 4 * quad;  // the lane's first unit
   float cr[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // LSTM dc, GRU dh carried to the next kernel step
+  // raw inputs: the gradient of last_states joins ds_h at the last time step (kernel step 0)
+  f32x4_t dl = {0.f, 0.f, 0.f, 0.f};
+  if (DIRECT && a.raw && a.dl_h && colv && tv)
+    dl = *reinterpret_cast<const f32x4_t*>(a.dl_h + (long long)(a.bbase + b0 + col) * a.last_sb + (long long)n * D + gu);
   block_barrier();  // barrier -1
 
   for (int s = 0; s < T; ++s) {
@@ -953,8 +1018,17 @@ __global__ void __launch_bounds__((BWDL_NCW + 1) * 64, 1) fused_bwd_local_kernel
         float da[G][4], dh[4], dc[4];
         f32x4_t rc[2];  // compact records: the four units' (r0[0], r0[1]) pairs
         if constexpr (REC == 2) {
-          rc[0] = *reinterpret_cast<const f32x4_t*>(rr);
-          rc[1] = *reinterpret_cast<const f32x4_t*>(rr + 4);
+          if (a.raw) {  // row col of the slot: h, then ds_h, D floats each
+            const float* rw = reinterpret_cast<const float*>(ring + (s & (BWDX_RING - 1)) * BWDL_SLOT) + col * 2 * D + gu;
+            const f32x4_t hv = *reinterpret_cast<const f32x4_t*>(rw);
+            f32x4_t dv = *reinterpret_cast<const f32x4_t*>(rw + D);
+            if (s == 0) dv += dl;
+            rc[0] = f32x4_t{1.0f - hv[0] * hv[0], dv[0], 1.0f - hv[1] * hv[1], dv[1]};
+            rc[1] = f32x4_t{1.0f - hv[2] * hv[2], dv[2], 1.0f - hv[3] * hv[3], dv[3]};
+          } else {
+            rc[0] = *reinterpret_cast<const f32x4_t*>(rr);
+            rc[1] = *reinterpret_cast<const f32x4_t*>(rr + 4);
+          }
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {

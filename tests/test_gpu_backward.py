@@ -325,6 +325,37 @@ def test_bwd_fused_chunks(w, px, chunks):
     run_bwd_case(w, "fused", env={"FRNN_FUSED_BWD_PX": px})
 
 
+_ELMAN_IN = fi.HeadwiseWorkload("bwd_elman_inputs_D64", "elman", torch.bfloat16, B=9, T=11, N=3, D=64, seed=214,
+                                s0_var=1.0)
+
+
+@pytest.mark.parametrize("raw", [1, 0])
+@pytest.mark.parametrize("given", ["both", "dstates", "dlast"])
+def test_bwd_elman_local_inputs(raw, given):
+    """The single-workgroup design on an Elman cell: its I/O wave loads h and ds_h themselves (raw)
+    or two-float records (FRNN_BWD_ELMAN_RAW=0); either gradient of the forward's outputs may be
+    absent (read as zeros), and dlast joins ds_h only at the last time step."""
+    hw = _hw()
+    w = _ELMAN_IN
+    assert "workgroup-local" in hw.frnn_bwd_plan_str(hw._desc(w.B, w.T, w.N, w.D, w.cell, w.dtype), "fused")
+    x = {k: (v.cuda() if v is not None else None) for k, v in fi.make_inputs(w).items()}
+    ct = fi.backward_cotangents(w)
+    ds = ct["dstates"] if given in ("both", "dstates") else None
+    dl = ct["dlast"] if given in ("both", "dlast") else None
+    _log(f"bwd case {w.name} raw={raw} given={given}")
+    st, _ = hw.frnn_fwd(x["Wx"], x["R"], x["b"], x["states0"], cell="elman")
+    with _env({"FRNN_BWD_ELMAN_RAW": raw}):
+        grads = hw.frnn_bwd(x["Wx"], x["R"], x["b"], x["states0"], st, None if ds is None else ds.cuda(),
+                            None if dl is None else dl.cuda(), cell="elman", path="fused")
+    torch.cuda.synchronize()
+    f = fi.to_f64
+    ref = oracle.headwise_bwd("elman", f(x["Wx"]), f(x["R"]), f(x["b"]), f(x["states0"]), f(ds), f(dl))
+    for name, gv, rv in zip(("dWx", "dR", "db", "dstates0"), grads, ref):
+        e = float(np.abs(gv.double().cpu().numpy() - rv).max())
+        scale = max(1.0, float(np.abs(rv).max()))
+        assert e <= TOL[w.dtype] * scale, f"{name}: {e} > {TOL[w.dtype]} * {scale}"
+
+
 def test_bwd_fused_matches_alternating():
     """The two backward paths agree closely (same operand roundings, different summation orders)."""
     hw = _hw()
