@@ -253,11 +253,13 @@ int raise_lds_limits() {
     }
   }
   for (const int D : {32, 64}) {
-    const fused_bwd_fn fns[3] = {fused_bwd_local_lstm(D), fused_bwd_local_gru(D), fused_bwd_local_elman(D)};
-    const int gates[3] = {4, 3, 1};
-    for (int c = 0; c < 3; ++c)
-      if (fns[c] && !raise(reinterpret_cast<const void*>(fns[c]), fused_bwdl_lds(gates[c], D, fused_bwdl_max_br(D)).total))
-        return FRNN_EHIP;
+    for (const bool bf : {false, true}) {
+      const fused_bwd_fn fns[3] = {fused_bwd_local_lstm(D, bf), fused_bwd_local_gru(D, bf), fused_bwd_local_elman(D, bf)};
+      const int gates[3] = {4, 3, 1};
+      for (int c = 0; c < 3; ++c)
+        if (fns[c] && !raise(reinterpret_cast<const void*>(fns[c]), fused_bwdl_lds(gates[c], D, fused_bwdl_max_br(D), bf).total))
+          return FRNN_EHIP;
+    }
   }
   return FRNN_OK;
 }
@@ -699,7 +701,7 @@ int bwd_dr_parts(int T, int B, int N, int D, int G) {
 }
 
 struct BwdLayout {
-  size_t zeros, hprev, hprevT, rt, rpk, rpk32, hr, da, daT, tmp, dhpart, carry, rec, dstate, xbuf, total;
+  size_t zeros, hprev, hprevT, rt, rpk, hr, da, daT, tmp, dhpart, carry, rec, dstate, xbuf, total;
 };
 
 // Fused backward design: groups of BR batch rows of one head on one die, W workgroups each owning
@@ -775,14 +777,16 @@ int plan_fused_bwd_da(int B, int N, int D, int cell, const DevInfo& di, FusedBwd
 
 // The single-workgroup design, a head and BR batch rows per workgroup (as many rows
 // as the I/O wave's limits allow), the batch in chunks when the groups exceed the CUs.
-int plan_fused_bwd_local(int B, int N, int D, int cell, const DevInfo& di, FusedBwdPlan* out) {
-  const fused_bwd_fn fn = cell == FRNN_CELL_LSTM ? fused_bwd_local_lstm(D)
-                          : cell == FRNN_CELL_GRU ? fused_bwd_local_gru(D)
-                                                  : fused_bwd_local_elman(D);
+// bf16 inputs multiply on the bf16 MFMA, fp32 ones on the fp32 MFMA.
+int plan_fused_bwd_local(int B, int N, int D, int cell, int f32, const DevInfo& di, FusedBwdPlan* out) {
+  const bool bf = !f32;
+  const fused_bwd_fn fn = cell == FRNN_CELL_LSTM ? fused_bwd_local_lstm(D, bf)
+                          : cell == FRNN_CELL_GRU ? fused_bwd_local_gru(D, bf)
+                                                  : fused_bwd_local_elman(D, bf);
   if (!fn || D / 16 > BWDL_NCW) return FRNN_EUNSUPPORTED;
   const int G = gates_of(cell);
   FusedBwdPlan fp;
-  fp.local = 1; fp.fn = fn; fp.W = 1; fp.ncw = BWDL_NCW; fp.ks = 1; fp.mtw = 1; fp.ktw = G * D / 4;
+  fp.local = 1; fp.fn = fn; fp.W = 1; fp.ncw = BWDL_NCW; fp.ks = 1; fp.mtw = 1; fp.ktw = G * D / (bf ? 32 : 4);
   fp.BR = std::max(1, std::min(B, fused_bwdl_max_br(D)));
   const long long bmax = (long long)fp.BR * std::max(1, di.cus / N);
   if (di.cus < N) return FRNN_EUNSUPPORTED;
@@ -791,24 +795,22 @@ int plan_fused_bwd_local(int B, int N, int D, int cell, const DevInfo& di, Fused
   fp.groups = N * ((fp.Bc + fp.BR - 1) / fp.BR);
   fp.grid = fp.groups;
   fp.n_xcd = 1; fp.U = D;
-  fp.lds = (size_t)fused_bwdl_lds(G, D, fp.BR).total;
+  fp.lds = (size_t)fused_bwdl_lds(G, D, fp.BR, bf).total;
   *out = fp;
   return FRNN_OK;
 }
 
-// fp32 operands take the single-workgroup design. bf16 operands take the partial-sum design where
-// it has a plan with no more launches than the da design, else the da design; heads that neither
-// die-local design tiles (a head of 32 units, say) run the single-workgroup design on fp32
-// fragments of R, and so do Elman heads of at most 64 units, where it measured 17-22 % faster than
-// either die-local design (B x N from 16 x 1 to 256 x 4, T = 512; LSTM and GRU heads of 64 units
-// keep the die-local designs, which measured up to 1.7x faster there). FRNN_FUSED_BWD_PX pins a
-// design: 1 the partial sums, 0 the da exchange, 2 the single workgroup.
+// Heads of at most 64 units take the single-workgroup design: on the bf16 MFMA it measured 1.2-2.6x
+// faster than the partial-sum design for every cell (B x N from 16 x 1 to 256 x 4, T = 512), and
+// fp32 operands have no other. Wider bf16 heads take the partial-sum design where it has a plan
+// with no more launches than the da design, else the da design. FRNN_FUSED_BWD_PX pins a design:
+// 1 the partial sums, 0 the da exchange, 2 the single workgroup.
 int plan_fused_bwd(int B, int N, int D, int cell, int f32, const DevInfo& di, FusedBwdPlan* out) {
-  if (f32) return plan_fused_bwd_local(B, N, D, cell, di, out);
+  if (f32) return plan_fused_bwd_local(B, N, D, cell, f32, di, out);
   const int design = env_int("FRNN_FUSED_BWD_PX", -1);
-  if (design == 2) return plan_fused_bwd_local(B, N, D, cell, di, out);
-  if (design < 0 && cell == FRNN_CELL_ELMAN && plan_fused_bwd_local(B, N, D, cell, di, out) == FRNN_OK) return FRNN_OK;
-  if (!di.periodic || D % 32 != 0) return design < 0 ? plan_fused_bwd_local(B, N, D, cell, di, out) : FRNN_EUNSUPPORTED;
+  if (design == 2) return plan_fused_bwd_local(B, N, D, cell, f32, di, out);
+  if (design < 0 && plan_fused_bwd_local(B, N, D, cell, f32, di, out) == FRNN_OK) return FRNN_OK;
+  if (!di.periodic || D % 32 != 0) return design < 0 ? plan_fused_bwd_local(B, N, D, cell, f32, di, out) : FRNN_EUNSUPPORTED;
   FusedBwdPlan px, da;
   const bool has_px = design != 0 && plan_fused_bwdx(B, N, D, cell, di, &px);
   const bool has_da = design != 1 && plan_fused_bwd_da(B, N, D, cell, di, &da) == FRNN_OK;
@@ -820,7 +822,7 @@ int plan_fused_bwd(int B, int N, int D, int cell, int f32, const DevInfo& di, Fu
     *out = da;
     return FRNN_OK;
   }
-  return design < 0 ? plan_fused_bwd_local(B, N, D, cell, di, out) : FRNN_EUNSUPPORTED;
+  return design < 0 ? plan_fused_bwd_local(B, N, D, cell, f32, di, out) : FRNN_EUNSUPPORTED;
 }
 
 int plan_fused_bwd_da(int B, int N, int D, int cell, const DevInfo& di, FusedBwdPlan* out) {
@@ -891,10 +893,8 @@ BwdLayout bwd_layout(int B, int T, int N, int D, int cell, int f32, int path) {
   L.tmp = q;    q += align256((size_t)P * N * (D + 1) * G * D * 4);
   L.dhpart = q; q += align256((size_t)BWD_KS * B * N * D * 4);
   L.carry = q;  q += align256((size_t)B * N * D * 4);
-  L.rec = L.dstate = L.xbuf = L.rpk32 = q;
+  L.rec = L.dstate = L.xbuf = q;
   if (path == FRNN_PATH_FUSED) {
-    // R as fp32 fragments for the single-workgroup design on bf16 inputs (heads of at most 64)
-    L.rpk32 = q;  q += (!f32 && D <= 64) ? align256((size_t)N * G * D * D * 4) : 0;
     L.rec = q;    q += align256((size_t)T * B * N * D * BWD_REC * 4);
     L.dstate = q; q += align256((size_t)T * B * N * D * 2 * 4);
     // exchange words: groups * BR <= N * (B + 3) rows (BR <= 4), two parities, G*D words a row
@@ -991,14 +991,8 @@ int run_fused_bwd(int cell, const BwdArgs& a, const FusedBwdPlan& fp, const DevI
     launch_bwd_cell_kernel(kBwdRecord, cell, f32, a.wx_f32, dim3(pgrid), dim3(256), st, a, 0, rec);
   }
   const void* fn = reinterpret_cast<const void*>(fp.fn);
-  // the single-workgroup design multiplies on the fp32 MFMA: bf16 R widened into fp32 fragments
+  // the single-workgroup design takes R's fragments in its inputs' type: the packed operand
   const void* rpk_local = a.rpk;
-  if (fp.local && !f32) {
-    const long long np = (long long)a.N * (a.D / 16) * (gates_of(cell) * a.D / 4) * 64;
-    hipLaunchKernelGGL(bwd_rpack_kernel, dim3((unsigned)std::min<long long>((np + 255) / 256, 65536)), dim3(256), 0, st, a,
-                       (void*)(base + L.rpk32), 1);
-    rpk_local = base + L.rpk32;
-  }
   // the batch in chunks of at most Bc rows, one launch each (rows never interact)
   for (int b0 = 0; b0 < a.B; b0 += fp.Bc) {
     const int Bch = std::min(fp.Bc, a.B - b0);
@@ -1161,7 +1155,7 @@ int run_backward(const BwdProblem& q, int path, const FusedBwdPlan& fbp, const D
   {
     const long long np = (long long)N * (D / 16) * (G * D / (f32 ? 4 : 32)) * 64;
     hipLaunchKernelGGL(bwd_rpack_kernel, dim3((unsigned)std::min<long long>((np + 255) / 256, 65536)), dim3(256), 0, st, a,
-                       (void*)(base + L.rpk), 0);
+                       (void*)(base + L.rpk));
   }
   const dim3 hgrid(D / 16, a.ks, ((B + 15) / 16) * N);
   if (path == FRNN_PATH_FUSED) {

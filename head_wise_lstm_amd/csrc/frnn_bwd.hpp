@@ -417,13 +417,10 @@ __global__ void __launch_bounds__(BWD_STEP_WAVES * 64) bwd_step_kernel(BwdArgs a
 
 // R in the dh kernel's A-fragment order: [N][D/16 row tiles][G*D/KW k-tiles][64 lanes] x (8 bf16
 // | 1 fp32); lane (m, quad) of tile (dt, kt) holds R[g][n][16 dt + m][e0 + 8 quad ..] (bf16) or
-// [e0 + quad] (fp32), with (g, e0) the k-tile's gate and first unit. With f32_out the fp32 order
-// (KW = 4) is written whatever R's type (bf16 values widen exactly): the single-workgroup fused
-// design multiplies on the fp32 MFMA for bf16 inputs too. One thread per lane entry.
-__global__ void __launch_bounds__(256) bwd_rpack_kernel(BwdArgs a, void* out, int f32_out) {
+// [e0 + quad] (fp32), with (g, e0) the k-tile's gate and first unit. One thread per lane entry.
+__global__ void __launch_bounds__(256) bwd_rpack_kernel(BwdArgs a, void* out) {
   const int G = cell_gates(a.cell), D = a.D;
-  const bool o32 = a.f32 || f32_out;
-  const int KW = o32 ? 4 : 32;
+  const int KW = a.f32 ? 4 : 32;
   const int KT = G * D / KW, DT = D / 16;
   const long long total = (long long)a.N * DT * KT * 64;
   for (long long idx = (long long)blockIdx.x * 256 + threadIdx.x; idx < total; idx += (long long)gridDim.x * 256) {
@@ -438,8 +435,6 @@ __global__ void __launch_bounds__(256) bwd_rpack_kernel(BwdArgs a, void* out, in
     const long long row = (long long)g * a.r_sg + (long long)n * a.r_sn + (long long)(dt * 16 + m) * a.r_sd + e0;
     if (a.f32) {
       reinterpret_cast<float*>(out)[idx] = reinterpret_cast<const float*>(a.R)[row + quad];
-    } else if (o32) {
-      reinterpret_cast<float*>(out)[idx] = bf2f(reinterpret_cast<const uint16_t*>(a.R)[row + quad]);
     } else {
       reinterpret_cast<u32x4_t*>(out)[idx] =
           *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const uint16_t*>(a.R) + row + 8 * quad);

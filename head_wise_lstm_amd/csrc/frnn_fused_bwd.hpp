@@ -810,17 +810,22 @@ __global__ void __launch_bounds__((NCW + 1) * 64, 1) fused_bwdx_kernel(FusedBwdA
 
 namespace frnn {
 
-// ============================================================================ single-workgroup fp32 design
-// fp32 operands for heads of at most 64 units: a whole head (and a block of BR batch rows) per
-// workgroup, so the step's da stays in LDS (two parities) as the next step's B operand: no
-// exchange, no bounded wait. Each compute wave owns one 16-row tile of R's rows d, resident in
-// VGPRs, with k = (g, e) over G*D in the fp32 MFMA's k-tiles of four (v_mfma_f32_16x16x4_f32, A = R
-// packed by bwd_rpack_kernel, B = da^T). Lane l of the result holds dh_R of units 4*(l/16)..+3 of
-// its tile for batch column l%16, as in the die-local design, and applies the same linear step.
-// The I/O wave streams the records into an LDS ring as the partial-sum design's does, and the
-// lanes that apply a step store its (dh, dc) (one barrier per step).
+// ============================================================================ single-workgroup design
+// Heads of at most 64 units: a whole head (and a block of BR batch rows) per workgroup, so the
+// step's da stays in LDS (two parities) as the next step's B operand: no exchange, no bounded
+// wait. Each compute wave owns one 16-row tile of R's rows d, resident in VGPRs, with k = (g, e)
+// over G*D, A = R packed by bwd_rpack_kernel and B = da^T:
+//   * fp32 inputs (BF = false): the fp32 MFMA's k-tiles of four (v_mfma_f32_16x16x4_f32), da
+//     kept in fp32;
+//   * bf16 inputs (BF = true): the bf16 MFMA's k-tiles of 32 (v_mfma_f32_16x16x32_bf16), da
+//     rounded to bf16 as the die-local designs' operand is (an eighth of the MFMAs).
+// Lane l of the result holds dh_R of units 4*(l/16)..+3 of its tile for batch column l%16, as in
+// the die-local design, and applies the same linear step. The I/O wave streams the records into
+// an LDS ring as the partial-sum design's does, and the lanes that apply a step store its (dh, dc)
+// (one barrier per step).
 constexpr int BWDL_NCW = 4;
-__host__ __device__ constexpr int fused_bwdl_row(int G, int D) { return G * D + 4; }  // floats per da row
+// da row of the LDS stage: floats (fp32), or bf16 elements padded by 16 bytes (bf16)
+__host__ __device__ constexpr int fused_bwdl_row(int G, int D, bool bf = false) { return bf ? G * D + 8 : G * D + 4; }
 // The design's record ring: BWDX_RING slots of BWDL_SLOT bytes, BWDL_NE 16-byte LDS-direct loads
 // per I/O lane and step; twice the partial-sum design's slot, so that a 64-unit head takes four
 // batch rows a workgroup.
@@ -836,17 +841,18 @@ struct FusedBwdlLds {
 };
 
 // A group's records of one step fit one slot of the record ring.
-__host__ __device__ inline FusedBwdlLds fused_bwdl_lds(int G, int D, int BR) {
+__host__ __device__ inline FusedBwdlLds fused_bwdl_lds(int G, int D, int BR, bool bf = false) {
   FusedBwdlLds L;
   L.da = 0;
-  L.rin = 2 * 16 * fused_bwdl_row(G, D) * 4;  // a multiple of 16 bytes, as the ring's loads need
+  L.rin = 2 * 16 * fused_bwdl_row(G, D, bf) * (bf ? 2 : 4);  // a multiple of 16 bytes, as the ring's loads need
   L.total = L.rin + BWDX_RING * BWDL_SLOT;
   (void)BR;
   return L;
 }
 
 // The single-workgroup design's I/O wave: the partial-sum design's load-only ring (see biox_wave)
-// with NE loads per lane and step of records of REC floats, on this design's schedule. The compute waves apply step s between barriers s and s + 1, so the
+// with NE loads per lane and step of records of REC floats, on this design's schedule. The
+// compute waves apply step s between barriers s and s + 1, so the
 // records of step s land by barrier s, and interval k issues step k + BWDX_RING - 2, whose slot's
 // last reader, step k - 2, finished at barrier k - 1. The design never aborts (it has no bounded
 // wait), so the wave joins every barrier, -1 .. T.
@@ -937,7 +943,7 @@ __device__ __forceinline__ void biol_raw_wave(const FusedBwdArgs& a, int n, int 
 // one ring slot; compact records then take a quarter of the slot's loads.
 __host__ __device__ constexpr int fused_bwdl_max_br(int D) { return BWDL_SLOT / (D * BWD_REC * 4); }
 
-template <int CELL, int KT>
+template <int CELL, int KT, bool BF>
 __global__ void __launch_bounds__((BWDL_NCW + 1) * 64, 1) fused_bwd_local_kernel(FusedBwdArgs a) {
   constexpr int G = cell_gates(CELL);
   constexpr int NCW = BWDL_NCW;
@@ -954,13 +960,14 @@ __global__ void __launch_bounds__((BWDL_NCW + 1) * 64, 1) fused_bwd_local_kernel
   const int n = group % N, bblk = group / N;
   const int b0 = bblk * a.BR;
   const int nvalid = min(a.BR, a.B - b0);
-  const FusedBwdlLds lay = fused_bwdl_lds(G, D, a.BR);
-  const int ROW = fused_bwdl_row(G, D);
+  const FusedBwdlLds lay = fused_bwdl_lds(G, D, a.BR, BF);
+  const int ROW = fused_bwdl_row(G, D, BF);  // elements of a da row (fp32, or bf16)
   float* dab = reinterpret_cast<float*>(smem + lay.da);
+  uint16_t* dabh = reinterpret_cast<uint16_t*>(smem + lay.da);
   char* const ring = smem + lay.rin;
   // both parities of da start at zero: step 0 has no dh_R, and rows of padding batch columns
   // are never written
-  for (int i = threadIdx.x; i < 2 * 16 * ROW; i += (NCW + 1) * 64) dab[i] = 0.0f;
+  for (int i = threadIdx.x; i < 2 * 16 * ROW * (BF ? 1 : 2) / 2; i += (NCW + 1) * 64) dab[i] = 0.0f;
 
   if (wave == NCW) {
     if (DIRECT && a.raw) {
@@ -984,11 +991,13 @@ __global__ void __launch_bounds__((BWDL_NCW + 1) * 64, 1) fused_bwd_local_kernel
   const bool colv = col < nvalid;
   const int tt = wave;  // the wave's tile of R's rows
   const bool tv = tt < TPH;
-  float Ra[KT];
+  // R's A fragments: KT k-tiles of 4 (fp32) or 32 (bf16) of the wave's tile
+  typedef typename std::conditional<BF, bf16x8_t, float>::type afrag_t;
+  afrag_t Ra[KT];
   {
-    const float* rp = reinterpret_cast<const float*>(a.rpk) + ((long long)n * TPH + min(tt, TPH - 1)) * KT * 64 + lane;
+    const afrag_t* rp = reinterpret_cast<const afrag_t*>(a.rpk) + ((long long)n * TPH + min(tt, TPH - 1)) * KT * 64 + lane;
 #pragma unroll
-    for (int kk = 0; kk < KT; ++kk) Ra[kk] = tv ? rp[(long long)kk * 64] : 0.0f;
+    for (int kk = 0; kk < KT; ++kk) Ra[kk] = rp[(long long)kk * 64];
   }
   const int gu = 16 * tt + 4 * quad;  // the lane's first unit
   float cr[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // LSTM dc, GRU dh carried to the next kernel step
@@ -1003,11 +1012,20 @@ __global__ void __launch_bounds__((BWDL_NCW + 1) * 64, 1) fused_bwd_local_kernel
     if (tv) {  // (uniform in the wave; every wave reaches every barrier)
       // ---- dh_R = sum over k of R[d][k] da[k] for this wave's 16 rows d, all batch columns
       f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-      const float* bp = dab + ((s + 1) & 1) * 16 * ROW + col * ROW + quad;
+      if constexpr (BF) {  // lane (col, quad): da[col][32 kk + 8 quad ..+7]
+        const uint16_t* bp = dabh + ((s + 1) & 1) * 16 * ROW + col * ROW + 8 * quad;
 #pragma unroll
-      for (int kk = 0; kk < KT; kk += 2) {
-        acc0 = mfma_f32(Ra[kk], bp[kk * 4], acc0);
-        if (kk + 1 < KT) acc1 = mfma_f32(Ra[kk + 1], bp[(kk + 1) * 4], acc1);
+        for (int kk = 0; kk < KT; kk += 2) {
+          acc0 = mfma_bf16(Ra[kk], *reinterpret_cast<const bf16x8_t*>(bp + kk * 32), acc0);
+          if (kk + 1 < KT) acc1 = mfma_bf16(Ra[kk + 1], *reinterpret_cast<const bf16x8_t*>(bp + (kk + 1) * 32), acc1);
+        }
+      } else {  // lane (col, quad): da[col][4 kk + quad]
+        const float* bp = dab + ((s + 1) & 1) * 16 * ROW + col * ROW + quad;
+#pragma unroll
+        for (int kk = 0; kk < KT; kk += 2) {
+          acc0 = mfma_f32(Ra[kk], bp[kk * 4], acc0);
+          if (kk + 1 < KT) acc1 = mfma_f32(Ra[kk + 1], bp[(kk + 1) * 4], acc1);
+        }
       }
       const f32x4_t pre = acc0 + acc1;
       if (colv) {
@@ -1061,10 +1079,21 @@ __global__ void __launch_bounds__((BWDL_NCW + 1) * 64, 1) fused_bwd_local_kernel
             da[0][i] = dh[i] * r0[0];
           }
         }
-        float* dw = dab + (s & 1) * 16 * ROW + col * ROW + gu;
+        if constexpr (BF) {
+          uint16_t* dw = dabh + (s & 1) * 16 * ROW + col * ROW + gu;
 #pragma unroll
-        for (int g = 0; g < G; ++g)
-          *reinterpret_cast<f32x4_t*>(dw + g * D) = f32x4_t{da[g][0], da[g][1], da[g][2], da[g][3]};
+          for (int g = 0; g < G; ++g) {
+            uint2 v;
+            v.x = (uint32_t)f2bf(da[g][0]) | ((uint32_t)f2bf(da[g][1]) << 16);
+            v.y = (uint32_t)f2bf(da[g][2]) | ((uint32_t)f2bf(da[g][3]) << 16);
+            *reinterpret_cast<uint2*>(dw + g * D) = v;
+          }
+        } else {
+          float* dw = dab + (s & 1) * 16 * ROW + col * ROW + gu;
+#pragma unroll
+          for (int g = 0; g < G; ++g)
+            *reinterpret_cast<f32x4_t*>(dw + g * D) = f32x4_t{da[g][0], da[g][1], da[g][2], da[g][3]};
+        }
         if constexpr (DIRECT) {
           const long long bg = (long long)a.bbase + b0 + col, t = T - 1 - s;
           if (a.dWx) {

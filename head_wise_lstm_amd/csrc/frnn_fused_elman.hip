@@ -28,9 +28,9 @@ FusedBwdxTable fused_bwdx_table_elman() {
 
 FusedBwdTable fused_bwd_table_elman() { return FusedBwdTable{kBwdTable, (int)(sizeof(kBwdTable) / sizeof(kBwdTable[0]))}; }
 
-fused_bwd_fn fused_bwd_local_elman(int D) {
-  if (D == 32) return &fused_bwd_local_kernel<CELL_ELMAN, 1 * 32 / 4>;
-  if (D == 64) return &fused_bwd_local_kernel<CELL_ELMAN, 1 * 64 / 4>;
+fused_bwd_fn fused_bwd_local_elman(int D, bool bf) {
+  if (D == 32) return bf ? &fused_bwd_local_kernel<CELL_ELMAN, 1 * 32 / 32, true> : &fused_bwd_local_kernel<CELL_ELMAN, 1 * 32 / 4, false>;
+  if (D == 64) return bf ? &fused_bwd_local_kernel<CELL_ELMAN, 1 * 64 / 32, true> : &fused_bwd_local_kernel<CELL_ELMAN, 1 * 64 / 4, false>;
   return nullptr;
 }
 

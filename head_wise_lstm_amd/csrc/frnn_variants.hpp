@@ -114,10 +114,11 @@ FusedBwdxTable fused_bwdx_table_lstm();
 FusedBwdxTable fused_bwdx_table_elman();
 FusedBwdxTable fused_bwdx_table_gru();
 
-// The single-workgroup fp32 backward (fused_bwd_local_kernel) of a cell for heads of D units,
-// D = 32 or 64 (its k-tiles, G*D/4, are a template parameter), or null for any other D.
-fused_bwd_fn fused_bwd_local_lstm(int D);
-fused_bwd_fn fused_bwd_local_elman(int D);
-fused_bwd_fn fused_bwd_local_gru(int D);
+// The single-workgroup backward (fused_bwd_local_kernel) of a cell for heads of D units, D = 32 or
+// 64 (its k-tiles, G*D/4 on the fp32 MFMA or G*D/32 on the bf16 one where bf, are a template
+// parameter), or null for any other D.
+fused_bwd_fn fused_bwd_local_lstm(int D, bool bf);
+fused_bwd_fn fused_bwd_local_elman(int D, bool bf);
+fused_bwd_fn fused_bwd_local_gru(int D, bool bf);
 
 }  // namespace frnn
