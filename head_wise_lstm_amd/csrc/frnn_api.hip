@@ -1030,6 +1030,9 @@ int run_fused_bwd(int cell, const BwdArgs& a, const FusedBwdPlan& fp, const DevI
     f.rpk = a.rpk;
     f.rec = rec + (size_t)b0 * a.N * a.D * BWD_REC;
     f.dstate = dstate + (size_t)b0 * a.N * a.D * 2;
+    f.bbase = b0;
+    f.dWx = a.dWx; f.wx_sb = a.wx_sb; f.wx_st = a.wx_st;
+    f.da = a.da; f.Kp = a.Kp; f.f32op = a.f32; f.carry = a.carry;
     f.xbuf = reinterpret_cast<uint32_t*>(base + L.xbuf);
     f.err = reinterpret_cast<int*>(base - kErrBytes);
     f.timeout_ticks = (long long)env_int("FRNN_TIMEOUT_MS", 2000) * di.wall_khz;
@@ -1038,9 +1041,9 @@ int run_fused_bwd(int cell, const BwdArgs& a, const FusedBwdPlan& fp, const DevI
     const int lrc = launch_resident(fn, grid, fused_threads(fp.ncw), fp.lds, args, di.cus, st);
     if (lrc != FRNN_OK) return lrc;
   }
-  if (compact) {
-    // the serial kernel stored dWx and da; an Elman cell carries nothing to the step before, and
-    // the carries are zero from the start
+  if (compact || fp.px) {
+    // the serial kernel stored dWx, da and the carries of time step 0 (an Elman cell's are zero
+    // from the start)
   } else if (f32) {
     if (cell == FRNN_CELL_LSTM) hipLaunchKernelGGL((bwd_post_kernel<CELL_LSTM, true>), dim3(pgrid), dim3(256), 0, st, a, rec, dstate);
     else if (cell == FRNN_CELL_GRU) hipLaunchKernelGGL((bwd_post_kernel<CELL_GRU, true>), dim3(pgrid), dim3(256), 0, st, a, rec, dstate);

@@ -50,13 +50,15 @@ struct FusedBwdArgs {
   int* err;
   long long timeout_ticks;
   int stall_step;    // a failure-handling test's hook: this step publishes a stale tag (-1: none)
-  // the single-workgroup design on an Elman cell stores dWx and the dR operand da itself (as
-  // bwd_apply lays them out) instead of dh: row b of this launch is batch row bbase + b
+  // The partial-sum design, and the single-workgroup design on an Elman cell, store dWx and the
+  // dR operand da themselves (as bwd_apply lays them out) instead of the state gradients, and the
+  // partial-sum design the carries of time step 0: row b of this launch is batch row bbase + b.
   int bbase;
-  float* dWx;        // [B,T,N,D] slices (or null)
+  float* dWx;        // [B,T,G,N,D] slices (or null)
   long long wx_sb, wx_st;
-  void* da;          // [N][Kp][D] dR operand (fp32 where f32op, else bf16)
+  void* da;          // [N][Kp][G*D] dR operand (fp32 where f32op, else bf16)
   int Kp, f32op;
+  float* carry;      // [B][N][D]
   // raw = 1: no records at all; the I/O wave loads each step's h and its state gradient ds_h
   // straight from the forward's states and the caller's gradient (or the zero page), in rows of
   // [h: D floats][ds_h: D floats], and the step's coefficients 1 - h^2 and ds_h (+ dl_h at the
@@ -524,10 +526,15 @@ __device__ __forceinline__ void biox_wave(const BwdxDma& c, char* ring, const in
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 }
 
-// x + (x of the lane D places up in the 16-lane row; 0 past the row's end).
-template <int D>
-__device__ __forceinline__ float row_shl_add(float x) {
-  return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x100 + D, 0xF, 0xF, true));
+// The sum of x over the lane's 16-lane row, in every lane of the row: the lanes of each quad swap
+// and add (quad_perm 1,0,3,2 then 2,3,0,1), then the halves of each 8-lane half-row and of the
+// row (half-row and row mirrors). Every lane adds the same pairs, so all sixteen get the same bits.
+__device__ __forceinline__ float row_allreduce_add(float x) {
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, true));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, true));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, true));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xF, 0xF, true));
+  return x;
 }
 
 // xbuf: [groups][2][W][BR][D] words. NCW * MTW = D / 16; KTW * 32 = G * D / W; the last KTL of
@@ -639,7 +646,8 @@ __global__ void __launch_bounds__((NCW + 1) * 64, 1) fused_bwdx_kernel(FusedBwdA
     vmask[e] = pv ? 0xFFFF0000u : 0u;
   }
   const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(xb, (short)0, 2 * xpar * 4, 0x00020000);
-  float cr[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // LSTM dc, GRU dh carried to the next step, for the quad
+  const int ui = chunk & 3, gi = chunk >> 2;  // the lane's unit of the quad, and gate
+  float cr = 0.0f;  // LSTM dc, GRU dh of unit ui carried to the next step
 
   // Step 0 has no dh_R: publish zero partials with tag 0 (parity 1), polled like any other step.
   if (col < nvalid) {
@@ -654,21 +662,15 @@ __global__ void __launch_bounds__((NCW + 1) * 64, 1) fused_bwdx_kernel(FusedBwdA
   for (int s = 0; s < T; ++s) {
     // ---- A. poll this workgroup's units in every slot, add the partials, apply the step
     if (poller) {
-      // this step's records of the lane's four units (in the ring since barrier s-1)
-      const bool mathlane = cv && chunk == 0;
+      // this step's records of the lane's unit ui of the quad (in the ring since barrier s-1)
       const float* rr = reinterpret_cast<const float*>(ring + (s & (BWDX_RING - 1)) * BWDX_SLOT) +
-                        (mathlane ? pr : 0) * UW * BWD_REC + (mathlane ? 4 * pq : 0) * BWD_REC;
-      f32x4_t rc[4][2];
+                        (cv ? pr : 0) * UW * BWD_REC + (cv ? 4 * pq + ui : 0) * BWD_REC;
+      f32x4_t rc[2];
       // The records go out before the poll (their latency hidden behind it) unless R k-tiles live
-      // in LDS: those designs hold up to 96 VGPRs of R, and 32 registers of records held through
-      // the poll would push values out to scratch. They read each unit's records where they are
-      // used, after the poll.
+      // in LDS: those designs hold up to 96 VGPRs of R. They read the records after the poll.
       if constexpr (KTL == 0) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          rc[i][0] = *reinterpret_cast<const f32x4_t*>(rr + i * BWD_REC);
-          rc[i][1] = *reinterpret_cast<const f32x4_t*>(rr + i * BWD_REC + 4);
-        }
+        rc[0] = *reinterpret_cast<const f32x4_t*>(rr);
+        rc[1] = *reinterpret_cast<const f32x4_t*>(rr + 4);
       }
       const uint32_t tag = (uint32_t)s & 0xFFFFu;
       // 16-byte loads that bypass the CU cache (cache policy sc1, the coherence of an agent-scope
@@ -703,61 +705,53 @@ __global__ void __launch_bounds__((NCW + 1) * 64, 1) fused_bwdx_kernel(FusedBwdA
         }
       }
       if (ok) {
+        // every lane of the row gets the quad's four sums; lane (gi, ui) then applies the step to
+        // unit ui and forms gate gi of da and dWx
         float sum[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           sum[i] = 0.0f;
 #pragma unroll
           for (int e = 0; e < BWDX_NP; ++e) sum[i] += __uint_as_float(v[e][i] & vmask[e]);
-          // lane 16c' gathers the sixteen chunks of its combination: x[p] += x[p + d], d = 8, 4,
-          // 2, 1 (row shifts; lanes past the 16-lane row read 0, and only lanes 16c' use it)
-          sum[i] = row_shl_add<1>(row_shl_add<2>(row_shl_add<4>(row_shl_add<8>(sum[i]))));
+          sum[i] = row_allreduce_add(sum[i]);
         }
-        if (mathlane) {
-          float da[G][4], dh[4], dc[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            f32x4_t r0, r1;
-            if constexpr (KTL > 0) {
-              r0 = *reinterpret_cast<const f32x4_t*>(rr + i * BWD_REC);
-              r1 = *reinterpret_cast<const f32x4_t*>(rr + i * BWD_REC + 4);
-            } else {
-              r0 = rc[i][0];
-              r1 = rc[i][1];
-            }
-            if constexpr (CELL == CELL_LSTM) {
-              dh[i] = sum[i] + r1[2];
-              dc[i] = cr[i] + r1[3] + dh[i] * r0[0];
-              da[0][i] = dc[i] * r0[1];
-              da[1][i] = dc[i] * r0[2];
-              da[2 % G][i] = dc[i] * r0[3];
-              da[3 % G][i] = dh[i] * r1[0];
-              cr[i] = dc[i] * r1[1];
-            } else if constexpr (CELL == CELL_GRU) {
-              dh[i] = sum[i] + r1[0] + cr[i];
-              dc[i] = 0.0f;
-              da[0][i] = dh[i] * r0[0];
-              da[1 % G][i] = dh[i] * r0[1];
-              da[2 % G][i] = dh[i] * r0[2];
-              cr[i] = dh[i] * r0[3];
-            } else {
-              dh[i] = sum[i] + r0[1];
-              dc[i] = 0.0f;
-              da[0][i] = dh[i] * r0[0];
-            }
+        if (cv) {
+          f32x4_t r0, r1;
+          if constexpr (KTL > 0) {
+            r0 = *reinterpret_cast<const f32x4_t*>(rr);
+            r1 = *reinterpret_cast<const f32x4_t*>(rr + 4);
+          } else {
+            r0 = rc[0];
+            r1 = rc[1];
           }
-          uint32_t* sg = stage + ((s & 1) * 16 + pr) * SROW;
-#pragma unroll
-          for (int g = 0; g < G; ++g)
-            *reinterpret_cast<uint2*>(sg + ((g * UW + 4 * pq) >> 1)) =
-                make_uint2((uint32_t)f2bf(da[g][0]) | ((uint32_t)f2bf(da[g][1]) << 16),
-                           (uint32_t)f2bf(da[g][2]) | ((uint32_t)f2bf(da[g][3]) << 16));
-          // (dh, dc) of the four units, straight to memory: these waves' next wait on memory is
-          // the next step's poll, long after the stores have landed
-          float* ro = a.dstate + (long long)s * a.Bs * N * D * 2 + ((long long)(b0 + pr) * N + n) * D * 2 +
-                      (long long)(u0 + 4 * pq) * 2;
-          *reinterpret_cast<f32x4_t*>(ro) = f32x4_t{dh[0], dc[0], dh[1], dc[1]};
-          *reinterpret_cast<f32x4_t*>(ro + 4) = f32x4_t{dh[2], dc[2], dh[3], dc[3]};
+          const float su = ui == 0 ? sum[0] : ui == 1 ? sum[1] : ui == 2 ? sum[2] : sum[3];
+          float dag, dwg;  // gate gi of da and of dWx (they differ in the GRU's n gate)
+          if constexpr (CELL == CELL_LSTM) {
+            const float dh = su + r1[2];
+            const float dc = cr + r1[3] + dh * r0[0];
+            dag = gi == 0 ? dc * r0[1] : gi == 1 ? dc * r0[2] : gi == 2 ? dc * r0[3] : dh * r1[0];
+            dwg = dag;
+            cr = dc * r1[1];
+          } else if constexpr (CELL == CELL_GRU) {
+            const float dh = su + r1[0] + cr;
+            dag = gi == 0 ? dh * r0[0] : gi == 1 ? dh * r0[1] : dh * r0[2];
+            dwg = gi == 2 ? dh * r1[1] : dag;
+            cr = dh * r0[3];
+          } else {
+            const float dh = su + r0[1];
+            dag = dh * r0[0];
+            dwg = dag;
+          }
+          if (gi < G) {
+            const uint16_t dab = f2bf(dag);
+            reinterpret_cast<uint16_t*>(stage + ((s & 1) * 16 + pr) * SROW)[gi * UW + 4 * pq + ui] = dab;
+            // dWx and the dR operand straight to memory: these waves' next wait on memory is the
+            // next step's poll, long after the stores have landed
+            const long long bg = (long long)a.bbase + b0 + pr, t = T - 1 - s, u = u0 + 4 * pq + ui;
+            if (a.dWx) a.dWx[bg * a.wx_sb + t * a.wx_st + ((long long)gi * N + n) * D + u] = dwg;
+            reinterpret_cast<uint16_t*>(a.da)[((n * (long long)a.Kp + t * a.Bs + bg) * G + gi) * D + u] = dab;
+            if (CELL != CELL_ELMAN && gi == 0 && s == T - 1) a.carry[(bg * N + n) * D + u] = cr;
+          }
         }
       }
     }
