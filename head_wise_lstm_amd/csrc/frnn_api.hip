@@ -963,6 +963,16 @@ void launch_bwd_cell_kernel(BwdCellKernel k, int cell, bool f32, bool wx_f32, di
   else launch_bwd_cell_kernel_c<CELL_ELMAN>(k, f32, wx_f32, grid, block, st, a, t, rec);
 }
 
+// The single-workgroup design on an Elman cell needs no records where the forward's states and
+// their gradients sit in 16-byte aligned rows: its I/O wave loads h and ds_h itself, and then no
+// step needs h.R either (FRNN_BWD_ELMAN_RAW=0 pins the records).
+bool bwd_elman_raw(const BwdArgs& a, const FusedBwdPlan& fp) {
+  auto al16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
+  return fp.local && a.cell == FRNN_CELL_ELMAN && al16(a.st_h) && (!a.ds_h || al16(a.ds_h)) &&
+         (!a.dl_h || al16(a.dl_h)) && a.st_sb % 4 == 0 && a.st_st % 4 == 0 && a.last_sb % 4 == 0 && a.D % 4 == 0 &&
+         env_int("FRNN_BWD_ELMAN_RAW", 1) != 0;
+}
+
 // The fused serial part: records of every step, the persistent kernel, then dWx / da / carries.
 int run_fused_bwd(int cell, const BwdArgs& a, const FusedBwdPlan& fp, const DevInfo& di, char* base,
                   const BwdLayout& L, hipStream_t st) {
@@ -975,12 +985,8 @@ int run_fused_bwd(int cell, const BwdArgs& a, const FusedBwdPlan& fp, const DevI
   // stores its dWx and da itself
   const bool compact = fp.local && cell == FRNN_CELL_ELMAN;
   const int rec_f = compact ? 2 : BWD_REC;
-  // ... or, where the states and their gradient sit in 16-byte aligned rows, none at all: its I/O
-  // wave loads h and ds_h themselves
-  auto al16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
-  const bool raw = compact && al16(a.st_h) && (!a.ds_h || al16(a.ds_h)) && (!a.dl_h || al16(a.dl_h)) &&
-                   a.st_sb % 4 == 0 && a.st_st % 4 == 0 && a.last_sb % 4 == 0 && a.D % 4 == 0 &&
-                   env_int("FRNN_BWD_ELMAN_RAW", 1) != 0;
+  // ... or none at all (bwd_elman_raw)
+  const bool raw = compact && bwd_elman_raw(a, fp);
   if (raw) {
     // no records
   } else if (compact) {
@@ -1133,13 +1139,17 @@ int run_backward(const BwdProblem& q, int path, const FusedBwdPlan& fbp, const D
                       ((size_t)Kp - (size_t)T * B) * G * D * elt, st) != hipSuccess)
         return FRNN_EHIP;
   }
-  // 1. h_{t-1} for every step, R^T, and h.R for every step
-  hipLaunchKernelGGL(bwd_hprev_kernel, dim3((unsigned)std::min<long long>(((long long)N * Kp * (D / 8) + 255) / 256, 65536)),
-                     dim3(256), 0, st, a);
+  // 1. h_{t-1} for every step, R^T, and h.R for every step (none of it where the serial part reads
+  // no records: the dR GEMM's h^T then comes straight from the states)
+  const bool no_hr = path == FRNN_PATH_FUSED && bwd_elman_raw(a, fbp);
+  const bool hT_direct = no_hr && !f32;
+  if (!hT_direct)
+    hipLaunchKernelGGL(bwd_hprev_kernel, dim3((unsigned)std::min<long long>(((long long)N * Kp * (D / 8) + 255) / 256, 65536)),
+                       dim3(256), 0, st, a);
   // R_g^T of every (head, gate): one launch per gate over the heads, or per head over the gates,
   // whichever makes fewer launches
   const bool by_head = N >= G;
-  for (int i = 0; i < (by_head ? G : N); ++i) {
+  for (int i = 0; i < (no_hr ? 0 : by_head ? G : N); ++i) {
     const int g = by_head ? i : 0, n = by_head ? 0 : i;
     const size_t src = (size_t)g * a.r_sg + (size_t)n * a.r_sn, dst = ((size_t)n * G + g) * D * D;
     const long long src_z = by_head ? a.r_sn : a.r_sg, dst_z = by_head ? (long long)G * D * D : (long long)D * D;
@@ -1151,8 +1161,8 @@ int run_backward(const BwdProblem& q, int path, const FusedBwdPlan& fbp, const D
                                  reinterpret_cast<uint16_t*>(rt) + dst, D, st, by_head ? N : G, src_z, dst_z);
   }
   // h.R of every head in one launch
-  if (launch_gemm(f32, T * B, G * D, D, base + L.hprev, D, rt, D, hr, (long long)G * D, st, 1, 0, 0, 0, false, N,
-                  (long long)Kp * D, (long long)G * D * D, (long long)T * B * G * D) != hipSuccess)
+  if (!no_hr && launch_gemm(f32, T * B, G * D, D, base + L.hprev, D, rt, D, hr, (long long)G * D, st, 1, 0, 0, 0, false, N,
+                            (long long)Kp * D, (long long)G * D * D, (long long)T * B * G * D) != hipSuccess)
     return FRNN_EHIP;
   // 2. the serial part (R packed once as the dh kernels' A fragments)
   {
@@ -1191,7 +1201,12 @@ int run_backward(const BwdProblem& q, int path, const FusedBwdPlan& fbp, const D
     // h^T and da^T of every head, one launch each
     const long long h_z = (long long)Kp * D, ht_z = (long long)(D + 1) * Kp;
     const long long d_z = (long long)Kp * G * D, dt_z = (long long)G * D * Kp;
-    if (f32) {
+    if (hT_direct) {
+      hipLaunchKernelGGL(bwd_hprevT_kernel, dim3((D + 63) / 64, std::min(Kp / 64, 65535), N), dim3(256), 0, st, a,
+                         reinterpret_cast<uint16_t*>(hT));
+      launch_transpose<uint16_t>(reinterpret_cast<const uint16_t*>(a.da), (long long)G * D, Kp, G * D,
+                                 reinterpret_cast<uint16_t*>(daT), Kp, st, N, d_z, dt_z);
+    } else if (f32) {
       launch_transpose<uint32_t>(reinterpret_cast<const uint32_t*>(a.hprev), D, Kp, D, reinterpret_cast<uint32_t*>(hT), Kp,
                                  st, N, h_z, ht_z);
       launch_transpose<uint32_t>(reinterpret_cast<const uint32_t*>(a.da), (long long)G * D, Kp, G * D,

@@ -106,6 +106,55 @@ __global__ void __launch_bounds__(256) bwd_hprev_kernel(BwdArgs a) {
   }
 }
 
+// The dR GEMM's A operand straight from the states, bf16: hT[n][d][k] = h_{t-1}[b][n][d] for k = t*B
+// + b < T*B (the initial state, or zero, for t = 0), zero for k up to Kp (row d = D, the ones, is
+// bwd_ones_row_kernel's). 64 k x 64 d tiles through LDS: each row of a tile is read as 256 bytes
+// of fp32 (16-byte loads), and each output row written as 128 bytes (8-byte stores). Grid
+// (ceil(D / 64), min(Kp / 64, 65535), N), the k tiles repeating by gridDim.y; D a multiple of 32
+// (a tile's rows past D stay empty). Where the h.R recompute is not needed this replaces
+// bwd_hprev_kernel and the transpose of its output.
+__global__ void __launch_bounds__(256) bwd_hprevT_kernel(BwdArgs a, uint16_t* hT) {
+  __shared__ __attribute__((aligned(16))) uint16_t s[64][68];
+  const int d0 = blockIdx.x * 64, n = blockIdx.z;
+  const int D = a.D, TB = a.T * a.B;
+  const int t16 = threadIdx.x >> 4, c4 = (threadIdx.x & 15) * 4;  // row t16 + 16 i, 4 d from c4
+  for (int kb = blockIdx.y; kb * 64 < a.Kp; kb += gridDim.y) {
+    const int k0 = kb * 64;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int k = k0 + t16 + 16 * i, d = d0 + c4;
+      float v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      if (k < TB && d < D) {
+        const int t = k / a.B, b = k - t * a.B;
+        if (t > 0) {
+          const f32x4_t x = *reinterpret_cast<const f32x4_t*>(a.st_h + (long long)b * a.st_sb + (long long)(t - 1) * a.st_st +
+                                                           (long long)n * D + d);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) v[q] = x[q];
+        } else if (a.s0_h) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) v[q] = ld_f(a.s0_h, (long long)b * a.s0_sb + (long long)n * D + d + q, false);
+        }
+      }
+      uint2 w;
+      w.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
+      w.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
+      *reinterpret_cast<uint2*>(&s[t16 + 16 * i][c4]) = w;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int j = t16 + 16 * i, d = d0 + j;  // output row d, 4 k from k0 + c4
+      if (d >= D) continue;
+      uint2 w;
+      w.x = (uint32_t)s[c4][j] | ((uint32_t)s[c4 + 1][j] << 16);
+      w.y = (uint32_t)s[c4 + 2][j] | ((uint32_t)s[c4 + 3][j] << 16);
+      *reinterpret_cast<uint2*>(hT + ((long long)n * (D + 1) + d) * a.Kp + k0 + c4) = w;
+    }
+    __syncthreads();
+  }
+}
+
 // The coefficients of step t for one (b, n, unit): everything the backward of the step needs
 // that does not depend on the gradient arriving from later steps (the gates from the recomputed
 // h.R, Wx and the bias, the states, and the gradients of the step's own outputs). The record

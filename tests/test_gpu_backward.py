@@ -330,18 +330,21 @@ _ELMAN_IN = fi.HeadwiseWorkload("bwd_elman_inputs_D64", "elman", torch.bfloat16,
 
 
 @pytest.mark.parametrize("raw", [1, 0])
-@pytest.mark.parametrize("given", ["both", "dstates", "dlast"])
+@pytest.mark.parametrize("given", ["both", "dstates", "dlast", "no_states0"])
 def test_bwd_elman_local_inputs(raw, given):
-    """The single-workgroup design on an Elman cell: its I/O wave loads h and ds_h themselves (raw)
-    or two-float records (FRNN_BWD_ELMAN_RAW=0); either gradient of the forward's outputs may be
-    absent (read as zeros), and dlast joins ds_h only at the last time step."""
+    """The single-workgroup design on an Elman cell: its I/O wave loads h and ds_h themselves (raw;
+    no h.R recompute, the dR GEMM's h^T straight from the states) or two-float records
+    (FRNN_BWD_ELMAN_RAW=0); either gradient of the forward's outputs may be absent (read as zeros),
+    dlast joins ds_h only at the last time step, and an absent initial state reads as zeros."""
     hw = _hw()
     w = _ELMAN_IN
     assert "workgroup-local" in hw.frnn_bwd_plan_str(hw._desc(w.B, w.T, w.N, w.D, w.cell, w.dtype), "fused")
     x = {k: (v.cuda() if v is not None else None) for k, v in fi.make_inputs(w).items()}
     ct = fi.backward_cotangents(w)
-    ds = ct["dstates"] if given in ("both", "dstates") else None
-    dl = ct["dlast"] if given in ("both", "dlast") else None
+    ds = ct["dstates"] if given != "dlast" else None
+    dl = ct["dlast"] if given != "dstates" else None
+    if given == "no_states0":
+        x["states0"] = None
     _log(f"bwd case {w.name} raw={raw} given={given}")
     st, _ = hw.frnn_fwd(x["Wx"], x["R"], x["b"], x["states0"], cell="elman")
     with _env({"FRNN_BWD_ELMAN_RAW": raw}):
