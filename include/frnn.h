@@ -168,18 +168,19 @@ int frnn_fwd(const frnn_desc* d, int path, const void* Wx, const void* R, const 
  *   dstates0    [S, B, 1, N, D]   fp32, written, or NULL
  * The contractions take bf16 operands (fp32 for fp32 inputs) with fp32 accumulation, like the
  * forward. T == 0: dstates0 = dlast, dR = db = 0. Both paths first recompute h.R for every step
- * with one MFMA GEMM per head and end with one GEMM per head that forms dR and db; they differ in
- * the serial part, t = T-1 .. 0:
- *   FRNN_PATH_ALTERNATING: per step, a pointwise kernel and an MFMA kernel (2*T launches);
+ * with one MFMA GEMM (all heads in one launch) and end with one GEMM over all heads that forms dR
+ * and db; they differ in the serial part, t = T-1 .. 0:
+ *   FRNN_PATH_ALTERNATING: per step, one or two kernels (T or 2*T launches);
  *   FRNN_PATH_FUSED: one launch for all T steps (per chunk of batch rows where the batch
- *     exceeds one launch). Either the workgroups of one die share a head and exchange the
- *     gradient reaching h through R every step (bf16 inputs; the forward's die-local design
- *     with h and R^T exchanged), or one workgroup holds a whole head of 32 or 64 units and
- *     keeps that gradient in LDS, multiplying on the fp32 MFMA (fp32 inputs, bf16 Elman heads,
- *     and bf16 heads no die-local design tiles). LSTM and GRU heads of 1024 units keep part of
- *     R in LDS. Shapes this build has no fused design for (fp32 heads wider than 64 units, say)
- *     return FRNN_EUNSUPPORTED before any launch; frnn_bwd_plan_str says which design a shape
- *     gets.
+ *     exceeds one launch). Either one workgroup holds a whole head of 32 or 64 units and keeps
+ *     that gradient in LDS, multiplying on the MFMA of the inputs' type (every head of at most
+ *     64 units; on an Elman cell with the states in 16-byte aligned rows it reads h and dstates
+ *     directly and the h.R recompute is skipped), or the workgroups of one die share a wider
+ *     head and exchange the gradient reaching h through R every step (bf16 inputs; the
+ *     forward's die-local design with h and R^T exchanged). LSTM and GRU heads of 1024 units
+ *     keep part of R in LDS. Shapes this build has no fused design for (fp32 heads wider than 64
+ *     units, say) return FRNN_EUNSUPPORTED before any launch; frnn_bwd_plan_str says which design
+ *     a shape gets.
  * The workspace grows with T (it holds every step's h.R and gradient).
  */
 int frnn_bwd(const frnn_desc* d, int path, const void* Wx, const void* R, const void* b,

@@ -168,9 +168,9 @@ def test_bwd_alternating_each_form(w, one):
 
 
 # Every fused backward design on the small bf16 cases, pinned with FRNN_FUSED_BWD_PX: the
-# partial-sum design (the planner's choice where it has one), the da-exchange design, and, for
-# heads of at most 64 units, the single-workgroup design on fp32 fragments of R (the planner's
-# choice for heads neither die-local design tiles). Heads of 32 units have only the last.
+# partial-sum design (the planner's choice for heads wider than 64 units), the da-exchange design,
+# and, for heads of at most 64 units, the single-workgroup design (the planner's choice there).
+# Heads of 32 units have only the last.
 _DESIGN_NAME = {1: "die-local-partials", 0: "design=die-local ", 2: "workgroup-local"}
 
 
