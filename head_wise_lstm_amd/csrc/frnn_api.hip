@@ -963,9 +963,9 @@ void launch_bwd_cell_kernel(BwdCellKernel k, int cell, bool f32, bool wx_f32, di
   else launch_bwd_cell_kernel_c<CELL_ELMAN>(k, f32, wx_f32, grid, block, st, a, t, rec);
 }
 
-// The single-workgroup design on an Elman cell needs no records where the forward's states and
-// their gradients sit in 16-byte aligned rows: its I/O wave loads h and ds_h itself, and then no
-// step needs h.R either (FRNN_BWD_ELMAN_RAW=0 pins the records).
+// The single-workgroup design on an Elman cell needs no records: its I/O wave loads h and ds_h
+// itself (16-byte rows, which the boundary's alignment rules guarantee; checked again here), and
+// then no step needs h.R either. FRNN_BWD_ELMAN_RAW=0 pins compact records.
 bool bwd_elman_raw(const BwdArgs& a, const FusedBwdPlan& fp) {
   auto al16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
   return fp.local && a.cell == FRNN_CELL_ELMAN && al16(a.st_h) && (!a.ds_h || al16(a.ds_h)) &&
@@ -981,8 +981,7 @@ int run_fused_bwd(int cell, const BwdArgs& a, const FusedBwdPlan& fp, const DevI
   float* rec = reinterpret_cast<float*>(base + L.rec);
   float* dstate = reinterpret_cast<float*>(base + L.dstate);
   const bool f32 = a.f32 != 0;
-  // the single-workgroup design keeps an Elman cell's records compact (two coefficients) and
-  // stores its dWx and da itself
+  // the single-workgroup design keeps an Elman cell's records compact (two coefficients)
   const bool compact = fp.local && cell == FRNN_CELL_ELMAN;
   const int rec_f = compact ? 2 : BWD_REC;
   // ... or none at all (bwd_elman_raw)
@@ -1013,7 +1012,7 @@ int run_fused_bwd(int cell, const BwdArgs& a, const FusedBwdPlan& fp, const DevI
       f.dstate = dstate + (size_t)b0 * a.N * a.D * 2;
       f.bbase = b0;
       f.dWx = a.dWx; f.wx_sb = a.wx_sb; f.wx_st = a.wx_st;
-      f.da = a.da; f.Kp = a.Kp; f.f32op = a.f32;
+      f.da = a.da; f.Kp = a.Kp; f.f32op = a.f32; f.carry = a.carry;
       f.raw = raw ? 1 : 0;
       f.st_h = a.st_h; f.ds_h = a.ds_h; f.dl_h = a.dl_h; f.zeros = a.zeros;
       f.st_sb = a.st_sb; f.st_st = a.st_st; f.last_sb = a.last_sb;
@@ -1047,7 +1046,7 @@ int run_fused_bwd(int cell, const BwdArgs& a, const FusedBwdPlan& fp, const DevI
     const int lrc = launch_resident(fn, grid, fused_threads(fp.ncw), fp.lds, args, di.cus, st);
     if (lrc != FRNN_OK) return lrc;
   }
-  if (compact || fp.px) {
+  if (fp.local || fp.px) {
     // the serial kernel stored dWx, da and the carries of time step 0 (an Elman cell's are zero
     // from the start)
   } else if (f32) {

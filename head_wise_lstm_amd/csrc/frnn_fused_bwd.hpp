@@ -50,9 +50,9 @@ struct FusedBwdArgs {
   int* err;
   long long timeout_ticks;
   int stall_step;    // a failure-handling test's hook: this step publishes a stale tag (-1: none)
-  // The partial-sum design, and the single-workgroup design on an Elman cell, store dWx and the
-  // dR operand da themselves (as bwd_apply lays them out) instead of the state gradients, and the
-  // partial-sum design the carries of time step 0: row b of this launch is batch row bbase + b.
+  // The partial-sum and single-workgroup designs store dWx, the dR operand da (as bwd_apply lays
+  // them out) and the carries of time step 0 themselves, instead of the state gradients: row b of
+  // this launch is batch row bbase + b.
   int bbase;
   float* dWx;        // [B,T,G,N,D] slices (or null)
   long long wx_sb, wx_st;
@@ -815,8 +815,8 @@ namespace frnn {
 //     rounded to bf16 as the die-local designs' operand is (an eighth of the MFMAs).
 // Lane l of the result holds dh_R of units 4*(l/16)..+3 of its tile for batch column l%16, as in
 // the die-local design, and applies the same linear step. The I/O wave streams the records into
-// an LDS ring as the partial-sum design's does, and the lanes that apply a step store its (dh, dc)
-// (one barrier per step).
+// an LDS ring as the partial-sum design's does, and the lanes that apply a step store its dWx and
+// da (one barrier per step).
 constexpr int BWDL_NCW = 4;
 // da row of the LDS stage: floats (fp32), or bf16 elements padded by 16 bytes (bf16)
 __host__ __device__ constexpr int fused_bwdl_row(int G, int D, bool bf = false) { return bf ? G * D + 8 : G * D + 4; }
@@ -942,7 +942,7 @@ __global__ void __launch_bounds__((BWDL_NCW + 1) * 64, 1) fused_bwd_local_kernel
   constexpr int G = cell_gates(CELL);
   constexpr int NCW = BWDL_NCW;
   constexpr int REC = bwdl_rec(CELL);  // floats a record
-  constexpr bool DIRECT = CELL == CELL_ELMAN;  // dWx and da out, instead of (dh, dc)
+  constexpr bool ELM = CELL == CELL_ELMAN;  // the cell whose records may be read raw
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -964,7 +964,7 @@ __global__ void __launch_bounds__((BWDL_NCW + 1) * 64, 1) fused_bwd_local_kernel
   for (int i = threadIdx.x; i < 2 * 16 * ROW * (BF ? 1 : 2) / 2; i += (NCW + 1) * 64) dab[i] = 0.0f;
 
   if (wave == NCW) {
-    if (DIRECT && a.raw) {
+    if (ELM && a.raw) {
       biol_raw_wave<BWDL_NE * REC / BWD_REC>(a, n, b0, nvalid, lane, ring);
       return;
     }
@@ -997,7 +997,7 @@ __global__ void __launch_bounds__((BWDL_NCW + 1) * 64, 1) fused_bwd_local_kernel
   float cr[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // LSTM dc, GRU dh carried to the next kernel step
   // raw inputs: the gradient of last_states joins ds_h at the last time step (kernel step 0)
   f32x4_t dl = {0.f, 0.f, 0.f, 0.f};
-  if (DIRECT && a.raw && a.dl_h && colv && tv)
+  if (ELM && a.raw && a.dl_h && colv && tv)
     dl = *reinterpret_cast<const f32x4_t*>(a.dl_h + (long long)(a.bbase + b0 + col) * a.last_sb + (long long)n * D + gu);
   block_barrier();  // barrier -1
 
@@ -1026,8 +1026,8 @@ __global__ void __launch_bounds__((BWDL_NCW + 1) * 64, 1) fused_bwd_local_kernel
         // ---- the linear step for the lane's four units; da into this step's parity, (dh, dc) out
         const float* rr = reinterpret_cast<const float*>(ring + (s & (BWDX_RING - 1)) * BWDL_SLOT) + col * D * REC +
                           gu * REC;
-        // (dh, dc), or dWx and da, straight to memory: these waves never wait on memory
-        float da[G][4], dh[4], dc[4];
+        // dWx, da and the carries straight to memory: these waves never wait on memory
+        float da[G][4], dh[4], dc[4], dwn[4];  // dwn: the GRU's n-gate dWx (its da differs)
         f32x4_t rc[2];  // compact records: the four units' (r0[0], r0[1]) pairs
         if constexpr (REC == 2) {
           if (a.raw) {  // row col of the slot: h, then ds_h, D floats each
@@ -1066,6 +1066,7 @@ __global__ void __launch_bounds__((BWDL_NCW + 1) * 64, 1) fused_bwd_local_kernel
             da[0][i] = dh[i] * r0[0];
             da[1 % G][i] = dh[i] * r0[1];
             da[2 % G][i] = dh[i] * r0[2];
+            dwn[i] = dh[i] * r1[1];
             cr[i] = dh[i] * r0[3];
           } else {
             dh[i] = pre[i] + r0[1];
@@ -1088,27 +1089,27 @@ __global__ void __launch_bounds__((BWDL_NCW + 1) * 64, 1) fused_bwd_local_kernel
           for (int g = 0; g < G; ++g)
             *reinterpret_cast<f32x4_t*>(dw + g * D) = f32x4_t{da[g][0], da[g][1], da[g][2], da[g][3]};
         }
-        if constexpr (DIRECT) {
-          const long long bg = (long long)a.bbase + b0 + col, t = T - 1 - s;
-          if (a.dWx) {
-            float* dw = a.dWx + bg * a.wx_sb + t * a.wx_st + (long long)n * D + gu;
+        const long long bg = (long long)a.bbase + b0 + col, t = T - 1 - s;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) dw[i] = da[0][i];
-          }
-          const long long drow = ((long long)n * a.Kp + t * a.Bs + bg) * D + gu;
+        for (int g = 0; g < G; ++g) {
+          const bool nw = CELL == CELL_GRU && g == 2;
+          const f32x4_t wv = nw ? f32x4_t{dwn[0], dwn[1], dwn[2], dwn[3]} : f32x4_t{da[g][0], da[g][1], da[g][2], da[g][3]};
+          // (a unit quad of dWx is 16-byte aligned: the boundary takes aligned pointers and
+          // strides of whole multiples of four elements)
+          if (a.dWx) *reinterpret_cast<f32x4_t*>(a.dWx + bg * a.wx_sb + t * a.wx_st + ((long long)g * N + n) * D + gu) = wv;
+          const long long drow = (((long long)n * a.Kp + t * a.Bs + bg) * G + g) * D + gu;
           if (a.f32op) {
-            *reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(a.da) + drow) = f32x4_t{da[0][0], da[0][1], da[0][2], da[0][3]};
+            *reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(a.da) + drow) = f32x4_t{da[g][0], da[g][1], da[g][2], da[g][3]};
           } else {
             uint2 w;
-            w.x = (uint32_t)f2bf(da[0][0]) | ((uint32_t)f2bf(da[0][1]) << 16);
-            w.y = (uint32_t)f2bf(da[0][2]) | ((uint32_t)f2bf(da[0][3]) << 16);
+            w.x = (uint32_t)f2bf(da[g][0]) | ((uint32_t)f2bf(da[g][1]) << 16);
+            w.y = (uint32_t)f2bf(da[g][2]) | ((uint32_t)f2bf(da[g][3]) << 16);
             *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.da) + drow) = w;
           }
-        } else {
-          float* ro = a.dstate + (long long)s * a.Bs * N * D * 2 + ((long long)(b0 + col) * N + n) * D * 2 + gu * 2;
-          *reinterpret_cast<f32x4_t*>(ro) = f32x4_t{dh[0], dc[0], dh[1], dc[1]};
-          *reinterpret_cast<f32x4_t*>(ro + 4) = f32x4_t{dh[2], dc[2], dh[3], dc[3]};
         }
+        // the carries past time step 0 (the initial state's gradient adds them)
+        if (CELL != CELL_ELMAN && s == T - 1)
+          *reinterpret_cast<f32x4_t*>(a.carry + (bg * N + n) * D + gu) = f32x4_t{cr[0], cr[1], cr[2], cr[3]};
       }
     }
   }
