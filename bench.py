@@ -91,8 +91,9 @@ def write_traffic(args) -> None:
     ff, wf = true_kib / fc, true_kib / wc
     w = fi.get_workload(args.workload)
     if args.backward:
-        # the serial kernel's own: the step records read once, (dh, dc) written once, R read once
-        alg = float(w.T * w.B * w.N * w.D * (8 + 2) * 4 + w.G * w.N * w.D * w.D * 2)
+        # the partial-sum serial kernel's own: the step records (8 floats a unit) read once, dWx
+        # (fp32) and the dR operand da (bf16) of every gate written once, R read once
+        alg = float(w.T * w.B * w.N * w.D * (8 * 4 + w.G * (4 + 2)) + w.G * w.N * w.D * w.D * 2)
     else:
         alg = headwise_bytes(w, 2 if "bf16" in w.name else 4)
     rd, wr = fk * 1024 * ff, wk * 1024 * wf
