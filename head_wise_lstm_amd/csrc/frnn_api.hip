@@ -509,21 +509,33 @@ void launch_transpose(const E* src, long long lds, int K, int Nc, E* dst, long l
 }
 
 // Launch of the bf16 GEMM of ProjArgs: with bf16 A whose rows (and Bt's, and the parts' offsets)
-// start on 16-byte boundaries, the kernel that loads its tiles straight into LDS; otherwise the
-// register-staged one (fp32 A is rounded as it is staged). FRNN_PROJ_DMA=0 pins the latter.
-void launch_proj(const ProjArgs& pa, dim3 grid, hipStream_t st) {
-  if (pa.M <= 0 || pa.Nc <= 0) return;
+// start on 16-byte boundaries, the kernel that loads its tiles straight into LDS (128-row tiles
+// where the product has at most 128 rows); otherwise the register-staged one (fp32 A is rounded
+// as it is staged). FRNN_PROJ_DMA=0 pins the latter. The grid's x is proj_tiles(pa).
+bool proj_dma(const ProjArgs& pa) {
   const bool aligned = reinterpret_cast<uintptr_t>(pa.A) % 16 == 0 && reinterpret_cast<uintptr_t>(pa.Bt) % 16 == 0 &&
                        pa.lda % 8 == 0 && pa.ldb % 8 == 0 && pa.a_z % 8 == 0 && pa.b_z % 8 == 0 &&
                        pa.a_h % 8 == 0 && pa.b_h % 8 == 0;
-  const bool dma = !pa.a_f32 && aligned && env_int("FRNN_PROJ_DMA", 1);
+  return !pa.a_f32 && aligned && env_int("FRNN_PROJ_DMA", 1);
+}
+int proj_bm(const ProjArgs& pa) { return proj_dma(pa) && pa.M <= 128 ? 128 : PJ_BM; }
+unsigned proj_tiles(const ProjArgs& pa) {
+  const int bm = proj_bm(pa);
+  return (unsigned)(((pa.Nc + PJ_BN - 1) / PJ_BN) * ((pa.M + bm - 1) / bm));
+}
+
+void launch_proj(const ProjArgs& pa, dim3 grid, hipStream_t st) {
+  if (pa.M <= 0 || pa.Nc <= 0) return;
+  const bool dma = proj_dma(pa), small = proj_bm(pa) == 128;
   if (pa.nt) {
     if (pa.a_f32) hipLaunchKernelGGL((proj_gemm_kernel<true, true>), grid, dim3(256), 0, st, pa);
-    else if (dma) hipLaunchKernelGGL(proj_gemm_dma_kernel<true>, grid, dim3(256), 0, st, pa);
+    else if (dma && small) hipLaunchKernelGGL((proj_gemm_dma_kernel<true, 128>), grid, dim3(256), 0, st, pa);
+    else if (dma) hipLaunchKernelGGL((proj_gemm_dma_kernel<true>), grid, dim3(256), 0, st, pa);
     else hipLaunchKernelGGL((proj_gemm_kernel<false, true>), grid, dim3(256), 0, st, pa);
   } else {
     if (pa.a_f32) hipLaunchKernelGGL((proj_gemm_kernel<true, false>), grid, dim3(256), 0, st, pa);
-    else if (dma) hipLaunchKernelGGL(proj_gemm_dma_kernel<false>, grid, dim3(256), 0, st, pa);
+    else if (dma && small) hipLaunchKernelGGL((proj_gemm_dma_kernel<false, 128>), grid, dim3(256), 0, st, pa);
+    else if (dma) hipLaunchKernelGGL((proj_gemm_dma_kernel<false>), grid, dim3(256), 0, st, pa);
     else hipLaunchKernelGGL((proj_gemm_kernel<false, false>), grid, dim3(256), 0, st, pa);
   }
 }
@@ -555,7 +567,7 @@ hipError_t launch_gemm(bool f32, int M, int Nc, int K, const void* A, long long 
   pa.a_z = a_z; pa.b_z = b_z; pa.c_z = c_z;
   pa.a_h = a_h; pa.b_h = b_h; pa.c_h = c_h;
   pa.nt = 1;  // every caller's product is read by a streaming kernel
-  const dim3 pgrid(((Nc + PJ_BN - 1) / PJ_BN) * ((M + PJ_BM - 1) / PJ_BM), parts, heads);
+  const dim3 pgrid(proj_tiles(pa), parts, heads);
   launch_proj(pa, pgrid, st);
   return hipGetLastError();
 }
@@ -1644,7 +1656,7 @@ int frnn_lstm_stack_fwd(int L, int dirs, int T, int B, int I, int H, int path, c
     pa.C = wx;
     pa.ldc = G4;
     stack_transpose_wi(Wi, l, dirs, in, H, wit, st);
-    const dim3 pgrid(((pa.Nc + PJ_BN - 1) / PJ_BN) * ((pa.M + PJ_BM - 1) / PJ_BM));
+    const dim3 pgrid(proj_tiles(pa));
     launch_proj(pa, pgrid, st);
     if (hipGetLastError() != hipSuccess) return FRNN_EHIP;
     // recurrence, one head per direction: R[g][n][d][e] = Wh of direction n at [d][g*H + e], read
@@ -1821,7 +1833,7 @@ int frnn_lstm_stack_bwd(int L, int dirs, int T, int B, int I, int H, int path, c
       pa.C = layer_wx(l) + (size_t)k * 4 * H;
       pa.ldc = G4;
       launch_transpose<uint16_t>(reinterpret_cast<const uint16_t*>(Wi[j]), 4 * H, in, 4 * H, wit, in, st);
-      const dim3 pgrid(((pa.Nc + PJ_BN - 1) / PJ_BN) * ((pa.M + PJ_BM - 1) / PJ_BM));
+      const dim3 pgrid(proj_tiles(pa));
       launch_proj(pa, pgrid, st);
       if (hipGetLastError() != hipSuccess) return FRNN_EHIP;
       Problem p;

@@ -45,7 +45,7 @@ struct FusedBwdArgs {
   uint32_t* ctr;     // per-die workgroup counters (filled with 0xFFFF before the launch)
   const void* rpk;   // R as A fragments: [N][D/16][G*D/32][64] x 8 bf16 (bwd_rpack_kernel)
   const float* rec;  // [T][B][N][D][BWD_REC], indexed by the kernel step s
-  float* dstate;     // [T][B][N][D][2]: (dh, dc) of kernel step s
+  float* dstate;     // [T][B][N][D][2]: (dh, dc) of kernel step s (the da design's output)
   uint32_t* xbuf;    // [groups][2][BR][G*D] exchange words
   int* err;
   long long timeout_ticks;
@@ -826,8 +826,8 @@ __host__ __device__ constexpr int fused_bwdl_row(int G, int D, bool bf = false) 
 constexpr int BWDL_NE = 8;
 constexpr int BWDL_SLOT = 64 * 16 * BWDL_NE;
 // Floats a record in this design: an Elman cell's two coefficients alone (compact records:
-// bwd_record_kernel with REC = 2), else BWD_REC. With an Elman cell the design also stores the
-// step's dWx and da itself, so no post kernel runs.
+// bwd_record_kernel with REC = 2, read where FRNN_BWD_ELMAN_RAW=0 pins them instead of the raw
+// inputs), else BWD_REC.
 __host__ __device__ constexpr int bwdl_rec(int cell) { return cell == CELL_ELMAN ? 2 : BWD_REC; }
 
 struct FusedBwdlLds {

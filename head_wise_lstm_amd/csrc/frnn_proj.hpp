@@ -294,10 +294,13 @@ __global__ void __launch_bounds__(256, 2) proj_gemm_kernel(ProjArgs p) {
 // different 16-byte bank groups. Rows past the end load the last row: only outputs that are never
 // stored depend on them. A and Bt rows must start on 16-byte boundaries.
 constexpr int PD_STAGES = 3;
-constexpr int PD_A_BYTES = PJ_BM * PJ_BK * 2, PD_B_BYTES = PJ_BN * PJ_BK * 2;
-constexpr int PD_STAGE_BYTES = PD_A_BYTES + PD_B_BYTES;  // 24 KB: two workgroups fit a CU with 3 stages
-constexpr int PD_A_LOADS = PJ_BM / 16 / 4, PD_B_LOADS = PJ_BN / 16 / 4;  // per wave and stage: 4 and 2
-constexpr int PD_LOADS = PD_A_LOADS + PD_B_LOADS;
+// BM rows a tile: 256, or 128 for products of at most 128 rows (a head's dR and db, D + 1 rows),
+// which would leave most of a 256-row tile's loads and MFMAs on rows past the end
+__host__ __device__ constexpr int pd_a_bytes(int BM) { return BM * PJ_BK * 2; }
+constexpr int PD_B_BYTES = PJ_BN * PJ_BK * 2;
+__host__ __device__ constexpr int pd_stage_bytes(int BM) { return pd_a_bytes(BM) + PD_B_BYTES; }  // 24 KB at 256 rows
+__host__ __device__ constexpr int pd_a_loads(int BM) { return BM / 16 / 4; }  // per wave and stage: 4 (256 rows)
+constexpr int PD_B_LOADS = PJ_BN / 16 / 4;                                    // 2
 
 typedef __attribute__((address_space(3))) void pd_lds_t;
 typedef __attribute__((address_space(1))) void pd_glb_t;
@@ -306,8 +309,11 @@ typedef __attribute__((address_space(1))) void pd_glb_t;
 // LDS operation remain (expcnt left alone).
 __host__ __device__ constexpr int pd_vmcnt(int n) { return (n & 0xF) | (7 << 4) | ((n >> 4) << 14); }
 
-template <bool NT>
+template <bool NT, int BM = PJ_BM>
 __global__ void __launch_bounds__(256, 2) proj_gemm_dma_kernel(ProjArgs p) {
+  constexpr int PD_A_BYTES = pd_a_bytes(BM), PD_STAGE_BYTES = pd_stage_bytes(BM);
+  constexpr int PD_A_LOADS = pd_a_loads(BM), PD_LOADS = PD_A_LOADS + PD_B_LOADS;
+  constexpr int WMB = BM / 32;  // 16-row blocks of a wave's half of the tile
   __shared__ __attribute__((aligned(1024))) char ring[PD_STAGES * PD_STAGE_BYTES];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int col = lane & 15, quad = lane >> 4;
@@ -320,10 +326,11 @@ __global__ void __launch_bounds__(256, 2) proj_gemm_dma_kernel(ProjArgs p) {
   const int ntn = (p.Nc + PJ_BN - 1) / PJ_BN;
   const int L = blockIdx.x, G = gridDim.x;
   const int tile = (G % PJ_DIES == 0) ? (L % PJ_DIES) * (G / PJ_DIES) + L / PJ_DIES : L;
-  const long long m0 = (long long)(tile / ntn) * PJ_BM;
+  const long long m0 = (long long)(tile / ntn) * BM;
   const int n0 = (tile % ntn) * PJ_BN;
 
-  // this lane's source rows: A blocks 4 wave + e, B blocks 2 wave + e; the chunk for position lane % 4
+  // this lane's source rows: A blocks PD_A_LOADS wave + e, B blocks 2 wave + e; the chunk for
+  // position lane % 4
   const int brow = lane >> 2, chunk = (lane & 3) ^ ((lane >> 4) & 3);
   const char* asrc[PD_A_LOADS];
   const char* bsrc[PD_B_LOADS];
@@ -352,9 +359,9 @@ __global__ void __launch_bounds__(256, 2) proj_gemm_dma_kernel(ProjArgs p) {
   // fragment (row col of a 16-row block, k 8 quad .. 8 quad + 7)
   const int foff = col * 64 + ((quad ^ (col >> 2)) & 3) * 16;
 
-  f32x4_t acc[8][4];
+  f32x4_t acc[WMB][4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < WMB; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
@@ -376,8 +383,8 @@ __global__ void __launch_bounds__(256, 2) proj_gemm_dma_kernel(ProjArgs p) {
     for (int j = 0; j < 4; ++j)
       bfr[j] = *reinterpret_cast<const bf16x8_t*>(st + PD_A_BYTES + 1024 * (wn * 4 + j) + foff);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const bf16x8_t af = *reinterpret_cast<const bf16x8_t*>(st + 1024 * (wm * 8 + i) + foff);
+    for (int i = 0; i < WMB; ++i) {
+      const bf16x8_t af = *reinterpret_cast<const bf16x8_t*>(st + 1024 * (wm * WMB + i) + foff);
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[i][j] = mfma_bf16(af, bfr[j], acc[i][j]);
     }
@@ -389,10 +396,10 @@ __global__ void __launch_bounds__(256, 2) proj_gemm_dma_kernel(ProjArgs p) {
     if (gn >= p.Nc) continue;
     const float bias = (p.b1 ? bf2f(p.b1[gn]) : 0.0f) + (p.b2 ? bf2f(p.b2[gn]) : 0.0f);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < WMB; ++i) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const long long gm = m0 + wm * 128 + i * 16 + 4 * quad + r;
+        const long long gm = m0 + wm * (BM / 2) + i * 16 + 4 * quad + r;
         if (gm < p.M) proj_put<NT>(&p.C[gm * p.ldc + gn], acc[i][j][r] + bias);
       }
     }
