@@ -320,6 +320,19 @@ def test_fused_bwd_planner(lib):
     # step's records of four 64-unit rows fill one 8 KB ring slot), all 192 groups in one launch
     s = hw.frnn_bwd_plan_str(D(B=64, T=8, N=12, Dm=64, cell=1), 1)
     assert "design=workgroup-local " in s and "BR=4 " in s and "groups=192 " in s and "chunks=1 " in s, s
+    # every bf16 head of at most 64 units takes it (on the bf16 MFMA: k-tiles of 32), wider ones
+    # the partial sums
+    for cell, G in ((0, 4), (2, 3)):
+        s = hw.frnn_bwd_plan_str(D(B=16, T=8, N=1, Dm=64, cell=cell), 1)
+        assert "design=workgroup-local " in s and f"KTW={G * 64 // 32} " in s, s
+        s = hw.frnn_bwd_plan_str(D(B=16, T=8, N=1, Dm=64, cell=cell, ind=0), 1)
+        assert "design=workgroup-local " in s and f"KTW={G * 64 // 4} " in s, s  # fp32: k-tiles of 4
+        assert "die-local-partials" in hw.frnn_bwd_plan_str(D(B=16, T=8, N=1, Dm=128, cell=cell), 1)
+    # the dR GEMM's K (T*B) is padded to whole k-tiles of every part: 64 parts for twelve narrow heads
+    s = hw.frnn_bwd_plan_str(D(B=64, T=2048, N=12, Dm=64, cell=1), 0)
+    assert "dR_gemm=65x64x131072 " in s, s
+    s = hw.frnn_bwd_plan_str(D(B=3, T=5, N=12, Dm=64, cell=1), 0)
+    assert "dR_gemm=65x64x256 " in s, s
     # the partial-sum design needs more launches than the da exchange there
     old = os.environ.get("FRNN_FUSED_BWD_PX")
     try:
