@@ -64,6 +64,25 @@ def test_write_traffic_scales_by_the_copy_calibration(tmp_path):
     assert e["kernel_sources_sha256_16"] == bench.kernel_sources_hash()
 
 
+def test_write_traffic_backward_algorithmic_bytes(tmp_path):
+    # the partial-sum serial kernel's own bytes: 8-float step records read once, dWx (fp32) and the
+    # dR operand da (bf16) of every gate written once, R read once
+    kname = "void frnn::fused_bwdx_kernel<0, 8, 6, 3, 0>(frnn::FusedBwdArgs)"
+    true_kib = 256 * 1024.0
+    fetch, write = tmp_path / "fetch.csv", tmp_path / "write.csv"
+    _write_counters(fetch, [(kname, 100.0)] + [("__amd_rocclr_copyBuffer", true_kib)] * 5)
+    _write_counters(write, [(kname, 50.0)] + [("__amd_rocclr_copyBuffer", true_kib)] * 5)
+    tj = tmp_path / "traffic.json"
+    args = types.SimpleNamespace(write_traffic=[str(fetch), str(write), str(fetch), str(write)], backward=True,
+                                 path="fused", copy_mib=256, workload="lstm_bf16_B16_T1024_N1_D768",
+                                 traffic_json=str(tj))
+    bench.write_traffic(args)
+    e = json.load(open(tj))["lstm_bf16_B16_T1024_N1_D768:fused:backward"]
+    B, T, N, D, G = 16, 1024, 1, 768, 4
+    assert e["kernel"] == kname
+    assert e["algorithmic_bytes"] == B * T * N * D * (8 * 4 + G * (4 + 2)) + G * N * D * D * 2 == 709361664
+
+
 def test_headwise_flops_and_bytes():
     w = types.SimpleNamespace(B=16, T=1024, N=1, D=768, G=4, S=2, s0_var=None)
     assert bench.headwise_flops(w) == 2.0 * 16 * 1 * 4 * 768 * 768 * 1024 == pytest.approx(77.31e9, rel=1e-3)
